@@ -1,0 +1,199 @@
+"""Thin ctypes binding of the C ABI in ``include/gs.h`` (same names).
+
+Argument marshalling only: tensors become device pointers, cameras become
+``gs_camera`` structs, the current HIP stream is passed through. Every step of
+the computation runs in the HIP library; if that library is not built, every
+call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgs_hip.so")
+
+GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_CAPACITY, GS_ERR_HIP, GS_ERR_UNSUPPORTED = range(5)
+GS_TILE = 16
+GS_MAX_VIEWS = 16
+GS_REC_FLOATS = 12
+GS_GRAD2D_ROWS = 9
+(REC_U, REC_V, REC_A, REC_B, REC_C, REC_OPACITY, REC_R, REC_G, REC_BLUE,
+ REC_EXT_X, REC_EXT_Y, REC_DEPTH) = range(12)
+
+# every function the header declares, for the export check
+EXPORTS = (
+    "gs_abi_version", "gs_status_string", "gs_param_rows", "gs_tiles_x", "gs_tiles_y",
+    "gs_sort_end_bit", "gs_preprocess_workspace_bytes", "gs_sort_workspace_bytes",
+    "gs_preprocess", "gs_emit_intersections", "gs_sort_keys", "gs_tile_ranges",
+    "gs_rasterize_fwd", "gs_loss_l1", "gs_rasterize_bwd", "gs_preprocess_bwd", "gs_adam_step",
+)
+
+
+class GsError(RuntimeError):
+    pass
+
+
+class GsCamera(ctypes.Structure):
+    _fields_ = [
+        ("width", ctypes.c_int32), ("height", ctypes.c_int32),
+        ("fx", ctypes.c_float), ("fy", ctypes.c_float),
+        ("cx", ctypes.c_float), ("cy", ctypes.c_float),
+        ("R", ctypes.c_float * 9), ("t", ctypes.c_float * 3),
+        ("near_plane", ctypes.c_float), ("far_plane", ctypes.c_float),
+    ]
+
+
+_P = ctypes.c_void_p
+_I32, _I64, _U64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+_F32, _F64, _SZ = ctypes.c_float, ctypes.c_double, ctypes.c_size_t
+_LIB = None
+
+
+def lib():
+    """Load the HIP library (raises when it is not built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise GsError(f"HIP library {LIB_PATH} is not built (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "gs_abi_version": ([], ctypes.c_int),
+            "gs_status_string": ([ctypes.c_int], ctypes.c_char_p),
+            "gs_param_rows": ([_I32], ctypes.c_int),
+            "gs_tiles_x": ([_I32], _I32),
+            "gs_tiles_y": ([_I32], _I32),
+            "gs_sort_end_bit": ([_I32, _I64], _I32),
+            "gs_preprocess_workspace_bytes": ([_I64, _I32], _SZ),
+            "gs_sort_workspace_bytes": ([_U64], _SZ),
+            "gs_preprocess": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+            "gs_emit_intersections": ([_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _U64, _P, _P], ctypes.c_int),
+            "gs_sort_keys": ([_P, _P, _P, _P, _U64, _I32, _P, _SZ, _P, _P], ctypes.c_int),
+            "gs_tile_ranges": ([_P, _U64, _I64, _P, _P], ctypes.c_int),
+            "gs_rasterize_fwd": ([_P, _I64, _P, _P, _P, _I32, _P, _P, _P, _P, _P], ctypes.c_int),
+            "gs_loss_l1": ([_P, _P, _I64, _F32, _P, _P, _I32, _P], ctypes.c_int),
+            "gs_rasterize_bwd": ([_P, _I64, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _I32, _P], ctypes.c_int),
+            "gs_preprocess_bwd": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P], ctypes.c_int),
+            "gs_adam_step": ([_P, _P, _P, _P, _I64, _F64, _F64, _F64, _F64, _I64, _P], ctypes.c_int),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _LIB = L
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return lib().gs_status_string(status).decode()
+
+
+def _check(status: int, name: str):
+    if status != GS_OK:
+        raise GsError(f"{name} failed: {status_string(status)} ({status})")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def cameras(cams: Sequence):
+    arr = (GsCamera * len(cams))()
+    for k, c in enumerate(cams):
+        o = arr[k]
+        o.width, o.height = int(c.width), int(c.height)
+        o.fx, o.fy, o.cx, o.cy = c.fx, c.fy, c.cx, c.cy
+        for i in range(9):
+            o.R[i] = c.R[i]
+        for i in range(3):
+            o.t[i] = c.t[i]
+        o.near_plane, o.far_plane = c.near, c.far
+    return arr
+
+
+# ---- queries (host only) ----------------------------------------------------
+def abi_version() -> int:
+    return lib().gs_abi_version()
+
+
+def param_rows(sh_degree: int) -> int:
+    return lib().gs_param_rows(sh_degree)
+
+
+def sort_end_bit(n_views: int, tiles_per_view: int) -> int:
+    return lib().gs_sort_end_bit(n_views, tiles_per_view)
+
+
+def preprocess_workspace_bytes(n: int, n_views: int) -> int:
+    return lib().gs_preprocess_workspace_bytes(n, n_views)
+
+
+def sort_workspace_bytes(n_keys: int) -> int:
+    return lib().gs_sort_workspace_bytes(n_keys)
+
+
+# ---- the step ----------------------------------------------------------------
+def gs_preprocess(params, n, sh_degree, cams, rec, rect, offsets, total, ws, stream=None):
+    cc = cameras(cams)
+    _check(lib().gs_preprocess(_ptr(params), n, sh_degree, cc, len(cams), _ptr(rec), _ptr(rect),
+                               _ptr(offsets), _ptr(total), _ptr(ws), ws.numel() * ws.element_size(),
+                               _stream(stream)), "gs_preprocess")
+
+
+def gs_emit_intersections(rec, rect, offsets, n, n_views, width, height, keys, vals, capacity,
+                          overflow, stream=None):
+    _check(lib().gs_emit_intersections(_ptr(rec), _ptr(rect), _ptr(offsets), n, n_views, width, height,
+                                       _ptr(keys), _ptr(vals), capacity, _ptr(overflow),
+                                       _stream(stream)), "gs_emit_intersections")
+
+
+def gs_sort_keys(keys, vals, keys_alt, vals_alt, n_keys, end_bit, ws, stream=None) -> bool:
+    """Returns True when the sorted data ended in the alt pair."""
+    alt = ctypes.c_int32(0)
+    _check(lib().gs_sort_keys(_ptr(keys), _ptr(vals), _ptr(keys_alt), _ptr(vals_alt), n_keys, end_bit,
+                              _ptr(ws), ws.numel() * ws.element_size(), ctypes.byref(alt),
+                              _stream(stream)), "gs_sort_keys")
+    return bool(alt.value)
+
+
+def gs_tile_ranges(keys, n_keys, n_tiles_total, ranges, stream=None):
+    _check(lib().gs_tile_ranges(_ptr(keys), n_keys, n_tiles_total, _ptr(ranges), _stream(stream)),
+           "gs_tile_ranges")
+
+
+def gs_rasterize_fwd(rec, n, ranges, vals, cams, bg, image, T_final, n_contrib, stream=None):
+    bgv = (ctypes.c_float * 3)(*bg)
+    _check(lib().gs_rasterize_fwd(_ptr(rec), n, _ptr(ranges), _ptr(vals), cameras(cams), len(cams), bgv,
+                                  _ptr(image), _ptr(T_final), _ptr(n_contrib), _stream(stream)),
+           "gs_rasterize_fwd")
+
+
+def gs_loss_l1(image, target, count, scale, dL_dimage, loss, accumulate=False, stream=None):
+    _check(lib().gs_loss_l1(_ptr(image), _ptr(target), count, scale, _ptr(dL_dimage), _ptr(loss),
+                            int(bool(accumulate)), _stream(stream)), "gs_loss_l1")
+
+
+def gs_rasterize_bwd(rec, n, ranges, vals, cams, bg, T_final, n_contrib, dL_dimage, grad2d,
+                     accumulate=False, stream=None):
+    bgv = (ctypes.c_float * 3)(*bg)
+    _check(lib().gs_rasterize_bwd(_ptr(rec), n, _ptr(ranges), _ptr(vals), cameras(cams), len(cams), bgv,
+                                  _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimage), _ptr(grad2d),
+                                  int(bool(accumulate)), _stream(stream)), "gs_rasterize_bwd")
+
+
+def gs_preprocess_bwd(params, n, sh_degree, cams, rect, grad2d, grad_params, stream=None):
+    _check(lib().gs_preprocess_bwd(_ptr(params), n, sh_degree, cameras(cams), len(cams), _ptr(rect),
+                                   _ptr(grad2d), _ptr(grad_params), _stream(stream)), "gs_preprocess_bwd")
+
+
+def gs_adam_step(params, grad, m, v, count, lr, beta1, beta2, eps, step, stream=None):
+    _check(lib().gs_adam_step(_ptr(params), _ptr(grad), _ptr(m), _ptr(v), count, lr, beta1, beta2, eps,
+                              step, _stream(stream)), "gs_adam_step")

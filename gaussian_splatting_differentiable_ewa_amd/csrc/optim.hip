@@ -1,0 +1,142 @@
+// gs_loss_l1 and gs_adam_step: element-wise streaming kernels (HBM-bound).
+//
+// L1 loss with views averaged ("On Scaling Up 3D Gaussian Splatting
+// Training", answer on the Independent Gradients Hypothesis: gradients
+// averaged over the views of a batch); Adam of Kingma & Ba (reference [12] of
+// "A Scalable PyTorch Abstraction for Multi-GPU Gaussian Splatting") with the
+// two moment vectors that make up 708 bytes per Gaussian ("AMD ROCm team
+// open-sources distributed 3D Gaussian Splatting...", section "Distributed
+// training architecture and memory scaling").
+#include <math.h>
+
+#include "internal.h"
+
+namespace gs {
+
+constexpr int EW_THREADS = 256;
+
+__global__ __launch_bounds__(EW_THREADS) void k_loss_l1(const float* __restrict__ image,
+                                                        const float* __restrict__ target, int64_t count,
+                                                        float scale, float* __restrict__ dL,
+                                                        double* __restrict__ loss)
+{
+    __shared__ double s_part[EW_THREADS / 64];
+    const int64_t stride = (int64_t)gridDim.x * EW_THREADS * 4;
+    double acc = 0.0;
+    for (int64_t base = ((int64_t)blockIdx.x * EW_THREADS + threadIdx.x) * 4; base < count; base += stride) {
+        if (base + 4 <= count) {
+            const float4 a = *(const float4*)(image + base), b = *(const float4*)(target + base);
+            const float d0 = a.x - b.x, d1 = a.y - b.y, d2 = a.z - b.z, d3 = a.w - b.w;
+            acc += (double)(fabsf(d0) + fabsf(d1)) + (double)(fabsf(d2) + fabsf(d3));
+            *(float4*)(dL + base) =
+                make_float4(d0 > 0.f ? scale : (d0 < 0.f ? -scale : 0.f), d1 > 0.f ? scale : (d1 < 0.f ? -scale : 0.f),
+                            d2 > 0.f ? scale : (d2 < 0.f ? -scale : 0.f), d3 > 0.f ? scale : (d3 < 0.f ? -scale : 0.f));
+        } else {
+            for (int64_t i = base; i < count; ++i) {
+                const float d = image[i] - target[i];
+                acc += (double)fabsf(d);
+                dL[i] = d > 0.f ? scale : (d < 0.f ? -scale : 0.f);
+            }
+        }
+    }
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = 0.0;
+        for (int w = 0; w < EW_THREADS / 64; ++w) t += s_part[w];
+        atomicAdd(loss, t * (double)scale);
+    }
+}
+
+struct AdamConsts {
+    float b1, omb1, b2, omb2;  // beta and 1 - beta, each rounded once from fp64
+    float eps;
+    float step_size;     // lr / (1 - beta1^t)
+    float inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^t)
+};
+
+__device__ __forceinline__ void adam1(float& p, float g, float& m, float& v, const AdamConsts& c)
+{
+    m = c.b1 * m + c.omb1 * g;
+    v = c.b2 * v + c.omb2 * (g * g);
+    p = p - c.step_size * m / (sqrtf(v) * c.inv_sqrt_bc2 + c.eps);
+}
+
+__global__ __launch_bounds__(EW_THREADS) void k_adam(float* __restrict__ params, const float* __restrict__ grad,
+                                                     float* __restrict__ m, float* __restrict__ v, int64_t count,
+                                                     const AdamConsts c)
+{
+    const int64_t stride = (int64_t)gridDim.x * EW_THREADS * 4;
+    for (int64_t base = ((int64_t)blockIdx.x * EW_THREADS + threadIdx.x) * 4; base < count; base += stride) {
+        if (base + 4 <= count) {
+            float4 p = *(float4*)(params + base), mm = *(float4*)(m + base), vv = *(float4*)(v + base);
+            const float4 g = *(const float4*)(grad + base);
+            adam1(p.x, g.x, mm.x, vv.x, c);
+            adam1(p.y, g.y, mm.y, vv.y, c);
+            adam1(p.z, g.z, mm.z, vv.z, c);
+            adam1(p.w, g.w, mm.w, vv.w, c);
+            *(float4*)(params + base) = p;
+            *(float4*)(m + base) = mm;
+            *(float4*)(v + base) = vv;
+        } else {
+            for (int64_t i = base; i < count; ++i) adam1(params[i], grad[i], m[i], v[i], c);
+        }
+    }
+}
+
+// Enough blocks to fill the chip several times over; each thread then walks
+// its grid-stride range.
+static unsigned stream_blocks(int64_t count)
+{
+    const int64_t need = (count / 4 + EW_THREADS - 1) / EW_THREADS;
+    const int64_t cap = 256 * 32;
+    return (unsigned)(need < 1 ? 1 : (need > cap ? cap : need));
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace gs
+
+using namespace gs;
+
+extern "C" {
+
+gs_status gs_loss_l1(const float* image, const float* target, int64_t count, float scale, float* dL_dimage,
+                     double* loss, int32_t accumulate, void* stream)
+{
+    if (count < 0 || !loss) return GS_ERR_INVALID_ARGUMENT;
+    if (count > 0 && (!image || !target || !dL_dimage)) return GS_ERR_INVALID_ARGUMENT;
+    if (!aligned16(image) || !aligned16(target) || !aligned16(dL_dimage)) return GS_ERR_INVALID_ARGUMENT;
+    hipStream_t s = (hipStream_t)stream;
+    if (!accumulate && fill_u32((uint32_t*)loss, 2, 0u, s) != hipSuccess) return GS_ERR_HIP;
+    if (count == 0) return GS_OK;
+    hipLaunchKernelGGL(k_loss_l1, dim3(stream_blocks(count)), dim3(EW_THREADS), 0, s, image, target,
+                       count, scale, dL_dimage, loss);
+    return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
+}
+
+gs_status gs_adam_step(float* params, const float* grad, float* m, float* v, int64_t count, double lr, double beta1,
+                       double beta2, double eps, int64_t step, void* stream)
+{
+    if (count < 0 || step < 1) return GS_ERR_INVALID_ARGUMENT;
+    if (count > 0 && (!params || !grad || !m || !v)) return GS_ERR_INVALID_ARGUMENT;
+    if (!aligned16(params) || !aligned16(grad) || !aligned16(m) || !aligned16(v)) return GS_ERR_INVALID_ARGUMENT;
+    if (count == 0) return GS_OK;
+    if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) || !(eps >= 0.0)) return GS_ERR_INVALID_ARGUMENT;
+    const double bc1 = 1.0 - pow(beta1, (double)step);
+    const double bc2 = 1.0 - pow(beta2, (double)step);
+    AdamConsts c;
+    c.b1 = (float)beta1;
+    c.omb1 = (float)(1.0 - beta1);
+    c.b2 = (float)beta2;
+    c.omb2 = (float)(1.0 - beta2);
+    c.eps = (float)eps;
+    c.step_size = (float)(lr / bc1);
+    c.inv_sqrt_bc2 = (float)(1.0 / sqrt(bc2));
+    hipLaunchKernelGGL(k_adam, dim3(stream_blocks(count)), dim3(EW_THREADS), 0, (hipStream_t)stream, params, grad, m,
+                       v, count, c);
+    return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
+}
+
+}  // extern "C"

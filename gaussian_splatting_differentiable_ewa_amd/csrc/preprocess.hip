@@ -1,0 +1,180 @@
+// gs_preprocess (Gaussian-wise projection + prefix sum of tile counts),
+// gs_emit_intersections and gs_tile_ranges.
+//
+// Layout: parameters are [P][n] SoA, so a wave's 64 lanes read 64 consecutive
+// floats of each row (one 256-byte line per row). Each lane writes its
+// 48-byte record per view as three 16-byte stores.
+#include <math.h>
+
+#include "internal.h"
+#include "project.h"
+
+namespace gs {
+
+constexpr int PRE_THREADS = 256;
+
+// Half-extent of the region where alpha = o exp(-d^T Q d / 2) reaches 1/255:
+// the ellipse d^T Q d <= 2 ln(255 o), whose bounding half-widths are
+// sqrt(tau a) and sqrt(tau c) (a, c the diagonal of Q^-1 = Sigma2). The
+// threshold is widened (x1.002 + 0.01, +0.05 px) so that fp32 rounding of the
+// per-pixel test can never fall outside it. Negative: no pixel can reach it.
+__device__ __forceinline__ void alpha_extent(float o, float a, float c, float& ex, float& ey)
+{
+    const float t = 255.f * o;
+    if (!(t > 1.f)) {
+        ex = -1.f;
+        ey = -1.f;
+        return;
+    }
+    const float tau = 2.f * logf(t) * 1.002f + 0.01f;
+    ex = sqrtf(tau * a) + 0.05f;
+    ey = sqrtf(tau * c) + 0.05f;
+}
+
+__global__ __launch_bounds__(PRE_THREADS) void k_preprocess(const float* __restrict__ P, int64_t n, int deg,
+                                                            const DevCameras cams, const ShConsts K,
+                                                            float* __restrict__ rec, uint16_t* __restrict__ rect,
+                                                            uint32_t* __restrict__ counts)
+{
+    const int64_t g = (int64_t)blockIdx.x * PRE_THREADS + threadIdx.x;
+    if (g >= n) return;
+    const float x = P[0 * n + g], y = P[1 * n + g], z = P[2 * n + g];
+    GaussLocal L;
+    gauss_local(P[3 * n + g], P[4 * n + g], P[5 * n + g], P[6 * n + g], P[7 * n + g], P[8 * n + g],
+                P[9 * n + g], P[10 * n + g], L);
+    const int nb = (deg + 1) * (deg + 1);
+    const float* sh = P + 11 * n;
+    for (int v = 0; v < cams.n_views; ++v) {
+        const DevCamera& cam = cams.c[v];
+        ViewProj p;
+        view_project(x, y, z, L, cam, cams.tiles_x, cams.tiles_y, p);
+        const int64_t idx = (int64_t)v * n + g;
+        if (!p.visible) {
+            counts[idx] = 0u;
+            *(uint2*)(rect + 4 * idx) = make_uint2(0u, 0u);
+            continue;
+        }
+        float d[3], dist;
+        view_dir(x, y, z, cam, d, dist);
+        float Y[16];
+        sh_eval_basis(K, deg, d, Y);
+        bool cl;
+        const float r = sh_channel(sh, n, g, nb, 0, Y, cl);
+        const float gg = sh_channel(sh, n, g, nb, 1, Y, cl);
+        const float b = sh_channel(sh, n, g, nb, 2, Y, cl);
+        float ex, ey;
+        alpha_extent(L.o, p.a, p.c, ex, ey);
+        float4* out = (float4*)(rec + idx * GS_REC_FLOATS);
+        out[0] = make_float4(p.u, p.v, p.A, p.B);
+        out[1] = make_float4(p.C, L.o, r, gg);
+        out[2] = make_float4(b, ex, ey, p.zc);
+        *(uint2*)(rect + 4 * idx) = make_uint2((uint32_t)p.x0 | ((uint32_t)p.y0 << 16),
+                                               (uint32_t)p.x1 | ((uint32_t)p.y1 << 16));
+        counts[idx] = (uint32_t)((p.x1 - p.x0) * (p.y1 - p.y0));
+    }
+}
+
+// One thread per (view, Gaussian): its tiles in row-major order, at its offset.
+__global__ __launch_bounds__(256) void k_emit(const float* __restrict__ rec, const uint16_t* __restrict__ rect,
+                                              const uint32_t* __restrict__ offsets, int64_t n, int64_t total_entries,
+                                              int32_t tiles_x, int64_t tiles_per_view, uint64_t* __restrict__ keys,
+                                              uint32_t* __restrict__ vals, uint64_t capacity,
+                                              int32_t* __restrict__ overflow)
+{
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total_entries) return;
+    const uint2 rr = *(const uint2*)(rect + 4 * idx);
+    const uint32_t x0 = rr.x & 0xffffu, y0 = rr.x >> 16, x1 = rr.y & 0xffffu, y1 = rr.y >> 16;
+    if (x1 <= x0 || y1 <= y0) return;
+    const int64_t v = idx / n, g = idx - v * n;
+    const uint32_t zb = __float_as_uint(rec[idx * GS_REC_FLOATS + GS_REC_DEPTH]);
+    uint64_t k = offsets[idx];
+    const uint64_t tbase = (uint64_t)v * (uint64_t)tiles_per_view;
+    bool over = false;
+    for (uint32_t ty = y0; ty < y1; ++ty)
+        for (uint32_t tx = x0; tx < x1; ++tx, ++k) {
+            if (k >= capacity) {
+                over = true;
+                continue;
+            }
+            keys[k] = ((tbase + (uint64_t)ty * tiles_x + tx) << 32) | zb;
+            vals[k] = (uint32_t)g;
+        }
+    if (over) *overflow = 1;
+}
+
+__global__ __launch_bounds__(256) void k_ranges(const uint64_t* __restrict__ keys, uint64_t n_keys,
+                                                uint64_t n_tiles_total, uint32_t* __restrict__ ranges)
+{
+    const uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_keys) return;
+    const uint32_t t = (uint32_t)(keys[i] >> 32);
+    if (t >= n_tiles_total) return;  // not a key of this tile grid
+    if (i == 0 || (uint32_t)(keys[i - 1] >> 32) != t) ranges[2 * (uint64_t)t] = (uint32_t)i;
+    if (i + 1 == n_keys || (uint32_t)(keys[i + 1] >> 32) != t) ranges[2 * (uint64_t)t + 1] = (uint32_t)(i + 1);
+}
+
+}  // namespace gs
+
+using namespace gs;
+
+extern "C" {
+
+gs_status gs_preprocess(const float* params, int64_t n, int32_t sh_degree, const gs_camera* cams,
+                        int32_t n_views, float* rec, uint16_t* rect, uint32_t* offsets, uint64_t* total,
+                        void* ws, size_t ws_bytes, void* stream)
+{
+    if (n < 0 || sh_degree < 0 || sh_degree > 3) return GS_ERR_INVALID_ARGUMENT;
+    if (!offsets || !total || !ws) return GS_ERR_INVALID_ARGUMENT;
+    if (n > 0 && (!params || !rec || !rect)) return GS_ERR_INVALID_ARGUMENT;
+    if (n > ((int64_t)1 << 31)) return GS_ERR_INVALID_ARGUMENT;
+    DevCameras dc;
+    if (!make_dev_cameras(cams, n_views, dc)) return GS_ERR_INVALID_ARGUMENT;
+    const uint64_t entries = (uint64_t)n * (uint64_t)n_views;
+    if (ws_bytes < scan_workspace_bytes(entries)) return GS_ERR_INVALID_ARGUMENT;
+    hipStream_t s = (hipStream_t)stream;
+    if (n > 0) {
+        hipLaunchKernelGGL(k_preprocess, dim3(grid_for((uint64_t)n, PRE_THREADS)), dim3(PRE_THREADS), 0, s,
+                           params, n, sh_degree, dc, sh_constants(), rec, rect, offsets);
+        if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
+    }
+    // counts were written into `offsets`; scan them in place
+    if (scan_u32(offsets, offsets, entries, total, ws, s) != hipSuccess) return GS_ERR_HIP;
+    return GS_OK;
+}
+
+gs_status gs_emit_intersections(const float* rec, const uint16_t* rect, const uint32_t* offsets, int64_t n,
+                                int32_t n_views, int32_t width, int32_t height, uint64_t* keys, uint32_t* vals,
+                                uint64_t capacity, int32_t* overflow, void* stream)
+{
+    if (n < 0 || n_views < 1 || n_views > GS_MAX_VIEWS || width <= 0 || height <= 0)
+        return GS_ERR_INVALID_ARGUMENT;
+    if (!offsets || !overflow) return GS_ERR_INVALID_ARGUMENT;
+    if (n > 0 && (!rec || !rect)) return GS_ERR_INVALID_ARGUMENT;
+    if (capacity > 0 && (!keys || !vals)) return GS_ERR_INVALID_ARGUMENT;
+    const int64_t tx = gs_tiles_x(width), tpv = tx * gs_tiles_y(height);
+    if (tpv * n_views >= ((int64_t)1 << 31)) return GS_ERR_INVALID_ARGUMENT;
+    const int64_t entries = n * n_views;
+    if (fill_u32((uint32_t*)overflow, 1, 0u, (hipStream_t)stream) != hipSuccess) return GS_ERR_HIP;
+    if (entries == 0) return GS_OK;
+    hipLaunchKernelGGL(k_emit, dim3(grid_for((uint64_t)entries, 256)), dim3(256), 0, (hipStream_t)stream, rec,
+                       rect, offsets, n, entries, (int32_t)tx, tpv, keys, vals, capacity, overflow);
+    return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
+}
+
+gs_status gs_tile_ranges(const uint64_t* keys, uint64_t n_keys, int64_t n_tiles_total, uint32_t* ranges,
+                         void* stream)
+{
+    if (n_tiles_total < 0 || !ranges || (n_keys > 0 && !keys)) return GS_ERR_INVALID_ARGUMENT;
+    if (n_keys >= ((uint64_t)1 << 32)) return GS_ERR_INVALID_ARGUMENT;
+    hipStream_t s = (hipStream_t)stream;
+    if (fill_u32(ranges, 2 * (uint64_t)n_tiles_total, 0u, s) != hipSuccess) return GS_ERR_HIP;
+    if (n_keys > 0) {
+        hipLaunchKernelGGL(k_ranges, dim3(grid_for(n_keys, 256)), dim3(256), 0, s, keys, n_keys,
+                           (uint64_t)n_tiles_total, ranges);
+        if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
+    }
+    return GS_OK;
+}
+
+}  // extern "C"

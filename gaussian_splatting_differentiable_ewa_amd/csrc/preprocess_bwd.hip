@@ -1,0 +1,245 @@
+// gs_preprocess_bwd: chain rule from the 2D gradients (u, v, conic, opacity,
+// colour) of every (view, Gaussian) to the 59 (SH degree 3) parameters of the
+// Gaussian, summed over the views -- the Gaussian-wise half of the backward
+// pass ("Gaussian-wise computations" of "On Scaling Up 3D Gaussian Splatting
+// Training"; parameter set from its answer on the storage requirement).
+//
+// One thread per Gaussian. The forward quantities are recomputed with the same
+// fixed-order code as gs_preprocess (project.h), so every decision (culling,
+// guard-band clamp, colour clamp) is the forward's; the gradient arithmetic
+// itself is ordinary fp32.
+#include "internal.h"
+#include "project.h"
+
+namespace gs {
+
+template <int DEG>
+__global__ __launch_bounds__(256) void k_preprocess_bwd(const float* __restrict__ P, int64_t n, const DevCameras cams,
+                                                        const ShConsts K, const uint16_t* __restrict__ rect,
+                                                        const float* __restrict__ grad2d, float* __restrict__ out)
+{
+    constexpr int NB = (DEG + 1) * (DEG + 1);
+    constexpr int ROWS = 11 + 3 * NB;
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (g >= n) return;
+    const float x = P[0 * n + g], y = P[1 * n + g], z = P[2 * n + g];
+    GaussLocal L;
+    gauss_local(P[3 * n + g], P[4 * n + g], P[5 * n + g], P[6 * n + g], P[7 * n + g], P[8 * n + g],
+                P[9 * n + g], P[10 * n + g], L);
+    const float* sh = P + 11 * n;
+
+    float gpx = 0.f, gpy = 0.f, gpz = 0.f, gop = 0.f;
+    float gM[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) gM[i] = 0.f;
+    float gsh[3 * NB];
+#pragma unroll
+    for (int i = 0; i < 3 * NB; ++i) gsh[i] = 0.f;
+    bool any = false;
+
+    for (int v = 0; v < cams.n_views; ++v) {
+        const int64_t idx = (int64_t)v * n + g;
+        const uint2 rr = *(const uint2*)(rect + 4 * idx);
+        if ((rr.y & 0xffffu) <= (rr.x & 0xffffu) || (rr.y >> 16) <= (rr.x >> 16)) continue;  // culled
+        any = true;
+        const DevCamera& cam = cams.c[v];
+        ViewProj p;
+        view_project(x, y, z, L, cam, cams.tiles_x, cams.tiles_y, p);
+        const float* g2 = grad2d + (int64_t)v * GS_GRAD2D_ROWS * n + g;
+        const float gu = g2[0], gv = g2[n], gA = g2[2 * n], gB = g2[3 * n], gC = g2[4 * n];
+        const float go = g2[5 * n];
+        const float grgb[3] = {g2[6 * n], g2[7 * n], g2[8 * n]};
+        gop += go;
+
+        // conic Q = Sigma2^-1: dL/dSigma2 = -Q G Q, G = [[gA, gB/2], [gB/2, gC]]
+        const float hB = 0.5f * gB;
+        const float X00 = gA * p.A + hB * p.B, X01 = gA * p.B + hB * p.C;
+        const float X10 = hB * p.A + gC * p.B, X11 = hB * p.B + gC * p.C;
+        const float ga = -(p.A * X00 + p.B * X10);
+        const float gc = -(p.B * X01 + p.C * X11);
+        const float s01 = -0.5f * ((p.A * X01 + p.B * X11) + (p.B * X00 + p.C * X10));
+        // Sigma2 = T Sigma3 T^T (+ 0.3 I): dSigma3 = T^T G2 T, dT = 2 G2 T Sigma3
+        float Yt[6];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            Yt[k] = ga * p.T[k] + s01 * p.T[3 + k];
+            Yt[3 + k] = s01 * p.T[k] + gc * p.T[3 + k];
+        }
+        float dS3[9];
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+#pragma unroll
+            for (int l = 0; l < 3; ++l) dS3[3 * k + l] = p.T[k] * Yt[l] + p.T[3 + k] * Yt[3 + l];
+        float TS[6];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+                TS[3 * i + k] = p.T[3 * i] * L.S3[k] + p.T[3 * i + 1] * L.S3[3 + k] + p.T[3 * i + 2] * L.S3[6 + k];
+        float dT[6];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            dT[k] = 2.f * (ga * TS[k] + s01 * TS[3 + k]);
+            dT[3 + k] = 2.f * (s01 * TS[k] + gc * TS[3 + k]);
+        }
+        // Sigma3 = M M^T: dM = 2 dSigma3 M
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+                gM[3 * i + j] += 2.f * (dS3[3 * i] * L.M[j] + dS3[3 * i + 1] * L.M[3 + j] + dS3[3 * i + 2] * L.M[6 + j]);
+        // T = J W
+        const float* W = cam.R;
+        const float dJ00 = dT[0] * W[0] + dT[1] * W[1] + dT[2] * W[2];
+        const float dJ02 = dT[0] * W[6] + dT[1] * W[7] + dT[2] * W[8];
+        const float dJ11 = dT[3] * W[3] + dT[4] * W[4] + dT[5] * W[5];
+        const float dJ12 = dT[3] * W[6] + dT[4] * W[7] + dT[5] * W[8];
+        // projected mean and Jacobian -> camera-space mean
+        const float zi = 1.f / p.zc, zi2 = zi * zi, zi3 = zi2 * zi;
+        float dxc = gu * cam.fx * zi;
+        float dyc = gv * cam.fy * zi;
+        float dzc = -(gu * cam.fx * p.xc + gv * cam.fy * p.yc) * zi2;
+        dzc -= (dJ00 * cam.fx + dJ11 * cam.fy) * zi2;
+        if (p.clx) {  // J02 = -fx L / z with L the clamped x/z
+            dzc += dJ02 * cam.fx * p.Lx * zi2;
+        } else {
+            dxc -= dJ02 * cam.fx * zi2;
+            dzc += 2.f * dJ02 * cam.fx * p.xc * zi3;
+        }
+        if (p.cly) {
+            dzc += dJ12 * cam.fy * p.Ly * zi2;
+        } else {
+            dyc -= dJ12 * cam.fy * zi2;
+            dzc += 2.f * dJ12 * cam.fy * p.yc * zi3;
+        }
+        gpx += W[0] * dxc + W[3] * dyc + W[6] * dzc;
+        gpy += W[1] * dxc + W[4] * dyc + W[7] * dzc;
+        gpz += W[2] * dxc + W[5] * dyc + W[8] * dzc;
+
+        // colour: coefficients and view direction
+        float d[3], dist;
+        view_dir(x, y, z, cam, d, dist);
+        float Yb[16];
+        sh_eval_basis(K, DEG, d, Yb);
+        float gcol[3];
+#pragma unroll
+        for (int ch = 0; ch < 3; ++ch) {
+            bool clamped;
+            (void)sh_channel(sh, n, g, NB, ch, Yb, clamped);
+            gcol[ch] = clamped ? 0.f : grgb[ch];
+        }
+        float e[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const float c0 = sh[(int64_t)(3 * k) * n + g], c1 = sh[(int64_t)(3 * k + 1) * n + g],
+                        c2 = sh[(int64_t)(3 * k + 2) * n + g];
+            e[k] = gcol[0] * c0 + gcol[1] * c1 + gcol[2] * c2;
+            gsh[3 * k] += Yb[k] * gcol[0];
+            gsh[3 * k + 1] += Yb[k] * gcol[1];
+            gsh[3 * k + 2] += Yb[k] * gcol[2];
+        }
+        float gdx = 0.f, gdy = 0.f, gdz = 0.f;
+        const float dx_ = d[0], dy_ = d[1], dz_ = d[2];
+        if (DEG >= 1) {
+            gdy -= K.c1 * e[1];
+            gdz += K.c1 * e[2 % NB];
+            gdx -= K.c1 * e[3 % NB];
+        }
+        if (DEG >= 2) {
+            const float xx = dx_ * dx_, yy = dy_ * dy_, zz = dz_ * dz_;
+            gdx += K.c2a * dy_ * e[4 % NB] - 2.f * K.c2b * dx_ * e[6 % NB] - K.c2a * dz_ * e[7 % NB] +
+                   2.f * K.c2c * dx_ * e[8 % NB];
+            gdy += K.c2a * dx_ * e[4 % NB] - K.c2a * dz_ * e[5 % NB] - 2.f * K.c2b * dy_ * e[6 % NB] -
+                   2.f * K.c2c * dy_ * e[8 % NB];
+            gdz += -K.c2a * dy_ * e[5 % NB] + 4.f * K.c2b * dz_ * e[6 % NB] - K.c2a * dx_ * e[7 % NB];
+            if (DEG >= 3) {
+                const float xy = dx_ * dy_, yz = dy_ * dz_, xz = dx_ * dz_;
+                gdx += -6.f * K.c3a * xy * e[9 % NB] + K.c3b * yz * e[10 % NB] + 2.f * K.c3c * xy * e[11 % NB] -
+                       6.f * K.c3d * xz * e[12 % NB] - K.c3c * (4.f * zz - 3.f * xx - yy) * e[13 % NB] +
+                       2.f * K.c3e * xz * e[14 % NB] - K.c3a * (3.f * xx - 3.f * yy) * e[15 % NB];
+                gdy += -K.c3a * (3.f * xx - 3.f * yy) * e[9 % NB] + K.c3b * xz * e[10 % NB] -
+                       K.c3c * (4.f * zz - xx - 3.f * yy) * e[11 % NB] - 6.f * K.c3d * yz * e[12 % NB] +
+                       2.f * K.c3c * xy * e[13 % NB] - 2.f * K.c3e * yz * e[14 % NB] + 6.f * K.c3a * xy * e[15 % NB];
+                gdz += K.c3b * xy * e[10 % NB] - 8.f * K.c3c * yz * e[11 % NB] +
+                       K.c3d * (6.f * zz - 3.f * xx - 3.f * yy) * e[12 % NB] - 8.f * K.c3c * xz * e[13 % NB] +
+                       K.c3e * (xx - yy) * e[14 % NB];
+            }
+        }
+        // d = (p - c) / |p - c|: project out the radial part
+        const float dg = dx_ * gdx + dy_ * gdy + dz_ * gdz;
+        const float inv = 1.f / dist;
+        gpx += (gdx - dx_ * dg) * inv;
+        gpy += (gdy - dy_ * dg) * inv;
+        gpz += (gdz - dz_ * dg) * inv;
+    }
+
+    float G[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) G[r] = 0.f;
+    if (any) {
+        G[0] = gpx;
+        G[1] = gpy;
+        G[2] = gpz;
+        // M = R diag(s)
+        float gR[9];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const float gs = gM[j] * L.Rm[j] + gM[3 + j] * L.Rm[3 + j] + gM[6 + j] * L.Rm[6 + j];
+            G[3 + j] = gs * L.s[j];  // d/d log-scale
+#pragma unroll
+            for (int i = 0; i < 3; ++i) gR[3 * i + j] = gM[3 * i + j] * L.s[j];
+        }
+        // rotation of the unit quaternion (w, x, y, z)
+        const float w = L.q[0], qx = L.q[1], qy = L.q[2], qz = L.q[3];
+        const float gw = 2.f * (-qz * gR[1] + qy * gR[2] + qz * gR[3] - qx * gR[5] - qy * gR[6] + qx * gR[7]);
+        const float gx = 2.f * (qy * gR[1] + qz * gR[2] + qy * gR[3] - 2.f * qx * gR[4] - w * gR[5] + qz * gR[6] +
+                                w * gR[7] - 2.f * qx * gR[8]);
+        const float gy = 2.f * (-2.f * qy * gR[0] + qx * gR[1] + w * gR[2] + qx * gR[3] + qz * gR[5] - w * gR[6] +
+                                qz * gR[7] - 2.f * qy * gR[8]);
+        const float gz = 2.f * (-2.f * qz * gR[0] - w * gR[1] + qx * gR[2] + w * gR[3] - 2.f * qz * gR[4] +
+                                qy * gR[5] + qx * gR[6] + qy * gR[7]);
+        if (L.qn > 0.f) {
+            const float dot = w * gw + qx * gx + qy * gy + qz * gz;
+            const float inv = 1.f / L.qn;
+            G[6] = (gw - w * dot) * inv;
+            G[7] = (gx - qx * dot) * inv;
+            G[8] = (gy - qy * dot) * inv;
+            G[9] = (gz - qz * dot) * inv;
+        }
+        G[10] = gop * L.o * (1.f - L.o);
+#pragma unroll
+        for (int i = 0; i < 3 * NB; ++i) G[11 + i] = gsh[i];
+    }
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) out[(int64_t)r * n + g] = G[r];
+}
+
+}  // namespace gs
+
+using namespace gs;
+
+extern "C" {
+
+gs_status gs_preprocess_bwd(const float* params, int64_t n, int32_t sh_degree, const gs_camera* cams,
+                            int32_t n_views, const uint16_t* rect, const float* grad2d, float* grad_params,
+                            void* stream)
+{
+    if (n < 0 || sh_degree < 0 || sh_degree > 3) return GS_ERR_INVALID_ARGUMENT;
+    if (n > 0 && (!params || !rect || !grad2d || !grad_params)) return GS_ERR_INVALID_ARGUMENT;
+    if (n > ((int64_t)1 << 31)) return GS_ERR_INVALID_ARGUMENT;
+    DevCameras dc;
+    if (!make_dev_cameras(cams, n_views, dc)) return GS_ERR_INVALID_ARGUMENT;
+    if (n == 0) return GS_OK;
+    const dim3 grid(grid_for((uint64_t)n, 256)), block(256);
+    hipStream_t s = (hipStream_t)stream;
+    const ShConsts K = sh_constants();
+    switch (sh_degree) {
+        case 0: hipLaunchKernelGGL(k_preprocess_bwd<0>, grid, block, 0, s, params, n, dc, K, rect, grad2d, grad_params); break;
+        case 1: hipLaunchKernelGGL(k_preprocess_bwd<1>, grid, block, 0, s, params, n, dc, K, rect, grad2d, grad_params); break;
+        case 2: hipLaunchKernelGGL(k_preprocess_bwd<2>, grid, block, 0, s, params, n, dc, K, rect, grad2d, grad_params); break;
+        default: hipLaunchKernelGGL(k_preprocess_bwd<3>, grid, block, 0, s, params, n, dc, K, rect, grad2d, grad_params); break;
+    }
+    return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,282 @@
+/*
+ * gs.h -- C ABI of the MI355X (gfx950) library for one training step of the
+ * tile-based differentiable Gaussian rasterizer.
+ *
+ * The step, in call order:
+ *   gs_preprocess          project Gaussians (EWA 2D covariance, SH colour),
+ *                          tile rectangles, prefix sum of tile counts
+ *   gs_emit_intersections  one (tile, depth) key per Gaussian-tile overlap
+ *   gs_sort_keys           LSD radix sort of the keys with their payloads
+ *   gs_tile_ranges         [start, end) of each tile in the sorted list
+ *   gs_rasterize_fwd       front-to-back alpha blending per 16x16 tile
+ *   gs_loss_l1             L1 loss against target images, dL/dimage
+ *   gs_rasterize_bwd       back-to-front gradients to the 2D quantities
+ *   gs_preprocess_bwd      gradients to all per-Gaussian parameters
+ *   gs_adam_step           fused Adam update
+ *
+ * What the pages fix, and where (the formulas themselves are readings of the
+ * 3DGS method, reference [10] of "A Scalable PyTorch Abstraction for Multi-GPU
+ * Gaussian Splatting"):
+ *   - per-tile sorted lists of Gaussian-to-pixel intersections: "AMD ROCm team
+ *     open-sources distributed 3D Gaussian Splatting training for multi-GPU
+ *     scaling", section "Distributed training architecture and memory scaling";
+ *   - 16x16 pixel blocks: "On Scaling Up 3D Gaussian Splatting Training",
+ *     answer (1) on pixel block size;
+ *   - 59 fp32 parameters (3 xyz, 3 scale, 4 rotation, 1 opacity, 48 SH): same
+ *     page, answer on the storage requirement;
+ *   - Adam with two moment vectors (708 bytes per Gaussian): the ROCm page,
+ *     same section; Adam is reference [12] of the fVDB page;
+ *   - forward and backward rasterization as separate passes whose off-chip
+ *     traffic dominates: "ByteSplat: Efficient Distributed 3D Gaussian
+ *     Splatting Training via Intra- and Inter-GPU communication reduction",
+ *     abstract;
+ *   - gradients averaged over a batch of views: "On Scaling Up 3D Gaussian
+ *     Splatting Training", answer on the Independent Gradients Hypothesis.
+ *
+ * Conventions for every entry point
+ *   Memory: every array argument is device memory owned by the caller (e.g. a
+ *     framework tensor's data pointer), unless marked "host". The library
+ *     allocates nothing and keeps no state between calls.
+ *   Streams: `stream` is a hipStream_t (NULL = the null stream). Each call
+ *     validates its arguments on the host and enqueues kernels on `stream`; it
+ *     never synchronises.
+ *   Errors: argument errors return GS_ERR_INVALID_ARGUMENT before any HIP call
+ *     (so they are testable without a GPU); a failed launch returns GS_ERR_HIP.
+ *     Device-side capacity overflow is reported through a device flag.
+ *   Parameter block: `params` is [P][n] fp32, structure of arrays, P = 11 +
+ *     3 (d+1)^2 for SH degree d (59 at d = 3):
+ *       rows 0-2 mean x y z, rows 3-5 log-scale, rows 6-9 quaternion w x y z,
+ *       row 10 opacity logit, row 11 + 3k + c SH coefficient k of channel c.
+ *     Gradients and the Adam moments use the same layout.
+ *   Views: all views of one call share one image size; at most GS_MAX_VIEWS.
+ *   Pixels: pixel (i, j) has its centre at (i + 0.5, j + 0.5); images are
+ *     [V][3][H][W] fp32, per-pixel maps [V][H][W].
+ */
+#ifndef GS_H
+#define GS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GS_ABI_VERSION 1
+#define GS_TILE 16
+#define GS_MAX_VIEWS 16
+#define GS_REC_FLOATS 12 /* floats per projected record */
+#define GS_GRAD2D_ROWS 9 /* 2D gradient rows per (view, Gaussian) */
+
+typedef enum gs_status {
+    GS_OK = 0,
+    GS_ERR_INVALID_ARGUMENT = 1,
+    GS_ERR_CAPACITY = 2,
+    GS_ERR_HIP = 3,
+    GS_ERR_UNSUPPORTED = 4
+} gs_status;
+
+/* Pinhole camera (host memory). World to camera: p_c = R p + t, R row-major;
+ * camera axes x right, y down, z forward. A Gaussian is culled unless
+ * near_plane < z_c < far_plane (far_plane may be +infinity). */
+typedef struct gs_camera {
+    int32_t width, height;
+    float fx, fy, cx, cy;
+    float R[9];
+    float t[3];
+    float near_plane, far_plane;
+} gs_camera;
+
+/* Projected record of (view v, Gaussian g), rec[(v * n + g) * 12 + field]:
+ *   0 u, 1 v          projected mean (pixels)
+ *   2 A, 3 B, 4 C     conic = inverse of the 2D covariance [[a, b], [b, c]]
+ *                     (EWA: J R Sigma3 R^T J^T plus 0.3 px^2 on the diagonal)
+ *   5 opacity         sigmoid of the logit
+ *   6 r, 7 g, 8 b     SH colour + 0.5, clamped at 0
+ *   9 ext_x, 10 ext_y half-extent of the region where alpha can reach 1/255
+ *                     (slightly enlarged; negative when it cannot anywhere)
+ *   11 depth          view-space z
+ * Written only for visible (view, Gaussian) pairs. */
+enum {
+    GS_REC_U = 0, GS_REC_V = 1, GS_REC_A = 2, GS_REC_B = 3, GS_REC_C = 4,
+    GS_REC_OPACITY = 5, GS_REC_R = 6, GS_REC_G = 7, GS_REC_BLUE = 8,
+    GS_REC_EXT_X = 9, GS_REC_EXT_Y = 10, GS_REC_DEPTH = 11
+};
+
+/* 2D gradient rows, grad2d[(v * 9 + row) * n + g]. */
+enum {
+    GS_G2_U = 0, GS_G2_V = 1, GS_G2_A = 2, GS_G2_B = 3, GS_G2_C = 4,
+    GS_G2_OPACITY = 5, GS_G2_R = 6, GS_G2_G = 7, GS_G2_BLUE = 8
+};
+
+int gs_abi_version(void);
+const char* gs_status_string(gs_status status);
+
+/* Rows of the parameter block at SH degree d (0..3), or -1. */
+int gs_param_rows(int32_t sh_degree);
+
+/* Tiles per row / column / image for one view. */
+int32_t gs_tiles_x(int32_t width);
+int32_t gs_tiles_y(int32_t height);
+
+/* Number of low key bits the sort must cover: 32 depth bits plus enough bits
+ * for every (view, tile) index. */
+int32_t gs_sort_end_bit(int32_t n_views, int64_t tiles_per_view);
+
+/* Workspace of gs_preprocess for n Gaussians and V views (bytes). */
+size_t gs_preprocess_workspace_bytes(int64_t n, int32_t n_views);
+
+/* Workspace of gs_sort_keys for n_keys keys (bytes). */
+size_t gs_sort_workspace_bytes(uint64_t n_keys);
+
+/*
+ * gs_preprocess -- the Gaussian-wise stage ("Gaussian-wise computations" of
+ * "On Scaling Up 3D Gaussian Splatting Training"; 3D-to-2D transformation).
+ * For every view v and Gaussian g: culling (near/far, det <= 0, empty tile
+ * rectangle), EWA 2D covariance and its conic, radius ceil(3 sqrt(lambda_max)),
+ * tile rectangle [x0, x1) x [y0, y1), SH colour; then an exclusive prefix sum
+ * of the per-(v, g) tile counts (the scan is decoupled look-back in
+ * reference [21] of the fVDB page; here a reduce-then-scan).
+ *   params   [P][n] fp32 (P from sh_degree), read only
+ *   cams     host array of n_views cameras, all of one image size
+ *   rec      out [n_views][n][12] fp32 (see GS_REC_*)
+ *   rect     out [n_views][n][4] uint16 x0 y0 x1 y1 (all 0 when culled)
+ *   offsets  out [n_views * n + 1] uint32: offsets[i] = sum of the tile counts
+ *            of entries before i (low 32 bits); the count of entry i is the
+ *            area of its rectangle
+ *   total    out device uint64: total intersection count K
+ *   ws       device workspace of gs_preprocess_workspace_bytes(n, n_views)
+ * n may be 0. Errors: n < 0, sh_degree outside 0..3, n_views outside
+ * 1..GS_MAX_VIEWS, views of different sizes, null pointers, small workspace,
+ * n_views * tiles_per_view >= 2^31.
+ */
+gs_status gs_preprocess(const float* params, int64_t n, int32_t sh_degree, const gs_camera* cams,
+                        int32_t n_views, float* rec, uint16_t* rect, uint32_t* offsets,
+                        uint64_t* total, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * gs_emit_intersections -- one key per (view, Gaussian, tile) overlap, the
+ * per-tile intersection lists of the ROCm page before sorting:
+ *   key = ((v * tiles_per_view + ty * tiles_x + tx) << 32) | bits(depth)
+ * (bits = IEEE pattern of the fp32 view-space depth, monotone for depth > 0),
+ * payload = g. Entry (v, g) writes its count keys at offsets[v * n + g] in
+ * row-major tile order.
+ *   rec, rect, offsets  from gs_preprocess
+ *   keys, vals          out, capacity entries each
+ *   overflow            device int32: 1 when an entry would fall at or past
+ *                       `capacity` (such entries are not written), else 0
+ * Errors: null pointers, n < 0, bad view count.
+ */
+gs_status gs_emit_intersections(const float* rec, const uint16_t* rect, const uint32_t* offsets,
+                                int64_t n, int32_t n_views, int32_t width, int32_t height,
+                                uint64_t* keys, uint32_t* vals, uint64_t capacity,
+                                int32_t* overflow, void* stream);
+
+/*
+ * gs_sort_keys -- stable LSD radix sort (8-bit digits) of n_keys 64-bit keys
+ * with uint32 payloads on bits [0, end_bit), the GPU radix sort of reference
+ * [22] of the fVDB page. Keys emitted in Gaussian order come out ordered by
+ * (key, Gaussian index): a total order, so the result is unique.
+ *   keys/vals           in: unsorted; ping buffer
+ *   keys_alt/vals_alt   pong buffer of the same size
+ *   end_bit             1..64 (gs_sort_end_bit gives the bits a step needs)
+ *   ws                  gs_sort_workspace_bytes(n_keys)
+ *   result_in_alt       host out: 1 when the sorted data is in the alt pair
+ * Errors: null pointers (when n_keys > 0), end_bit outside 1..64, small
+ * workspace, n_keys >= 2^32.
+ */
+gs_status gs_sort_keys(uint64_t* keys, uint32_t* vals, uint64_t* keys_alt, uint32_t* vals_alt,
+                       uint64_t n_keys, int32_t end_bit, void* ws, size_t ws_bytes,
+                       int32_t* result_in_alt, void* stream);
+
+/*
+ * gs_tile_ranges -- for every (view, tile) id t = key >> 32, the range
+ * [start, end) of its keys in the sorted list; (0, 0) when it has none.
+ *   keys      sorted keys
+ *   ranges    out [n_tiles_total][2] uint32 (every entry written)
+ * Errors: null pointers, n_keys >= 2^32.
+ */
+gs_status gs_tile_ranges(const uint64_t* keys, uint64_t n_keys, int64_t n_tiles_total,
+                         uint32_t* ranges, void* stream);
+
+/*
+ * gs_rasterize_fwd -- per pixel, front to back over its tile's sorted list
+ * (alpha compositing of the fVDB page; 16x16 tiles):
+ *   power = -(A dx^2 + 2 B dx dy + C dy^2) / 2, dx = u - px, dy = v - py;
+ *   skip if power > 0; alpha = min(0.99, o exp(power)); skip if alpha < 1/255;
+ *   T' = T (1 - alpha); if T' < 1e-4 stop without blending this entry;
+ *   otherwise C += rgb alpha T, T = T'.
+ *   image     out [V][3][H][W] = C + T_final * bg
+ *   T_final   out [V][H][W]
+ *   n_contrib out [V][H][W] int32: 1-based list position of the last blended
+ *             entry, 0 if none
+ *   bg        host float[3]
+ * Errors: null pointers, bad view count, views of different sizes.
+ */
+gs_status gs_rasterize_fwd(const float* rec, int64_t n, const uint32_t* ranges,
+                           const uint32_t* vals, const gs_camera* cams, int32_t n_views,
+                           const float* bg, float* image, float* T_final, int32_t* n_contrib,
+                           void* stream);
+
+/*
+ * gs_loss_l1 -- L = scale * sum |image - target| over `count` elements and
+ * dL/dimage = scale * sign(image - target) (sign(0) = 0). For views averaged
+ * over a batch ("On Scaling Up 3D Gaussian Splatting Training", answer on the
+ * Independent Gradients Hypothesis) pass scale = 1 / (3 H W V).
+ *   loss      device double: overwritten, or added to when `accumulate` is
+ *             non-zero
+ * Arrays must be 16-byte aligned.
+ * Errors: null pointers, count < 0, misaligned arrays.
+ */
+gs_status gs_loss_l1(const float* image, const float* target, int64_t count, float scale,
+                     float* dL_dimage, double* loss, int32_t accumulate, void* stream);
+
+/*
+ * gs_rasterize_bwd -- back to front over each pixel's blended entries
+ * (backward rasterization of the ByteSplat abstract), gradients to the 2D
+ * quantities of every (view, Gaussian):
+ *   grad2d  [V][9][n] fp32 (rows GS_G2_*): du dv dA dB dC dopacity dr dg db;
+ *           zeroed first unless `accumulate` is non-zero
+ * Inputs as in gs_rasterize_fwd plus its T_final and n_contrib and dL/dimage.
+ * Floating-point atomics make the summation order, and so the last bits, vary
+ * between runs. Errors: as gs_rasterize_fwd.
+ */
+gs_status gs_rasterize_bwd(const float* rec, int64_t n, const uint32_t* ranges,
+                           const uint32_t* vals, const gs_camera* cams, int32_t n_views,
+                           const float* bg, const float* T_final, const int32_t* n_contrib,
+                           const float* dL_dimage, float* grad2d, int32_t accumulate,
+                           void* stream);
+
+/*
+ * gs_preprocess_bwd -- chain rule from the 2D gradients to all P parameters
+ * of every Gaussian, summed over views: conic inverse, EWA covariance
+ * (including the depth dependence of the Jacobian), projected mean, 3D
+ * covariance from scale and rotation, quaternion normalisation, sigmoid,
+ * SH colour (coefficients and view direction). Zero where a Gaussian is culled
+ * in every view.
+ *   grad_params  out [P][n] fp32, overwritten
+ * Errors: as gs_preprocess.
+ */
+gs_status gs_preprocess_bwd(const float* params, int64_t n, int32_t sh_degree,
+                            const gs_camera* cams, int32_t n_views, const uint16_t* rect,
+                            const float* grad2d, float* grad_params, void* stream);
+
+/*
+ * gs_adam_step -- Adam (Kingma & Ba, reference [12] of the fVDB page),
+ * element-wise over `count` floats, in place:
+ *   m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2;
+ *   param -= lr (m / (1 - b1^step)) / (sqrt(v / (1 - b2^step)) + eps)
+ * step is 1-based; beta, 1 - beta, lr / (1 - b1^step) and 1 / sqrt(1 -
+ * b2^step) are formed in fp64 on the host and rounded once to fp32.
+ * Arrays must be 16-byte aligned.
+ * Errors: null pointers, count < 0, step < 1, beta outside [0, 1), eps < 0,
+ * misaligned arrays.
+ */
+gs_status gs_adam_step(float* params, const float* grad, float* m, float* v, int64_t count,
+                       double lr, double beta1, double beta2, double eps, int64_t step, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GS_H */
