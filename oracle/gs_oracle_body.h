@@ -332,14 +332,16 @@ static inline int FN(pair_eval)(const REAL* r, REAL px, REAL py, REAL Tcur, REAL
     const REAL alpha = R_FMIN((REAL)0.99f, oG);
     if (OR_IS_F32) {
         const double d = (double)oG;
-        if (fabs(d - 1.0 / 255.0) <= OR_ALPHA_BAND * (1.0 / 255.0)) *amb |= 1;
+        if (fabs(d - 1.0 / 255.0) <= OR_ALPHA_BAND * (1.0 / 255.0)) *amb |= 1 | 4;
         if (fabs(d - 0.99) <= OR_ALPHA_BAND * 0.99) *amb |= 2;
     }
     if (alpha < (REAL)(1.0f / 255.0f)) return 0;
     const REAL Tn = Tcur * (1.0f - alpha);
     if (OR_IS_F32) {
-        const double rel = *relerr + (double)alpha / (1.0 - (double)alpha) * OR_ALPHA_REL + 1.2e-7;
-        if (fabs((double)Tn - 1e-4) <= OR_T_SAFETY * rel * 1e-4) *amb |= 1;
+        /* a clamped alpha is the constant 0.99 on both sides: no exp() error */
+        const int clamped_safe = (double)oG > 0.99 * (1.0 + OR_ALPHA_BAND);
+        const double rel = *relerr + (clamped_safe ? 0.0 : (double)alpha / (1.0 - (double)alpha) * OR_ALPHA_REL);
+        if (fabs((double)Tn - 1e-4) <= OR_T_SAFETY * rel * 1e-4) *amb |= 1 | 8;
         if (!(Tn < (REAL)1e-4f)) *relerr = rel;
     }
     *alpha_out = alpha;
