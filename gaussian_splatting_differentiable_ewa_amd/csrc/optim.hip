@@ -86,11 +86,11 @@ __global__ __launch_bounds__(EW_THREADS) void k_adam(float* __restrict__ params,
 }
 
 // Enough blocks to fill the chip several times over; each thread then walks
-// its grid-stride range.
-static unsigned stream_blocks(int64_t count)
+// its grid-stride range. The loss uses fewer blocks: each block ends with one
+// fp64 atomic on the same address.
+static unsigned stream_blocks(int64_t count, int64_t cap = 256 * 32)
 {
     const int64_t need = (count / 4 + EW_THREADS - 1) / EW_THREADS;
-    const int64_t cap = 256 * 32;
     return (unsigned)(need < 1 ? 1 : (need > cap ? cap : need));
 }
 
@@ -111,7 +111,7 @@ gs_status gs_loss_l1(const float* image, const float* target, int64_t count, flo
     hipStream_t s = (hipStream_t)stream;
     if (!accumulate && fill_u32((uint32_t*)loss, 2, 0u, s) != hipSuccess) return GS_ERR_HIP;
     if (count == 0) return GS_OK;
-    hipLaunchKernelGGL(k_loss_l1, dim3(stream_blocks(count)), dim3(EW_THREADS), 0, s, image, target,
+    hipLaunchKernelGGL(k_loss_l1, dim3(stream_blocks(count, 256 * 4)), dim3(EW_THREADS), 0, s, image, target,
                        count, scale, dL_dimage, loss);
     return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
 }

@@ -31,19 +31,26 @@ __device__ __forceinline__ void alpha_extent(float o, float a, float c, float& e
     ey = sqrtf(tau * c) + 0.05f;
 }
 
-__global__ __launch_bounds__(PRE_THREADS) void k_preprocess(const float* __restrict__ P, int64_t n, int deg,
+// One thread per Gaussian: its parameters are loaded once (all rows issued
+// together), then every view is pure arithmetic plus the record stores.
+template <int DEG>
+__global__ __launch_bounds__(PRE_THREADS) void k_preprocess(const float* __restrict__ P, int64_t n,
                                                             const DevCameras cams, const ShConsts K,
                                                             float* __restrict__ rec, uint16_t* __restrict__ rect,
                                                             uint32_t* __restrict__ counts)
 {
+    constexpr int NB = (DEG + 1) * (DEG + 1);
     const int64_t g = (int64_t)blockIdx.x * PRE_THREADS + threadIdx.x;
     if (g >= n) return;
-    const float x = P[0 * n + g], y = P[1 * n + g], z = P[2 * n + g];
+    float raw[11];
+#pragma unroll
+    for (int r = 0; r < 11; ++r) raw[r] = P[(int64_t)r * n + g];
+    float sh[3 * NB];
+#pragma unroll
+    for (int k = 0; k < 3 * NB; ++k) sh[k] = P[(int64_t)(11 + k) * n + g];
+    const float x = raw[0], y = raw[1], z = raw[2];
     GaussLocal L;
-    gauss_local(P[3 * n + g], P[4 * n + g], P[5 * n + g], P[6 * n + g], P[7 * n + g], P[8 * n + g],
-                P[9 * n + g], P[10 * n + g], L);
-    const int nb = (deg + 1) * (deg + 1);
-    const float* sh = P + 11 * n;
+    gauss_local(raw[3], raw[4], raw[5], raw[6], raw[7], raw[8], raw[9], raw[10], L);
     for (int v = 0; v < cams.n_views; ++v) {
         const DevCamera& cam = cams.c[v];
         ViewProj p;
@@ -57,11 +64,11 @@ __global__ __launch_bounds__(PRE_THREADS) void k_preprocess(const float* __restr
         float d[3], dist;
         view_dir(x, y, z, cam, d, dist);
         float Y[16];
-        sh_eval_basis(K, deg, d, Y);
+        sh_eval_basis(K, DEG, d, Y);
         bool cl;
-        const float r = sh_channel(sh, n, g, nb, 0, Y, cl);
-        const float gg = sh_channel(sh, n, g, nb, 1, Y, cl);
-        const float b = sh_channel(sh, n, g, nb, 2, Y, cl);
+        const float r = sh_channel_reg<NB>(sh, 0, Y, cl);
+        const float gg = sh_channel_reg<NB>(sh, 1, Y, cl);
+        const float b = sh_channel_reg<NB>(sh, 2, Y, cl);
         float ex, ey;
         alpha_extent(L.o, p.a, p.c, ex, ey);
         float4* out = (float4*)(rec + idx * GS_REC_FLOATS);
@@ -134,8 +141,14 @@ gs_status gs_preprocess(const float* params, int64_t n, int32_t sh_degree, const
     if (ws_bytes < scan_workspace_bytes(entries)) return GS_ERR_INVALID_ARGUMENT;
     hipStream_t s = (hipStream_t)stream;
     if (n > 0) {
-        hipLaunchKernelGGL(k_preprocess, dim3(grid_for((uint64_t)n, PRE_THREADS)), dim3(PRE_THREADS), 0, s,
-                           params, n, sh_degree, dc, sh_constants(), rec, rect, offsets);
+        const dim3 grid(grid_for((uint64_t)n, PRE_THREADS)), block(PRE_THREADS);
+        const ShConsts K = sh_constants();
+        switch (sh_degree) {
+            case 0: hipLaunchKernelGGL(k_preprocess<0>, grid, block, 0, s, params, n, dc, K, rec, rect, offsets); break;
+            case 1: hipLaunchKernelGGL(k_preprocess<1>, grid, block, 0, s, params, n, dc, K, rec, rect, offsets); break;
+            case 2: hipLaunchKernelGGL(k_preprocess<2>, grid, block, 0, s, params, n, dc, K, rec, rect, offsets); break;
+            default: hipLaunchKernelGGL(k_preprocess<3>, grid, block, 0, s, params, n, dc, K, rec, rect, offsets); break;
+        }
         if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     }
     // counts were written into `offsets`; scan them in place

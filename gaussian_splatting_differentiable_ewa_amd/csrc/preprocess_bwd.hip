@@ -26,7 +26,9 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(const float* __restrict_
     GaussLocal L;
     gauss_local(P[3 * n + g], P[4 * n + g], P[5 * n + g], P[6 * n + g], P[7 * n + g], P[8 * n + g],
                 P[9 * n + g], P[10 * n + g], L);
-    const float* sh = P + 11 * n;
+    float sh[3 * NB];  // coefficients, loaded once for all views
+#pragma unroll
+    for (int k = 0; k < 3 * NB; ++k) sh[k] = P[(int64_t)(11 + k) * n + g];
 
     float gpx = 0.f, gpy = 0.f, gpz = 0.f, gop = 0.f;
     float gM[9];
@@ -45,10 +47,10 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(const float* __restrict_
         const DevCamera& cam = cams.c[v];
         ViewProj p;
         view_project(x, y, z, L, cam, cams.tiles_x, cams.tiles_y, p);
-        const float* g2 = grad2d + (int64_t)v * GS_GRAD2D_ROWS * n + g;
-        const float gu = g2[0], gv = g2[n], gA = g2[2 * n], gB = g2[3 * n], gC = g2[4 * n];
-        const float go = g2[5 * n];
-        const float grgb[3] = {g2[6 * n], g2[7 * n], g2[8 * n]};
+        const float* g2 = grad2d + idx * GS_GRAD2D_ROWS;  // one 36-byte record
+        const float gu = g2[0], gv = g2[1], gA = g2[2], gB = g2[3], gC = g2[4];
+        const float go = g2[5];
+        const float grgb[3] = {g2[6], g2[7], g2[8]};
         gop += go;
 
         // conic Q = Sigma2^-1: dL/dSigma2 = -Q G Q, G = [[gA, gB/2], [gB/2, gC]]
@@ -125,14 +127,13 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(const float* __restrict_
 #pragma unroll
         for (int ch = 0; ch < 3; ++ch) {
             bool clamped;
-            (void)sh_channel(sh, n, g, NB, ch, Yb, clamped);
+            (void)sh_channel_reg<NB>(sh, ch, Yb, clamped);
             gcol[ch] = clamped ? 0.f : grgb[ch];
         }
         float e[NB];
 #pragma unroll
         for (int k = 0; k < NB; ++k) {
-            const float c0 = sh[(int64_t)(3 * k) * n + g], c1 = sh[(int64_t)(3 * k + 1) * n + g],
-                        c2 = sh[(int64_t)(3 * k + 2) * n + g];
+            const float c0 = sh[3 * k], c1 = sh[3 * k + 1], c2 = sh[3 * k + 2];
             e[k] = gcol[0] * c0 + gcol[1] * c1 + gcol[2] * c2;
             gsh[3 * k] += Yb[k] * gcol[0];
             gsh[3 * k + 1] += Yb[k] * gcol[1];

@@ -185,6 +185,19 @@ __device__ __forceinline__ void sh_eval_basis(const ShConsts& K, int deg, const 
     Y[15] = -(K.c3a * (x * (xx - 3.f * yy)));
 }
 
+// The same sum with the coefficients already in registers (sh[3k + c]).
+template <int NB>
+__device__ __forceinline__ float sh_channel_reg(const float* sh, int ch, const float Y[16], bool& clamped)
+{
+#pragma clang fp contract(off)
+    float acc = Y[0] * sh[ch];
+#pragma unroll
+    for (int k = 1; k < NB; ++k) acc = acc + Y[k] * sh[3 * k + ch];
+    acc = acc + 0.5f;
+    clamped = acc < 0.f;
+    return clamped ? 0.f : acc;
+}
+
 // Colour of channel c: sum_k Y_k sh[k][c] in index order, + 0.5, clamped at
 // zero. `sh` points at row 11 of the parameter block, stride n.
 __device__ __forceinline__ float sh_channel(const float* __restrict__ sh, int64_t n, int64_t g,

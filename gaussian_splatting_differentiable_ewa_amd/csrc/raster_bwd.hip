@@ -1,0 +1,263 @@
+// gs_rasterize_bwd: back-to-front gradients of the alpha compositing to the
+// 2D quantities of every (view, Gaussian) (backward rasterization of the
+// ByteSplat abstract), on the work decomposition of raster_fwd.hip: one
+// wavefront per 8x8 quarter of a tile, each 16-lane DPP row owning a 4x4
+// sub-block with its own list of entries.
+//
+// For I = sum_i c_i a_i T_i + T_final bg over the blended entries of a pixel
+// (T_i = prod_{j<i} (1 - a_j), a = min(0.99, o G), G = exp(power)):
+//   dI/dc_i = a_i T_i
+//   dI/da_i = T_i (c_i - S_i), S_i the colour behind entry i normalised by
+//             T_{i+1}: S <- a_i c_i + (1 - a_i) S walking back from S = bg
+//   da/do = G and da/dpower = o G unless the 0.99 clamp is active
+//   dpower/du = -(A dx + B dy), dpower/dv = -(B dx + C dy),
+//   dpower/dA = -dx^2/2, dpower/dB = -dx dy, dpower/dC = -dy^2/2.
+//
+// Each row works through its entries in sub-batches of 8, in two phases:
+//   1. pixel-parallel, entries in reverse order: every lane rebuilds
+//      T_i = T_{i+1} / (1 - a_i) and S for its pixel and writes two numbers
+//      per (pixel, entry) to LDS: (dL/da_i) G_i (zero when clamped or not
+//      blended) and a_i T_i;
+//   2. entry-parallel: lane pairs own one entry each and sum the nine
+//      gradient terms over the sub-block's 16 pixels from those two numbers
+//      (moments of dx, dy, scaled by o at the end); one DPP step joins the
+//      pair and the pair's first lane stores the nine sums in its row's
+//      slice of an LDS table (rows never share a slice: no LDS atomics).
+// No cross-lane reduction runs per (pixel, entry). After each batch of 64
+// entries each lane sums its entry over the rows that held it, and every
+// (entry, quarter) with a contribution issues its global fp32 atomics.
+#include "raster_common.h"
+
+namespace gs {
+
+constexpr int SUB = 8;            // entries per row per sub-batch
+constexpr int CSTRIDE = SUB + 1;  // padded slot stride of the coefficient table
+
+__global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restrict__ rec, int64_t n,
+                                                           const uint32_t* __restrict__ ranges,
+                                                           const uint32_t* __restrict__ vals, int W, int H, int TX,
+                                                           int T, float bg0, float bg1, float bg2,
+                                                           const float* __restrict__ T_final,
+                                                           const int32_t* __restrict__ n_contrib,
+                                                           const float* __restrict__ dL_dimage,
+                                                           float* __restrict__ grad2d)
+{
+#pragma clang fp contract(off)
+    __shared__ float4 s_rec[3 * RW_BATCH];
+    __shared__ uint8_t s_mask[RW_BATCH];
+    __shared__ uint16_t s_list[4 * RW_BATCH];
+    __shared__ float s_part[4][GS_GRAD2D_ROWS][RW_BATCH];  // [row][gradient][slot] sums of each row
+    __shared__ float2 s_coef[4][16][CSTRIDE];  // [row][pixel][slot]
+    __shared__ float4 s_g[RW_THREADS];         // dL/dimage of each lane's pixel
+    __shared__ uint32_t s_gid[RW_BATCH];       // Gaussian of each staged slot
+    __shared__ uint8_t s_rows[RW_BATCH];       // rows whose list held each slot
+    __shared__ uint8_t s_live[RW_BATCH];       // slots with a contribution, compacted
+    const QuarterCtx t = quarter_ctx(W, H, TX, T);
+    if (t.empty) return;
+    const int64_t HW = (int64_t)H * W;
+    const int64_t pix = (int64_t)t.j * W + t.i;
+    int32_t my_last = 0;
+    float Tr = 1.f, g0 = 0.f, g1 = 0.f, g2 = 0.f;
+    if (t.inside) {
+        my_last = n_contrib[(int64_t)t.view * HW + pix];
+        Tr = T_final[(int64_t)t.view * HW + pix];
+        const float* gimg = dL_dimage + (int64_t)t.view * 3 * HW + pix;
+        g0 = gimg[0];
+        g1 = gimg[HW];
+        g2 = gimg[2 * HW];
+    }
+    if (g0 == 0.f && g1 == 0.f && g2 == 0.f) my_last = 0;  // this pixel adds nothing
+    const uint2 rg = *(const uint2*)(ranges + 2 * (uint64_t)t.tile_lin);
+    // never walk past the tile's list, whatever n_contrib holds
+    const int32_t row_last = min(row_max16(my_last), (int32_t)(rg.y - rg.x));
+    const int32_t rl0 = __builtin_amdgcn_readlane(row_last, 0), rl1 = __builtin_amdgcn_readlane(row_last, 16);
+    const int32_t rl2 = __builtin_amdgcn_readlane(row_last, 32), rl3 = __builtin_amdgcn_readlane(row_last, 48);
+    const int32_t wave_last = max(max(rl0, rl1), max(rl2, rl3));
+    if (wave_last <= 0) return;
+    const int q = t.lane & 15;
+    s_g[t.lane] = make_float4(g0, g1, g2, 0.f);
+    const float* rv = rec + (int64_t)t.view * n * GS_REC_FLOATS;
+    float* g2d = grad2d + (int64_t)t.view * n * GS_GRAD2D_ROWS;  // [n][9] records of this view
+    // origin of this row's 4x4 sub-block (pixel centres)
+    const float sbx = (float)(t.qx0 + (t.row & 1) * 4) + 0.5f;
+    const float sby = (float)(t.qy0 + (t.row >> 1) * 4) + 0.5f;
+    float2(*coef)[CSTRIDE] = s_coef[t.row];
+    const float4* grow = &s_g[t.row * 16];
+    // colour behind the current entry, normalised by the transmittance in
+    // front of it; starts as the background behind the last blended entry
+    float acc0 = bg0, acc1 = bg1, acc2 = bg2;
+    // lane s of a batch holds list position hi - s (1-based): slots run back
+    // to front. Two-stage prefetch as in the forward pass.
+    Entry cur, nxt;
+    {
+        const int32_t p0 = wave_last - t.lane, p1 = wave_last - RW_BATCH - t.lane;
+        cur.valid = p0 >= 1;
+        cur.gid = cur.valid ? vals[rg.x + (uint32_t)(p0 - 1)] : 0u;
+        gather_record(cur, rv);
+        nxt.valid = p1 >= 1;
+        nxt.gid = nxt.valid ? vals[rg.x + (uint32_t)(p1 - 1)] : 0u;
+    }
+    for (int32_t hi = wave_last; hi >= 1; hi -= RW_BATCH) {
+        stage_entry(cur, t.lane, t, W, H, s_rec, s_mask);
+        gather_record(nxt, rv);
+        const int32_t p2 = hi - 2 * RW_BATCH - t.lane;
+        const bool v2 = p2 >= 1;
+        const uint32_t gid2 = v2 ? vals[rg.x + (uint32_t)(p2 - 1)] : 0u;
+        uint32_t cnt[4];
+        rows_compact(s_mask, s_list, t.lane, cnt, [&](int s, int r) {
+            const int32_t rl = r == 0 ? rl0 : r == 1 ? rl1 : r == 2 ? rl2 : rl3;
+            return hi - s <= rl;
+        });
+        const uint32_t my_cnt = t.row == 0 ? cnt[0] : t.row == 1 ? cnt[1] : t.row == 2 ? cnt[2] : cnt[3];
+        const uint32_t iters = max(max(cnt[0], cnt[1]), max(cnt[2], cnt[3]));
+        const uint16_t* my_list = s_list + t.row * RW_BATCH;
+        for (uint32_t sb = 0; sb < iters; sb += SUB) {
+            // ---- phase 1: this lane's pixel, entries sb .. sb+7 of its row
+            const uint32_t n_sub = min((uint32_t)SUB, iters - sb);
+            for (uint32_t i = 0; i < n_sub; ++i) {
+                const uint32_t it = sb + i;
+                const bool has = it < my_cnt;
+                const int idx = has ? (int)my_list[it] : 0;
+                const int32_t pos = hi - idx;
+                const float4 q0 = s_rec[3 * idx], q1 = s_rec[3 * idx + 1], q2 = s_rec[3 * idx + 2];
+                float dx, dy;
+                const float power = entry_power(q0, q1, t.px, t.py, dx, dy);
+                const float G = exp_fast(power);
+                const float oG = q1.y * G;
+                const float alpha = fminf(ALPHA_MAX, oG);
+                // the forward's decision for this pixel
+                const bool contrib = has && pos <= my_last && !(power > 0.f) && !(alpha < ALPHA_MIN);
+                // transmittance in front of this entry (a reciprocal: the
+                // gradients need no correctly rounded division)
+                Tr = contrib ? Tr * __builtin_amdgcn_rcpf(1.f - alpha) : Tr;
+                const float wk = contrib ? alpha * Tr : 0.f;
+                const float dLda = Tr * (((q1.z - acc0) * g0 + (q1.w - acc1) * g1) + (q2.x - acc2) * g2);
+                const float ak = contrib ? alpha : 0.f;  // colour behind: unchanged when 0
+                acc0 = ak * q1.z + (1.f - ak) * acc0;
+                acc1 = ak * q1.w + (1.f - ak) * acc1;
+                acc2 = ak * q2.x + (1.f - ak) * acc2;
+                const float dG = (contrib && !(oG > ALPHA_MAX)) ? dLda * G : 0.f;
+                coef[q][i] = make_float2(dG, wk);
+            }
+            asm volatile("" ::: "memory");  // phase-1 writes precede phase-2 reads (in order per wave)
+            // ---- phase 2: lanes (e, h) = (q & 7, q >> 3): entry slot e, pixels h*8 .. h*8+7
+            const uint32_t e = (uint32_t)q & 7u, h = (uint32_t)q >> 3;
+            const bool has_e = sb + e < my_cnt;
+            const int idx = has_e ? (int)my_list[sb + e] : 0;
+            const float4 q0 = s_rec[3 * idx], q1 = s_rec[3 * idx + 1];
+            float go = 0.f, mx = 0.f, my = 0.f, mxx = 0.f, mxy = 0.f, myy = 0.f, gr = 0.f, gg = 0.f, gb = 0.f;
+            if (e < n_sub) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int pp = (int)h * 8 + k;  // pixel of the sub-block: (pp & 3, pp >> 2)
+                    const float2 c = coef[pp][e];
+                    const float4 gp = grow[pp];
+                    const float dx = q0.x - (sbx + (float)(pp & 3));
+                    const float dy = q0.y - (sby + (float)(pp >> 2));
+                    const float cdx = c.x * dx, cdy = c.x * dy;
+                    go += c.x;
+                    mx += cdx;
+                    my += cdy;
+                    mxx = __builtin_fmaf(cdx, dx, mxx);
+                    mxy = __builtin_fmaf(cdx, dy, mxy);
+                    myy = __builtin_fmaf(cdy, dy, myy);
+                    gr = __builtin_fmaf(c.y, gp.x, gr);
+                    gg = __builtin_fmaf(c.y, gp.y, gg);
+                    gb = __builtin_fmaf(c.y, gp.z, gb);
+                }
+            }
+            asm volatile("" ::: "memory");  // phase-2 reads precede the next phase-1 writes
+            // join the two pixel halves of each entry (lanes q and q + 8): row_ror:8
+#define GS_ROR8(v) (v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false)))
+            go = GS_ROR8(go);
+            mx = GS_ROR8(mx);
+            my = GS_ROR8(my);
+            mxx = GS_ROR8(mxx);
+            mxy = GS_ROR8(mxy);
+            myy = GS_ROR8(myy);
+            gr = GS_ROR8(gr);
+            gg = GS_ROR8(gg);
+            gb = GS_ROR8(gb);
+#undef GS_ROR8
+            if (h == 0 && has_e) {
+                // dL/dpower = (dL/da) o G: the o factor is applied here. Each
+                // row owns its slice, so these are plain stores.
+                const float o = q1.y, nA = q0.z, nB = q0.w, nC = q1.x;
+                const float Mx = o * mx, My = o * my;
+                float* part = &s_part[t.row][0][idx];
+                part[0 * RW_BATCH] = 2.f * nA * Mx + nB * My;  // u
+                part[1 * RW_BATCH] = nB * Mx + 2.f * nC * My;  // v
+                part[2 * RW_BATCH] = -0.5f * o * mxx;          // A
+                part[3 * RW_BATCH] = -o * mxy;                 // B
+                part[4 * RW_BATCH] = -0.5f * o * myy;          // C
+                part[5 * RW_BATCH] = go;                       // opacity
+                part[6 * RW_BATCH] = gr;
+                part[7 * RW_BATCH] = gg;
+                part[8 * RW_BATCH] = gb;
+            }
+        }
+        asm volatile("" ::: "memory");  // row sums precede the flush reads
+        // The wave's sum of each staged entry (over the rows whose list held
+        // it: the same test as their compaction) goes to global memory. Nine
+        // lanes serve one entry, so each atomic instruction touches one
+        // 36-byte record per entry instead of nine scattered words.
+        {
+            const uint32_t m4 = s_mask[t.lane];
+            const int32_t pos = hi - t.lane;
+            const uint32_t rows = ((m4 & 1u) && pos <= rl0 ? 1u : 0u) | (((m4 >> 1) & 1u) && pos <= rl1 ? 2u : 0u) |
+                                  (((m4 >> 2) & 1u) && pos <= rl2 ? 4u : 0u) | (((m4 >> 3) & 1u) && pos <= rl3 ? 8u : 0u);
+            const bool live = cur.valid && rows != 0u;
+            const uint64_t lm = ballot(live);
+            s_rows[t.lane] = (uint8_t)rows;
+            s_gid[t.lane] = cur.gid;
+            if (live) s_live[mask_rank(lm)] = (uint8_t)t.lane;
+            asm volatile("" ::: "memory");
+            const uint32_t nlive = (uint32_t)__popcll(lm);
+            const uint32_t ke = (uint32_t)t.lane / 9u, kk = (uint32_t)t.lane - 9u * ke;
+            for (uint32_t c = 0; c < nlive; c += 7) {
+                const uint32_t ei = c + ke;
+                if (t.lane < 63 && ei < nlive) {
+                    const int s = s_live[ei];
+                    const uint32_t rs = s_rows[s];
+                    float a = 0.f;
+                    if (rs & 1u) a += s_part[0][kk][s];
+                    if (rs & 2u) a += s_part[1][kk][s];
+                    if (rs & 4u) a += s_part[2][kk][s];
+                    if (rs & 8u) a += s_part[3][kk][s];
+                    if (a != 0.f) atomicAdd(g2d + (int64_t)s_gid[s] * GS_GRAD2D_ROWS + kk, a);
+                }
+            }
+        }
+        asm volatile("" ::: "memory");
+        cur = nxt;
+        nxt.valid = v2;
+        nxt.gid = gid2;
+    }
+}
+
+}  // namespace gs
+
+using namespace gs;
+
+extern "C" {
+
+gs_status gs_rasterize_bwd(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
+                           const gs_camera* cams, int32_t n_views, const float* bg, const float* T_final,
+                           const int32_t* n_contrib, const float* dL_dimage, float* grad2d, int32_t accumulate,
+                           void* stream)
+{
+    RasterArgs a;
+    if (!raster_args(rec, n, ranges, vals, cams, n_views, bg, a)) return GS_ERR_INVALID_ARGUMENT;
+    if (!T_final || !n_contrib || !dL_dimage || (n > 0 && !grad2d)) return GS_ERR_INVALID_ARGUMENT;
+    hipStream_t s = (hipStream_t)stream;
+    if (!accumulate && n > 0) {
+        if (fill_u32((uint32_t*)grad2d, (uint64_t)n_views * GS_GRAD2D_ROWS * (uint64_t)n, 0u, s) != hipSuccess)
+            return GS_ERR_HIP;
+    }
+    hipLaunchKernelGGL(k_raster_bwd, dim3((unsigned)a.n_blocks), dim3(RW_THREADS), 0, s, rec, n, ranges, vals,
+                       a.dc.width, a.dc.height, a.dc.tiles_x, a.dc.tiles_per_view, bg[0], bg[1], bg[2], T_final,
+                       n_contrib, dL_dimage, grad2d);
+    return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,161 @@
+// Shared pieces of the forward and backward raster kernels: the work unit
+// (one wavefront per 8x8 quarter of a 16x16 tile), staging of list entries,
+// per-row compaction and the fixed-order per-pair arithmetic. The design is
+// described in raster_fwd.hip.
+#pragma once
+
+#include "internal.h"
+
+namespace gs {
+
+constexpr int RW_THREADS = 64;  // one wavefront: an 8x8 quarter of a tile
+constexpr int RW_BATCH = 64;    // list entries staged per round, one per lane
+constexpr float ALPHA_MIN = 1.0f / 255.0f;
+constexpr float ALPHA_MAX = 0.99f;
+constexpr float T_MIN = 1e-4f;
+constexpr float LOG2E = 1.44269504088896340736f;
+
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
+
+// Blocks are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8).
+// Renumber so that each XCD receives runs of 16 consecutive logical blocks
+// (four neighbouring tiles, whose quarters share list entries and records in
+// that XCD's L2) while the runs alternate between XCDs (dense and sparse image
+// regions spread over all of them).
+__device__ __forceinline__ uint32_t xcd_chunked(uint32_t bid, uint32_t nblocks)
+{
+    constexpr uint32_t CH = 16u;
+    const uint32_t full = nblocks / (8u * CH) * (8u * CH);
+    if (bid >= full) return bid;
+    const uint32_t x = bid & 7u, idx = bid >> 3;
+    return (x + 8u * (idx / CH)) * CH + idx % CH;
+}
+
+struct QuarterCtx {
+    uint32_t view, tile_lin;  // tile_lin = view * tiles_per_view + tile
+    int qx0, qy0;             // quarter origin (pixels)
+    int lane, row;            // row = 16-lane DPP row = 4x4 sub-block (row & 1, row >> 1)
+    int i, j;                 // this lane's pixel: (lane & 3, (lane >> 2) & 3) within the sub-block
+    bool inside;
+    bool empty;               // the quarter lies outside the image
+    float px, py;
+};
+
+__device__ __forceinline__ QuarterCtx quarter_ctx(int W, int H, int TX, int T)
+{
+    QuarterCtx t;
+    const uint32_t lb = xcd_chunked(blockIdx.x, gridDim.x);
+    const uint32_t quad = lb & 3u;
+    t.tile_lin = lb >> 2;
+    t.view = t.tile_lin / (uint32_t)T;
+    const uint32_t tile = t.tile_lin - t.view * (uint32_t)T;
+    const uint32_t ty = tile / (uint32_t)TX, tx = tile - ty * (uint32_t)TX;
+    t.qx0 = (int)tx * 16 + (int)(quad & 1u) * 8;
+    t.qy0 = (int)ty * 16 + (int)(quad >> 1) * 8;
+    t.lane = (int)threadIdx.x;
+    t.row = t.lane >> 4;
+    const int q = t.lane & 15;
+    t.i = t.qx0 + (t.row & 1) * 4 + (q & 3);
+    t.j = t.qy0 + (t.row >> 1) * 4 + (q >> 2);
+    t.inside = t.i < W && t.j < H;
+    t.empty = t.qx0 >= W || t.qy0 >= H;
+    t.px = (float)t.i + 0.5f;
+    t.py = (float)t.j + 0.5f;
+    return t;
+}
+
+// One list entry on its way from global memory to LDS.
+struct Entry {
+    float4 a, b, c;  // record: (u v A B) (C o r g) (b ex ey z)
+    uint32_t gid;
+    bool valid;
+};
+
+__device__ __forceinline__ void gather_record(Entry& E, const float* __restrict__ rv)
+{
+    if (E.valid) {
+        const float4* rp = (const float4*)(rv + (int64_t)E.gid * GS_REC_FLOATS);
+        E.a = rp[0];
+        E.b = rp[1];
+        E.c = rp[2];
+    }
+}
+
+// Stage the lane's entry at slot `s`: (u, v, -A/2, -B) (-C/2, o, r, g)
+// (b, -, -, -), and the 4-bit mask of the quarter's 4x4 sub-blocks (clipped
+// to the image) whose pixel centres the entry's alpha >= 1/255 region
+// touches; an invalid entry gets mask 0.
+__device__ __forceinline__ void stage_entry(const Entry& E, int s, const QuarterCtx& t, int W, int H,
+                                            float4* __restrict__ s_rec, uint8_t* __restrict__ s_mask)
+{
+    uint32_t mask = 0;
+    if (E.valid) {
+        const float lo_x = E.a.x - E.c.y, hi_x = E.a.x + E.c.y, lo_y = E.a.y - E.c.z, hi_y = E.a.y + E.c.z;
+        uint32_t xm = 0, ym = 0;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const float x0 = (float)(t.qx0 + 4 * k) + 0.5f, x1 = (float)min(t.qx0 + 4 * k + 4, W) - 0.5f;
+            const float y0 = (float)(t.qy0 + 4 * k) + 0.5f, y1 = (float)min(t.qy0 + 4 * k + 4, H) - 0.5f;
+            xm |= (uint32_t)(hi_x >= x0 && lo_x <= x1) << k;
+            ym |= (uint32_t)(hi_y >= y0 && lo_y <= y1) << k;
+        }
+        mask = (xm & ym & 1u) | (((xm >> 1) & ym & 1u) << 1) | ((xm & (ym >> 1) & 1u) << 2) |
+               (((xm >> 1) & (ym >> 1) & 1u) << 3);
+    }
+    s_rec[3 * s + 0] = make_float4(E.a.x, E.a.y, -0.5f * E.a.z, -E.a.w);
+    s_rec[3 * s + 1] = make_float4(-0.5f * E.b.x, E.b.y, E.b.z, E.b.w);
+    s_rec[3 * s + 2] = make_float4(E.c.x, 0.f, 0.f, 0.f);
+    s_mask[s] = (uint8_t)mask;
+}
+
+// Per-row compaction of the 64 staged entries: for row r, the slots
+// (ascending) whose bit r is set and for which `extra(slot, r)` holds.
+// lists[r * 64 + k]; counts in cnt[4] (wave-uniform).
+template <typename Pred>
+__device__ __forceinline__ void rows_compact(const uint8_t* __restrict__ s_mask, uint16_t* __restrict__ lists,
+                                             int lane, uint32_t cnt[4], Pred extra)
+{
+    asm volatile("" ::: "memory");  // staging writes precede these reads (LDS is in order per wave)
+    const uint32_t m4 = s_mask[lane];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const bool keep = ((m4 >> r) & 1u) && extra(lane, r);
+        const uint64_t m = ballot(keep);
+        if (keep) lists[r * RW_BATCH + mask_rank(m)] = (uint16_t)lane;
+        cnt[r] = (uint32_t)__popcll(m);
+    }
+    asm volatile("" ::: "memory");  // list writes precede their reads
+}
+
+__device__ __forceinline__ float entry_power(const float4& q0, const float4& q1, float px, float py, float& dx,
+                                             float& dy)
+{
+#pragma clang fp contract(off)
+    dx = q0.x - px;
+    dy = q0.y - py;
+    return __builtin_fmaf(dx, __builtin_fmaf(q0.z, dx, q0.w * dy), (q1.x * dy) * dy);
+}
+
+__device__ __forceinline__ int row_max16(int x)
+{
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) x = max(x, __shfl_xor(x, off));
+    return x;
+}
+
+struct RasterArgs {
+    DevCameras dc;
+    int64_t n_blocks;
+};
+
+static inline bool raster_args(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
+                               const gs_camera* cams, int32_t n_views, const float* bg, RasterArgs& a)
+{
+    if (n < 0 || !ranges || !bg) return false;
+    if (n > 0 && (!rec || !vals)) return false;
+    if (!make_dev_cameras(cams, n_views, a.dc)) return false;
+    a.n_blocks = (int64_t)n_views * a.dc.tiles_per_view * 4;
+    return a.n_blocks < ((int64_t)1 << 31);
+}
+
+}  // namespace gs

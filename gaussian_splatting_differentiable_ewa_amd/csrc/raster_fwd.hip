@@ -1,0 +1,133 @@
+// gs_rasterize_fwd: per-tile alpha compositing over the sorted intersection
+// lists (forward rasterization of the ByteSplat abstract; 16x16 pixel blocks
+// of "On Scaling Up 3D Gaussian Splatting Training", answer (1); depth-sorted
+// per-tile lists of the ROCm page, section "Distributed training architecture
+// and memory scaling").
+//
+// Work decomposition (gfx950, wave64):
+//   * one 64-lane workgroup per 8x8 quarter of a 16x16 tile, one lane per
+//     pixel; the four quarters of a tile are independent wavefronts, so each
+//     stops as soon as its own pixels are saturated and nothing waits at a
+//     barrier;
+//   * each 16-lane DPP row owns a 4x4 sub-block of the quarter and walks its
+//     own list of entries;
+//   * the tile's sorted list is read in batches of 64: each lane gathers one
+//     entry's 48-byte record (the next batch's gathers are in flight while the
+//     current batch is evaluated), computes the 4-bit mask of sub-blocks that
+//     the region where the entry's alpha can reach 1/255 touches, and stages
+//     it in LDS; each row compacts the entries of its bit (ballot + mbcnt,
+//     list order kept);
+//   * in the pixel loop every row reads its own next entry (an LDS broadcast
+//     within the row), so one instruction stream advances four sub-blocks on
+//     four different entries. An entry skipped by the mask has alpha < 1/255
+//     at every pixel of the sub-block and would have been skipped anyway:
+//     results are unchanged.
+//
+// Per (pixel, entry), in this fixed fp32 order:
+//   dx = u - px, dy = v - py
+//   power = fma(dx, fma(-A/2, dx, -B*dy), (-C/2*dy)*dy)
+//   skip if power > 0; alpha = min(0.99, o * exp(power)); skip if alpha < 1/255
+//   T' = T (1 - alpha); stop before this entry if T' < 1e-4
+//   w = alpha T; C_c = fma(rgb_c, w, C_c); T = T'
+#include "raster_common.h"
+
+namespace gs {
+
+__global__ __launch_bounds__(RW_THREADS) void k_raster_fwd(const float* __restrict__ rec, int64_t n,
+                                                           const uint32_t* __restrict__ ranges,
+                                                           const uint32_t* __restrict__ vals, int W, int H, int TX,
+                                                           int T, float bg0, float bg1, float bg2,
+                                                           float* __restrict__ image, float* __restrict__ T_final,
+                                                           int32_t* __restrict__ n_contrib)
+{
+#pragma clang fp contract(off)
+    __shared__ float4 s_rec[3 * RW_BATCH];
+    __shared__ uint8_t s_mask[RW_BATCH];
+    __shared__ uint16_t s_list[4 * RW_BATCH];
+    const QuarterCtx t = quarter_ctx(W, H, TX, T);
+    if (t.empty) return;
+    const uint2 rg = *(const uint2*)(ranges + 2 * (uint64_t)t.tile_lin);
+    const float* rv = rec + (int64_t)t.view * n * GS_REC_FLOATS;
+    float Tr = 1.f, C0 = 0.f, C1 = 0.f, C2 = 0.f;
+    int32_t last = 0;
+    bool done = !t.inside;
+    // two-stage prefetch: records of batch k+1 and ids of batch k+2 are
+    // requested while batch k is evaluated
+    Entry cur, nxt;
+    cur.valid = rg.x + t.lane < rg.y;
+    cur.gid = cur.valid ? vals[rg.x + t.lane] : 0u;
+    gather_record(cur, rv);
+    nxt.valid = rg.x + RW_BATCH + t.lane < rg.y;
+    nxt.gid = nxt.valid ? vals[rg.x + RW_BATCH + t.lane] : 0u;
+    for (uint32_t base = rg.x; base < rg.y; base += RW_BATCH) {
+        if (ballot(!done) == 0ull) break;
+        stage_entry(cur, t.lane, t, W, H, s_rec, s_mask);
+        gather_record(nxt, rv);
+        const uint32_t j2 = base + 2 * RW_BATCH + t.lane;
+        const bool v2 = j2 < rg.y;
+        const uint32_t gid2 = v2 ? vals[j2] : 0u;
+        uint32_t cnt[4];
+        rows_compact(s_mask, s_list, t.lane, cnt, [](int, int) { return true; });
+        const uint32_t my_cnt = t.row == 0 ? cnt[0] : t.row == 1 ? cnt[1] : t.row == 2 ? cnt[2] : cnt[3];
+        const uint32_t iters = max(max(cnt[0], cnt[1]), max(cnt[2], cnt[3]));
+        const uint16_t* my_list = s_list + t.row * RW_BATCH;
+        const int32_t pos0 = (int32_t)(base - rg.x) + 1;
+        for (uint32_t it = 0; it < iters; ++it) {
+            const bool has = it < my_cnt;
+            const int idx = has ? (int)my_list[it] : 0;  // exhausted rows idle on slot 0
+            const float4 q0 = s_rec[3 * idx], q1 = s_rec[3 * idx + 1], q2 = s_rec[3 * idx + 2];
+            // branch-free update: only lanes that blend change state (a zero
+            // weight adds exactly 0)
+            float dx, dy;
+            const float power = entry_power(q0, q1, t.px, t.py, dx, dy);
+            const float alpha = fminf(ALPHA_MAX, q1.y * exp_fast(power));
+            const float Tn = Tr * (1.f - alpha);
+            const bool keep = has && !done && !(power > 0.f) && !(alpha < ALPHA_MIN);
+            const bool stop = keep && Tn < T_MIN;
+            const bool blend = keep && !stop;
+            const float w = blend ? alpha * Tr : 0.f;
+            C0 = __builtin_fmaf(q1.z, w, C0);
+            C1 = __builtin_fmaf(q1.w, w, C1);
+            C2 = __builtin_fmaf(q2.x, w, C2);
+            Tr = blend ? Tn : Tr;
+            last = blend ? pos0 + idx : last;
+            done = done || stop;
+            if ((it & 3) == 3 && ballot(!done) == 0ull) break;
+        }
+        asm volatile("" ::: "memory");  // this batch's LDS reads precede the next staging
+        cur = nxt;
+        nxt.valid = v2;
+        nxt.gid = gid2;
+    }
+    if (t.inside) {
+        const int64_t HW = (int64_t)H * W;
+        const int64_t pix = (int64_t)t.j * W + t.i;
+        float* img = image + (int64_t)t.view * 3 * HW + pix;
+        img[0] = C0 + Tr * bg0;
+        img[HW] = C1 + Tr * bg1;
+        img[2 * HW] = C2 + Tr * bg2;
+        T_final[(int64_t)t.view * HW + pix] = Tr;
+        n_contrib[(int64_t)t.view * HW + pix] = last;
+    }
+}
+
+}  // namespace gs
+
+using namespace gs;
+
+extern "C" {
+
+gs_status gs_rasterize_fwd(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
+                           const gs_camera* cams, int32_t n_views, const float* bg, float* image, float* T_final,
+                           int32_t* n_contrib, void* stream)
+{
+    RasterArgs a;
+    if (!raster_args(rec, n, ranges, vals, cams, n_views, bg, a)) return GS_ERR_INVALID_ARGUMENT;
+    if (!image || !T_final || !n_contrib) return GS_ERR_INVALID_ARGUMENT;
+    hipLaunchKernelGGL(k_raster_fwd, dim3((unsigned)a.n_blocks), dim3(RW_THREADS), 0, (hipStream_t)stream, rec, n,
+                       ranges, vals, a.dc.width, a.dc.height, a.dc.tiles_x, a.dc.tiles_per_view, bg[0], bg[1], bg[2],
+                       image, T_final, n_contrib);
+    return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
+}
+
+}  // extern "C"

@@ -103,7 +103,8 @@ enum {
     GS_REC_EXT_X = 9, GS_REC_EXT_Y = 10, GS_REC_DEPTH = 11
 };
 
-/* 2D gradient rows, grad2d[(v * 9 + row) * n + g]. */
+/* 2D gradients of (view v, Gaussian g), one 9-float record each:
+ * grad2d[(v * n + g) * 9 + row]. */
 enum {
     GS_G2_U = 0, GS_G2_V = 1, GS_G2_A = 2, GS_G2_B = 3, GS_G2_C = 4,
     GS_G2_OPACITY = 5, GS_G2_R = 6, GS_G2_G = 7, GS_G2_BLUE = 8
@@ -235,7 +236,7 @@ gs_status gs_loss_l1(const float* image, const float* target, int64_t count, flo
  * gs_rasterize_bwd -- back to front over each pixel's blended entries
  * (backward rasterization of the ByteSplat abstract), gradients to the 2D
  * quantities of every (view, Gaussian):
- *   grad2d  [V][9][n] fp32 (rows GS_G2_*): du dv dA dB dC dopacity dr dg db;
+ *   grad2d  [V][n][9] fp32 (rows GS_G2_*): du dv dA dB dC dopacity dr dg db;
  *           zeroed first unless `accumulate` is non-zero
  * Inputs as in gs_rasterize_fwd plus its T_final and n_contrib and dL/dimage.
  * Floating-point atomics make the summation order, and so the last bits, vary

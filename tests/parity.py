@@ -69,12 +69,12 @@ def gpu_backward(b: Buffers, params_t: torch.Tensor, dL_np: np.ndarray, bg=(0.0,
     grad = torch.empty_like(params_t)
     b.backward(params_t, grad, bg)
     torch.cuda.synchronize()
-    g2 = np_(b.grad2d).reshape(b.V, L.GS_GRAD2D_ROWS, b.n)
+    g2 = np_(b.grad2d).reshape(b.V, b.n, L.GS_GRAD2D_ROWS)
     return g2, np_(grad)
 
 
 def gpu_preprocess_bwd(b: Buffers, params_t: torch.Tensor, grad2d_np: np.ndarray):
-    """Parameter gradients from a given [V][9][n] 2D gradient."""
+    """Parameter gradients from a given [V][n][9] 2D gradient."""
     b.grad2d.copy_(torch.from_numpy(np.ascontiguousarray(grad2d_np, dtype=np.float32).reshape(-1)))
     grad = torch.empty_like(params_t)
     L.gs_preprocess_bwd(params_t, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, grad)
@@ -170,9 +170,9 @@ def check_forward(gpu, fwd):
 
 
 def check_grad2d(g2_gpu, g2_ref, gabs):
-    """g2_gpu [V][9][n] vs oracle [V][n][9]."""
-    ref = np.transpose(g2_ref, (0, 2, 1))
-    A = np.transpose(gabs, (0, 2, 1))
+    """g2_gpu and the oracle's, both [V][n][9]."""
+    ref = g2_ref
+    A = gabs
     err = np.abs(g2_gpu.astype(np.float64) - ref)
     lim = GRAD_RTOL * np.abs(ref) + GRAD_AFLOOR * A
     bad = err > lim

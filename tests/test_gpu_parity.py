@@ -74,7 +74,7 @@ def test_backward(run):
     print(st)
     # parameter gradients, stage-wise: both fed the GPU's 2D gradients
     sh = run["cfg"].sh_degree
-    g_ref = O.preprocess_bwd(run["params"], sh, run["cams"], np.transpose(g2_gpu, (0, 2, 1)).astype(np.float64))
+    g_ref = O.preprocess_bwd(run["params"], sh, run["cams"], g2_gpu.astype(np.float64))
     g_gpu = PY.gpu_preprocess_bwd(run["buf"], run["gpu"]["params_t"], g2_gpu)
     st = PY.check_param_grads(g_gpu, g_ref)
     print(st)
