@@ -426,7 +426,8 @@ double FN(or_loss_l1)(const REAL* img, const REAL* tgt, int64_t per_view, int V,
  *   dI/da_i = c_i T_i - (sum_{k>i} c_k a_k T_k + T_final bg) / (1 - a_i)
  *   da/do = G, da/dpower = o G (zero when the 0.99 clamp is active)
  * grad2d [V][n][9] (fp64, accumulated): du dv dA dB dC do dr dg db.
- * gabs (optional) accumulates |contribution| per slot (tolerance floors).
+ * gabs (optional) accumulates, per slot, the absolute values of the terms
+ * each contribution is summed from (tolerance floors).
  * ------------------------------------------------------------------------ */
 void FN(or_render_bwd)(const REAL* rec, const int32_t* iv, int64_t n, const or_camera* cams, int V,
                        const float* bg, const REAL* dL_dimg, double* grad2d, double* gabs)
@@ -501,13 +502,20 @@ void FN(or_render_bwd)(const REAL* rec, const int32_t* iv, int64_t n, const or_c
                         for (int k = 0; k < m; ++k) {
                             const REAL* r = rv + L.ids[idx[k]] * OR_REC;
                             double* ac = acc + idx[k] * 18;
-                            double dIda = 0;
+                            /* dI/da is a sum over channels of differences (own
+                             * colour minus colour behind): the tolerance floor
+                             * takes the absolute value of every term of it and
+                             * of the dpower products, so that cancellation in
+                             * any of them is covered whatever the fp32 order */
+                            double dIda = 0, dIda_abs = 0;
                             for (int ch = 0; ch < 3; ++ch) {
                                 const double c = (double)r[10 + ch];
                                 const double dc = g3[ch] * al[k] * Ti[k];
                                 ac[6 + ch] += dc;
                                 ac[9 + 6 + ch] += fabs(dc);
-                                dIda += g3[ch] * (c * Ti[k] - suf[3 * (k + 1) + ch] / (1.0 - al[k]));
+                                const double t_own = c * Ti[k], t_behind = suf[3 * (k + 1) + ch] / (1.0 - al[k]);
+                                dIda += g3[ch] * (t_own - t_behind);
+                                dIda_abs += fabs(g3[ch]) * (fabs(t_own) + fabs(t_behind));
                             }
                             if (cl[k]) continue;
                             const double dx = (double)r[0] - (double)px, dy = (double)r[1] - (double)py;
@@ -517,7 +525,11 @@ void FN(or_render_bwd)(const REAL* rec, const int32_t* iv, int64_t n, const or_c
                                 -dpow * (A * dx + B * dy), -dpow * (B * dx + C * dy),
                                 -0.5 * dpow * dx * dx, -dpow * dx * dy, -0.5 * dpow * dy * dy,
                                 dIda * Gs[k]};
-                            for (int q = 0; q < 6; ++q) { ac[q] += d[q]; ac[9 + q] += fabs(d[q]); }
+                            const double pa = dIda_abs * o * Gs[k];
+                            const double da[6] = {
+                                pa * (fabs(A * dx) + fabs(B * dy)), pa * (fabs(B * dx) + fabs(C * dy)),
+                                0.5 * pa * dx * dx, pa * fabs(dx * dy), 0.5 * pa * dy * dy, dIda_abs * Gs[k]};
+                            for (int q = 0; q < 6; ++q) { ac[q] += d[q]; ac[9 + q] += da[q]; }
                         }
                     }
             }
