@@ -31,9 +31,9 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(const float* __restrict_
     for (int k = 0; k < 3 * NB; ++k) sh[k] = P[(int64_t)(11 + k) * n + g];
 
     float gpx = 0.f, gpy = 0.f, gpz = 0.f, gop = 0.f;
-    float gM[9];
+    float gS3[9];  // dL/dSigma3, summed over the views
 #pragma unroll
-    for (int i = 0; i < 9; ++i) gM[i] = 0.f;
+    for (int i = 0; i < 9; ++i) gS3[i] = 0.f;
     float gsh[3 * NB];
 #pragma unroll
     for (int i = 0; i < 3 * NB; ++i) gsh[i] = 0.f;
@@ -53,13 +53,18 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(const float* __restrict_
         const float grgb[3] = {g2[6], g2[7], g2[8]};
         gop += go;
 
-        // conic Q = Sigma2^-1: dL/dSigma2 = -Q G Q, G = [[gA, gB/2], [gB/2, gC]]
-        const float hB = 0.5f * gB;
-        const float X00 = gA * p.A + hB * p.B, X01 = gA * p.B + hB * p.C;
-        const float X10 = hB * p.A + gC * p.B, X11 = hB * p.B + gC * p.C;
-        const float ga = -(p.A * X00 + p.B * X10);
-        const float gc = -(p.B * X01 + p.C * X11);
-        const float s01 = -0.5f * ((p.A * X01 + p.B * X11) + (p.B * X00 + p.C * X10));
+        // conic Q = Sigma2^-1: dL/dSigma2 = -Q G Q, G = [[gA, gB/2], [gB/2, gC]].
+        // In fp64: for a needle-like footprint Q is nearly singular and the
+        // products cancel by orders of magnitude; fp32 here would cost the
+        // rotation gradient (which depends on the small components) most of
+        // its digits. The result is rounded back to fp32.
+        const double qA = p.A, qB = p.B, qC = p.C;
+        const double hB = 0.5 * (double)gB;
+        const double X00 = (double)gA * qA + hB * qB, X01 = (double)gA * qB + hB * qC;
+        const double X10 = hB * qA + (double)gC * qB, X11 = hB * qB + (double)gC * qC;
+        const float ga = (float)(-(qA * X00 + qB * X10));
+        const float gc = (float)(-(qB * X01 + qC * X11));
+        const float s01 = (float)(-0.5 * ((qA * X01 + qB * X11) + (qB * X00 + qC * X10)));
         // Sigma2 = T Sigma3 T^T (+ 0.3 I): dSigma3 = T^T G2 T, dT = 2 G2 T Sigma3
         float Yt[6];
 #pragma unroll
@@ -84,12 +89,8 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(const float* __restrict_
             dT[k] = 2.f * (ga * TS[k] + s01 * TS[3 + k]);
             dT[3 + k] = 2.f * (s01 * TS[k] + gc * TS[3 + k]);
         }
-        // Sigma3 = M M^T: dM = 2 dSigma3 M
 #pragma unroll
-        for (int i = 0; i < 3; ++i)
-#pragma unroll
-            for (int j = 0; j < 3; ++j)
-                gM[3 * i + j] += 2.f * (dS3[3 * i] * L.M[j] + dS3[3 * i + 1] * L.M[3 + j] + dS3[3 * i + 2] * L.M[6 + j]);
+        for (int i = 0; i < 9; ++i) gS3[i] += dS3[i];
         // T = J W
         const float* W = cam.R;
         const float dJ00 = dT[0] * W[0] + dT[1] * W[1] + dT[2] * W[2];
@@ -181,31 +182,41 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(const float* __restrict_
         G[0] = gpx;
         G[1] = gpy;
         G[2] = gpz;
-        // M = R diag(s)
-        float gR[9];
+        // Sigma3 = R diag(d) R^T with d = s^2. In the rotated frame,
+        // G' = R^T dL/dSigma3 R: d/d log s_j = 2 d_j G'_jj, and a rotation
+        // R -> R (I + [w]x) changes L by g . w with
+        // g = ((d1 - d2) (G'12 + G'21), (d2 - d0) (G'20 + G'02), (d0 - d1) (G'01 + G'10)).
+        // The scale differences appear as explicit factors, computed as
+        // (s_i - s_j)(s_i + s_j): a Gaussian with two nearly equal scales keeps
+        // the full relative precision of its (small) gradient about that axis.
+        const float* Rm = L.Rm;
+        float Y[9];  // dL/dSigma3 R
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            const float gs = gM[j] * L.Rm[j] + gM[3 + j] * L.Rm[3 + j] + gM[6 + j] * L.Rm[6 + j];
-            G[3 + j] = gs * L.s[j];  // d/d log-scale
+        for (int i = 0; i < 3; ++i)
 #pragma unroll
-            for (int i = 0; i < 3; ++i) gR[3 * i + j] = gM[3 * i + j] * L.s[j];
-        }
-        // rotation of the unit quaternion (w, x, y, z)
-        const float w = L.q[0], qx = L.q[1], qy = L.q[2], qz = L.q[3];
-        const float gw = 2.f * (-qz * gR[1] + qy * gR[2] + qz * gR[3] - qx * gR[5] - qy * gR[6] + qx * gR[7]);
-        const float gx = 2.f * (qy * gR[1] + qz * gR[2] + qy * gR[3] - 2.f * qx * gR[4] - w * gR[5] + qz * gR[6] +
-                                w * gR[7] - 2.f * qx * gR[8]);
-        const float gy = 2.f * (-2.f * qy * gR[0] + qx * gR[1] + w * gR[2] + qx * gR[3] + qz * gR[5] - w * gR[6] +
-                                qz * gR[7] - 2.f * qy * gR[8]);
-        const float gz = 2.f * (-2.f * qz * gR[0] - w * gR[1] + qx * gR[2] + w * gR[3] - 2.f * qz * gR[4] +
-                                qy * gR[5] + qx * gR[6] + qy * gR[7]);
+            for (int j = 0; j < 3; ++j)
+                Y[3 * i + j] = gS3[3 * i] * Rm[j] + gS3[3 * i + 1] * Rm[3 + j] + gS3[3 * i + 2] * Rm[6 + j];
+        float Gp[9];  // R^T dL/dSigma3 R
+#pragma unroll
+        for (int a = 0; a < 3; ++a)
+#pragma unroll
+            for (int b = 0; b < 3; ++b) Gp[3 * a + b] = Rm[a] * Y[b] + Rm[3 + a] * Y[3 + b] + Rm[6 + a] * Y[6 + b];
+        const float s0 = L.s[0], s1 = L.s[1], s2 = L.s[2];
+        G[3] = 2.f * (s0 * s0) * Gp[0];
+        G[4] = 2.f * (s1 * s1) * Gp[4];
+        G[5] = 2.f * (s2 * s2) * Gp[8];
+        const float om0 = ((s1 - s2) * (s1 + s2)) * (Gp[5] + Gp[7]);
+        const float om1 = ((s2 - s0) * (s2 + s0)) * (Gp[6] + Gp[2]);
+        const float om2 = ((s0 - s1) * (s0 + s1)) * (Gp[1] + Gp[3]);
+        // unit quaternion (w, v): the body rotation w = 2 vec(conj(q^) dq^),
+        // and dq^ = (I - q^ q^T) dq / |q| (the radial part drops out of it)
         if (L.qn > 0.f) {
-            const float dot = w * gw + qx * gx + qy * gy + qz * gz;
-            const float inv = 1.f / L.qn;
-            G[6] = (gw - w * dot) * inv;
-            G[7] = (gx - qx * dot) * inv;
-            G[8] = (gy - qy * dot) * inv;
-            G[9] = (gz - qz * dot) * inv;
+            const float w = L.q[0], qx = L.q[1], qy = L.q[2], qz = L.q[3];
+            const float k = 2.f / L.qn;
+            G[6] = -k * (qx * om0 + qy * om1 + qz * om2);
+            G[7] = k * (w * om0 + (qy * om2 - qz * om1));
+            G[8] = k * (w * om1 + (qz * om0 - qx * om2));
+            G[9] = k * (w * om2 + (qx * om1 - qy * om0));
         }
         G[10] = gop * L.o * (1.f - L.o);
 #pragma unroll

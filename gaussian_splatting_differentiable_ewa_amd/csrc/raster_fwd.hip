@@ -72,10 +72,18 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_fwd(const float* __restri
         const uint32_t iters = max(max(cnt[0], cnt[1]), max(cnt[2], cnt[3]));
         const uint16_t* my_list = s_list + t.row * RW_BATCH;
         const int32_t pos0 = (int32_t)(base - rg.x) + 1;
+        // software pipeline: the next entry's slot and record are read from
+        // LDS while the current one is evaluated (exhausted rows idle on slot 0)
+        int idx_n = my_cnt > 0 ? (int)my_list[0] : 0;
+        float4 n0 = s_rec[3 * idx_n], n1 = s_rec[3 * idx_n + 1], n2 = s_rec[3 * idx_n + 2];
         for (uint32_t it = 0; it < iters; ++it) {
             const bool has = it < my_cnt;
-            const int idx = has ? (int)my_list[it] : 0;  // exhausted rows idle on slot 0
-            const float4 q0 = s_rec[3 * idx], q1 = s_rec[3 * idx + 1], q2 = s_rec[3 * idx + 2];
+            const int idx = idx_n;
+            const float4 q0 = n0, q1 = n1, q2 = n2;
+            idx_n = it + 1 < my_cnt ? (int)my_list[it + 1] : 0;
+            n0 = s_rec[3 * idx_n];
+            n1 = s_rec[3 * idx_n + 1];
+            n2 = s_rec[3 * idx_n + 2];
             // branch-free update: only lanes that blend change state (a zero
             // weight adds exactly 0)
             float dx, dy;

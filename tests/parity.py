@@ -176,7 +176,12 @@ def check_grad2d(g2_gpu, g2_ref, gabs):
     err = np.abs(g2_gpu.astype(np.float64) - ref)
     lim = GRAD_RTOL * np.abs(ref) + GRAD_AFLOOR * A
     bad = err > lim
-    assert not bad.any(), f"{bad.sum()} 2D gradients out of tolerance, worst {(err - lim).max()}"
+    if bad.any():
+        where = np.argwhere(bad)[:8]
+        detail = [(tuple(int(x) for x in w), float(ref[tuple(w)]), float(g2_gpu[tuple(w)]), float(A[tuple(w)]))
+                  for w in where]
+        raise AssertionError(f"{bad.sum()} 2D gradients out of tolerance, worst {(err - lim).max()}; "
+                             f"(index, ref, gpu, abs-sum): {detail}")
     nz = np.abs(ref) > 0
     within = np.mean(err[nz] <= GRAD_RTOL * np.abs(ref[nz])) if nz.any() else 1.0
     return {"grad2d_within_1e-3_rel": float(within)}
