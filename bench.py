@@ -8,8 +8,13 @@ seeded scene, fp32. Inputs are synthetic and resident in HBM before timing.
 
 Prints one JSON line. `value` is iterations/s of the whole step; Mpix/s and
 the per-stage breakdown ride along. The roofline object describes the step's
-dominant kernel, timed with HIP events on the stream it runs on; the
-cpu_baseline object times the CPU oracle on a bounded sample on this host.
+dominant kernel, timed with HIP events on the stream it runs on: for a raster
+kernel, fp32 work is 12 flops per evaluated (pixel, entry) pair -- every entry
+of a pixel's list up to its last contributor, summed from n_contrib -- against
+the fp32 FMA rate without packed math; for the others, algorithmic HBM bytes
+against 8 TB/s. `traffic` is the kernel's measured HBM bytes per dispatch from
+the committed counter summary (null once the kernel's sources have changed).
+The cpu_baseline object times the CPU oracle on a bounded sample on this host.
 """
 
 from __future__ import annotations
@@ -23,9 +28,57 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (packed); 78.6 without packing
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+# fp32 FMA rate without packed-fp32 instructions (which this build leaves
+# disabled): 256 CUs x 64 lanes x 2 flops x 2.4 GHz. The published 157.3
+# TFLOP/s counts packed (two-wide) fp32.
+FP32_FMA_PEAK_TFLOPS = 78.6
+# fp32 operations every evaluated (pixel, entry) pair costs in either raster
+# pass: dx, dy (2), the power polynomial (3 mul + 2 fma = 7), exp (1),
+# opacity x G (1), the 0.99 clamp (1)
+FLOPS_PER_PAIR = 12
 METRIC = "fwd+bwd+Adam iters/s & Mpix/s, 1M Gaussians SH3 @1080p; % of HBM roofline"
+CSRC = os.path.join(ROOT, "gaussian_splatting_differentiable_ewa_amd", "csrc")
+# sources each kernel is built from (a change voids its stored traffic counts)
+KERNEL_SOURCES = {
+    "k_raster_bwd": ["raster_bwd.hip", "raster_common.h", "internal.h", "common.h"],
+    "k_raster_fwd": ["raster_fwd.hip", "raster_common.h", "internal.h", "common.h"],
+    "k_adam": ["optim.hip", "internal.h", "common.h"],
+    "k_preprocess_bwd": ["preprocess_bwd.hip", "project.h", "internal.h", "common.h"],
+}
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_digest(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload):
+    return os.path.join(PROFILES, f"traffic_{workload}.md")
+
+
+def stored_traffic(workload, kernel):
+    """HBM bytes per dispatch of `kernel` from the committed counter summary,
+    or None when there is none or the kernel's sources changed since."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    digest = kernel_digest(kernel)
+    with open(path) as fh:
+        for line in fh:
+            parts = line.strip().strip("|").split("|")
+            parts = [p.strip() for p in parts]
+            if len(parts) >= 6 and parts[0] == kernel and parts[5] == digest:
+                try:
+                    return int(parts[4])
+                except ValueError:
+                    return None
+    return None
 
 
 def parse():
@@ -37,6 +90,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-views", type=int, default=1,
                     help="views of the workload the CPU oracle runs (its time is scaled to all views)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no benchmark: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
+                         "WRITE_SIZE, csv output) into the traffic summary under profiles/")
+    ap.add_argument("--traffic-command", default="",
+                    help="the counter command, COUNTER standing for the counter name (quoted in the summary)")
     return ap.parse_args()
 
 
@@ -63,6 +121,11 @@ def stage_bytes(P, n, V, K, n_vis_per_view, n_any, n_px):
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        from gaussian_splatting_differentiable_ewa_amd import scenes as S
+        traffic_summary(args.traffic_summary[0], args.traffic_summary[1], S.CONFIGS[args.config].name,
+                        args.traffic_command)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU layout is a design "
               "note, not a measured path.", file=sys.stderr)
@@ -88,7 +151,8 @@ def main():
 
     b = ts.buf
     stream = torch.cuda.current_stream()
-    names = ["preprocess", "intersections", "raster_fwd", "loss", "raster_bwd", "preprocess_bwd", "adam"]
+    names = ["preprocess", "intersections", "raster_fwd", "loss", "grad2d_zero", "raster_bwd", "preprocess_bwd",
+             "adam"]
 
     def step_timed(ev):
         ts.t += 1
@@ -101,19 +165,23 @@ def main():
         ev[3].record(stream)
         b.loss_l1(ts.target)
         ev[4].record(stream)
-        L.gs_rasterize_bwd(b.rec, b.n, b.ranges, b.sorted_vals, b.cams, ts.bg, b.T_final, b.n_contrib, b.dL,
-                           b.grad2d)
+        # the 2D-gradient buffer is cleared on its own, so that the next
+        # event pair brackets the backward raster kernel alone
+        b.grad2d.zero_()
         ev[5].record(stream)
-        L.gs_preprocess_bwd(ts.params, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, ts.grad)
+        L.gs_rasterize_bwd(b.rec, b.n, b.ranges, b.sorted_vals, b.cams, ts.bg, b.T_final, b.n_contrib, b.dL,
+                           b.grad2d, accumulate=True)
         ev[6].record(stream)
+        L.gs_preprocess_bwd(ts.params, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, ts.grad)
+        ev[7].record(stream)
         L.gs_adam_step(ts.params, ts.grad, ts.m, ts.v, ts.params.numel(), ts.lr, ts.betas[0], ts.betas[1],
                        ts.eps, ts.t)
-        ev[7].record(stream)
+        ev[8].record(stream)
 
     for _ in range(args.warmup):
         ts.step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
@@ -136,16 +204,32 @@ def main():
     frac_step = step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9)
 
     # dominant kernel: the single-kernel stage with the largest time
-    single = {"raster_fwd": sb["raster_fwd"], "raster_bwd": sb["raster_bwd"], "adam": sb["adam"],
-              "preprocess_bwd": sb["preprocess_bwd"]}
+    pairs = int(b.n_contrib.sum(dtype=torch.int64))  # (pixel, entry) pairs up to each last contributor
+    single = {"raster_fwd": "k_raster_fwd", "raster_bwd": "k_raster_bwd", "adam": "k_adam",
+              "preprocess_bwd": "k_preprocess_bwd"}
     dom = max(single, key=lambda k: stage_ms[k])
-    dom_kernel = {"raster_fwd": "k_raster_fwd", "raster_bwd": "k_raster_bwd", "adam": "k_adam",
-                  "preprocess_bwd": "k_preprocess_bwd<3>"}[dom]
-    achieved = single[dom] / (stage_ms[dom] * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "kernel": dom_kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "algorithmic_bytes": int(single[dom])}
+    kern = single[dom]
+    dur_s = stage_ms[dom] * 1e-3
+    if dom.startswith("raster"):
+        flops = FLOPS_PER_PAIR * pairs
+        achieved = flops / dur_s / 1e12
+        roofline = {"bound": "alu", "kernel": kern, "achieved": round(achieved, 3), "peak": FP32_FMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / FP32_FMA_PEAK_TFLOPS, 4),
+                    "traffic": stored_traffic(cfg.name, kern), "algorithmic_flops": flops,
+                    "pairs": pairs, "flops_per_pair": FLOPS_PER_PAIR, "algorithmic_bytes": int(sb[dom]),
+                    "hbm_gbs_algorithmic": round(sb[dom] / dur_s / 1e9, 1)}
+    else:
+        achieved = sb[dom] / dur_s / 1e9
+        roofline = {"bound": "hbm", "kernel": kern, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": stored_traffic(cfg.name, kern), "algorithmic_bytes": int(sb[dom])}
+    roofline["avg_launch_ms"] = round(stage_ms[dom], 4)
 
+    # intersection statistics and a plain device copy for the achievable HBM rate
+    rng_ = b.ranges.view(-1, 2).to(torch.int64)
+    max_per_tile = int((rng_[:, 1] - rng_[:, 0]).max())
+    peak_list_bytes = 2 * 12 * b.capacity + b.sort_ws.numel()
+    copy_gbs = copy_probe(torch, dev)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, params_np, cams, args.cpu_sample_views)
@@ -158,11 +242,87 @@ def main():
                    "width": W, "height": H},
         "mpix_per_s": round(mpix, 2),
         "step_hbm_fraction": round(frac_step, 4), "step_algorithmic_bytes": int(step_bytes),
-        "intersections": b.K, "visible_per_view": n_vis,
+        "intersections": b.K, "k_per_gaussian": round(b.K / b.n, 4), "visible_per_view": n_vis,
+        "max_per_tile": max_per_tile, "peak_intersection_bytes": int(peak_list_bytes),
+        "hbm_copy_gbs": round(copy_gbs, 1),
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+COPY_BYTES = 1 << 30
+
+
+def copy_probe(torch, dev, reps=5):
+    """Device-to-device copy of 1 GiB (read + write counted): the achievable
+    HBM rate, and the known-size dispatch that calibrates the traffic
+    counters."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * COPY_BYTES * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def traffic_summary(fetch_dir, write_dir, workload, command):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of every library kernel from
+    two counter runs, scaled by what the same counters read for the 1 GiB
+    copy (the largest copy dispatch), written as a table under profiles/."""
+    import csv
+    import glob
+
+    def load(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        assert files, f"no counter_collection.csv under {d}"
+        per = {}
+        for f in files:
+            with open(f) as fh:
+                for row in csv.DictReader(fh):
+                    if row["Counter_Name"] != counter:
+                        continue
+                    per.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return per
+
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    copy_name = [k for k in fetch if "copyBuffer" in k or "copy" in k.lower()]
+    assert copy_name, "the copy dispatch is missing from the counter run"
+    cf = max(max(fetch[k]) for k in copy_name)
+    cw = max(max(write.get(k, [0.0])) for k in copy_name)
+    f_scale = (COPY_BYTES / 1024.0) / cf
+    w_scale = (COPY_BYTES / 1024.0) / cw
+    rows = []
+    for name in sorted(fetch):
+        short = name.split("(")[0].replace("void ", "").replace("gs::", "")
+        base = short.split("<")[0]
+        if not base.startswith("k_"):
+            continue
+        fk = sum(fetch[name]) / len(fetch[name])
+        wk = sum(write.get(name, [0.0])) / max(1, len(write.get(name, [])))
+        total = int(round((fk * f_scale + wk * w_scale) * 1024.0))
+        digest = kernel_digest(base) if base in KERNEL_SOURCES else "-"
+        rows.append(f"| {base} | {len(fetch[name])} | {fk:.1f} | {wk:.1f} | {total} | {digest} |")
+    text = [f"# HBM traffic per dispatch, {workload}", "",
+            "Two counter runs of the same benchmark command, one counter each:", "",
+            "    " + command.replace("COUNTER", "FETCH_SIZE"),
+            "    " + command.replace("COUNTER", "WRITE_SIZE"), "",
+            f"Calibration: the 1 GiB device copy read {cf:.1f} KiB (FETCH_SIZE) and wrote {cw:.1f} KiB "
+            f"(WRITE_SIZE) against {COPY_BYTES // 1024} KiB each way: scale factors {f_scale:.4f} and "
+            f"{w_scale:.4f}.", "",
+            "The digest column is a hash of the kernel's sources when the counters were taken; the "
+            "benchmark reports the bytes only while it matches.", "",
+            "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) | sources digest |",
+            "|---|---|---|---|---|---|"] + rows
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(traffic_file(workload), "w") as fh:
+        fh.write("\n".join(text) + "\n")
+    print(traffic_file(workload))
 
 
 def cpu_baseline(cfg, params_np, cams, sample_views):
