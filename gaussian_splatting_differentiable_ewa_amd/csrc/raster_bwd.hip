@@ -43,15 +43,15 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
                                                            float* __restrict__ grad2d)
 {
 #pragma clang fp contract(off)
-    __shared__ float4 s_rec[3 * RW_BATCH];
+    // about 10 KB of LDS per wave, so that 16 waves fit a CU
+    __shared__ float4 s_rec[2 * RW_BATCH];  // (u v -A/2 -B) (-C/2 o r g) per slot
+    __shared__ float s_b[RW_BATCH];         // blue of each slot
     __shared__ uint8_t s_mask[RW_BATCH];
     __shared__ uint16_t s_list[4 * RW_BATCH];
-    __shared__ float s_part[4][GS_GRAD2D_ROWS][RW_BATCH];  // [row][gradient][slot] sums of each row
-    __shared__ float2 s_coef[4][16][CSTRIDE];  // [row][pixel][slot]
-    __shared__ float4 s_g[RW_THREADS];         // dL/dimage of each lane's pixel
-    __shared__ uint32_t s_gid[RW_BATCH];       // Gaussian of each staged slot
-    __shared__ uint8_t s_rows[RW_BATCH];       // rows whose list held each slot
-    __shared__ uint8_t s_live[RW_BATCH];       // slots with a contribution, compacted
+    __shared__ float s_sum[GS_GRAD2D_ROWS][RW_BATCH];  // [gradient][slot], summed over the rows
+    __shared__ float2 s_coef[4][16][CSTRIDE];          // [row][pixel][slot]
+    __shared__ uint32_t s_gid[RW_BATCH];               // Gaussian of each staged slot
+    __shared__ uint8_t s_live[RW_BATCH];               // slots with a contribution, compacted
     const QuarterCtx t = quarter_ctx(W, H, TX, T);
     if (t.empty) return;
     const int64_t HW = (int64_t)H * W;
@@ -75,14 +75,22 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
     const int32_t wave_last = max(max(rl0, rl1), max(rl2, rl3));
     if (wave_last <= 0) return;
     const int q = t.lane & 15;
-    s_g[t.lane] = make_float4(g0, g1, g2, 0.f);
+    // phase-2 lanes (e, h) sum over pixels h*8 .. h*8+7 of their row: the
+    // dL/dimage of those pixels, taken from the lanes that own them
+    float gh0[8], gh1[8], gh2[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int src = (t.lane & ~15) + (q >> 3) * 8 + k;
+        gh0[k] = __shfl(g0, src);
+        gh1[k] = __shfl(g1, src);
+        gh2[k] = __shfl(g2, src);
+    }
     const float* rv = rec + (int64_t)t.view * n * GS_REC_FLOATS;
     float* g2d = grad2d + (int64_t)t.view * n * GS_GRAD2D_ROWS;  // [n][9] records of this view
     // origin of this row's 4x4 sub-block (pixel centres)
     const float sbx = (float)(t.qx0 + (t.row & 1) * 4) + 0.5f;
     const float sby = (float)(t.qy0 + (t.row >> 1) * 4) + 0.5f;
     float2(*coef)[CSTRIDE] = s_coef[t.row];
-    const float4* grow = &s_g[t.row * 16];
     // colour behind the current entry, normalised by the transmittance in
     // front of it; starts as the background behind the last blended entry
     float acc0 = bg0, acc1 = bg1, acc2 = bg2;
@@ -98,7 +106,9 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
         nxt.gid = nxt.valid ? vals[rg.x + (uint32_t)(p1 - 1)] : 0u;
     }
     for (int32_t hi = wave_last; hi >= 1; hi -= RW_BATCH) {
-        stage_entry(cur, t.lane, t, W, H, s_rec, s_mask);
+        stage_entry_pair(cur, t.lane, t, W, H, s_rec, s_b, s_mask);
+#pragma unroll
+        for (int k = 0; k < GS_GRAD2D_ROWS; ++k) s_sum[k][t.lane] = 0.f;
         gather_record(nxt, rv);
         const int32_t p2 = hi - 2 * RW_BATCH - t.lane;
         const bool v2 = p2 >= 1;
@@ -119,7 +129,8 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
                 const bool has = it < my_cnt;
                 const int idx = has ? (int)my_list[it] : 0;
                 const int32_t pos = hi - idx;
-                const float4 q0 = s_rec[3 * idx], q1 = s_rec[3 * idx + 1], q2 = s_rec[3 * idx + 2];
+                const float4 q0 = s_rec[2 * idx], q1 = s_rec[2 * idx + 1];
+                const float qb = s_b[idx];
                 float dx, dy;
                 const float power = entry_power(q0, q1, t.px, t.py, dx, dy);
                 const float G = exp_fast(power);
@@ -131,11 +142,11 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
                 // gradients need no correctly rounded division)
                 Tr = contrib ? Tr * __builtin_amdgcn_rcpf(1.f - alpha) : Tr;
                 const float wk = contrib ? alpha * Tr : 0.f;
-                const float dLda = Tr * (((q1.z - acc0) * g0 + (q1.w - acc1) * g1) + (q2.x - acc2) * g2);
+                const float dLda = Tr * (((q1.z - acc0) * g0 + (q1.w - acc1) * g1) + (qb - acc2) * g2);
                 const float ak = contrib ? alpha : 0.f;  // colour behind: unchanged when 0
                 acc0 = ak * q1.z + (1.f - ak) * acc0;
                 acc1 = ak * q1.w + (1.f - ak) * acc1;
-                acc2 = ak * q2.x + (1.f - ak) * acc2;
+                acc2 = ak * qb + (1.f - ak) * acc2;
                 const float dG = (contrib && !(oG > ALPHA_MAX)) ? dLda * G : 0.f;
                 coef[q][i] = make_float2(dG, wk);
             }
@@ -144,14 +155,13 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
             const uint32_t e = (uint32_t)q & 7u, h = (uint32_t)q >> 3;
             const bool has_e = sb + e < my_cnt;
             const int idx = has_e ? (int)my_list[sb + e] : 0;
-            const float4 q0 = s_rec[3 * idx], q1 = s_rec[3 * idx + 1];
+            const float4 q0 = s_rec[2 * idx], q1 = s_rec[2 * idx + 1];
             float go = 0.f, mx = 0.f, my = 0.f, mxx = 0.f, mxy = 0.f, myy = 0.f, gr = 0.f, gg = 0.f, gb = 0.f;
             if (e < n_sub) {
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     const int pp = (int)h * 8 + k;  // pixel of the sub-block: (pp & 3, pp >> 2)
                     const float2 c = coef[pp][e];
-                    const float4 gp = grow[pp];
                     const float dx = q0.x - (sbx + (float)(pp & 3));
                     const float dy = q0.y - (sby + (float)(pp >> 2));
                     const float cdx = c.x * dx, cdy = c.x * dy;
@@ -161,9 +171,9 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
                     mxx = __builtin_fmaf(cdx, dx, mxx);
                     mxy = __builtin_fmaf(cdx, dy, mxy);
                     myy = __builtin_fmaf(cdy, dy, myy);
-                    gr = __builtin_fmaf(c.y, gp.x, gr);
-                    gg = __builtin_fmaf(c.y, gp.y, gg);
-                    gb = __builtin_fmaf(c.y, gp.z, gb);
+                    gr = __builtin_fmaf(c.y, gh0[k], gr);
+                    gg = __builtin_fmaf(c.y, gh1[k], gg);
+                    gb = __builtin_fmaf(c.y, gh2[k], gb);
                 }
             }
             asm volatile("" ::: "memory");  // phase-2 reads precede the next phase-1 writes
@@ -180,20 +190,19 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
             gb = GS_ROR8(gb);
 #undef GS_ROR8
             if (h == 0 && has_e) {
-                // dL/dpower = (dL/da) o G: the o factor is applied here. Each
-                // row owns its slice, so these are plain stores.
+                // dL/dpower = (dL/da) o G: the o factor is applied here. Rows
+                // holding the same slot add into one LDS sum.
                 const float o = q1.y, nA = q0.z, nB = q0.w, nC = q1.x;
                 const float Mx = o * mx, My = o * my;
-                float* part = &s_part[t.row][0][idx];
-                part[0 * RW_BATCH] = 2.f * nA * Mx + nB * My;  // u
-                part[1 * RW_BATCH] = nB * Mx + 2.f * nC * My;  // v
-                part[2 * RW_BATCH] = -0.5f * o * mxx;          // A
-                part[3 * RW_BATCH] = -o * mxy;                 // B
-                part[4 * RW_BATCH] = -0.5f * o * myy;          // C
-                part[5 * RW_BATCH] = go;                       // opacity
-                part[6 * RW_BATCH] = gr;
-                part[7 * RW_BATCH] = gg;
-                part[8 * RW_BATCH] = gb;
+                atomicAdd(&s_sum[0][idx], 2.f * nA * Mx + nB * My);  // u
+                atomicAdd(&s_sum[1][idx], nB * Mx + 2.f * nC * My);  // v
+                atomicAdd(&s_sum[2][idx], -0.5f * o * mxx);          // A
+                atomicAdd(&s_sum[3][idx], -o * mxy);                 // B
+                atomicAdd(&s_sum[4][idx], -0.5f * o * myy);          // C
+                atomicAdd(&s_sum[5][idx], go);                       // opacity
+                atomicAdd(&s_sum[6][idx], gr);
+                atomicAdd(&s_sum[7][idx], gg);
+                atomicAdd(&s_sum[8][idx], gb);
             }
         }
         asm volatile("" ::: "memory");  // row sums precede the flush reads
@@ -208,7 +217,6 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
                                   (((m4 >> 2) & 1u) && pos <= rl2 ? 4u : 0u) | (((m4 >> 3) & 1u) && pos <= rl3 ? 8u : 0u);
             const bool live = cur.valid && rows != 0u;
             const uint64_t lm = ballot(live);
-            s_rows[t.lane] = (uint8_t)rows;
             s_gid[t.lane] = cur.gid;
             if (live) s_live[mask_rank(lm)] = (uint8_t)t.lane;
             asm volatile("" ::: "memory");
@@ -218,12 +226,7 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
                 const uint32_t ei = c + ke;
                 if (t.lane < 63 && ei < nlive) {
                     const int s = s_live[ei];
-                    const uint32_t rs = s_rows[s];
-                    float a = 0.f;
-                    if (rs & 1u) a += s_part[0][kk][s];
-                    if (rs & 2u) a += s_part[1][kk][s];
-                    if (rs & 4u) a += s_part[2][kk][s];
-                    if (rs & 8u) a += s_part[3][kk][s];
+                    const float a = s_sum[kk][s];
                     if (a != 0.f) atomicAdd(g2d + (int64_t)s_gid[s] * GS_GRAD2D_ROWS + kk, a);
                 }
             }

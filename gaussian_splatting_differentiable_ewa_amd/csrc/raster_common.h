@@ -85,8 +85,19 @@ __device__ __forceinline__ void gather_record(Entry& E, const float* __restrict_
 // (b, -, -, -), and the 4-bit mask of the quarter's 4x4 sub-blocks (clipped
 // to the image) whose pixel centres the entry's alpha >= 1/255 region
 // touches; an invalid entry gets mask 0.
+__device__ __forceinline__ uint32_t entry_mask(const Entry& E, const QuarterCtx& t, int W, int H);
+
 __device__ __forceinline__ void stage_entry(const Entry& E, int s, const QuarterCtx& t, int W, int H,
                                             float4* __restrict__ s_rec, uint8_t* __restrict__ s_mask)
+{
+    s_rec[3 * s + 0] = make_float4(E.a.x, E.a.y, -0.5f * E.a.z, -E.a.w);
+    s_rec[3 * s + 1] = make_float4(-0.5f * E.b.x, E.b.y, E.b.z, E.b.w);
+    s_rec[3 * s + 2] = make_float4(E.c.x, 0.f, 0.f, 0.f);
+    s_mask[s] = (uint8_t)entry_mask(E, t, W, H);
+}
+
+// The 4-bit sub-block mask of the lane's entry (see stage_entry).
+__device__ __forceinline__ uint32_t entry_mask(const Entry& E, const QuarterCtx& t, int W, int H)
 {
     uint32_t mask = 0;
     if (E.valid) {
@@ -102,10 +113,19 @@ __device__ __forceinline__ void stage_entry(const Entry& E, int s, const Quarter
         mask = (xm & ym & 1u) | (((xm >> 1) & ym & 1u) << 1) | ((xm & (ym >> 1) & 1u) << 2) |
                (((xm >> 1) & (ym >> 1) & 1u) << 3);
     }
-    s_rec[3 * s + 0] = make_float4(E.a.x, E.a.y, -0.5f * E.a.z, -E.a.w);
-    s_rec[3 * s + 1] = make_float4(-0.5f * E.b.x, E.b.y, E.b.z, E.b.w);
-    s_rec[3 * s + 2] = make_float4(E.c.x, 0.f, 0.f, 0.f);
-    s_mask[s] = (uint8_t)mask;
+    return mask;
+}
+
+// As stage_entry, with the record in two vectors (u v -A/2 -B) (-C/2 o r g)
+// and blue in its own array.
+__device__ __forceinline__ void stage_entry_pair(const Entry& E, int s, const QuarterCtx& t, int W, int H,
+                                                 float4* __restrict__ s_rec, float* __restrict__ s_b,
+                                                 uint8_t* __restrict__ s_mask)
+{
+    s_rec[2 * s + 0] = make_float4(E.a.x, E.a.y, -0.5f * E.a.z, -E.a.w);
+    s_rec[2 * s + 1] = make_float4(-0.5f * E.b.x, E.b.y, E.b.z, E.b.w);
+    s_b[s] = E.c.x;
+    s_mask[s] = (uint8_t)entry_mask(E, t, W, H);
 }
 
 // Per-row compaction of the 64 staged entries: for row r, the slots
