@@ -85,6 +85,7 @@ __device__ __forceinline__ void gather_record(Entry& E, const float* __restrict_
 // (b, -, -, -), and the 4-bit mask of the quarter's 4x4 sub-blocks (clipped
 // to the image) whose pixel centres the entry's alpha >= 1/255 region
 // touches; an invalid entry gets mask 0.
+template <bool REFINE>
 __device__ __forceinline__ uint32_t entry_mask(const Entry& E, const QuarterCtx& t, int W, int H);
 
 __device__ __forceinline__ void stage_entry(const Entry& E, int s, const QuarterCtx& t, int W, int H,
@@ -93,25 +94,80 @@ __device__ __forceinline__ void stage_entry(const Entry& E, int s, const Quarter
     s_rec[3 * s + 0] = make_float4(E.a.x, E.a.y, -0.5f * E.a.z, -E.a.w);
     s_rec[3 * s + 1] = make_float4(-0.5f * E.b.x, E.b.y, E.b.z, E.b.w);
     s_rec[3 * s + 2] = make_float4(E.c.x, 0.f, 0.f, 0.f);
-    s_mask[s] = (uint8_t)entry_mask(E, t, W, H);
+    s_mask[s] = (uint8_t)entry_mask<false>(E, t, W, H);
 }
 
-// The 4-bit sub-block mask of the lane's entry (see stage_entry).
+// Smallest value of Q(X, y) = A X^2 + 2 B X y + C y^2 over y in [y0, y1]
+// (C > 0, rC ~ 1/C); `mag` receives the sum of the magnitudes of its terms.
+// An approximate minimiser only raises the value by C times its error
+// squared, far below the widening of the test that uses it.
+__device__ __forceinline__ float conic_edge_min(float X, float y0, float y1, float A, float B, float C, float rC,
+                                                float& mag)
+{
+    const float ys = fminf(fmaxf(-(B * X) * rC, y0), y1);
+    const float t1 = A * X * X, t2 = 2.f * B * X * ys, t3 = C * ys * ys;
+    mag = fabsf(t1) + fabsf(t2) + t3;
+    return (t1 + t2) + t3;
+}
+
+// Whether the entry's alpha >= 1/255 region (Q(d) <= tau, d = pixel centre -
+// mean, conic (A, B, C)) meets the rectangle [x0, x1] x [y0, y1] of pixel
+// centres. The smallest Q over the rectangle lies on a side facing the mean
+// (or is 0 with the mean inside); the comparison is widened by 1e-5 of the
+// terms' magnitude so that rounding can only keep a sub-block, never drop one.
+__device__ __forceinline__ bool conic_meets_rect(float u, float v, float A, float B, float C, float tau, float x0,
+                                                 float x1, float y0, float y1)
+{
+    const float X0 = x0 - u, X1 = x1 - u, Y0 = y0 - v, Y1 = y1 - v;
+    if (X0 <= 0.f && X1 >= 0.f && Y0 <= 0.f && Y1 >= 0.f) return true;
+    float q = INFINITY, mag = 0.f, m;
+    if (X0 > 0.f || X1 < 0.f) {
+        q = conic_edge_min(X0 > 0.f ? X0 : X1, Y0, Y1, A, B, C, __builtin_amdgcn_rcpf(C), m);
+        mag = m;
+    }
+    if (Y0 > 0.f || Y1 < 0.f) {
+        const float qy = conic_edge_min(Y0 > 0.f ? Y0 : Y1, X0, X1, C, B, A, __builtin_amdgcn_rcpf(A), m);
+        if (qy < q) {
+            q = qy;
+            mag = m;
+        }
+    }
+    return q <= tau + 1e-5f * mag;
+}
+
+// The 4-bit sub-block mask of the lane's entry (see stage_entry): the
+// record's axis-aligned alpha extent box, then, with REFINE, the ellipse
+// itself against each remaining sub-block's rectangle of pixel centres (worth
+// its cost where a (row, entry) pair costs more than the test).
+template <bool REFINE>
 __device__ __forceinline__ uint32_t entry_mask(const Entry& E, const QuarterCtx& t, int W, int H)
 {
     uint32_t mask = 0;
     if (E.valid) {
         const float lo_x = E.a.x - E.c.y, hi_x = E.a.x + E.c.y, lo_y = E.a.y - E.c.z, hi_y = E.a.y + E.c.z;
+        float x0[2], x1[2], y0[2], y1[2];
         uint32_t xm = 0, ym = 0;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            const float x0 = (float)(t.qx0 + 4 * k) + 0.5f, x1 = (float)min(t.qx0 + 4 * k + 4, W) - 0.5f;
-            const float y0 = (float)(t.qy0 + 4 * k) + 0.5f, y1 = (float)min(t.qy0 + 4 * k + 4, H) - 0.5f;
-            xm |= (uint32_t)(hi_x >= x0 && lo_x <= x1) << k;
-            ym |= (uint32_t)(hi_y >= y0 && lo_y <= y1) << k;
+            x0[k] = (float)(t.qx0 + 4 * k) + 0.5f;
+            x1[k] = (float)min(t.qx0 + 4 * k + 4, W) - 0.5f;
+            y0[k] = (float)(t.qy0 + 4 * k) + 0.5f;
+            y1[k] = (float)min(t.qy0 + 4 * k + 4, H) - 0.5f;
+            xm |= (uint32_t)(hi_x >= x0[k] && lo_x <= x1[k]) << k;
+            ym |= (uint32_t)(hi_y >= y0[k] && lo_y <= y1[k]) << k;
         }
         mask = (xm & ym & 1u) | (((xm >> 1) & ym & 1u) << 1) | ((xm & (ym >> 1) & 1u) << 2) |
                (((xm >> 1) & (ym >> 1) & 1u) << 3);
+        if (REFINE && mask) {
+            // the threshold of the record's extent, widened a little more
+            const float tau = 2.f * __logf(255.f * E.b.y) * 1.004f + 0.02f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (((mask >> r) & 1u) &&
+                    !conic_meets_rect(E.a.x, E.a.y, E.a.z, E.a.w, E.b.x, tau, x0[r & 1], x1[r & 1], y0[r >> 1], y1[r >> 1]))
+                    mask &= ~(1u << r);
+            }
+        }
     }
     return mask;
 }
@@ -125,7 +181,7 @@ __device__ __forceinline__ void stage_entry_pair(const Entry& E, int s, const Qu
     s_rec[2 * s + 0] = make_float4(E.a.x, E.a.y, -0.5f * E.a.z, -E.a.w);
     s_rec[2 * s + 1] = make_float4(-0.5f * E.b.x, E.b.y, E.b.z, E.b.w);
     s_b[s] = E.c.x;
-    s_mask[s] = (uint8_t)entry_mask(E, t, W, H);
+    s_mask[s] = (uint8_t)entry_mask<true>(E, t, W, H);
 }
 
 // Per-row compaction of the 64 staged entries: for row r, the slots
