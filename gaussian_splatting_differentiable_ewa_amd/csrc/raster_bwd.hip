@@ -47,7 +47,7 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
     __shared__ float4 s_rec[2 * RW_BATCH];  // (u v -A/2 -B) (-C/2 o r g) per slot
     __shared__ float s_b[RW_BATCH];         // blue of each slot
     __shared__ uint8_t s_mask[RW_BATCH];
-    __shared__ uint16_t s_list[4 * RW_BATCH];
+    __shared__ __align__(16) uint16_t s_list[4 * RW_BATCH];  // read 8 ids at a time
     __shared__ float s_sum[GS_GRAD2D_ROWS][RW_BATCH];  // [gradient][slot], summed over the rows
     __shared__ float2 s_coef[4][16][CSTRIDE];          // [row][pixel][slot]
     __shared__ uint32_t s_gid[RW_BATCH];               // Gaussian of each staged slot
@@ -122,15 +122,32 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
         const uint32_t iters = max(max(cnt[0], cnt[1]), max(cnt[2], cnt[3]));
         const uint16_t* my_list = s_list + t.row * RW_BATCH;
         for (uint32_t sb = 0; sb < iters; sb += SUB) {
-            // ---- phase 1: this lane's pixel, entries sb .. sb+7 of its row
+            // ---- phase 1: this lane's pixel, entries sb .. sb+7 of its row.
+            // The eight slot ids come in one 16-byte read (ids past the row's
+            // count are stale and masked); each entry's record is read while
+            // the one before it is evaluated.
             const uint32_t n_sub = min((uint32_t)SUB, iters - sb);
-            for (uint32_t i = 0; i < n_sub; ++i) {
+            const uint4 ids = *(const uint4*)(my_list + sb);
+            const uint32_t idw[4] = {ids.x, ids.y, ids.z, ids.w};
+            int idx_n = sb < my_cnt ? (int)(idw[0] & 0xffffu) : 0;
+            float4 n0 = s_rec[2 * idx_n], n1 = s_rec[2 * idx_n + 1];
+            float nb = s_b[idx_n];
+#pragma unroll
+            for (uint32_t i = 0; i < (uint32_t)SUB; ++i) {
+                if (i >= n_sub) break;  // wave-uniform
                 const uint32_t it = sb + i;
                 const bool has = it < my_cnt;
-                const int idx = has ? (int)my_list[it] : 0;
+                const int idx = idx_n;
+                const float4 q0 = n0, q1 = n1;
+                const float qb = nb;
+                if (i + 1 < (uint32_t)SUB) {
+                    const bool hn = i + 1 < n_sub && it + 1 < my_cnt;
+                    idx_n = hn ? (int)((idw[(i + 1) >> 1] >> (16 * ((i + 1) & 1))) & 0xffffu) : 0;
+                    n0 = s_rec[2 * idx_n];
+                    n1 = s_rec[2 * idx_n + 1];
+                    nb = s_b[idx_n];
+                }
                 const int32_t pos = hi - idx;
-                const float4 q0 = s_rec[2 * idx], q1 = s_rec[2 * idx + 1];
-                const float qb = s_b[idx];
                 float dx, dy;
                 const float power = entry_power(q0, q1, t.px, t.py, dx, dy);
                 const float G = exp_fast(power);
