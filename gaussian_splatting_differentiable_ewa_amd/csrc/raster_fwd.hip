@@ -43,7 +43,7 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_fwd(const float* __restri
 #pragma clang fp contract(off)
     __shared__ float4 s_rec[3 * RW_BATCH];
     __shared__ uint8_t s_mask[RW_BATCH];
-    __shared__ uint16_t s_list[4 * RW_BATCH];
+    __shared__ __align__(16) uint16_t s_list[4 * RW_BATCH];  // read 8 ids at a time
     const QuarterCtx t = quarter_ctx(W, H, TX, T);
     if (t.empty) return;
     const uint2 rg = *(const uint2*)(ranges + 2 * (uint64_t)t.tile_lin);
@@ -72,35 +72,45 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_fwd(const float* __restri
         const uint32_t iters = max(max(cnt[0], cnt[1]), max(cnt[2], cnt[3]));
         const uint16_t* my_list = s_list + t.row * RW_BATCH;
         const int32_t pos0 = (int32_t)(base - rg.x) + 1;
-        // software pipeline: the next entry's slot and record are read from
-        // LDS while the current one is evaluated (exhausted rows idle on slot 0)
-        int idx_n = my_cnt > 0 ? (int)my_list[0] : 0;
-        float4 n0 = s_rec[3 * idx_n], n1 = s_rec[3 * idx_n + 1], n2 = s_rec[3 * idx_n + 2];
-        for (uint32_t it = 0; it < iters; ++it) {
-            const bool has = it < my_cnt;
-            const int idx = idx_n;
-            const float4 q0 = n0, q1 = n1, q2 = n2;
-            idx_n = it + 1 < my_cnt ? (int)my_list[it + 1] : 0;
-            n0 = s_rec[3 * idx_n];
-            n1 = s_rec[3 * idx_n + 1];
-            n2 = s_rec[3 * idx_n + 2];
-            // branch-free update: only lanes that blend change state (a zero
-            // weight adds exactly 0)
-            float dx, dy;
-            const float power = entry_power(q0, q1, t.px, t.py, dx, dy);
-            const float alpha = fminf(ALPHA_MAX, q1.y * exp_fast(power));
-            const float Tn = Tr * (1.f - alpha);
-            const bool keep = has && !done && !(power > 0.f) && !(alpha < ALPHA_MIN);
-            const bool stop = keep && Tn < T_MIN;
-            const bool blend = keep && !stop;
-            const float w = blend ? alpha * Tr : 0.f;
-            C0 = __builtin_fmaf(q1.z, w, C0);
-            C1 = __builtin_fmaf(q1.w, w, C1);
-            C2 = __builtin_fmaf(q2.x, w, C2);
-            Tr = blend ? Tn : Tr;
-            last = blend ? pos0 + idx : last;
-            done = done || stop;
-            if ((it & 3) == 3 && ballot(!done) == 0ull) break;
+        // groups of 8 entries: their slot ids in one 16-byte read (ids past
+        // the row's count are stale and masked); each record is read while
+        // the entry before it is evaluated (exhausted rows idle on slot 0)
+        for (uint32_t sb = 0; sb < iters; sb += 8) {
+            const uint4 ids = *(const uint4*)(my_list + sb);
+            const uint32_t idw[4] = {ids.x, ids.y, ids.z, ids.w};
+            int idx_n = sb < my_cnt ? (int)(idw[0] & 0xffffu) : 0;
+            float4 n0 = s_rec[3 * idx_n], n1 = s_rec[3 * idx_n + 1], n2 = s_rec[3 * idx_n + 2];
+#pragma unroll
+            for (uint32_t i = 0; i < 8u; ++i) {
+                const uint32_t it = sb + i;
+                if (it >= iters) break;  // wave-uniform
+                const bool has = it < my_cnt;
+                const int idx = idx_n;
+                const float4 q0 = n0, q1 = n1, q2 = n2;
+                if (i + 1 < 8u) {
+                    idx_n = it + 1 < my_cnt ? (int)((idw[(i + 1) >> 1] >> (16 * ((i + 1) & 1))) & 0xffffu) : 0;
+                    n0 = s_rec[3 * idx_n];
+                    n1 = s_rec[3 * idx_n + 1];
+                    n2 = s_rec[3 * idx_n + 2];
+                }
+                // branch-free update: only lanes that blend change state (a
+                // zero weight adds exactly 0)
+                float dx, dy;
+                const float power = entry_power(q0, q1, t.px, t.py, dx, dy);
+                const float alpha = fminf(ALPHA_MAX, q1.y * exp_fast(power));
+                const float Tn = Tr * (1.f - alpha);
+                const bool keep = has && !done && !(power > 0.f) && !(alpha < ALPHA_MIN);
+                const bool stop = keep && Tn < T_MIN;
+                const bool blend = keep && !stop;
+                const float w = blend ? alpha * Tr : 0.f;
+                C0 = __builtin_fmaf(q1.z, w, C0);
+                C1 = __builtin_fmaf(q1.w, w, C1);
+                C2 = __builtin_fmaf(q2.x, w, C2);
+                Tr = blend ? Tn : Tr;
+                last = blend ? pos0 + idx : last;
+                done = done || stop;
+            }
+            if (ballot(!done) == 0ull) break;
         }
         asm volatile("" ::: "memory");  // this batch's LDS reads precede the next staging
         cur = nxt;
