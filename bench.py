@@ -228,7 +228,7 @@ def main():
     # intersection statistics and a plain device copy for the achievable HBM rate
     rng_ = b.ranges.view(-1, 2).to(torch.int64)
     max_per_tile = int((rng_[:, 1] - rng_[:, 0]).max())
-    peak_list_bytes = 2 * 12 * b.capacity + b.sort_ws.numel()
+    peak_list_bytes = b.workspace_bytes()
     copy_gbs = copy_probe(torch, dev)
     cpu = None
     if not args.no_cpu_baseline:

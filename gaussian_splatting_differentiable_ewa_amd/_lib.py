@@ -27,7 +27,8 @@ GS_GRAD2D_ROWS = 9
 EXPORTS = (
     "gs_abi_version", "gs_status_string", "gs_param_rows", "gs_tiles_x", "gs_tiles_y",
     "gs_sort_end_bit", "gs_preprocess_workspace_bytes", "gs_sort_workspace_bytes",
-    "gs_preprocess", "gs_emit_intersections", "gs_sort_keys", "gs_tile_ranges",
+    "gs_tile_lists_workspace_bytes",
+    "gs_preprocess", "gs_emit_intersections", "gs_sort_keys", "gs_tile_lists", "gs_tile_ranges",
     "gs_rasterize_fwd", "gs_loss_l1", "gs_rasterize_bwd", "gs_preprocess_bwd", "gs_adam_step",
 )
 
@@ -68,10 +69,12 @@ def lib():
             "gs_sort_end_bit": ([_I32, _I64], _I32),
             "gs_preprocess_workspace_bytes": ([_I64, _I32], _SZ),
             "gs_sort_workspace_bytes": ([_U64], _SZ),
+            "gs_tile_lists_workspace_bytes": ([_I64, _I32, _I32, _I32, _U64], _SZ),
             "gs_preprocess": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
             "gs_emit_intersections": ([_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _U64, _P, _P], ctypes.c_int),
             "gs_sort_keys": ([_P, _P, _P, _P, _U64, _I32, _P, _SZ, _P, _P], ctypes.c_int),
             "gs_tile_ranges": ([_P, _U64, _I64, _P, _P], ctypes.c_int),
+            "gs_tile_lists": ([_P, _P, _I64, _I32, _I32, _I32, _P, _U64, _P, _P, _P, _SZ, _P], ctypes.c_int),
             "gs_rasterize_fwd": ([_P, _I64, _P, _P, _P, _I32, _P, _P, _P, _P, _P], ctypes.c_int),
             "gs_loss_l1": ([_P, _P, _I64, _F32, _P, _P, _I32, _P], ctypes.c_int),
             "gs_rasterize_bwd": ([_P, _I64, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _I32, _P], ctypes.c_int),
@@ -140,6 +143,10 @@ def sort_workspace_bytes(n_keys: int) -> int:
     return lib().gs_sort_workspace_bytes(n_keys)
 
 
+def tile_lists_workspace_bytes(n: int, n_views: int, width: int, height: int, capacity: int) -> int:
+    return lib().gs_tile_lists_workspace_bytes(n, n_views, width, height, capacity)
+
+
 # ---- the step ----------------------------------------------------------------
 def gs_preprocess(params, n, sh_degree, cams, rec, rect, offsets, total, ws, stream=None):
     cc = cameras(cams)
@@ -153,6 +160,12 @@ def gs_emit_intersections(rec, rect, offsets, n, n_views, width, height, keys, v
     _check(lib().gs_emit_intersections(_ptr(rec), _ptr(rect), _ptr(offsets), n, n_views, width, height,
                                        _ptr(keys), _ptr(vals), capacity, _ptr(overflow),
                                        _stream(stream)), "gs_emit_intersections")
+
+
+def gs_tile_lists(rec, rect, n, n_views, width, height, vals, capacity, ranges, overflow, ws, stream=None):
+    _check(lib().gs_tile_lists(_ptr(rec), _ptr(rect), n, n_views, width, height, _ptr(vals), capacity,
+                               _ptr(ranges), _ptr(overflow), _ptr(ws), ws.numel() * ws.element_size(),
+                               _stream(stream)), "gs_tile_lists")
 
 
 def gs_sort_keys(keys, vals, keys_alt, vals_alt, n_keys, end_bit, ws, stream=None) -> bool:

@@ -1,0 +1,562 @@
+// gs_tile_lists: the per-tile lists of Gaussian ids in depth order and their
+// ranges -- the same result as gs_emit_intersections + gs_sort_keys +
+// gs_tile_ranges (per-tile depth-sorted intersection lists, "AMD ROCm team
+// open-sources distributed 3D Gaussian Splatting training", section
+// "Distributed training architecture and memory scaling"), built by binning
+// instead of one global sort of 64-bit keys, with no global atomics:
+//   1. k_bin_count    workgroup (view, chunk of Gaussians, band of tile rows):
+//                     LDS counters of the band's tiles, one increment per
+//                     (Gaussian, tile); written as table[view][chunk][tile];
+//   2. k_bin_colscan  per (view, tile): exclusive prefix over the chunks (in
+//                     place) and the tile's total;
+//   3. prefix sum of the totals: each tile's first slot, i.e. its range
+//      (k_tl_ranges writes (0, 0) for empty tiles);
+//   4. k_bin_fill     the workgroups of step 1 again: LDS cursors start at
+//                     tile start + chunk prefix; each (Gaussian, tile) takes
+//                     the next slot (LDS atomic) and writes (depth bits, id);
+//   5. k_tl_sort_small one wave per tile of up to 64 entries: bitonic sort of
+//                     the 64-bit (depth bits, id) across the lanes;
+//      k_tl_sort      one workgroup per longer tile: stable LSD radix sort by
+//                     the 32 depth bits (8-bit digits; digits equal across the
+//                     tile are skipped), in LDS for up to 4096 entries and
+//                     through a global scratch copy beyond, then runs of equal
+//                     depth put in id order.
+// (depth, id) is a total order, so the arbitrary slot order of step 4 never
+// shows: the lists equal those of the global key sort. The positive fp32
+// depths order like their bit patterns.
+#include <algorithm>
+
+#include "internal.h"
+
+namespace gs {
+
+constexpr int TL_THREADS = 256;
+constexpr int TL_CAP = 4096;                    // entries a tile sorts in LDS
+constexpr int TL_ROUNDS = TL_CAP / TL_THREADS;  // rounds of 64 keys per wave, at most
+constexpr int GL_CHUNK = 4096;                  // entries per chunk of the global-memory path
+constexpr int GL_ROUNDS = GL_CHUNK / TL_THREADS;
+
+// the pair's tile rectangle, clipped to the tile grid
+__device__ __forceinline__ bool rect_of(const uint16_t* __restrict__ rect, int64_t idx, uint32_t tiles_x,
+                                        uint32_t tiles_y, uint32_t& x0, uint32_t& y0, uint32_t& x1, uint32_t& y1)
+{
+    const uint2 rr = *(const uint2*)(rect + 4 * idx);
+    x0 = rr.x & 0xffffu;
+    y0 = rr.x >> 16;
+    x1 = min(rr.y & 0xffffu, tiles_x);
+    y1 = min(rr.y >> 16, tiles_y);
+    return x1 > x0 && y1 > y0;
+}
+
+constexpr int BAND_TILES = 8192;  // LDS counters of one band of tile rows
+
+struct BinGrid {
+    int32_t tiles_x, tiles_y;
+    int64_t tiles;      // per view
+    int64_t n;          // Gaussians
+    int32_t chunks;     // chunks of Gaussians per view
+    int64_t chunk;      // Gaussians per chunk
+    int32_t band_rows;  // tile rows per band
+    int32_t bands;
+};
+
+// the workgroup's (view, chunk, band) and its Gaussians and tile rows
+struct BinBlock {
+    int64_t v, c, g0, g1;
+    uint32_t ty0, ty1;
+};
+
+__device__ __forceinline__ BinBlock bin_block(const BinGrid& G)
+{
+    BinBlock B;
+    const int64_t per_view = (int64_t)G.chunks * G.bands;
+    B.v = blockIdx.x / per_view;
+    const int64_t rem = blockIdx.x - B.v * per_view;
+    B.c = rem / G.bands;
+    const int64_t band = rem - B.c * G.bands;
+    B.g0 = B.c * G.chunk;
+    B.g1 = min(G.n, B.g0 + G.chunk);
+    B.ty0 = (uint32_t)(band * G.band_rows);
+    B.ty1 = min((uint32_t)G.tiles_y, B.ty0 + (uint32_t)G.band_rows);
+    return B;
+}
+
+// the pair's tile rectangle, clipped to the rows [ty0, ty1) and the grid
+__device__ __forceinline__ bool band_rect(const uint16_t* __restrict__ rect, int64_t idx, const BinGrid& G,
+                                          uint32_t ty0, uint32_t ty1, uint32_t& x0, uint32_t& y0, uint32_t& x1,
+                                          uint32_t& y1)
+{
+    const uint2 rr = *(const uint2*)(rect + 4 * idx);
+    x0 = rr.x & 0xffffu;
+    y0 = max(rr.x >> 16, ty0);
+    x1 = min(rr.y & 0xffffu, (uint32_t)G.tiles_x);
+    y1 = min(rr.y >> 16, ty1);
+    return x1 > x0 && y1 > y0;
+}
+
+__global__ __launch_bounds__(256) void k_bin_count(const uint16_t* __restrict__ rect, const BinGrid G,
+                                                   uint32_t* __restrict__ table)
+{
+    __shared__ uint32_t cnt[BAND_TILES];
+    const BinBlock B = bin_block(G);
+    const uint32_t nt = (B.ty1 - B.ty0) * (uint32_t)G.tiles_x;
+    for (uint32_t i = threadIdx.x; i < nt; i += 256) cnt[i] = 0u;
+    __syncthreads();
+    for (int64_t g = B.g0 + threadIdx.x; g < B.g1; g += 256) {
+        uint32_t x0, y0, x1, y1;
+        if (!band_rect(rect, B.v * G.n + g, G, B.ty0, B.ty1, x0, y0, x1, y1)) continue;
+        for (uint32_t ty = y0; ty < y1; ++ty)
+            for (uint32_t tx = x0; tx < x1; ++tx) atomicAdd(&cnt[(ty - B.ty0) * G.tiles_x + tx], 1u);
+    }
+    __syncthreads();
+    uint32_t* row = table + (B.v * G.chunks + B.c) * G.tiles + (int64_t)B.ty0 * G.tiles_x;
+    for (uint32_t i = threadIdx.x; i < nt; i += 256) row[i] = cnt[i];
+}
+
+__global__ __launch_bounds__(256) void k_bin_colscan(uint32_t* __restrict__ table, const BinGrid G, int32_t n_views,
+                                                     uint32_t* __restrict__ totals)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)n_views * G.tiles) return;
+    const int64_t v = i / G.tiles, tile = i - v * G.tiles;
+    uint32_t* col = table + v * G.chunks * G.tiles + tile;
+    uint32_t run = 0u;
+    for (int32_t c = 0; c < G.chunks; ++c) {
+        const uint32_t x = col[(int64_t)c * G.tiles];
+        col[(int64_t)c * G.tiles] = run;
+        run += x;
+    }
+    totals[i] = run;
+}
+
+__global__ __launch_bounds__(256) void k_tl_ranges(const uint32_t* __restrict__ starts, int64_t n_tiles,
+                                                   uint32_t* __restrict__ ranges)
+{
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= n_tiles) return;
+    const uint32_t s = starts[t], e = starts[t + 1];
+    *(uint2*)(ranges + 2 * t) = e > s ? make_uint2(s, e) : make_uint2(0u, 0u);
+}
+
+__global__ __launch_bounds__(256) void k_bin_fill(const float* __restrict__ rec, const uint16_t* __restrict__ rect,
+                                                  const BinGrid G, const uint32_t* __restrict__ table,
+                                                  const uint32_t* __restrict__ starts, uint2* __restrict__ pairs,
+                                                  uint64_t capacity, int32_t* __restrict__ overflow)
+{
+    __shared__ uint32_t cur[BAND_TILES];
+    const BinBlock B = bin_block(G);
+    const uint32_t nt = (B.ty1 - B.ty0) * (uint32_t)G.tiles_x;
+    const int64_t first = (int64_t)B.ty0 * G.tiles_x;
+    const uint32_t* row = table + (B.v * G.chunks + B.c) * G.tiles + first;
+    const uint32_t* st = starts + B.v * G.tiles + first;
+    for (uint32_t i = threadIdx.x; i < nt; i += 256) cur[i] = st[i] + row[i];
+    __syncthreads();
+    bool over = false;
+    for (int64_t g = B.g0 + threadIdx.x; g < B.g1; g += 256) {
+        const int64_t idx = B.v * G.n + g;
+        uint32_t x0, y0, x1, y1;
+        if (!band_rect(rect, idx, G, B.ty0, B.ty1, x0, y0, x1, y1)) continue;
+        const uint32_t zb = __float_as_uint(rec[idx * GS_REC_FLOATS + GS_REC_DEPTH]);
+        for (uint32_t ty = y0; ty < y1; ++ty)
+            for (uint32_t tx = x0; tx < x1; ++tx) {
+                const uint32_t pos = atomicAdd(&cur[(ty - B.ty0) * G.tiles_x + tx], 1u);
+                if (pos < capacity)
+                    pairs[pos] = make_uint2(zb, (uint32_t)g);
+                else
+                    over = true;
+            }
+    }
+    if (over) *overflow = 1;
+}
+
+// Tiles of up to 64 entries, one wave each: a bitonic sort of the 64-bit
+// values (depth bits << 32 | id) across the lanes (absent lanes hold the
+// largest value and sort last).
+__global__ __launch_bounds__(256) void k_tl_sort_small(const uint32_t* __restrict__ ranges, int64_t n_tiles,
+                                                       const uint64_t* __restrict__ total_dev, uint64_t capacity,
+                                                       const uint2* __restrict__ pairs, uint32_t* __restrict__ vals)
+{
+    const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (tile >= n_tiles) return;
+    const uint2 rg = *(const uint2*)(ranges + 2 * tile);
+    const uint64_t limit = min(capacity, *total_dev);
+    const uint32_t start = rg.x, end = (uint32_t)min((uint64_t)rg.y, limit);
+    if (end <= start || end - start > 64u) return;  // wave-uniform
+    const uint32_t n = end - start, lane = threadIdx.x & 63u;
+    uint64_t key = ~0ull;
+    if (lane < n) {
+        const uint2 p = pairs[start + lane];
+        key = ((uint64_t)p.x << 32) | p.y;
+    }
+    if (n > 1) {
+#pragma unroll
+        for (uint32_t k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+            for (uint32_t j = k >> 1; j > 0; j >>= 1) {
+                const uint32_t lo = __shfl_xor((uint32_t)key, (int)j), hi = __shfl_xor((uint32_t)(key >> 32), (int)j);
+                const uint64_t other = ((uint64_t)hi << 32) | lo;
+                const bool up = (lane & k) == 0u;          // this run sorts ascending
+                const bool take_min = ((lane & j) == 0u) == up;
+                key = take_min ? (other < key ? other : key) : (other > key ? other : key);
+            }
+        }
+    }
+    if (lane < n) vals[start + lane] = (uint32_t)key;
+}
+
+// lanes of the wave (among `valid`) whose 8-bit digit equals this lane's
+__device__ __forceinline__ uint64_t tl_peers(uint32_t d, uint64_t valid)
+{
+    uint64_t peers = valid;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const bool bit = (d >> b) & 1u;
+        const uint64_t m = ballot(bit);
+        peers &= bit ? m : ~m;
+    }
+    return peers;
+}
+
+// Exclusive prefix over the 256 values held one per thread: a scan within
+// each wave (shuffles), then the wave totals. Two barriers.
+__device__ __forceinline__ uint32_t tl_exclusive_256(uint32_t v, uint32_t* wsum)
+{
+    const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (uint32_t off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    uint32_t before = 0;
+    for (uint32_t k = 0; k < w; ++k) before += wsum[k];
+    __syncthreads();
+    return before + x - v;
+}
+
+// OR and AND of a value over the workgroup
+__device__ __forceinline__ void tl_or_and(uint32_t v_or, uint32_t v_and, uint32_t* s2, uint32_t& o, uint32_t& a)
+{
+    if (threadIdx.x == 0) {
+        s2[0] = 0u;
+        s2[1] = 0xffffffffu;
+    }
+    __syncthreads();
+    atomicOr(&s2[0], v_or);
+    atomicAnd(&s2[1], v_and);
+    __syncthreads();
+    o = s2[0];
+    a = s2[1];
+    __syncthreads();
+}
+
+// Orders each run of equal keys by Gaussian index (insertion sort by swaps;
+// runs are rare and short). Every run is handled by the thread that owns its
+// first element. less(a, b): item a's index is below item b's.
+template <typename KeyAt, typename ValAt, typename Less, typename Swap>
+__device__ __forceinline__ void tl_fix_ties(uint32_t n, KeyAt key_at, ValAt, Less less, Swap swap)
+{
+    for (uint32_t i = threadIdx.x; i + 1 < n; i += TL_THREADS) {
+        const uint32_t k = key_at(i);
+        if ((i > 0 && key_at(i - 1) == k) || key_at(i + 1) != k) continue;
+        uint32_t j = i + 1;
+        while (j < n && key_at(j) == k) ++j;
+        for (uint32_t a = i + 1; a < j; ++a)
+            for (uint32_t b = a; b > i && less(b, b - 1); --b) swap(b, b - 1);
+    }
+}
+
+__global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restrict__ ranges,
+                                                        const uint64_t* __restrict__ total_dev, uint64_t capacity,
+                                                        uint2* __restrict__ pairs, uint2* __restrict__ alt,
+                                                        uint32_t* __restrict__ vals)
+{
+    __shared__ uint32_t s_key[TL_CAP];
+    __shared__ uint16_t s_idx[TL_CAP];  // position of each key in the tile's unsorted pairs
+    __shared__ uint32_t wcnt[4][256];
+    __shared__ uint32_t s_misc[8];
+    const uint2 rg = *(const uint2*)(ranges + 2 * (uint64_t)blockIdx.x);
+    const uint64_t limit = min(capacity, *total_dev);
+    const uint32_t start = rg.x, end = (uint32_t)min((uint64_t)rg.y, limit);
+    if (end <= start) return;
+    const uint32_t n = end - start;
+    const uint32_t t = threadIdx.x, lane = t & 63u, wave = t >> 6;
+    if (n <= 64u) return;  // k_tl_sort_small
+    if (n <= (uint32_t)TL_CAP) {
+        // wave w holds the contiguous run [w L, (w + 1) L), L = 64 R
+        const uint32_t R = (n + TL_THREADS - 1) / TL_THREADS;
+        const uint32_t wbeg = wave * 64u * R;
+        uint32_t key[TL_ROUNDS], idx[TL_ROUNDS], rank[TL_ROUNDS];
+        uint32_t kor = 0u, kand = 0xffffffffu;
+#pragma unroll
+        for (int r = 0; r < TL_ROUNDS; ++r) {
+            const uint32_t i = wbeg + (uint32_t)r * 64u + lane;
+            const bool valid = (uint32_t)r < R && i < n;
+            const uint2 p = valid ? pairs[start + i] : make_uint2(0u, 0u);
+            key[r] = p.x;
+            idx[r] = i;
+            if (valid) {
+                kor |= p.x;
+                kand &= p.x;
+                s_key[i] = p.x;
+                s_idx[i] = (uint16_t)i;
+            }
+        }
+        uint32_t o, a;
+        tl_or_and(kor, kand, s_misc, o, a);
+        const uint32_t differ = o ^ a;  // bits that are not equal across the tile
+        for (int shift = 0; shift < 32; shift += 8) {
+            if (((differ >> shift) & 255u) == 0u) continue;  // uniform digit: order unchanged
+#pragma unroll
+            for (int w = 0; w < 4; ++w) wcnt[w][t] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < TL_ROUNDS; ++r) {
+                if ((uint32_t)r >= R) break;  // uniform across the workgroup
+                const uint32_t i = wbeg + (uint32_t)r * 64u + lane;
+                const bool valid = i < n;
+                const uint32_t d = (key[r] >> shift) & 255u;
+                const uint64_t peers = tl_peers(d, ballot(valid));
+                const uint32_t below = mask_rank(peers);
+                const uint32_t prior = wcnt[wave][d];
+                rank[r] = prior + below;
+                asm volatile("" ::: "memory");  // every lane has read the counter
+                if (valid && below == 0u) wcnt[wave][d] = prior + (uint32_t)__popcll(peers);
+                asm volatile("" ::: "memory");
+            }
+            __syncthreads();
+            {
+                const uint32_t c0 = wcnt[0][t], c1 = wcnt[1][t], c2 = wcnt[2][t], c3 = wcnt[3][t];
+                const uint32_t lo = tl_exclusive_256(c0 + c1 + c2 + c3, s_misc);
+                wcnt[0][t] = lo;
+                wcnt[1][t] = lo + c0;
+                wcnt[2][t] = lo + c0 + c1;
+                wcnt[3][t] = lo + c0 + c1 + c2;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < TL_ROUNDS; ++r) {
+                if ((uint32_t)r >= R) break;
+                const uint32_t i = wbeg + (uint32_t)r * 64u + lane;
+                if (i < n) {
+                    const uint32_t pos = wcnt[wave][(key[r] >> shift) & 255u] + rank[r];
+                    s_key[pos] = key[r];
+                    s_idx[pos] = (uint16_t)idx[r];
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < TL_ROUNDS; ++r) {
+                if ((uint32_t)r >= R) break;
+                const uint32_t i = wbeg + (uint32_t)r * 64u + lane;
+                if (i < n) {
+                    key[r] = s_key[i];
+                    idx[r] = s_idx[i];
+                }
+            }
+        }
+        __syncthreads();
+        // equal depths: order the run's items by Gaussian index
+        const uint2* tp = pairs + start;
+        tl_fix_ties(
+            n, [&](uint32_t i) { return s_key[i]; }, [&](uint32_t i) { return tp[s_idx[i]].y; },
+            [&](uint32_t i, uint32_t a) { return tp[s_idx[i]].y < tp[s_idx[a]].y; },
+            [&](uint32_t i, uint32_t a) { const uint16_t x = s_idx[i]; s_idx[i] = s_idx[a]; s_idx[a] = x; });
+        __syncthreads();
+        for (uint32_t i = t; i < n; i += TL_THREADS) vals[start + i] = tp[s_idx[i]].y;
+        return;
+    }
+
+    // a list longer than the LDS holds: the same passes over global memory,
+    // chunk by chunk (chunks in order keep the sort stable), ping-ponging
+    // between the pairs and a scratch copy of the same slots
+    uint2* src = pairs + start;
+    uint2* dst = alt + start;
+    uint32_t kor = 0u, kand = 0xffffffffu;
+    for (uint32_t i = t; i < n; i += TL_THREADS) {
+        const uint32_t k = src[i].x;
+        kor |= k;
+        kand &= k;
+    }
+    uint32_t o, a;
+    tl_or_and(kor, kand, s_misc, o, a);
+    const uint32_t differ = o ^ a;
+    uint32_t* hist = &wcnt[0][0];        // [256] digit totals of the list
+    uint32_t* running = &wcnt[1][0];     // [256] next free slot of each digit
+    uint32_t(*cw)[256] = (uint32_t(*)[256])s_key;  // [4][256] per-wave counts of a chunk
+    for (int shift = 0; shift < 32; shift += 8) {
+        if (((differ >> shift) & 255u) == 0u) continue;
+        hist[t] = 0u;
+        __syncthreads();
+        for (uint32_t base = 0; base < n; base += TL_THREADS) {
+            const uint32_t i = base + t;
+            const bool valid = i < n;
+            const uint32_t d = valid ? (src[i].x >> shift) & 255u : 0u;
+            const uint64_t peers = tl_peers(d, ballot(valid));
+            if (valid && mask_rank(peers) == 0u) atomicAdd(&hist[d], (uint32_t)__popcll(peers));
+        }
+        __syncthreads();
+        running[t] = tl_exclusive_256(hist[t], s_misc);
+        __syncthreads();
+        for (uint32_t base = 0; base < n; base += (uint32_t)GL_CHUNK) {
+            // chunk [base, base + 4096): wave w ranks its run of 1024
+#pragma unroll
+            for (int w = 0; w < 4; ++w) cw[w][t] = 0u;
+            __syncthreads();
+            uint2 item[GL_ROUNDS];
+            uint32_t rk[GL_ROUNDS];
+#pragma unroll
+            for (int r = 0; r < GL_ROUNDS; ++r) {
+                const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
+                const bool valid = i < n;
+                item[r] = valid ? src[i] : make_uint2(0u, 0u);
+                const uint32_t d = (item[r].x >> shift) & 255u;
+                const uint64_t peers = tl_peers(d, ballot(valid));
+                const uint32_t below = mask_rank(peers);
+                const uint32_t prior = cw[wave][d];
+                rk[r] = prior + below;
+                asm volatile("" ::: "memory");
+                if (valid && below == 0u) cw[wave][d] = prior + (uint32_t)__popcll(peers);
+                asm volatile("" ::: "memory");
+            }
+            __syncthreads();
+            {
+                const uint32_t c0 = cw[0][t], c1 = cw[1][t], c2 = cw[2][t], c3 = cw[3][t];
+                const uint32_t b0 = running[t];
+                cw[0][t] = b0;
+                cw[1][t] = b0 + c0;
+                cw[2][t] = b0 + c0 + c1;
+                cw[3][t] = b0 + c0 + c1 + c2;
+                running[t] = b0 + c0 + c1 + c2 + c3;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < GL_ROUNDS; ++r) {
+                const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
+                if (i < n) {
+                    const uint32_t pos = cw[wave][(item[r].x >> shift) & 255u] + rk[r];
+                    if (pos < n) dst[pos] = item[r];
+                }
+            }
+            __syncthreads();
+        }
+        uint2* tmp = src;
+        src = dst;
+        dst = tmp;
+    }
+    tl_fix_ties(
+        n, [&](uint32_t i) { return src[i].x; }, [&](uint32_t i) { return src[i].y; },
+        [&](uint32_t i, uint32_t a) { return src[i].y < src[a].y; },
+        [&](uint32_t i, uint32_t a) { const uint32_t x = src[i].y; src[i].y = src[a].y; src[a].y = x; });
+    __syncthreads();
+    for (uint32_t i = t; i < n; i += TL_THREADS) vals[start + i] = src[i].y;
+}
+
+// workspace: table [V][chunks][T] | totals [V T + 1] | total (u64) | scan
+// workspace | pairs [capacity] | scratch pairs [capacity]
+struct TlLayout {
+    size_t table, totals, total, scan, pairs, alt, bytes;
+};
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Chunks per view: about 4M table entries in all, at least 1024 Gaussians
+// per chunk.
+static BinGrid bin_grid(int64_t n, int32_t n_views, int32_t width, int32_t height)
+{
+    BinGrid G;
+    G.tiles_x = gs_tiles_x(width);
+    G.tiles_y = gs_tiles_y(height);
+    G.tiles = (int64_t)G.tiles_x * G.tiles_y;
+    G.n = n;
+    const int64_t by_table = std::max<int64_t>(1, ((int64_t)1 << 22) / std::max<int64_t>(1, G.tiles * n_views));
+    const int64_t by_size = std::max<int64_t>(1, (n + 1023) / 1024);
+    G.chunks = (int32_t)std::min<int64_t>(by_table, by_size);
+    G.chunk = std::max<int64_t>(1, (n + G.chunks - 1) / G.chunks);
+    G.band_rows = std::max<int32_t>(1, std::min<int32_t>(G.tiles_y, BAND_TILES / G.tiles_x));
+    G.bands = (G.tiles_y + G.band_rows - 1) / G.band_rows;
+    return G;
+}
+
+static TlLayout tl_layout(const BinGrid& G, int32_t n_views, uint64_t capacity)
+{
+    const uint64_t n_tiles = (uint64_t)G.tiles * n_views;
+    TlLayout L;
+    L.table = 0;
+    L.totals = align256((size_t)n_tiles * G.chunks * 4);
+    L.total = L.totals + align256((n_tiles + 1) * 4);
+    L.scan = L.total + 256;
+    L.pairs = L.scan + align256(scan_workspace_bytes(n_tiles));
+    L.alt = L.pairs + align256(capacity * 8);
+    L.bytes = L.alt + align256(capacity * 8);
+    return L;
+}
+
+static bool tl_sizes_ok(int64_t n, int32_t n_views, int32_t width, int32_t height)
+{
+    if (n < 0 || n_views < 1 || n_views > GS_MAX_VIEWS || width <= 0 || height <= 0) return false;
+    if (gs_tiles_x(width) > BAND_TILES || gs_tiles_y(height) > 65535) return false;
+    return (int64_t)gs_tiles_x(width) * gs_tiles_y(height) * n_views < ((int64_t)1 << 31);
+}
+
+}  // namespace gs
+
+using namespace gs;
+
+extern "C" {
+
+size_t gs_tile_lists_workspace_bytes(int64_t n, int32_t n_views, int32_t width, int32_t height, uint64_t capacity)
+{
+    if (!tl_sizes_ok(n, n_views, width, height)) return 0;
+    return tl_layout(bin_grid(n, n_views, width, height), n_views, capacity).bytes;
+}
+
+gs_status gs_tile_lists(const float* rec, const uint16_t* rect, int64_t n, int32_t n_views, int32_t width,
+                        int32_t height, uint32_t* vals, uint64_t capacity, uint32_t* ranges, int32_t* overflow,
+                        void* ws, size_t ws_bytes, void* stream)
+{
+    if (!tl_sizes_ok(n, n_views, width, height)) return GS_ERR_INVALID_ARGUMENT;
+    if (!ranges || !overflow || !ws) return GS_ERR_INVALID_ARGUMENT;
+    if (n > 0 && (!rec || !rect)) return GS_ERR_INVALID_ARGUMENT;
+    if (capacity > 0 && !vals) return GS_ERR_INVALID_ARGUMENT;
+    if (capacity >= ((uint64_t)1 << 32)) return GS_ERR_INVALID_ARGUMENT;
+    const BinGrid G = bin_grid(n, n_views, width, height);
+    const TlLayout L = tl_layout(G, n_views, capacity);
+    if (ws_bytes < L.bytes) return GS_ERR_INVALID_ARGUMENT;
+    const int64_t n_tiles = G.tiles * n_views;
+    char* w = (char*)ws;
+    uint32_t* table = (uint32_t*)(w + L.table);
+    uint32_t* totals = (uint32_t*)(w + L.totals);
+    uint64_t* total = (uint64_t*)(w + L.total);
+    uint2* pairs = (uint2*)(w + L.pairs);
+    uint2* alt = (uint2*)(w + L.alt);
+    hipStream_t s = (hipStream_t)stream;
+    if (fill_u32((uint32_t*)overflow, 1, 0u, s) != hipSuccess) return GS_ERR_HIP;
+    const unsigned bin_blocks = (unsigned)((int64_t)n_views * G.chunks * G.bands);
+    if (n > 0) {
+        hipLaunchKernelGGL(k_bin_count, dim3(bin_blocks), dim3(256), 0, s, rect, G, table);
+        if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
+    } else if (fill_u32(table, (uint64_t)n_tiles * G.chunks, 0u, s) != hipSuccess) {
+        return GS_ERR_HIP;
+    }
+    hipLaunchKernelGGL(k_bin_colscan, dim3(grid_for((uint64_t)n_tiles, 256)), dim3(256), 0, s, table, G, n_views,
+                       totals);
+    if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
+    if (scan_u32(totals, totals, (uint64_t)n_tiles, total, w + L.scan, s) != hipSuccess) return GS_ERR_HIP;
+    hipLaunchKernelGGL(k_tl_ranges, dim3(grid_for((uint64_t)n_tiles, 256)), dim3(256), 0, s, totals, n_tiles, ranges);
+    if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
+    if (n == 0) return GS_OK;
+    hipLaunchKernelGGL(k_bin_fill, dim3(bin_blocks), dim3(256), 0, s, rec, rect, G, table, totals, pairs, capacity,
+                       overflow);
+    if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
+    hipLaunchKernelGGL(k_tl_sort_small, dim3(grid_for((uint64_t)n_tiles, 4)), dim3(256), 0, s, ranges, n_tiles, total,
+                       capacity, pairs, vals);
+    if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
+    hipLaunchKernelGGL(k_tl_sort, dim3((unsigned)n_tiles), dim3(TL_THREADS), 0, s, ranges, total, capacity, pairs,
+                       alt, vals);
+    return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
+}
+
+}  // extern "C"

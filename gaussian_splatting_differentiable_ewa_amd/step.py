@@ -2,8 +2,13 @@
 
 PyTorch only allocates device memory and provides the stream; every stage is a
 call into the HIP library (``_lib``). The only device-to-host transfer per step
-is the intersection count K, read after ``gs_preprocess`` to size the key
+is the intersection count K, read after ``gs_preprocess`` to size the list
 buffers (they are kept and only grown).
+
+The per-tile lists come from ``gs_tile_lists`` (binning, then a sort of each
+tile on its own) unless ``lists="radix"`` selects the global 64-bit key path
+(``gs_emit_intersections``, ``gs_sort_keys``, ``gs_tile_ranges``); both give
+the same ids and ranges.
 """
 
 from __future__ import annotations
@@ -18,7 +23,10 @@ from . import _lib as L
 class Buffers:
     """Device buffers of one step for N Gaussians and a set of same-size views."""
 
-    def __init__(self, n: int, sh_degree: int, cams: Sequence, device="cuda"):
+    def __init__(self, n: int, sh_degree: int, cams: Sequence, device="cuda", lists: str = "binned"):
+        if lists not in ("binned", "radix"):
+            raise ValueError(f"unknown list builder {lists!r}")
+        self.lists = lists
         self.n = int(n)
         self.sh_degree = int(sh_degree)
         self.cams = list(cams)
@@ -53,12 +61,24 @@ class Buffers:
             return
         cap = int(K * slack) + 4096
         dev = self.device
-        self.keys = torch.empty(cap, dtype=torch.int64, device=dev)
         self.vals = torch.empty(cap, dtype=torch.int32, device=dev)
-        self.keys_alt = torch.empty(cap, dtype=torch.int64, device=dev)
-        self.vals_alt = torch.empty(cap, dtype=torch.int32, device=dev)
-        self.sort_ws = torch.empty(L.sort_workspace_bytes(cap), dtype=torch.uint8, device=dev)
+        if self.lists == "radix":
+            self.keys = torch.empty(cap, dtype=torch.int64, device=dev)
+            self.keys_alt = torch.empty(cap, dtype=torch.int64, device=dev)
+            self.vals_alt = torch.empty(cap, dtype=torch.int32, device=dev)
+            self.sort_ws = torch.empty(L.sort_workspace_bytes(cap), dtype=torch.uint8, device=dev)
+        else:
+            self.tl_ws = torch.empty(L.tile_lists_workspace_bytes(self.n, self.V, self.W, self.H, cap), dtype=torch.uint8,
+                                     device=dev)
         self.capacity = cap
+
+    def workspace_bytes(self) -> int:
+        """Bytes of the intersection lists and their workspaces."""
+        if self.capacity == 0:
+            return 0
+        if self.lists == "radix":
+            return 2 * 12 * self.capacity + self.sort_ws.numel()
+        return 4 * self.capacity + self.tl_ws.numel()
 
     @property
     def sorted_keys(self):
@@ -74,11 +94,16 @@ class Buffers:
                         self.total, self.pre_ws)
 
     def intersections(self):
-        """Read K, then emit, sort and range the keys."""
+        """Read K, then build the per-tile lists and their ranges."""
         self.K = int(self.total.item())
         if self.K >= 2 ** 32:
             raise L.GsError(f"{self.K} intersections exceed the 32-bit key index")
         self.ensure_capacity(self.K)
+        if self.lists == "binned":
+            self.sorted_in_alt = False
+            L.gs_tile_lists(self.rec, self.rect, self.n, self.V, self.W, self.H, self.vals, self.capacity,
+                            self.ranges, self.overflow, self.tl_ws)
+            return
         L.gs_emit_intersections(self.rec, self.rect, self.offsets, self.n, self.V, self.W, self.H,
                                 self.keys, self.vals, self.capacity, self.overflow)
         self.sorted_in_alt = L.gs_sort_keys(self.keys, self.vals, self.keys_alt, self.vals_alt, self.K,

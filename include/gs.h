@@ -190,6 +190,34 @@ gs_status gs_sort_keys(uint64_t* keys, uint32_t* vals, uint64_t* keys_alt, uint3
                        uint64_t n_keys, int32_t end_bit, void* ws, size_t ws_bytes,
                        int32_t* result_in_alt, void* stream);
 
+/* Workspace of gs_tile_lists (bytes) for n Gaussians and a list capacity; 0 on
+ * invalid sizes. */
+size_t gs_tile_lists_workspace_bytes(int64_t n, int32_t n_views, int32_t width, int32_t height,
+                                     uint64_t capacity);
+
+/*
+ * gs_tile_lists -- the per-tile intersection lists in depth order and their
+ * ranges in one call: the same vals and ranges as gs_emit_intersections,
+ * gs_sort_keys and gs_tile_ranges together (the per-tile depth-sorted lists
+ * of the ROCm page, section "Distributed training architecture and memory
+ * scaling"), built by counting each tile's intersections (LDS counters per
+ * chunk of Gaussians), scanning the counts into ranges, filling every tile's
+ * slots and sorting each tile's slots by (depth, Gaussian index) on its own.
+ *   rec, rect, n, n_views, width, height   as for gs_emit_intersections
+ *   vals       device out [capacity]: Gaussian ids, tile by tile, front to back
+ *   capacity   slots in vals (>= the total of gs_preprocess; < 2^32)
+ *   ranges     device out [n_views * tiles][2]: [start, end), (0, 0) if empty
+ *   overflow   device int32: cleared, then set to 1 if the intersections
+ *              exceed capacity (vals then incomplete)
+ *   ws         device workspace of gs_tile_lists_workspace_bytes(...)
+ * Errors: as gs_emit_intersections, plus a small workspace, capacity >= 2^32
+ * or more than 8192 tile columns.
+ */
+gs_status gs_tile_lists(const float* rec, const uint16_t* rect, int64_t n, int32_t n_views,
+                        int32_t width, int32_t height, uint32_t* vals, uint64_t capacity,
+                        uint32_t* ranges, int32_t* overflow, void* ws, size_t ws_bytes,
+                        void* stream);
+
 /*
  * gs_tile_ranges -- for every (view, tile) id t = key >> 32, the range
  * [start, end) of its keys in the sorted list; (0, 0) when it has none.

@@ -50,17 +50,27 @@ def gpu_forward(params_np: np.ndarray, sh: int, cams, bg=(0.0, 0.0, 0.0)):
            "rect": np_(b.rect).view(np.uint16).reshape(b.V, b.n, 4).astype(np.int32),
            "offsets": np_(b.offsets).view(np.uint32).astype(np.uint64),
            "total": int(np_(b.total)[0])}
+    # the global key path first (its keys are checked too), then the binned
+    # path the step uses; the raster runs on the binned lists
+    br = Buffers(p.shape[1], sh, cams, device=dev, lists="radix")
+    br.rec, br.rect, br.offsets, br.total = b.rec, b.rect, b.offsets, b.total
+    br.intersections()
+    torch.cuda.synchronize()
+    K = br.K
+    out["keys"] = np_(br.sorted_keys[:K]).view(np.uint64)
+    out["vals"] = np_(br.sorted_vals[:K]).view(np.uint32)
+    out["ranges"] = np_(br.ranges).view(np.uint32).reshape(-1, 2)
+    out["overflow"] = int(np_(br.overflow)[0])
+    del br
     b.intersections()
     b.rasterize(bg)
     torch.cuda.synchronize()
-    K = b.K
-    out["keys"] = np_(b.sorted_keys[:K]).view(np.uint64)
-    out["vals"] = np_(b.sorted_vals[:K]).view(np.uint32)
-    out["ranges"] = np_(b.ranges).view(np.uint32).reshape(-1, 2)
+    out["binned_vals"] = np_(b.sorted_vals[:K]).view(np.uint32)
+    out["binned_ranges"] = np_(b.ranges).view(np.uint32).reshape(-1, 2)
+    out["binned_overflow"] = int(np_(b.overflow)[0])
     out["image"] = np_(b.image)
     out["T_final"] = np_(b.T_final)
     out["n_contrib"] = np_(b.n_contrib)
-    out["overflow"] = int(np_(b.overflow)[0])
     return b, out
 
 
@@ -151,6 +161,10 @@ def check_keys(gpu, cams):
     assert np.array_equal(gpu["vals"], vals), "sorted ids differ"
     rng = O.tile_ranges(keys, V * cams[0].n_tiles)
     assert np.array_equal(gpu["ranges"], rng), "tile ranges differ"
+    # the binned lists: the same ids and ranges
+    assert gpu["binned_overflow"] == 0
+    assert np.array_equal(gpu["binned_vals"], vals), "binned lists differ"
+    assert np.array_equal(gpu["binned_ranges"], rng), "binned ranges differ"
     return keys.size
 
 

@@ -1,0 +1,72 @@
+"""gs_tile_lists through the C ABI against the oracle's emission and library
+sort (ordered by tile, depth bits, Gaussian index) on synthetic rectangles
+and depths built to stress it: many equal depths (the order of equal depths
+is decided by the index), tiles with more entries than one workgroup sorts
+in LDS (4096), empty tiles and views, and a capacity with slack."""
+
+import numpy as np
+import pytest
+
+from gaussian_splatting_differentiable_ewa_amd import _lib as L
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+W, H = 256, 192  # 16 x 12 tiles
+
+
+def _scene(seed, n, V, big_share, depth_levels):
+    rng = np.random.default_rng(seed)
+    TX, TY = (W + 15) // 16, (H + 15) // 16
+    rect = np.zeros((V, n, 4), np.int32)
+    for v in range(V):
+        x0 = rng.integers(0, TX, n)
+        y0 = rng.integers(0, TY, n)
+        w = rng.integers(0, 4, n)  # width 0 culls the Gaussian in this view
+        h = rng.integers(1, 4, n)
+        big = rng.random(n) < big_share[v]
+        x0[big], y0[big], w[big], h[big] = 0, 0, TX, TY
+        rect[v, :, 0], rect[v, :, 1] = x0, y0
+        rect[v, :, 2], rect[v, :, 3] = np.minimum(x0 + w, TX), np.minimum(y0 + h, TY)
+    vis = ((rect[..., 2] > rect[..., 0]) & (rect[..., 3] > rect[..., 1])).astype(np.uint8)
+    if depth_levels:
+        z = rng.choice(np.linspace(0.5, 60.0, depth_levels).astype(np.float32), (V, n))
+    else:
+        z = rng.uniform(0.02, 200.0, (V, n)).astype(np.float32)
+    rec = np.zeros((V, n, L.GS_REC_FLOATS), np.float32)
+    rec[..., L.REC_DEPTH] = z
+    return rect, vis, z.astype(np.float32), rec, TX, TY
+
+
+CASES = [
+    # seed, n, views, share of whole-image rectangles per view, depth levels
+    (1, 3000, 1, (0.0,), 0),
+    (2, 3000, 2, (0.0, 0.0), 12),        # heavy ties
+    (3, 9000, 2, (0.6, 0.0), 0),         # view 0: every tile > 4096 entries
+    (4, 9000, 2, (0.55, 0.02), 7),       # long lists with heavy ties
+    (5, 500, 3, (0.0, 1.0, 0.0), 3),     # every Gaussian in every tile of view 1
+]
+
+
+@pytest.mark.parametrize("seed,n,V,big,levels", CASES)
+def test_tile_lists_match_oracle(seed, n, V, big, levels):
+    import torch
+    dev = torch.device("cuda:0")
+    rect, vis, z, rec, TX, TY = _scene(seed, n, V, big, levels)
+    rect[vis == 0] = 0  # culled pairs carry an empty rectangle, as preprocess writes them
+    keys, vals = O.emit_sorted(rect, vis, z, TX, TY)
+    ranges = O.tile_ranges(keys, V * TX * TY)
+    K = vals.size
+    print(f"[tile_lists] seed {seed}: K {K}, longest list {int((ranges[:, 1] - ranges[:, 0]).max())}", flush=True)
+    rec_t = torch.from_numpy(rec.reshape(-1)).to(dev)
+    rect_t = torch.from_numpy(rect.astype(np.int16).reshape(-1)).to(dev)
+    for cap in (K, K + 1000):
+        out = torch.full((max(cap, 1),), -1, dtype=torch.int32, device=dev)
+        rng_t = torch.full((V * TX * TY * 2,), -1, dtype=torch.int32, device=dev)
+        ovf = torch.full((1,), 5, dtype=torch.int32, device=dev)
+        ws = torch.empty(L.tile_lists_workspace_bytes(n, V, W, H, cap), dtype=torch.uint8, device=dev)
+        L.gs_tile_lists(rec_t, rect_t, n, V, W, H, out, cap, rng_t, ovf, ws)
+        torch.cuda.synchronize()
+        assert int(ovf.item()) == 0
+        assert np.array_equal(out.cpu().numpy()[:K].view(np.uint32), vals)
+        assert np.array_equal(rng_t.cpu().numpy().view(np.uint32).reshape(-1, 2), ranges)
