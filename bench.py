@@ -242,7 +242,8 @@ def main():
                    "width": W, "height": H},
         "mpix_per_s": round(mpix, 2),
         "step_hbm_fraction": round(frac_step, 4), "step_algorithmic_bytes": int(step_bytes),
-        "intersections": b.K, "k_per_gaussian": round(b.K / b.n, 4), "visible_per_view": n_vis,
+        "intersections": b.K, "k_per_gaussian": round(b.K / b.n, 4), "list_builder": b.path,
+        "visible_per_view": n_vis,
         "max_per_tile": max_per_tile, "peak_intersection_bytes": int(peak_list_bytes),
         "hbm_copy_gbs": round(copy_gbs, 1),
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},

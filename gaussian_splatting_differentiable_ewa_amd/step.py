@@ -6,9 +6,11 @@ is the intersection count K, read after ``gs_preprocess`` to size the list
 buffers (they are kept and only grown).
 
 The per-tile lists come from ``gs_tile_lists`` (binning, then a sort of each
-tile on its own) unless ``lists="radix"`` selects the global 64-bit key path
-(``gs_emit_intersections``, ``gs_sort_keys``, ``gs_tile_ranges``); both give
-the same ids and ranges.
+tile on its own) or from the global 64-bit key path (``gs_emit_intersections``,
+``gs_sort_keys``, ``gs_tile_ranges``); both give the same ids and ranges.
+``lists="auto"`` picks binning unless the (view, Gaussian) pairs outnumber the
+intersections (a large scene mostly outside the views, where binning's two
+passes over every pair cost more than the sort).
 """
 
 from __future__ import annotations
@@ -23,10 +25,11 @@ from . import _lib as L
 class Buffers:
     """Device buffers of one step for N Gaussians and a set of same-size views."""
 
-    def __init__(self, n: int, sh_degree: int, cams: Sequence, device="cuda", lists: str = "binned"):
-        if lists not in ("binned", "radix"):
+    def __init__(self, n: int, sh_degree: int, cams: Sequence, device="cuda", lists: str = "auto"):
+        if lists not in ("auto", "binned", "radix"):
             raise ValueError(f"unknown list builder {lists!r}")
         self.lists = lists
+        self.path = "binned" if lists == "auto" else lists
         self.n = int(n)
         self.sh_degree = int(sh_degree)
         self.cams = list(cams)
@@ -52,17 +55,19 @@ class Buffers:
         self.overflow = torch.zeros(1, dtype=torch.int32, device=dev)
         self.end_bit = L.sort_end_bit(V, self.T)
         self.capacity = 0
+        self.allocated_for = None
         self.K = 0
         self.sorted_in_alt = False
         self.device = dev
 
     def ensure_capacity(self, K: int, slack: float = 1.25):
-        if K <= self.capacity and self.capacity > 0:
+        if K <= self.capacity and self.capacity > 0 and self.allocated_for == self.path:
             return
-        cap = int(K * slack) + 4096
+        cap = max(int(K * slack) + 4096, self.capacity)
         dev = self.device
         self.vals = torch.empty(cap, dtype=torch.int32, device=dev)
-        if self.lists == "radix":
+        self.allocated_for = self.path
+        if self.path == "radix":
             self.keys = torch.empty(cap, dtype=torch.int64, device=dev)
             self.keys_alt = torch.empty(cap, dtype=torch.int64, device=dev)
             self.vals_alt = torch.empty(cap, dtype=torch.int32, device=dev)
@@ -76,7 +81,7 @@ class Buffers:
         """Bytes of the intersection lists and their workspaces."""
         if self.capacity == 0:
             return 0
-        if self.lists == "radix":
+        if self.path == "radix":
             return 2 * 12 * self.capacity + self.sort_ws.numel()
         return 4 * self.capacity + self.tl_ws.numel()
 
@@ -98,8 +103,10 @@ class Buffers:
         self.K = int(self.total.item())
         if self.K >= 2 ** 32:
             raise L.GsError(f"{self.K} intersections exceed the 32-bit key index")
+        if self.lists == "auto":
+            self.path = "binned" if self.V * self.n <= self.K else "radix"
         self.ensure_capacity(self.K)
-        if self.lists == "binned":
+        if self.path == "binned":
             self.sorted_in_alt = False
             L.gs_tile_lists(self.rec, self.rect, self.n, self.V, self.W, self.H, self.vals, self.capacity,
                             self.ranges, self.overflow, self.tl_ws)
