@@ -159,11 +159,13 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
                 // gradients need no correctly rounded division)
                 Tr = contrib ? Tr * __builtin_amdgcn_rcpf(1.f - alpha) : Tr;
                 const float wk = contrib ? alpha * Tr : 0.f;
-                const float dLda = Tr * (((q1.z - acc0) * g0 + (q1.w - acc1) * g1) + (qb - acc2) * g2);
-                const float ak = contrib ? alpha : 0.f;  // colour behind: unchanged when 0
-                acc0 = ak * q1.z + (1.f - ak) * acc0;
-                acc1 = ak * q1.w + (1.f - ak) * acc1;
-                acc2 = ak * qb + (1.f - ak) * acc2;
+                const float d0 = q1.z - acc0, d1 = q1.w - acc1, d2 = qb - acc2;
+                const float dLda = Tr * ((d0 * g0 + d1 * g1) + d2 * g2);
+                // colour behind: S' = a c + (1 - a) S = S + a (c - S), unchanged when a = 0
+                const float ak = contrib ? alpha : 0.f;
+                acc0 = __builtin_fmaf(ak, d0, acc0);
+                acc1 = __builtin_fmaf(ak, d1, acc1);
+                acc2 = __builtin_fmaf(ak, d2, acc2);
                 const float dG = (contrib && !(oG > ALPHA_MAX)) ? dLda * G : 0.f;
                 coef[q][i] = make_float2(dG, wk);
             }
