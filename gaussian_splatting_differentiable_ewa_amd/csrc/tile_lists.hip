@@ -16,6 +16,7 @@
 //                     the next slot (LDS atomic) and writes (depth bits, id);
 //   5. k_tl_sort_small one wave per tile of up to 64 entries: bitonic sort of
 //                     the 64-bit (depth bits, id) across the lanes;
+//      k_tl_sort_wave one wave per tile of up to 512 entries and
 //      k_tl_sort      one workgroup per longer tile: stable LSD radix sort by
 //                     the 32 depth bits (8-bit digits; digits equal across the
 //                     tile are skipped), in LDS for up to 4096 entries and
@@ -268,6 +269,133 @@ __device__ __forceinline__ void tl_fix_ties(uint32_t n, KeyAt key_at, ValAt, Les
     }
 }
 
+constexpr int WV_CAP = 512;  // entries one wave sorts alone
+constexpr int WV_ROUNDS = WV_CAP / 64;
+
+// Tiles of 65..512 entries, one wave each (four per workgroup, no barriers:
+// LDS is in order within a wave): the LSD radix sort of k_tl_sort on one
+// wave's registers and a private slice of LDS.
+__global__ __launch_bounds__(256) void k_tl_sort_wave(const uint32_t* __restrict__ ranges, int64_t n_tiles,
+                                                      const uint64_t* __restrict__ total_dev, uint64_t capacity,
+                                                      const uint2* __restrict__ pairs, uint32_t* __restrict__ vals)
+{
+    __shared__ uint32_t s_key[4][WV_CAP];
+    __shared__ uint16_t s_idx[4][WV_CAP];
+    __shared__ uint32_t s_cnt[4][256];
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    const int64_t tile = (int64_t)blockIdx.x * 4 + wave;
+    if (tile >= n_tiles) return;
+    const uint2 rg = *(const uint2*)(ranges + 2 * tile);
+    const uint64_t limit = min(capacity, *total_dev);
+    const uint32_t start = rg.x, end = (uint32_t)min((uint64_t)rg.y, limit);
+    if (end <= start) return;
+    const uint32_t n = end - start;
+    if (n <= 64u || n > (uint32_t)WV_CAP) return;  // wave-uniform
+    uint32_t* sk = s_key[wave];
+    uint16_t* si = s_idx[wave];
+    uint32_t* cnt = s_cnt[wave];
+    const uint32_t R = (n + 63u) / 64u;
+    uint32_t key[WV_ROUNDS], idx[WV_ROUNDS], rank[WV_ROUNDS];
+    uint32_t kor = 0u, kand = 0xffffffffu;
+#pragma unroll
+    for (int r = 0; r < WV_ROUNDS; ++r) {
+        const uint32_t i = (uint32_t)r * 64u + lane;
+        key[r] = 0u;
+        idx[r] = i;
+        if ((uint32_t)r < R && i < n) {
+            key[r] = pairs[start + i].x;
+            kor |= key[r];
+            kand &= key[r];
+            sk[i] = key[r];
+            si[i] = (uint16_t)i;
+        }
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        kor |= __shfl_xor(kor, off);
+        kand &= __shfl_xor(kand, off);
+    }
+    const uint32_t differ = kor ^ kand;
+    for (int shift = 0; shift < 32; shift += 8) {
+        if (((differ >> shift) & 255u) == 0u) continue;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) cnt[lane * 4 + k] = 0u;
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int r = 0; r < WV_ROUNDS; ++r) {
+            if ((uint32_t)r >= R) break;
+            const uint32_t i = (uint32_t)r * 64u + lane;
+            const bool valid = i < n;
+            const uint32_t d = (key[r] >> shift) & 255u;
+            const uint64_t peers = tl_peers(d, ballot(valid));
+            const uint32_t below = mask_rank(peers);
+            const uint32_t prior = cnt[d];
+            rank[r] = prior + below;
+            asm volatile("" ::: "memory");
+            if (valid && below == 0u) cnt[d] = prior + (uint32_t)__popcll(peers);
+            asm volatile("" ::: "memory");
+        }
+        // exclusive prefix over the 256 digit counts: four per lane
+        uint32_t c[4], sum = 0u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            c[k] = cnt[lane * 4 + k];
+            sum += c[k];
+        }
+        uint32_t x = sum;
+#pragma unroll
+        for (uint32_t off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        uint32_t run = x - sum;
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            cnt[lane * 4 + k] = run;
+            run += c[k];
+        }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int r = 0; r < WV_ROUNDS; ++r) {
+            if ((uint32_t)r >= R) break;
+            const uint32_t i = (uint32_t)r * 64u + lane;
+            if (i < n) {
+                const uint32_t pos = cnt[(key[r] >> shift) & 255u] + rank[r];
+                sk[pos] = key[r];
+                si[pos] = (uint16_t)idx[r];
+            }
+        }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int r = 0; r < WV_ROUNDS; ++r) {
+            if ((uint32_t)r >= R) break;
+            const uint32_t i = (uint32_t)r * 64u + lane;
+            if (i < n) {
+                key[r] = sk[i];
+                idx[r] = si[i];
+            }
+        }
+        asm volatile("" ::: "memory");
+    }
+    // equal depths: order the run's items by Gaussian index (one lane per run)
+    const uint2* tp = pairs + start;
+    for (uint32_t i = lane; i + 1 < n; i += 64) {
+        const uint32_t k = sk[i];
+        if ((i > 0 && sk[i - 1] == k) || sk[i + 1] != k) continue;
+        uint32_t j = i + 1;
+        while (j < n && sk[j] == k) ++j;
+        for (uint32_t a = i + 1; a < j; ++a)
+            for (uint32_t b = a; b > i && tp[si[b]].y < tp[si[b - 1]].y; --b) {
+                const uint16_t tmp = si[b];
+                si[b] = si[b - 1];
+                si[b - 1] = tmp;
+            }
+    }
+    asm volatile("" ::: "memory");
+    for (uint32_t i = lane; i < n; i += 64) vals[start + i] = tp[si[i]].y;
+}
+
 __global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restrict__ ranges,
                                                         const uint64_t* __restrict__ total_dev, uint64_t capacity,
                                                         uint2* __restrict__ pairs, uint2* __restrict__ alt,
@@ -283,7 +411,7 @@ __global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restri
     if (end <= start) return;
     const uint32_t n = end - start;
     const uint32_t t = threadIdx.x, lane = t & 63u, wave = t >> 6;
-    if (n <= 64u) return;  // k_tl_sort_small
+    if (n <= (uint32_t)WV_CAP) return;  // k_tl_sort_small, k_tl_sort_wave
     if (n <= (uint32_t)TL_CAP) {
         // wave w holds the contiguous run [w L, (w + 1) L), L = 64 R
         const uint32_t R = (n + TL_THREADS - 1) / TL_THREADS;
@@ -552,6 +680,9 @@ gs_status gs_tile_lists(const float* rec, const uint16_t* rect, int64_t n, int32
                        overflow);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     hipLaunchKernelGGL(k_tl_sort_small, dim3(grid_for((uint64_t)n_tiles, 4)), dim3(256), 0, s, ranges, n_tiles, total,
+                       capacity, pairs, vals);
+    if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
+    hipLaunchKernelGGL(k_tl_sort_wave, dim3(grid_for((uint64_t)n_tiles, 4)), dim3(256), 0, s, ranges, n_tiles, total,
                        capacity, pairs, vals);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     hipLaunchKernelGGL(k_tl_sort, dim3((unsigned)n_tiles), dim3(TL_THREADS), 0, s, ranges, total, capacity, pairs,
