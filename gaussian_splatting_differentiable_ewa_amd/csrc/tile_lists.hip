@@ -82,12 +82,11 @@ __device__ __forceinline__ BinBlock bin_block(const BinGrid& G)
     return B;
 }
 
-// the pair's tile rectangle, clipped to the rows [ty0, ty1) and the grid
-__device__ __forceinline__ bool band_rect(const uint16_t* __restrict__ rect, int64_t idx, const BinGrid& G,
-                                          uint32_t ty0, uint32_t ty1, uint32_t& x0, uint32_t& y0, uint32_t& x1,
-                                          uint32_t& y1)
+// a pair's tile rectangle (as stored), clipped to the rows [ty0, ty1) and the
+// grid
+__device__ __forceinline__ bool band_rect(uint2 rr, const BinGrid& G, uint32_t ty0, uint32_t ty1, uint32_t& x0,
+                                          uint32_t& y0, uint32_t& x1, uint32_t& y1)
 {
-    const uint2 rr = *(const uint2*)(rect + 4 * idx);
     x0 = rr.x & 0xffffu;
     y0 = max(rr.x >> 16, ty0);
     x1 = min(rr.y & 0xffffu, (uint32_t)G.tiles_x);
@@ -103,31 +102,55 @@ __global__ __launch_bounds__(256) void k_bin_count(const uint16_t* __restrict__ 
     const uint32_t nt = (B.ty1 - B.ty0) * (uint32_t)G.tiles_x;
     for (uint32_t i = threadIdx.x; i < nt; i += 256) cnt[i] = 0u;
     __syncthreads();
-    for (int64_t g = B.g0 + threadIdx.x; g < B.g1; g += 256) {
-        uint32_t x0, y0, x1, y1;
-        if (!band_rect(rect, B.v * G.n + g, G, B.ty0, B.ty1, x0, y0, x1, y1)) continue;
-        for (uint32_t ty = y0; ty < y1; ++ty)
-            for (uint32_t tx = x0; tx < x1; ++tx) atomicAdd(&cnt[(ty - B.ty0) * G.tiles_x + tx], 1u);
+    // four Gaussians per thread and round: their rectangles are requested
+    // together
+    for (int64_t g4 = B.g0 + threadIdx.x; g4 < B.g1; g4 += 4 * 256) {
+        uint2 rr[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t g = g4 + 256 * k;
+            rr[k] = g < B.g1 ? *(const uint2*)(rect + 4 * (B.v * G.n + g)) : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t x0, y0, x1, y1;
+            if (!band_rect(rr[k], G, B.ty0, B.ty1, x0, y0, x1, y1)) continue;
+            for (uint32_t ty = y0; ty < y1; ++ty)
+                for (uint32_t tx = x0; tx < x1; ++tx) atomicAdd(&cnt[(ty - B.ty0) * G.tiles_x + tx], 1u);
+        }
     }
     __syncthreads();
     uint32_t* row = table + (B.v * G.chunks + B.c) * G.tiles + (int64_t)B.ty0 * G.tiles_x;
     for (uint32_t i = threadIdx.x; i < nt; i += 256) row[i] = cnt[i];
 }
 
+// 64 tiles per workgroup, each wave one quarter of the chunks: quarter sums,
+// then every wave rewrites its quarter as an exclusive prefix
 __global__ __launch_bounds__(256) void k_bin_colscan(uint32_t* __restrict__ table, const BinGrid G, int32_t n_views,
                                                      uint32_t* __restrict__ totals)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (int64_t)n_views * G.tiles) return;
-    const int64_t v = i / G.tiles, tile = i - v * G.tiles;
+    __shared__ uint32_t part[4][64];
+    const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+    const int64_t i = (int64_t)blockIdx.x * 64 + lane;
+    const bool ok = i < (int64_t)n_views * G.tiles;
+    const int64_t v = ok ? i / G.tiles : 0, tile = ok ? i - v * G.tiles : 0;
     uint32_t* col = table + v * G.chunks * G.tiles + tile;
+    const int32_t q = (G.chunks + 3) / 4, c0 = min((int32_t)w * q, G.chunks), c1 = min(c0 + q, G.chunks);
+    uint32_t sum = 0u;
+    if (ok)
+        for (int32_t c = c0; c < c1; ++c) sum += col[(int64_t)c * G.tiles];
+    part[w][lane] = sum;
+    __syncthreads();
     uint32_t run = 0u;
-    for (int32_t c = 0; c < G.chunks; ++c) {
-        const uint32_t x = col[(int64_t)c * G.tiles];
-        col[(int64_t)c * G.tiles] = run;
-        run += x;
+    for (uint32_t k = 0; k < w; ++k) run += part[k][lane];
+    if (ok) {
+        for (int32_t c = c0; c < c1; ++c) {
+            const uint32_t x = col[(int64_t)c * G.tiles];
+            col[(int64_t)c * G.tiles] = run;
+            run += x;
+        }
+        if (w == 3) totals[i] = run;
     }
-    totals[i] = run;
 }
 
 __global__ __launch_bounds__(256) void k_tl_ranges(const uint32_t* __restrict__ starts, int64_t n_tiles,
@@ -153,19 +176,30 @@ __global__ __launch_bounds__(256) void k_bin_fill(const float* __restrict__ rec,
     for (uint32_t i = threadIdx.x; i < nt; i += 256) cur[i] = st[i] + row[i];
     __syncthreads();
     bool over = false;
-    for (int64_t g = B.g0 + threadIdx.x; g < B.g1; g += 256) {
-        const int64_t idx = B.v * G.n + g;
-        uint32_t x0, y0, x1, y1;
-        if (!band_rect(rect, idx, G, B.ty0, B.ty1, x0, y0, x1, y1)) continue;
-        const uint32_t zb = __float_as_uint(rec[idx * GS_REC_FLOATS + GS_REC_DEPTH]);
-        for (uint32_t ty = y0; ty < y1; ++ty)
-            for (uint32_t tx = x0; tx < x1; ++tx) {
-                const uint32_t pos = atomicAdd(&cur[(ty - B.ty0) * G.tiles_x + tx], 1u);
-                if (pos < capacity)
-                    pairs[pos] = make_uint2(zb, (uint32_t)g);
-                else
-                    over = true;
-            }
+    for (int64_t g4 = B.g0 + threadIdx.x; g4 < B.g1; g4 += 4 * 256) {
+        uint2 rr[4];
+        uint32_t zb[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t g = g4 + 256 * k, idx = B.v * G.n + g;
+            const bool in = g < B.g1;
+            rr[k] = in ? *(const uint2*)(rect + 4 * idx) : make_uint2(0u, 0u);
+            zb[k] = in ? __float_as_uint(rec[idx * GS_REC_FLOATS + GS_REC_DEPTH]) : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t x0, y0, x1, y1;
+            if (!band_rect(rr[k], G, B.ty0, B.ty1, x0, y0, x1, y1)) continue;
+            const uint32_t gid = (uint32_t)(g4 + 256 * k);
+            for (uint32_t ty = y0; ty < y1; ++ty)
+                for (uint32_t tx = x0; tx < x1; ++tx) {
+                    const uint32_t pos = atomicAdd(&cur[(ty - B.ty0) * G.tiles_x + tx], 1u);
+                    if (pos < capacity)
+                        pairs[pos] = make_uint2(zb[k], gid);
+                    else
+                        over = true;
+                }
+        }
     }
     if (over) *overflow = 1;
 }
@@ -669,7 +703,7 @@ gs_status gs_tile_lists(const float* rec, const uint16_t* rect, int64_t n, int32
     } else if (fill_u32(table, (uint64_t)n_tiles * G.chunks, 0u, s) != hipSuccess) {
         return GS_ERR_HIP;
     }
-    hipLaunchKernelGGL(k_bin_colscan, dim3(grid_for((uint64_t)n_tiles, 256)), dim3(256), 0, s, table, G, n_views,
+    hipLaunchKernelGGL(k_bin_colscan, dim3(grid_for((uint64_t)n_tiles, 64)), dim3(256), 0, s, table, G, n_views,
                        totals);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     if (scan_u32(totals, totals, (uint64_t)n_tiles, total, w + L.scan, s) != hipSuccess) return GS_ERR_HIP;
