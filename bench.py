@@ -43,6 +43,7 @@ CSRC = os.path.join(ROOT, "gaussian_splatting_differentiable_ewa_amd", "csrc")
 KERNEL_SOURCES = {
     "k_raster_bwd": ["raster_bwd.hip", "raster_common.h", "internal.h", "common.h"],
     "k_raster_fwd": ["raster_fwd.hip", "raster_common.h", "internal.h", "common.h"],
+    "k_raster_fwd_l1": ["raster_fwd.hip", "raster_common.h", "internal.h", "common.h"],
     "k_adam": ["optim.hip", "internal.h", "common.h"],
     "k_preprocess_bwd": ["preprocess_bwd.hip", "project.h", "internal.h", "common.h"],
 }
@@ -111,8 +112,9 @@ def stage_bytes(P, n, V, K, n_vis_per_view, n_any, n_px):
         "emit": 16 * V * n + 12 * K,          # rect + offset per pair, key + id per intersection
         "sort": 24 * K,                       # one read + one write of key + id
         "ranges": 8 * K + 8 * V * n_px // 256,
-        "raster_fwd": 4 * K + 36 * Nv + 20 * V * n_px,
-        "loss": 36 * V * n_px,
+        # forward raster with the L1 loss fused: ids, one record read per
+        # visible pair, target read, T_final + n_contrib + dL/dimage written
+        "raster_fwd_loss": 4 * K + 36 * Nv + 32 * V * n_px,
         "raster_bwd": 4 * K + 36 * Nv + 32 * V * n_px + 36 * Nv * 2,
         "preprocess_bwd": Bp * n_any + 44 * Nv + Bp * n,
         "adam": 7 * Bp * n,
@@ -151,8 +153,7 @@ def main():
 
     b = ts.buf
     stream = torch.cuda.current_stream()
-    names = ["preprocess", "intersections", "raster_fwd", "loss", "grad2d_zero", "raster_bwd", "preprocess_bwd",
-             "adam"]
+    names = ["preprocess", "intersections", "raster_fwd_loss", "grad2d_zero", "raster_bwd", "preprocess_bwd", "adam"]
 
     def step_timed(ev):
         ts.t += 1
@@ -161,22 +162,20 @@ def main():
         ev[1].record(stream)
         b.intersections()
         ev[2].record(stream)
-        b.rasterize(ts.bg)
+        b.rasterize_loss_l1(ts.target, ts.bg)
         ev[3].record(stream)
-        b.loss_l1(ts.target)
-        ev[4].record(stream)
         # the 2D-gradient buffer is cleared on its own, so that the next
         # event pair brackets the backward raster kernel alone
         b.grad2d.zero_()
-        ev[5].record(stream)
+        ev[4].record(stream)
         L.gs_rasterize_bwd(b.rec, b.n, b.ranges, b.sorted_vals, b.cams, ts.bg, b.T_final, b.n_contrib, b.dL,
                            b.grad2d, accumulate=True)
-        ev[6].record(stream)
+        ev[5].record(stream)
         L.gs_preprocess_bwd(ts.params, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, ts.grad)
-        ev[7].record(stream)
+        ev[6].record(stream)
         L.gs_adam_step(ts.params, ts.grad, ts.m, ts.v, ts.params.numel(), ts.lr, ts.betas[0], ts.betas[1],
                        ts.eps, ts.t)
-        ev[8].record(stream)
+        ev[7].record(stream)
 
     for _ in range(args.warmup):
         ts.step()
@@ -205,7 +204,7 @@ def main():
 
     # dominant kernel: the single-kernel stage with the largest time
     pairs = int(b.n_contrib.sum(dtype=torch.int64))  # (pixel, entry) pairs up to each last contributor
-    single = {"raster_fwd": "k_raster_fwd", "raster_bwd": "k_raster_bwd", "adam": "k_adam",
+    single = {"raster_fwd_loss": "k_raster_fwd_l1", "raster_bwd": "k_raster_bwd", "adam": "k_adam",
               "preprocess_bwd": "k_preprocess_bwd"}
     dom = max(single, key=lambda k: stage_ms[k])
     kern = single[dom]

@@ -27,9 +27,9 @@ GS_GRAD2D_ROWS = 9
 EXPORTS = (
     "gs_abi_version", "gs_status_string", "gs_param_rows", "gs_tiles_x", "gs_tiles_y",
     "gs_sort_end_bit", "gs_preprocess_workspace_bytes", "gs_sort_workspace_bytes",
-    "gs_tile_lists_workspace_bytes",
+    "gs_tile_lists_workspace_bytes", "gs_rasterize_fwd_l1_workspace_bytes",
     "gs_preprocess", "gs_emit_intersections", "gs_sort_keys", "gs_tile_lists", "gs_tile_ranges",
-    "gs_rasterize_fwd", "gs_loss_l1", "gs_rasterize_bwd", "gs_preprocess_bwd", "gs_adam_step",
+    "gs_rasterize_fwd", "gs_rasterize_fwd_l1", "gs_loss_l1", "gs_rasterize_bwd", "gs_preprocess_bwd", "gs_adam_step",
 )
 
 
@@ -70,12 +70,15 @@ def lib():
             "gs_preprocess_workspace_bytes": ([_I64, _I32], _SZ),
             "gs_sort_workspace_bytes": ([_U64], _SZ),
             "gs_tile_lists_workspace_bytes": ([_I64, _I32, _I32, _I32, _U64], _SZ),
+            "gs_rasterize_fwd_l1_workspace_bytes": ([_I32, _I32, _I32], _SZ),
             "gs_preprocess": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
             "gs_emit_intersections": ([_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _U64, _P, _P], ctypes.c_int),
             "gs_sort_keys": ([_P, _P, _P, _P, _U64, _I32, _P, _SZ, _P, _P], ctypes.c_int),
             "gs_tile_ranges": ([_P, _U64, _I64, _P, _P], ctypes.c_int),
             "gs_tile_lists": ([_P, _P, _I64, _I32, _I32, _I32, _P, _U64, _P, _P, _P, _SZ, _P], ctypes.c_int),
             "gs_rasterize_fwd": ([_P, _I64, _P, _P, _P, _I32, _P, _P, _P, _P, _P], ctypes.c_int),
+            "gs_rasterize_fwd_l1": ([_P, _I64, _P, _P, _P, _I32, _P, _P, _F32, _P, _P, _P, _P, _P, _I32, _P, _SZ, _P],
+                                    ctypes.c_int),
             "gs_loss_l1": ([_P, _P, _I64, _F32, _P, _P, _I32, _P], ctypes.c_int),
             "gs_rasterize_bwd": ([_P, _I64, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _I32, _P], ctypes.c_int),
             "gs_preprocess_bwd": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P], ctypes.c_int),
@@ -143,6 +146,10 @@ def sort_workspace_bytes(n_keys: int) -> int:
     return lib().gs_sort_workspace_bytes(n_keys)
 
 
+def rasterize_fwd_l1_workspace_bytes(n_views: int, width: int, height: int) -> int:
+    return lib().gs_rasterize_fwd_l1_workspace_bytes(n_views, width, height)
+
+
 def tile_lists_workspace_bytes(n: int, n_views: int, width: int, height: int, capacity: int) -> int:
     return lib().gs_tile_lists_workspace_bytes(n, n_views, width, height, capacity)
 
@@ -187,6 +194,16 @@ def gs_rasterize_fwd(rec, n, ranges, vals, cams, bg, image, T_final, n_contrib, 
     _check(lib().gs_rasterize_fwd(_ptr(rec), n, _ptr(ranges), _ptr(vals), cameras(cams), len(cams), bgv,
                                   _ptr(image), _ptr(T_final), _ptr(n_contrib), _stream(stream)),
            "gs_rasterize_fwd")
+
+
+def gs_rasterize_fwd_l1(rec, n, ranges, vals, cams, bg, target, scale, image, T_final, n_contrib, dL_dimage, loss,
+                        ws, accumulate=False, stream=None):
+    """image may be None (not written)."""
+    bgv = (ctypes.c_float * 3)(*bg)
+    _check(lib().gs_rasterize_fwd_l1(_ptr(rec), n, _ptr(ranges), _ptr(vals), cameras(cams), len(cams), bgv,
+                                     _ptr(target), scale, _ptr(image), _ptr(T_final), _ptr(n_contrib),
+                                     _ptr(dL_dimage), _ptr(loss), int(bool(accumulate)), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)), "gs_rasterize_fwd_l1")
 
 
 def gs_loss_l1(image, target, count, scale, dL_dimage, loss, accumulate=False, stream=None):

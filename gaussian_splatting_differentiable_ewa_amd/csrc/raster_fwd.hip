@@ -33,19 +33,37 @@
 
 namespace gs {
 
-__global__ __launch_bounds__(RW_THREADS) void k_raster_fwd(const float* __restrict__ rec, int64_t n,
-                                                           const uint32_t* __restrict__ ranges,
-                                                           const uint32_t* __restrict__ vals, int W, int H, int TX,
-                                                           int T, float bg0, float bg1, float bg2,
-                                                           float* __restrict__ image, float* __restrict__ T_final,
-                                                           int32_t* __restrict__ n_contrib)
+// The L1 loss fused at the end (L1 = true): each lane reads its pixel's
+// target, writes dL/dimage = scale sign(I - I*) and the wave's sum of |I - I*|
+// goes to partial[block] (0 for quarters outside the image); image may then
+// be null.
+template <bool L1>
+__device__ __forceinline__ void raster_fwd_body(const float* __restrict__ rec, int64_t n,
+                                                const uint32_t* __restrict__ ranges,
+                                                const uint32_t* __restrict__ vals, int W, int H, int TX, int T,
+                                                float bg0, float bg1, float bg2, float* __restrict__ image,
+                                                float* __restrict__ T_final, int32_t* __restrict__ n_contrib,
+                                                const float* __restrict__ target, float scale,
+                                                float* __restrict__ dL, double* __restrict__ partial)
 {
 #pragma clang fp contract(off)
     __shared__ float4 s_rec[3 * RW_BATCH];
     __shared__ uint8_t s_mask[RW_BATCH];
     __shared__ __align__(16) uint16_t s_list[4 * RW_BATCH];  // read 8 ids at a time
     const QuarterCtx t = quarter_ctx(W, H, TX, T);
-    if (t.empty) return;
+    if (t.empty) {
+        if (L1 && t.lane == 0) partial[blockIdx.x] = 0.0;
+        return;
+    }
+    // the target of this lane's pixel, requested now and used at the end
+    float tg0 = 0.f, tg1 = 0.f, tg2 = 0.f;
+    if (L1 && t.inside) {
+        const int64_t HW = (int64_t)H * W;
+        const int64_t o = (int64_t)t.view * 3 * HW + (int64_t)t.j * W + t.i;
+        tg0 = target[o];
+        tg1 = target[o + HW];
+        tg2 = target[o + 2 * HW];
+    }
     const uint2 rg = *(const uint2*)(ranges + 2 * (uint64_t)t.tile_lin);
     const float* rv = rec + (int64_t)t.view * n * GS_REC_FLOATS;
     float Tr = 1.f, C0 = 0.f, C1 = 0.f, C2 = 0.f;
@@ -117,16 +135,74 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_fwd(const float* __restri
         nxt.valid = v2;
         nxt.gid = gid2;
     }
+    float ad = 0.f;  // |I - I*| summed over the channels
     if (t.inside) {
         const int64_t HW = (int64_t)H * W;
         const int64_t pix = (int64_t)t.j * W + t.i;
-        float* img = image + (int64_t)t.view * 3 * HW + pix;
-        img[0] = C0 + Tr * bg0;
-        img[HW] = C1 + Tr * bg1;
-        img[2 * HW] = C2 + Tr * bg2;
+        const int64_t o = (int64_t)t.view * 3 * HW + pix;
+        const float i0 = C0 + Tr * bg0, i1 = C1 + Tr * bg1, i2 = C2 + Tr * bg2;
+        if (!L1 || image) {
+            image[o] = i0;
+            image[o + HW] = i1;
+            image[o + 2 * HW] = i2;
+        }
         T_final[(int64_t)t.view * HW + pix] = Tr;
         n_contrib[(int64_t)t.view * HW + pix] = last;
+        if (L1) {
+            const float d0 = i0 - tg0, d1 = i1 - tg1, d2 = i2 - tg2;
+            dL[o] = d0 > 0.f ? scale : (d0 < 0.f ? -scale : 0.f);
+            dL[o + HW] = d1 > 0.f ? scale : (d1 < 0.f ? -scale : 0.f);
+            dL[o + 2 * HW] = d2 > 0.f ? scale : (d2 < 0.f ? -scale : 0.f);
+            ad = (fabsf(d0) + fabsf(d1)) + fabsf(d2);
+        }
     }
+    if (L1) {
+        double acc = (double)ad;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+        if (t.lane == 0) partial[blockIdx.x] = acc;
+    }
+}
+
+__global__ __launch_bounds__(RW_THREADS) void k_raster_fwd(const float* __restrict__ rec, int64_t n,
+                                                           const uint32_t* __restrict__ ranges,
+                                                           const uint32_t* __restrict__ vals, int W, int H, int TX,
+                                                           int T, float bg0, float bg1, float bg2,
+                                                           float* __restrict__ image, float* __restrict__ T_final,
+                                                           int32_t* __restrict__ n_contrib)
+{
+    raster_fwd_body<false>(rec, n, ranges, vals, W, H, TX, T, bg0, bg1, bg2, image, T_final, n_contrib, nullptr, 0.f,
+                           nullptr, nullptr);
+}
+
+__global__ __launch_bounds__(RW_THREADS) void k_raster_fwd_l1(const float* __restrict__ rec, int64_t n,
+                                                              const uint32_t* __restrict__ ranges,
+                                                              const uint32_t* __restrict__ vals, int W, int H, int TX,
+                                                              int T, float bg0, float bg1, float bg2,
+                                                              float* __restrict__ image, float* __restrict__ T_final,
+                                                              int32_t* __restrict__ n_contrib,
+                                                              const float* __restrict__ target, float scale,
+                                                              float* __restrict__ dL, double* __restrict__ partial)
+{
+    raster_fwd_body<true>(rec, n, ranges, vals, W, H, TX, T, bg0, bg1, bg2, image, T_final, n_contrib, target, scale,
+                          dL, partial);
+}
+
+// loss += scale * sum of the per-quarter partial sums: each workgroup sums a
+// contiguous slice, then one fp64 atomic per workgroup
+__global__ __launch_bounds__(256) void k_loss_partials(const double* __restrict__ partial, int64_t count,
+                                                       double scale, double* __restrict__ loss)
+{
+    __shared__ double s_w[4];
+    const int64_t per = (count + gridDim.x - 1) / gridDim.x;
+    const int64_t b0 = (int64_t)blockIdx.x * per, b1 = min(count, b0 + per);
+    double acc = 0.0;
+    for (int64_t i = b0 + threadIdx.x; i < b1; i += 256) acc += partial[i];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) atomicAdd(loss, (((s_w[0] + s_w[1]) + s_w[2]) + s_w[3]) * scale);
 }
 
 }  // namespace gs
@@ -134,6 +210,34 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_fwd(const float* __restri
 using namespace gs;
 
 extern "C" {
+
+size_t gs_rasterize_fwd_l1_workspace_bytes(int32_t n_views, int32_t width, int32_t height)
+{
+    if (n_views < 1 || n_views > GS_MAX_VIEWS || width <= 0 || height <= 0) return 0;
+    const int64_t quarters = (int64_t)n_views * gs_tiles_x(width) * gs_tiles_y(height) * 4;
+    return (size_t)quarters * sizeof(double);
+}
+
+gs_status gs_rasterize_fwd_l1(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
+                              const gs_camera* cams, int32_t n_views, const float* bg, const float* target,
+                              float scale, float* image, float* T_final, int32_t* n_contrib, float* dL_dimage,
+                              double* loss, int32_t accumulate, void* ws, size_t ws_bytes, void* stream)
+{
+    RasterArgs a;
+    if (!raster_args(rec, n, ranges, vals, cams, n_views, bg, a)) return GS_ERR_INVALID_ARGUMENT;
+    if (!T_final || !n_contrib || !target || !dL_dimage || !loss || !ws) return GS_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < (size_t)a.n_blocks * sizeof(double)) return GS_ERR_INVALID_ARGUMENT;
+    hipStream_t s = (hipStream_t)stream;
+    double* partial = (double*)ws;
+    hipLaunchKernelGGL(k_raster_fwd_l1, dim3((unsigned)a.n_blocks), dim3(RW_THREADS), 0, s, rec, n, ranges, vals,
+                       a.dc.width, a.dc.height, a.dc.tiles_x, a.dc.tiles_per_view, bg[0], bg[1], bg[2], image, T_final,
+                       n_contrib, target, scale, dL_dimage, partial);
+    if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
+    if (!accumulate && fill_u32((uint32_t*)loss, 2, 0u, s) != hipSuccess) return GS_ERR_HIP;
+    const unsigned red_blocks = (unsigned)(a.n_blocks < 256 * 64 ? (a.n_blocks + 63) / 64 : 256);
+    hipLaunchKernelGGL(k_loss_partials, dim3(red_blocks), dim3(256), 0, s, partial, a.n_blocks, (double)scale, loss);
+    return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
+}
 
 gs_status gs_rasterize_fwd(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
                            const gs_camera* cams, int32_t n_views, const float* bg, float* image, float* T_final,

@@ -53,6 +53,8 @@ class Buffers:
         self.loss = torch.zeros(1, dtype=torch.float64, device=dev)
         self.grad2d = torch.empty(V * L.GS_GRAD2D_ROWS * n, dtype=torch.float32, device=dev)
         self.overflow = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.fwd_l1_ws = torch.empty(L.rasterize_fwd_l1_workspace_bytes(V, self.W, self.H), dtype=torch.uint8,
+                                     device=dev)
         self.end_bit = L.sort_end_bit(V, self.T)
         self.capacity = 0
         self.allocated_for = None
@@ -125,6 +127,14 @@ class Buffers:
         scale = 1.0 / (3.0 * self.H * self.W * self.V)
         L.gs_loss_l1(self.image, target, self.image.numel(), scale, self.dL, self.loss)
 
+    def rasterize_loss_l1(self, target, bg=(0.0, 0.0, 0.0), image: bool = False):
+        """Forward raster and L1 loss in one pass; the image is written only
+        when asked for."""
+        scale = 1.0 / (3.0 * self.H * self.W * self.V)
+        L.gs_rasterize_fwd_l1(self.rec, self.n, self.ranges, self.sorted_vals, self.cams, bg, target, scale,
+                              self.image if image else None, self.T_final, self.n_contrib, self.dL, self.loss,
+                              self.fwd_l1_ws)
+
     def backward(self, params, grad, bg=(0.0, 0.0, 0.0)):
         L.gs_rasterize_bwd(self.rec, self.n, self.ranges, self.sorted_vals, self.cams, bg, self.T_final,
                            self.n_contrib, self.dL, self.grad2d)
@@ -163,8 +173,7 @@ class TrainStep:
         self.t += 1
         b.preprocess(self.params)
         b.intersections()
-        b.rasterize(self.bg)
-        b.loss_l1(self.target)
+        b.rasterize_loss_l1(self.target, self.bg)
         b.backward(self.params, self.grad, self.bg)
         L.gs_adam_step(self.params, self.grad, self.m, self.v, self.params.numel(), self.lr, self.betas[0],
                        self.betas[1], self.eps, self.t)

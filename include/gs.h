@@ -10,6 +10,7 @@
  *   gs_tile_ranges         [start, end) of each tile in the sorted list
  *   gs_rasterize_fwd       front-to-back alpha blending per 16x16 tile
  *   gs_loss_l1             L1 loss against target images, dL/dimage
+ *   (gs_rasterize_fwd_l1   the two calls above in one pass)
  *   gs_rasterize_bwd       back-to-front gradients to the 2D quantities
  *   gs_preprocess_bwd      gradients to all per-Gaussian parameters
  *   gs_adam_step           fused Adam update
@@ -259,6 +260,30 @@ gs_status gs_rasterize_fwd(const float* rec, int64_t n, const uint32_t* ranges,
  */
 gs_status gs_loss_l1(const float* image, const float* target, int64_t count, float scale,
                      float* dL_dimage, double* loss, int32_t accumulate, void* stream);
+
+/* Workspace of gs_rasterize_fwd_l1 (bytes): one double per 8x8 quarter of
+ * every tile; 0 on invalid sizes. */
+size_t gs_rasterize_fwd_l1_workspace_bytes(int32_t n_views, int32_t width, int32_t height);
+
+/*
+ * gs_rasterize_fwd_l1 -- gs_rasterize_fwd and gs_loss_l1 in one pass: the
+ * same blending (alpha compositing of the fVDB page; 16x16 tiles), then per
+ * pixel dL/dimage = scale * sign(I - target) and the loss (+)= scale *
+ * sum |I - target| (views averaged as for gs_loss_l1: "On Scaling Up 3D
+ * Gaussian Splatting Training", answer on the Independent Gradients
+ * Hypothesis). T_final, n_contrib and dL_dimage equal those of the two calls.
+ *   target    [V][3][H][W]
+ *   image     out [V][3][H][W], or null when not wanted
+ *   loss      device double: overwritten, or added to when `accumulate`
+ *   ws        device workspace of gs_rasterize_fwd_l1_workspace_bytes(...)
+ * Errors: as gs_rasterize_fwd, plus null target / dL_dimage / loss / ws or a
+ * small workspace.
+ */
+gs_status gs_rasterize_fwd_l1(const float* rec, int64_t n, const uint32_t* ranges,
+                              const uint32_t* vals, const gs_camera* cams, int32_t n_views,
+                              const float* bg, const float* target, float scale, float* image,
+                              float* T_final, int32_t* n_contrib, float* dL_dimage, double* loss,
+                              int32_t accumulate, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * gs_rasterize_bwd -- back to front over each pixel's blended entries

@@ -92,6 +92,17 @@ def gpu_preprocess_bwd(b: Buffers, params_t: torch.Tensor, grad2d_np: np.ndarray
     return np_(grad)
 
 
+def gpu_forward_l1(b: Buffers, target_np, bg=(0.0, 0.0, 0.0)):
+    """The fused forward + L1 pass on the lists already in `b`: image, T_final,
+    n_contrib, dL/dimage and the loss."""
+    dev = b.device
+    tgt = torch.from_numpy(np.ascontiguousarray(target_np, dtype=np.float32)).to(dev)
+    b.rasterize_loss_l1(tgt, bg, image=True)
+    torch.cuda.synchronize()
+    return {"image": np_(b.image), "T_final": np_(b.T_final), "n_contrib": np_(b.n_contrib), "dL": np_(b.dL),
+            "loss": float(np_(b.loss)[0])}
+
+
 def gpu_loss(image_np, target_np):
     dev = torch.device("cuda:0")
     img = torch.from_numpy(np.ascontiguousarray(image_np)).to(dev)

@@ -106,6 +106,14 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert lib.gs_tile_ranges(None, 10, 4, fake, None) == INV
     # raster
     bg = (ctypes.c_float * 3)(0, 0, 0)
+    qws = L.rasterize_fwd_l1_workspace_bytes(1, 256, 256)
+    assert qws == 16 * 16 * 4 * 8 and L.rasterize_fwd_l1_workspace_bytes(0, 256, 256) == 0
+    f1 = lib.gs_rasterize_fwd_l1
+    assert f1(fake, 10, fake, fake, cams, 1, bg, None, 1.0, None, fake, fake, fake, fake, 0, fake, qws, None) == INV
+    assert f1(fake, 10, fake, fake, cams, 1, bg, fake, 1.0, None, fake, fake, None, fake, 0, fake, qws, None) == INV
+    assert f1(fake, 10, fake, fake, cams, 1, bg, fake, 1.0, None, fake, fake, fake, None, 0, fake, qws, None) == INV
+    assert f1(fake, 10, fake, fake, cams, 1, bg, fake, 1.0, None, fake, fake, fake, fake, 0, fake, qws - 8, None) == INV
+    assert f1(fake, 10, fake, fake, cams, 1, bg, fake, 1.0, None, fake, fake, fake, fake, 0, None, qws, None) == INV
     assert lib.gs_rasterize_fwd(fake, 10, fake, fake, cams, 1, None, fake, fake, fake, None) == INV
     assert lib.gs_rasterize_fwd(fake, 10, fake, fake, cams, 1, bg, None, fake, fake, None) == INV
     assert lib.gs_rasterize_fwd(fake, -5, fake, fake, cams, 1, bg, fake, fake, fake, None) == INV

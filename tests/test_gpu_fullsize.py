@@ -85,6 +85,11 @@ def test_loss(run):
     loss_g, dL_g = PY.gpu_loss(run["gpu"]["image"], run["target"])
     assert loss_g == pytest.approx(loss_o, rel=1e-6)
     assert np.array_equal(dL_g, dL_o)
+    # the fused forward + L1 pass the step uses
+    fused = PY.gpu_forward_l1(run["buf"], run["target"])
+    assert np.array_equal(fused["image"], run["gpu"]["image"])
+    assert np.array_equal(fused["dL"], dL_o)
+    assert fused["loss"] == pytest.approx(loss_o, rel=1e-6)
 
 
 def test_backward_and_adam(run):

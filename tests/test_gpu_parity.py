@@ -64,6 +64,18 @@ def test_loss(run):
     assert np.array_equal(dL_g, dL_o)
 
 
+def test_forward_l1_fused(run):
+    """The fused forward + L1 pass equals the two separate calls: image,
+    T_final, n_contrib and dL/dimage bit for bit, the loss to fp64 rounding."""
+    gpu = run["gpu"]
+    fused = PY.gpu_forward_l1(run["buf"], run["target"])
+    for k in ("image", "T_final", "n_contrib"):
+        assert np.array_equal(fused[k], gpu[k]), k
+    loss_o, dL_o = O.loss_l1(gpu["image"], run["target"])
+    assert np.array_equal(fused["dL"], dL_o)
+    assert fused["loss"] == pytest.approx(loss_o, rel=1e-6)
+
+
 def test_backward(run):
     fwd = run["fwd"]
     _, dL = O.loss_l1(fwd["image"], run["target"])
