@@ -65,8 +65,9 @@ __device__ __forceinline__ void adam1(float& p, float g, float& m, float& v, con
 
 __global__ __launch_bounds__(EW_THREADS) void k_adam(float* __restrict__ params, const float* __restrict__ grad,
                                                      float* __restrict__ m, float* __restrict__ v, int64_t count,
-                                                     const AdamConsts c)
+                                                     const AdamConsts c, const int32_t* __restrict__ skip)
 {
+    if (skip && *skip != 0) return;  // the step's lists overflowed: no update
     const int64_t stride = (int64_t)gridDim.x * EW_THREADS * 4;
     for (int64_t base = ((int64_t)blockIdx.x * EW_THREADS + threadIdx.x) * 4; base < count; base += stride) {
         if (base + 4 <= count) {
@@ -116,8 +117,8 @@ gs_status gs_loss_l1(const float* image, const float* target, int64_t count, flo
     return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
 }
 
-gs_status gs_adam_step(float* params, const float* grad, float* m, float* v, int64_t count, double lr, double beta1,
-                       double beta2, double eps, int64_t step, void* stream)
+static gs_status adam_launch(float* params, const float* grad, float* m, float* v, int64_t count, double lr,
+                             double beta1, double beta2, double eps, int64_t step, const int32_t* skip, void* stream)
 {
     if (count < 0 || step < 1) return GS_ERR_INVALID_ARGUMENT;
     if (count > 0 && (!params || !grad || !m || !v)) return GS_ERR_INVALID_ARGUMENT;
@@ -135,8 +136,21 @@ gs_status gs_adam_step(float* params, const float* grad, float* m, float* v, int
     c.step_size = (float)(lr / bc1);
     c.inv_sqrt_bc2 = (float)(1.0 / sqrt(bc2));
     hipLaunchKernelGGL(k_adam, dim3(stream_blocks(count)), dim3(EW_THREADS), 0, (hipStream_t)stream, params, grad, m,
-                       v, count, c);
+                       v, count, c, skip);
     return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
+}
+
+gs_status gs_adam_step(float* params, const float* grad, float* m, float* v, int64_t count, double lr, double beta1,
+                       double beta2, double eps, int64_t step, void* stream)
+{
+    return adam_launch(params, grad, m, v, count, lr, beta1, beta2, eps, step, nullptr, stream);
+}
+
+gs_status gs_adam_step_unless(float* params, const float* grad, float* m, float* v, int64_t count, double lr,
+                              double beta1, double beta2, double eps, int64_t step, const int32_t* skip, void* stream)
+{
+    if (!skip) return GS_ERR_INVALID_ARGUMENT;
+    return adam_launch(params, grad, m, v, count, lr, beta1, beta2, eps, step, skip, stream);
 }
 
 }  // extern "C"

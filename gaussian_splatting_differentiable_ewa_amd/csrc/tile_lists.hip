@@ -153,12 +153,14 @@ __global__ __launch_bounds__(256) void k_bin_colscan(uint32_t* __restrict__ tabl
     }
 }
 
+// ranges, cut at the capacity: when the lists overflow, readers of the
+// ranges stay inside the filled slots
 __global__ __launch_bounds__(256) void k_tl_ranges(const uint32_t* __restrict__ starts, int64_t n_tiles,
-                                                   uint32_t* __restrict__ ranges)
+                                                   uint64_t capacity, uint32_t* __restrict__ ranges)
 {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= n_tiles) return;
-    const uint32_t s = starts[t], e = starts[t + 1];
+    const uint32_t s = (uint32_t)min((uint64_t)starts[t], capacity), e = (uint32_t)min((uint64_t)starts[t + 1], capacity);
     *(uint2*)(ranges + 2 * t) = e > s ? make_uint2(s, e) : make_uint2(0u, 0u);
 }
 
@@ -707,7 +709,8 @@ gs_status gs_tile_lists(const float* rec, const uint16_t* rect, int64_t n, int32
                        totals);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     if (scan_u32(totals, totals, (uint64_t)n_tiles, total, w + L.scan, s) != hipSuccess) return GS_ERR_HIP;
-    hipLaunchKernelGGL(k_tl_ranges, dim3(grid_for((uint64_t)n_tiles, 256)), dim3(256), 0, s, totals, n_tiles, ranges);
+    hipLaunchKernelGGL(k_tl_ranges, dim3(grid_for((uint64_t)n_tiles, 256)), dim3(256), 0, s, totals, n_tiles, capacity,
+                       ranges);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     if (n == 0) return GS_OK;
     hipLaunchKernelGGL(k_bin_fill, dim3(bin_blocks), dim3(256), 0, s, rec, rect, G, table, totals, pairs, capacity,

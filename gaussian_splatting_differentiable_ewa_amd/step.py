@@ -1,9 +1,15 @@
 """One training step on one GPU through the C ABI.
 
 PyTorch only allocates device memory and provides the stream; every stage is a
-call into the HIP library (``_lib``). The only device-to-host transfer per step
-is the intersection count K, read after ``gs_preprocess`` to size the list
-buffers (they are kept and only grown).
+call into the HIP library (``_lib``). The intersection count K sizes the list
+buffers (kept, and only grown). ``Buffers.intersections`` reads it on the host
+after ``gs_preprocess``; ``TrainStep`` does so only when it must (the first
+step, the global-sort builder), and otherwise builds the lists with the
+capacity it has and lets the device guard the update: the lists' overflow flag
+is folded into a sticky flag, Adam is skipped while it is set, and K and the
+flag are copied back without waiting. When a copied flag shows an overflow,
+the steps from that one on are redone with larger buffers (their updates were
+skipped, so the state is exactly that of the step before).
 
 The per-tile lists come from ``gs_tile_lists`` (binning, then a sort of each
 tile on its own) or from the global 64-bit key path (``gs_emit_intersections``,
@@ -100,8 +106,18 @@ class Buffers:
         L.gs_preprocess(params, self.n, self.sh_degree, self.cams, self.rec, self.rect, self.offsets,
                         self.total, self.pre_ws)
 
-    def intersections(self):
-        """Read K, then build the per-tile lists and their ranges."""
+    def lists_without_count(self) -> bool:
+        """Whether the lists can be built before K is known on the host."""
+        return self.path == "binned" and self.capacity > 0 and self.lists != "radix"
+
+    def intersections(self, read_count: bool = True):
+        """Build the per-tile lists and their ranges: read K first, or (with
+        read_count False and lists_without_count()) build them with the
+        present capacity; the overflow flag then tells whether K fitted."""
+        if not read_count and self.lists_without_count():
+            L.gs_tile_lists(self.rec, self.rect, self.n, self.V, self.W, self.H, self.vals, self.capacity,
+                            self.ranges, self.overflow, self.tl_ws)
+            return
         self.K = int(self.total.item())
         if self.K >= 2 ** 32:
             raise L.GsError(f"{self.K} intersections exceed the 32-bit key index")
@@ -151,11 +167,17 @@ def render(params: torch.Tensor, sh_degree: int, cams: Sequence, bg=(0.0, 0.0, 0
 
 
 class TrainStep:
-    """Parameters, Adam state and buffers of fwd + L1 + bwd + Adam steps."""
+    """Parameters, Adam state and buffers of fwd + L1 + bwd + Adam steps.
+
+    ``t`` counts the updates applied; with ``defer_count`` a call of ``step``
+    may be redone later (see the module note), and ``flush`` settles every
+    step launched so far."""
+
+    RING = 4  # steps whose count and flag may be in flight
 
     def __init__(self, params: torch.Tensor, sh_degree: int, cams: Sequence, target: torch.Tensor,
                  lr=1e-3, betas=(0.9, 0.999), eps=1e-15, bg=(0.0, 0.0, 0.0),
-                 m: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None):
+                 m: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None, defer_count: bool = True):
         assert params.is_cuda and params.dtype == torch.float32 and params.is_contiguous()
         self.params = params
         self.sh_degree = sh_degree
@@ -167,13 +189,81 @@ class TrainStep:
         self.grad = torch.empty_like(params)
         self.lr, self.betas, self.eps, self.bg = lr, betas, eps, bg
         self.t = 0
+        self.defer_count = defer_count
+        dev = params.device
+        self.sticky = torch.zeros(1, dtype=torch.int32, device=dev)  # an unverified step overflowed
+        self._host = [(torch.zeros(1, dtype=torch.int64, pin_memory=True),
+                       torch.zeros(1, dtype=torch.int32, pin_memory=True)) for _ in range(self.RING)]
+        self._pending = []  # (t, event, host K, host flag), oldest first
+        self._slot = 0
+        self.redone = 0  # steps redone after an overflow
 
-    def step(self):
+    def step(self, marks=None):
+        """One step. `marks`, if given, holds 8 events recorded on the stream
+        around the stages (preprocess, lists, forward + loss, 2D-gradient
+        clear, backward raster, preprocess backward, Adam)."""
         b = self.buf
+        self._settle(block=len(self._pending) >= self.RING - 1)
+        mark = (lambda i: marks[i].record()) if marks is not None else (lambda i: None)
+        deferred = self.defer_count and b.lists_without_count()
         self.t += 1
+        mark(0)
         b.preprocess(self.params)
-        b.intersections()
+        mark(1)
+        b.intersections(read_count=not deferred)
+        if deferred:
+            torch.maximum(self.sticky, b.overflow, out=self.sticky)
+        mark(2)
         b.rasterize_loss_l1(self.target, self.bg)
-        b.backward(self.params, self.grad, self.bg)
-        L.gs_adam_step(self.params, self.grad, self.m, self.v, self.params.numel(), self.lr, self.betas[0],
-                       self.betas[1], self.eps, self.t)
+        mark(3)
+        # the 2D-gradient buffer is cleared on its own (a launch of its own,
+        # so that a timing mark can bracket the backward raster alone)
+        b.grad2d.zero_()
+        mark(4)
+        L.gs_rasterize_bwd(b.rec, b.n, b.ranges, b.sorted_vals, b.cams, self.bg, b.T_final, b.n_contrib, b.dL,
+                           b.grad2d, accumulate=True)
+        mark(5)
+        L.gs_preprocess_bwd(self.params, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, self.grad)
+        mark(6)
+        args = (self.params, self.grad, self.m, self.v, self.params.numel(), self.lr, self.betas[0],
+                self.betas[1], self.eps, self.t)
+        if deferred:
+            L.gs_adam_step_unless(*args, self.sticky)
+            hk, hf = self._host[self._slot]
+            self._slot = (self._slot + 1) % self.RING
+            hk.copy_(b.total, non_blocking=True)
+            hf.copy_(self.sticky, non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record()
+            self._pending.append((self.t, ev, hk, hf))
+        else:
+            L.gs_adam_step(*args)
+        mark(7)
+
+    def flush(self):
+        """Settle every launched step (waits for the GPU)."""
+        while self._pending:
+            self._settle(block=True)
+
+    def _settle(self, block: bool):
+        """Check the oldest launched steps' copied K and flag, in order."""
+        b = self.buf
+        while self._pending:
+            t, ev, hk, hf = self._pending[0]
+            if not ev.query():
+                if not block:
+                    return
+                ev.synchronize()
+                block = False  # one wait frees a slot
+            self._pending.pop(0)
+            b.K = int(hk.item())
+            if int(hf.item()) != 0:
+                # step t is the first whose lists overflowed: every update from
+                # it on was skipped, so redo from step t with room for K
+                torch.cuda.synchronize()
+                self.redone += self.t - (t - 1)
+                self._pending.clear()
+                self.sticky.zero_()
+                b.ensure_capacity(b.K, slack=1.5)
+                self.t = t - 1
+                return

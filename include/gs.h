@@ -209,7 +209,8 @@ size_t gs_tile_lists_workspace_bytes(int64_t n, int32_t n_views, int32_t width, 
  *   capacity   slots in vals (>= the total of gs_preprocess; < 2^32)
  *   ranges     device out [n_views * tiles][2]: [start, end), (0, 0) if empty
  *   overflow   device int32: cleared, then set to 1 if the intersections
- *              exceed capacity (vals then incomplete)
+ *              exceed capacity (the lists are then incomplete, and the ranges
+ *              are cut at capacity so that their readers stay in bounds)
  *   ws         device workspace of gs_tile_lists_workspace_bytes(...)
  * Errors: as gs_emit_intersections, plus a small workspace, capacity >= 2^32
  * or more than 8192 tile columns.
@@ -328,6 +329,17 @@ gs_status gs_preprocess_bwd(const float* params, int64_t n, int32_t sh_degree,
  */
 gs_status gs_adam_step(float* params, const float* grad, float* m, float* v, int64_t count,
                        double lr, double beta1, double beta2, double eps, int64_t step, void* stream);
+
+/*
+ * gs_adam_step_unless -- gs_adam_step, skipped on the device when *skip is
+ * non-zero (skip: device int32, e.g. the overflow flag of gs_tile_lists, so
+ * that a step whose lists did not fit its buffers leaves the parameters and
+ * moments untouched and a caller that does not wait for the intersection
+ * count can redo it). Errors: as gs_adam_step, plus a null skip.
+ */
+gs_status gs_adam_step_unless(float* params, const float* grad, float* m, float* v, int64_t count,
+                              double lr, double beta1, double beta2, double eps, int64_t step,
+                              const int32_t* skip, void* stream);
 
 #ifdef __cplusplus
 }

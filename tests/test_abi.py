@@ -130,6 +130,10 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert lib.gs_adam_step(fake, fake, fake, fake, -1, 1e-3, 0.9, 0.999, 1e-15, 1, None) == INV
     assert lib.gs_adam_step(fake, fake, fake, fake, 10, 1e-3, 0.9, 0.999, -1.0, 1, None) == INV
     assert lib.gs_adam_step(None, fake, fake, fake, 10, 1e-3, 0.9, 0.999, 1e-15, 1, None) == INV
+    # the guarded variant needs its flag, and checks the same arguments
+    assert lib.gs_adam_step_unless(fake, fake, fake, fake, 10, 1e-3, 0.9, 0.999, 1e-15, 1, None, None) == INV
+    assert lib.gs_adam_step_unless(fake, fake, fake, fake, 10, 1e-3, 0.9, 0.999, 1e-15, 0, fake, None) == INV
+    assert lib.gs_adam_step_unless(None, fake, fake, fake, 10, 1e-3, 0.9, 0.999, 1e-15, 1, fake, None) == INV
 
 
 def test_product_path_does_not_reach_the_oracle():

@@ -1,0 +1,62 @@
+"""The step driver's deferred intersection count on the GPU: steps build the
+lists with the capacity they have, Adam is skipped on the device when the
+lists overflowed, and the step is redone with larger buffers. Checked by
+forcing an overflow with a tiny capacity."""
+
+import numpy as np
+import pytest
+
+from gaussian_splatting_differentiable_ewa_amd import _lib as L
+from gaussian_splatting_differentiable_ewa_amd import scenes as S
+from gaussian_splatting_differentiable_ewa_amd.step import TrainStep, render
+
+pytestmark = pytest.mark.gpu
+
+
+def _shrink(b, cap):
+    import torch
+    b.capacity = cap
+    b.vals = torch.empty(cap, dtype=torch.int32, device=b.device)
+    b.tl_ws = torch.empty(L.tile_lists_workspace_bytes(b.n, b.V, b.W, b.H, cap), dtype=torch.uint8, device=b.device)
+
+
+def test_deferred_count_redoes_overflowing_steps():
+    import torch
+    dev = torch.device("cuda:0")
+    cfg = S.CONFIGS[0]
+    cams = cfg.cameras()
+    p = torch.from_numpy(S.make_params(cfg)).to(dev)
+    target = render(torch.from_numpy(S.make_target_params(cfg)).to(dev), cfg.sh_degree, cams).clone()
+    ts = TrainStep(p.clone(), cfg.sh_degree, cams, target, lr=cfg.lr, betas=(cfg.beta1, cfg.beta2), eps=cfg.eps)
+    ts.step()  # first step: K read on the host
+    ts.flush()
+    b = ts.buf
+    assert ts.t == 1 and b.path == "binned" and b.lists_without_count()
+    after1 = ts.params.clone()
+    m1, v1 = ts.m.clone(), ts.v.clone()
+
+    # one overflowing step: Adam is skipped on the device, then redone
+    _shrink(b, 16)
+    ts.step()
+    torch.cuda.synchronize()
+    assert int(ts.sticky.item()) == 1
+    assert torch.equal(ts.params, after1) and torch.equal(ts.m, m1) and torch.equal(ts.v, v1)
+    ts.flush()
+    assert ts.t == 1 and ts.redone == 1 and int(ts.sticky.item()) == 0
+    assert b.capacity >= b.K > 16
+    ts.step()
+    ts.flush()
+    assert ts.t == 2 and ts.redone == 1
+    assert not torch.equal(ts.params, after1)
+    assert np.isfinite(float(b.loss.item()))
+
+    # two calls in a row that overflow: the second may find the first's flag
+    # already (and run with the new capacity) or not (and be redone too);
+    # either way every call is an applied update or a redone one
+    _shrink(b, 16)
+    t0, r0 = ts.t, ts.redone
+    ts.step()
+    ts.step()
+    ts.flush()
+    assert (ts.t - t0) + (ts.redone - r0) == 2
+    assert ts.redone > r0 and int(ts.sticky.item()) == 0 and b.capacity >= b.K > 16
