@@ -44,8 +44,8 @@ KERNEL_SOURCES = {
     "k_raster_bwd": ["raster_bwd.hip", "raster_common.h", "internal.h", "common.h"],
     "k_raster_fwd": ["raster_fwd.hip", "raster_common.h", "internal.h", "common.h"],
     "k_raster_fwd_l1": ["raster_fwd.hip", "raster_common.h", "internal.h", "common.h"],
-    "k_adam": ["optim.hip", "internal.h", "common.h"],
-    "k_preprocess_bwd": ["preprocess_bwd.hip", "project.h", "internal.h", "common.h"],
+    "k_adam": ["optim.hip", "adam.h", "internal.h", "common.h"],
+    "k_preprocess_bwd": ["preprocess_bwd.hip", "adam.h", "project.h", "internal.h", "common.h"],
 }
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -118,6 +118,10 @@ def stage_bytes(P, n, V, K, n_vis_per_view, n_any, n_px):
         "raster_bwd": 4 * K + 36 * Nv + 32 * V * n_px + 36 * Nv * 2,
         "preprocess_bwd": Bp * n_any + 44 * Nv + Bp * n,
         "adam": 7 * Bp * n,
+        # the two above in one pass: parameters read once, every (view,
+        # Gaussian) rectangle and each visible pair's 2D gradient read, the
+        # gradient never stored; moments read, parameters and moments written
+        "preprocess_bwd_adam": Bp * n + 8 * V * n + 36 * Nv + 2 * Bp * n + 3 * Bp * n,
     }
 
 
@@ -152,7 +156,7 @@ def main():
     print(f"[bench] {cfg.name}: inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     b = ts.buf
-    names = ["preprocess", "intersections", "raster_fwd_loss", "grad2d_zero", "raster_bwd", "preprocess_bwd", "adam"]
+    names = ts.stage_names
 
     for _ in range(args.warmup):
         ts.step()
@@ -182,13 +186,15 @@ def main():
     n_vis = [int(x) for x in vis.sum(axis=1)]
     n_any = int(vis.any(axis=0).sum())
     sb = stage_bytes(b.P, b.n, V, b.K, n_vis, n_any, H * W)
-    step_bytes = sum(sb.values())
+    unused = ["preprocess_bwd", "adam"] if ts.fused_adam else ["preprocess_bwd_adam"]
+    step_bytes = sum(v for k, v in sb.items() if k not in unused)
     frac_step = step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9)
 
     # dominant kernel: the single-kernel stage with the largest time
     pairs = int(b.n_contrib.sum(dtype=torch.int64))  # (pixel, entry) pairs up to each last contributor
     single = {"raster_fwd_loss": "k_raster_fwd_l1", "raster_bwd": "k_raster_bwd", "adam": "k_adam",
-              "preprocess_bwd": "k_preprocess_bwd"}
+              "preprocess_bwd": "k_preprocess_bwd", "preprocess_bwd_adam": "k_preprocess_bwd"}
+    single = {k: v for k, v in single.items() if k in stage_ms}
     dom = max(single, key=lambda k: stage_ms[k])
     kern = single[dom]
     dur_s = stage_ms[dom] * 1e-3

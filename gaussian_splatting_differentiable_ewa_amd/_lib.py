@@ -30,7 +30,7 @@ EXPORTS = (
     "gs_tile_lists_workspace_bytes", "gs_rasterize_fwd_l1_workspace_bytes",
     "gs_preprocess", "gs_emit_intersections", "gs_sort_keys", "gs_tile_lists", "gs_tile_ranges",
     "gs_rasterize_fwd", "gs_rasterize_fwd_l1", "gs_loss_l1", "gs_rasterize_bwd", "gs_preprocess_bwd",
-    "gs_adam_step", "gs_adam_step_unless",
+    "gs_adam_step", "gs_adam_step_unless", "gs_preprocess_bwd_adam",
 )
 
 
@@ -85,6 +85,8 @@ def lib():
             "gs_preprocess_bwd": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P], ctypes.c_int),
             "gs_adam_step": ([_P, _P, _P, _P, _I64, _F64, _F64, _F64, _F64, _I64, _P], ctypes.c_int),
             "gs_adam_step_unless": ([_P, _P, _P, _P, _I64, _F64, _F64, _F64, _F64, _I64, _P, _P], ctypes.c_int),
+            "gs_preprocess_bwd_adam": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _F64, _F64, _F64, _F64, _I64, _P,
+                                        _P, _P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -229,6 +231,13 @@ def gs_preprocess_bwd(params, n, sh_degree, cams, rect, grad2d, grad_params, str
 def gs_adam_step(params, grad, m, v, count, lr, beta1, beta2, eps, step, stream=None):
     _check(lib().gs_adam_step(_ptr(params), _ptr(grad), _ptr(m), _ptr(v), count, lr, beta1, beta2, eps,
                               step, _stream(stream)), "gs_adam_step")
+
+
+def gs_preprocess_bwd_adam(params, n, sh_degree, cams, rect, grad2d, m, v, lr, beta1, beta2, eps, step, skip=None,
+                           grad_params=None, stream=None):
+    _check(lib().gs_preprocess_bwd_adam(_ptr(params), n, sh_degree, cameras(cams), len(cams), _ptr(rect), _ptr(grad2d),
+                                        _ptr(m), _ptr(v), lr, beta1, beta2, eps, step, _ptr(skip), _ptr(grad_params),
+                                        _stream(stream)), "gs_preprocess_bwd_adam")
 
 
 def gs_adam_step_unless(params, grad, m, v, count, lr, beta1, beta2, eps, step, skip, stream=None):

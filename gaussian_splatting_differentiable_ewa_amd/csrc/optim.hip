@@ -9,6 +9,7 @@
 // training architecture and memory scaling").
 #include <math.h>
 
+#include "adam.h"
 #include "internal.h"
 
 namespace gs {
@@ -47,20 +48,6 @@ __global__ __launch_bounds__(EW_THREADS) void k_loss_l1(const float* __restrict_
         for (int w = 0; w < EW_THREADS / 64; ++w) t += s_part[w];
         atomicAdd(loss, t * (double)scale);
     }
-}
-
-struct AdamConsts {
-    float b1, omb1, b2, omb2;  // beta and 1 - beta, each rounded once from fp64
-    float eps;
-    float step_size;     // lr / (1 - beta1^t)
-    float inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^t)
-};
-
-__device__ __forceinline__ void adam1(float& p, float g, float& m, float& v, const AdamConsts& c)
-{
-    m = c.b1 * m + c.omb1 * g;
-    v = c.b2 * v + c.omb2 * (g * g);
-    p = p - c.step_size * m / (sqrtf(v) * c.inv_sqrt_bc2 + c.eps);
 }
 
 __global__ __launch_bounds__(EW_THREADS) void k_adam(float* __restrict__ params, const float* __restrict__ grad,
@@ -124,17 +111,8 @@ static gs_status adam_launch(float* params, const float* grad, float* m, float* 
     if (count > 0 && (!params || !grad || !m || !v)) return GS_ERR_INVALID_ARGUMENT;
     if (!aligned16(params) || !aligned16(grad) || !aligned16(m) || !aligned16(v)) return GS_ERR_INVALID_ARGUMENT;
     if (count == 0) return GS_OK;
-    if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) || !(eps >= 0.0)) return GS_ERR_INVALID_ARGUMENT;
-    const double bc1 = 1.0 - pow(beta1, (double)step);
-    const double bc2 = 1.0 - pow(beta2, (double)step);
     AdamConsts c;
-    c.b1 = (float)beta1;
-    c.omb1 = (float)(1.0 - beta1);
-    c.b2 = (float)beta2;
-    c.omb2 = (float)(1.0 - beta2);
-    c.eps = (float)eps;
-    c.step_size = (float)(lr / bc1);
-    c.inv_sqrt_bc2 = (float)(1.0 / sqrt(bc2));
+    if (!adam_consts(lr, beta1, beta2, eps, step, c)) return GS_ERR_INVALID_ARGUMENT;
     hipLaunchKernelGGL(k_adam, dim3(stream_blocks(count)), dim3(EW_THREADS), 0, (hipStream_t)stream, params, grad, m,
                        v, count, c, skip);
     return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;

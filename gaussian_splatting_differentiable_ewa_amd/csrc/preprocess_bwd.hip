@@ -8,20 +8,31 @@
 // fixed-order code as gs_preprocess (project.h), so every decision (culling,
 // guard-band clamp, colour clamp) is the forward's; the gradient arithmetic
 // itself is ordinary fp32.
+//
+// With ADAM, the thread applies the Adam update to its Gaussian's P
+// parameters as soon as their gradients are formed (the element-wise update
+// of gs_adam_step, same arithmetic), so the gradient never goes through HBM
+// and the parameters are read once.
+#include "adam.h"
 #include "internal.h"
 #include "project.h"
 
 namespace gs {
 
-template <int DEG>
-__global__ __launch_bounds__(256) void k_preprocess_bwd(const float* __restrict__ P, int64_t n, const DevCameras cams,
+// P is written only with ADAM (each thread its own Gaussian's elements,
+// after reading them); out may then be null.
+template <int DEG, bool ADAM>
+__global__ __launch_bounds__(256) void k_preprocess_bwd(float* __restrict__ P, int64_t n, const DevCameras cams,
                                                         const ShConsts K, const uint16_t* __restrict__ rect,
-                                                        const float* __restrict__ grad2d, float* __restrict__ out)
+                                                        const float* __restrict__ grad2d, float* __restrict__ out,
+                                                        float* __restrict__ m, float* __restrict__ v,
+                                                        const AdamConsts ac, const int32_t* __restrict__ skip)
 {
     constexpr int NB = (DEG + 1) * (DEG + 1);
     constexpr int ROWS = 11 + 3 * NB;
     const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (g >= n) return;
+    if (ADAM && skip && *skip != 0) return;  // the step's lists overflowed: no update
     const float x = P[0 * n + g], y = P[1 * n + g], z = P[2 * n + g];
     GaussLocal L;
     gauss_local(P[3 * n + g], P[4 * n + g], P[5 * n + g], P[6 * n + g], P[7 * n + g], P[8 * n + g],
@@ -222,8 +233,57 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(const float* __restrict_
 #pragma unroll
         for (int i = 0; i < 3 * NB; ++i) G[11 + i] = gsh[i];
     }
+    if (!ADAM || out) {
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) out[(int64_t)r * n + g] = G[r];
+        for (int r = 0; r < ROWS; ++r) out[(int64_t)r * n + g] = G[r];
+    }
+    if (ADAM) {
+        // the parameters still in registers (position, SH) are not read
+        // again; the moments of CH rows are requested before any is used, so
+        // that each wave keeps many loads in flight
+        constexpr int CH = 20;
+#pragma unroll
+        for (int r0 = 0; r0 < ROWS; r0 += CH) {
+            float mm[CH], vv[CH], pp[CH];
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int r = r0 + c;
+                if (r < ROWS) {
+                    const int64_t e = (int64_t)r * n + g;
+                    mm[c] = m[e];
+                    vv[c] = v[e];
+                    pp[c] = r == 0 ? x : r == 1 ? y : r == 2 ? z : r >= 11 ? sh[r - 11] : P[e];
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int r = r0 + c;
+                if (r < ROWS) {
+                    const int64_t e = (int64_t)r * n + g;
+                    adam1(pp[c], G[r], mm[c], vv[c], ac);
+                    P[e] = pp[c];
+                    m[e] = mm[c];
+                    v[e] = vv[c];
+                }
+            }
+        }
+    }
+}
+
+template <bool ADAM>
+static gs_status pbwd_launch(float* params, int64_t n, int32_t sh_degree, const DevCameras& dc,
+                             const uint16_t* rect, const float* grad2d, float* out, float* m, float* v,
+                             const AdamConsts& c, const int32_t* skip, hipStream_t s)
+{
+    const dim3 grid(grid_for((uint64_t)n, 256)), block(256);
+    const ShConsts K = sh_constants();
+    switch (sh_degree) {
+        case 0: hipLaunchKernelGGL((k_preprocess_bwd<0, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip); break;
+        case 1: hipLaunchKernelGGL((k_preprocess_bwd<1, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip); break;
+        case 2: hipLaunchKernelGGL((k_preprocess_bwd<2, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip); break;
+        default: hipLaunchKernelGGL((k_preprocess_bwd<3, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip); break;
+    }
+    return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
 }
 
 }  // namespace gs
@@ -242,16 +302,25 @@ gs_status gs_preprocess_bwd(const float* params, int64_t n, int32_t sh_degree, c
     DevCameras dc;
     if (!make_dev_cameras(cams, n_views, dc)) return GS_ERR_INVALID_ARGUMENT;
     if (n == 0) return GS_OK;
-    const dim3 grid(grid_for((uint64_t)n, 256)), block(256);
-    hipStream_t s = (hipStream_t)stream;
-    const ShConsts K = sh_constants();
-    switch (sh_degree) {
-        case 0: hipLaunchKernelGGL(k_preprocess_bwd<0>, grid, block, 0, s, params, n, dc, K, rect, grad2d, grad_params); break;
-        case 1: hipLaunchKernelGGL(k_preprocess_bwd<1>, grid, block, 0, s, params, n, dc, K, rect, grad2d, grad_params); break;
-        case 2: hipLaunchKernelGGL(k_preprocess_bwd<2>, grid, block, 0, s, params, n, dc, K, rect, grad2d, grad_params); break;
-        default: hipLaunchKernelGGL(k_preprocess_bwd<3>, grid, block, 0, s, params, n, dc, K, rect, grad2d, grad_params); break;
-    }
-    return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
+    return pbwd_launch<false>((float*)params, n, sh_degree, dc, rect, grad2d, grad_params, nullptr, nullptr,
+                              AdamConsts{}, nullptr, (hipStream_t)stream);
+}
+
+gs_status gs_preprocess_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs_camera* cams,
+                                 int32_t n_views, const uint16_t* rect, const float* grad2d, float* m, float* v,
+                                 double lr, double beta1, double beta2, double eps, int64_t step,
+                                 const int32_t* skip, float* grad_params, void* stream)
+{
+    if (n < 0 || sh_degree < 0 || sh_degree > 3) return GS_ERR_INVALID_ARGUMENT;
+    if (n > 0 && (!params || !rect || !grad2d || !m || !v)) return GS_ERR_INVALID_ARGUMENT;
+    if (n > ((int64_t)1 << 31)) return GS_ERR_INVALID_ARGUMENT;
+    DevCameras dc;
+    if (!make_dev_cameras(cams, n_views, dc)) return GS_ERR_INVALID_ARGUMENT;
+    AdamConsts c;
+    if (!adam_consts(lr, beta1, beta2, eps, step, c)) return GS_ERR_INVALID_ARGUMENT;
+    if (n == 0) return GS_OK;
+    return pbwd_launch<true>(params, n, sh_degree, dc, rect, grad2d, grad_params, m, v, c, skip,
+                             (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -171,13 +171,18 @@ class TrainStep:
 
     ``t`` counts the updates applied; with ``defer_count`` a call of ``step``
     may be redone later (see the module note), and ``flush`` settles every
-    step launched so far."""
+    step launched so far. With ``fused_adam`` (the default) the preprocess
+    backward applies Adam itself (``gs_preprocess_bwd_adam``) and ``grad`` is
+    not written; otherwise ``gs_preprocess_bwd`` writes ``grad`` and
+    ``gs_adam_step`` follows. ``write_image`` keeps the rendered image in
+    ``buf.image`` (the step itself needs only the loss gradient)."""
 
     RING = 4  # steps whose count and flag may be in flight
 
     def __init__(self, params: torch.Tensor, sh_degree: int, cams: Sequence, target: torch.Tensor,
                  lr=1e-3, betas=(0.9, 0.999), eps=1e-15, bg=(0.0, 0.0, 0.0),
-                 m: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None, defer_count: bool = True):
+                 m: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None, defer_count: bool = True,
+                 fused_adam: bool = True, write_image: bool = False):
         assert params.is_cuda and params.dtype == torch.float32 and params.is_contiguous()
         self.params = params
         self.sh_degree = sh_degree
@@ -186,10 +191,12 @@ class TrainStep:
         self.target = target.contiguous()
         self.m = torch.zeros_like(params) if m is None else m
         self.v = torch.zeros_like(params) if v is None else v
-        self.grad = torch.empty_like(params)
+        self.grad = None if fused_adam else torch.empty_like(params)
         self.lr, self.betas, self.eps, self.bg = lr, betas, eps, bg
         self.t = 0
         self.defer_count = defer_count
+        self.fused_adam = fused_adam
+        self.write_image = write_image
         dev = params.device
         self.sticky = torch.zeros(1, dtype=torch.int32, device=dev)  # an unverified step overflowed
         self._host = [(torch.zeros(1, dtype=torch.int64, pin_memory=True),
@@ -198,10 +205,15 @@ class TrainStep:
         self._slot = 0
         self.redone = 0  # steps redone after an overflow
 
+    @property
+    def stage_names(self):
+        """The stages that ``step(marks)`` brackets, in order."""
+        tail = ["preprocess_bwd_adam"] if self.fused_adam else ["preprocess_bwd", "adam"]
+        return ["preprocess", "intersections", "raster_fwd_loss", "grad2d_zero", "raster_bwd"] + tail
+
     def step(self, marks=None):
-        """One step. `marks`, if given, holds 8 events recorded on the stream
-        around the stages (preprocess, lists, forward + loss, 2D-gradient
-        clear, backward raster, preprocess backward, Adam)."""
+        """One step. `marks`, if given, holds len(stage_names) + 1 events,
+        recorded on the stream around the stages."""
         b = self.buf
         self._settle(block=len(self._pending) >= self.RING - 1)
         mark = (lambda i: marks[i].record()) if marks is not None else (lambda i: None)
@@ -214,7 +226,7 @@ class TrainStep:
         if deferred:
             torch.maximum(self.sticky, b.overflow, out=self.sticky)
         mark(2)
-        b.rasterize_loss_l1(self.target, self.bg)
+        b.rasterize_loss_l1(self.target, self.bg, image=self.write_image)
         mark(3)
         # the 2D-gradient buffer is cleared on its own (a launch of its own,
         # so that a timing mark can bracket the backward raster alone)
@@ -223,12 +235,20 @@ class TrainStep:
         L.gs_rasterize_bwd(b.rec, b.n, b.ranges, b.sorted_vals, b.cams, self.bg, b.T_final, b.n_contrib, b.dL,
                            b.grad2d, accumulate=True)
         mark(5)
-        L.gs_preprocess_bwd(self.params, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, self.grad)
-        mark(6)
-        args = (self.params, self.grad, self.m, self.v, self.params.numel(), self.lr, self.betas[0],
-                self.betas[1], self.eps, self.t)
+        skip = self.sticky if deferred else None
+        if self.fused_adam:
+            L.gs_preprocess_bwd_adam(self.params, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, self.m, self.v, self.lr,
+                                     self.betas[0], self.betas[1], self.eps, self.t, skip=skip)
+        else:
+            L.gs_preprocess_bwd(self.params, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, self.grad)
+            mark(6)
+            args = (self.params, self.grad, self.m, self.v, self.params.numel(), self.lr, self.betas[0],
+                    self.betas[1], self.eps, self.t)
+            if deferred:
+                L.gs_adam_step_unless(*args, skip)
+            else:
+                L.gs_adam_step(*args)
         if deferred:
-            L.gs_adam_step_unless(*args, self.sticky)
             hk, hf = self._host[self._slot]
             self._slot = (self._slot + 1) % self.RING
             hk.copy_(b.total, non_blocking=True)
@@ -236,9 +256,7 @@ class TrainStep:
             ev = torch.cuda.Event()
             ev.record()
             self._pending.append((self.t, ev, hk, hf))
-        else:
-            L.gs_adam_step(*args)
-        mark(7)
+        mark(len(self.stage_names))
 
     def flush(self):
         """Settle every launched step (waits for the GPU)."""

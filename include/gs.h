@@ -14,6 +14,7 @@
  *   gs_rasterize_bwd       back-to-front gradients to the 2D quantities
  *   gs_preprocess_bwd      gradients to all per-Gaussian parameters
  *   gs_adam_step           fused Adam update
+ *   (gs_preprocess_bwd_adam  the two calls above in one pass)
  *
  * What the pages fix, and where (the formulas themselves are readings of the
  * 3DGS method, reference [10] of "A Scalable PyTorch Abstraction for Multi-GPU
@@ -315,6 +316,24 @@ gs_status gs_rasterize_bwd(const float* rec, int64_t n, const uint32_t* ranges,
 gs_status gs_preprocess_bwd(const float* params, int64_t n, int32_t sh_degree,
                             const gs_camera* cams, int32_t n_views, const uint16_t* rect,
                             const float* grad2d, float* grad_params, void* stream);
+
+/*
+ * gs_preprocess_bwd_adam -- gs_preprocess_bwd followed by gs_adam_step over
+ * the [P][n] parameter block, in one pass: each Gaussian's gradient is applied
+ * to its parameters and moments as soon as it is formed (same arithmetic as
+ * the two calls), so it never goes through device memory.
+ *   params       in/out [P][n] fp32: read for the chain rule, then updated
+ *   m, v         in/out [P][n] fp32 Adam moments
+ *   lr .. step   as gs_adam_step
+ *   skip         device int32 or NULL: when non-zero, nothing is written (as
+ *                gs_adam_step_unless)
+ *   grad_params  out [P][n] fp32 or NULL: the gradient, if wanted
+ * Errors: as gs_preprocess_bwd and gs_adam_step (m and v must not be null).
+ */
+gs_status gs_preprocess_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs_camera* cams,
+                                 int32_t n_views, const uint16_t* rect, const float* grad2d, float* m,
+                                 float* v, double lr, double beta1, double beta2, double eps,
+                                 int64_t step, const int32_t* skip, float* grad_params, void* stream);
 
 /*
  * gs_adam_step -- Adam (Kingma & Ba, reference [12] of the fVDB page),

@@ -92,6 +92,22 @@ def gpu_preprocess_bwd(b: Buffers, params_t: torch.Tensor, grad2d_np: np.ndarray
     return np_(grad)
 
 
+def gpu_preprocess_bwd_adam(b: Buffers, params_t: torch.Tensor, grad2d_np: np.ndarray, m_np, v_np, lr, b1, b2, eps,
+                            step, skip: int = 0):
+    """The fused preprocess backward + Adam on a copy of the parameters:
+    (parameters, m, v, gradient) after the call."""
+    dev = b.device
+    b.grad2d.copy_(torch.from_numpy(np.ascontiguousarray(grad2d_np, dtype=np.float32).reshape(-1)))
+    th = params_t.clone()
+    m, v = (torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev) for a in (m_np, v_np))
+    grad = torch.full_like(params_t, 7.0)
+    flag = torch.full((1,), skip, dtype=torch.int32, device=dev)
+    L.gs_preprocess_bwd_adam(th, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, m, v, lr, b1, b2, eps, step, skip=flag,
+                             grad_params=grad)
+    torch.cuda.synchronize()
+    return np_(th), np_(m), np_(v), np_(grad)
+
+
 def gpu_forward_l1(b: Buffers, target_np, bg=(0.0, 0.0, 0.0)):
     """The fused forward + L1 pass on the lists already in `b`: image, T_final,
     n_contrib, dL/dimage and the loss."""

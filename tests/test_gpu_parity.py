@@ -109,3 +109,28 @@ def test_adam(run, step):
     ref = O.adam(theta, g, m0, v0, cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, step)
     gpu = PY.gpu_adam(theta, g, m0, v0, cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, step)
     PY.check_adam(gpu, ref, theta, g, m0, cfg.lr, cfg.beta1)
+
+
+@pytest.mark.parametrize("step", [1, 3])
+def test_preprocess_bwd_adam_fused(run, step):
+    """The fused pass writes the gradient of gs_preprocess_bwd and the update
+    of gs_adam_step (checked against the oracle's Adam on that gradient), and
+    nothing at all when its skip flag is set."""
+    cfg, b = run["cfg"], run["buf"]
+    params_t = run["gpu"]["params_t"]
+    rng = np.random.default_rng(20 + step)
+    g2 = (rng.standard_normal((b.V, b.n, 9)) * 1e-3).astype(np.float32)
+    g_sep = PY.gpu_preprocess_bwd(b, params_t, g2)
+    m0, v0 = S.adam_state(b.P, b.n, seed=None if step == 1 else 5)
+    th, m, v, g = PY.gpu_preprocess_bwd_adam(b, params_t, g2, m0, v0, cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, step)
+    gd = np.abs(g.astype(np.float64) - g_sep)
+    row = np.abs(g_sep).max(axis=1, keepdims=True).astype(np.float64)
+    print(f"fused gradient vs gs_preprocess_bwd: max abs diff {gd.max():.3e}")
+    assert np.all(gd <= 1e-6 * row)
+    ref = O.adam(run["params"], g, m0, v0, cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, step)
+    PY.check_adam((th, m, v), ref, run["params"], g, m0, cfg.lr, cfg.beta1)
+    # a set flag leaves parameters, moments and the gradient output untouched
+    th, m, v, g = PY.gpu_preprocess_bwd_adam(b, params_t, g2, m0, v0, cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, step,
+                                             skip=1)
+    assert np.array_equal(th, run["params"]) and np.array_equal(m, m0) and np.array_equal(v, v0)
+    assert np.all(g == 7.0)
