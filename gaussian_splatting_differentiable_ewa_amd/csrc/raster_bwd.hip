@@ -13,25 +13,36 @@
 //   dpower/du = -(A dx + B dy), dpower/dv = -(B dx + C dy),
 //   dpower/dA = -dx^2/2, dpower/dB = -dx dy, dpower/dC = -dy^2/2.
 //
+// Only dL/dI . S is needed, never S itself: each lane keeps that one scalar
+// (sum over channels of dL/dI_c S_c, with the same recurrence) instead of the
+// three channels.
+//
 // Each row works through its entries in sub-batches of 8, in two phases:
 //   1. pixel-parallel, entries in reverse order: every lane rebuilds
-//      T_i = T_{i+1} / (1 - a_i) and S for its pixel and writes two numbers
-//      per (pixel, entry) to LDS: (dL/da_i) G_i (zero when clamped or not
-//      blended) and a_i T_i;
+//      T_i = T_{i+1} / (1 - a_i) and dL/dI . S for its pixel and writes two
+//      numbers per (pixel, entry) to LDS: (dL/da_i) G_i (zero when clamped or
+//      not blended) and a_i T_i;
 //   2. entry-parallel: lane pairs own one entry each and sum the nine
-//      gradient terms over the sub-block's 16 pixels from those two numbers
-//      (moments of dx, dy, scaled by o at the end); one DPP step joins the
-//      pair and the pair's first lane stores the nine sums in its row's
-//      slice of an LDS table (rows never share a slice: no LDS atomics).
+//      gradient terms over 8 of the sub-block's 16 pixels from those two
+//      numbers (sums of the weight times the pixel offsets 0..3 and their
+//      products, turned into moments of dx, dy about the entry's mean, scaled
+//      by o at the end); one DPP step joins the pair, and the pair's first
+//      lane adds the nine sums into the wave's LDS table of its entry (rows
+//      holding the same entry add into the same sums: LDS float atomics).
 // No cross-lane reduction runs per (pixel, entry). After each batch of 64
-// entries each lane sums its entry over the rows that held it, and every
-// (entry, quarter) with a contribution issues its global fp32 atomics.
+// entries every entry with a contribution issues its global fp32 atomics.
+//
+// A row's list holds byte offsets of the staged records; its tail, up to the
+// longest row's count, holds an extra slot of opacity 0, which no pixel
+// blends, so phase 1 needs no per-entry bound test.
 #include "raster_common.h"
 
 namespace gs {
 
 constexpr int SUB = 8;            // entries per row per sub-batch
 constexpr int CSTRIDE = SUB + 1;  // padded slot stride of the coefficient table
+constexpr uint32_t SLOT_BYTES = 32;                   // (u v -A/2 -B) (-C/2 o r g) per slot
+constexpr uint32_t PAD_OFF = RW_BATCH * SLOT_BYTES;  // the opacity-0 slot
 
 __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restrict__ rec, int64_t n,
                                                            const uint32_t* __restrict__ ranges,
@@ -44,10 +55,10 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
 {
 #pragma clang fp contract(off)
     // about 10 KB of LDS per wave, so that 16 waves fit a CU
-    __shared__ float4 s_rec[2 * RW_BATCH];  // (u v -A/2 -B) (-C/2 o r g) per slot
-    __shared__ float s_b[RW_BATCH];         // blue of each slot
+    __shared__ float4 s_rec[2 * (RW_BATCH + 1)];  // (u v -A/2 -B) (-C/2 o r g) per slot, + the padding slot
+    __shared__ float s_b[RW_BATCH + 1];           // blue of each slot
     __shared__ uint8_t s_mask[RW_BATCH];
-    __shared__ __align__(16) uint16_t s_list[4 * RW_BATCH];  // read 8 ids at a time
+    __shared__ __align__(16) uint16_t s_list[4 * RW_BATCH];  // record byte offsets, read 8 at a time
     __shared__ float s_sum[GS_GRAD2D_ROWS][RW_BATCH];  // [gradient][slot], summed over the rows
     __shared__ float2 s_coef[4][16][CSTRIDE];          // [row][pixel][slot]
     __shared__ uint32_t s_gid[RW_BATCH];               // Gaussian of each staged slot
@@ -75,6 +86,11 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
     const int32_t wave_last = max(max(rl0, rl1), max(rl2, rl3));
     if (wave_last <= 0) return;
     const int q = t.lane & 15;
+    if (t.lane == 0) {  // the padding slot: opacity 0 (alpha 0 at every pixel)
+        s_rec[2 * RW_BATCH] = make_float4(0.f, 0.f, 0.f, 0.f);
+        s_rec[2 * RW_BATCH + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        s_b[RW_BATCH] = 0.f;
+    }
     // phase-2 lanes (e, h) sum over pixels h*8 .. h*8+7 of their row: the
     // dL/dimage of those pixels, taken from the lanes that own them
     float gh0[8], gh1[8], gh2[8];
@@ -91,9 +107,11 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
     const float sbx = (float)(t.qx0 + (t.row & 1) * 4) + 0.5f;
     const float sby = (float)(t.qy0 + (t.row >> 1) * 4) + 0.5f;
     float2(*coef)[CSTRIDE] = s_coef[t.row];
-    // colour behind the current entry, normalised by the transmittance in
-    // front of it; starts as the background behind the last blended entry
-    float acc0 = bg0, acc1 = bg1, acc2 = bg2;
+    // dL/dI . S, S the colour behind the current entry normalised by the
+    // transmittance in front of it; S starts as the background
+    float sproj = __builtin_fmaf(g2, bg2, __builtin_fmaf(g1, bg1, g0 * bg0));
+    const char* recb = (const char*)s_rec;
+    const char* bb = (const char*)s_b;
     // lane s of a batch holds list position hi - s (1-based): slots run back
     // to front. Two-stage prefetch as in the forward pass.
     Entry cur, nxt;
@@ -113,89 +131,106 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
         const int32_t p2 = hi - 2 * RW_BATCH - t.lane;
         const bool v2 = p2 >= 1;
         const uint32_t gid2 = v2 ? vals[rg.x + (uint32_t)(p2 - 1)] : 0u;
+        // per row, the staged slots in front of the row's last contributor,
+        // ascending, as record offsets; the rest of the row's list is padding
         uint32_t cnt[4];
-        rows_compact(s_mask, s_list, t.lane, cnt, [&](int s, int r) {
-            const int32_t rl = r == 0 ? rl0 : r == 1 ? rl1 : r == 2 ? rl2 : rl3;
-            return hi - s <= rl;
-        });
+        {
+            asm volatile("" ::: "memory");  // staging writes precede these reads (LDS is in order per wave)
+            const uint32_t m4 = s_mask[t.lane];
+            const int32_t pos = hi - t.lane;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int32_t rl = r == 0 ? rl0 : r == 1 ? rl1 : r == 2 ? rl2 : rl3;
+                const bool keep = ((m4 >> r) & 1u) && pos <= rl;
+                const uint64_t m = ballot(keep);
+                cnt[r] = (uint32_t)__popcll(m);
+                if (keep) s_list[r * RW_BATCH + mask_rank(m)] = (uint16_t)(t.lane * SLOT_BYTES);
+                if ((uint32_t)t.lane >= cnt[r]) s_list[r * RW_BATCH + t.lane] = (uint16_t)PAD_OFF;
+            }
+            asm volatile("" ::: "memory");  // list writes precede their reads
+        }
         const uint32_t my_cnt = t.row == 0 ? cnt[0] : t.row == 1 ? cnt[1] : t.row == 2 ? cnt[2] : cnt[3];
         const uint32_t iters = max(max(cnt[0], cnt[1]), max(cnt[2], cnt[3]));
         const uint16_t* my_list = s_list + t.row * RW_BATCH;
+        // slot k is in front of this pixel's last contributor iff hi - k <= my_last
+        const int32_t thr = (hi - my_last) * (int32_t)SLOT_BYTES;
         for (uint32_t sb = 0; sb < iters; sb += SUB) {
-            // ---- phase 1: this lane's pixel, entries sb .. sb+7 of its row.
-            // The eight slot ids come in one 16-byte read (ids past the row's
-            // count are stale and masked); each entry's record is read while
-            // the one before it is evaluated.
+            // ---- phase 1: this lane's pixel, entries sb .. sb+7 of its row
+            // (their offsets in one 16-byte read)
             const uint32_t n_sub = min((uint32_t)SUB, iters - sb);
             const uint4 ids = *(const uint4*)(my_list + sb);
             const uint32_t idw[4] = {ids.x, ids.y, ids.z, ids.w};
-            int idx_n = sb < my_cnt ? (int)(idw[0] & 0xffffu) : 0;
-            float4 n0 = s_rec[2 * idx_n], n1 = s_rec[2 * idx_n + 1];
-            float nb = s_b[idx_n];
 #pragma unroll
             for (uint32_t i = 0; i < (uint32_t)SUB; ++i) {
                 if (i >= n_sub) break;  // wave-uniform
-                const uint32_t it = sb + i;
-                const bool has = it < my_cnt;
-                const int idx = idx_n;
-                const float4 q0 = n0, q1 = n1;
-                const float qb = nb;
-                if (i + 1 < (uint32_t)SUB) {
-                    const bool hn = i + 1 < n_sub && it + 1 < my_cnt;
-                    idx_n = hn ? (int)((idw[(i + 1) >> 1] >> (16 * ((i + 1) & 1))) & 0xffffu) : 0;
-                    n0 = s_rec[2 * idx_n];
-                    n1 = s_rec[2 * idx_n + 1];
-                    nb = s_b[idx_n];
-                }
-                const int32_t pos = hi - idx;
+                const uint32_t off = (idw[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+                const float4 q0 = *(const float4*)(recb + off);
+                const float4 q1 = *(const float4*)(recb + off + 16);
+                const float qb = *(const float*)(bb + (off >> 3));
                 float dx, dy;
                 const float power = entry_power(q0, q1, t.px, t.py, dx, dy);
                 const float G = exp_fast(power);
                 const float oG = q1.y * G;
                 const float alpha = fminf(ALPHA_MAX, oG);
                 // the forward's decision for this pixel
-                const bool contrib = has && pos <= my_last && !(power > 0.f) && !(alpha < ALPHA_MIN);
+                const bool contrib = (int32_t)off >= thr && !(power > 0.f) && !(alpha < ALPHA_MIN);
                 // transmittance in front of this entry (a reciprocal: the
                 // gradients need no correctly rounded division)
                 Tr = contrib ? Tr * __builtin_amdgcn_rcpf(1.f - alpha) : Tr;
-                const float wk = contrib ? alpha * Tr : 0.f;
-                const float d0 = q1.z - acc0, d1 = q1.w - acc1, d2 = qb - acc2;
-                const float dLda = Tr * ((d0 * g0 + d1 * g1) + d2 * g2);
-                // colour behind: S' = a c + (1 - a) S = S + a (c - S), unchanged when a = 0
                 const float ak = contrib ? alpha : 0.f;
-                acc0 = __builtin_fmaf(ak, d0, acc0);
-                acc1 = __builtin_fmaf(ak, d1, acc1);
-                acc2 = __builtin_fmaf(ak, d2, acc2);
+                // dI/da = T (c - S), projected on dL/dI; then S' = S + a (c - S)
+                const float d = __builtin_fmaf(g2, qb, __builtin_fmaf(g1, q1.w, g0 * q1.z)) - sproj;
+                const float dLda = Tr * d;
+                sproj = __builtin_fmaf(ak, d, sproj);
                 const float dG = (contrib && !(oG > ALPHA_MAX)) ? dLda * G : 0.f;
-                coef[q][i] = make_float2(dG, wk);
+                coef[q][i] = make_float2(dG, ak * Tr);
             }
             asm volatile("" ::: "memory");  // phase-1 writes precede phase-2 reads (in order per wave)
-            // ---- phase 2: lanes (e, h) = (q & 7, q >> 3): entry slot e, pixels h*8 .. h*8+7
+            // ---- phase 2: lanes (e, h) = (q & 7, q >> 3): entry e of the
+            // sub-batch, pixels h*8 .. h*8+7 of the sub-block, i.e. offsets
+            // (k & 3, 2h + (k >> 2)) from its first pixel centre, k = 0..7
             const uint32_t e = (uint32_t)q & 7u, h = (uint32_t)q >> 3;
-            const bool has_e = sb + e < my_cnt;
-            const int idx = has_e ? (int)my_list[sb + e] : 0;
-            const float4 q0 = s_rec[2 * idx], q1 = s_rec[2 * idx + 1];
-            float go = 0.f, mx = 0.f, my = 0.f, mxx = 0.f, mxy = 0.f, myy = 0.f, gr = 0.f, gg = 0.f, gb = 0.f;
+            const uint32_t off_e = my_list[sb + e];
+            const float4 q0 = *(const float4*)(recb + off_e);
+            const float4 q1 = *(const float4*)(recb + off_e + 16);
+            // c: weight sums over the lane's 8 pixels, times 1, x, y, x^2, xy
+            // (y^2 = y for y in {0, 1}); w: the colour sums
+            float c0 = 0.f, cx = 0.f, cy = 0.f, cxx = 0.f, cxy = 0.f, gr = 0.f, gg = 0.f, gb = 0.f;
             if (e < n_sub) {
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
-                    const int pp = (int)h * 8 + k;  // pixel of the sub-block: (pp & 3, pp >> 2)
-                    const float2 c = coef[pp][e];
-                    const float dx = q0.x - (sbx + (float)(pp & 3));
-                    const float dy = q0.y - (sby + (float)(pp >> 2));
-                    const float cdx = c.x * dx, cdy = c.x * dy;
-                    go += c.x;
-                    mx += cdx;
-                    my += cdy;
-                    mxx = __builtin_fmaf(cdx, dx, mxx);
-                    mxy = __builtin_fmaf(cdx, dy, mxy);
-                    myy = __builtin_fmaf(cdy, dy, myy);
+                    const float2 c = coef[(int)h * 8 + k][e];
+                    const int x = k & 3;
+                    c0 += c.x;
+                    if (x == 1) {
+                        cx += c.x;
+                        cxx += c.x;
+                    } else if (x > 1) {
+                        cx = __builtin_fmaf((float)x, c.x, cx);
+                        cxx = __builtin_fmaf((float)(x * x), c.x, cxx);
+                    }
+                    if (k >= 4) {
+                        cy += c.x;
+                        if (x == 1)
+                            cxy += c.x;
+                        else if (x > 1)
+                            cxy = __builtin_fmaf((float)x, c.x, cxy);
+                    }
                     gr = __builtin_fmaf(c.y, gh0[k], gr);
                     gg = __builtin_fmaf(c.y, gh1[k], gg);
                     gb = __builtin_fmaf(c.y, gh2[k], gb);
                 }
             }
             asm volatile("" ::: "memory");  // phase-2 reads precede the next phase-1 writes
+            // moments of dx = ux - x, dy = uy - y about the mean (ux, uy) in
+            // the lane's pixel frame
+            const float ux = q0.x - sbx, uy = q0.y - (sby + (float)(2 * h));
+            float go = c0;
+            float mx = __builtin_fmaf(ux, c0, -cx);
+            float my = __builtin_fmaf(uy, c0, -cy);
+            float mxx = __builtin_fmaf(ux, __builtin_fmaf(ux, c0, -2.f * cx), cxx);
+            float mxy = __builtin_fmaf(ux, __builtin_fmaf(uy, c0, -cy), __builtin_fmaf(-uy, cx, cxy));
+            float myy = __builtin_fmaf(uy, __builtin_fmaf(uy, c0, -2.f * cy), cy);
             // join the two pixel halves of each entry (lanes q and q + 8): row_ror:8
 #define GS_ROR8(v) (v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false)))
             go = GS_ROR8(go);
@@ -208,9 +243,10 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
             gg = GS_ROR8(gg);
             gb = GS_ROR8(gb);
 #undef GS_ROR8
-            if (h == 0 && has_e) {
+            if (h == 0 && sb + e < my_cnt) {
                 // dL/dpower = (dL/da) o G: the o factor is applied here. Rows
                 // holding the same slot add into one LDS sum.
+                const int idx = (int)(off_e / SLOT_BYTES);
                 const float o = q1.y, nA = q0.z, nB = q0.w, nC = q1.x;
                 const float Mx = o * mx, My = o * my;
                 atomicAdd(&s_sum[0][idx], 2.f * nA * Mx + nB * My);  // u
