@@ -28,7 +28,8 @@
 //      products, turned into moments of dx, dy about the entry's mean, scaled
 //      by o at the end); one DPP step joins the pair, and the pair's first
 //      lane adds the nine sums into the wave's LDS table of its entry (rows
-//      holding the same entry add into the same sums: LDS float atomics).
+//      holding the same entry add into the same sums, one row after the
+//      other).
 // No cross-lane reduction runs per (pixel, entry). After each batch of 64
 // entries every entry with a contribution issues its global fp32 atomics.
 //
@@ -243,21 +244,29 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
             gg = GS_ROR8(gg);
             gb = GS_ROR8(gb);
 #undef GS_ROR8
-            if (h == 0 && sb + e < my_cnt) {
-                // dL/dpower = (dL/da) o G: the o factor is applied here. Rows
-                // holding the same slot add into one LDS sum.
-                const int idx = (int)(off_e / SLOT_BYTES);
-                const float o = q1.y, nA = q0.z, nB = q0.w, nC = q1.x;
-                const float Mx = o * mx, My = o * my;
-                atomicAdd(&s_sum[0][idx], 2.f * nA * Mx + nB * My);  // u
-                atomicAdd(&s_sum[1][idx], nB * Mx + 2.f * nC * My);  // v
-                atomicAdd(&s_sum[2][idx], -0.5f * o * mxx);          // A
-                atomicAdd(&s_sum[3][idx], -o * mxy);                 // B
-                atomicAdd(&s_sum[4][idx], -0.5f * o * myy);          // C
-                atomicAdd(&s_sum[5][idx], go);                       // opacity
-                atomicAdd(&s_sum[6][idx], gr);
-                atomicAdd(&s_sum[7][idx], gg);
-                atomicAdd(&s_sum[8][idx], gb);
+            // dL/dpower = (dL/da) o G: the o factor is applied here
+            const float o = q1.y, nA = q0.z, nB = q0.w, nC = q1.x;
+            const float Mx = o * mx, My = o * my;
+            const float gsum[GS_GRAD2D_ROWS] = {2.f * nA * Mx + nB * My,  // u
+                                                nB * Mx + 2.f * nC * My,  // v
+                                                -0.5f * o * mxx,          // A
+                                                -o * mxy,                 // B
+                                                -0.5f * o * myy,          // C
+                                                go,                       // opacity
+                                                gr, gg, gb};
+            // Rows holding the same slot add into one LDS sum, one row at a
+            // time (LDS operations of a wave complete in order; within a row
+            // the slots are distinct): plain read-add-write, which costs far
+            // less here than LDS float atomics
+            const bool own = h == 0 && sb + e < my_cnt;
+            const int idx = (int)(off_e / SLOT_BYTES);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                if (own && t.row == rr) {
+#pragma unroll
+                    for (int k = 0; k < GS_GRAD2D_ROWS; ++k) s_sum[k][idx] += gsum[k];
+                }
+                asm volatile("" ::: "memory");
             }
         }
         asm volatile("" ::: "memory");  // row sums precede the flush reads
