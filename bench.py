@@ -112,10 +112,12 @@ def stage_bytes(P, n, V, K, n_vis_per_view, n_any, n_px):
         "emit": 16 * V * n + 12 * K,          # rect + offset per pair, key + id per intersection
         "sort": 24 * K,                       # one read + one write of key + id
         "ranges": 8 * K + 8 * V * n_px // 256,
-        # forward raster with the L1 loss fused: ids, one record read per
-        # visible pair, target read, T_final + n_contrib + dL/dimage written
-        "raster_fwd_loss": 4 * K + 36 * Nv + 32 * V * n_px,
-        "raster_bwd": 4 * K + 36 * Nv + 32 * V * n_px + 36 * Nv * 2,
+        # per list entry: id read, record gathered, 16-bit sub-block mask written
+        "tile_masks": (4 + 48 + 2) * K,
+        # forward raster with the L1 loss fused: ids and masks, one record read
+        # per visible pair, target read, T_final + n_contrib + dL/dimage written
+        "raster_fwd_loss": 6 * K + 36 * Nv + 32 * V * n_px,
+        "raster_bwd": 6 * K + 36 * Nv + 32 * V * n_px + 36 * Nv * 2,
         "preprocess_bwd": Bp * n_any + 44 * Nv + Bp * n,
         "adam": 7 * Bp * n,
         # the two above in one pass: parameters read once, every (view,

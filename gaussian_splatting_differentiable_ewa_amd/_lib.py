@@ -28,7 +28,8 @@ EXPORTS = (
     "gs_abi_version", "gs_status_string", "gs_param_rows", "gs_tiles_x", "gs_tiles_y",
     "gs_sort_end_bit", "gs_preprocess_workspace_bytes", "gs_sort_workspace_bytes",
     "gs_tile_lists_workspace_bytes", "gs_rasterize_fwd_l1_workspace_bytes",
-    "gs_preprocess", "gs_emit_intersections", "gs_sort_keys", "gs_tile_lists", "gs_tile_ranges",
+    "gs_preprocess", "gs_emit_intersections", "gs_sort_keys", "gs_tile_lists", "gs_tile_ranges", "gs_tile_masks",
+    "gs_tile_masks_workspace_bytes",
     "gs_rasterize_fwd", "gs_rasterize_fwd_l1", "gs_loss_l1", "gs_rasterize_bwd", "gs_preprocess_bwd",
     "gs_adam_step", "gs_adam_step_unless", "gs_preprocess_bwd_adam",
 )
@@ -77,11 +78,13 @@ def lib():
             "gs_sort_keys": ([_P, _P, _P, _P, _U64, _I32, _P, _SZ, _P, _P], ctypes.c_int),
             "gs_tile_ranges": ([_P, _U64, _I64, _P, _P], ctypes.c_int),
             "gs_tile_lists": ([_P, _P, _I64, _I32, _I32, _I32, _P, _U64, _P, _P, _P, _SZ, _P], ctypes.c_int),
-            "gs_rasterize_fwd": ([_P, _I64, _P, _P, _P, _I32, _P, _P, _P, _P, _P], ctypes.c_int),
-            "gs_rasterize_fwd_l1": ([_P, _I64, _P, _P, _P, _I32, _P, _P, _F32, _P, _P, _P, _P, _P, _I32, _P, _SZ, _P],
-                                    ctypes.c_int),
+            "gs_tile_masks_workspace_bytes": ([_U64], _SZ),
+            "gs_tile_masks": ([_P, _I64, _P, _P, _U64, _P, _I32, _P, _P, _SZ, _P], ctypes.c_int),
+            "gs_rasterize_fwd": ([_P, _I64, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P], ctypes.c_int),
+            "gs_rasterize_fwd_l1": ([_P, _I64, _P, _P, _P, _P, _I32, _P, _P, _F32, _P, _P, _P, _P, _P, _I32, _P, _SZ,
+                                     _P], ctypes.c_int),
             "gs_loss_l1": ([_P, _P, _I64, _F32, _P, _P, _I32, _P], ctypes.c_int),
-            "gs_rasterize_bwd": ([_P, _I64, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _I32, _P], ctypes.c_int),
+            "gs_rasterize_bwd": ([_P, _I64, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _I32, _P], ctypes.c_int),
             "gs_preprocess_bwd": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P], ctypes.c_int),
             "gs_adam_step": ([_P, _P, _P, _P, _I64, _F64, _F64, _F64, _F64, _I64, _P], ctypes.c_int),
             "gs_adam_step_unless": ([_P, _P, _P, _P, _I64, _F64, _F64, _F64, _F64, _I64, _P, _P], ctypes.c_int),
@@ -193,18 +196,29 @@ def gs_tile_ranges(keys, n_keys, n_tiles_total, ranges, stream=None):
            "gs_tile_ranges")
 
 
-def gs_rasterize_fwd(rec, n, ranges, vals, cams, bg, image, T_final, n_contrib, stream=None):
+def tile_masks_workspace_bytes(capacity: int) -> int:
+    return lib().gs_tile_masks_workspace_bytes(capacity)
+
+
+def gs_tile_masks(rec, n, ranges, vals, capacity, cams, masks, ws, stream=None):
+    _check(lib().gs_tile_masks(_ptr(rec), n, _ptr(ranges), _ptr(vals), capacity, cameras(cams), len(cams),
+                               _ptr(masks), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "gs_tile_masks")
+
+
+def gs_rasterize_fwd(rec, n, ranges, vals, masks, cams, bg, image, T_final, n_contrib, stream=None):
     bgv = (ctypes.c_float * 3)(*bg)
-    _check(lib().gs_rasterize_fwd(_ptr(rec), n, _ptr(ranges), _ptr(vals), cameras(cams), len(cams), bgv,
+    _check(lib().gs_rasterize_fwd(_ptr(rec), n, _ptr(ranges), _ptr(vals), _ptr(masks), cameras(cams), len(cams), bgv,
                                   _ptr(image), _ptr(T_final), _ptr(n_contrib), _stream(stream)),
            "gs_rasterize_fwd")
 
 
-def gs_rasterize_fwd_l1(rec, n, ranges, vals, cams, bg, target, scale, image, T_final, n_contrib, dL_dimage, loss,
+def gs_rasterize_fwd_l1(rec, n, ranges, vals, masks, cams, bg, target, scale, image, T_final, n_contrib, dL_dimage, loss,
                         ws, accumulate=False, stream=None):
     """image may be None (not written)."""
     bgv = (ctypes.c_float * 3)(*bg)
-    _check(lib().gs_rasterize_fwd_l1(_ptr(rec), n, _ptr(ranges), _ptr(vals), cameras(cams), len(cams), bgv,
+    _check(lib().gs_rasterize_fwd_l1(_ptr(rec), n, _ptr(ranges), _ptr(vals), _ptr(masks), cameras(cams), len(cams),
+                                     bgv,
                                      _ptr(target), scale, _ptr(image), _ptr(T_final), _ptr(n_contrib),
                                      _ptr(dL_dimage), _ptr(loss), int(bool(accumulate)), _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream(stream)), "gs_rasterize_fwd_l1")
@@ -215,10 +229,10 @@ def gs_loss_l1(image, target, count, scale, dL_dimage, loss, accumulate=False, s
                             int(bool(accumulate)), _stream(stream)), "gs_loss_l1")
 
 
-def gs_rasterize_bwd(rec, n, ranges, vals, cams, bg, T_final, n_contrib, dL_dimage, grad2d,
+def gs_rasterize_bwd(rec, n, ranges, vals, masks, cams, bg, T_final, n_contrib, dL_dimage, grad2d,
                      accumulate=False, stream=None):
     bgv = (ctypes.c_float * 3)(*bg)
-    _check(lib().gs_rasterize_bwd(_ptr(rec), n, _ptr(ranges), _ptr(vals), cameras(cams), len(cams), bgv,
+    _check(lib().gs_rasterize_bwd(_ptr(rec), n, _ptr(ranges), _ptr(vals), _ptr(masks), cameras(cams), len(cams), bgv,
                                   _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimage), _ptr(grad2d),
                                   int(bool(accumulate)), _stream(stream)), "gs_rasterize_bwd")
 

@@ -23,10 +23,10 @@
 //      numbers per (pixel, entry) to LDS: (dL/da_i) G_i (zero when clamped or
 //      not blended) and a_i T_i;
 //   2. entry-parallel: lane pairs own one entry each and sum the nine
-//      gradient terms over 8 of the sub-block's 16 pixels from those two
-//      numbers (sums of the weight times the pixel offsets 0..3 and their
-//      products, turned into moments of dx, dy about the entry's mean, scaled
-//      by o at the end); one DPP step joins the pair, and the pair's first
+//      gradient terms over 8 of the sub-block's 16 pixels (two rows of four)
+//      from those two numbers: the moments of dx, dy, formed from the
+//      weights summed per column and per row and the 4 + 2 distinct dx and
+//      dy, scaled by o at the end; one DPP step joins the pair, and the pair's first
 //      lane adds the nine sums into the wave's LDS table of its entry (rows
 //      holding the same entry add into the same sums, one row after the
 //      other).
@@ -47,7 +47,8 @@ constexpr uint32_t PAD_OFF = RW_BATCH * SLOT_BYTES;  // the opacity-0 slot
 
 __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restrict__ rec, int64_t n,
                                                            const uint32_t* __restrict__ ranges,
-                                                           const uint32_t* __restrict__ vals, int W, int H, int TX,
+                                                           const uint32_t* __restrict__ vals,
+                                                           const uint16_t* __restrict__ masks, int W, int H, int TX,
                                                            int T, float bg0, float bg1, float bg2,
                                                            const float* __restrict__ T_final,
                                                            const int32_t* __restrict__ n_contrib,
@@ -104,9 +105,11 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
     }
     const float* rv = rec + (int64_t)t.view * n * GS_REC_FLOATS;
     float* g2d = grad2d + (int64_t)t.view * n * GS_GRAD2D_ROWS;  // [n][9] records of this view
-    // origin of this row's 4x4 sub-block (pixel centres)
+    // phase 2: pixel centres of the columns of this row's 4x4 sub-block and
+    // of the first of the lane's two rows (h = (lane & 15) >> 3)
     const float sbx = (float)(t.qx0 + (t.row & 1) * 4) + 0.5f;
-    const float sby = (float)(t.qy0 + (t.row >> 1) * 4) + 0.5f;
+    const float pxc[4] = {sbx, sbx + 1.f, sbx + 2.f, sbx + 3.f};
+    const float pyc0 = (float)(t.qy0 + (t.row >> 1) * 4 + 2 * ((t.lane & 15) >> 3)) + 0.5f;
     float2(*coef)[CSTRIDE] = s_coef[t.row];
     // dL/dI . S, S the colour behind the current entry normalised by the
     // transmittance in front of it; S starts as the background
@@ -115,23 +118,20 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
     const char* bb = (const char*)s_b;
     // lane s of a batch holds list position hi - s (1-based): slots run back
     // to front. Two-stage prefetch as in the forward pass.
-    Entry cur, nxt;
+    Entry cur, nxt, nx2;
     {
         const int32_t p0 = wave_last - t.lane, p1 = wave_last - RW_BATCH - t.lane;
-        cur.valid = p0 >= 1;
-        cur.gid = cur.valid ? vals[rg.x + (uint32_t)(p0 - 1)] : 0u;
+        load_entry(cur, p0 >= 1, rg.x + (uint32_t)(p0 - 1), vals, masks, t);
         gather_record(cur, rv);
-        nxt.valid = p1 >= 1;
-        nxt.gid = nxt.valid ? vals[rg.x + (uint32_t)(p1 - 1)] : 0u;
+        load_entry(nxt, p1 >= 1, rg.x + (uint32_t)(p1 - 1), vals, masks, t);
     }
     for (int32_t hi = wave_last; hi >= 1; hi -= RW_BATCH) {
-        stage_entry_pair(cur, t.lane, t, W, H, s_rec, s_b, s_mask);
+        stage_entry_pair(cur, t.lane, s_rec, s_b, s_mask);
 #pragma unroll
         for (int k = 0; k < GS_GRAD2D_ROWS; ++k) s_sum[k][t.lane] = 0.f;
         gather_record(nxt, rv);
         const int32_t p2 = hi - 2 * RW_BATCH - t.lane;
-        const bool v2 = p2 >= 1;
-        const uint32_t gid2 = v2 ? vals[rg.x + (uint32_t)(p2 - 1)] : 0u;
+        load_entry(nx2, p2 >= 1, rg.x + (uint32_t)(p2 - 1), vals, masks, t);
         // per row, the staged slots in front of the row's last contributor,
         // ascending, as record offsets; the rest of the row's list is padding
         uint32_t cnt[4];
@@ -194,44 +194,45 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
             const uint32_t off_e = my_list[sb + e];
             const float4 q0 = *(const float4*)(recb + off_e);
             const float4 q1 = *(const float4*)(recb + off_e + 16);
-            // c: weight sums over the lane's 8 pixels, times 1, x, y, x^2, xy
-            // (y^2 = y for y in {0, 1}); w: the colour sums
-            float c0 = 0.f, cx = 0.f, cy = 0.f, cxx = 0.f, cxy = 0.f, gr = 0.f, gg = 0.f, gb = 0.f;
+            // the lane's 8 pixels are columns x = 0..3 of rows y = 0, 1 (of
+            // its half of the sub-block): with dx_x = u - (x centre) and dy_y
+            // = v - (y centre), each moment is a sum of weight times products
+            // of dx_x, dy_y, formed from per-column and per-row weight sums
+            // (dx, dy exactly as in a per-pixel sum: no expansion about a
+            // far-away origin, whose terms would cancel)
+            float cw[8], gr = 0.f, gg = 0.f, gb = 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) cw[k] = 0.f;
             if (e < n_sub) {
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     const float2 c = coef[(int)h * 8 + k][e];
-                    const int x = k & 3;
-                    c0 += c.x;
-                    if (x == 1) {
-                        cx += c.x;
-                        cxx += c.x;
-                    } else if (x > 1) {
-                        cx = __builtin_fmaf((float)x, c.x, cx);
-                        cxx = __builtin_fmaf((float)(x * x), c.x, cxx);
-                    }
-                    if (k >= 4) {
-                        cy += c.x;
-                        if (x == 1)
-                            cxy += c.x;
-                        else if (x > 1)
-                            cxy = __builtin_fmaf((float)x, c.x, cxy);
-                    }
+                    cw[k] = c.x;
                     gr = __builtin_fmaf(c.y, gh0[k], gr);
                     gg = __builtin_fmaf(c.y, gh1[k], gg);
                     gb = __builtin_fmaf(c.y, gh2[k], gb);
                 }
             }
             asm volatile("" ::: "memory");  // phase-2 reads precede the next phase-1 writes
-            // moments of dx = ux - x, dy = uy - y about the mean (ux, uy) in
-            // the lane's pixel frame
-            const float ux = q0.x - sbx, uy = q0.y - (sby + (float)(2 * h));
-            float go = c0;
-            float mx = __builtin_fmaf(ux, c0, -cx);
-            float my = __builtin_fmaf(uy, c0, -cy);
-            float mxx = __builtin_fmaf(ux, __builtin_fmaf(ux, c0, -2.f * cx), cxx);
-            float mxy = __builtin_fmaf(ux, __builtin_fmaf(uy, c0, -cy), __builtin_fmaf(-uy, cx, cxy));
-            float myy = __builtin_fmaf(uy, __builtin_fmaf(uy, c0, -2.f * cy), cy);
+            float dxs[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) dxs[x] = q0.x - pxc[x];
+            const float dy0 = q0.y - pyc0, dy1 = q0.y - (pyc0 + 1.f);
+            float t0 = cw[0] * dxs[0], t1 = cw[4] * dxs[0], r0 = cw[0], r1 = cw[4];
+            float mxx = (cw[0] + cw[4]) * (dxs[0] * dxs[0]);
+#pragma unroll
+            for (int x = 1; x < 4; ++x) {
+                t0 = __builtin_fmaf(cw[x], dxs[x], t0);
+                t1 = __builtin_fmaf(cw[4 + x], dxs[x], t1);
+                r0 += cw[x];
+                r1 += cw[4 + x];
+                mxx = __builtin_fmaf(cw[x] + cw[4 + x], dxs[x] * dxs[x], mxx);
+            }
+            float go = r0 + r1;
+            float mx = t0 + t1;
+            float my = __builtin_fmaf(r0, dy0, r1 * dy1);
+            float mxy = __builtin_fmaf(t0, dy0, t1 * dy1);
+            float myy = __builtin_fmaf(r0, dy0 * dy0, r1 * (dy1 * dy1));
             // join the two pixel halves of each entry (lanes q and q + 8): row_ror:8
 #define GS_ROR8(v) (v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false)))
             go = GS_ROR8(go);
@@ -297,8 +298,9 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_bwd(const float* __restri
         }
         asm volatile("" ::: "memory");
         cur = nxt;
-        nxt.valid = v2;
-        nxt.gid = gid2;
+        nxt.valid = nx2.valid;
+        nxt.gid = nx2.gid;
+        nxt.m4 = nx2.m4;
     }
 }
 
@@ -309,12 +311,12 @@ using namespace gs;
 extern "C" {
 
 gs_status gs_rasterize_bwd(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
-                           const gs_camera* cams, int32_t n_views, const float* bg, const float* T_final,
+                           const uint16_t* masks, const gs_camera* cams, int32_t n_views, const float* bg, const float* T_final,
                            const int32_t* n_contrib, const float* dL_dimage, float* grad2d, int32_t accumulate,
                            void* stream)
 {
     RasterArgs a;
-    if (!raster_args(rec, n, ranges, vals, cams, n_views, bg, a)) return GS_ERR_INVALID_ARGUMENT;
+    if (!raster_args(rec, n, ranges, vals, masks, cams, n_views, bg, a)) return GS_ERR_INVALID_ARGUMENT;
     if (!T_final || !n_contrib || !dL_dimage || (n > 0 && !grad2d)) return GS_ERR_INVALID_ARGUMENT;
     hipStream_t s = (hipStream_t)stream;
     if (!accumulate && n > 0) {
@@ -322,7 +324,7 @@ gs_status gs_rasterize_bwd(const float* rec, int64_t n, const uint32_t* ranges, 
             return GS_ERR_HIP;
     }
     hipLaunchKernelGGL(k_raster_bwd, dim3((unsigned)a.n_blocks), dim3(RW_THREADS), 0, s, rec, n, ranges, vals,
-                       a.dc.width, a.dc.height, a.dc.tiles_x, a.dc.tiles_per_view, bg[0], bg[1], bg[2], T_final,
+                       masks, a.dc.width, a.dc.height, a.dc.tiles_x, a.dc.tiles_per_view, bg[0], bg[1], bg[2], T_final,
                        n_contrib, dL_dimage, grad2d);
     return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
 }

@@ -34,6 +34,7 @@ __device__ __forceinline__ uint32_t xcd_chunked(uint32_t bid, uint32_t nblocks)
 struct QuarterCtx {
     uint32_t view, tile_lin;  // tile_lin = view * tiles_per_view + tile
     int qx0, qy0;             // quarter origin (pixels)
+    int mshift;               // bit of the quarter's first sub-block in a 16-bit tile mask
     int lane, row;            // row = 16-lane DPP row = 4x4 sub-block (row & 1, row >> 1)
     int i, j;                 // this lane's pixel: (lane & 3, (lane >> 2) & 3) within the sub-block
     bool inside;
@@ -52,6 +53,7 @@ __device__ __forceinline__ QuarterCtx quarter_ctx(int W, int H, int TX, int T)
     const uint32_t ty = tile / (uint32_t)TX, tx = tile - ty * (uint32_t)TX;
     t.qx0 = (int)tx * 16 + (int)(quad & 1u) * 8;
     t.qy0 = (int)ty * 16 + (int)(quad >> 1) * 8;
+    t.mshift = (int)(quad >> 1) * 8 + (int)(quad & 1u) * 2;
     t.lane = (int)threadIdx.x;
     t.row = t.lane >> 4;
     const int q = t.lane & 15;
@@ -64,13 +66,35 @@ __device__ __forceinline__ QuarterCtx quarter_ctx(int W, int H, int TX, int T)
     return t;
 }
 
-// One list entry on its way from global memory to LDS.
+// One list entry on its way from global memory to LDS. An entry is valid
+// when it lies in the list and its sub-block mask meets this quarter; only
+// valid entries are gathered.
 struct Entry {
     float4 a, b, c;  // record: (u v A B) (C o r g) (b ex ey z)
     uint32_t gid;
+    uint32_t m4;     // the quarter's 4 bits of the entry's tile mask
     bool valid;
 };
 
+// The quarter's 4 sub-block bits (row r = sub-block (r & 1, r >> 1)) of a
+// 16-bit tile mask (bit 4 sy + sx for sub-block (sx, sy) of the tile).
+__device__ __forceinline__ uint32_t quarter_bits(uint32_t m16, const QuarterCtx& t)
+{
+    const uint32_t m = m16 >> t.mshift;
+    return (m & 3u) | ((m >> 2) & 0xcu);
+}
+
+// Id and mask of list position p (when in the list), for this quarter.
+__device__ __forceinline__ void load_entry(Entry& E, bool in_list, uint32_t p, const uint32_t* __restrict__ vals,
+                                           const uint16_t* __restrict__ masks, const QuarterCtx& t)
+{
+    E.m4 = in_list ? quarter_bits(masks[p], t) : 0u;
+    E.valid = E.m4 != 0u;
+    E.gid = E.valid ? vals[p] : 0u;
+}
+
+// An invalid entry gets a zero record (opacity 0): a kernel may evaluate a
+// staged slot that no row holds, and must find finite values there.
 __device__ __forceinline__ void gather_record(Entry& E, const float* __restrict__ rv)
 {
     if (E.valid) {
@@ -78,23 +102,20 @@ __device__ __forceinline__ void gather_record(Entry& E, const float* __restrict_
         E.a = rp[0];
         E.b = rp[1];
         E.c = rp[2];
+    } else {
+        E.a = E.b = E.c = make_float4(0.f, 0.f, 0.f, 0.f);
     }
 }
 
 // Stage the lane's entry at slot `s`: (u, v, -A/2, -B) (-C/2, o, r, g)
-// (b, -, -, -), and the 4-bit mask of the quarter's 4x4 sub-blocks (clipped
-// to the image) whose pixel centres the entry's alpha >= 1/255 region
-// touches; an invalid entry gets mask 0.
-template <bool REFINE>
-__device__ __forceinline__ uint32_t entry_mask(const Entry& E, const QuarterCtx& t, int W, int H);
-
-__device__ __forceinline__ void stage_entry(const Entry& E, int s, const QuarterCtx& t, int W, int H,
-                                            float4* __restrict__ s_rec, uint8_t* __restrict__ s_mask)
+// (b, -, -, -), and its 4 sub-block bits for this quarter (0 if invalid).
+__device__ __forceinline__ void stage_entry(const Entry& E, int s, float4* __restrict__ s_rec,
+                                            uint8_t* __restrict__ s_mask)
 {
     s_rec[3 * s + 0] = make_float4(E.a.x, E.a.y, -0.5f * E.a.z, -E.a.w);
     s_rec[3 * s + 1] = make_float4(-0.5f * E.b.x, E.b.y, E.b.z, E.b.w);
     s_rec[3 * s + 2] = make_float4(E.c.x, 0.f, 0.f, 0.f);
-    s_mask[s] = (uint8_t)entry_mask<false>(E, t, W, H);
+    s_mask[s] = (uint8_t)(E.valid ? E.m4 : 0u);
 }
 
 // Smallest value of Q(X, y) = A X^2 + 2 B X y + C y^2 over y in [y0, y1]
@@ -135,38 +156,41 @@ __device__ __forceinline__ bool conic_meets_rect(float u, float v, float A, floa
     return q <= tau + 1e-5f * mag;
 }
 
-// The 4-bit sub-block mask of the lane's entry (see stage_entry): the
-// record's axis-aligned alpha extent box, then, with REFINE, the ellipse
-// itself against each remaining sub-block's rectangle of pixel centres (worth
-// its cost where a (row, entry) pair costs more than the test).
-template <bool REFINE>
-__device__ __forceinline__ uint32_t entry_mask(const Entry& E, const QuarterCtx& t, int W, int H)
+// The 16-bit mask of a list entry in its tile (tile origin (tx0, ty0)
+// pixels): bit 4 sy + sx is set when the entry's alpha >= 1/255 region may
+// touch a pixel centre of the 4x4 sub-block (sx, sy). First the record's
+// axis-aligned alpha extent box against the sub-blocks' rectangles of pixel
+// centres (clipped to the image; sub-blocks outside it get 0), then the
+// ellipse itself against each remaining rectangle, so that an entry is
+// dropped from a sub-block only where its alpha is below 1/255 at every
+// pixel: skipping it there leaves every result unchanged.
+__device__ __forceinline__ uint32_t tile_mask16(const Entry& E, int tx0, int ty0, int W, int H)
 {
+    const float lo_x = E.a.x - E.c.y, hi_x = E.a.x + E.c.y, lo_y = E.a.y - E.c.z, hi_y = E.a.y + E.c.z;
+    float x0[4], x1[4], y0[4], y1[4];
+    uint32_t xm = 0, ym = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int bx = tx0 + 4 * k, by = ty0 + 4 * k;
+        x0[k] = (float)bx + 0.5f;
+        x1[k] = (float)min(bx + 4, W) - 0.5f;
+        y0[k] = (float)by + 0.5f;
+        y1[k] = (float)min(by + 4, H) - 0.5f;
+        xm |= (uint32_t)(bx < W && hi_x >= x0[k] && lo_x <= x1[k]) << k;
+        ym |= (uint32_t)(by < H && hi_y >= y0[k] && lo_y <= y1[k]) << k;
+    }
     uint32_t mask = 0;
-    if (E.valid) {
-        const float lo_x = E.a.x - E.c.y, hi_x = E.a.x + E.c.y, lo_y = E.a.y - E.c.z, hi_y = E.a.y + E.c.z;
-        float x0[2], x1[2], y0[2], y1[2];
-        uint32_t xm = 0, ym = 0;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            x0[k] = (float)(t.qx0 + 4 * k) + 0.5f;
-            x1[k] = (float)min(t.qx0 + 4 * k + 4, W) - 0.5f;
-            y0[k] = (float)(t.qy0 + 4 * k) + 0.5f;
-            y1[k] = (float)min(t.qy0 + 4 * k + 4, H) - 0.5f;
-            xm |= (uint32_t)(hi_x >= x0[k] && lo_x <= x1[k]) << k;
-            ym |= (uint32_t)(hi_y >= y0[k] && lo_y <= y1[k]) << k;
-        }
-        mask = (xm & ym & 1u) | (((xm >> 1) & ym & 1u) << 1) | ((xm & (ym >> 1) & 1u) << 2) |
-               (((xm >> 1) & (ym >> 1) & 1u) << 3);
-        if (REFINE && mask) {
-            // the threshold of the record's extent, widened a little more
-            const float tau = 2.f * __logf(255.f * E.b.y) * 1.004f + 0.02f;
+    for (int sy = 0; sy < 4; ++sy)
+        if ((ym >> sy) & 1u) mask |= xm << (4 * sy);
+    if (mask) {
+        // the threshold of the record's extent, widened a little more
+        const float tau = 2.f * __logf(255.f * E.b.y) * 1.004f + 0.02f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (((mask >> r) & 1u) &&
-                    !conic_meets_rect(E.a.x, E.a.y, E.a.z, E.a.w, E.b.x, tau, x0[r & 1], x1[r & 1], y0[r >> 1], y1[r >> 1]))
-                    mask &= ~(1u << r);
-            }
+        for (int b = 0; b < 16; ++b) {
+            if (((mask >> b) & 1u) &&
+                !conic_meets_rect(E.a.x, E.a.y, E.a.z, E.a.w, E.b.x, tau, x0[b & 3], x1[b & 3], y0[b >> 2], y1[b >> 2]))
+                mask &= ~(1u << b);
         }
     }
     return mask;
@@ -174,14 +198,13 @@ __device__ __forceinline__ uint32_t entry_mask(const Entry& E, const QuarterCtx&
 
 // As stage_entry, with the record in two vectors (u v -A/2 -B) (-C/2 o r g)
 // and blue in its own array.
-__device__ __forceinline__ void stage_entry_pair(const Entry& E, int s, const QuarterCtx& t, int W, int H,
-                                                 float4* __restrict__ s_rec, float* __restrict__ s_b,
-                                                 uint8_t* __restrict__ s_mask)
+__device__ __forceinline__ void stage_entry_pair(const Entry& E, int s, float4* __restrict__ s_rec,
+                                                 float* __restrict__ s_b, uint8_t* __restrict__ s_mask)
 {
     s_rec[2 * s + 0] = make_float4(E.a.x, E.a.y, -0.5f * E.a.z, -E.a.w);
     s_rec[2 * s + 1] = make_float4(-0.5f * E.b.x, E.b.y, E.b.z, E.b.w);
     s_b[s] = E.c.x;
-    s_mask[s] = (uint8_t)entry_mask<true>(E, t, W, H);
+    s_mask[s] = (uint8_t)(E.valid ? E.m4 : 0u);
 }
 
 // Per-row compaction of the 64 staged entries: for row r, the slots
@@ -225,10 +248,11 @@ struct RasterArgs {
 };
 
 static inline bool raster_args(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
-                               const gs_camera* cams, int32_t n_views, const float* bg, RasterArgs& a)
+                               const uint16_t* masks, const gs_camera* cams, int32_t n_views, const float* bg,
+                               RasterArgs& a)
 {
     if (n < 0 || !ranges || !bg) return false;
-    if (n > 0 && (!rec || !vals)) return false;
+    if (n > 0 && (!rec || !vals || !masks)) return false;
     if (!make_dev_cameras(cams, n_views, a.dc)) return false;
     a.n_blocks = (int64_t)n_views * a.dc.tiles_per_view * 4;
     return a.n_blocks < ((int64_t)1 << 31);

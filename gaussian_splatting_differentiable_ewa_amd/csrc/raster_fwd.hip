@@ -40,7 +40,8 @@ namespace gs {
 template <bool L1>
 __device__ __forceinline__ void raster_fwd_body(const float* __restrict__ rec, int64_t n,
                                                 const uint32_t* __restrict__ ranges,
-                                                const uint32_t* __restrict__ vals, int W, int H, int TX, int T,
+                                                const uint32_t* __restrict__ vals,
+                                                const uint16_t* __restrict__ masks, int W, int H, int TX, int T,
                                                 float bg0, float bg1, float bg2, float* __restrict__ image,
                                                 float* __restrict__ T_final, int32_t* __restrict__ n_contrib,
                                                 const float* __restrict__ target, float scale,
@@ -71,19 +72,16 @@ __device__ __forceinline__ void raster_fwd_body(const float* __restrict__ rec, i
     bool done = !t.inside;
     // two-stage prefetch: records of batch k+1 and ids of batch k+2 are
     // requested while batch k is evaluated
-    Entry cur, nxt;
-    cur.valid = rg.x + t.lane < rg.y;
-    cur.gid = cur.valid ? vals[rg.x + t.lane] : 0u;
+    Entry cur, nxt, nx2;
+    load_entry(cur, rg.x + t.lane < rg.y, rg.x + t.lane, vals, masks, t);
     gather_record(cur, rv);
-    nxt.valid = rg.x + RW_BATCH + t.lane < rg.y;
-    nxt.gid = nxt.valid ? vals[rg.x + RW_BATCH + t.lane] : 0u;
+    load_entry(nxt, rg.x + RW_BATCH + t.lane < rg.y, rg.x + RW_BATCH + t.lane, vals, masks, t);
     for (uint32_t base = rg.x; base < rg.y; base += RW_BATCH) {
         if (ballot(!done) == 0ull) break;
-        stage_entry(cur, t.lane, t, W, H, s_rec, s_mask);
+        stage_entry(cur, t.lane, s_rec, s_mask);
         gather_record(nxt, rv);
         const uint32_t j2 = base + 2 * RW_BATCH + t.lane;
-        const bool v2 = j2 < rg.y;
-        const uint32_t gid2 = v2 ? vals[j2] : 0u;
+        load_entry(nx2, j2 < rg.y, j2, vals, masks, t);
         uint32_t cnt[4];
         rows_compact(s_mask, s_list, t.lane, cnt, [](int, int) { return true; });
         const uint32_t my_cnt = t.row == 0 ? cnt[0] : t.row == 1 ? cnt[1] : t.row == 2 ? cnt[2] : cnt[3];
@@ -132,8 +130,9 @@ __device__ __forceinline__ void raster_fwd_body(const float* __restrict__ rec, i
         }
         asm volatile("" ::: "memory");  // this batch's LDS reads precede the next staging
         cur = nxt;
-        nxt.valid = v2;
-        nxt.gid = gid2;
+        nxt.valid = nx2.valid;
+        nxt.gid = nx2.gid;
+        nxt.m4 = nx2.m4;
     }
     float ad = 0.f;  // |I - I*| summed over the channels
     if (t.inside) {
@@ -166,25 +165,27 @@ __device__ __forceinline__ void raster_fwd_body(const float* __restrict__ rec, i
 
 __global__ __launch_bounds__(RW_THREADS) void k_raster_fwd(const float* __restrict__ rec, int64_t n,
                                                            const uint32_t* __restrict__ ranges,
-                                                           const uint32_t* __restrict__ vals, int W, int H, int TX,
+                                                           const uint32_t* __restrict__ vals,
+                                                           const uint16_t* __restrict__ masks, int W, int H, int TX,
                                                            int T, float bg0, float bg1, float bg2,
                                                            float* __restrict__ image, float* __restrict__ T_final,
                                                            int32_t* __restrict__ n_contrib)
 {
-    raster_fwd_body<false>(rec, n, ranges, vals, W, H, TX, T, bg0, bg1, bg2, image, T_final, n_contrib, nullptr, 0.f,
+    raster_fwd_body<false>(rec, n, ranges, vals, masks, W, H, TX, T, bg0, bg1, bg2, image, T_final, n_contrib, nullptr, 0.f,
                            nullptr, nullptr);
 }
 
 __global__ __launch_bounds__(RW_THREADS) void k_raster_fwd_l1(const float* __restrict__ rec, int64_t n,
                                                               const uint32_t* __restrict__ ranges,
-                                                              const uint32_t* __restrict__ vals, int W, int H, int TX,
+                                                              const uint32_t* __restrict__ vals,
+                                                              const uint16_t* __restrict__ masks, int W, int H, int TX,
                                                               int T, float bg0, float bg1, float bg2,
                                                               float* __restrict__ image, float* __restrict__ T_final,
                                                               int32_t* __restrict__ n_contrib,
                                                               const float* __restrict__ target, float scale,
                                                               float* __restrict__ dL, double* __restrict__ partial)
 {
-    raster_fwd_body<true>(rec, n, ranges, vals, W, H, TX, T, bg0, bg1, bg2, image, T_final, n_contrib, target, scale,
+    raster_fwd_body<true>(rec, n, ranges, vals, masks, W, H, TX, T, bg0, bg1, bg2, image, T_final, n_contrib, target, scale,
                           dL, partial);
 }
 
@@ -219,18 +220,18 @@ size_t gs_rasterize_fwd_l1_workspace_bytes(int32_t n_views, int32_t width, int32
 }
 
 gs_status gs_rasterize_fwd_l1(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
-                              const gs_camera* cams, int32_t n_views, const float* bg, const float* target,
+                              const uint16_t* masks, const gs_camera* cams, int32_t n_views, const float* bg, const float* target,
                               float scale, float* image, float* T_final, int32_t* n_contrib, float* dL_dimage,
                               double* loss, int32_t accumulate, void* ws, size_t ws_bytes, void* stream)
 {
     RasterArgs a;
-    if (!raster_args(rec, n, ranges, vals, cams, n_views, bg, a)) return GS_ERR_INVALID_ARGUMENT;
+    if (!raster_args(rec, n, ranges, vals, masks, cams, n_views, bg, a)) return GS_ERR_INVALID_ARGUMENT;
     if (!T_final || !n_contrib || !target || !dL_dimage || !loss || !ws) return GS_ERR_INVALID_ARGUMENT;
     if (ws_bytes < (size_t)a.n_blocks * sizeof(double)) return GS_ERR_INVALID_ARGUMENT;
     hipStream_t s = (hipStream_t)stream;
     double* partial = (double*)ws;
     hipLaunchKernelGGL(k_raster_fwd_l1, dim3((unsigned)a.n_blocks), dim3(RW_THREADS), 0, s, rec, n, ranges, vals,
-                       a.dc.width, a.dc.height, a.dc.tiles_x, a.dc.tiles_per_view, bg[0], bg[1], bg[2], image, T_final,
+                       masks, a.dc.width, a.dc.height, a.dc.tiles_x, a.dc.tiles_per_view, bg[0], bg[1], bg[2], image, T_final,
                        n_contrib, target, scale, dL_dimage, partial);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     if (!accumulate && fill_u32((uint32_t*)loss, 2, 0u, s) != hipSuccess) return GS_ERR_HIP;
@@ -240,14 +241,14 @@ gs_status gs_rasterize_fwd_l1(const float* rec, int64_t n, const uint32_t* range
 }
 
 gs_status gs_rasterize_fwd(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
-                           const gs_camera* cams, int32_t n_views, const float* bg, float* image, float* T_final,
+                           const uint16_t* masks, const gs_camera* cams, int32_t n_views, const float* bg, float* image, float* T_final,
                            int32_t* n_contrib, void* stream)
 {
     RasterArgs a;
-    if (!raster_args(rec, n, ranges, vals, cams, n_views, bg, a)) return GS_ERR_INVALID_ARGUMENT;
+    if (!raster_args(rec, n, ranges, vals, masks, cams, n_views, bg, a)) return GS_ERR_INVALID_ARGUMENT;
     if (!image || !T_final || !n_contrib) return GS_ERR_INVALID_ARGUMENT;
     hipLaunchKernelGGL(k_raster_fwd, dim3((unsigned)a.n_blocks), dim3(RW_THREADS), 0, (hipStream_t)stream, rec, n,
-                       ranges, vals, a.dc.width, a.dc.height, a.dc.tiles_x, a.dc.tiles_per_view, bg[0], bg[1], bg[2],
+                       ranges, vals, masks, a.dc.width, a.dc.height, a.dc.tiles_x, a.dc.tiles_per_view, bg[0], bg[1], bg[2],
                        image, T_final, n_contrib);
     return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
 }

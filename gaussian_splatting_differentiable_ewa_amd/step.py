@@ -74,6 +74,8 @@ class Buffers:
         cap = max(int(K * slack) + 4096, self.capacity)
         dev = self.device
         self.vals = torch.empty(cap, dtype=torch.int32, device=dev)
+        self.masks = torch.empty(cap, dtype=torch.int16, device=dev)
+        self.tm_ws = torch.empty(L.tile_masks_workspace_bytes(cap), dtype=torch.uint8, device=dev)
         self.allocated_for = self.path
         if self.path == "radix":
             self.keys = torch.empty(cap, dtype=torch.int64, device=dev)
@@ -90,8 +92,8 @@ class Buffers:
         if self.capacity == 0:
             return 0
         if self.path == "radix":
-            return 2 * 12 * self.capacity + self.sort_ws.numel()
-        return 4 * self.capacity + self.tl_ws.numel()
+            return 2 * 12 * self.capacity + 6 * self.capacity + self.sort_ws.numel()
+        return 10 * self.capacity + self.tl_ws.numel()
 
     @property
     def sorted_keys(self):
@@ -111,9 +113,19 @@ class Buffers:
         return self.path == "binned" and self.capacity > 0 and self.lists != "radix"
 
     def intersections(self, read_count: bool = True):
-        """Build the per-tile lists and their ranges: read K first, or (with
-        read_count False and lists_without_count()) build them with the
-        present capacity; the overflow flag then tells whether K fitted."""
+        """Build the per-tile lists, their ranges and sub-block masks: read K
+        first, or (with read_count False and lists_without_count()) build
+        them with the present capacity; the overflow flag then tells whether
+        K fitted."""
+        self.build_lists(read_count)
+        self.tile_masks()
+
+    def tile_masks(self):
+        L.gs_tile_masks(self.rec, self.n, self.ranges, self.sorted_vals, self.capacity, self.cams, self.masks,
+                        self.tm_ws)
+
+    def build_lists(self, read_count: bool = True):
+        """The lists and ranges alone (see ``intersections``)."""
         if not read_count and self.lists_without_count():
             L.gs_tile_lists(self.rec, self.rect, self.n, self.V, self.W, self.H, self.vals, self.capacity,
                             self.ranges, self.overflow, self.tl_ws)
@@ -136,7 +148,7 @@ class Buffers:
         L.gs_tile_ranges(self.sorted_keys, self.K, self.V * self.T, self.ranges)
 
     def rasterize(self, bg=(0.0, 0.0, 0.0)):
-        L.gs_rasterize_fwd(self.rec, self.n, self.ranges, self.sorted_vals, self.cams, bg, self.image,
+        L.gs_rasterize_fwd(self.rec, self.n, self.ranges, self.sorted_vals, self.masks, self.cams, bg, self.image,
                            self.T_final, self.n_contrib)
 
     def loss_l1(self, target):
@@ -147,12 +159,12 @@ class Buffers:
         """Forward raster and L1 loss in one pass; the image is written only
         when asked for."""
         scale = 1.0 / (3.0 * self.H * self.W * self.V)
-        L.gs_rasterize_fwd_l1(self.rec, self.n, self.ranges, self.sorted_vals, self.cams, bg, target, scale,
+        L.gs_rasterize_fwd_l1(self.rec, self.n, self.ranges, self.sorted_vals, self.masks, self.cams, bg, target, scale,
                               self.image if image else None, self.T_final, self.n_contrib, self.dL, self.loss,
                               self.fwd_l1_ws)
 
     def backward(self, params, grad, bg=(0.0, 0.0, 0.0)):
-        L.gs_rasterize_bwd(self.rec, self.n, self.ranges, self.sorted_vals, self.cams, bg, self.T_final,
+        L.gs_rasterize_bwd(self.rec, self.n, self.ranges, self.sorted_vals, self.masks, self.cams, bg, self.T_final,
                            self.n_contrib, self.dL, self.grad2d)
         L.gs_preprocess_bwd(params, self.n, self.sh_degree, self.cams, self.rect, self.grad2d, grad)
 
@@ -209,7 +221,7 @@ class TrainStep:
     def stage_names(self):
         """The stages that ``step(marks)`` brackets, in order."""
         tail = ["preprocess_bwd_adam"] if self.fused_adam else ["preprocess_bwd", "adam"]
-        return ["preprocess", "intersections", "raster_fwd_loss", "grad2d_zero", "raster_bwd"] + tail
+        return ["preprocess", "intersections", "tile_masks", "raster_fwd_loss", "grad2d_zero", "raster_bwd"] + tail
 
     def step(self, marks=None):
         """One step. `marks`, if given, holds len(stage_names) + 1 events,
@@ -222,26 +234,28 @@ class TrainStep:
         mark(0)
         b.preprocess(self.params)
         mark(1)
-        b.intersections(read_count=not deferred)
+        b.build_lists(read_count=not deferred)
         if deferred:
             torch.maximum(self.sticky, b.overflow, out=self.sticky)
         mark(2)
-        b.rasterize_loss_l1(self.target, self.bg, image=self.write_image)
+        b.tile_masks()
         mark(3)
+        b.rasterize_loss_l1(self.target, self.bg, image=self.write_image)
+        mark(4)
         # the 2D-gradient buffer is cleared on its own (a launch of its own,
         # so that a timing mark can bracket the backward raster alone)
         b.grad2d.zero_()
-        mark(4)
-        L.gs_rasterize_bwd(b.rec, b.n, b.ranges, b.sorted_vals, b.cams, self.bg, b.T_final, b.n_contrib, b.dL,
-                           b.grad2d, accumulate=True)
         mark(5)
+        L.gs_rasterize_bwd(b.rec, b.n, b.ranges, b.sorted_vals, b.masks, b.cams, self.bg, b.T_final, b.n_contrib, b.dL,
+                           b.grad2d, accumulate=True)
+        mark(6)
         skip = self.sticky if deferred else None
         if self.fused_adam:
             L.gs_preprocess_bwd_adam(self.params, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, self.m, self.v, self.lr,
                                      self.betas[0], self.betas[1], self.eps, self.t, skip=skip)
         else:
             L.gs_preprocess_bwd(self.params, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, self.grad)
-            mark(6)
+            mark(7)
             args = (self.params, self.grad, self.m, self.v, self.params.numel(), self.lr, self.betas[0],
                     self.betas[1], self.eps, self.t)
             if deferred:

@@ -8,6 +8,8 @@
  *   gs_emit_intersections  one (tile, depth) key per Gaussian-tile overlap
  *   gs_sort_keys           LSD radix sort of the keys with their payloads
  *   gs_tile_ranges         [start, end) of each tile in the sorted list
+ *   (gs_tile_lists         the three calls above, binned per tile)
+ *   gs_tile_masks          per list entry, the 4x4-pixel sub-blocks it touches
  *   gs_rasterize_fwd       front-to-back alpha blending per 16x16 tile
  *   gs_loss_l1             L1 loss against target images, dL/dimage
  *   (gs_rasterize_fwd_l1   the two calls above in one pass)
@@ -231,6 +233,32 @@ gs_status gs_tile_lists(const float* rec, const uint16_t* rect, int64_t n, int32
 gs_status gs_tile_ranges(const uint64_t* keys, uint64_t n_keys, int64_t n_tiles_total,
                          uint32_t* ranges, void* stream);
 
+/* Bytes of the workspace of gs_tile_masks for lists of `capacity` slots. */
+size_t gs_tile_masks_workspace_bytes(uint64_t capacity);
+
+/*
+ * gs_tile_masks -- for every entry of the per-tile lists (ranges and vals as
+ * produced by gs_tile_ranges / gs_tile_lists), the 16-bit mask of the tile's
+ * 4x4-pixel sub-blocks that the entry's alpha >= 1/255 region can touch: bit
+ * 4 sy + sx for sub-block (sx, sy), 0 for sub-blocks outside the image. A
+ * cleared bit means alpha < 1/255 at every pixel centre of that sub-block,
+ * where the blending rule (alpha compositing of the fVDB page: entries with
+ * alpha below 1/255 are skipped) leaves the pixel untouched; the raster calls
+ * skip those (entry, sub-block) pairs, so their results do not depend on the
+ * masks beyond that. The test is the record's alpha-extent box, then the
+ * ellipse itself, widened so that rounding only ever sets a bit.
+ *   rec, n    records of gs_preprocess
+ *   capacity  slots of vals and masks (every range lies below it), < 2^32
+ *   masks     out uint16 per list entry, at the entry's list position (slots
+ *             in no range are left as they are)
+ *   ws        device workspace of gs_tile_masks_workspace_bytes(capacity)
+ * Errors: null pointers, bad view count, views of different sizes, a small
+ * workspace.
+ */
+gs_status gs_tile_masks(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
+                        uint64_t capacity, const gs_camera* cams, int32_t n_views, uint16_t* masks,
+                        void* ws, size_t ws_bytes, void* stream);
+
 /*
  * gs_rasterize_fwd -- per pixel, front to back over its tile's sorted list
  * (alpha compositing of the fVDB page; 16x16 tiles):
@@ -242,11 +270,13 @@ gs_status gs_tile_ranges(const uint64_t* keys, uint64_t n_keys, int64_t n_tiles_
  *   T_final   out [V][H][W]
  *   n_contrib out [V][H][W] int32: 1-based list position of the last blended
  *             entry, 0 if none
+ *   masks     the lists' sub-block masks of gs_tile_masks
  *   bg        host float[3]
  * Errors: null pointers, bad view count, views of different sizes.
  */
 gs_status gs_rasterize_fwd(const float* rec, int64_t n, const uint32_t* ranges,
-                           const uint32_t* vals, const gs_camera* cams, int32_t n_views,
+                           const uint32_t* vals, const uint16_t* masks, const gs_camera* cams,
+                           int32_t n_views,
                            const float* bg, float* image, float* T_final, int32_t* n_contrib,
                            void* stream);
 
@@ -282,7 +312,8 @@ size_t gs_rasterize_fwd_l1_workspace_bytes(int32_t n_views, int32_t width, int32
  * small workspace.
  */
 gs_status gs_rasterize_fwd_l1(const float* rec, int64_t n, const uint32_t* ranges,
-                              const uint32_t* vals, const gs_camera* cams, int32_t n_views,
+                              const uint32_t* vals, const uint16_t* masks, const gs_camera* cams,
+                              int32_t n_views,
                               const float* bg, const float* target, float scale, float* image,
                               float* T_final, int32_t* n_contrib, float* dL_dimage, double* loss,
                               int32_t accumulate, void* ws, size_t ws_bytes, void* stream);
@@ -298,7 +329,8 @@ gs_status gs_rasterize_fwd_l1(const float* rec, int64_t n, const uint32_t* range
  * between runs. Errors: as gs_rasterize_fwd.
  */
 gs_status gs_rasterize_bwd(const float* rec, int64_t n, const uint32_t* ranges,
-                           const uint32_t* vals, const gs_camera* cams, int32_t n_views,
+                           const uint32_t* vals, const uint16_t* masks, const gs_camera* cams,
+                           int32_t n_views,
                            const float* bg, const float* T_final, const int32_t* n_contrib,
                            const float* dL_dimage, float* grad2d, int32_t accumulate,
                            void* stream);

@@ -109,16 +109,29 @@ def test_invalid_arguments_rejected_on_host(lib):
     qws = L.rasterize_fwd_l1_workspace_bytes(1, 256, 256)
     assert qws == 16 * 16 * 4 * 8 and L.rasterize_fwd_l1_workspace_bytes(0, 256, 256) == 0
     f1 = lib.gs_rasterize_fwd_l1
-    assert f1(fake, 10, fake, fake, cams, 1, bg, None, 1.0, None, fake, fake, fake, fake, 0, fake, qws, None) == INV
-    assert f1(fake, 10, fake, fake, cams, 1, bg, fake, 1.0, None, fake, fake, None, fake, 0, fake, qws, None) == INV
-    assert f1(fake, 10, fake, fake, cams, 1, bg, fake, 1.0, None, fake, fake, fake, None, 0, fake, qws, None) == INV
-    assert f1(fake, 10, fake, fake, cams, 1, bg, fake, 1.0, None, fake, fake, fake, fake, 0, fake, qws - 8, None) == INV
-    assert f1(fake, 10, fake, fake, cams, 1, bg, fake, 1.0, None, fake, fake, fake, fake, 0, None, qws, None) == INV
-    assert lib.gs_rasterize_fwd(fake, 10, fake, fake, cams, 1, None, fake, fake, fake, None) == INV
-    assert lib.gs_rasterize_fwd(fake, 10, fake, fake, cams, 1, bg, None, fake, fake, None) == INV
-    assert lib.gs_rasterize_fwd(fake, -5, fake, fake, cams, 1, bg, fake, fake, fake, None) == INV
-    assert lib.gs_rasterize_bwd(fake, 10, fake, fake, cams, 1, bg, fake, fake, None, fake, 0, None) == INV
-    assert lib.gs_rasterize_bwd(fake, 10, fake, fake, cams, 0, bg, fake, fake, fake, fake, 0, None) == INV
+    assert f1(fake, 10, fake, fake, fake, cams, 1, bg, None, 1.0, None, fake, fake, fake, fake, 0, fake, qws, None) == INV
+    assert f1(fake, 10, fake, fake, fake, cams, 1, bg, fake, 1.0, None, fake, fake, None, fake, 0, fake, qws, None) == INV
+    assert f1(fake, 10, fake, fake, fake, cams, 1, bg, fake, 1.0, None, fake, fake, fake, None, 0, fake, qws, None) == INV
+    assert f1(fake, 10, fake, fake, fake, cams, 1, bg, fake, 1.0, None, fake, fake, fake, fake, 0, fake, qws - 8,
+              None) == INV
+    assert f1(fake, 10, fake, fake, fake, cams, 1, bg, fake, 1.0, None, fake, fake, fake, fake, 0, None, qws, None) == INV
+    assert f1(fake, 10, fake, fake, None, cams, 1, bg, fake, 1.0, None, fake, fake, fake, fake, 0, fake, qws, None) == INV
+    assert lib.gs_rasterize_fwd(fake, 10, fake, fake, fake, cams, 1, None, fake, fake, fake, None) == INV
+    assert lib.gs_rasterize_fwd(fake, 10, fake, fake, fake, cams, 1, bg, None, fake, fake, None) == INV
+    assert lib.gs_rasterize_fwd(fake, -5, fake, fake, fake, cams, 1, bg, fake, fake, fake, None) == INV
+    assert lib.gs_rasterize_fwd(fake, 10, fake, fake, None, cams, 1, bg, fake, fake, fake, None) == INV  # no masks
+    assert lib.gs_rasterize_bwd(fake, 10, fake, fake, fake, cams, 1, bg, fake, fake, None, fake, 0, None) == INV
+    assert lib.gs_rasterize_bwd(fake, 10, fake, fake, fake, cams, 0, bg, fake, fake, fake, fake, 0, None) == INV
+    assert lib.gs_rasterize_bwd(fake, 10, fake, fake, None, cams, 1, bg, fake, fake, fake, fake, 0, None) == INV
+    # tile masks
+    mws = L.tile_masks_workspace_bytes(100)
+    assert mws == 400
+    assert lib.gs_tile_masks(fake, 10, fake, fake, 100, cams, 1, None, fake, mws, None) == INV
+    assert lib.gs_tile_masks(fake, 10, None, fake, 100, cams, 1, fake, fake, mws, None) == INV
+    assert lib.gs_tile_masks(fake, -1, fake, fake, 100, cams, 1, fake, fake, mws, None) == INV
+    assert lib.gs_tile_masks(fake, 10, fake, fake, 100, cams, 0, fake, fake, mws, None) == INV
+    assert lib.gs_tile_masks(fake, 10, fake, fake, 100, cams, 1, fake, fake, mws - 4, None) == INV
+    assert lib.gs_tile_masks(fake, 10, fake, fake, 1 << 32, cams, 1, fake, fake, 1 << 40, None) == INV
     # loss, preprocess_bwd, adam
     assert lib.gs_loss_l1(fake, fake, -1, 1.0, fake, fake, 0, None) == INV
     assert lib.gs_loss_l1(fake, fake, 10, 1.0, fake, None, 0, None) == INV

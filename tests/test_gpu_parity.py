@@ -49,6 +49,13 @@ def test_keys_sort_ranges(run):
     assert K == run["gpu"]["total"]
 
 
+def test_tile_masks(run):
+    gpu = run["gpu"]
+    st = PY.check_masks(gpu["masks"], gpu["binned_vals"], gpu["binned_ranges"], run["orc"], run["cams"],
+                        sample=200000)
+    print(st)
+
+
 def test_forward(run):
     st = PY.check_forward(run["gpu"], run["fwd"])
     print(st)
