@@ -118,80 +118,66 @@ __device__ __forceinline__ void stage_entry(const Entry& E, int s, float4* __res
     s_mask[s] = (uint8_t)(E.valid ? E.m4 : 0u);
 }
 
-// Smallest value of Q(X, y) = A X^2 + 2 B X y + C y^2 over y in [y0, y1]
-// (C > 0, rC ~ 1/C); `mag` receives the sum of the magnitudes of its terms.
-// An approximate minimiser only raises the value by C times its error
-// squared, far below the widening of the test that uses it.
-__device__ __forceinline__ float conic_edge_min(float X, float y0, float y1, float A, float B, float C, float rC,
-                                                float& mag)
-{
-    const float ys = fminf(fmaxf(-(B * X) * rC, y0), y1);
-    const float t1 = A * X * X, t2 = 2.f * B * X * ys, t3 = C * ys * ys;
-    mag = fabsf(t1) + fabsf(t2) + t3;
-    return (t1 + t2) + t3;
-}
-
-// Whether the entry's alpha >= 1/255 region (Q(d) <= tau, d = pixel centre -
-// mean, conic (A, B, C)) meets the rectangle [x0, x1] x [y0, y1] of pixel
-// centres. The smallest Q over the rectangle lies on a side facing the mean
-// (or is 0 with the mean inside); the comparison is widened by 1e-5 of the
-// terms' magnitude so that rounding can only keep a sub-block, never drop one.
-__device__ __forceinline__ bool conic_meets_rect(float u, float v, float A, float B, float C, float tau, float x0,
-                                                 float x1, float y0, float y1)
-{
-    const float X0 = x0 - u, X1 = x1 - u, Y0 = y0 - v, Y1 = y1 - v;
-    if (X0 <= 0.f && X1 >= 0.f && Y0 <= 0.f && Y1 >= 0.f) return true;
-    float q = INFINITY, mag = 0.f, m;
-    if (X0 > 0.f || X1 < 0.f) {
-        q = conic_edge_min(X0 > 0.f ? X0 : X1, Y0, Y1, A, B, C, __builtin_amdgcn_rcpf(C), m);
-        mag = m;
-    }
-    if (Y0 > 0.f || Y1 < 0.f) {
-        const float qy = conic_edge_min(Y0 > 0.f ? Y0 : Y1, X0, X1, C, B, A, __builtin_amdgcn_rcpf(A), m);
-        if (qy < q) {
-            q = qy;
-            mag = m;
-        }
-    }
-    return q <= tau + 1e-5f * mag;
-}
-
 // The 16-bit mask of a list entry in its tile (tile origin (tx0, ty0)
 // pixels): bit 4 sy + sx is set when the entry's alpha >= 1/255 region may
-// touch a pixel centre of the 4x4 sub-block (sx, sy). First the record's
-// axis-aligned alpha extent box against the sub-blocks' rectangles of pixel
-// centres (clipped to the image; sub-blocks outside it get 0), then the
-// ellipse itself against each remaining rectangle, so that an entry is
-// dropped from a sub-block only where its alpha is below 1/255 at every
-// pixel: skipping it there leaves every result unchanged.
+// meet the rectangle of pixel centres of the 4x4 sub-block (sx, sy) (clipped
+// to the image; sub-blocks outside it get 0). With the conic (A, B, C),
+// alpha >= 1/255 is Q(d) = A dx^2 + 2 B dx dy + C dy^2 <= tau = 2 ln(255 o),
+// an ellipse. For fixed dy it covers dx = -(B/A) dy -+ w(dy) with w^2 =
+// (tau - dy^2 / S_yy) / A (S the 2D covariance, the conic's inverse; S_yy
+// comes from the record's y extent, ey = sqrt(tau' S_yy) + 0.05 with the
+// preprocess's tau', so no determinant, which cancels for thin footprints,
+// is formed). Per row of sub-blocks (a band y0 <= y <= y1) the right end is
+// concave in dy and largest at the ellipse's rightmost point dy_R = -(B/C)
+// dx_max, dx_max = sqrt(tau S_xx) (from ex likewise), the left end smallest
+// at -dy_R: each is taken at that dy clamped into the band, and a sub-block
+// is kept when its x range meets the span. tau is widened, w^2 gets a slack
+// of a few 1e-6 tau / A (a square root near zero magnifies rounding) and
+// the spans a margin of 0.01 px plus a few 1e-6 of the coordinates, so
+// rounding can only keep a sub-block: a cleared bit means alpha < 1/255 at
+// every pixel centre of the sub-block. (Hardware square roots and
+// reciprocals, 1 ulp, are well inside these margins.)
 __device__ __forceinline__ uint32_t tile_mask16(const Entry& E, int tx0, int ty0, int W, int H)
 {
-    const float lo_x = E.a.x - E.c.y, hi_x = E.a.x + E.c.y, lo_y = E.a.y - E.c.z, hi_y = E.a.y + E.c.z;
-    float x0[4], x1[4], y0[4], y1[4];
-    uint32_t xm = 0, ym = 0;
+    const float u = E.a.x, v = E.a.y, A = E.a.z, B = E.a.w, C = E.b.x, o = E.b.y, ex = E.c.y, ey = E.c.z;
+    if (!(255.f * o > 1.f) || !(ex > 0.05f) || !(ey > 0.05f) || !(A > 0.f) || !(C > 0.f)) return 0u;
+    const float l255o = __logf(255.f * o);
+    const float tau = 2.f * l255o * 1.004f + 0.02f;     // >= the blend threshold's 2 ln(255 o)
+    const float tau_rec = 2.f * l255o * 1.002f + 0.01f;  // the extents' threshold
+    const float sy = (ey - 0.05f) * (ey - 0.05f) * __builtin_amdgcn_rcpf(tau_rec);  // ~ S_yy
+    const float sx = (ex - 0.05f) * (ex - 0.05f) * __builtin_amdgcn_rcpf(tau_rec);  // ~ S_xx
+    const float rA = __builtin_amdgcn_rcpf(A), kY = __builtin_amdgcn_rcpf(sy);
+    const float dxm = __builtin_amdgcn_sqrtf(tau * sx), dym = __builtin_amdgcn_sqrtf(tau * sy);
+    const float mx = 0.01f + 4e-6f * (fabsf(u) + dxm), my = 0.01f + 4e-6f * (fabsf(v) + dym);
+    const float slack = 4e-6f * tau * rA;
+    const float dyR = -B * dxm * __builtin_amdgcn_rcpf(C);
+    const float bA = B * rA;
+    float x0[4], x1[4];
+    uint32_t cols = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const int bx = tx0 + 4 * k, by = ty0 + 4 * k;
+        const int bx = tx0 + 4 * k;
         x0[k] = (float)bx + 0.5f;
         x1[k] = (float)min(bx + 4, W) - 0.5f;
-        y0[k] = (float)by + 0.5f;
-        y1[k] = (float)min(by + 4, H) - 0.5f;
-        xm |= (uint32_t)(bx < W && hi_x >= x0[k] && lo_x <= x1[k]) << k;
-        ym |= (uint32_t)(by < H && hi_y >= y0[k] && lo_y <= y1[k]) << k;
+        cols |= (uint32_t)(bx < W) << k;
     }
     uint32_t mask = 0;
 #pragma unroll
-    for (int sy = 0; sy < 4; ++sy)
-        if ((ym >> sy) & 1u) mask |= xm << (4 * sy);
-    if (mask) {
-        // the threshold of the record's extent, widened a little more
-        const float tau = 2.f * __logf(255.f * E.b.y) * 1.004f + 0.02f;
+    for (int r = 0; r < 4; ++r) {
+        const int by = ty0 + 4 * r;
+        if (by >= H) break;
+        const float a = fmaxf((float)by + 0.5f - v - my, -dym - my);
+        const float b = fminf((float)min(by + 4, H) - 0.5f - v + my, dym + my);
+        if (!(a <= b)) continue;  // the band misses the ellipse
+        const float dR = fminf(fmaxf(dyR, a), b), dL = fminf(fmaxf(-dyR, a), b);
+        const float wR = __builtin_amdgcn_sqrtf(fmaxf((tau - dR * dR * kY) * rA, 0.f) + slack);
+        const float wL = __builtin_amdgcn_sqrtf(fmaxf((tau - dL * dL * kY) * rA, 0.f) + slack);
+        const float xr = u - bA * dR + wR + mx;
+        const float xl = u - bA * dL - wL - mx;
+        uint32_t row = 0;
 #pragma unroll
-        for (int b = 0; b < 16; ++b) {
-            if (((mask >> b) & 1u) &&
-                !conic_meets_rect(E.a.x, E.a.y, E.a.z, E.a.w, E.b.x, tau, x0[b & 3], x1[b & 3], y0[b >> 2], y1[b >> 2]))
-                mask &= ~(1u << b);
-        }
+        for (int k = 0; k < 4; ++k) row |= (uint32_t)(xr >= x0[k] && xl <= x1[k]) << k;
+        mask |= (row & cols) << (4 * r);
     }
     return mask;
 }
