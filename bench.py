@@ -46,6 +46,7 @@ KERNEL_SOURCES = {
     "k_raster_fwd_l1": ["raster_fwd.hip", "raster_common.h", "internal.h", "common.h"],
     "k_adam": ["optim.hip", "adam.h", "internal.h", "common.h"],
     "k_preprocess_bwd": ["preprocess_bwd.hip", "adam.h", "project.h", "internal.h", "common.h"],
+    "k_tile_masks": ["tile_masks.hip", "raster_common.h", "internal.h", "common.h"],
 }
 PROFILES = os.path.join(ROOT, "profiles")
 
