@@ -108,13 +108,14 @@ __device__ __forceinline__ void gather_record(Entry& E, const float* __restrict_
 }
 
 // Stage the lane's entry at slot `s`: (u, v, -A/2, -B) (-C/2, o, r, g)
-// (b, -, -, -), and its 4 sub-block bits for this quarter (0 if invalid).
-__device__ __forceinline__ void stage_entry(const Entry& E, int s, float4* __restrict__ s_rec,
+// (b, pos, -, -) with pos its 1-based list position (int bits), and its 4
+// sub-block bits for this quarter (0 if invalid).
+__device__ __forceinline__ void stage_entry(const Entry& E, int s, int32_t pos, float4* __restrict__ s_rec,
                                             uint8_t* __restrict__ s_mask)
 {
     s_rec[3 * s + 0] = make_float4(E.a.x, E.a.y, -0.5f * E.a.z, -E.a.w);
     s_rec[3 * s + 1] = make_float4(-0.5f * E.b.x, E.b.y, E.b.z, E.b.w);
-    s_rec[3 * s + 2] = make_float4(E.c.x, 0.f, 0.f, 0.f);
+    s_rec[3 * s + 2] = make_float4(E.c.x, __int_as_float(pos), 0.f, 0.f);
     s_mask[s] = (uint8_t)(E.valid ? E.m4 : 0u);
 }
 
@@ -191,25 +192,6 @@ __device__ __forceinline__ void stage_entry_pair(const Entry& E, int s, float4* 
     s_rec[2 * s + 1] = make_float4(-0.5f * E.b.x, E.b.y, E.b.z, E.b.w);
     s_b[s] = E.c.x;
     s_mask[s] = (uint8_t)(E.valid ? E.m4 : 0u);
-}
-
-// Per-row compaction of the 64 staged entries: for row r, the slots
-// (ascending) whose bit r is set and for which `extra(slot, r)` holds.
-// lists[r * 64 + k]; counts in cnt[4] (wave-uniform).
-template <typename Pred>
-__device__ __forceinline__ void rows_compact(const uint8_t* __restrict__ s_mask, uint16_t* __restrict__ lists,
-                                             int lane, uint32_t cnt[4], Pred extra)
-{
-    asm volatile("" ::: "memory");  // staging writes precede these reads (LDS is in order per wave)
-    const uint32_t m4 = s_mask[lane];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const bool keep = ((m4 >> r) & 1u) && extra(lane, r);
-        const uint64_t m = ballot(keep);
-        if (keep) lists[r * RW_BATCH + mask_rank(m)] = (uint16_t)lane;
-        cnt[r] = (uint32_t)__popcll(m);
-    }
-    asm volatile("" ::: "memory");  // list writes precede their reads
 }
 
 __device__ __forceinline__ float entry_power(const float4& q0, const float4& q1, float px, float py, float& dx,

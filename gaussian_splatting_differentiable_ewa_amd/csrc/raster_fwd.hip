@@ -21,7 +21,10 @@
 //     within the row), so one instruction stream advances four sub-blocks on
 //     four different entries. An entry skipped by the mask has alpha < 1/255
 //     at every pixel of the sub-block and would have been skipped anyway:
-//     results are unchanged.
+//     results are unchanged. Row lists hold record byte offsets and are
+//     padded to the longest row's count with a slot of opacity 0 (never
+//     blended), so the loop needs no per-entry bound test; each staged
+//     record carries its list position for n_contrib.
 //
 // Per (pixel, entry), in this fixed fp32 order:
 //   dx = u - px, dy = v - py
@@ -48,9 +51,12 @@ __device__ __forceinline__ void raster_fwd_body(const float* __restrict__ rec, i
                                                 float* __restrict__ dL, double* __restrict__ partial)
 {
 #pragma clang fp contract(off)
-    __shared__ float4 s_rec[3 * RW_BATCH];
+    // records at a stride of 48 bytes, and an extra slot of opacity 0 that
+    // pads each row's list to the longest row's count (no pixel blends it)
+    constexpr uint32_t SLOT_BYTES = 48, PAD_OFF = RW_BATCH * SLOT_BYTES;
+    __shared__ float4 s_rec[3 * (RW_BATCH + 1)];
     __shared__ uint8_t s_mask[RW_BATCH];
-    __shared__ __align__(16) uint16_t s_list[4 * RW_BATCH];  // read 8 ids at a time
+    __shared__ __align__(16) uint16_t s_list[4 * RW_BATCH];  // record byte offsets, read 8 at a time
     const QuarterCtx t = quarter_ctx(W, H, TX, T);
     if (t.empty) {
         if (L1 && t.lane == 0) partial[blockIdx.x] = 0.0;
@@ -70,6 +76,12 @@ __device__ __forceinline__ void raster_fwd_body(const float* __restrict__ rec, i
     float Tr = 1.f, C0 = 0.f, C1 = 0.f, C2 = 0.f;
     int32_t last = 0;
     bool done = !t.inside;
+    if (t.lane == 0) {
+        s_rec[3 * RW_BATCH] = make_float4(0.f, 0.f, 0.f, 0.f);
+        s_rec[3 * RW_BATCH + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        s_rec[3 * RW_BATCH + 2] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const char* recb = (const char*)s_rec;
     // two-stage prefetch: records of batch k+1 and ids of batch k+2 are
     // requested while batch k is evaluated
     Entry cur, nxt, nx2;
@@ -78,44 +90,46 @@ __device__ __forceinline__ void raster_fwd_body(const float* __restrict__ rec, i
     load_entry(nxt, rg.x + RW_BATCH + t.lane < rg.y, rg.x + RW_BATCH + t.lane, vals, masks, t);
     for (uint32_t base = rg.x; base < rg.y; base += RW_BATCH) {
         if (ballot(!done) == 0ull) break;
-        stage_entry(cur, t.lane, s_rec, s_mask);
+        stage_entry(cur, t.lane, (int32_t)(base - rg.x) + t.lane + 1, s_rec, s_mask);
         gather_record(nxt, rv);
         const uint32_t j2 = base + 2 * RW_BATCH + t.lane;
         load_entry(nx2, j2 < rg.y, j2, vals, masks, t);
+        // per row, the staged entries of its sub-block in list order, as
+        // record offsets; the rest of the row's list is the padding slot
         uint32_t cnt[4];
-        rows_compact(s_mask, s_list, t.lane, cnt, [](int, int) { return true; });
-        const uint32_t my_cnt = t.row == 0 ? cnt[0] : t.row == 1 ? cnt[1] : t.row == 2 ? cnt[2] : cnt[3];
+        {
+            asm volatile("" ::: "memory");  // staging writes precede these reads (LDS is in order per wave)
+            const uint32_t m4 = s_mask[t.lane];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool keep = (m4 >> r) & 1u;
+                const uint64_t m = ballot(keep);
+                cnt[r] = (uint32_t)__popcll(m);
+                if (keep) s_list[r * RW_BATCH + mask_rank(m)] = (uint16_t)(t.lane * SLOT_BYTES);
+                if ((uint32_t)t.lane >= cnt[r]) s_list[r * RW_BATCH + t.lane] = (uint16_t)PAD_OFF;
+            }
+            asm volatile("" ::: "memory");  // list writes precede their reads
+        }
         const uint32_t iters = max(max(cnt[0], cnt[1]), max(cnt[2], cnt[3]));
         const uint16_t* my_list = s_list + t.row * RW_BATCH;
-        const int32_t pos0 = (int32_t)(base - rg.x) + 1;
-        // groups of 8 entries: their slot ids in one 16-byte read (ids past
-        // the row's count are stale and masked); each record is read while
-        // the entry before it is evaluated (exhausted rows idle on slot 0)
+        // groups of 8 entries: their record offsets in one 16-byte read
         for (uint32_t sb = 0; sb < iters; sb += 8) {
             const uint4 ids = *(const uint4*)(my_list + sb);
             const uint32_t idw[4] = {ids.x, ids.y, ids.z, ids.w};
-            int idx_n = sb < my_cnt ? (int)(idw[0] & 0xffffu) : 0;
-            float4 n0 = s_rec[3 * idx_n], n1 = s_rec[3 * idx_n + 1], n2 = s_rec[3 * idx_n + 2];
 #pragma unroll
             for (uint32_t i = 0; i < 8u; ++i) {
-                const uint32_t it = sb + i;
-                if (it >= iters) break;  // wave-uniform
-                const bool has = it < my_cnt;
-                const int idx = idx_n;
-                const float4 q0 = n0, q1 = n1, q2 = n2;
-                if (i + 1 < 8u) {
-                    idx_n = it + 1 < my_cnt ? (int)((idw[(i + 1) >> 1] >> (16 * ((i + 1) & 1))) & 0xffffu) : 0;
-                    n0 = s_rec[3 * idx_n];
-                    n1 = s_rec[3 * idx_n + 1];
-                    n2 = s_rec[3 * idx_n + 2];
-                }
+                if (sb + i >= iters) break;  // wave-uniform
+                const uint32_t off = (idw[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+                const float4 q0 = *(const float4*)(recb + off);
+                const float4 q1 = *(const float4*)(recb + off + 16);
+                const float2 q2 = *(const float2*)(recb + off + 32);
                 // branch-free update: only lanes that blend change state (a
                 // zero weight adds exactly 0)
                 float dx, dy;
                 const float power = entry_power(q0, q1, t.px, t.py, dx, dy);
                 const float alpha = fminf(ALPHA_MAX, q1.y * exp_fast(power));
                 const float Tn = Tr * (1.f - alpha);
-                const bool keep = has && !done && !(power > 0.f) && !(alpha < ALPHA_MIN);
+                const bool keep = !done && !(power > 0.f) && !(alpha < ALPHA_MIN);
                 const bool stop = keep && Tn < T_MIN;
                 const bool blend = keep && !stop;
                 const float w = blend ? alpha * Tr : 0.f;
@@ -123,7 +137,7 @@ __device__ __forceinline__ void raster_fwd_body(const float* __restrict__ rec, i
                 C1 = __builtin_fmaf(q1.w, w, C1);
                 C2 = __builtin_fmaf(q2.x, w, C2);
                 Tr = blend ? Tn : Tr;
-                last = blend ? pos0 + idx : last;
+                last = blend ? __float_as_int(q2.y) : last;
                 done = done || stop;
             }
             if (ballot(!done) == 0ull) break;
