@@ -138,47 +138,84 @@ __device__ __forceinline__ void stage_entry(const Entry& E, int s, int32_t pos, 
 // rounding can only keep a sub-block: a cleared bit means alpha < 1/255 at
 // every pixel centre of the sub-block. (Hardware square roots and
 // reciprocals, 1 ulp, are well inside these margins.)
-__device__ __forceinline__ uint32_t tile_mask16(const Entry& E, int tx0, int ty0, int W, int H)
+struct MaskGeom {
+    float u, v, bA, rA, kY, tau, dym, dyR, mx, my, slack;
+    bool ok;  // false: alpha < 1/255 everywhere (or a degenerate record)
+};
+
+__device__ __forceinline__ MaskGeom mask_geom(const Entry& E)
 {
+    MaskGeom M;
     const float u = E.a.x, v = E.a.y, A = E.a.z, B = E.a.w, C = E.b.x, o = E.b.y, ex = E.c.y, ey = E.c.z;
-    if (!(255.f * o > 1.f) || !(ex > 0.05f) || !(ey > 0.05f) || !(A > 0.f) || !(C > 0.f)) return 0u;
-    const float l255o = __logf(255.f * o);
-    const float tau = 2.f * l255o * 1.004f + 0.02f;     // >= the blend threshold's 2 ln(255 o)
+    M.ok = (255.f * o > 1.f) && (ex > 0.05f) && (ey > 0.05f) && (A > 0.f) && (C > 0.f);
+    const float l255o = __logf(fmaxf(255.f * o, 1.f));
+    M.tau = 2.f * l255o * 1.004f + 0.02f;                // >= the blend threshold's 2 ln(255 o)
     const float tau_rec = 2.f * l255o * 1.002f + 0.01f;  // the extents' threshold
     const float sy = (ey - 0.05f) * (ey - 0.05f) * __builtin_amdgcn_rcpf(tau_rec);  // ~ S_yy
     const float sx = (ex - 0.05f) * (ex - 0.05f) * __builtin_amdgcn_rcpf(tau_rec);  // ~ S_xx
-    const float rA = __builtin_amdgcn_rcpf(A), kY = __builtin_amdgcn_rcpf(sy);
-    const float dxm = __builtin_amdgcn_sqrtf(tau * sx), dym = __builtin_amdgcn_sqrtf(tau * sy);
-    const float mx = 0.01f + 4e-6f * (fabsf(u) + dxm), my = 0.01f + 4e-6f * (fabsf(v) + dym);
-    const float slack = 4e-6f * tau * rA;
-    const float dyR = -B * dxm * __builtin_amdgcn_rcpf(C);
-    const float bA = B * rA;
-    float x0[4], x1[4];
-    uint32_t cols = 0;
+    M.rA = __builtin_amdgcn_rcpf(A);
+    M.kY = __builtin_amdgcn_rcpf(sy);
+    const float dxm = __builtin_amdgcn_sqrtf(M.tau * sx);
+    M.dym = __builtin_amdgcn_sqrtf(M.tau * sy);
+    M.mx = 0.01f + 4e-6f * (fabsf(u) + dxm);
+    M.my = 0.01f + 4e-6f * (fabsf(v) + M.dym);
+    M.slack = 4e-6f * M.tau * M.rA;
+    M.dyR = -B * dxm * __builtin_amdgcn_rcpf(C);
+    M.bA = B * M.rA;
+    M.u = u;
+    M.v = v;
+    return M;
+}
+
+// The ellipse's x span [xl, xr] inside the band of pixel-centre rows
+// [yc0, yc1]; false when the band misses it.
+__device__ __forceinline__ bool band_span(const MaskGeom& M, float yc0, float yc1, float& xl, float& xr)
+{
+    const float a = fmaxf(yc0 - M.v - M.my, -M.dym - M.my);
+    const float b = fminf(yc1 - M.v + M.my, M.dym + M.my);
+    if (!(a <= b)) return false;
+    const float dR = fminf(fmaxf(M.dyR, a), b), dL = fminf(fmaxf(-M.dyR, a), b);
+    const float wR = __builtin_amdgcn_sqrtf(fmaxf((M.tau - dR * dR * M.kY) * M.rA, 0.f) + M.slack);
+    const float wL = __builtin_amdgcn_sqrtf(fmaxf((M.tau - dL * dL * M.kY) * M.rA, 0.f) + M.slack);
+    xr = M.u - M.bA * dR + wR + M.mx;
+    xl = M.u - M.bA * dL - wL - M.mx;
+    return true;
+}
+
+// Bits of the four sub-block columns from pixel tx0 whose pixel-centre
+// range meets [xl, xr] (columns outside the image never).
+__device__ __forceinline__ uint32_t span_cols(float xl, float xr, int tx0, int W)
+{
+    uint32_t row = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int bx = tx0 + 4 * k;
-        x0[k] = (float)bx + 0.5f;
-        x1[k] = (float)min(bx + 4, W) - 0.5f;
-        cols |= (uint32_t)(bx < W) << k;
+        const float x0 = (float)bx + 0.5f, x1 = (float)min(bx + 4, W) - 0.5f;
+        row |= (uint32_t)(bx < W && xr >= x0 && xl <= x1) << k;
     }
+    return row;
+}
+
+// The pixel-centre rows of sub-block row r of the tile row starting at ty0.
+__device__ __forceinline__ bool band_rows(int ty0, int r, int H, float& yc0, float& yc1)
+{
+    const int by = ty0 + 4 * r;
+    yc0 = (float)by + 0.5f;
+    yc1 = (float)min(by + 4, H) - 0.5f;
+    return by < H;
+}
+
+__device__ __forceinline__ uint32_t tile_mask16(const Entry& E, int tx0, int ty0, int W, int H)
+{
+    const MaskGeom M = mask_geom(E);
+    if (!M.ok) return 0u;
     uint32_t mask = 0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int by = ty0 + 4 * r;
-        if (by >= H) break;
-        const float a = fmaxf((float)by + 0.5f - v - my, -dym - my);
-        const float b = fminf((float)min(by + 4, H) - 0.5f - v + my, dym + my);
-        if (!(a <= b)) continue;  // the band misses the ellipse
-        const float dR = fminf(fmaxf(dyR, a), b), dL = fminf(fmaxf(-dyR, a), b);
-        const float wR = __builtin_amdgcn_sqrtf(fmaxf((tau - dR * dR * kY) * rA, 0.f) + slack);
-        const float wL = __builtin_amdgcn_sqrtf(fmaxf((tau - dL * dL * kY) * rA, 0.f) + slack);
-        const float xr = u - bA * dR + wR + mx;
-        const float xl = u - bA * dL - wL - mx;
-        uint32_t row = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) row |= (uint32_t)(xr >= x0[k] && xl <= x1[k]) << k;
-        mask |= (row & cols) << (4 * r);
+        float yc0, yc1, xl, xr;
+        if (!band_rows(ty0, r, H, yc0, yc1)) break;
+        if (!band_span(M, yc0, yc1, xl, xr)) continue;  // the band misses the ellipse
+        mask |= span_cols(xl, xr, tx0, W) << (4 * r);
     }
     return mask;
 }

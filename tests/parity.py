@@ -61,6 +61,7 @@ def gpu_forward(params_np: np.ndarray, sh: int, cams, bg=(0.0, 0.0, 0.0)):
     out["vals"] = np_(br.sorted_vals[:K]).view(np.uint32)
     out["ranges"] = np_(br.ranges).view(np.uint32).reshape(-1, 2)
     out["overflow"] = int(np_(br.overflow)[0])
+    out["radix_masks"] = np_(br.masks[:K]).view(np.uint16)  # gs_tile_masks on the sorted keys' lists
     del br
     b.intersections()
     b.rasterize(bg)

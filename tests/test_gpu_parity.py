@@ -51,6 +51,11 @@ def test_keys_sort_ranges(run):
 
 def test_tile_masks(run):
     gpu = run["gpu"]
+    # the binned builder forms the masks while filling; gs_tile_masks computes
+    # them from the finished lists (here those of the global key path, which
+    # are the same lists): identical bits
+    assert np.array_equal(gpu["vals"], gpu["binned_vals"])
+    assert np.array_equal(gpu["masks"], gpu["radix_masks"])
     st = PY.check_masks(gpu["masks"], gpu["binned_vals"], gpu["binned_ranges"], run["orc"], run["cams"],
                         sample=200000)
     print(st)
