@@ -89,7 +89,7 @@ def lib():
             "gs_adam_step": ([_P, _P, _P, _P, _I64, _F64, _F64, _F64, _F64, _I64, _P], ctypes.c_int),
             "gs_adam_step_unless": ([_P, _P, _P, _P, _I64, _F64, _F64, _F64, _F64, _I64, _P, _P], ctypes.c_int),
             "gs_preprocess_bwd_adam": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _F64, _F64, _F64, _F64, _I64, _P,
-                                        _P, _P], ctypes.c_int),
+                                        _P, _P, _P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -248,10 +248,12 @@ def gs_adam_step(params, grad, m, v, count, lr, beta1, beta2, eps, step, stream=
 
 
 def gs_preprocess_bwd_adam(params, n, sh_degree, cams, rect, grad2d, m, v, lr, beta1, beta2, eps, step, skip=None,
-                           grad_params=None, stream=None):
+                           grad_params=None, state=None, stream=None):
+    """state (optional): uint8 [n], 0 where the Gaussian's moments are zero
+    (see the header); never-seen Gaussians are then skipped."""
     _check(lib().gs_preprocess_bwd_adam(_ptr(params), n, sh_degree, cameras(cams), len(cams), _ptr(rect), _ptr(grad2d),
-                                        _ptr(m), _ptr(v), lr, beta1, beta2, eps, step, _ptr(skip), _ptr(grad_params),
-                                        _stream(stream)), "gs_preprocess_bwd_adam")
+                                        _ptr(m), _ptr(v), lr, beta1, beta2, eps, step, _ptr(skip), _ptr(state),
+                                        _ptr(grad_params), _stream(stream)), "gs_preprocess_bwd_adam")
 
 
 def gs_adam_step_unless(params, grad, m, v, count, lr, beta1, beta2, eps, step, skip, stream=None):

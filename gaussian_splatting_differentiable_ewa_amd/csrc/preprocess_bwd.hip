@@ -12,7 +12,10 @@
 // With ADAM, the thread applies the Adam update to its Gaussian's P
 // parameters as soon as their gradients are formed (the element-wise update
 // of gs_adam_step, same arithmetic), so the gradient never goes through HBM
-// and the parameters are read once.
+// and the parameters are read once. With a state array, a Gaussian culled in
+// every view whose moments are known to be zero is skipped without a read:
+// with g = m = v = 0 Adam leaves theta, m and v as they are (eps > 0), so
+// only Gaussians seen at least once cost moment traffic.
 #include "adam.h"
 #include "internal.h"
 #include "project.h"
@@ -26,13 +29,29 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(float* __restrict__ P, i
                                                         const ShConsts K, const uint16_t* __restrict__ rect,
                                                         const float* __restrict__ grad2d, float* __restrict__ out,
                                                         float* __restrict__ m, float* __restrict__ v,
-                                                        const AdamConsts ac, const int32_t* __restrict__ skip)
+                                                        const AdamConsts ac, const int32_t* __restrict__ skip,
+                                                        uint8_t* __restrict__ state)
 {
     constexpr int NB = (DEG + 1) * (DEG + 1);
     constexpr int ROWS = 11 + 3 * NB;
     const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (g >= n) return;
     if (ADAM && skip && *skip != 0) return;  // the step's lists overflowed: no update
+    if (ADAM && state) {
+        bool seen = false;  // visible in some view
+        for (int v = 0; v < cams.n_views; ++v) {
+            const uint2 rr = *(const uint2*)(rect + 4 * ((int64_t)v * n + g));
+            seen = seen || ((rr.y & 0xffffu) > (rr.x & 0xffffu) && (rr.y >> 16) > (rr.x >> 16));
+        }
+        if (!seen && state[g] == 0) {
+            if (out) {
+#pragma unroll
+                for (int r = 0; r < ROWS; ++r) out[(int64_t)r * n + g] = 0.f;
+            }
+            return;
+        }
+        if (seen) state[g] = 1;
+    }
     const float x = P[0 * n + g], y = P[1 * n + g], z = P[2 * n + g];
     GaussLocal L;
     gauss_local(P[3 * n + g], P[4 * n + g], P[5 * n + g], P[6 * n + g], P[7 * n + g], P[8 * n + g],
@@ -273,15 +292,15 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(float* __restrict__ P, i
 template <bool ADAM>
 static gs_status pbwd_launch(float* params, int64_t n, int32_t sh_degree, const DevCameras& dc,
                              const uint16_t* rect, const float* grad2d, float* out, float* m, float* v,
-                             const AdamConsts& c, const int32_t* skip, hipStream_t s)
+                             const AdamConsts& c, const int32_t* skip, uint8_t* state, hipStream_t s)
 {
     const dim3 grid(grid_for((uint64_t)n, 256)), block(256);
     const ShConsts K = sh_constants();
     switch (sh_degree) {
-        case 0: hipLaunchKernelGGL((k_preprocess_bwd<0, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip); break;
-        case 1: hipLaunchKernelGGL((k_preprocess_bwd<1, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip); break;
-        case 2: hipLaunchKernelGGL((k_preprocess_bwd<2, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip); break;
-        default: hipLaunchKernelGGL((k_preprocess_bwd<3, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip); break;
+        case 0: hipLaunchKernelGGL((k_preprocess_bwd<0, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip, state); break;
+        case 1: hipLaunchKernelGGL((k_preprocess_bwd<1, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip, state); break;
+        case 2: hipLaunchKernelGGL((k_preprocess_bwd<2, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip, state); break;
+        default: hipLaunchKernelGGL((k_preprocess_bwd<3, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip, state); break;
     }
     return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
 }
@@ -303,13 +322,13 @@ gs_status gs_preprocess_bwd(const float* params, int64_t n, int32_t sh_degree, c
     if (!make_dev_cameras(cams, n_views, dc)) return GS_ERR_INVALID_ARGUMENT;
     if (n == 0) return GS_OK;
     return pbwd_launch<false>((float*)params, n, sh_degree, dc, rect, grad2d, grad_params, nullptr, nullptr,
-                              AdamConsts{}, nullptr, (hipStream_t)stream);
+                              AdamConsts{}, nullptr, nullptr, (hipStream_t)stream);
 }
 
 gs_status gs_preprocess_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs_camera* cams,
                                  int32_t n_views, const uint16_t* rect, const float* grad2d, float* m, float* v,
                                  double lr, double beta1, double beta2, double eps, int64_t step,
-                                 const int32_t* skip, float* grad_params, void* stream)
+                                 const int32_t* skip, uint8_t* state, float* grad_params, void* stream)
 {
     if (n < 0 || sh_degree < 0 || sh_degree > 3) return GS_ERR_INVALID_ARGUMENT;
     if (n > 0 && (!params || !rect || !grad2d || !m || !v)) return GS_ERR_INVALID_ARGUMENT;
@@ -319,7 +338,7 @@ gs_status gs_preprocess_bwd_adam(float* params, int64_t n, int32_t sh_degree, co
     AdamConsts c;
     if (!adam_consts(lr, beta1, beta2, eps, step, c)) return GS_ERR_INVALID_ARGUMENT;
     if (n == 0) return GS_OK;
-    return pbwd_launch<true>(params, n, sh_degree, dc, rect, grad2d, grad_params, m, v, c, skip,
+    return pbwd_launch<true>(params, n, sh_degree, dc, rect, grad2d, grad_params, m, v, c, skip, state,
                              (hipStream_t)stream);
 }
 

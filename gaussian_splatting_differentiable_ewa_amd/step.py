@@ -203,6 +203,15 @@ class TrainStep:
         self.target = target.contiguous()
         self.m = torch.zeros_like(params) if m is None else m
         self.v = torch.zeros_like(params) if v is None else v
+        # per Gaussian, 0 while its moments are zero (all of them when the
+        # moments start at zero): a Gaussian never seen is skipped by Adam
+        fresh = m is None and v is None
+        self.adam_state = (torch.zeros if fresh else torch.ones)(params.shape[1], dtype=torch.uint8,
+                                                                 device=params.device)
+        # the flags pay off only when most Gaussians are out of view (then
+        # the moment traffic of the unseen ones is skipped); decided once, at
+        # the first step, from the share visible in some view
+        self._use_state = None
         self.grad = None if fused_adam else torch.empty_like(params)
         self.lr, self.betas, self.eps, self.bg = lr, betas, eps, bg
         self.t = 0
@@ -250,9 +259,14 @@ class TrainStep:
                            b.grad2d, accumulate=True)
         mark(6)
         skip = self.sticky if deferred else None
+        if self._use_state is None:
+            r = b.rect.view(b.V, b.n, 4).view(torch.int16)
+            seen = ((r[..., 2] > r[..., 0]) & (r[..., 3] > r[..., 1])).any(dim=0)
+            self._use_state = self.eps > 0 and float(seen.float().mean()) < 0.5
         if self.fused_adam:
             L.gs_preprocess_bwd_adam(self.params, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, self.m, self.v, self.lr,
-                                     self.betas[0], self.betas[1], self.eps, self.t, skip=skip)
+                                     self.betas[0], self.betas[1], self.eps, self.t, skip=skip,
+                                     state=self.adam_state if self._use_state else None)
         else:
             L.gs_preprocess_bwd(self.params, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, self.grad)
             mark(7)

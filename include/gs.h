@@ -359,13 +359,21 @@ gs_status gs_preprocess_bwd(const float* params, int64_t n, int32_t sh_degree,
  *   lr .. step   as gs_adam_step
  *   skip         device int32 or NULL: when non-zero, nothing is written (as
  *                gs_adam_step_unless)
+ *   state        device uint8 [n] or NULL: per Gaussian, 0 asserts that its
+ *                rows of m and v are all zero. A Gaussian culled in every view
+ *                (zero gradient) with state 0 is then skipped without reading
+ *                anything: with g = m = v = 0 the update leaves theta, m and v
+ *                unchanged when eps > 0 (with eps = 0 the dense update would
+ *                write 0/0). Every Gaussian visible in some view gets state 1.
+ *                Start it at 0 together with zero moments, or at 1.
  *   grad_params  out [P][n] fp32 or NULL: the gradient, if wanted
  * Errors: as gs_preprocess_bwd and gs_adam_step (m and v must not be null).
  */
 gs_status gs_preprocess_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs_camera* cams,
                                  int32_t n_views, const uint16_t* rect, const float* grad2d, float* m,
                                  float* v, double lr, double beta1, double beta2, double eps,
-                                 int64_t step, const int32_t* skip, float* grad_params, void* stream);
+                                 int64_t step, const int32_t* skip, uint8_t* state, float* grad_params,
+                                 void* stream);
 
 /*
  * gs_adam_step -- Adam (Kingma & Ba, reference [12] of the fVDB page),

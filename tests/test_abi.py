@@ -145,13 +145,13 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert lib.gs_adam_step(None, fake, fake, fake, 10, 1e-3, 0.9, 0.999, 1e-15, 1, None) == INV
     # the fused preprocess backward + Adam: both checks apply
     assert lib.gs_preprocess_bwd_adam(fake, 10, 3, cams, 1, fake, fake, None, fake, 1e-3, 0.9, 0.999, 1e-15, 1,
-                                      None, None, None) == INV
+                                      None, None, None, None) == INV
     assert lib.gs_preprocess_bwd_adam(fake, 10, 3, cams, 1, fake, fake, fake, fake, 1e-3, 0.9, 0.999, 1e-15, 0,
-                                      None, None, None) == INV
+                                      None, None, None, None) == INV
     assert lib.gs_preprocess_bwd_adam(fake, 10, 3, cams, 1, fake, fake, fake, fake, 1e-3, 1.5, 0.999, 1e-15, 1,
-                                      None, None, None) == INV
+                                      None, None, None, None) == INV
     assert lib.gs_preprocess_bwd_adam(fake, 10, 4, cams, 1, fake, fake, fake, fake, 1e-3, 0.9, 0.999, 1e-15, 1,
-                                      None, None, None) == INV
+                                      None, None, None, None) == INV
     # the guarded variant needs its flag, and checks the same arguments
     assert lib.gs_adam_step_unless(fake, fake, fake, fake, 10, 1e-3, 0.9, 0.999, 1e-15, 1, None, None) == INV
     assert lib.gs_adam_step_unless(fake, fake, fake, fake, 10, 1e-3, 0.9, 0.999, 1e-15, 0, fake, None) == INV

@@ -146,3 +146,48 @@ def test_preprocess_bwd_adam_fused(run, step):
                                              skip=1)
     assert np.array_equal(th, run["params"]) and np.array_equal(m, m0) and np.array_equal(v, v0)
     assert np.all(g == 7.0)
+
+
+def test_adam_state_skip(run):
+    """With the state flags, Gaussians culled in every view and never seen
+    are skipped; the result equals the dense update bit for bit over three
+    calls whose visibility changes (seen, then culled: the moments keep
+    decaying and theta keeps moving; never seen: untouched)."""
+    import torch
+    from gaussian_splatting_differentiable_ewa_amd import _lib as L
+    cfg, b = run["cfg"], run["buf"]
+    dev = b.device
+    p0 = run["gpu"]["params_t"]
+    rect0 = b.rect.clone()
+    rng = np.random.default_rng(7)
+    g2 = torch.from_numpy((rng.standard_normal((b.V * b.n * 9,)) * 1e-3).astype(np.float32)).to(dev)
+    n = b.n
+    # visibility per call: all, then a half, then a different half
+    keep = [np.ones(n, bool), rng.random(n) < 0.5, rng.random(n) < 0.5]
+    keep[0][: n // 4] = False  # a quarter is never seen in the first call
+    keep[1][: n // 8] = False  # an eighth never at all
+    keep[2][: n // 8] = False
+    dense = [p0.clone(), torch.zeros_like(p0), torch.zeros_like(p0)]
+    skip = [p0.clone(), torch.zeros_like(p0), torch.zeros_like(p0)]
+    state = torch.zeros(n, dtype=torch.uint8, device=dev)
+    for step, kp in enumerate(keep, start=1):
+        r = rect0.view(b.V, n, 4).clone()
+        r[:, torch.from_numpy(~kp).to(dev)] = 0
+        b.rect.copy_(r.view(-1))
+        b.grad2d.copy_(g2)
+        args = (n, b.sh_degree, b.cams, b.rect, b.grad2d)
+        hyper = (cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, step)
+        L.gs_preprocess_bwd_adam(dense[0], *args, dense[1], dense[2], *hyper)
+        L.gs_preprocess_bwd_adam(skip[0], *args, skip[1], skip[2], *hyper, state=state)
+    torch.cuda.synchronize()
+    b.rect.copy_(rect0)
+    for a, c in zip(dense, skip):
+        assert torch.equal(a, c)
+    st = state.cpu().numpy()
+    r0 = rect0.view(b.V, n, 4).cpu().numpy().view(np.uint16).astype(np.int32)
+    vis0 = ((r0[..., 2] > r0[..., 0]) & (r0[..., 3] > r0[..., 1])).any(axis=0)  # visible in the scene itself
+    ever = (keep[0] | keep[1] | keep[2]) & vis0
+    assert np.array_equal(st != 0, ever)
+    # never seen: untouched
+    assert torch.equal(skip[0][:, : n // 8], p0[:, : n // 8])
+    print({"never_seen": int((~ever).sum()), "seen": int(ever.sum())})
