@@ -77,7 +77,7 @@ def lib():
             "gs_emit_intersections": ([_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _U64, _P, _P], ctypes.c_int),
             "gs_sort_keys": ([_P, _P, _P, _P, _U64, _I32, _P, _SZ, _P, _P], ctypes.c_int),
             "gs_tile_ranges": ([_P, _U64, _I64, _P, _P], ctypes.c_int),
-            "gs_tile_lists": ([_P, _P, _I64, _I32, _I32, _I32, _P, _U64, _P, _P, _P, _SZ, _P], ctypes.c_int),
+            "gs_tile_lists": ([_P, _P, _I64, _I32, _I32, _I32, _P, _P, _U64, _P, _P, _P, _SZ, _P], ctypes.c_int),
             "gs_tile_masks_workspace_bytes": ([_U64], _SZ),
             "gs_tile_masks": ([_P, _I64, _P, _P, _U64, _P, _I32, _P, _P, _SZ, _P], ctypes.c_int),
             "gs_rasterize_fwd": ([_P, _I64, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P], ctypes.c_int),
@@ -176,8 +176,10 @@ def gs_emit_intersections(rec, rect, offsets, n, n_views, width, height, keys, v
                                        _stream(stream)), "gs_emit_intersections")
 
 
-def gs_tile_lists(rec, rect, n, n_views, width, height, vals, capacity, ranges, overflow, ws, stream=None):
-    _check(lib().gs_tile_lists(_ptr(rec), _ptr(rect), n, n_views, width, height, _ptr(vals), capacity,
+def gs_tile_lists(rec, rect, n, n_views, width, height, vals, capacity, ranges, overflow, ws, masks=None,
+                  stream=None):
+    """masks (optional): the entries' sub-block masks, as gs_tile_masks."""
+    _check(lib().gs_tile_lists(_ptr(rec), _ptr(rect), n, n_views, width, height, _ptr(vals), _ptr(masks), capacity,
                                _ptr(ranges), _ptr(overflow), _ptr(ws), ws.numel() * ws.element_size(),
                                _stream(stream)), "gs_tile_lists")
 

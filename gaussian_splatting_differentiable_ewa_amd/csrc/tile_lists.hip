@@ -25,9 +25,14 @@
 // (depth, id) is a total order, so the arbitrary slot order of step 4 never
 // shows: the lists equal those of the global key sort. The positive fp32
 // depths order like their bit patterns.
+//
+// With a mask output, each sort kernel also writes every entry's 16-bit
+// sub-block mask (gs_tile_masks' test, tile_mask16 in raster_common.h) as it
+// writes the entry's id: the record gathers and the test fill the latency of
+// the sorts.
 #include <algorithm>
 
-#include "internal.h"
+#include "raster_common.h"
 
 namespace gs {
 
@@ -206,12 +211,34 @@ __global__ __launch_bounds__(256) void k_bin_fill(const float* __restrict__ rec,
     if (over) *overflow = 1;
 }
 
+// Where a kernel writes the id of a tile's entry, its mask too (when wanted).
+struct MaskOut {
+    uint16_t* masks;
+    const float* rec;
+    int64_t n;
+    int W, H, TX, T;
+};
+
+__device__ __forceinline__ void write_mask(const MaskOut& mo, int64_t tile_lin, uint32_t pos, uint32_t id)
+{
+    if (!mo.masks) return;
+    const int64_t view = tile_lin / mo.T;
+    const int tile = (int)(tile_lin - view * mo.T);
+    const int ty = tile / mo.TX, tx = tile - ty * mo.TX;
+    Entry E;
+    E.valid = true;
+    E.gid = id;
+    gather_record(E, mo.rec + view * mo.n * GS_REC_FLOATS);
+    mo.masks[pos] = (uint16_t)tile_mask16(E, tx * 16, ty * 16, mo.W, mo.H);
+}
+
 // Tiles of up to 64 entries, one wave each: a bitonic sort of the 64-bit
 // values (depth bits << 32 | id) across the lanes (absent lanes hold the
 // largest value and sort last).
 __global__ __launch_bounds__(256) void k_tl_sort_small(const uint32_t* __restrict__ ranges, int64_t n_tiles,
                                                        const uint64_t* __restrict__ total_dev, uint64_t capacity,
-                                                       const uint2* __restrict__ pairs, uint32_t* __restrict__ vals)
+                                                       const uint2* __restrict__ pairs, uint32_t* __restrict__ vals,
+                                                       const MaskOut mo)
 {
     const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (tile >= n_tiles) return;
@@ -238,7 +265,10 @@ __global__ __launch_bounds__(256) void k_tl_sort_small(const uint32_t* __restric
             }
         }
     }
-    if (lane < n) vals[start + lane] = (uint32_t)key;
+    if (lane < n) {
+        vals[start + lane] = (uint32_t)key;
+        write_mask(mo, tile, start + lane, (uint32_t)key);
+    }
 }
 
 // lanes of the wave (among `valid`) whose 8-bit digit equals this lane's
@@ -313,7 +343,8 @@ constexpr int WV_ROUNDS = WV_CAP / 64;
 // wave's registers and a private slice of LDS.
 __global__ __launch_bounds__(256) void k_tl_sort_wave(const uint32_t* __restrict__ ranges, int64_t n_tiles,
                                                       const uint64_t* __restrict__ total_dev, uint64_t capacity,
-                                                      const uint2* __restrict__ pairs, uint32_t* __restrict__ vals)
+                                                      const uint2* __restrict__ pairs, uint32_t* __restrict__ vals,
+                                                      const MaskOut mo)
 {
     __shared__ uint32_t s_key[4][WV_CAP];
     __shared__ uint16_t s_idx[4][WV_CAP];
@@ -429,13 +460,17 @@ __global__ __launch_bounds__(256) void k_tl_sort_wave(const uint32_t* __restrict
             }
     }
     asm volatile("" ::: "memory");
-    for (uint32_t i = lane; i < n; i += 64) vals[start + i] = tp[si[i]].y;
+    for (uint32_t i = lane; i < n; i += 64) {
+        const uint32_t id = tp[si[i]].y;
+        vals[start + i] = id;
+        write_mask(mo, tile, start + i, id);
+    }
 }
 
 __global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restrict__ ranges,
                                                         const uint64_t* __restrict__ total_dev, uint64_t capacity,
                                                         uint2* __restrict__ pairs, uint2* __restrict__ alt,
-                                                        uint32_t* __restrict__ vals)
+                                                        uint32_t* __restrict__ vals, const MaskOut mo)
 {
     __shared__ uint32_t s_key[TL_CAP];
     __shared__ uint16_t s_idx[TL_CAP];  // position of each key in the tile's unsorted pairs
@@ -529,7 +564,11 @@ __global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restri
             [&](uint32_t i, uint32_t a) { return tp[s_idx[i]].y < tp[s_idx[a]].y; },
             [&](uint32_t i, uint32_t a) { const uint16_t x = s_idx[i]; s_idx[i] = s_idx[a]; s_idx[a] = x; });
         __syncthreads();
-        for (uint32_t i = t; i < n; i += TL_THREADS) vals[start + i] = tp[s_idx[i]].y;
+        for (uint32_t i = t; i < n; i += TL_THREADS) {
+            const uint32_t id = tp[s_idx[i]].y;
+            vals[start + i] = id;
+            write_mask(mo, blockIdx.x, start + i, id);
+        }
         return;
     }
 
@@ -615,7 +654,11 @@ __global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restri
         [&](uint32_t i, uint32_t a) { return src[i].y < src[a].y; },
         [&](uint32_t i, uint32_t a) { const uint32_t x = src[i].y; src[i].y = src[a].y; src[a].y = x; });
     __syncthreads();
-    for (uint32_t i = t; i < n; i += TL_THREADS) vals[start + i] = src[i].y;
+    for (uint32_t i = t; i < n; i += TL_THREADS) {
+        const uint32_t id = src[i].y;
+        vals[start + i] = id;
+        write_mask(mo, blockIdx.x, start + i, id);
+    }
 }
 
 // workspace: table [V][chunks][T] | totals [V T + 1] | total (u64) | scan
@@ -678,8 +721,8 @@ size_t gs_tile_lists_workspace_bytes(int64_t n, int32_t n_views, int32_t width, 
 }
 
 gs_status gs_tile_lists(const float* rec, const uint16_t* rect, int64_t n, int32_t n_views, int32_t width,
-                        int32_t height, uint32_t* vals, uint64_t capacity, uint32_t* ranges, int32_t* overflow,
-                        void* ws, size_t ws_bytes, void* stream)
+                        int32_t height, uint32_t* vals, uint16_t* masks, uint64_t capacity, uint32_t* ranges,
+                        int32_t* overflow, void* ws, size_t ws_bytes, void* stream)
 {
     if (!tl_sizes_ok(n, n_views, width, height)) return GS_ERR_INVALID_ARGUMENT;
     if (!ranges || !overflow || !ws) return GS_ERR_INVALID_ARGUMENT;
@@ -716,14 +759,22 @@ gs_status gs_tile_lists(const float* rec, const uint16_t* rect, int64_t n, int32
     hipLaunchKernelGGL(k_bin_fill, dim3(bin_blocks), dim3(256), 0, s, rec, rect, G, table, totals, pairs, capacity,
                        overflow);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
+    MaskOut mo;
+    mo.masks = masks;
+    mo.rec = rec;
+    mo.n = n;
+    mo.W = width;
+    mo.H = height;
+    mo.TX = G.tiles_x;
+    mo.T = (int)G.tiles;
     hipLaunchKernelGGL(k_tl_sort_small, dim3(grid_for((uint64_t)n_tiles, 4)), dim3(256), 0, s, ranges, n_tiles, total,
-                       capacity, pairs, vals);
+                       capacity, pairs, vals, mo);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     hipLaunchKernelGGL(k_tl_sort_wave, dim3(grid_for((uint64_t)n_tiles, 4)), dim3(256), 0, s, ranges, n_tiles, total,
-                       capacity, pairs, vals);
+                       capacity, pairs, vals, mo);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     hipLaunchKernelGGL(k_tl_sort, dim3((unsigned)n_tiles), dim3(TL_THREADS), 0, s, ranges, total, capacity, pairs,
-                       alt, vals);
+                       alt, vals, mo);
     return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
 }
 

@@ -75,9 +75,9 @@ class Buffers:
         dev = self.device
         self.vals = torch.empty(cap, dtype=torch.int32, device=dev)
         self.masks = torch.empty(cap, dtype=torch.int16, device=dev)
-        self.tm_ws = torch.empty(L.tile_masks_workspace_bytes(cap), dtype=torch.uint8, device=dev)
         self.allocated_for = self.path
         if self.path == "radix":
+            self.tm_ws = torch.empty(L.tile_masks_workspace_bytes(cap), dtype=torch.uint8, device=dev)
             self.keys = torch.empty(cap, dtype=torch.int64, device=dev)
             self.keys_alt = torch.empty(cap, dtype=torch.int64, device=dev)
             self.vals_alt = torch.empty(cap, dtype=torch.int32, device=dev)
@@ -93,7 +93,7 @@ class Buffers:
             return 0
         if self.path == "radix":
             return 2 * 12 * self.capacity + 6 * self.capacity + self.sort_ws.numel()
-        return 10 * self.capacity + self.tl_ws.numel()
+        return 6 * self.capacity + self.tl_ws.numel()
 
     @property
     def sorted_keys(self):
@@ -121,6 +121,10 @@ class Buffers:
         self.tile_masks()
 
     def tile_masks(self):
+        """The lists' sub-block masks: written by the binned builder with the
+        lists; computed from the finished lists on the global-sort path."""
+        if self.path == "binned":
+            return
         L.gs_tile_masks(self.rec, self.n, self.ranges, self.sorted_vals, self.capacity, self.cams, self.masks,
                         self.tm_ws)
 
@@ -128,7 +132,7 @@ class Buffers:
         """The lists and ranges alone (see ``intersections``)."""
         if not read_count and self.lists_without_count():
             L.gs_tile_lists(self.rec, self.rect, self.n, self.V, self.W, self.H, self.vals, self.capacity,
-                            self.ranges, self.overflow, self.tl_ws)
+                            self.ranges, self.overflow, self.tl_ws, masks=self.masks)
             return
         self.K = int(self.total.item())
         if self.K >= 2 ** 32:
@@ -139,7 +143,7 @@ class Buffers:
         if self.path == "binned":
             self.sorted_in_alt = False
             L.gs_tile_lists(self.rec, self.rect, self.n, self.V, self.W, self.H, self.vals, self.capacity,
-                            self.ranges, self.overflow, self.tl_ws)
+                            self.ranges, self.overflow, self.tl_ws, masks=self.masks)
             return
         L.gs_emit_intersections(self.rec, self.rect, self.offsets, self.n, self.V, self.W, self.H,
                                 self.keys, self.vals, self.capacity, self.overflow)

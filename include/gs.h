@@ -209,7 +209,10 @@ size_t gs_tile_lists_workspace_bytes(int64_t n, int32_t n_views, int32_t width, 
  * slots and sorting each tile's slots by (depth, Gaussian index) on its own.
  *   rec, rect, n, n_views, width, height   as for gs_emit_intersections
  *   vals       device out [capacity]: Gaussian ids, tile by tile, front to back
- *   capacity   slots in vals (>= the total of gs_preprocess; < 2^32)
+ *   masks      device out [capacity] uint16, or NULL: each entry's sub-block
+ *              mask, exactly as gs_tile_masks computes it (written with the
+ *              entry's id by the per-tile sorts)
+ *   capacity   slots in vals and masks (>= the total of gs_preprocess; < 2^32)
  *   ranges     device out [n_views * tiles][2]: [start, end), (0, 0) if empty
  *   overflow   device int32: cleared, then set to 1 if the intersections
  *              exceed capacity (the lists are then incomplete, and the ranges
@@ -219,9 +222,9 @@ size_t gs_tile_lists_workspace_bytes(int64_t n, int32_t n_views, int32_t width, 
  * or more than 8192 tile columns.
  */
 gs_status gs_tile_lists(const float* rec, const uint16_t* rect, int64_t n, int32_t n_views,
-                        int32_t width, int32_t height, uint32_t* vals, uint64_t capacity,
-                        uint32_t* ranges, int32_t* overflow, void* ws, size_t ws_bytes,
-                        void* stream);
+                        int32_t width, int32_t height, uint32_t* vals, uint16_t* masks,
+                        uint64_t capacity, uint32_t* ranges, int32_t* overflow, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /*
  * gs_tile_ranges -- for every (view, tile) id t = key >> 32, the range

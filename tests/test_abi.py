@@ -90,17 +90,17 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert alt.value == 0
     # gs_tile_lists
     big = ctypes.c_size_t(1 << 40)
-    assert lib.gs_tile_lists(fake, fake, -1, 1, 256, 256, fake, 10, fake, fake, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, 10, 0, 256, 256, fake, 10, fake, fake, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 0, fake, 10, fake, fake, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, fake, 10, None, fake, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, fake, 10, fake, None, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, None, 10, fake, fake, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, fake, 1 << 32, fake, fake, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, -1, 1, 256, 256, fake, None, 10, fake, fake, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, 10, 0, 256, 256, fake, None, 10, fake, fake, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 0, fake, None, 10, fake, fake, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, fake, None, 10, None, fake, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, fake, None, 10, fake, None, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, None, None, 10, fake, fake, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, fake, None, 1 << 32, fake, fake, fake, big, None) == INV
     need = L.tile_lists_workspace_bytes(10, 1, 256, 256, 10)
     assert need > 0 and L.tile_lists_workspace_bytes(10, 0, 256, 256, 10) == 0
     assert L.tile_lists_workspace_bytes(10, 1, 16 * 8193, 256, 10) == 0
-    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, fake, 10, fake, fake, fake, need - 1, None) == INV
+    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, fake, None, 10, fake, fake, fake, need - 1, None) == INV
     # gs_tile_ranges
     assert lib.gs_tile_ranges(fake, 10, -1, fake, None) == INV
     assert lib.gs_tile_ranges(None, 10, 4, fake, None) == INV
