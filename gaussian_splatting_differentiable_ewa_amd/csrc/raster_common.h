@@ -183,17 +183,17 @@ __device__ __forceinline__ bool band_span(const MaskGeom& M, float yc0, float yc
 }
 
 // Bits of the four sub-block columns from pixel tx0 whose pixel-centre
-// range meets [xl, xr] (columns outside the image never).
+// range [tx0 + 4k + 0.5, min(tx0 + 4k + 4, W) - 0.5] meets [xl, xr]
+// (columns outside the image never): k runs from the first column whose
+// right centre is >= xl to the last whose left centre is <= xr.
 __device__ __forceinline__ uint32_t span_cols(float xl, float xr, int tx0, int W)
 {
-    uint32_t row = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int bx = tx0 + 4 * k;
-        const float x0 = (float)bx + 0.5f, x1 = (float)min(bx + 4, W) - 0.5f;
-        row |= (uint32_t)(bx < W && xr >= x0 && xl <= x1) << k;
-    }
-    return row;
+    if (xl > (float)W - 0.5f) return 0u;  // right of every pixel centre (and of a clipped last column)
+    const float base = (float)tx0;
+    const int khi = (int)floorf(fminf(fmaxf((xr - base - 0.5f) * 0.25f, -8.f), 8.f));
+    const int klo = (int)ceilf(fminf(fmaxf((xl - base - 3.5f) * 0.25f, -8.f), 8.f));
+    const int hi = min(khi, min(3, ((W - tx0 + 3) >> 2) - 1)), lo = max(klo, 0);
+    return hi < lo ? 0u : ((2u << hi) - 1u) & ~((1u << lo) - 1u);
 }
 
 // The pixel-centre rows of sub-block row r of the tile row starting at ty0.
