@@ -90,6 +90,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="scene id (2 = the headline workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--band-rows", type=int, default=None,
+                    help="memory-capped mode: lists and raster one window of this many tile rows at a time")
     ap.add_argument("--cpu-sample-views", type=int, default=1,
                     help="views of the workload the CPU oracle runs (its time is scaled to all views)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -155,7 +157,7 @@ def main():
     params = torch.from_numpy(params_np).to(dev)
     target = render(torch.from_numpy(S.make_target_params(cfg)).to(dev), cfg.sh_degree, cams).clone()
     ts = TrainStep(params.clone(), cfg.sh_degree, cams, target, lr=cfg.lr, betas=(cfg.beta1, cfg.beta2),
-                   eps=cfg.eps)
+                   eps=cfg.eps, band_rows=args.band_rows)
     print(f"[bench] {cfg.name}: inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     b = ts.buf
@@ -234,6 +236,7 @@ def main():
         "mpix_per_s": round(mpix, 2),
         "step_hbm_fraction": round(frac_step, 4), "step_algorithmic_bytes": int(step_bytes),
         "intersections": b.K, "k_per_gaussian": round(b.K / b.n, 4), "list_builder": b.path,
+        "band_rows": args.band_rows,
         "host_count_read": not ts.defer_count or not b.lists_without_count(), "redone_steps": redone,
         "visible_per_view": n_vis,
         "max_per_tile": max_per_tile, "peak_intersection_bytes": int(peak_list_bytes),

@@ -77,14 +77,16 @@ def lib():
             "gs_emit_intersections": ([_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _U64, _P, _P], ctypes.c_int),
             "gs_sort_keys": ([_P, _P, _P, _P, _U64, _I32, _P, _SZ, _P, _P], ctypes.c_int),
             "gs_tile_ranges": ([_P, _U64, _I64, _P, _P], ctypes.c_int),
-            "gs_tile_lists": ([_P, _P, _I64, _I32, _I32, _I32, _P, _P, _U64, _P, _P, _P, _SZ, _P], ctypes.c_int),
+            "gs_tile_lists": ([_P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P, _U64, _P, _P, _P, _SZ, _P],
+                              ctypes.c_int),
             "gs_tile_masks_workspace_bytes": ([_U64], _SZ),
             "gs_tile_masks": ([_P, _I64, _P, _P, _U64, _P, _I32, _P, _P, _SZ, _P], ctypes.c_int),
-            "gs_rasterize_fwd": ([_P, _I64, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P], ctypes.c_int),
-            "gs_rasterize_fwd_l1": ([_P, _I64, _P, _P, _P, _P, _I32, _P, _P, _F32, _P, _P, _P, _P, _P, _I32, _P, _SZ,
-                                     _P], ctypes.c_int),
+            "gs_rasterize_fwd": ([_P, _I64, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P], ctypes.c_int),
+            "gs_rasterize_fwd_l1": ([_P, _I64, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _F32, _P, _P, _P, _P, _P,
+                                     _I32, _P, _SZ, _P], ctypes.c_int),
             "gs_loss_l1": ([_P, _P, _I64, _F32, _P, _P, _I32, _P], ctypes.c_int),
-            "gs_rasterize_bwd": ([_P, _I64, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _I32, _P], ctypes.c_int),
+            "gs_rasterize_bwd": ([_P, _I64, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _I32, _P],
+                                 ctypes.c_int),
             "gs_preprocess_bwd": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P], ctypes.c_int),
             "gs_adam_step": ([_P, _P, _P, _P, _I64, _F64, _F64, _F64, _F64, _I64, _P], ctypes.c_int),
             "gs_adam_step_unless": ([_P, _P, _P, _P, _I64, _F64, _F64, _F64, _F64, _I64, _P, _P], ctypes.c_int),
@@ -176,10 +178,20 @@ def gs_emit_intersections(rec, rect, offsets, n, n_views, width, height, keys, v
                                        _stream(stream)), "gs_emit_intersections")
 
 
+def tiles_y(height: int) -> int:
+    return int(lib().gs_tiles_y(height))
+
+
+def _window(height, rows):
+    return tiles_y(height) if rows is None else rows
+
+
 def gs_tile_lists(rec, rect, n, n_views, width, height, vals, capacity, ranges, overflow, ws, masks=None,
-                  stream=None):
-    """masks (optional): the entries' sub-block masks, as gs_tile_masks."""
-    _check(lib().gs_tile_lists(_ptr(rec), _ptr(rect), n, n_views, width, height, _ptr(vals), _ptr(masks), capacity,
+                  row0=0, rows=None, stream=None):
+    """masks (optional): the entries' sub-block masks, as gs_tile_masks;
+    row0, rows: the window of tile rows (the whole image by default)."""
+    _check(lib().gs_tile_lists(_ptr(rec), _ptr(rect), n, n_views, width, height, row0, _window(height, rows),
+                               _ptr(vals), _ptr(masks), capacity,
                                _ptr(ranges), _ptr(overflow), _ptr(ws), ws.numel() * ws.element_size(),
                                _stream(stream)), "gs_tile_lists")
 
@@ -208,19 +220,20 @@ def gs_tile_masks(rec, n, ranges, vals, capacity, cams, masks, ws, stream=None):
            "gs_tile_masks")
 
 
-def gs_rasterize_fwd(rec, n, ranges, vals, masks, cams, bg, image, T_final, n_contrib, stream=None):
+def gs_rasterize_fwd(rec, n, ranges, vals, masks, cams, bg, image, T_final, n_contrib, row0=0, rows=None, stream=None):
     bgv = (ctypes.c_float * 3)(*bg)
-    _check(lib().gs_rasterize_fwd(_ptr(rec), n, _ptr(ranges), _ptr(vals), _ptr(masks), cameras(cams), len(cams), bgv,
+    _check(lib().gs_rasterize_fwd(_ptr(rec), n, _ptr(ranges), _ptr(vals), _ptr(masks), cameras(cams), len(cams), row0,
+                                  _window(cams[0].height, rows), bgv,
                                   _ptr(image), _ptr(T_final), _ptr(n_contrib), _stream(stream)),
            "gs_rasterize_fwd")
 
 
 def gs_rasterize_fwd_l1(rec, n, ranges, vals, masks, cams, bg, target, scale, image, T_final, n_contrib, dL_dimage, loss,
-                        ws, accumulate=False, stream=None):
+                        ws, accumulate=False, row0=0, rows=None, stream=None):
     """image may be None (not written)."""
     bgv = (ctypes.c_float * 3)(*bg)
     _check(lib().gs_rasterize_fwd_l1(_ptr(rec), n, _ptr(ranges), _ptr(vals), _ptr(masks), cameras(cams), len(cams),
-                                     bgv,
+                                     row0, _window(cams[0].height, rows), bgv,
                                      _ptr(target), scale, _ptr(image), _ptr(T_final), _ptr(n_contrib),
                                      _ptr(dL_dimage), _ptr(loss), int(bool(accumulate)), _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream(stream)), "gs_rasterize_fwd_l1")
@@ -232,9 +245,10 @@ def gs_loss_l1(image, target, count, scale, dL_dimage, loss, accumulate=False, s
 
 
 def gs_rasterize_bwd(rec, n, ranges, vals, masks, cams, bg, T_final, n_contrib, dL_dimage, grad2d,
-                     accumulate=False, stream=None):
+                     accumulate=False, row0=0, rows=None, stream=None):
     bgv = (ctypes.c_float * 3)(*bg)
-    _check(lib().gs_rasterize_bwd(_ptr(rec), n, _ptr(ranges), _ptr(vals), _ptr(masks), cameras(cams), len(cams), bgv,
+    _check(lib().gs_rasterize_bwd(_ptr(rec), n, _ptr(ranges), _ptr(vals), _ptr(masks), cameras(cams), len(cams), row0,
+                                  _window(cams[0].height, rows), bgv,
                                   _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimage), _ptr(grad2d),
                                   int(bool(accumulate)), _stream(stream)), "gs_rasterize_bwd")
 

@@ -42,7 +42,9 @@ struct QuarterCtx {
     float px, py;
 };
 
-__device__ __forceinline__ QuarterCtx quarter_ctx(int W, int H, int TX, int T)
+// T: tiles per view in the window of tile rows the launch covers, row0: the
+// window's first tile row.
+__device__ __forceinline__ QuarterCtx quarter_ctx(int W, int H, int TX, int T, int row0)
 {
     QuarterCtx t;
     const uint32_t lb = xcd_chunked(blockIdx.x, gridDim.x);
@@ -50,7 +52,7 @@ __device__ __forceinline__ QuarterCtx quarter_ctx(int W, int H, int TX, int T)
     t.tile_lin = lb >> 2;
     t.view = t.tile_lin / (uint32_t)T;
     const uint32_t tile = t.tile_lin - t.view * (uint32_t)T;
-    const uint32_t ty = tile / (uint32_t)TX, tx = tile - ty * (uint32_t)TX;
+    const uint32_t wy = tile / (uint32_t)TX, tx = tile - wy * (uint32_t)TX, ty = wy + (uint32_t)row0;
     t.qx0 = (int)tx * 16 + (int)(quad & 1u) * 8;
     t.qy0 = (int)ty * 16 + (int)(quad >> 1) * 8;
     t.mshift = (int)(quad >> 1) * 8 + (int)(quad & 1u) * 2;
@@ -249,17 +251,21 @@ __device__ __forceinline__ int row_max16(int x)
 
 struct RasterArgs {
     DevCameras dc;
+    int32_t row0, T;  // the window of tile rows: first row, tiles per view
     int64_t n_blocks;
 };
 
 static inline bool raster_args(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
-                               const uint16_t* masks, const gs_camera* cams, int32_t n_views, const float* bg,
-                               RasterArgs& a)
+                               const uint16_t* masks, const gs_camera* cams, int32_t n_views, int32_t row0,
+                               int32_t rows, const float* bg, RasterArgs& a)
 {
     if (n < 0 || !ranges || !bg) return false;
     if (n > 0 && (!rec || !vals || !masks)) return false;
     if (!make_dev_cameras(cams, n_views, a.dc)) return false;
-    a.n_blocks = (int64_t)n_views * a.dc.tiles_per_view * 4;
+    if (row0 < 0 || rows < 1 || row0 + rows > a.dc.tiles_y) return false;
+    a.row0 = row0;
+    a.T = a.dc.tiles_x * rows;
+    a.n_blocks = (int64_t)n_views * a.T * 4;
     return a.n_blocks < ((int64_t)1 << 31);
 }
 

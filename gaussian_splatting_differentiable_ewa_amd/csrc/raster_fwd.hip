@@ -45,7 +45,7 @@ __device__ __forceinline__ void raster_fwd_body(const float* __restrict__ rec, i
                                                 const uint32_t* __restrict__ ranges,
                                                 const uint32_t* __restrict__ vals,
                                                 const uint16_t* __restrict__ masks, int W, int H, int TX, int T,
-                                                float bg0, float bg1, float bg2, float* __restrict__ image,
+                                                int row0, float bg0, float bg1, float bg2, float* __restrict__ image,
                                                 float* __restrict__ T_final, int32_t* __restrict__ n_contrib,
                                                 const float* __restrict__ target, float scale,
                                                 float* __restrict__ dL, double* __restrict__ partial)
@@ -57,7 +57,7 @@ __device__ __forceinline__ void raster_fwd_body(const float* __restrict__ rec, i
     __shared__ float4 s_rec[3 * (RW_BATCH + 1)];
     __shared__ uint8_t s_mask[RW_BATCH];
     __shared__ __align__(16) uint16_t s_list[4 * RW_BATCH];  // record byte offsets, read 8 at a time
-    const QuarterCtx t = quarter_ctx(W, H, TX, T);
+    const QuarterCtx t = quarter_ctx(W, H, TX, T, row0);
     if (t.empty) {
         if (L1 && t.lane == 0) partial[blockIdx.x] = 0.0;
         return;
@@ -181,11 +181,11 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_fwd(const float* __restri
                                                            const uint32_t* __restrict__ ranges,
                                                            const uint32_t* __restrict__ vals,
                                                            const uint16_t* __restrict__ masks, int W, int H, int TX,
-                                                           int T, float bg0, float bg1, float bg2,
+                                                           int T, int row0, float bg0, float bg1, float bg2,
                                                            float* __restrict__ image, float* __restrict__ T_final,
                                                            int32_t* __restrict__ n_contrib)
 {
-    raster_fwd_body<false>(rec, n, ranges, vals, masks, W, H, TX, T, bg0, bg1, bg2, image, T_final, n_contrib, nullptr, 0.f,
+    raster_fwd_body<false>(rec, n, ranges, vals, masks, W, H, TX, T, row0, bg0, bg1, bg2, image, T_final, n_contrib, nullptr, 0.f,
                            nullptr, nullptr);
 }
 
@@ -193,13 +193,13 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_fwd_l1(const float* __res
                                                               const uint32_t* __restrict__ ranges,
                                                               const uint32_t* __restrict__ vals,
                                                               const uint16_t* __restrict__ masks, int W, int H, int TX,
-                                                              int T, float bg0, float bg1, float bg2,
+                                                              int T, int row0, float bg0, float bg1, float bg2,
                                                               float* __restrict__ image, float* __restrict__ T_final,
                                                               int32_t* __restrict__ n_contrib,
                                                               const float* __restrict__ target, float scale,
                                                               float* __restrict__ dL, double* __restrict__ partial)
 {
-    raster_fwd_body<true>(rec, n, ranges, vals, masks, W, H, TX, T, bg0, bg1, bg2, image, T_final, n_contrib, target, scale,
+    raster_fwd_body<true>(rec, n, ranges, vals, masks, W, H, TX, T, row0, bg0, bg1, bg2, image, T_final, n_contrib, target, scale,
                           dL, partial);
 }
 
@@ -234,18 +234,19 @@ size_t gs_rasterize_fwd_l1_workspace_bytes(int32_t n_views, int32_t width, int32
 }
 
 gs_status gs_rasterize_fwd_l1(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
-                              const uint16_t* masks, const gs_camera* cams, int32_t n_views, const float* bg, const float* target,
+                              const uint16_t* masks, const gs_camera* cams, int32_t n_views, int32_t row0,
+                              int32_t rows, const float* bg, const float* target,
                               float scale, float* image, float* T_final, int32_t* n_contrib, float* dL_dimage,
                               double* loss, int32_t accumulate, void* ws, size_t ws_bytes, void* stream)
 {
     RasterArgs a;
-    if (!raster_args(rec, n, ranges, vals, masks, cams, n_views, bg, a)) return GS_ERR_INVALID_ARGUMENT;
+    if (!raster_args(rec, n, ranges, vals, masks, cams, n_views, row0, rows, bg, a)) return GS_ERR_INVALID_ARGUMENT;
     if (!T_final || !n_contrib || !target || !dL_dimage || !loss || !ws) return GS_ERR_INVALID_ARGUMENT;
     if (ws_bytes < (size_t)a.n_blocks * sizeof(double)) return GS_ERR_INVALID_ARGUMENT;
     hipStream_t s = (hipStream_t)stream;
     double* partial = (double*)ws;
     hipLaunchKernelGGL(k_raster_fwd_l1, dim3((unsigned)a.n_blocks), dim3(RW_THREADS), 0, s, rec, n, ranges, vals,
-                       masks, a.dc.width, a.dc.height, a.dc.tiles_x, a.dc.tiles_per_view, bg[0], bg[1], bg[2], image, T_final,
+                       masks, a.dc.width, a.dc.height, a.dc.tiles_x, a.T, a.row0, bg[0], bg[1], bg[2], image, T_final,
                        n_contrib, target, scale, dL_dimage, partial);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     if (!accumulate && fill_u32((uint32_t*)loss, 2, 0u, s) != hipSuccess) return GS_ERR_HIP;
@@ -255,14 +256,15 @@ gs_status gs_rasterize_fwd_l1(const float* rec, int64_t n, const uint32_t* range
 }
 
 gs_status gs_rasterize_fwd(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
-                           const uint16_t* masks, const gs_camera* cams, int32_t n_views, const float* bg, float* image, float* T_final,
+                           const uint16_t* masks, const gs_camera* cams, int32_t n_views, int32_t row0, int32_t rows,
+                           const float* bg, float* image, float* T_final,
                            int32_t* n_contrib, void* stream)
 {
     RasterArgs a;
-    if (!raster_args(rec, n, ranges, vals, masks, cams, n_views, bg, a)) return GS_ERR_INVALID_ARGUMENT;
+    if (!raster_args(rec, n, ranges, vals, masks, cams, n_views, row0, rows, bg, a)) return GS_ERR_INVALID_ARGUMENT;
     if (!image || !T_final || !n_contrib) return GS_ERR_INVALID_ARGUMENT;
     hipLaunchKernelGGL(k_raster_fwd, dim3((unsigned)a.n_blocks), dim3(RW_THREADS), 0, (hipStream_t)stream, rec, n,
-                       ranges, vals, masks, a.dc.width, a.dc.height, a.dc.tiles_x, a.dc.tiles_per_view, bg[0], bg[1], bg[2],
+                       ranges, vals, masks, a.dc.width, a.dc.height, a.dc.tiles_x, a.T, a.row0, bg[0], bg[1], bg[2],
                        image, T_final, n_contrib);
     return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
 }

@@ -42,23 +42,12 @@ constexpr int TL_ROUNDS = TL_CAP / TL_THREADS;  // rounds of 64 keys per wave, a
 constexpr int GL_CHUNK = 4096;                  // entries per chunk of the global-memory path
 constexpr int GL_ROUNDS = GL_CHUNK / TL_THREADS;
 
-// the pair's tile rectangle, clipped to the tile grid
-__device__ __forceinline__ bool rect_of(const uint16_t* __restrict__ rect, int64_t idx, uint32_t tiles_x,
-                                        uint32_t tiles_y, uint32_t& x0, uint32_t& y0, uint32_t& x1, uint32_t& y1)
-{
-    const uint2 rr = *(const uint2*)(rect + 4 * idx);
-    x0 = rr.x & 0xffffu;
-    y0 = rr.x >> 16;
-    x1 = min(rr.y & 0xffffu, tiles_x);
-    y1 = min(rr.y >> 16, tiles_y);
-    return x1 > x0 && y1 > y0;
-}
-
 constexpr int BAND_TILES = 8192;  // LDS counters of one band of tile rows
 
 struct BinGrid {
-    int32_t tiles_x, tiles_y;
-    int64_t tiles;      // per view
+    int32_t tiles_x, tiles_y;  // tiles_y: rows of the window of tile rows the lists cover
+    int32_t row0;              // the window's first tile row in the image
+    int64_t tiles;      // per view, in the window
     int64_t n;          // Gaussians
     int32_t chunks;     // chunks of Gaussians per view
     int64_t chunk;      // Gaussians per chunk
@@ -87,16 +76,18 @@ __device__ __forceinline__ BinBlock bin_block(const BinGrid& G)
     return B;
 }
 
-// a pair's tile rectangle (as stored), clipped to the rows [ty0, ty1) and the
-// grid
+// a pair's tile rectangle (as stored, image rows), in the window's rows and
+// clipped to its rows [ty0, ty1) and the grid
 __device__ __forceinline__ bool band_rect(uint2 rr, const BinGrid& G, uint32_t ty0, uint32_t ty1, uint32_t& x0,
                                           uint32_t& y0, uint32_t& x1, uint32_t& y1)
 {
     x0 = rr.x & 0xffffu;
-    y0 = max(rr.x >> 16, ty0);
     x1 = min(rr.y & 0xffffu, (uint32_t)G.tiles_x);
-    y1 = min(rr.y >> 16, ty1);
-    return x1 > x0 && y1 > y0;
+    const int32_t ly0 = max((int32_t)(rr.x >> 16) - G.row0, (int32_t)ty0);
+    const int32_t ly1 = min((int32_t)(rr.y >> 16) - G.row0, (int32_t)ty1);
+    y0 = (uint32_t)max(ly0, 0);
+    y1 = (uint32_t)max(ly1, 0);
+    return x1 > x0 && ly1 > ly0;
 }
 
 __global__ __launch_bounds__(256) void k_bin_count(const uint16_t* __restrict__ rect, const BinGrid G,
@@ -216,7 +207,7 @@ struct MaskOut {
     uint16_t* masks;
     const float* rec;
     int64_t n;
-    int W, H, TX, T;
+    int W, H, TX, T, row0;  // T: tiles per view in the window, row0: its first tile row
 };
 
 __device__ __forceinline__ void write_mask(const MaskOut& mo, int64_t tile_lin, uint32_t pos, uint32_t id)
@@ -224,7 +215,7 @@ __device__ __forceinline__ void write_mask(const MaskOut& mo, int64_t tile_lin, 
     if (!mo.masks) return;
     const int64_t view = tile_lin / mo.T;
     const int tile = (int)(tile_lin - view * mo.T);
-    const int ty = tile / mo.TX, tx = tile - ty * mo.TX;
+    const int wy = tile / mo.TX, tx = tile - wy * mo.TX, ty = wy + mo.row0;
     Entry E;
     E.valid = true;
     E.gid = id;
@@ -671,11 +662,13 @@ static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Chunks per view: about 4M table entries in all, at least 1024 Gaussians
 // per chunk.
-static BinGrid bin_grid(int64_t n, int32_t n_views, int32_t width, int32_t height)
+static BinGrid bin_grid(int64_t n, int32_t n_views, int32_t width, int32_t height, int32_t row0 = 0,
+                        int32_t rows = -1)
 {
     BinGrid G;
     G.tiles_x = gs_tiles_x(width);
-    G.tiles_y = gs_tiles_y(height);
+    G.tiles_y = rows < 0 ? gs_tiles_y(height) : rows;
+    G.row0 = row0;
     G.tiles = (int64_t)G.tiles_x * G.tiles_y;
     G.n = n;
     const int64_t by_table = std::max<int64_t>(1, ((int64_t)1 << 22) / std::max<int64_t>(1, G.tiles * n_views));
@@ -692,7 +685,9 @@ static TlLayout tl_layout(const BinGrid& G, int32_t n_views, uint64_t capacity)
     const uint64_t n_tiles = (uint64_t)G.tiles * n_views;
     TlLayout L;
     L.table = 0;
-    L.totals = align256((size_t)n_tiles * G.chunks * 4);
+    // the table of any window of rows fits in the larger of the whole
+    // image's and 4M counters
+    L.totals = align256(std::max<size_t>((size_t)n_tiles * G.chunks, (size_t)1 << 22) * 4);
     L.total = L.totals + align256((n_tiles + 1) * 4);
     L.scan = L.total + 256;
     L.pairs = L.scan + align256(scan_workspace_bytes(n_tiles));
@@ -721,15 +716,17 @@ size_t gs_tile_lists_workspace_bytes(int64_t n, int32_t n_views, int32_t width, 
 }
 
 gs_status gs_tile_lists(const float* rec, const uint16_t* rect, int64_t n, int32_t n_views, int32_t width,
-                        int32_t height, uint32_t* vals, uint16_t* masks, uint64_t capacity, uint32_t* ranges,
-                        int32_t* overflow, void* ws, size_t ws_bytes, void* stream)
+                        int32_t height, int32_t row0, int32_t rows, uint32_t* vals, uint16_t* masks,
+                        uint64_t capacity, uint32_t* ranges, int32_t* overflow, void* ws, size_t ws_bytes,
+                        void* stream)
 {
     if (!tl_sizes_ok(n, n_views, width, height)) return GS_ERR_INVALID_ARGUMENT;
+    if (row0 < 0 || rows < 1 || row0 + rows > gs_tiles_y(height)) return GS_ERR_INVALID_ARGUMENT;
     if (!ranges || !overflow || !ws) return GS_ERR_INVALID_ARGUMENT;
     if (n > 0 && (!rec || !rect)) return GS_ERR_INVALID_ARGUMENT;
     if (capacity > 0 && !vals) return GS_ERR_INVALID_ARGUMENT;
     if (capacity >= ((uint64_t)1 << 32)) return GS_ERR_INVALID_ARGUMENT;
-    const BinGrid G = bin_grid(n, n_views, width, height);
+    const BinGrid G = bin_grid(n, n_views, width, height, row0, rows);
     const TlLayout L = tl_layout(G, n_views, capacity);
     if (ws_bytes < L.bytes) return GS_ERR_INVALID_ARGUMENT;
     const int64_t n_tiles = G.tiles * n_views;
@@ -767,6 +764,7 @@ gs_status gs_tile_lists(const float* rec, const uint16_t* rect, int64_t n, int32
     mo.H = height;
     mo.TX = G.tiles_x;
     mo.T = (int)G.tiles;
+    mo.row0 = row0;
     hipLaunchKernelGGL(k_tl_sort_small, dim3(grid_for((uint64_t)n_tiles, 4)), dim3(256), 0, s, ranges, n_tiles, total,
                        capacity, pairs, vals, mo);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;

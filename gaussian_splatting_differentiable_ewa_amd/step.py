@@ -159,13 +159,14 @@ class Buffers:
         scale = 1.0 / (3.0 * self.H * self.W * self.V)
         L.gs_loss_l1(self.image, target, self.image.numel(), scale, self.dL, self.loss)
 
-    def rasterize_loss_l1(self, target, bg=(0.0, 0.0, 0.0), image: bool = False):
-        """Forward raster and L1 loss in one pass; the image is written only
-        when asked for."""
+    def rasterize_loss_l1(self, target, bg=(0.0, 0.0, 0.0), image: bool = False, row0: int = 0,
+                          rows: Optional[int] = None, accumulate: bool = False):
+        """Forward raster and L1 loss in one pass (over a window of tile rows
+        when given); the image is written only when asked for."""
         scale = 1.0 / (3.0 * self.H * self.W * self.V)
         L.gs_rasterize_fwd_l1(self.rec, self.n, self.ranges, self.sorted_vals, self.masks, self.cams, bg, target, scale,
                               self.image if image else None, self.T_final, self.n_contrib, self.dL, self.loss,
-                              self.fwd_l1_ws)
+                              self.fwd_l1_ws, accumulate=accumulate, row0=row0, rows=rows)
 
     def backward(self, params, grad, bg=(0.0, 0.0, 0.0)):
         L.gs_rasterize_bwd(self.rec, self.n, self.ranges, self.sorted_vals, self.masks, self.cams, bg, self.T_final,
@@ -198,7 +199,7 @@ class TrainStep:
     def __init__(self, params: torch.Tensor, sh_degree: int, cams: Sequence, target: torch.Tensor,
                  lr=1e-3, betas=(0.9, 0.999), eps=1e-15, bg=(0.0, 0.0, 0.0),
                  m: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None, defer_count: bool = True,
-                 fused_adam: bool = True, write_image: bool = False):
+                 fused_adam: bool = True, write_image: bool = False, band_rows: Optional[int] = None):
         assert params.is_cuda and params.dtype == torch.float32 and params.is_contiguous()
         self.params = params
         self.sh_degree = sh_degree
@@ -221,6 +222,11 @@ class TrainStep:
         self.t = 0
         self.defer_count = defer_count
         self.fused_adam = fused_adam
+        self.band_rows = band_rows
+        if band_rows is not None:
+            if band_rows < 1:
+                raise ValueError("band_rows must be positive")
+            self.buf.lists, self.buf.path = "binned", "binned"
         self.write_image = write_image
         dev = params.device
         self.sticky = torch.zeros(1, dtype=torch.int32, device=dev)  # an unverified step overflowed
@@ -234,7 +240,39 @@ class TrainStep:
     def stage_names(self):
         """The stages that ``step(marks)`` brackets, in order."""
         tail = ["preprocess_bwd_adam"] if self.fused_adam else ["preprocess_bwd", "adam"]
+        if self.band_rows is not None:
+            return ["preprocess", "grad2d_zero", "bands"] + tail
         return ["preprocess", "intersections", "tile_masks", "raster_fwd_loss", "grad2d_zero", "raster_bwd"] + tail
+
+    def _bands(self, mark):
+        """The image in windows of band_rows tile rows: each window's lists
+        (list buffers sized for the largest window), forward + loss and
+        backward raster, 2D gradients and loss summed over the windows. The
+        capacity is checked after each window's lists (a read of the overflow
+        flag) and doubled, and the window redone, when they did not fit."""
+        b = self.buf
+        mark(0)
+        b.preprocess(self.params)
+        mark(1)
+        b.grad2d.zero_()
+        mark(2)
+        if b.capacity == 0:
+            nb = -(-b.TY // self.band_rows)
+            b.ensure_capacity(max(2 * int(b.total.item()) // nb, 1 << 16))
+        for i, row0 in enumerate(range(0, b.TY, self.band_rows)):
+            rows = min(self.band_rows, b.TY - row0)
+            while True:
+                L.gs_tile_lists(b.rec, b.rect, b.n, b.V, b.W, b.H, b.vals, b.capacity, b.ranges, b.overflow, b.tl_ws,
+                                masks=b.masks, row0=row0, rows=rows)
+                if int(b.overflow.item()) == 0:
+                    break
+                b.ensure_capacity(2 * b.capacity, slack=1.0)
+            b.rasterize_loss_l1(self.target, self.bg, image=self.write_image, row0=row0, rows=rows,
+                                accumulate=i > 0)
+            L.gs_rasterize_bwd(b.rec, b.n, b.ranges, b.sorted_vals, b.masks, b.cams, self.bg, b.T_final, b.n_contrib,
+                               b.dL, b.grad2d, accumulate=True, row0=row0, rows=rows)
+        b.K = int(b.total.item())
+        mark(3)
 
     def step(self, marks=None):
         """One step. `marks`, if given, holds len(stage_names) + 1 events,
@@ -242,26 +280,31 @@ class TrainStep:
         b = self.buf
         self._settle(block=len(self._pending) >= self.RING - 1)
         mark = (lambda i: marks[i].record()) if marks is not None else (lambda i: None)
-        deferred = self.defer_count and b.lists_without_count()
+        deferred = self.defer_count and b.lists_without_count() and self.band_rows is None
         self.t += 1
-        mark(0)
-        b.preprocess(self.params)
-        mark(1)
-        b.build_lists(read_count=not deferred)
-        if deferred:
-            torch.maximum(self.sticky, b.overflow, out=self.sticky)
-        mark(2)
-        b.tile_masks()
-        mark(3)
-        b.rasterize_loss_l1(self.target, self.bg, image=self.write_image)
-        mark(4)
-        # the 2D-gradient buffer is cleared on its own (a launch of its own,
-        # so that a timing mark can bracket the backward raster alone)
-        b.grad2d.zero_()
-        mark(5)
-        L.gs_rasterize_bwd(b.rec, b.n, b.ranges, b.sorted_vals, b.masks, b.cams, self.bg, b.T_final, b.n_contrib, b.dL,
-                           b.grad2d, accumulate=True)
-        mark(6)
+        if self.band_rows is not None:
+            self._bands(mark)
+            m0 = 4
+        else:
+            mark(0)
+            b.preprocess(self.params)
+            mark(1)
+            b.build_lists(read_count=not deferred)
+            if deferred:
+                torch.maximum(self.sticky, b.overflow, out=self.sticky)
+            mark(2)
+            b.tile_masks()
+            mark(3)
+            b.rasterize_loss_l1(self.target, self.bg, image=self.write_image)
+            mark(4)
+            # the 2D-gradient buffer is cleared on its own (a launch of its own,
+            # so that a timing mark can bracket the backward raster alone)
+            b.grad2d.zero_()
+            mark(5)
+            L.gs_rasterize_bwd(b.rec, b.n, b.ranges, b.sorted_vals, b.masks, b.cams, self.bg, b.T_final, b.n_contrib,
+                               b.dL, b.grad2d, accumulate=True)
+            mark(6)
+            m0 = 7
         skip = self.sticky if deferred else None
         if self._use_state is None:
             r = b.rect.view(b.V, b.n, 4).view(torch.int16)
@@ -273,7 +316,7 @@ class TrainStep:
                                      state=self.adam_state if self._use_state else None)
         else:
             L.gs_preprocess_bwd(self.params, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, self.grad)
-            mark(7)
+            mark(m0)
             args = (self.params, self.grad, self.m, self.v, self.params.numel(), self.lr, self.betas[0],
                     self.betas[1], self.eps, self.t)
             if deferred:

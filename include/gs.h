@@ -208,23 +208,29 @@ size_t gs_tile_lists_workspace_bytes(int64_t n, int32_t n_views, int32_t width, 
  * chunk of Gaussians), scanning the counts into ranges, filling every tile's
  * slots and sorting each tile's slots by (depth, Gaussian index) on its own.
  *   rec, rect, n, n_views, width, height   as for gs_emit_intersections
+ *   row0, rows the window of tile rows [row0, row0 + rows) the lists cover
+ *              (0 and gs_tiles_y(height) for the whole image): only
+ *              intersections with its tiles are listed, so that an image can
+ *              be processed band by band with list buffers sized for a band
  *   vals       device out [capacity]: Gaussian ids, tile by tile, front to back
  *   masks      device out [capacity] uint16, or NULL: each entry's sub-block
  *              mask, exactly as gs_tile_masks computes it (written with the
  *              entry's id by the per-tile sorts)
  *   capacity   slots in vals and masks (>= the total of gs_preprocess; < 2^32)
- *   ranges     device out [n_views * tiles][2]: [start, end), (0, 0) if empty
+ *   ranges     device out [n_views * tiles_x * rows][2]: [start, end), (0, 0)
+ *              if empty, tiles of the window in row-major order per view
  *   overflow   device int32: cleared, then set to 1 if the intersections
  *              exceed capacity (the lists are then incomplete, and the ranges
  *              are cut at capacity so that their readers stay in bounds)
  *   ws         device workspace of gs_tile_lists_workspace_bytes(...)
- * Errors: as gs_emit_intersections, plus a small workspace, capacity >= 2^32
+ * Errors: as gs_emit_intersections, plus a small workspace, capacity >= 2^32,
+ * a window outside the tile rows
  * or more than 8192 tile columns.
  */
 gs_status gs_tile_lists(const float* rec, const uint16_t* rect, int64_t n, int32_t n_views,
-                        int32_t width, int32_t height, uint32_t* vals, uint16_t* masks,
-                        uint64_t capacity, uint32_t* ranges, int32_t* overflow, void* ws,
-                        size_t ws_bytes, void* stream);
+                        int32_t width, int32_t height, int32_t row0, int32_t rows, uint32_t* vals,
+                        uint16_t* masks, uint64_t capacity, uint32_t* ranges, int32_t* overflow,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /*
  * gs_tile_ranges -- for every (view, tile) id t = key >> 32, the range
@@ -274,12 +280,16 @@ gs_status gs_tile_masks(const float* rec, int64_t n, const uint32_t* ranges, con
  *   n_contrib out [V][H][W] int32: 1-based list position of the last blended
  *             entry, 0 if none
  *   masks     the lists' sub-block masks of gs_tile_masks
+ *   row0, rows the window of tile rows the lists and ranges cover (as
+ *             gs_tile_lists; 0 and gs_tiles_y(height) for the whole image):
+ *             only the window's pixels are written
  *   bg        host float[3]
- * Errors: null pointers, bad view count, views of different sizes.
+ * Errors: null pointers, bad view count, views of different sizes, a window
+ * outside the tile rows.
  */
 gs_status gs_rasterize_fwd(const float* rec, int64_t n, const uint32_t* ranges,
                            const uint32_t* vals, const uint16_t* masks, const gs_camera* cams,
-                           int32_t n_views,
+                           int32_t n_views, int32_t row0, int32_t rows,
                            const float* bg, float* image, float* T_final, int32_t* n_contrib,
                            void* stream);
 
@@ -316,7 +326,7 @@ size_t gs_rasterize_fwd_l1_workspace_bytes(int32_t n_views, int32_t width, int32
  */
 gs_status gs_rasterize_fwd_l1(const float* rec, int64_t n, const uint32_t* ranges,
                               const uint32_t* vals, const uint16_t* masks, const gs_camera* cams,
-                              int32_t n_views,
+                              int32_t n_views, int32_t row0, int32_t rows,
                               const float* bg, const float* target, float scale, float* image,
                               float* T_final, int32_t* n_contrib, float* dL_dimage, double* loss,
                               int32_t accumulate, void* ws, size_t ws_bytes, void* stream);
@@ -333,7 +343,7 @@ gs_status gs_rasterize_fwd_l1(const float* rec, int64_t n, const uint32_t* range
  */
 gs_status gs_rasterize_bwd(const float* rec, int64_t n, const uint32_t* ranges,
                            const uint32_t* vals, const uint16_t* masks, const gs_camera* cams,
-                           int32_t n_views,
+                           int32_t n_views, int32_t row0, int32_t rows,
                            const float* bg, const float* T_final, const int32_t* n_contrib,
                            const float* dL_dimage, float* grad2d, int32_t accumulate,
                            void* stream);

@@ -90,17 +90,17 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert alt.value == 0
     # gs_tile_lists
     big = ctypes.c_size_t(1 << 40)
-    assert lib.gs_tile_lists(fake, fake, -1, 1, 256, 256, fake, None, 10, fake, fake, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, 10, 0, 256, 256, fake, None, 10, fake, fake, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 0, fake, None, 10, fake, fake, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, fake, None, 10, None, fake, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, fake, None, 10, fake, None, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, None, None, 10, fake, fake, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, fake, None, 1 << 32, fake, fake, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, -1, 1, 256, 256, 0, 16, fake, None, 10, fake, fake, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, 10, 0, 256, 256, 0, 16, fake, None, 10, fake, fake, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 0, 0, 16, fake, None, 10, fake, fake, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, 0, 16, fake, None, 10, None, fake, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, 0, 16, fake, None, 10, fake, None, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, 0, 16, None, None, 10, fake, fake, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, 0, 16, fake, None, 1 << 32, fake, fake, fake, big, None) == INV
     need = L.tile_lists_workspace_bytes(10, 1, 256, 256, 10)
     assert need > 0 and L.tile_lists_workspace_bytes(10, 0, 256, 256, 10) == 0
     assert L.tile_lists_workspace_bytes(10, 1, 16 * 8193, 256, 10) == 0
-    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, fake, None, 10, fake, fake, fake, need - 1, None) == INV
+    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, 0, 16, fake, None, 10, fake, fake, fake, need - 1, None) == INV
     # gs_tile_ranges
     assert lib.gs_tile_ranges(fake, 10, -1, fake, None) == INV
     assert lib.gs_tile_ranges(None, 10, 4, fake, None) == INV
@@ -109,20 +109,26 @@ def test_invalid_arguments_rejected_on_host(lib):
     qws = L.rasterize_fwd_l1_workspace_bytes(1, 256, 256)
     assert qws == 16 * 16 * 4 * 8 and L.rasterize_fwd_l1_workspace_bytes(0, 256, 256) == 0
     f1 = lib.gs_rasterize_fwd_l1
-    assert f1(fake, 10, fake, fake, fake, cams, 1, bg, None, 1.0, None, fake, fake, fake, fake, 0, fake, qws, None) == INV
-    assert f1(fake, 10, fake, fake, fake, cams, 1, bg, fake, 1.0, None, fake, fake, None, fake, 0, fake, qws, None) == INV
-    assert f1(fake, 10, fake, fake, fake, cams, 1, bg, fake, 1.0, None, fake, fake, fake, None, 0, fake, qws, None) == INV
-    assert f1(fake, 10, fake, fake, fake, cams, 1, bg, fake, 1.0, None, fake, fake, fake, fake, 0, fake, qws - 8,
+    assert f1(fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, None, 1.0, None, fake, fake, fake, fake, 0, fake, qws, None) == INV
+    assert f1(fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, fake, 1.0, None, fake, fake, None, fake, 0, fake, qws, None) == INV
+    assert f1(fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, fake, 1.0, None, fake, fake, fake, None, 0, fake, qws, None) == INV
+    assert f1(fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, fake, 1.0, None, fake, fake, fake, fake, 0, fake,
+              qws - 8, None) == INV
+    # windows of tile rows outside the 16 rows of a 256-pixel image
+    assert f1(fake, 10, fake, fake, fake, cams, 1, 8, 9, bg, fake, 1.0, None, fake, fake, fake, fake, 0, fake, qws,
               None) == INV
-    assert f1(fake, 10, fake, fake, fake, cams, 1, bg, fake, 1.0, None, fake, fake, fake, fake, 0, None, qws, None) == INV
-    assert f1(fake, 10, fake, fake, None, cams, 1, bg, fake, 1.0, None, fake, fake, fake, fake, 0, fake, qws, None) == INV
-    assert lib.gs_rasterize_fwd(fake, 10, fake, fake, fake, cams, 1, None, fake, fake, fake, None) == INV
-    assert lib.gs_rasterize_fwd(fake, 10, fake, fake, fake, cams, 1, bg, None, fake, fake, None) == INV
-    assert lib.gs_rasterize_fwd(fake, -5, fake, fake, fake, cams, 1, bg, fake, fake, fake, None) == INV
-    assert lib.gs_rasterize_fwd(fake, 10, fake, fake, None, cams, 1, bg, fake, fake, fake, None) == INV  # no masks
-    assert lib.gs_rasterize_bwd(fake, 10, fake, fake, fake, cams, 1, bg, fake, fake, None, fake, 0, None) == INV
-    assert lib.gs_rasterize_bwd(fake, 10, fake, fake, fake, cams, 0, bg, fake, fake, fake, fake, 0, None) == INV
-    assert lib.gs_rasterize_bwd(fake, 10, fake, fake, None, cams, 1, bg, fake, fake, fake, fake, 0, None) == INV
+    assert lib.gs_rasterize_fwd(fake, 10, fake, fake, fake, cams, 1, 0, 0, bg, fake, fake, fake, None) == INV
+    assert lib.gs_rasterize_bwd(fake, 10, fake, fake, fake, cams, 1, -1, 4, bg, fake, fake, fake, fake, 0, None) == INV
+    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, 12, 5, fake, None, 10, fake, fake, fake, big, None) == INV
+    assert f1(fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, fake, 1.0, None, fake, fake, fake, fake, 0, None, qws, None) == INV
+    assert f1(fake, 10, fake, fake, None, cams, 1, 0, 16, bg, fake, 1.0, None, fake, fake, fake, fake, 0, fake, qws, None) == INV
+    assert lib.gs_rasterize_fwd(fake, 10, fake, fake, fake, cams, 1, 0, 16, None, fake, fake, fake, None) == INV
+    assert lib.gs_rasterize_fwd(fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, None, fake, fake, None) == INV
+    assert lib.gs_rasterize_fwd(fake, -5, fake, fake, fake, cams, 1, 0, 16, bg, fake, fake, fake, None) == INV
+    assert lib.gs_rasterize_fwd(fake, 10, fake, fake, None, cams, 1, 0, 16, bg, fake, fake, fake, None) == INV  # no masks
+    assert lib.gs_rasterize_bwd(fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, fake, fake, None, fake, 0, None) == INV
+    assert lib.gs_rasterize_bwd(fake, 10, fake, fake, fake, cams, 0, 0, 16, bg, fake, fake, fake, fake, 0, None) == INV
+    assert lib.gs_rasterize_bwd(fake, 10, fake, fake, None, cams, 1, 0, 16, bg, fake, fake, fake, fake, 0, None) == INV
     # tile masks
     mws = L.tile_masks_workspace_bytes(100)
     assert mws == 400

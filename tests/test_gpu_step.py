@@ -60,3 +60,38 @@ def test_deferred_count_redoes_overflowing_steps():
     ts.flush()
     assert (ts.t - t0) + (ts.redone - r0) == 2
     assert ts.redone > r0 and int(ts.sticky.item()) == 0 and b.capacity >= b.K > 16
+
+
+@pytest.mark.parametrize("band_rows", [8, 13])
+def test_bands_equal_whole_image(band_rows):
+    """The memory-capped mode (lists built and rasterized one window of tile
+    rows at a time, 2D gradients and loss summed over the windows) gives the
+    image, T_final and n_contrib of the whole-image step bit for bit, and the
+    same loss and 2D gradients up to summation order; its list buffers are
+    sized for a window."""
+    import torch
+    dev = torch.device("cuda:0")
+    cfg = S.CONFIGS[1]  # 1280x720: 45 tile rows, the last window ragged
+    cams = cfg.cameras()
+    p = torch.from_numpy(S.make_params(cfg)).to(dev)
+    target = render(torch.from_numpy(S.make_target_params(cfg)).to(dev), cfg.sh_degree, cams).clone()
+    kw = dict(lr=cfg.lr, betas=(cfg.beta1, cfg.beta2), eps=cfg.eps, write_image=True)
+    whole = TrainStep(p.clone(), cfg.sh_degree, cams, target, **kw)
+    banded = TrainStep(p.clone(), cfg.sh_degree, cams, target, band_rows=band_rows, **kw)
+    whole.step()
+    banded.step()
+    whole.flush()
+    banded.flush()
+    torch.cuda.synchronize()
+    a, b = whole.buf, banded.buf
+    assert torch.equal(a.image, b.image)
+    assert torch.equal(a.T_final, b.T_final)
+    assert torch.equal(a.n_contrib, b.n_contrib)
+    assert torch.equal(a.dL, b.dL)
+    la, lb = float(a.loss.item()), float(b.loss.item())
+    assert abs(la - lb) <= 1e-12 * abs(la)
+    ga, gb = a.grad2d.double(), b.grad2d.double()
+    scale = ga.abs().max()
+    assert torch.all((ga - gb).abs() <= 1e-4 * ga.abs() + 1e-7 * scale)
+    assert b.capacity < a.capacity
+    print({"band_rows": band_rows, "whole_slots": a.capacity, "window_slots": b.capacity})
