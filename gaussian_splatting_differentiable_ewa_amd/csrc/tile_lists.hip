@@ -223,6 +223,37 @@ __device__ __forceinline__ void write_mask(const MaskOut& mo, int64_t tile_lin, 
     mo.masks[pos] = (uint16_t)tile_mask16(E, tx * 16, ty * 16, mo.W, mo.H);
 }
 
+// The ids of a sorted tile and, when wanted, their masks: positions first,
+// first + stride, ... of the tile, four at a time so that the id reads and
+// then the record gathers of four entries are in flight together.
+template <uint32_t STRIDE, typename IdAt>
+__device__ __forceinline__ void write_ids_masks(const MaskOut& mo, int64_t tile_lin, uint32_t start, uint32_t n,
+                                                uint32_t first, IdAt id_at, uint32_t* __restrict__ vals)
+{
+    const int64_t view = tile_lin / mo.T;
+    const int tile = (int)(tile_lin - view * mo.T);
+    const int wy = tile / mo.TX, tx = tile - wy * mo.TX, ty = wy + mo.row0;
+    const float* rv = mo.rec + view * mo.n * GS_REC_FLOATS;
+    for (uint32_t i0 = first; i0 < n; i0 += 4 * STRIDE) {
+        Entry E[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t i = i0 + (uint32_t)k * STRIDE;
+            E[k].valid = i < n;
+            E[k].gid = E[k].valid ? id_at(i) : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (E[k].valid) vals[start + i0 + (uint32_t)k * STRIDE] = E[k].gid;
+        if (!mo.masks) continue;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) gather_record(E[k], rv);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (E[k].valid) mo.masks[start + i0 + (uint32_t)k * STRIDE] = (uint16_t)tile_mask16(E[k], tx * 16, ty * 16, mo.W, mo.H);
+    }
+}
+
 // Tiles of up to 64 entries, one wave each: a bitonic sort of the 64-bit
 // values (depth bits << 32 | id) across the lanes (absent lanes hold the
 // largest value and sort last).
@@ -451,11 +482,7 @@ __global__ __launch_bounds__(256) void k_tl_sort_wave(const uint32_t* __restrict
             }
     }
     asm volatile("" ::: "memory");
-    for (uint32_t i = lane; i < n; i += 64) {
-        const uint32_t id = tp[si[i]].y;
-        vals[start + i] = id;
-        write_mask(mo, tile, start + i, id);
-    }
+    write_ids_masks<64u>(mo, tile, start, n, lane, [&](uint32_t i) { return tp[si[i]].y; }, vals);
 }
 
 __global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restrict__ ranges,
@@ -555,11 +582,8 @@ __global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restri
             [&](uint32_t i, uint32_t a) { return tp[s_idx[i]].y < tp[s_idx[a]].y; },
             [&](uint32_t i, uint32_t a) { const uint16_t x = s_idx[i]; s_idx[i] = s_idx[a]; s_idx[a] = x; });
         __syncthreads();
-        for (uint32_t i = t; i < n; i += TL_THREADS) {
-            const uint32_t id = tp[s_idx[i]].y;
-            vals[start + i] = id;
-            write_mask(mo, blockIdx.x, start + i, id);
-        }
+        write_ids_masks<(uint32_t)TL_THREADS>(mo, blockIdx.x, start, n, t, [&](uint32_t i) { return tp[s_idx[i]].y; },
+                                              vals);
         return;
     }
 
@@ -645,11 +669,7 @@ __global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restri
         [&](uint32_t i, uint32_t a) { return src[i].y < src[a].y; },
         [&](uint32_t i, uint32_t a) { const uint32_t x = src[i].y; src[i].y = src[a].y; src[a].y = x; });
     __syncthreads();
-    for (uint32_t i = t; i < n; i += TL_THREADS) {
-        const uint32_t id = src[i].y;
-        vals[start + i] = id;
-        write_mask(mo, blockIdx.x, start + i, id);
-    }
+    write_ids_masks<(uint32_t)TL_THREADS>(mo, blockIdx.x, start, n, t, [&](uint32_t i) { return src[i].y; }, vals);
 }
 
 // workspace: table [V][chunks][T] | totals [V T + 1] | total (u64) | scan
