@@ -41,9 +41,11 @@ METRIC = "fwd+bwd+Adam iters/s & Mpix/s, 1M Gaussians SH3 @1080p; % of HBM roofl
 CSRC = os.path.join(ROOT, "gaussian_splatting_differentiable_ewa_amd", "csrc")
 # sources each kernel is built from (a change voids its stored traffic counts)
 KERNEL_SOURCES = {
-    "k_raster_bwd": ["raster_bwd.hip", "raster_common.h", "internal.h", "common.h"],
-    "k_raster_fwd": ["raster_fwd.hip", "raster_common.h", "internal.h", "common.h"],
-    "k_raster_fwd_l1": ["raster_fwd.hip", "raster_common.h", "internal.h", "common.h"],
+    "k_raster_bwd": ["raster_bwd.hip", "raster_bwd.h", "raster_common.h", "internal.h", "common.h"],
+    "k_raster_fwd": ["raster_fwd.hip", "raster_fwd.h", "raster_common.h", "internal.h", "common.h"],
+    "k_raster_fwd_l1": ["raster_fwd.hip", "raster_fwd.h", "raster_common.h", "internal.h", "common.h"],
+    "k_raster_fwd_bwd_l1": ["raster_fused.hip", "raster_fwd.h", "raster_bwd.h", "raster_common.h", "internal.h",
+                            "common.h"],
     "k_adam": ["optim.hip", "adam.h", "internal.h", "common.h"],
     "k_preprocess_bwd": ["preprocess_bwd.hip", "adam.h", "project.h", "internal.h", "common.h"],
     "k_tile_masks": ["tile_masks.hip", "raster_common.h", "internal.h", "common.h"],
@@ -90,6 +92,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="scene id (2 = the headline workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-raster", action="store_true",
+                    help="forward + loss and backward raster as two passes instead of the fused one")
     ap.add_argument("--band-rows", type=int, default=None,
                     help="memory-capped mode: lists and raster one window of this many tile rows at a time")
     ap.add_argument("--cpu-sample-views", type=int, default=1,
@@ -121,6 +125,9 @@ def stage_bytes(P, n, V, K, n_vis_per_view, n_any, n_px):
         # per visible pair, target read, T_final + n_contrib + dL/dimage written
         "raster_fwd_loss": 6 * K + 36 * Nv + 32 * V * n_px,
         "raster_bwd": 6 * K + 36 * Nv + 32 * V * n_px + 36 * Nv * 2,
+        # the two raster passes and the loss in one: ids and masks, one record
+        # read per visible pair, target read, 2D gradients zeroed and written
+        "raster_fwd_bwd": 6 * K + 36 * Nv + 12 * V * n_px + 36 * Nv * 2,
         "preprocess_bwd": Bp * n_any + 44 * Nv + Bp * n,
         "adam": 7 * Bp * n,
         # the two above in one pass: parameters read once, every (view,
@@ -157,7 +164,7 @@ def main():
     params = torch.from_numpy(params_np).to(dev)
     target = render(torch.from_numpy(S.make_target_params(cfg)).to(dev), cfg.sh_degree, cams).clone()
     ts = TrainStep(params.clone(), cfg.sh_degree, cams, target, lr=cfg.lr, betas=(cfg.beta1, cfg.beta2),
-                   eps=cfg.eps, band_rows=args.band_rows)
+                   eps=cfg.eps, band_rows=args.band_rows, fused_raster=not args.separate_raster)
     print(f"[bench] {cfg.name}: inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     b = ts.buf
@@ -192,24 +199,31 @@ def main():
     n_any = int(vis.any(axis=0).sum())
     sb = stage_bytes(b.P, b.n, V, b.K, n_vis, n_any, H * W)
     unused = ["preprocess_bwd", "adam"] if ts.fused_adam else ["preprocess_bwd_adam"]
+    unused += ["raster_fwd_loss", "raster_bwd"] if ts.fused_raster else ["raster_fwd_bwd"]
     step_bytes = sum(v for k, v in sb.items() if k not in unused)
     frac_step = step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9)
 
     # dominant kernel: the single-kernel stage with the largest time
+    if ts.fused_raster:  # the timed steps keep n_contrib on chip: one more pass writes it
+        b.rasterize_fwd_bwd_l1(ts.target, ts.bg, outputs=True)
+        torch.cuda.synchronize()
     pairs = int(b.n_contrib.sum(dtype=torch.int64))  # (pixel, entry) pairs up to each last contributor
     single = {"raster_fwd_loss": "k_raster_fwd_l1", "raster_bwd": "k_raster_bwd", "adam": "k_adam",
-              "preprocess_bwd": "k_preprocess_bwd", "preprocess_bwd_adam": "k_preprocess_bwd"}
+              "preprocess_bwd": "k_preprocess_bwd", "preprocess_bwd_adam": "k_preprocess_bwd",
+              "raster_fwd_bwd": "k_raster_fwd_bwd_l1"}
     single = {k: v for k, v in single.items() if k in stage_ms}
     dom = max(single, key=lambda k: stage_ms[k])
     kern = single[dom]
     dur_s = stage_ms[dom] * 1e-3
     if dom.startswith("raster"):
-        flops = FLOPS_PER_PAIR * pairs
+        # the fused pass evaluates every pair twice (forward, then backward)
+        per_pair = FLOPS_PER_PAIR * (2 if dom == "raster_fwd_bwd" else 1)
+        flops = per_pair * pairs
         achieved = flops / dur_s / 1e12
         roofline = {"bound": "alu", "kernel": kern, "achieved": round(achieved, 3), "peak": FP32_FMA_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / FP32_FMA_PEAK_TFLOPS, 4),
                     "traffic": stored_traffic(cfg.name, kern), "algorithmic_flops": flops,
-                    "pairs": pairs, "flops_per_pair": FLOPS_PER_PAIR, "algorithmic_bytes": int(sb[dom]),
+                    "pairs": pairs, "flops_per_pair": per_pair, "algorithmic_bytes": int(sb[dom]),
                     "hbm_gbs_algorithmic": round(sb[dom] / dur_s / 1e9, 1)}
     else:
         achieved = sb[dom] / dur_s / 1e9
@@ -236,7 +250,7 @@ def main():
         "mpix_per_s": round(mpix, 2),
         "step_hbm_fraction": round(frac_step, 4), "step_algorithmic_bytes": int(step_bytes),
         "intersections": b.K, "k_per_gaussian": round(b.K / b.n, 4), "list_builder": b.path,
-        "band_rows": args.band_rows,
+        "band_rows": args.band_rows, "raster": "separate" if args.separate_raster else "fused",
         "host_count_read": not ts.defer_count or not b.lists_without_count(), "redone_steps": redone,
         "visible_per_view": n_vis,
         "max_per_tile": max_per_tile, "peak_intersection_bytes": int(peak_list_bytes),

@@ -30,8 +30,8 @@ EXPORTS = (
     "gs_tile_lists_workspace_bytes", "gs_rasterize_fwd_l1_workspace_bytes",
     "gs_preprocess", "gs_emit_intersections", "gs_sort_keys", "gs_tile_lists", "gs_tile_ranges", "gs_tile_masks",
     "gs_tile_masks_workspace_bytes",
-    "gs_rasterize_fwd", "gs_rasterize_fwd_l1", "gs_loss_l1", "gs_rasterize_bwd", "gs_preprocess_bwd",
-    "gs_adam_step", "gs_adam_step_unless", "gs_preprocess_bwd_adam",
+    "gs_rasterize_fwd", "gs_rasterize_fwd_l1", "gs_loss_l1", "gs_rasterize_bwd", "gs_rasterize_fwd_bwd_l1",
+    "gs_preprocess_bwd", "gs_adam_step", "gs_adam_step_unless", "gs_preprocess_bwd_adam",
 )
 
 
@@ -85,6 +85,8 @@ def lib():
             "gs_rasterize_fwd_l1": ([_P, _I64, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _F32, _P, _P, _P, _P, _P,
                                      _I32, _P, _SZ, _P], ctypes.c_int),
             "gs_loss_l1": ([_P, _P, _I64, _F32, _P, _P, _I32, _P], ctypes.c_int),
+            "gs_rasterize_fwd_bwd_l1": ([_P, _I64, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _F32, _P, _P, _P, _P,
+                                         _P, _P, _I32, _P, _SZ, _P], ctypes.c_int),
             "gs_rasterize_bwd": ([_P, _I64, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _I32, _P],
                                  ctypes.c_int),
             "gs_preprocess_bwd": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P], ctypes.c_int),
@@ -251,6 +253,18 @@ def gs_rasterize_bwd(rec, n, ranges, vals, masks, cams, bg, T_final, n_contrib, 
                                   _window(cams[0].height, rows), bgv,
                                   _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimage), _ptr(grad2d),
                                   int(bool(accumulate)), _stream(stream)), "gs_rasterize_bwd")
+
+
+def gs_rasterize_fwd_bwd_l1(rec, n, ranges, vals, masks, cams, bg, target, scale, loss, grad2d, ws, image=None,
+                            T_final=None, n_contrib=None, dL_dimage=None, accumulate=False, row0=0, rows=None,
+                            stream=None):
+    """image, T_final, n_contrib and dL_dimage are optional outputs."""
+    bgv = (ctypes.c_float * 3)(*bg)
+    _check(lib().gs_rasterize_fwd_bwd_l1(_ptr(rec), n, _ptr(ranges), _ptr(vals), _ptr(masks), cameras(cams),
+                                         len(cams), row0, _window(cams[0].height, rows), bgv, _ptr(target), scale,
+                                         _ptr(image), _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimage), _ptr(loss),
+                                         _ptr(grad2d), int(bool(accumulate)), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream(stream)), "gs_rasterize_fwd_bwd_l1")
 
 
 def gs_preprocess_bwd(params, n, sh_degree, cams, rect, grad2d, grad_params, stream=None):

@@ -23,6 +23,11 @@ hipError_t scan_u32(const uint32_t* in, uint32_t* out, uint64_t count, uint64_t*
 // Fill `count` uint32 with `value` (a kernel, so it is safe inside graphs).
 hipError_t fill_u32(uint32_t* dst, uint64_t count, uint32_t value, hipStream_t stream);
 
+// *loss (+)= scale * sum of `count` per-quarter partial sums of |I - I*|
+// (the L1 loss of the raster kernels); zeroed first unless `accumulate`.
+hipError_t loss_from_partials(const double* partial, int64_t count, double scale, double* loss, bool accumulate,
+                              hipStream_t stream);
+
 inline unsigned grid_for(uint64_t items, unsigned per_block)
 {
     return (unsigned)((items + per_block - 1) / per_block);

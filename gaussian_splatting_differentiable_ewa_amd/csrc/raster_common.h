@@ -1,7 +1,7 @@
 // Shared pieces of the forward and backward raster kernels: the work unit
 // (one wavefront per 8x8 quarter of a 16x16 tile), staging of list entries,
 // per-row compaction and the fixed-order per-pair arithmetic. The design is
-// described in raster_fwd.hip.
+// described in raster_fwd.h.
 #pragma once
 
 #include "internal.h"
@@ -68,13 +68,14 @@ __device__ __forceinline__ QuarterCtx quarter_ctx(int W, int H, int TX, int T, i
     return t;
 }
 
-// One list entry on its way from global memory to LDS. An entry is valid
-// when it lies in the list and its sub-block mask meets this quarter; only
-// valid entries are gathered.
+// One list entry on its way from global memory to LDS: its list index (0-based
+// within the tile), Gaussian id and quarter bits; valid when the lane holds an
+// entry of the batch. Only valid entries are gathered.
 struct Entry {
     float4 a, b, c;  // record: (u v A B) (C o r g) (b ex ey z)
     uint32_t gid;
-    uint32_t m4;     // the quarter's 4 bits of the entry's tile mask
+    uint32_t m4;     // the quarter's 4 bits of the entry's tile mask (0 when invalid)
+    int32_t rel;
     bool valid;
 };
 
@@ -86,13 +87,119 @@ __device__ __forceinline__ uint32_t quarter_bits(uint32_t m16, const QuarterCtx&
     return (m & 3u) | ((m >> 2) & 0xcu);
 }
 
-// Id and mask of list position p (when in the list), for this quarter.
-__device__ __forceinline__ void load_entry(Entry& E, bool in_list, uint32_t p, const uint32_t* __restrict__ vals,
-                                           const uint16_t* __restrict__ masks, const QuarterCtx& t)
+// ---- Batches of list entries that meet the quarter
+// A wave reads its tile's list in chunks of 64 positions (one per lane) and
+// keeps only the positions whose mask meets its quarter (about one in four on
+// dense scenes). A batch is the compaction, in list order, of the kept
+// positions of the longest run of whole chunks (one to four) whose kept
+// count fits the 64 lanes, so staged slots are mostly useful ones. The
+// quarter bits of the next four chunks are requested one batch ahead.
+// Ascending walks (DESC = false) cover list indices 0, 1, ...; descending
+// ones (the backward pass) len - 1 down to 0.
+struct ChunkScan {
+    uint32_t m;    // quarter bits of this lane's position in chunks 0..3, chunk c at bits 4c..4c+3
+    int32_t next;  // list index (0-based, within the tile) of lane 0 of chunk 0
+};
+
+// The quarter bits of list index `rel` of the tile's list [base, base + len)
+// (0 outside it), restricted, when `rl` is given, to the rows whose last
+// contributor is at or behind it (1-based position rel + 1 <= rl[r]).
+__device__ __forceinline__ uint32_t index_bits(int32_t rel, int32_t len, uint32_t base,
+                                               const uint16_t* __restrict__ masks, const QuarterCtx& t,
+                                               const int32_t* rl)
 {
-    E.m4 = in_list ? quarter_bits(masks[p], t) : 0u;
-    E.valid = E.m4 != 0u;
-    E.gid = E.valid ? vals[p] : 0u;
+    if (rel < 0 || rel >= len) return 0u;
+    uint32_t m4 = quarter_bits(masks[base + (uint32_t)rel], t);
+    if (rl) {
+        const int32_t pos = rel + 1;
+        m4 &= (pos <= rl[0] ? 1u : 0u) | (pos <= rl[1] ? 2u : 0u) | (pos <= rl[2] ? 4u : 0u) | (pos <= rl[3] ? 8u : 0u);
+    }
+    return m4;
+}
+
+template <bool DESC>
+__device__ __forceinline__ int32_t chunk_index(int32_t next, int c, int lane)
+{
+    return DESC ? next - 64 * c - lane : next + 64 * c + lane;
+}
+
+template <bool DESC>
+__device__ __forceinline__ ChunkScan scan_start(int32_t first, int32_t len, uint32_t base,
+                                                const uint16_t* __restrict__ masks, const QuarterCtx& t,
+                                                const int32_t* rl)
+{
+    ChunkScan S;
+    S.next = first;
+    S.m = 0u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        S.m |= index_bits(chunk_index<DESC>(first, c, t.lane), len, base, masks, t, rl) << (4 * c);
+    return S;
+}
+
+// Whether list positions remain from the scan's first chunk on.
+template <bool DESC>
+__device__ __forceinline__ bool scan_left(const ChunkScan& S, int32_t len)
+{
+    return DESC ? S.next >= 0 : S.next < len;
+}
+
+// The next batch from the scan into E (lane s holds its s-th entry; lanes
+// beyond the batch are invalid), with the Gaussian ids requested; returns the
+// batch size (wave-uniform). `cs` is 128 bytes of LDS scratch, free between
+// the batches' other uses. The scan advances past the chunks taken and
+// requests the quarter bits of those that replace them.
+template <bool DESC>
+__device__ __forceinline__ uint32_t take_batch(ChunkScan& S, Entry& E, int32_t len, uint32_t base,
+                                               const uint32_t* __restrict__ vals,
+                                               const uint16_t* __restrict__ masks, const QuarterCtx& t,
+                                               const int32_t* rl, uint16_t* __restrict__ cs)
+{
+    uint64_t b[4];
+    uint32_t nc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        b[c] = ballot(((S.m >> (4 * c)) & 15u) != 0u);
+        nc[c] = (uint32_t)__popcll(b[c]);
+    }
+    uint32_t j = 1, tot = nc[0];
+    if (tot + nc[1] <= 64u) {
+        tot += nc[1];
+        j = 2;
+        if (tot + nc[2] <= 64u) {
+            tot += nc[2];
+            j = 3;
+            if (tot + nc[3] <= 64u) {
+                tot += nc[3];
+                j = 4;
+            }
+        }
+    }
+    // kept positions to their slots, as (offset in the window << 4) | bits
+    uint32_t off = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        if ((uint32_t)c < j) {
+            const uint32_t mc = (S.m >> (4 * c)) & 15u;
+            if (mc) cs[off + mask_rank(b[c])] = (uint16_t)(((uint32_t)(64 * c + t.lane) << 4) | mc);
+            off += nc[c];
+        }
+    }
+    asm volatile("" ::: "memory");  // scratch writes precede the reads (LDS is in order per wave)
+    const uint32_t e = (uint32_t)t.lane < tot ? (uint32_t)cs[t.lane] : 0u;
+    asm volatile("" ::: "memory");
+    E.valid = (uint32_t)t.lane < tot;
+    E.m4 = e & 15u;
+    E.rel = DESC ? S.next - (int32_t)(e >> 4) : S.next + (int32_t)(e >> 4);
+    E.gid = E.valid ? vals[base + (uint32_t)E.rel] : 0u;
+    // advance past the chunks taken and request the ones that replace them
+    S.m = j == 4u ? 0u : S.m >> (4 * j);
+    S.next = DESC ? S.next - 64 * (int32_t)j : S.next + 64 * (int32_t)j;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        if ((uint32_t)c >= 4u - j)
+            S.m |= index_bits(chunk_index<DESC>(S.next, c, t.lane), len, base, masks, t, rl) << (4 * c);
+    return tot;
 }
 
 // An invalid entry gets a zero record (opacity 0): a kernel may evaluate a
@@ -110,15 +217,12 @@ __device__ __forceinline__ void gather_record(Entry& E, const float* __restrict_
 }
 
 // Stage the lane's entry at slot `s`: (u, v, -A/2, -B) (-C/2, o, r, g)
-// (b, pos, -, -) with pos its 1-based list position (int bits), and its 4
-// sub-block bits for this quarter (0 if invalid).
-__device__ __forceinline__ void stage_entry(const Entry& E, int s, int32_t pos, float4* __restrict__ s_rec,
-                                            uint8_t* __restrict__ s_mask)
+// (b, pos, -, -) with pos its 1-based list position (int bits).
+__device__ __forceinline__ void stage_entry(const Entry& E, int s, float4* __restrict__ s_rec)
 {
     s_rec[3 * s + 0] = make_float4(E.a.x, E.a.y, -0.5f * E.a.z, -E.a.w);
     s_rec[3 * s + 1] = make_float4(-0.5f * E.b.x, E.b.y, E.b.z, E.b.w);
-    s_rec[3 * s + 2] = make_float4(E.c.x, __int_as_float(pos), 0.f, 0.f);
-    s_mask[s] = (uint8_t)(E.valid ? E.m4 : 0u);
+    s_rec[3 * s + 2] = make_float4(E.c.x, __int_as_float(E.rel + 1), 0.f, 0.f);
 }
 
 // The 16-bit mask of a list entry in its tile (tile origin (tx0, ty0)
@@ -223,14 +327,13 @@ __device__ __forceinline__ uint32_t tile_mask16(const Entry& E, int tx0, int ty0
 }
 
 // As stage_entry, with the record in two vectors (u v -A/2 -B) (-C/2 o r g)
-// and blue in its own array.
+// and (blue, pos) in an array of their own.
 __device__ __forceinline__ void stage_entry_pair(const Entry& E, int s, float4* __restrict__ s_rec,
-                                                 float* __restrict__ s_b, uint8_t* __restrict__ s_mask)
+                                                 float2* __restrict__ s_bp)
 {
     s_rec[2 * s + 0] = make_float4(E.a.x, E.a.y, -0.5f * E.a.z, -E.a.w);
     s_rec[2 * s + 1] = make_float4(-0.5f * E.b.x, E.b.y, E.b.z, E.b.w);
-    s_b[s] = E.c.x;
-    s_mask[s] = (uint8_t)(E.valid ? E.m4 : 0u);
+    s_bp[s] = make_float2(E.c.x, __int_as_float(E.rel + 1));
 }
 
 __device__ __forceinline__ float entry_power(const float4& q0, const float4& q1, float px, float py, float& dx,

@@ -1,0 +1,100 @@
+// gs_rasterize_fwd_bwd_l1: forward rasterization, L1 loss and backward
+// rasterization of the ByteSplat abstract in one pass per 8x8 quarter. The L1
+// gradient of a pixel depends on that pixel alone (sign(I - I*)), so the
+// wavefront that blended a quarter's pixels can walk its list back at once
+// with T_final, n_contrib and dL/dimage still in registers: they need not go
+// through device memory, and the list is walked by the same wave twice
+// without a second launch. The forward walk (raster_fwd.h) and the backward
+// walk (raster_bwd.h) share one LDS allocation, used by one after the other.
+#include "raster_bwd.h"
+#include "raster_fwd.h"
+
+namespace gs {
+
+constexpr size_t FUSED_LDS_BYTES = sizeof(FwdLds) > sizeof(BwdLds) ? sizeof(FwdLds) : sizeof(BwdLds);
+
+// image, T_final, n_contrib and dL may each be null (not written).
+__global__ __launch_bounds__(RW_THREADS) void k_raster_fwd_bwd_l1(
+    const float* __restrict__ rec, int64_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ vals,
+    const uint16_t* __restrict__ masks, int W, int H, int TX, int T, int row0, float bg0, float bg1, float bg2,
+    const float* __restrict__ target, float scale, float* __restrict__ image, float* __restrict__ T_final,
+    int32_t* __restrict__ n_contrib, float* __restrict__ dL, double* __restrict__ partial,
+    float* __restrict__ grad2d)
+{
+#pragma clang fp contract(off)
+    __shared__ __align__(16) unsigned char lds[FUSED_LDS_BYTES];
+    const QuarterCtx t = quarter_ctx(W, H, TX, T, row0);
+    if (t.empty) {
+        if (t.lane == 0) partial[blockIdx.x] = 0.0;
+        return;
+    }
+    const int64_t HW = (int64_t)H * W;
+    const int64_t pix = (int64_t)t.j * W + t.i;
+    const int64_t o = (int64_t)t.view * 3 * HW + pix;
+    float tg0 = 0.f, tg1 = 0.f, tg2 = 0.f;
+    if (t.inside) {
+        tg0 = target[o];
+        tg1 = target[o + HW];
+        tg2 = target[o + 2 * HW];
+    }
+    const FwdPixel P = raster_fwd_walk(*reinterpret_cast<FwdLds*>(lds), t, rec, n, ranges, vals, masks);
+    float g0 = 0.f, g1 = 0.f, g2 = 0.f, ad = 0.f;
+    int32_t last = 0;
+    if (t.inside) {
+        const float i0 = P.C0 + P.Tr * bg0, i1 = P.C1 + P.Tr * bg1, i2 = P.C2 + P.Tr * bg2;
+        const float d0 = i0 - tg0, d1 = i1 - tg1, d2 = i2 - tg2;
+        g0 = l1_grad(d0, scale);
+        g1 = l1_grad(d1, scale);
+        g2 = l1_grad(d2, scale);
+        ad = (fabsf(d0) + fabsf(d1)) + fabsf(d2);
+        last = P.last;
+        if (image) {
+            image[o] = i0;
+            image[o + HW] = i1;
+            image[o + 2 * HW] = i2;
+        }
+        if (T_final) T_final[(int64_t)t.view * HW + pix] = P.Tr;
+        if (n_contrib) n_contrib[(int64_t)t.view * HW + pix] = P.last;
+        if (dL) {
+            dL[o] = g0;
+            dL[o + HW] = g1;
+            dL[o + 2 * HW] = g2;
+        }
+    }
+    loss_partial(ad, t.lane, partial);
+    asm volatile("" ::: "memory");  // the forward's LDS reads precede the backward's writes (in order per wave)
+    raster_bwd_walk(*reinterpret_cast<BwdLds*>(lds), t, last, P.Tr, g0, g1, g2, bg0, bg1, bg2, rec, n, ranges, vals,
+                    masks, grad2d);
+}
+
+}  // namespace gs
+
+using namespace gs;
+
+extern "C" {
+
+gs_status gs_rasterize_fwd_bwd_l1(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
+                                  const uint16_t* masks, const gs_camera* cams, int32_t n_views, int32_t row0,
+                                  int32_t rows, const float* bg, const float* target, float scale, float* image,
+                                  float* T_final, int32_t* n_contrib, float* dL_dimage, double* loss, float* grad2d,
+                                  int32_t accumulate, void* ws, size_t ws_bytes, void* stream)
+{
+    RasterArgs a;
+    if (!raster_args(rec, n, ranges, vals, masks, cams, n_views, row0, rows, bg, a)) return GS_ERR_INVALID_ARGUMENT;
+    if (!target || !loss || !ws || (n > 0 && !grad2d)) return GS_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < (size_t)a.n_blocks * sizeof(double)) return GS_ERR_INVALID_ARGUMENT;
+    hipStream_t s = (hipStream_t)stream;
+    if (!accumulate && n > 0) {
+        if (fill_u32((uint32_t*)grad2d, (uint64_t)n_views * GS_GRAD2D_ROWS * (uint64_t)n, 0u, s) != hipSuccess)
+            return GS_ERR_HIP;
+    }
+    double* partial = (double*)ws;
+    hipLaunchKernelGGL(k_raster_fwd_bwd_l1, dim3((unsigned)a.n_blocks), dim3(RW_THREADS), 0, s, rec, n, ranges,
+                       vals, masks, a.dc.width, a.dc.height, a.dc.tiles_x, a.T, a.row0, bg[0], bg[1], bg[2], target,
+                       scale, image, T_final, n_contrib, dL_dimage, partial, grad2d);
+    if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
+    return loss_from_partials(partial, a.n_blocks, (double)scale, loss, accumulate != 0, s) == hipSuccess ? GS_OK
+                                                                                                           : GS_ERR_HIP;
+}
+
+}  // extern "C"

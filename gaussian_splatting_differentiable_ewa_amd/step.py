@@ -168,6 +168,21 @@ class Buffers:
                               self.image if image else None, self.T_final, self.n_contrib, self.dL, self.loss,
                               self.fwd_l1_ws, accumulate=accumulate, row0=row0, rows=rows)
 
+    def rasterize_fwd_bwd_l1(self, target, bg=(0.0, 0.0, 0.0), outputs: bool = False, image: bool = False,
+                             row0: int = 0, rows: Optional[int] = None, accumulate: bool = False):
+        """Forward raster, L1 loss and backward raster in one pass (over a
+        window of tile rows when given): the loss and the 2D gradients (both
+        zeroed first unless `accumulate`); T_final, n_contrib and dL/dimage
+        are written only with `outputs`, the image only with `image`."""
+        scale = 1.0 / (3.0 * self.H * self.W * self.V)
+        L.gs_rasterize_fwd_bwd_l1(self.rec, self.n, self.ranges, self.sorted_vals, self.masks, self.cams, bg, target,
+                                  scale, self.loss, self.grad2d, self.fwd_l1_ws,
+                                  image=self.image if image else None,
+                                  T_final=self.T_final if outputs else None,
+                                  n_contrib=self.n_contrib if outputs else None,
+                                  dL_dimage=self.dL if outputs else None,
+                                  accumulate=accumulate, row0=row0, rows=rows)
+
     def backward(self, params, grad, bg=(0.0, 0.0, 0.0)):
         L.gs_rasterize_bwd(self.rec, self.n, self.ranges, self.sorted_vals, self.masks, self.cams, bg, self.T_final,
                            self.n_contrib, self.dL, self.grad2d)
@@ -192,14 +207,19 @@ class TrainStep:
     backward applies Adam itself (``gs_preprocess_bwd_adam``) and ``grad`` is
     not written; otherwise ``gs_preprocess_bwd`` writes ``grad`` and
     ``gs_adam_step`` follows. ``write_image`` keeps the rendered image in
-    ``buf.image`` (the step itself needs only the loss gradient)."""
+    ``buf.image`` (the step itself needs only the loss gradient). With
+    ``fused_raster`` (the default) forward raster, L1 loss and backward raster
+    run as one pass (``gs_rasterize_fwd_bwd_l1``), which keeps T_final,
+    n_contrib and dL/dimage on chip; otherwise ``gs_rasterize_fwd_l1`` and
+    ``gs_rasterize_bwd`` run one after the other and write them."""
 
     RING = 4  # steps whose count and flag may be in flight
 
     def __init__(self, params: torch.Tensor, sh_degree: int, cams: Sequence, target: torch.Tensor,
                  lr=1e-3, betas=(0.9, 0.999), eps=1e-15, bg=(0.0, 0.0, 0.0),
                  m: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None, defer_count: bool = True,
-                 fused_adam: bool = True, write_image: bool = False, band_rows: Optional[int] = None):
+                 fused_adam: bool = True, write_image: bool = False, band_rows: Optional[int] = None,
+                 fused_raster: bool = True):
         assert params.is_cuda and params.dtype == torch.float32 and params.is_contiguous()
         self.params = params
         self.sh_degree = sh_degree
@@ -222,6 +242,7 @@ class TrainStep:
         self.t = 0
         self.defer_count = defer_count
         self.fused_adam = fused_adam
+        self.fused_raster = fused_raster
         self.band_rows = band_rows
         if band_rows is not None:
             if band_rows < 1:
@@ -242,6 +263,8 @@ class TrainStep:
         tail = ["preprocess_bwd_adam"] if self.fused_adam else ["preprocess_bwd", "adam"]
         if self.band_rows is not None:
             return ["preprocess", "grad2d_zero", "bands"] + tail
+        if self.fused_raster:
+            return ["preprocess", "intersections", "tile_masks", "grad2d_zero", "raster_fwd_bwd"] + tail
         return ["preprocess", "intersections", "tile_masks", "raster_fwd_loss", "grad2d_zero", "raster_bwd"] + tail
 
     def _bands(self, mark):
@@ -255,6 +278,7 @@ class TrainStep:
         b.preprocess(self.params)
         mark(1)
         b.grad2d.zero_()
+        b.loss.zero_()
         mark(2)
         if b.capacity == 0:
             nb = -(-b.TY // self.band_rows)
@@ -267,8 +291,12 @@ class TrainStep:
                 if int(b.overflow.item()) == 0:
                     break
                 b.ensure_capacity(2 * b.capacity, slack=1.0)
+            if self.fused_raster:
+                b.rasterize_fwd_bwd_l1(self.target, self.bg, outputs=self.write_image, image=self.write_image,
+                                       row0=row0, rows=rows, accumulate=True)
+                continue
             b.rasterize_loss_l1(self.target, self.bg, image=self.write_image, row0=row0, rows=rows,
-                                accumulate=i > 0)
+                                accumulate=True)
             L.gs_rasterize_bwd(b.rec, b.n, b.ranges, b.sorted_vals, b.masks, b.cams, self.bg, b.T_final, b.n_contrib,
                                b.dL, b.grad2d, accumulate=True, row0=row0, rows=rows)
         b.K = int(b.total.item())
@@ -295,16 +323,27 @@ class TrainStep:
             mark(2)
             b.tile_masks()
             mark(3)
-            b.rasterize_loss_l1(self.target, self.bg, image=self.write_image)
-            mark(4)
-            # the 2D-gradient buffer is cleared on its own (a launch of its own,
-            # so that a timing mark can bracket the backward raster alone)
-            b.grad2d.zero_()
-            mark(5)
-            L.gs_rasterize_bwd(b.rec, b.n, b.ranges, b.sorted_vals, b.masks, b.cams, self.bg, b.T_final, b.n_contrib,
-                               b.dL, b.grad2d, accumulate=True)
-            mark(6)
-            m0 = 7
+            if self.fused_raster:
+                # 2D gradients and loss cleared by launches of their own, so
+                # that a timing mark brackets the raster pass alone
+                b.grad2d.zero_()
+                b.loss.zero_()
+                mark(4)
+                b.rasterize_fwd_bwd_l1(self.target, self.bg, outputs=self.write_image, image=self.write_image,
+                                       accumulate=True)
+                mark(5)
+                m0 = 6
+            else:
+                b.rasterize_loss_l1(self.target, self.bg, image=self.write_image)
+                mark(4)
+                # the 2D-gradient buffer is cleared on its own (a launch of its
+                # own, so that a timing mark can bracket the backward raster)
+                b.grad2d.zero_()
+                mark(5)
+                L.gs_rasterize_bwd(b.rec, b.n, b.ranges, b.sorted_vals, b.masks, b.cams, self.bg, b.T_final,
+                                   b.n_contrib, b.dL, b.grad2d, accumulate=True)
+                mark(6)
+                m0 = 7
         skip = self.sticky if deferred else None
         if self._use_state is None:
             r = b.rect.view(b.V, b.n, 4).view(torch.int16)

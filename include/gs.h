@@ -14,6 +14,8 @@
  *   gs_loss_l1             L1 loss against target images, dL/dimage
  *   (gs_rasterize_fwd_l1   the two calls above in one pass)
  *   gs_rasterize_bwd       back-to-front gradients to the 2D quantities
+ *   (gs_rasterize_fwd_bwd_l1  gs_rasterize_fwd_l1 and gs_rasterize_bwd in one
+ *                          pass)
  *   gs_preprocess_bwd      gradients to all per-Gaussian parameters
  *   gs_adam_step           fused Adam update
  *   (gs_preprocess_bwd_adam  the two calls above in one pass)
@@ -347,6 +349,35 @@ gs_status gs_rasterize_bwd(const float* rec, int64_t n, const uint32_t* ranges,
                            const float* bg, const float* T_final, const int32_t* n_contrib,
                            const float* dL_dimage, float* grad2d, int32_t accumulate,
                            void* stream);
+
+/*
+ * gs_rasterize_fwd_bwd_l1 -- gs_rasterize_fwd_l1 followed by gs_rasterize_bwd,
+ * in one pass per 8x8 quarter of a tile: forward and backward rasterization of
+ * the ByteSplat abstract with the L1 loss between them (views averaged as for
+ * gs_loss_l1). The L1 gradient of a pixel is a function of that pixel alone,
+ * so each quarter blends its pixels, forms dL/dimage and walks its list back
+ * with T_final, n_contrib and dL/dimage kept on chip. Results equal those of
+ * the two calls (image, T_final, n_contrib, dL/dimage and loss bit for bit;
+ * grad2d up to the order of its floating-point atomic additions).
+ *   target     [V][3][H][W]
+ *   image      out [V][3][H][W], or null (not written)
+ *   T_final    out [V][H][W], or null
+ *   n_contrib  out [V][H][W], or null
+ *   dL_dimage  out [V][3][H][W], or null
+ *   loss       device double: overwritten, or added to when `accumulate`
+ *   grad2d     [V][n][9] fp32 as in gs_rasterize_bwd: zeroed first unless
+ *              `accumulate`
+ *   ws         device workspace of gs_rasterize_fwd_l1_workspace_bytes(...)
+ * Errors: as gs_rasterize_fwd, plus null target / loss / ws / grad2d (n > 0)
+ * or a small workspace.
+ */
+gs_status gs_rasterize_fwd_bwd_l1(const float* rec, int64_t n, const uint32_t* ranges,
+                                  const uint32_t* vals, const uint16_t* masks,
+                                  const gs_camera* cams, int32_t n_views, int32_t row0,
+                                  int32_t rows, const float* bg, const float* target, float scale,
+                                  float* image, float* T_final, int32_t* n_contrib,
+                                  float* dL_dimage, double* loss, float* grad2d,
+                                  int32_t accumulate, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * gs_preprocess_bwd -- chain rule from the 2D gradients to all P parameters

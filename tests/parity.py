@@ -121,6 +121,17 @@ def gpu_forward_l1(b: Buffers, target_np, bg=(0.0, 0.0, 0.0)):
             "loss": float(np_(b.loss)[0])}
 
 
+def gpu_fwd_bwd_l1(b: Buffers, target_np, bg=(0.0, 0.0, 0.0)):
+    """The fused forward + L1 + backward pass on the lists already in `b`,
+    with every optional output written."""
+    dev = b.device
+    tgt = torch.from_numpy(np.ascontiguousarray(target_np, dtype=np.float32)).to(dev)
+    b.rasterize_fwd_bwd_l1(tgt, bg, outputs=True, image=True)
+    torch.cuda.synchronize()
+    return {"image": np_(b.image), "T_final": np_(b.T_final), "n_contrib": np_(b.n_contrib), "dL": np_(b.dL),
+            "loss": float(np_(b.loss)[0]), "grad2d": np_(b.grad2d).reshape(b.V, b.n, L.GS_GRAD2D_ROWS).copy()}
+
+
 def gpu_loss(image_np, target_np):
     dev = torch.device("cuda:0")
     img = torch.from_numpy(np.ascontiguousarray(image_np)).to(dev)

@@ -129,6 +129,24 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert lib.gs_rasterize_bwd(fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, fake, fake, None, fake, 0, None) == INV
     assert lib.gs_rasterize_bwd(fake, 10, fake, fake, fake, cams, 0, 0, 16, bg, fake, fake, fake, fake, 0, None) == INV
     assert lib.gs_rasterize_bwd(fake, 10, fake, fake, None, cams, 1, 0, 16, bg, fake, fake, fake, fake, 0, None) == INV
+    f2 = lib.gs_rasterize_fwd_bwd_l1
+    ok = (fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, fake, 1.0, None, None, None, None, fake, fake, 0, fake, qws,
+          None)
+
+    def fb(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f2(*a)
+
+    assert fb(a10=None) == INV  # target
+    assert fb(a16=None) == INV  # loss
+    assert fb(a17=None) == INV  # grad2d
+    assert fb(a19=None) == INV  # workspace
+    assert fb(a20=qws - 8) == INV
+    assert fb(a4=None) == INV  # masks
+    assert fb(a7=8, a8=9) == INV  # window outside the image
+    assert fb(a6=0) == INV  # no views
     # tile masks
     mws = L.tile_masks_workspace_bytes(100)
     assert mws == 400

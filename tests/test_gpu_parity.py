@@ -110,6 +110,32 @@ def test_backward(run):
     assert st["e2e_within_1e-3_rel_of_significant"] > 0.999
 
 
+def test_fwd_bwd_l1_fused(run):
+    """The fused forward + L1 + backward pass: forward outputs equal the
+    separate forward bit for bit, dL/dimage and the loss equal the oracle's L1
+    on that image, and the 2D gradients match the oracle's backward fed the
+    same dL/dimage. Ambiguous pixels get a target equal to the GPU's own
+    value there, so that their dL/dimage is zero on both sides (the fused pass
+    forms its own)."""
+    gpu, fwd = run["gpu"], run["fwd"]
+    amb = np.broadcast_to((fwd["amb"] != 0)[:, None], gpu["image"].shape)
+    target = np.where(amb, gpu["image"], run["target"]).astype(np.float32)
+    fused = PY.gpu_fwd_bwd_l1(run["buf"], target)
+    for k in ("image", "T_final", "n_contrib"):
+        assert np.array_equal(fused[k], gpu[k]), k
+    loss_o, dL_o = O.loss_l1(gpu["image"], target)
+    assert np.array_equal(fused["dL"], dL_o)
+    assert not fused["dL"][amb].any()
+    assert fused["loss"] == pytest.approx(loss_o, rel=1e-6)
+    g2_ref, gabs = O.render_bwd(run["orc"], run["cams"], dL_o, with_abs=True)
+    st = PY.check_grad2d(fused["grad2d"], g2_ref, gabs)
+    print(st)
+    # and the separate backward on the same inputs: the same sums in another
+    # order of atomic additions
+    g2_sep, _ = PY.gpu_backward(run["buf"], run["gpu"]["params_t"], dL_o)
+    PY.check_grad2d(g2_sep, fused["grad2d"].astype(np.float64), gabs)
+
+
 @pytest.mark.parametrize("step", [1, 3])
 def test_adam(run, step):
     rng = np.random.default_rng(step)

@@ -62,8 +62,9 @@ def test_deferred_count_redoes_overflowing_steps():
     assert ts.redone > r0 and int(ts.sticky.item()) == 0 and b.capacity >= b.K > 16
 
 
+@pytest.mark.parametrize("fused_raster", [True, False], ids=["fused", "separate"])
 @pytest.mark.parametrize("band_rows", [8, 13])
-def test_bands_equal_whole_image(band_rows):
+def test_bands_equal_whole_image(band_rows, fused_raster):
     """The memory-capped mode (lists built and rasterized one window of tile
     rows at a time, 2D gradients and loss summed over the windows) gives the
     image, T_final and n_contrib of the whole-image step bit for bit, and the
@@ -75,7 +76,7 @@ def test_bands_equal_whole_image(band_rows):
     cams = cfg.cameras()
     p = torch.from_numpy(S.make_params(cfg)).to(dev)
     target = render(torch.from_numpy(S.make_target_params(cfg)).to(dev), cfg.sh_degree, cams).clone()
-    kw = dict(lr=cfg.lr, betas=(cfg.beta1, cfg.beta2), eps=cfg.eps, write_image=True)
+    kw = dict(lr=cfg.lr, betas=(cfg.beta1, cfg.beta2), eps=cfg.eps, write_image=True, fused_raster=fused_raster)
     whole = TrainStep(p.clone(), cfg.sh_degree, cams, target, **kw)
     banded = TrainStep(p.clone(), cfg.sh_degree, cams, target, band_rows=band_rows, **kw)
     whole.step()
@@ -95,3 +96,32 @@ def test_bands_equal_whole_image(band_rows):
     assert torch.all((ga - gb).abs() <= 1e-4 * ga.abs() + 1e-7 * scale)
     assert b.capacity < a.capacity
     print({"band_rows": band_rows, "whole_slots": a.capacity, "window_slots": b.capacity})
+
+
+def test_fused_raster_step_equals_separate():
+    """A whole-image step with the fused raster pass and one with the separate
+    forward + loss and backward calls: image, T_final, n_contrib, dL/dimage
+    bit for bit, the loss to rounding and the 2D gradients up to the order of
+    their atomic additions."""
+    import torch
+    dev = torch.device("cuda:0")
+    cfg = S.CONFIGS[1]
+    cams = cfg.cameras()
+    p = torch.from_numpy(S.make_params(cfg)).to(dev)
+    target = render(torch.from_numpy(S.make_target_params(cfg)).to(dev), cfg.sh_degree, cams).clone()
+    kw = dict(lr=cfg.lr, betas=(cfg.beta1, cfg.beta2), eps=cfg.eps, write_image=True)
+    fused = TrainStep(p.clone(), cfg.sh_degree, cams, target, fused_raster=True, **kw)
+    sep = TrainStep(p.clone(), cfg.sh_degree, cams, target, fused_raster=False, **kw)
+    fused.step()
+    sep.step()
+    fused.flush()
+    sep.flush()
+    torch.cuda.synchronize()
+    a, b = fused.buf, sep.buf
+    for k in ("image", "T_final", "n_contrib", "dL"):
+        assert torch.equal(getattr(a, k), getattr(b, k)), k
+    la, lb = float(a.loss.item()), float(b.loss.item())
+    assert abs(la - lb) <= 1e-12 * abs(la)
+    ga, gb = a.grad2d.double(), b.grad2d.double()
+    scale = ga.abs().max()
+    assert torch.all((ga - gb).abs() <= 1e-4 * ga.abs() + 1e-7 * scale)
