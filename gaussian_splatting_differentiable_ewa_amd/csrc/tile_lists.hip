@@ -20,7 +20,8 @@
 //      k_tl_sort      one workgroup per longer tile: stable LSD radix sort by
 //                     the 32 depth bits (8-bit digits; digits equal across the
 //                     tile are skipped), in LDS for up to 4096 entries and
-//                     through a global scratch copy beyond, then runs of equal
+//                     through a global scratch copy beyond (those tiles,
+//                     listed by k_tl_ranges, first), then runs of equal
 //                     depth put in id order.
 // (depth, id) is a total order, so the arbitrary slot order of step 4 never
 // shows: the lists equal those of the global key sort. The positive fp32
@@ -41,6 +42,7 @@ constexpr int TL_CAP = 4096;                    // entries a tile sorts in LDS
 constexpr int TL_ROUNDS = TL_CAP / TL_THREADS;  // rounds of 64 keys per wave, at most
 constexpr int GL_CHUNK = 4096;                  // entries per chunk of the global-memory path
 constexpr int GL_ROUNDS = GL_CHUNK / TL_THREADS;
+constexpr uint32_t TL_MAXBIG = 2048;            // tiles longer than TL_CAP that k_tl_sort takes first
 
 constexpr int BAND_TILES = 8192;  // LDS counters of one band of tile rows
 
@@ -123,9 +125,10 @@ __global__ __launch_bounds__(256) void k_bin_count(const uint16_t* __restrict__ 
 // 64 tiles per workgroup, each wave one quarter of the chunks: quarter sums,
 // then every wave rewrites its quarter as an exclusive prefix
 __global__ __launch_bounds__(256) void k_bin_colscan(uint32_t* __restrict__ table, const BinGrid G, int32_t n_views,
-                                                     uint32_t* __restrict__ totals)
+                                                     uint32_t* __restrict__ totals, uint32_t* __restrict__ big)
 {
     __shared__ uint32_t part[4][64];
+    if (blockIdx.x == 0 && threadIdx.x == 0) big[0] = 0u;  // k_tl_ranges counts the long tiles
     const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
     const int64_t i = (int64_t)blockIdx.x * 64 + lane;
     const bool ok = i < (int64_t)n_views * G.tiles;
@@ -150,14 +153,21 @@ __global__ __launch_bounds__(256) void k_bin_colscan(uint32_t* __restrict__ tabl
 }
 
 // ranges, cut at the capacity: when the lists overflow, readers of the
-// ranges stay inside the filled slots
+// ranges stay inside the filled slots. Tiles longer than the LDS sort holds
+// are listed in big[1 + k] (count in big[0], zeroed by k_bin_colscan), so that
+// k_tl_sort starts them first.
 __global__ __launch_bounds__(256) void k_tl_ranges(const uint32_t* __restrict__ starts, int64_t n_tiles,
-                                                   uint64_t capacity, uint32_t* __restrict__ ranges)
+                                                   uint64_t capacity, uint32_t* __restrict__ ranges,
+                                                   uint32_t* __restrict__ big)
 {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= n_tiles) return;
     const uint32_t s = (uint32_t)min((uint64_t)starts[t], capacity), e = (uint32_t)min((uint64_t)starts[t + 1], capacity);
     *(uint2*)(ranges + 2 * t) = e > s ? make_uint2(s, e) : make_uint2(0u, 0u);
+    if (e > s && e - s > (uint32_t)TL_CAP) {
+        const uint32_t k = atomicAdd(big, 1u);
+        if (k < TL_MAXBIG) big[1 + k] = (uint32_t)t;
+    }
 }
 
 __global__ __launch_bounds__(256) void k_bin_fill(const float* __restrict__ rec, const uint16_t* __restrict__ rect,
@@ -485,22 +495,38 @@ __global__ __launch_bounds__(256) void k_tl_sort_wave(const uint32_t* __restrict
     write_ids_masks<64u>(mo, tile, start, n, lane, [&](uint32_t i) { return tp[si[i]].y; }, vals);
 }
 
+// Launched with TL_MAXBIG + n_tiles workgroups: the first TL_MAXBIG take the
+// listed long tiles (those that sort through global memory and take longest),
+// the others tile blockIdx.x - TL_MAXBIG, unless it is a listed long tile.
+// When more long tiles exist than the list holds, every tile is taken in the
+// second range.
 __global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restrict__ ranges,
                                                         const uint64_t* __restrict__ total_dev, uint64_t capacity,
                                                         uint2* __restrict__ pairs, uint2* __restrict__ alt,
-                                                        uint32_t* __restrict__ vals, const MaskOut mo)
+                                                        uint32_t* __restrict__ vals, const uint32_t* __restrict__ big,
+                                                        const MaskOut mo)
 {
     __shared__ uint32_t s_key[TL_CAP];
     __shared__ uint16_t s_idx[TL_CAP];  // position of each key in the tile's unsorted pairs
     __shared__ uint32_t wcnt[4][256];
     __shared__ uint32_t s_misc[8];
-    const uint2 rg = *(const uint2*)(ranges + 2 * (uint64_t)blockIdx.x);
+    const uint32_t n_big = big[0];
+    const bool listed = n_big <= TL_MAXBIG;  // every long tile is in the list
+    int64_t tile;
+    if (blockIdx.x < TL_MAXBIG) {
+        if (!listed || blockIdx.x >= n_big) return;
+        tile = big[1 + blockIdx.x];
+    } else {
+        tile = (int64_t)blockIdx.x - TL_MAXBIG;
+    }
+    const uint2 rg = *(const uint2*)(ranges + 2 * (uint64_t)tile);
     const uint64_t limit = min(capacity, *total_dev);
     const uint32_t start = rg.x, end = (uint32_t)min((uint64_t)rg.y, limit);
     if (end <= start) return;
     const uint32_t n = end - start;
     const uint32_t t = threadIdx.x, lane = t & 63u, wave = t >> 6;
     if (n <= (uint32_t)WV_CAP) return;  // k_tl_sort_small, k_tl_sort_wave
+    if (blockIdx.x >= TL_MAXBIG && listed && rg.y - rg.x > (uint32_t)TL_CAP) return;  // taken first
     if (n <= (uint32_t)TL_CAP) {
         // wave w holds the contiguous run [w L, (w + 1) L), L = 64 R
         const uint32_t R = (n + TL_THREADS - 1) / TL_THREADS;
@@ -582,54 +608,75 @@ __global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restri
             [&](uint32_t i, uint32_t a) { return tp[s_idx[i]].y < tp[s_idx[a]].y; },
             [&](uint32_t i, uint32_t a) { const uint16_t x = s_idx[i]; s_idx[i] = s_idx[a]; s_idx[a] = x; });
         __syncthreads();
-        write_ids_masks<(uint32_t)TL_THREADS>(mo, blockIdx.x, start, n, t, [&](uint32_t i) { return tp[s_idx[i]].y; },
+        write_ids_masks<(uint32_t)TL_THREADS>(mo, tile, start, n, t, [&](uint32_t i) { return tp[s_idx[i]].y; },
                                               vals);
         return;
     }
 
     // a list longer than the LDS holds: the same passes over global memory,
     // chunk by chunk (chunks in order keep the sort stable), ping-ponging
-    // between the pairs and a scratch copy of the same slots
+    // between the pairs and a scratch copy of the same slots. One read of
+    // the list forms the histograms of all four digits (a digit with one
+    // value across the list is skipped), and each read of a chunk requests
+    // all its items before ranking them.
     uint2* src = pairs + start;
     uint2* dst = alt + start;
-    uint32_t kor = 0u, kand = 0xffffffffu;
-    for (uint32_t i = t; i < n; i += TL_THREADS) {
-        const uint32_t k = src[i].x;
-        kor |= k;
-        kand &= k;
-    }
-    uint32_t o, a;
-    tl_or_and(kor, kand, s_misc, o, a);
-    const uint32_t differ = o ^ a;
-    uint32_t* hist = &wcnt[0][0];        // [256] digit totals of the list
-    uint32_t* running = &wcnt[1][0];     // [256] next free slot of each digit
-    uint32_t(*cw)[256] = (uint32_t(*)[256])s_key;  // [4][256] per-wave counts of a chunk
-    for (int shift = 0; shift < 32; shift += 8) {
-        if (((differ >> shift) & 255u) == 0u) continue;
-        hist[t] = 0u;
-        __syncthreads();
-        for (uint32_t base = 0; base < n; base += TL_THREADS) {
-            const uint32_t i = base + t;
-            const bool valid = i < n;
-            const uint32_t d = valid ? (src[i].x >> shift) & 255u : 0u;
-            const uint64_t peers = tl_peers(d, ballot(valid));
-            if (valid && mask_rank(peers) == 0u) atomicAdd(&hist[d], (uint32_t)__popcll(peers));
+    uint32_t(*hist)[256] = wcnt;                   // [digit position][digit] totals of the list
+    uint32_t(*cw)[256] = (uint32_t(*)[256])s_key;  // [wave][digit] counts of a chunk
+    uint32_t* running = s_key + 4 * 256;           // [256] next free slot of each digit
+#pragma unroll
+    for (int w = 0; w < 4; ++w) hist[w][t] = 0u;
+    if (t == 0) s_misc[4] = 0u;
+    __syncthreads();
+    for (uint32_t base = 0; base < n; base += (uint32_t)GL_CHUNK) {
+        uint32_t k[GL_ROUNDS];
+#pragma unroll
+        for (int r = 0; r < GL_ROUNDS; ++r) {
+            const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
+            k[r] = i < n ? src[i].x : 0u;
         }
-        __syncthreads();
-        running[t] = tl_exclusive_256(hist[t], s_misc);
+#pragma unroll
+        for (int r = 0; r < GL_ROUNDS; ++r) {
+            const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
+            const uint64_t vm = ballot(i < n);
+            if (vm == 0ull) break;  // wave-uniform
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t d = (k[r] >> (8 * p)) & 255u;
+                const uint64_t peers = tl_peers(d, vm);
+                if (i < n && mask_rank(peers) == 0u) atomicAdd(&hist[p][d], (uint32_t)__popcll(peers));
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t c = hist[p][t];
+        if (c != 0u && c != n) atomicOr(&s_misc[4], 1u << p);  // two digits or more at position p
+    }
+    __syncthreads();
+    const uint32_t varies = s_misc[4];
+    for (int p = 0; p < 4; ++p) {
+        if (((varies >> p) & 1u) == 0u) continue;
+        const int shift = 8 * p;
+        running[t] = tl_exclusive_256(hist[p][t], s_misc);
         __syncthreads();
         for (uint32_t base = 0; base < n; base += (uint32_t)GL_CHUNK) {
             // chunk [base, base + 4096): wave w ranks its run of 1024
+            uint2 item[GL_ROUNDS];
+#pragma unroll
+            for (int r = 0; r < GL_ROUNDS; ++r) {
+                const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
+                item[r] = i < n ? src[i] : make_uint2(0u, 0u);
+            }
 #pragma unroll
             for (int w = 0; w < 4; ++w) cw[w][t] = 0u;
             __syncthreads();
-            uint2 item[GL_ROUNDS];
             uint32_t rk[GL_ROUNDS];
 #pragma unroll
             for (int r = 0; r < GL_ROUNDS; ++r) {
                 const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
                 const bool valid = i < n;
-                item[r] = valid ? src[i] : make_uint2(0u, 0u);
                 const uint32_t d = (item[r].x >> shift) & 255u;
                 const uint64_t peers = tl_peers(d, ballot(valid));
                 const uint32_t below = mask_rank(peers);
@@ -664,18 +711,40 @@ __global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restri
         src = dst;
         dst = tmp;
     }
-    tl_fix_ties(
-        n, [&](uint32_t i) { return src[i].x; }, [&](uint32_t i) { return src[i].y; },
-        [&](uint32_t i, uint32_t a) { return src[i].y < src[a].y; },
-        [&](uint32_t i, uint32_t a) { const uint32_t x = src[i].y; src[i].y = src[a].y; src[a].y = x; });
+    // equal depths: order each run's items by Gaussian index (runs are rare
+    // and short; the thread owning a run's first item sorts it), with the
+    // keys around eight items per thread requested together
+    for (uint32_t base = 0; base < n; base += 8u * TL_THREADS) {
+        uint32_t kp[8], kc[8], kn[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint32_t i = base + (uint32_t)u * TL_THREADS + t;
+            kc[u] = i < n ? src[i].x : 0u;
+            kp[u] = i > 0 && i < n ? src[i - 1].x : 0u;
+            kn[u] = i + 1 < n ? src[i + 1].x : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint32_t i = base + (uint32_t)u * TL_THREADS + t;
+            if (i + 1 >= n || kn[u] != kc[u] || (i > 0 && kp[u] == kc[u])) continue;
+            uint32_t j = i + 1;
+            while (j < n && src[j].x == kc[u]) ++j;
+            for (uint32_t x = i + 1; x < j; ++x)
+                for (uint32_t y = x; y > i && src[y].y < src[y - 1].y; --y) {
+                    const uint32_t g = src[y].y;
+                    src[y].y = src[y - 1].y;
+                    src[y - 1].y = g;
+                }
+        }
+    }
     __syncthreads();
-    write_ids_masks<(uint32_t)TL_THREADS>(mo, blockIdx.x, start, n, t, [&](uint32_t i) { return src[i].y; }, vals);
+    write_ids_masks<(uint32_t)TL_THREADS>(mo, tile, start, n, t, [&](uint32_t i) { return src[i].y; }, vals);
 }
 
 // workspace: table [V][chunks][T] | totals [V T + 1] | total (u64) | scan
 // workspace | pairs [capacity] | scratch pairs [capacity]
 struct TlLayout {
-    size_t table, totals, total, scan, pairs, alt, bytes;
+    size_t table, totals, total, scan, big, pairs, alt, bytes;
 };
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -710,7 +779,8 @@ static TlLayout tl_layout(const BinGrid& G, int32_t n_views, uint64_t capacity)
     L.totals = align256(std::max<size_t>((size_t)n_tiles * G.chunks, (size_t)1 << 22) * 4);
     L.total = L.totals + align256((n_tiles + 1) * 4);
     L.scan = L.total + 256;
-    L.pairs = L.scan + align256(scan_workspace_bytes(n_tiles));
+    L.big = L.scan + align256(scan_workspace_bytes(n_tiles));
+    L.pairs = L.big + align256((1 + TL_MAXBIG) * 4);
     L.alt = L.pairs + align256(capacity * 8);
     L.bytes = L.alt + align256(capacity * 8);
     return L;
@@ -756,6 +826,7 @@ gs_status gs_tile_lists(const float* rec, const uint16_t* rect, int64_t n, int32
     uint64_t* total = (uint64_t*)(w + L.total);
     uint2* pairs = (uint2*)(w + L.pairs);
     uint2* alt = (uint2*)(w + L.alt);
+    uint32_t* big = (uint32_t*)(w + L.big);
     hipStream_t s = (hipStream_t)stream;
     if (fill_u32((uint32_t*)overflow, 1, 0u, s) != hipSuccess) return GS_ERR_HIP;
     const unsigned bin_blocks = (unsigned)((int64_t)n_views * G.chunks * G.bands);
@@ -766,11 +837,11 @@ gs_status gs_tile_lists(const float* rec, const uint16_t* rect, int64_t n, int32
         return GS_ERR_HIP;
     }
     hipLaunchKernelGGL(k_bin_colscan, dim3(grid_for((uint64_t)n_tiles, 64)), dim3(256), 0, s, table, G, n_views,
-                       totals);
+                       totals, big);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     if (scan_u32(totals, totals, (uint64_t)n_tiles, total, w + L.scan, s) != hipSuccess) return GS_ERR_HIP;
     hipLaunchKernelGGL(k_tl_ranges, dim3(grid_for((uint64_t)n_tiles, 256)), dim3(256), 0, s, totals, n_tiles, capacity,
-                       ranges);
+                       ranges, big);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     if (n == 0) return GS_OK;
     hipLaunchKernelGGL(k_bin_fill, dim3(bin_blocks), dim3(256), 0, s, rec, rect, G, table, totals, pairs, capacity,
@@ -791,8 +862,8 @@ gs_status gs_tile_lists(const float* rec, const uint16_t* rect, int64_t n, int32
     hipLaunchKernelGGL(k_tl_sort_wave, dim3(grid_for((uint64_t)n_tiles, 4)), dim3(256), 0, s, ranges, n_tiles, total,
                        capacity, pairs, vals, mo);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
-    hipLaunchKernelGGL(k_tl_sort, dim3((unsigned)n_tiles), dim3(TL_THREADS), 0, s, ranges, total, capacity, pairs,
-                       alt, vals, mo);
+    hipLaunchKernelGGL(k_tl_sort, dim3((unsigned)(n_tiles + TL_MAXBIG)), dim3(TL_THREADS), 0, s, ranges, total,
+                       capacity, pairs, alt, vals, big, mo);
     return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
 }
 
