@@ -204,10 +204,7 @@ def main():
     frac_step = step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9)
 
     # dominant kernel: the single-kernel stage with the largest time
-    if ts.fused_raster:  # the timed steps keep n_contrib on chip: one more pass writes it
-        b.rasterize_fwd_bwd_l1(ts.target, ts.bg, outputs=True)
-        torch.cuda.synchronize()
-    pairs = int(b.n_contrib.sum(dtype=torch.int64))  # (pixel, entry) pairs up to each last contributor
+    pairs = ts.evaluated_pairs()  # (pixel, entry) pairs up to each last contributor (after the timed steps)
     single = {"raster_fwd_loss": "k_raster_fwd_l1", "raster_bwd": "k_raster_bwd", "adam": "k_adam",
               "preprocess_bwd": "k_preprocess_bwd", "preprocess_bwd_adam": "k_preprocess_bwd",
               "raster_fwd_bwd": "k_raster_fwd_bwd_l1"}
@@ -233,7 +230,10 @@ def main():
     roofline["avg_launch_ms"] = round(stage_ms[dom], 4)
 
     # intersection statistics and a plain device copy for the achievable HBM rate
-    rng_ = b.ranges.view(-1, 2).to(torch.int64)
+    # the ranges of the lists built last: in the memory-capped mode only the
+    # last window's tiles (the rest of the buffer is not theirs)
+    n_rng = b.V * b.TX * (b.TY - (b.TY - 1) // args.band_rows * args.band_rows) if args.band_rows else b.V * b.T
+    rng_ = b.ranges.view(-1, 2)[:n_rng].to(torch.int64)
     max_per_tile = int((rng_[:, 1] - rng_[:, 0]).max())
     peak_list_bytes = b.workspace_bytes()
     copy_gbs = copy_probe(torch, dev)

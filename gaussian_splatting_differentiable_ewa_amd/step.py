@@ -372,6 +372,21 @@ class TrainStep:
             self._pending.append((self.t, ev, hk, hf))
         mark(len(self.stage_names))
 
+    def evaluated_pairs(self) -> int:
+        """(pixel, list entry) pairs the raster passes evaluate: every entry of
+        a pixel's list up to its last contributor, summed from n_contrib. The
+        fused pass keeps n_contrib on chip, so one more step (an update like
+        any other) writes it, window by window in the memory-capped mode --
+        never a whole-image pass over a window's lists."""
+        if self.fused_raster:
+            keep = self.write_image
+            self.write_image = True
+            self.step()
+            self.flush()
+            self.write_image = keep
+        torch.cuda.synchronize()
+        return int(self.buf.n_contrib.sum(dtype=torch.int64))
+
     def flush(self):
         """Settle every launched step (waits for the GPU)."""
         while self._pending:

@@ -125,3 +125,25 @@ def test_fused_raster_step_equals_separate():
     ga, gb = a.grad2d.double(), b.grad2d.double()
     scale = ga.abs().max()
     assert torch.all((ga - gb).abs() <= 1e-4 * ga.abs() + 1e-7 * scale)
+
+
+def test_evaluated_pairs_windows_equal_whole_image():
+    """The pair count the benchmark reports (from n_contrib, which the fused
+    pass keeps on chip) comes from a step of the same mode: in the
+    memory-capped mode every window writes its rows; the count equals the
+    whole-image step's."""
+    import torch
+    dev = torch.device("cuda:0")
+    cfg = S.CONFIGS[1]
+    cams = cfg.cameras()
+    p = torch.from_numpy(S.make_params(cfg)).to(dev)
+    target = render(torch.from_numpy(S.make_target_params(cfg)).to(dev), cfg.sh_degree, cams).clone()
+    kw = dict(lr=cfg.lr, betas=(cfg.beta1, cfg.beta2), eps=cfg.eps)
+    whole = TrainStep(p.clone(), cfg.sh_degree, cams, target, **kw)
+    banded = TrainStep(p.clone(), cfg.sh_degree, cams, target, band_rows=13, **kw)
+    # the first step of each: both rasterize the same parameters
+    a, b = whole.evaluated_pairs(), banded.evaluated_pairs()
+    assert a == b and a > 0
+    assert whole.t == 1 and banded.t == 1
+    # and a second count (a second step) still reads only written rows
+    assert banded.evaluated_pairs() > 0 and banded.t == 2
