@@ -92,6 +92,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="scene id (2 = the headline workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--generated-order", action="store_true",
+                    help="keep the Gaussians in the generated (random) order instead of the Morton order of their means")
     ap.add_argument("--separate-raster", action="store_true",
                     help="forward + loss and backward raster as two passes instead of the fused one")
     ap.add_argument("--band-rows", type=int, default=None,
@@ -153,7 +155,7 @@ def main():
 
     from gaussian_splatting_differentiable_ewa_amd import _lib as L
     from gaussian_splatting_differentiable_ewa_amd import scenes as S
-    from gaussian_splatting_differentiable_ewa_amd.step import TrainStep, render
+    from gaussian_splatting_differentiable_ewa_amd.step import TrainStep, render, spatial_order
 
     L.lib()
     dev = torch.device("cuda:0")
@@ -161,7 +163,10 @@ def main():
     cams = cfg.cameras()
     t0 = time.time()
     params_np = S.make_params(cfg)
-    params = torch.from_numpy(params_np).to(dev)
+    # storage order of the Gaussians: Morton order of the means (set-up, not
+    # timed; the step's arithmetic does not depend on it), or as generated
+    perm = None if args.generated_order else spatial_order(params_np[:3])
+    params = torch.from_numpy(params_np if perm is None else np.ascontiguousarray(params_np[:, perm])).to(dev)
     target = render(torch.from_numpy(S.make_target_params(cfg)).to(dev), cfg.sh_degree, cams).clone()
     ts = TrainStep(params.clone(), cfg.sh_degree, cams, target, lr=cfg.lr, betas=(cfg.beta1, cfg.beta2),
                    eps=cfg.eps, band_rows=args.band_rows, fused_raster=not args.separate_raster)
@@ -251,6 +256,7 @@ def main():
         "step_hbm_fraction": round(frac_step, 4), "step_algorithmic_bytes": int(step_bytes),
         "intersections": b.K, "k_per_gaussian": round(b.K / b.n, 4), "list_builder": b.path,
         "band_rows": args.band_rows, "raster": "separate" if args.separate_raster else "fused",
+        "gaussian_order": "generated" if args.generated_order else "morton",
         "host_count_read": not ts.defer_count or not b.lists_without_count(), "redone_steps": redone,
         "visible_per_view": n_vis,
         "max_per_tile": max_per_tile, "peak_intersection_bytes": int(peak_list_bytes),

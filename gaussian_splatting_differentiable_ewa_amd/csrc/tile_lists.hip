@@ -4,7 +4,8 @@
 // open-sources distributed 3D Gaussian Splatting training", section
 // "Distributed training architecture and memory scaling"), built by binning
 // instead of one global sort of 64-bit keys, with no global atomics:
-//   1. k_bin_count    workgroup (view, chunk of Gaussians, band of tile rows):
+//   1. k_bin_count    workgroup (view, chunk of about 8192 Gaussians in runs of
+//                     8, band of tile rows):
 //                     LDS counters of the band's tiles, one increment per
 //                     (Gaussian, tile); written as table[view][chunk][tile];
 //   2. k_bin_colscan  per (view, tile): exclusive prefix over the chunks (in
@@ -57,11 +58,25 @@ struct BinGrid {
     int32_t bands;
 };
 
-// the workgroup's (view, chunk, band) and its Gaussians and tile rows
+// the workgroup's (view, chunk, band) and its Gaussians and tile rows. The
+// Gaussians are taken in runs of BIN_RUN consecutive ones, and chunk c holds
+// runs c, c + chunks, c + 2 chunks, ...: the 64 lanes of a wave then work on
+// eight places of the scene, not one, whatever the storage order (in a
+// spatial order, 64 consecutive Gaussians meet the same tile, and LDS
+// atomics on one counter serialise), while each run's rectangles still load
+// as one 64-byte piece.
+constexpr int64_t BIN_RUN = 8;
+
 struct BinBlock {
-    int64_t v, c, g0, g1;
+    int64_t v, c, len;  // len: local indices of the chunk (some past n in its last run)
     uint32_t ty0, ty1;
 };
+
+// The Gaussian at local index l of chunk c (may be >= n in the last run).
+__device__ __forceinline__ int64_t bin_gauss(const BinGrid& G, const BinBlock& B, int64_t l)
+{
+    return ((l / BIN_RUN) * G.chunks + B.c) * BIN_RUN + (l % BIN_RUN);
+}
 
 __device__ __forceinline__ BinBlock bin_block(const BinGrid& G)
 {
@@ -71,8 +86,8 @@ __device__ __forceinline__ BinBlock bin_block(const BinGrid& G)
     const int64_t rem = blockIdx.x - B.v * per_view;
     B.c = rem / G.bands;
     const int64_t band = rem - B.c * G.bands;
-    B.g0 = B.c * G.chunk;
-    B.g1 = min(G.n, B.g0 + G.chunk);
+    const int64_t runs = (G.n + BIN_RUN - 1) / BIN_RUN;
+    B.len = B.c < runs ? (runs - B.c + G.chunks - 1) / G.chunks * BIN_RUN : 0;
     B.ty0 = (uint32_t)(band * G.band_rows);
     B.ty1 = min((uint32_t)G.tiles_y, B.ty0 + (uint32_t)G.band_rows);
     return B;
@@ -102,12 +117,12 @@ __global__ __launch_bounds__(256) void k_bin_count(const uint16_t* __restrict__ 
     __syncthreads();
     // four Gaussians per thread and round: their rectangles are requested
     // together
-    for (int64_t g4 = B.g0 + threadIdx.x; g4 < B.g1; g4 += 4 * 256) {
+    for (int64_t l4 = threadIdx.x; l4 < B.len; l4 += 4 * 256) {
         uint2 rr[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int64_t g = g4 + 256 * k;
-            rr[k] = g < B.g1 ? *(const uint2*)(rect + 4 * (B.v * G.n + g)) : make_uint2(0u, 0u);
+            const int64_t l = l4 + 256 * k, g = bin_gauss(G, B, l);
+            rr[k] = l < B.len && g < G.n ? *(const uint2*)(rect + 4 * (B.v * G.n + g)) : make_uint2(0u, 0u);
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -184,13 +199,13 @@ __global__ __launch_bounds__(256) void k_bin_fill(const float* __restrict__ rec,
     for (uint32_t i = threadIdx.x; i < nt; i += 256) cur[i] = st[i] + row[i];
     __syncthreads();
     bool over = false;
-    for (int64_t g4 = B.g0 + threadIdx.x; g4 < B.g1; g4 += 4 * 256) {
+    for (int64_t l4 = threadIdx.x; l4 < B.len; l4 += 4 * 256) {
         uint2 rr[4];
         uint32_t zb[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int64_t g = g4 + 256 * k, idx = B.v * G.n + g;
-            const bool in = g < B.g1;
+            const int64_t l = l4 + 256 * k, g = bin_gauss(G, B, l), idx = B.v * G.n + g;
+            const bool in = l < B.len && g < G.n;
             rr[k] = in ? *(const uint2*)(rect + 4 * idx) : make_uint2(0u, 0u);
             zb[k] = in ? __float_as_uint(rec[idx * GS_REC_FLOATS + GS_REC_DEPTH]) : 0u;
         }
@@ -198,7 +213,7 @@ __global__ __launch_bounds__(256) void k_bin_fill(const float* __restrict__ rec,
         for (int k = 0; k < 4; ++k) {
             uint32_t x0, y0, x1, y1;
             if (!band_rect(rr[k], G, B.ty0, B.ty1, x0, y0, x1, y1)) continue;
-            const uint32_t gid = (uint32_t)(g4 + 256 * k);
+            const uint32_t gid = (uint32_t)bin_gauss(G, B, l4 + 256 * k);
             for (uint32_t ty = y0; ty < y1; ++ty)
                 for (uint32_t tx = x0; tx < x1; ++tx) {
                     const uint32_t pos = atomicAdd(&cur[(ty - B.ty0) * G.tiles_x + tx], 1u);
@@ -760,9 +775,17 @@ static BinGrid bin_grid(int64_t n, int32_t n_views, int32_t width, int32_t heigh
     G.row0 = row0;
     G.tiles = (int64_t)G.tiles_x * G.tiles_y;
     G.n = n;
-    const int64_t by_table = std::max<int64_t>(1, ((int64_t)1 << 22) / std::max<int64_t>(1, G.tiles * n_views));
+    // Chunks of at most about 8192 Gaussians (at least as many as fill a
+    // table of 4M counters), with the table capped at 32M counters and a
+    // chunk of at least 1024 Gaussians. A chunk's Gaussians are contiguous in
+    // storage, so that their rectangles load coalesced; in a spatial storage
+    // order they then meet few tiles, and a large chunk would pile its LDS
+    // atomics onto a few counters.
+    const int64_t tv = std::max<int64_t>(1, G.tiles * n_views);
+    const int64_t want = std::max<int64_t>((n + 8191) / 8192, ((int64_t)1 << 22) / tv);
+    const int64_t cap = std::max<int64_t>(1, ((int64_t)1 << 25) / tv);
     const int64_t by_size = std::max<int64_t>(1, (n + 1023) / 1024);
-    G.chunks = (int32_t)std::min<int64_t>(by_table, by_size);
+    G.chunks = (int32_t)std::min<int64_t>(std::min<int64_t>(want, cap), by_size);
     G.chunk = std::max<int64_t>(1, (n + G.chunks - 1) / G.chunks);
     G.band_rows = std::max<int32_t>(1, std::min<int32_t>(G.tiles_y, BAND_TILES / G.tiles_x));
     G.bands = (G.tiles_y + G.band_rows - 1) / G.band_rows;
@@ -775,7 +798,8 @@ static TlLayout tl_layout(const BinGrid& G, int32_t n_views, uint64_t capacity)
     TlLayout L;
     L.table = 0;
     // the table of any window of rows fits in the larger of the whole
-    // image's and 4M counters
+    // image's and 4M counters (a window has fewer tiles and at most as many
+    // chunks per 4M counters, or the whole image's table is at the cap too)
     L.totals = align256(std::max<size_t>((size_t)n_tiles * G.chunks, (size_t)1 << 22) * 4);
     L.total = L.totals + align256((n_tiles + 1) * 4);
     L.scan = L.total + 256;

@@ -189,6 +189,36 @@ class Buffers:
         L.gs_preprocess_bwd(params, self.n, self.sh_degree, self.cams, self.rect, self.grad2d, grad)
 
 
+def spatial_order(means) -> "numpy.ndarray":
+    """A storage order of the Gaussians by the Morton (Z-order) code of their
+    means, 10 bits per axis over the means' bounding box (ties by index).
+
+    The step's result does not depend on the order in which the Gaussians are
+    stored, apart from the order of equal depths in a tile's list (by index)
+    and the summation order of the atomics; what depends on it is locality:
+    neighbouring Gaussians share tiles, so a chunk of them fills long runs of
+    a tile's list, their records share cache lines in the list gathers, and a
+    wave of Gaussians tends to be seen or unseen as a whole. Apply it once,
+    at set-up, to the parameters (and moments): ``params[:, perm]``; the
+    inverse is ``numpy.argsort(perm)``. Host code (numpy), not part of the
+    step."""
+    import numpy as np
+
+    m = np.asarray(means, dtype=np.float64)
+    lo, hi = m.min(axis=1, keepdims=True), m.max(axis=1, keepdims=True)
+    q = np.clip(((m - lo) / np.maximum(hi - lo, 1e-30) * 1023.0).astype(np.int64), 0, 1023)
+
+    def spread(x):  # 10 bits to every third bit of 30
+        x = (x | (x << 16)) & 0x030000FF
+        x = (x | (x << 8)) & 0x0300F00F
+        x = (x | (x << 4)) & 0x030C30C3
+        x = (x | (x << 2)) & 0x09249249
+        return x
+
+    code = spread(q[0]) | (spread(q[1]) << 1) | (spread(q[2]) << 2)
+    return np.argsort(code, kind="stable")
+
+
 def render(params: torch.Tensor, sh_degree: int, cams: Sequence, bg=(0.0, 0.0, 0.0)) -> torch.Tensor:
     """Forward render of ``params`` through ``cams``; returns [V][3][H][W]."""
     b = Buffers(params.shape[1], sh_degree, cams, device=params.device)

@@ -8,7 +8,7 @@ import pytest
 
 from gaussian_splatting_differentiable_ewa_amd import _lib as L
 from gaussian_splatting_differentiable_ewa_amd import scenes as S
-from gaussian_splatting_differentiable_ewa_amd.step import TrainStep, render
+from gaussian_splatting_differentiable_ewa_amd.step import TrainStep, render, spatial_order
 
 pytestmark = pytest.mark.gpu
 
@@ -147,3 +147,78 @@ def test_evaluated_pairs_windows_equal_whole_image():
     assert whole.t == 1 and banded.t == 1
     # and a second count (a second step) still reads only written rows
     assert banded.evaluated_pairs() > 0 and banded.t == 2
+
+
+def _tie_tiles(buf):
+    """Tiles (view-major index) whose sorted list holds two entries of equal
+    depth bits, and the Gaussians listed in them."""
+    V, n = buf.V, buf.n
+    rng = buf.ranges.view(-1, 2).cpu().numpy().astype(np.int64)
+    vals = buf.sorted_vals.cpu().numpy().astype(np.int64)
+    z = buf.rec.view(V, n, L.GS_REC_FLOATS)[..., L.REC_DEPTH].cpu().numpy().view(np.uint32)
+    lens = rng[:, 1] - rng[:, 0]
+    tile = np.repeat(np.arange(rng.shape[0]), lens)
+    pos = np.concatenate([np.arange(a, b) for a, b in rng if b > a])
+    g = vals[pos]
+    d = z[tile // buf.T, g]
+    tie = (d[1:] == d[:-1]) & (tile[1:] == tile[:-1])
+    tiles = np.unique(tile[1:][tie])
+    gauss = np.unique(g[np.isin(tile, tiles)])
+    return tiles, gauss
+
+
+def test_spatial_order_same_step():
+    """A step on the Gaussians stored in Morton order (spatial_order) equals
+    the step on the generated order, mapped back: the same K; image, T_final
+    and n_contrib equal outside the tiles whose list holds two entries of
+    equal depth bits (the lists order those by Gaussian index, which the
+    permutation changes); 2D gradients (up to the atomics' summation order)
+    and updated parameters equal for the Gaussians listed in no such tile."""
+    import torch
+    dev = torch.device("cuda:0")
+    cfg = S.CONFIGS[1]
+    cams = cfg.cameras()
+    p_np = S.make_params(cfg)
+    perm = spatial_order(p_np[:3])
+    inv = np.argsort(perm)
+    assert np.array_equal(np.sort(perm), np.arange(p_np.shape[1]))
+    target = render(torch.from_numpy(S.make_target_params(cfg)).to(dev), cfg.sh_degree, cams).clone()
+    kw = dict(lr=cfg.lr, betas=(cfg.beta1, cfg.beta2), eps=cfg.eps, write_image=True)
+    a = TrainStep(torch.from_numpy(p_np).to(dev), cfg.sh_degree, cams, target, **kw)
+    b = TrainStep(torch.from_numpy(np.ascontiguousarray(p_np[:, perm])).to(dev), cfg.sh_degree, cams, target, **kw)
+    for ts in (a, b):
+        ts.step()
+        ts.flush()
+    torch.cuda.synchronize()
+    assert a.buf.K == b.buf.K > 0
+    tiles, gauss = _tie_tiles(a.buf)
+    tiles_b, gauss_b = _tie_tiles(b.buf)
+    assert np.array_equal(tiles, tiles_b) and np.array_equal(gauss, np.sort(perm[gauss_b]))
+    differ = ((a.buf.image != b.buf.image).any(dim=1) | (a.buf.n_contrib != b.buf.n_contrib)
+              | (a.buf.T_final != b.buf.T_final)).cpu().numpy()
+    V, H, W = differ.shape
+    TX = (W + 15) // 16
+    vv, jj, ii = np.nonzero(differ)
+    where = vv * a.buf.T + (jj // 16) * TX + ii // 16
+    print({"pixels_that_differ": int(differ.sum()), "tie_tiles": int(tiles.size), "tie_gaussians": int(gauss.size)})
+    assert np.isin(where, tiles).all()
+    n = a.buf.n
+    keep = np.ones(n, bool)
+    keep[gauss] = False
+    keep_t = torch.from_numpy(keep).to(dev)
+    ga = a.buf.grad2d.view(V, n, 9).double()[:, keep_t]
+    gb = b.buf.grad2d.view(V, n, 9).double()[:, torch.from_numpy(inv).to(dev)][:, keep_t]
+    # another order of the atomics: 1e-3 relative, with a floor of 1e-5 of
+    # each gradient component's largest magnitude (cancelling sums)
+    floor = ga.abs().amax(dim=1, keepdim=True)
+    err, lim = (ga - gb).abs(), 1e-3 * ga.abs() + 1e-5 * floor
+    bad = ~(err <= lim)
+    assert not bool(bad.any()), (f"{int(bad.sum())} of {bad.numel()} 2D gradients differ; worst excess "
+                                 f"{float((err - lim).max())}; within 1e-4 relative: "
+                                 f"{float((err <= 1e-4 * ga.abs()).double().mean())}")
+    pa = a.params[:, keep_t]
+    pb = b.params[:, torch.from_numpy(inv).to(dev)][:, keep_t]
+    # Adam at t = 1 moves each element by about lr sign(g): within 1e-5
+    # (|theta| + lr) except where a gradient is summation noise around zero
+    close = (pa - pb).abs() <= 1e-5 * (pa.abs() + cfg.lr)
+    assert float(close.double().mean()) >= 0.999
