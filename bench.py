@@ -108,9 +108,13 @@ def parse():
     return ap.parse_args()
 
 
-def stage_bytes(P, n, V, K, n_vis_per_view, n_any, n_px):
+def stage_bytes(P, n, V, K, n_vis_per_view, n_any, n_px, n_adam=None):
     """Algorithmic HBM bytes per stage of one step (what the method must
-    move with this layout: each input read once, each output written once)."""
+    move with this layout: each input read once, each output written once).
+    n_adam: the Gaussians the fused backward + Adam must read and update (all
+    n, unless the per-Gaussian state flags mark some with zero moments and
+    no gradient, whose update is the identity and moves nothing)."""
+    n_adam = n if n_adam is None else n_adam
     Bp = 4 * P
     Nv = sum(n_vis_per_view)
     return {
@@ -132,10 +136,11 @@ def stage_bytes(P, n, V, K, n_vis_per_view, n_any, n_px):
         "raster_fwd_bwd": 6 * K + 36 * Nv + 12 * V * n_px + 36 * Nv * 2,
         "preprocess_bwd": Bp * n_any + 44 * Nv + Bp * n,
         "adam": 7 * Bp * n,
-        # the two above in one pass: parameters read once, every (view,
-        # Gaussian) rectangle and each visible pair's 2D gradient read, the
-        # gradient never stored; moments read, parameters and moments written
-        "preprocess_bwd_adam": Bp * n + 8 * V * n + 36 * Nv + 2 * Bp * n + 3 * Bp * n,
+        # the two above in one pass: every (view, Gaussian) rectangle and
+        # each visible pair's 2D gradient read, the gradient never stored;
+        # for each Gaussian updated, parameters and moments read once,
+        # parameters and moments written
+        "preprocess_bwd_adam": 8 * V * n + 36 * Nv + 6 * Bp * n_adam,
     }
 
 
@@ -202,7 +207,10 @@ def main():
     vis = (rect[..., 2] > rect[..., 0]) & (rect[..., 3] > rect[..., 1])
     n_vis = [int(x) for x in vis.sum(axis=1)]
     n_any = int(vis.any(axis=0).sum())
-    sb = stage_bytes(b.P, b.n, V, b.K, n_vis, n_any, H * W)
+    # with the state flags on, the fused backward + Adam touches only the
+    # Gaussians whose moments are not known to be zero (those seen so far)
+    n_adam = int((ts.adam_state != 0).sum()) if ts.fused_adam and ts._use_state else b.n
+    sb = stage_bytes(b.P, b.n, V, b.K, n_vis, n_any, H * W, n_adam)
     unused = ["preprocess_bwd", "adam"] if ts.fused_adam else ["preprocess_bwd_adam"]
     unused += ["raster_fwd_loss", "raster_bwd"] if ts.fused_raster else ["raster_fwd_bwd"]
     step_bytes = sum(v for k, v in sb.items() if k not in unused)
@@ -258,7 +266,7 @@ def main():
         "band_rows": args.band_rows, "raster": "separate" if args.separate_raster else "fused",
         "gaussian_order": "generated" if args.generated_order else "morton",
         "host_count_read": not ts.defer_count or not b.lists_without_count(), "redone_steps": redone,
-        "visible_per_view": n_vis,
+        "visible_per_view": n_vis, "adam_gaussians": n_adam,
         "max_per_tile": max_per_tile, "peak_intersection_bytes": int(peak_list_bytes),
         "hbm_copy_gbs": round(copy_gbs, 1),
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
