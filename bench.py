@@ -92,6 +92,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="scene id (2 = the headline workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lists", choices=["auto", "binned", "radix"], default="auto",
+                    help="list builder: binning per tile, the global key sort, or chosen per scene")
     ap.add_argument("--generated-order", action="store_true",
                     help="keep the Gaussians in the generated (random) order instead of the Morton order of their means")
     ap.add_argument("--separate-raster", action="store_true",
@@ -174,7 +176,7 @@ def main():
     params = torch.from_numpy(params_np if perm is None else np.ascontiguousarray(params_np[:, perm])).to(dev)
     target = render(torch.from_numpy(S.make_target_params(cfg)).to(dev), cfg.sh_degree, cams).clone()
     ts = TrainStep(params.clone(), cfg.sh_degree, cams, target, lr=cfg.lr, betas=(cfg.beta1, cfg.beta2),
-                   eps=cfg.eps, band_rows=args.band_rows, fused_raster=not args.separate_raster)
+                   eps=cfg.eps, band_rows=args.band_rows, fused_raster=not args.separate_raster, lists=args.lists)
     print(f"[bench] {cfg.name}: inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     b = ts.buf

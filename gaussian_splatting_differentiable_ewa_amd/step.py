@@ -249,11 +249,11 @@ class TrainStep:
                  lr=1e-3, betas=(0.9, 0.999), eps=1e-15, bg=(0.0, 0.0, 0.0),
                  m: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None, defer_count: bool = True,
                  fused_adam: bool = True, write_image: bool = False, band_rows: Optional[int] = None,
-                 fused_raster: bool = True):
+                 fused_raster: bool = True, lists: str = "auto"):
         assert params.is_cuda and params.dtype == torch.float32 and params.is_contiguous()
         self.params = params
         self.sh_degree = sh_degree
-        self.buf = Buffers(params.shape[1], sh_degree, cams, device=params.device)
+        self.buf = Buffers(params.shape[1], sh_degree, cams, device=params.device, lists=lists)
         assert params.shape[0] == self.buf.P
         self.target = target.contiguous()
         self.m = torch.zeros_like(params) if m is None else m
