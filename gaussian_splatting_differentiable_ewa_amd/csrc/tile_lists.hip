@@ -5,7 +5,7 @@
 // "Distributed training architecture and memory scaling"), built by binning
 // instead of one global sort of 64-bit keys, with no global atomics:
 //   1. k_bin_count    workgroup (view, chunk of about 8192 Gaussians in runs of
-//                     8, band of tile rows):
+//                     16, band of tile rows):
 //                     LDS counters of the band's tiles, one increment per
 //                     (Gaussian, tile); written as table[view][chunk][tile];
 //   2. k_bin_colscan  per (view, tile): exclusive prefix over the chunks (in
@@ -61,11 +61,11 @@ struct BinGrid {
 // the workgroup's (view, chunk, band) and its Gaussians and tile rows. The
 // Gaussians are taken in runs of BIN_RUN consecutive ones, and chunk c holds
 // runs c, c + chunks, c + 2 chunks, ...: the 64 lanes of a wave then work on
-// eight places of the scene, not one, whatever the storage order (in a
+// four places of the scene, not one, whatever the storage order (in a
 // spatial order, 64 consecutive Gaussians meet the same tile, and LDS
 // atomics on one counter serialise), while each run's rectangles still load
-// as one 64-byte piece.
-constexpr int64_t BIN_RUN = 8;
+// as one 128-byte piece (runs of 4, 8, 16, 32 measured: 16 and 32 best).
+constexpr int64_t BIN_RUN = 16;
 
 struct BinBlock {
     int64_t v, c, len;  // len: local indices of the chunk (some past n in its last run)
