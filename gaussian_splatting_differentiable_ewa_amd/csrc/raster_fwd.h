@@ -88,13 +88,16 @@ __device__ __forceinline__ FwdPixel raster_fwd_walk(FwdLds& L, const QuarterCtx&
         gather_record(nxt, rv);
         const uint32_t n_nx2 = take_batch<false>(S, nx2, len, rg.x, vals, masks, t, nullptr, L.list);
         // per row, the staged entries of its sub-block in list order, as
-        // record offsets; the rest of the row's list is the padding slot
+        // record offsets; the rest of the row's list is the padding slot. A
+        // row whose 16 pixels have all stopped gets no entries (they could
+        // change nothing), so that it does not set the batch's length.
         uint32_t cnt[4];
         {
+            const uint64_t live = ballot(!done);
             asm volatile("" ::: "memory");  // compaction reads precede these writes (LDS is in order per wave)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const bool keep = (cur.m4 >> r) & 1u;
+                const bool keep = ((cur.m4 >> r) & 1u) && ((live >> (16 * r)) & 0xffffull) != 0ull;
                 const uint64_t m = ballot(keep);
                 cnt[r] = (uint32_t)__popcll(m);
                 if (keep) L.list[r * RW_BATCH + mask_rank(m)] = (uint16_t)(t.lane * SLOT_BYTES);
