@@ -94,6 +94,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--lists", choices=["auto", "binned", "radix"], default="auto",
                     help="list builder: binning per tile, the global key sort, or chosen per scene")
+    ap.add_argument("--no-state-flags", action="store_true",
+                    help="dense Adam: read every Gaussian's moments, also those known to be zero and unseen")
     ap.add_argument("--generated-order", action="store_true",
                     help="keep the Gaussians in the generated (random) order instead of the Morton order of their means")
     ap.add_argument("--separate-raster", action="store_true",
@@ -176,7 +178,8 @@ def main():
     params = torch.from_numpy(params_np if perm is None else np.ascontiguousarray(params_np[:, perm])).to(dev)
     target = render(torch.from_numpy(S.make_target_params(cfg)).to(dev), cfg.sh_degree, cams).clone()
     ts = TrainStep(params.clone(), cfg.sh_degree, cams, target, lr=cfg.lr, betas=(cfg.beta1, cfg.beta2),
-                   eps=cfg.eps, band_rows=args.band_rows, fused_raster=not args.separate_raster, lists=args.lists)
+                   eps=cfg.eps, band_rows=args.band_rows, fused_raster=not args.separate_raster, lists=args.lists,
+                   state_flags=not args.no_state_flags)
     print(f"[bench] {cfg.name}: inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     b = ts.buf
@@ -267,6 +270,7 @@ def main():
         "intersections": b.K, "k_per_gaussian": round(b.K / b.n, 4), "list_builder": b.path,
         "band_rows": args.band_rows, "raster": "separate" if args.separate_raster else "fused",
         "gaussian_order": "generated" if args.generated_order else "morton",
+        "adam_state_flags": bool(ts._use_state),
         "host_count_read": not ts.defer_count or not b.lists_without_count(), "redone_steps": redone,
         "visible_per_view": n_vis, "adam_gaussians": n_adam,
         "max_per_tile": max_per_tile, "peak_intersection_bytes": int(peak_list_bytes),

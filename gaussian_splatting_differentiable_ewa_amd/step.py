@@ -241,7 +241,11 @@ class TrainStep:
     ``fused_raster`` (the default) forward raster, L1 loss and backward raster
     run as one pass (``gs_rasterize_fwd_bwd_l1``), which keeps T_final,
     n_contrib and dL/dimage on chip; otherwise ``gs_rasterize_fwd_l1`` and
-    ``gs_rasterize_bwd`` run one after the other and write them."""
+    ``gs_rasterize_bwd`` run one after the other and write them. With
+    ``state_flags`` (the default; it takes effect when eps > 0) Adam keeps a
+    byte per Gaussian that says whether its moments may be non-zero, and skips
+    a Gaussian whose moments are zero and that no view sees, without reading
+    it: its update would leave parameters and moments unchanged."""
 
     RING = 4  # steps whose count and flag may be in flight
 
@@ -249,7 +253,7 @@ class TrainStep:
                  lr=1e-3, betas=(0.9, 0.999), eps=1e-15, bg=(0.0, 0.0, 0.0),
                  m: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None, defer_count: bool = True,
                  fused_adam: bool = True, write_image: bool = False, band_rows: Optional[int] = None,
-                 fused_raster: bool = True, lists: str = "auto"):
+                 fused_raster: bool = True, lists: str = "auto", state_flags: bool = True):
         assert params.is_cuda and params.dtype == torch.float32 and params.is_contiguous()
         self.params = params
         self.sh_degree = sh_degree
@@ -263,10 +267,10 @@ class TrainStep:
         fresh = m is None and v is None
         self.adam_state = (torch.zeros if fresh else torch.ones)(params.shape[1], dtype=torch.uint8,
                                                                  device=params.device)
-        # the flags pay off only when most Gaussians are out of view (then
-        # the moment traffic of the unseen ones is skipped); decided once, at
-        # the first step, from the share visible in some view
-        self._use_state = None
+        # with the flags, Adam skips a Gaussian with zero moments that no view
+        # sees (its update is the identity when eps > 0) without reading it;
+        # in a spatial storage order whole waves of such Gaussians skip
+        self._use_state = state_flags and eps > 0
         self.grad = None if fused_adam else torch.empty_like(params)
         self.lr, self.betas, self.eps, self.bg = lr, betas, eps, bg
         self.t = 0
@@ -375,10 +379,6 @@ class TrainStep:
                 mark(6)
                 m0 = 7
         skip = self.sticky if deferred else None
-        if self._use_state is None:
-            r = b.rect.view(b.V, b.n, 4).view(torch.int16)
-            seen = ((r[..., 2] > r[..., 0]) & (r[..., 3] > r[..., 1])).any(dim=0)
-            self._use_state = self.eps > 0 and float(seen.float().mean()) < 0.5
         if self.fused_adam:
             L.gs_preprocess_bwd_adam(self.params, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, self.m, self.v, self.lr,
                                      self.betas[0], self.betas[1], self.eps, self.t, skip=skip,
