@@ -21,9 +21,9 @@
 //      k_tl_sort      one workgroup per longer tile: stable LSD radix sort by
 //                     the 32 depth bits (8-bit digits; digits equal across the
 //                     tile are skipped), in LDS for up to 4096 entries and
-//                     through a global scratch copy beyond (those tiles,
-//                     listed by k_tl_ranges, first), then runs of equal
-//                     depth put in id order.
+//                     through a global scratch copy beyond; k_tl_ranges lists
+//                     its tiles by length class and it takes the longest
+//                     first; then runs of equal depth put in id order.
 // (depth, id) is a total order, so the arbitrary slot order of step 4 never
 // shows: the lists equal those of the global key sort. The positive fp32
 // depths order like their bit patterns.
@@ -43,7 +43,9 @@ constexpr int TL_CAP = 4096;                    // entries a tile sorts in LDS
 constexpr int TL_ROUNDS = TL_CAP / TL_THREADS;  // rounds of 64 keys per wave, at most
 constexpr int GL_CHUNK = 4096;                  // entries per chunk of the global-memory path
 constexpr int GL_ROUNDS = GL_CHUNK / TL_THREADS;
-constexpr uint32_t TL_MAXBIG = 2048;            // tiles longer than TL_CAP that k_tl_sort takes first
+constexpr int TL_CLASSES = 4;  // length classes of the tiles k_tl_sort takes, longest first
+constexpr int WV_CAP = 512;  // entries one wave sorts alone
+constexpr int WV_ROUNDS = WV_CAP / 64;
 
 constexpr int BAND_TILES = 8192;  // LDS counters of one band of tile rows
 
@@ -143,7 +145,7 @@ __global__ __launch_bounds__(256) void k_bin_colscan(uint32_t* __restrict__ tabl
                                                      uint32_t* __restrict__ totals, uint32_t* __restrict__ big)
 {
     __shared__ uint32_t part[4][64];
-    if (blockIdx.x == 0 && threadIdx.x == 0) big[0] = 0u;  // k_tl_ranges counts the long tiles
+    if (blockIdx.x == 0 && threadIdx.x < TL_CLASSES) big[threadIdx.x] = 0u;  // k_tl_ranges counts the classes
     const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
     const int64_t i = (int64_t)blockIdx.x * 64 + lane;
     const bool ok = i < (int64_t)n_views * G.tiles;
@@ -167,10 +169,19 @@ __global__ __launch_bounds__(256) void k_bin_colscan(uint32_t* __restrict__ tabl
     }
 }
 
+// Length class of a tile that k_tl_sort sorts (more than WV_CAP entries):
+// 0 longer than TL_CAP (sorted through global memory), 1 more than 2048, 2
+// more than 1024, 3 the rest.
+__device__ __forceinline__ int tl_class(uint32_t len)
+{
+    return len > (uint32_t)TL_CAP ? 0 : len > 2048u ? 1 : len > 1024u ? 2 : 3;
+}
+
 // ranges, cut at the capacity: when the lists overflow, readers of the
-// ranges stay inside the filled slots. Tiles longer than the LDS sort holds
-// are listed in big[1 + k] (count in big[0], zeroed by k_bin_colscan), so that
-// k_tl_sort starts them first.
+// ranges stay inside the filled slots. The tiles k_tl_sort sorts are listed
+// by length class: class c's count in big[c] (zeroed by k_bin_colscan), its
+// tiles in big[TL_CLASSES + c n_tiles + k], so that k_tl_sort takes the
+// longest first.
 __global__ __launch_bounds__(256) void k_tl_ranges(const uint32_t* __restrict__ starts, int64_t n_tiles,
                                                    uint64_t capacity, uint32_t* __restrict__ ranges,
                                                    uint32_t* __restrict__ big)
@@ -179,9 +190,10 @@ __global__ __launch_bounds__(256) void k_tl_ranges(const uint32_t* __restrict__ 
     if (t >= n_tiles) return;
     const uint32_t s = (uint32_t)min((uint64_t)starts[t], capacity), e = (uint32_t)min((uint64_t)starts[t + 1], capacity);
     *(uint2*)(ranges + 2 * t) = e > s ? make_uint2(s, e) : make_uint2(0u, 0u);
-    if (e > s && e - s > (uint32_t)TL_CAP) {
-        const uint32_t k = atomicAdd(big, 1u);
-        if (k < TL_MAXBIG) big[1 + k] = (uint32_t)t;
+    if (e > s && e - s > (uint32_t)WV_CAP) {
+        const int c = tl_class(e - s);
+        const uint32_t k = atomicAdd(big + c, 1u);
+        big[TL_CLASSES + (int64_t)c * n_tiles + k] = (uint32_t)t;
     }
 }
 
@@ -382,8 +394,6 @@ __device__ __forceinline__ void tl_fix_ties(uint32_t n, KeyAt key_at, ValAt, Les
     }
 }
 
-constexpr int WV_CAP = 512;  // entries one wave sorts alone
-constexpr int WV_ROUNDS = WV_CAP / 64;
 
 // Tiles of 65..512 entries, one wave each (four per workgroup, no barriers:
 // LDS is in order within a wave): the LSD radix sort of k_tl_sort on one
@@ -510,12 +520,11 @@ __global__ __launch_bounds__(256) void k_tl_sort_wave(const uint32_t* __restrict
     write_ids_masks<64u>(mo, tile, start, n, lane, [&](uint32_t i) { return tp[si[i]].y; }, vals);
 }
 
-// Launched with TL_MAXBIG + n_tiles workgroups: the first TL_MAXBIG take the
-// listed long tiles (those that sort through global memory and take longest),
-// the others tile blockIdx.x - TL_MAXBIG, unless it is a listed long tile.
-// When more long tiles exist than the list holds, every tile is taken in the
-// second range.
-__global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restrict__ ranges,
+// Launched with n_tiles workgroups: workgroup b takes the b-th tile of the
+// length-class lists of k_tl_ranges, longest class first (the workgroups
+// start in about that order, so the long tiles do not finish last); those
+// beyond the listed tiles return.
+__global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restrict__ ranges, int64_t n_tiles,
                                                         const uint64_t* __restrict__ total_dev, uint64_t capacity,
                                                         uint2* __restrict__ pairs, uint2* __restrict__ alt,
                                                         uint32_t* __restrict__ vals, const uint32_t* __restrict__ big,
@@ -525,14 +534,16 @@ __global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restri
     __shared__ uint16_t s_idx[TL_CAP];  // position of each key in the tile's unsorted pairs
     __shared__ uint32_t wcnt[4][256];
     __shared__ uint32_t s_misc[8];
-    const uint32_t n_big = big[0];
-    const bool listed = n_big <= TL_MAXBIG;  // every long tile is in the list
-    int64_t tile;
-    if (blockIdx.x < TL_MAXBIG) {
-        if (!listed || blockIdx.x >= n_big) return;
-        tile = big[1 + blockIdx.x];
-    } else {
-        tile = (int64_t)blockIdx.x - TL_MAXBIG;
+    int64_t tile = -1;
+    {
+        uint32_t b = blockIdx.x;
+#pragma unroll
+        for (int c = 0; c < TL_CLASSES; ++c) {
+            const uint32_t cnt = big[c];
+            if (tile < 0 && b < cnt) tile = big[TL_CLASSES + (int64_t)c * n_tiles + b];
+            if (tile < 0) b -= cnt;
+        }
+        if (tile < 0) return;
     }
     const uint2 rg = *(const uint2*)(ranges + 2 * (uint64_t)tile);
     const uint64_t limit = min(capacity, *total_dev);
@@ -541,7 +552,6 @@ __global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restri
     const uint32_t n = end - start;
     const uint32_t t = threadIdx.x, lane = t & 63u, wave = t >> 6;
     if (n <= (uint32_t)WV_CAP) return;  // k_tl_sort_small, k_tl_sort_wave
-    if (blockIdx.x >= TL_MAXBIG && listed && rg.y - rg.x > (uint32_t)TL_CAP) return;  // taken first
     if (n <= (uint32_t)TL_CAP) {
         // wave w holds the contiguous run [w L, (w + 1) L), L = 64 R
         const uint32_t R = (n + TL_THREADS - 1) / TL_THREADS;
@@ -804,7 +814,7 @@ static TlLayout tl_layout(const BinGrid& G, int32_t n_views, uint64_t capacity)
     L.total = L.totals + align256((n_tiles + 1) * 4);
     L.scan = L.total + 256;
     L.big = L.scan + align256(scan_workspace_bytes(n_tiles));
-    L.pairs = L.big + align256((1 + TL_MAXBIG) * 4);
+    L.pairs = L.big + align256((TL_CLASSES + TL_CLASSES * n_tiles) * 4);
     L.alt = L.pairs + align256(capacity * 8);
     L.bytes = L.alt + align256(capacity * 8);
     return L;
@@ -886,7 +896,7 @@ gs_status gs_tile_lists(const float* rec, const uint16_t* rect, int64_t n, int32
     hipLaunchKernelGGL(k_tl_sort_wave, dim3(grid_for((uint64_t)n_tiles, 4)), dim3(256), 0, s, ranges, n_tiles, total,
                        capacity, pairs, vals, mo);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
-    hipLaunchKernelGGL(k_tl_sort, dim3((unsigned)(n_tiles + TL_MAXBIG)), dim3(TL_THREADS), 0, s, ranges, total,
+    hipLaunchKernelGGL(k_tl_sort, dim3((unsigned)n_tiles), dim3(TL_THREADS), 0, s, ranges, n_tiles, total,
                        capacity, pairs, alt, vals, big, mo);
     return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
 }
