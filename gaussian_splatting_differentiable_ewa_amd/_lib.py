@@ -27,7 +27,7 @@ GS_GRAD2D_ROWS = 9
 EXPORTS = (
     "gs_abi_version", "gs_status_string", "gs_param_rows", "gs_tiles_x", "gs_tiles_y",
     "gs_sort_end_bit", "gs_preprocess_workspace_bytes", "gs_sort_workspace_bytes",
-    "gs_tile_lists_workspace_bytes", "gs_rasterize_fwd_l1_workspace_bytes",
+    "gs_tile_lists_workspace_bytes", "gs_rasterize_fwd_l1_workspace_bytes", "gs_rasterize_fwd_bwd_l1_workspace_bytes",
     "gs_preprocess", "gs_emit_intersections", "gs_sort_keys", "gs_tile_lists", "gs_tile_ranges", "gs_tile_masks",
     "gs_tile_masks_workspace_bytes",
     "gs_rasterize_fwd", "gs_rasterize_fwd_l1", "gs_loss_l1", "gs_rasterize_bwd", "gs_rasterize_fwd_bwd_l1",
@@ -73,6 +73,7 @@ def lib():
             "gs_sort_workspace_bytes": ([_U64], _SZ),
             "gs_tile_lists_workspace_bytes": ([_I64, _I32, _I32, _I32, _U64], _SZ),
             "gs_rasterize_fwd_l1_workspace_bytes": ([_I32, _I32, _I32], _SZ),
+            "gs_rasterize_fwd_bwd_l1_workspace_bytes": ([_I32, _I32, _I32], _SZ),
             "gs_preprocess": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
             "gs_emit_intersections": ([_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _U64, _P, _P], ctypes.c_int),
             "gs_sort_keys": ([_P, _P, _P, _P, _U64, _I32, _P, _SZ, _P, _P], ctypes.c_int),
@@ -159,6 +160,10 @@ def sort_workspace_bytes(n_keys: int) -> int:
 
 def rasterize_fwd_l1_workspace_bytes(n_views: int, width: int, height: int) -> int:
     return lib().gs_rasterize_fwd_l1_workspace_bytes(n_views, width, height)
+
+
+def rasterize_fwd_bwd_l1_workspace_bytes(n_views: int, width: int, height: int) -> int:
+    return lib().gs_rasterize_fwd_bwd_l1_workspace_bytes(n_views, width, height)
 
 
 def tile_lists_workspace_bytes(n: int, n_views: int, width: int, height: int, capacity: int) -> int:

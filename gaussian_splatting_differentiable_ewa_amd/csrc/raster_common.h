@@ -43,13 +43,16 @@ struct QuarterCtx {
 };
 
 // T: tiles per view in the window of tile rows the launch covers, row0: the
-// window's first tile row.
-__device__ __forceinline__ QuarterCtx quarter_ctx(int W, int H, int TX, int T, int row0)
+// window's first tile row. `order`, if given, lists the (view, tile)s in the
+// order their quarters are taken (the four quarters of a tile stay
+// consecutive); otherwise tile order.
+__device__ __forceinline__ QuarterCtx quarter_ctx(int W, int H, int TX, int T, int row0,
+                                                  const uint32_t* __restrict__ order = nullptr)
 {
     QuarterCtx t;
     const uint32_t lb = xcd_chunked(blockIdx.x, gridDim.x);
     const uint32_t quad = lb & 3u;
-    t.tile_lin = lb >> 2;
+    t.tile_lin = order ? order[lb >> 2] : lb >> 2;
     t.view = t.tile_lin / (uint32_t)T;
     const uint32_t tile = t.tile_lin - t.view * (uint32_t)T;
     const uint32_t wy = tile / (uint32_t)TX, tx = tile - wy * (uint32_t)TX, ty = wy + (uint32_t)row0;

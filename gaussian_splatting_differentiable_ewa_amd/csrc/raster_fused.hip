@@ -13,17 +13,60 @@ namespace gs {
 
 constexpr size_t FUSED_LDS_BYTES = sizeof(FwdLds) > sizeof(BwdLds) ? sizeof(FwdLds) : sizeof(BwdLds);
 
+// The order in which the pass takes the (view, tile)s: by list length, longest
+// first, in ORDER_CLASSES classes (ties in no particular order). A quarter's
+// time grows with its tile's list, and in tile order the quarters of long
+// lists that start late finish long after the rest. One workgroup: counts
+// per class, their prefix, then each tile's slot (LDS atomics).
+constexpr int ORDER_CLASSES = 8;
+constexpr int ORDER_THREADS = 1024;
+
+__device__ __forceinline__ int order_class(uint32_t len)
+{
+    // > 4096, > 2048, > 1024, > 512, > 256, > 128, > 64, the rest
+    int c = 0;
+#pragma unroll
+    for (int k = 12; k >= 6; --k) c += len <= (1u << k) ? 1 : 0;
+    return c;
+}
+
+__global__ __launch_bounds__(ORDER_THREADS) void k_tile_order(const uint32_t* __restrict__ ranges, int64_t n_tiles,
+                                                             uint32_t* __restrict__ order)
+{
+    __shared__ uint32_t cnt[ORDER_CLASSES];
+    if (threadIdx.x < ORDER_CLASSES) cnt[threadIdx.x] = 0u;
+    __syncthreads();
+    for (int64_t t = threadIdx.x; t < n_tiles; t += ORDER_THREADS) {
+        const uint2 rg = *(const uint2*)(ranges + 2 * t);
+        atomicAdd(&cnt[order_class(rg.y - rg.x)], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t run = 0u;
+        for (int c = 0; c < ORDER_CLASSES; ++c) {
+            const uint32_t k = cnt[c];
+            cnt[c] = run;
+            run += k;
+        }
+    }
+    __syncthreads();
+    for (int64_t t = threadIdx.x; t < n_tiles; t += ORDER_THREADS) {
+        const uint2 rg = *(const uint2*)(ranges + 2 * t);
+        order[atomicAdd(&cnt[order_class(rg.y - rg.x)], 1u)] = (uint32_t)t;
+    }
+}
+
 // image, T_final, n_contrib and dL may each be null (not written).
 __global__ __launch_bounds__(RW_THREADS) void k_raster_fwd_bwd_l1(
     const float* __restrict__ rec, int64_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ vals,
     const uint16_t* __restrict__ masks, int W, int H, int TX, int T, int row0, float bg0, float bg1, float bg2,
     const float* __restrict__ target, float scale, float* __restrict__ image, float* __restrict__ T_final,
     int32_t* __restrict__ n_contrib, float* __restrict__ dL, double* __restrict__ partial,
-    float* __restrict__ grad2d)
+    float* __restrict__ grad2d, const uint32_t* __restrict__ order)
 {
 #pragma clang fp contract(off)
     __shared__ __align__(16) unsigned char lds[FUSED_LDS_BYTES];
-    const QuarterCtx t = quarter_ctx(W, H, TX, T, row0);
+    const QuarterCtx t = quarter_ctx(W, H, TX, T, row0, order);
     if (t.empty) {
         if (t.lane == 0) partial[blockIdx.x] = 0.0;
         return;
@@ -73,6 +116,13 @@ using namespace gs;
 
 extern "C" {
 
+size_t gs_rasterize_fwd_bwd_l1_workspace_bytes(int32_t n_views, int32_t width, int32_t height)
+{
+    if (n_views < 1 || n_views > GS_MAX_VIEWS || width <= 0 || height <= 0) return 0;
+    const int64_t tiles = (int64_t)n_views * gs_tiles_x(width) * gs_tiles_y(height);
+    return (size_t)(tiles * 4 * sizeof(double) + tiles * sizeof(uint32_t));
+}
+
 gs_status gs_rasterize_fwd_bwd_l1(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
                                   const uint16_t* masks, const gs_camera* cams, int32_t n_views, int32_t row0,
                                   int32_t rows, const float* bg, const float* target, float scale, float* image,
@@ -82,16 +132,21 @@ gs_status gs_rasterize_fwd_bwd_l1(const float* rec, int64_t n, const uint32_t* r
     RasterArgs a;
     if (!raster_args(rec, n, ranges, vals, masks, cams, n_views, row0, rows, bg, a)) return GS_ERR_INVALID_ARGUMENT;
     if (!target || !loss || !ws || (n > 0 && !grad2d)) return GS_ERR_INVALID_ARGUMENT;
-    if (ws_bytes < (size_t)a.n_blocks * sizeof(double)) return GS_ERR_INVALID_ARGUMENT;
+    const int64_t n_tiles = a.n_blocks / 4;
+    if (ws_bytes < (size_t)a.n_blocks * sizeof(double) + (size_t)n_tiles * sizeof(uint32_t))
+        return GS_ERR_INVALID_ARGUMENT;
     hipStream_t s = (hipStream_t)stream;
     if (!accumulate && n > 0) {
         if (fill_u32((uint32_t*)grad2d, (uint64_t)n_views * GS_GRAD2D_ROWS * (uint64_t)n, 0u, s) != hipSuccess)
             return GS_ERR_HIP;
     }
     double* partial = (double*)ws;
+    uint32_t* order = (uint32_t*)(partial + a.n_blocks);
+    hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(ORDER_THREADS), 0, s, ranges, n_tiles, order);
+    if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     hipLaunchKernelGGL(k_raster_fwd_bwd_l1, dim3((unsigned)a.n_blocks), dim3(RW_THREADS), 0, s, rec, n, ranges,
                        vals, masks, a.dc.width, a.dc.height, a.dc.tiles_x, a.T, a.row0, bg[0], bg[1], bg[2], target,
-                       scale, image, T_final, n_contrib, dL_dimage, partial, grad2d);
+                       scale, image, T_final, n_contrib, dL_dimage, partial, grad2d, order);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     return loss_from_partials(partial, a.n_blocks, (double)scale, loss, accumulate != 0, s) == hipSuccess ? GS_OK
                                                                                                            : GS_ERR_HIP;

@@ -59,8 +59,9 @@ class Buffers:
         self.loss = torch.zeros(1, dtype=torch.float64, device=dev)
         self.grad2d = torch.empty(V * L.GS_GRAD2D_ROWS * n, dtype=torch.float32, device=dev)
         self.overflow = torch.zeros(1, dtype=torch.int32, device=dev)
-        self.fwd_l1_ws = torch.empty(L.rasterize_fwd_l1_workspace_bytes(V, self.W, self.H), dtype=torch.uint8,
-                                     device=dev)
+        self.fwd_l1_ws = torch.empty(max(L.rasterize_fwd_l1_workspace_bytes(V, self.W, self.H),
+                                         L.rasterize_fwd_bwd_l1_workspace_bytes(V, self.W, self.H)),
+                                     dtype=torch.uint8, device=dev)
         self.end_bit = L.sort_end_bit(V, self.T)
         self.capacity = 0
         self.allocated_for = None

@@ -367,10 +367,16 @@ gs_status gs_rasterize_bwd(const float* rec, int64_t n, const uint32_t* ranges,
  *   loss       device double: overwritten, or added to when `accumulate`
  *   grad2d     [V][n][9] fp32 as in gs_rasterize_bwd: zeroed first unless
  *              `accumulate`
- *   ws         device workspace of gs_rasterize_fwd_l1_workspace_bytes(...)
+ *   ws         device workspace of gs_rasterize_fwd_bwd_l1_workspace_bytes(...):
+ *              the per-quarter loss partials and the order in which the pass
+ *              takes the tiles (longest lists first)
  * Errors: as gs_rasterize_fwd, plus null target / loss / ws / grad2d (n > 0)
  * or a small workspace.
  */
+/* Workspace of gs_rasterize_fwd_bwd_l1 (bytes): one double per 8x8 quarter
+ * and one 32-bit tile index per tile of every view; 0 on invalid sizes. */
+size_t gs_rasterize_fwd_bwd_l1_workspace_bytes(int32_t n_views, int32_t width, int32_t height);
+
 gs_status gs_rasterize_fwd_bwd_l1(const float* rec, int64_t n, const uint32_t* ranges,
                                   const uint32_t* vals, const uint16_t* masks,
                                   const gs_camera* cams, int32_t n_views, int32_t row0,

@@ -130,7 +130,9 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert lib.gs_rasterize_bwd(fake, 10, fake, fake, fake, cams, 0, 0, 16, bg, fake, fake, fake, fake, 0, None) == INV
     assert lib.gs_rasterize_bwd(fake, 10, fake, fake, None, cams, 1, 0, 16, bg, fake, fake, fake, fake, 0, None) == INV
     f2 = lib.gs_rasterize_fwd_bwd_l1
-    ok = (fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, fake, 1.0, None, None, None, None, fake, fake, 0, fake, qws,
+    fws = L.rasterize_fwd_bwd_l1_workspace_bytes(1, 256, 256)
+    assert fws == 16 * 16 * (4 * 8 + 4) and L.rasterize_fwd_bwd_l1_workspace_bytes(1, 0, 256) == 0
+    ok = (fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, fake, 1.0, None, None, None, None, fake, fake, 0, fake, fws,
           None)
 
     def fb(**kw):
@@ -143,7 +145,7 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert fb(a16=None) == INV  # loss
     assert fb(a17=None) == INV  # grad2d
     assert fb(a19=None) == INV  # workspace
-    assert fb(a20=qws - 8) == INV
+    assert fb(a20=fws - 4) == INV
     assert fb(a4=None) == INV  # masks
     assert fb(a7=8, a8=9) == INV  # window outside the image
     assert fb(a6=0) == INV  # no views
