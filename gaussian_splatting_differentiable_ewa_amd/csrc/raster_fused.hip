@@ -14,12 +14,17 @@ namespace gs {
 constexpr size_t FUSED_LDS_BYTES = sizeof(FwdLds) > sizeof(BwdLds) ? sizeof(FwdLds) : sizeof(BwdLds);
 
 // The order in which the pass takes the (view, tile)s: by list length, longest
-// first, in ORDER_CLASSES classes (ties in no particular order). A quarter's
-// time grows with its tile's list, and in tile order the quarters of long
-// lists that start late finish long after the rest. One workgroup: counts
-// per class, their prefix, then each tile's slot (LDS atomics).
+// first, in ORDER_CLASSES classes, tile order within a class. A quarter's time
+// grows with its tile's list, and in tile order the quarters of long lists
+// that start late finish long after the rest. A counting sort over segments of
+// ORDER_SEG tiles: k_order_count counts each segment's classes, k_order_place
+// adds the counts of the classes before and of the segments before, and ranks
+// the segment's tiles by ballots (tile = segment base + 256 r + 64 wave + lane,
+// so rank order is tile order).
 constexpr int ORDER_CLASSES = 8;
-constexpr int ORDER_THREADS = 1024;
+constexpr int ORDER_THREADS = 256;
+constexpr int ORDER_R = 4;  // tiles per thread
+constexpr int ORDER_SEG = ORDER_THREADS * ORDER_R;
 
 __device__ __forceinline__ int order_class(uint32_t len)
 {
@@ -30,30 +35,89 @@ __device__ __forceinline__ int order_class(uint32_t len)
     return c;
 }
 
-__global__ __launch_bounds__(ORDER_THREADS) void k_tile_order(const uint32_t* __restrict__ ranges, int64_t n_tiles,
-                                                             uint32_t* __restrict__ order)
+// the classes of this thread's ORDER_R tiles (ORDER_CLASSES past the end)
+__device__ __forceinline__ void segment_classes(const uint32_t* __restrict__ ranges, int64_t n_tiles,
+                                                int (&c)[ORDER_R])
+{
+    const int64_t base = (int64_t)blockIdx.x * ORDER_SEG + threadIdx.x;
+    uint2 rg[ORDER_R];
+#pragma unroll
+    for (int r = 0; r < ORDER_R; ++r) {
+        const int64_t t = base + r * ORDER_THREADS;
+        rg[r] = t < n_tiles ? *(const uint2*)(ranges + 2 * t) : make_uint2(0u, 0u);
+    }
+#pragma unroll
+    for (int r = 0; r < ORDER_R; ++r)
+        c[r] = base + r * ORDER_THREADS < n_tiles ? order_class(rg[r].y - rg[r].x) : ORDER_CLASSES;
+}
+
+// table[segment][class]: the segment's tiles of each class
+__global__ __launch_bounds__(ORDER_THREADS) void k_order_count(const uint32_t* __restrict__ ranges, int64_t n_tiles,
+                                                              uint32_t* __restrict__ table)
 {
     __shared__ uint32_t cnt[ORDER_CLASSES];
     if (threadIdx.x < ORDER_CLASSES) cnt[threadIdx.x] = 0u;
+    int c[ORDER_R];
+    segment_classes(ranges, n_tiles, c);
     __syncthreads();
-    for (int64_t t = threadIdx.x; t < n_tiles; t += ORDER_THREADS) {
-        const uint2 rg = *(const uint2*)(ranges + 2 * t);
-        atomicAdd(&cnt[order_class(rg.y - rg.x)], 1u);
+#pragma unroll
+    for (int k = 0; k < ORDER_CLASSES; ++k) {
+        uint32_t m = 0u;
+#pragma unroll
+        for (int r = 0; r < ORDER_R; ++r) m += (uint32_t)__popcll(ballot(c[r] == k));
+        if ((threadIdx.x & 63u) == 0u && m) atomicAdd(&cnt[k], m);
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t run = 0u;
-        for (int c = 0; c < ORDER_CLASSES; ++c) {
-            const uint32_t k = cnt[c];
-            cnt[c] = run;
-            run += k;
+    if (threadIdx.x < ORDER_CLASSES) table[(int64_t)blockIdx.x * ORDER_CLASSES + threadIdx.x] = cnt[threadIdx.x];
+}
+
+__global__ __launch_bounds__(ORDER_THREADS) void k_order_place(const uint32_t* __restrict__ ranges, int64_t n_tiles,
+                                                              const uint32_t* __restrict__ table, uint32_t n_seg,
+                                                              uint32_t* __restrict__ order)
+{
+    constexpr int W = ORDER_THREADS / 64;
+    __shared__ uint32_t tot[ORDER_CLASSES], before[ORDER_CLASSES];
+    __shared__ uint32_t cnt[ORDER_R][W][ORDER_CLASSES];  // then: first slot of each (r, wave, class)
+    if (threadIdx.x < ORDER_CLASSES) tot[threadIdx.x] = before[threadIdx.x] = 0u;
+    int c[ORDER_R];
+    segment_classes(ranges, n_tiles, c);
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < n_seg * ORDER_CLASSES; i += ORDER_THREADS) {
+        const uint32_t v = table[i], k = i % ORDER_CLASSES;
+        if (v) {
+            atomicAdd(&tot[k], v);
+            if (i / ORDER_CLASSES < blockIdx.x) atomicAdd(&before[k], v);
+        }
+    }
+    const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+    uint32_t rank[ORDER_R];
+#pragma unroll
+    for (int r = 0; r < ORDER_R; ++r) {
+        rank[r] = 0u;
+#pragma unroll
+        for (int k = 0; k < ORDER_CLASSES; ++k) {
+            const uint64_t m = ballot(c[r] == k);
+            if (c[r] == k) rank[r] = mask_rank(m);
+            if (lane == 0u) cnt[r][w][k] = (uint32_t)__popcll(m);
         }
     }
     __syncthreads();
-    for (int64_t t = threadIdx.x; t < n_tiles; t += ORDER_THREADS) {
-        const uint2 rg = *(const uint2*)(ranges + 2 * t);
-        order[atomicAdd(&cnt[order_class(rg.y - rg.x)], 1u)] = (uint32_t)t;
+    if (threadIdx.x < ORDER_CLASSES) {
+        const int k = (int)threadIdx.x;
+        uint32_t run = before[k];
+        for (int j = 0; j < k; ++j) run += tot[j];
+        for (int r = 0; r < ORDER_R; ++r)
+            for (int v = 0; v < W; ++v) {
+                const uint32_t x = cnt[r][v][k];
+                cnt[r][v][k] = run;
+                run += x;
+            }
     }
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * ORDER_SEG + threadIdx.x;
+#pragma unroll
+    for (int r = 0; r < ORDER_R; ++r)
+        if (c[r] < ORDER_CLASSES) order[cnt[r][w][c[r]] + rank[r]] = (uint32_t)(base + r * ORDER_THREADS);
 }
 
 // image, T_final, n_contrib and dL may each be null (not written).
@@ -116,11 +180,18 @@ using namespace gs;
 
 extern "C" {
 
+// per quarter a loss partial; per tile its slot in the order; per segment of
+// ORDER_SEG tiles its class counts
+static size_t fused_ws_bytes(int64_t tiles)
+{
+    const int64_t segs = (tiles + ORDER_SEG - 1) / ORDER_SEG;
+    return (size_t)(tiles * 4 * sizeof(double) + tiles * sizeof(uint32_t) + segs * ORDER_CLASSES * sizeof(uint32_t));
+}
+
 size_t gs_rasterize_fwd_bwd_l1_workspace_bytes(int32_t n_views, int32_t width, int32_t height)
 {
     if (n_views < 1 || n_views > GS_MAX_VIEWS || width <= 0 || height <= 0) return 0;
-    const int64_t tiles = (int64_t)n_views * gs_tiles_x(width) * gs_tiles_y(height);
-    return (size_t)(tiles * 4 * sizeof(double) + tiles * sizeof(uint32_t));
+    return fused_ws_bytes((int64_t)n_views * gs_tiles_x(width) * gs_tiles_y(height));
 }
 
 gs_status gs_rasterize_fwd_bwd_l1(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
@@ -133,8 +204,7 @@ gs_status gs_rasterize_fwd_bwd_l1(const float* rec, int64_t n, const uint32_t* r
     if (!raster_args(rec, n, ranges, vals, masks, cams, n_views, row0, rows, bg, a)) return GS_ERR_INVALID_ARGUMENT;
     if (!target || !loss || !ws || (n > 0 && !grad2d)) return GS_ERR_INVALID_ARGUMENT;
     const int64_t n_tiles = a.n_blocks / 4;
-    if (ws_bytes < (size_t)a.n_blocks * sizeof(double) + (size_t)n_tiles * sizeof(uint32_t))
-        return GS_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < fused_ws_bytes(n_tiles)) return GS_ERR_INVALID_ARGUMENT;
     hipStream_t s = (hipStream_t)stream;
     if (!accumulate && n > 0) {
         if (fill_u32((uint32_t*)grad2d, (uint64_t)n_views * GS_GRAD2D_ROWS * (uint64_t)n, 0u, s) != hipSuccess)
@@ -142,7 +212,10 @@ gs_status gs_rasterize_fwd_bwd_l1(const float* rec, int64_t n, const uint32_t* r
     }
     double* partial = (double*)ws;
     uint32_t* order = (uint32_t*)(partial + a.n_blocks);
-    hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(ORDER_THREADS), 0, s, ranges, n_tiles, order);
+    uint32_t* table = order + n_tiles;
+    const uint32_t n_seg = (uint32_t)((n_tiles + ORDER_SEG - 1) / ORDER_SEG);
+    hipLaunchKernelGGL(k_order_count, dim3(n_seg), dim3(ORDER_THREADS), 0, s, ranges, n_tiles, table);
+    hipLaunchKernelGGL(k_order_place, dim3(n_seg), dim3(ORDER_THREADS), 0, s, ranges, n_tiles, table, n_seg, order);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     hipLaunchKernelGGL(k_raster_fwd_bwd_l1, dim3((unsigned)a.n_blocks), dim3(RW_THREADS), 0, s, rec, n, ranges,
                        vals, masks, a.dc.width, a.dc.height, a.dc.tiles_x, a.T, a.row0, bg[0], bg[1], bg[2], target,

@@ -187,13 +187,25 @@ __global__ __launch_bounds__(256) void k_tl_ranges(const uint32_t* __restrict__ 
                                                    uint32_t* __restrict__ big)
 {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (t >= n_tiles) return;
-    const uint32_t s = (uint32_t)min((uint64_t)starts[t], capacity), e = (uint32_t)min((uint64_t)starts[t + 1], capacity);
-    *(uint2*)(ranges + 2 * t) = e > s ? make_uint2(s, e) : make_uint2(0u, 0u);
-    if (e > s && e - s > (uint32_t)WV_CAP) {
-        const int c = tl_class(e - s);
-        const uint32_t k = atomicAdd(big + c, 1u);
-        big[TL_CLASSES + (int64_t)c * n_tiles + k] = (uint32_t)t;
+    const bool ok = t < n_tiles;
+    uint32_t s = 0u, e = 0u;
+    if (ok) {
+        s = (uint32_t)min((uint64_t)starts[t], capacity);
+        e = (uint32_t)min((uint64_t)starts[t + 1], capacity);
+        *(uint2*)(ranges + 2 * t) = e > s ? make_uint2(s, e) : make_uint2(0u, 0u);
+    }
+    // one counter atomic per class and wave (thousands of long tiles on four
+    // counters serialise otherwise)
+    const int c = ok && e > s && e - s > (uint32_t)WV_CAP ? tl_class(e - s) : TL_CLASSES;
+#pragma unroll
+    for (int k = 0; k < TL_CLASSES; ++k) {
+        const uint64_t m = ballot(c == k);
+        if (!m) continue;
+        const uint32_t lead = (uint32_t)__ffsll((unsigned long long)m) - 1u;
+        uint32_t first = 0u;
+        if (lane_id() == lead) first = atomicAdd(big + k, (uint32_t)__popcll(m));
+        first = __shfl(first, (int)lead);
+        if (c == k) big[TL_CLASSES + (int64_t)k * n_tiles + first + mask_rank(m)] = (uint32_t)t;
     }
 }
 

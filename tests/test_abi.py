@@ -131,7 +131,7 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert lib.gs_rasterize_bwd(fake, 10, fake, fake, None, cams, 1, 0, 16, bg, fake, fake, fake, fake, 0, None) == INV
     f2 = lib.gs_rasterize_fwd_bwd_l1
     fws = L.rasterize_fwd_bwd_l1_workspace_bytes(1, 256, 256)
-    assert fws == 16 * 16 * (4 * 8 + 4) and L.rasterize_fwd_bwd_l1_workspace_bytes(1, 0, 256) == 0
+    assert fws == 16 * 16 * (4 * 8 + 4) + 8 * 4 and L.rasterize_fwd_bwd_l1_workspace_bytes(1, 0, 256) == 0
     ok = (fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, fake, 1.0, None, None, None, None, fake, fake, 0, fake, fws,
           None)
 
