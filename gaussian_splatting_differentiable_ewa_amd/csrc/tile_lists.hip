@@ -182,11 +182,15 @@ __device__ __forceinline__ int tl_class(uint32_t len)
 // by length class: class c's count in big[c] (zeroed by k_bin_colscan), its
 // tiles in big[TL_CLASSES + c n_tiles + k], so that k_tl_sort takes the
 // longest first.
-__global__ __launch_bounds__(256) void k_tl_ranges(const uint32_t* __restrict__ starts, int64_t n_tiles,
-                                                   uint64_t capacity, uint32_t* __restrict__ ranges,
-                                                   uint32_t* __restrict__ big)
+constexpr int TR_THREADS = 1024;
+
+__global__ __launch_bounds__(TR_THREADS) void k_tl_ranges(const uint32_t* __restrict__ starts, int64_t n_tiles,
+                                                          uint64_t capacity, uint32_t* __restrict__ ranges,
+                                                          uint32_t* __restrict__ big)
 {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    __shared__ uint32_t cnt[TL_CLASSES];  // the block's tiles per class, then its first slot per class
+    if (threadIdx.x < TL_CLASSES) cnt[threadIdx.x] = 0u;
+    const int64_t t = (int64_t)blockIdx.x * TR_THREADS + threadIdx.x;
     const bool ok = t < n_tiles;
     uint32_t s = 0u, e = 0u;
     if (ok) {
@@ -194,19 +198,25 @@ __global__ __launch_bounds__(256) void k_tl_ranges(const uint32_t* __restrict__ 
         e = (uint32_t)min((uint64_t)starts[t + 1], capacity);
         *(uint2*)(ranges + 2 * t) = e > s ? make_uint2(s, e) : make_uint2(0u, 0u);
     }
-    // one counter atomic per class and wave (thousands of long tiles on four
-    // counters serialise otherwise)
+    // one device atomic per class and block (thousands of long tiles on four
+    // counters serialise otherwise): LDS slots per wave, then the block's base
     const int c = ok && e > s && e - s > (uint32_t)WV_CAP ? tl_class(e - s) : TL_CLASSES;
+    __syncthreads();
+    uint32_t slot = 0u;
 #pragma unroll
     for (int k = 0; k < TL_CLASSES; ++k) {
         const uint64_t m = ballot(c == k);
         if (!m) continue;
         const uint32_t lead = (uint32_t)__ffsll((unsigned long long)m) - 1u;
         uint32_t first = 0u;
-        if (lane_id() == lead) first = atomicAdd(big + k, (uint32_t)__popcll(m));
+        if (lane_id() == lead) first = atomicAdd(&cnt[k], (uint32_t)__popcll(m));
         first = __shfl(first, (int)lead);
-        if (c == k) big[TL_CLASSES + (int64_t)k * n_tiles + first + mask_rank(m)] = (uint32_t)t;
+        if (c == k) slot = first + mask_rank(m);
     }
+    __syncthreads();
+    if (threadIdx.x < TL_CLASSES && cnt[threadIdx.x]) cnt[threadIdx.x] = atomicAdd(big + threadIdx.x, cnt[threadIdx.x]);
+    __syncthreads();
+    if (c < TL_CLASSES) big[TL_CLASSES + (int64_t)c * n_tiles + cnt[c] + slot] = (uint32_t)t;
 }
 
 __global__ __launch_bounds__(256) void k_bin_fill(const float* __restrict__ rec, const uint16_t* __restrict__ rect,
@@ -886,8 +896,8 @@ gs_status gs_tile_lists(const float* rec, const uint16_t* rect, int64_t n, int32
                        totals, big);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     if (scan_u32(totals, totals, (uint64_t)n_tiles, total, w + L.scan, s) != hipSuccess) return GS_ERR_HIP;
-    hipLaunchKernelGGL(k_tl_ranges, dim3(grid_for((uint64_t)n_tiles, 256)), dim3(256), 0, s, totals, n_tiles, capacity,
-                       ranges, big);
+    hipLaunchKernelGGL(k_tl_ranges, dim3(grid_for((uint64_t)n_tiles, TR_THREADS)), dim3(TR_THREADS), 0, s, totals,
+                       n_tiles, capacity, ranges, big);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     if (n == 0) return GS_OK;
     hipLaunchKernelGGL(k_bin_fill, dim3(bin_blocks), dim3(256), 0, s, rec, rect, G, table, totals, pairs, capacity,
