@@ -74,11 +74,11 @@ def lib():
             "gs_tile_lists_workspace_bytes": ([_I64, _I32, _I32, _I32, _U64], _SZ),
             "gs_rasterize_fwd_l1_workspace_bytes": ([_I32, _I32, _I32], _SZ),
             "gs_rasterize_fwd_bwd_l1_workspace_bytes": ([_I32, _I32, _I32], _SZ),
-            "gs_preprocess": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+            "gs_preprocess": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
             "gs_emit_intersections": ([_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _U64, _P, _P], ctypes.c_int),
             "gs_sort_keys": ([_P, _P, _P, _P, _U64, _I32, _P, _SZ, _P, _P], ctypes.c_int),
             "gs_tile_ranges": ([_P, _U64, _I64, _P, _P], ctypes.c_int),
-            "gs_tile_lists": ([_P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P, _U64, _P, _P, _P, _SZ, _P],
+            "gs_tile_lists": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P, _U64, _P, _P, _P, _SZ, _P],
                               ctypes.c_int),
             "gs_tile_masks_workspace_bytes": ([_U64], _SZ),
             "gs_tile_masks": ([_P, _I64, _P, _P, _U64, _P, _I32, _P, _P, _SZ, _P], ctypes.c_int),
@@ -171,9 +171,9 @@ def tile_lists_workspace_bytes(n: int, n_views: int, width: int, height: int, ca
 
 
 # ---- the step ----------------------------------------------------------------
-def gs_preprocess(params, n, sh_degree, cams, rec, rect, offsets, total, ws, stream=None):
+def gs_preprocess(params, n, sh_degree, cams, rec, rect, offsets, total, ws, stream=None, depth=None):
     cc = cameras(cams)
-    _check(lib().gs_preprocess(_ptr(params), n, sh_degree, cc, len(cams), _ptr(rec), _ptr(rect),
+    _check(lib().gs_preprocess(_ptr(params), n, sh_degree, cc, len(cams), _ptr(rec), _ptr(rect), _ptr(depth),
                                _ptr(offsets), _ptr(total), _ptr(ws), ws.numel() * ws.element_size(),
                                _stream(stream)), "gs_preprocess")
 
@@ -194,10 +194,11 @@ def _window(height, rows):
 
 
 def gs_tile_lists(rec, rect, n, n_views, width, height, vals, capacity, ranges, overflow, ws, masks=None,
-                  row0=0, rows=None, stream=None):
+                  row0=0, rows=None, stream=None, depth=None):
     """masks (optional): the entries' sub-block masks, as gs_tile_masks;
-    row0, rows: the window of tile rows (the whole image by default)."""
-    _check(lib().gs_tile_lists(_ptr(rec), _ptr(rect), n, n_views, width, height, row0, _window(height, rows),
+    row0, rows: the window of tile rows (the whole image by default);
+    depth (optional): gs_preprocess's compact depths."""
+    _check(lib().gs_tile_lists(_ptr(rec), _ptr(rect), _ptr(depth), n, n_views, width, height, row0, _window(height, rows),
                                _ptr(vals), _ptr(masks), capacity,
                                _ptr(ranges), _ptr(overflow), _ptr(ws), ws.numel() * ws.element_size(),
                                _stream(stream)), "gs_tile_lists")

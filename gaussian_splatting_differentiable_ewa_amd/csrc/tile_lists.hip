@@ -220,7 +220,7 @@ __global__ __launch_bounds__(TR_THREADS) void k_tl_ranges(const uint32_t* __rest
 }
 
 __global__ __launch_bounds__(256) void k_bin_fill(const float* __restrict__ rec, const uint16_t* __restrict__ rect,
-                                                  const BinGrid G, const uint32_t* __restrict__ table,
+                                                  const float* __restrict__ depth, const BinGrid G, const uint32_t* __restrict__ table,
                                                   const uint32_t* __restrict__ starts, uint2* __restrict__ pairs,
                                                   uint64_t capacity, int32_t* __restrict__ overflow)
 {
@@ -241,7 +241,9 @@ __global__ __launch_bounds__(256) void k_bin_fill(const float* __restrict__ rec,
             const int64_t l = l4 + 256 * k, g = bin_gauss(G, B, l), idx = B.v * G.n + g;
             const bool in = l < B.len && g < G.n;
             rr[k] = in ? *(const uint2*)(rect + 4 * idx) : make_uint2(0u, 0u);
-            zb[k] = in ? __float_as_uint(rec[idx * GS_REC_FLOATS + GS_REC_DEPTH]) : 0u;
+            // the compact depths when given: one float of each 48-byte
+            // record would touch every cache line of the records
+            zb[k] = !in ? 0u : depth ? __float_as_uint(depth[idx]) : __float_as_uint(rec[idx * GS_REC_FLOATS + GS_REC_DEPTH]);
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -861,7 +863,7 @@ size_t gs_tile_lists_workspace_bytes(int64_t n, int32_t n_views, int32_t width, 
     return tl_layout(bin_grid(n, n_views, width, height), n_views, capacity).bytes;
 }
 
-gs_status gs_tile_lists(const float* rec, const uint16_t* rect, int64_t n, int32_t n_views, int32_t width,
+gs_status gs_tile_lists(const float* rec, const uint16_t* rect, const float* depth, int64_t n, int32_t n_views, int32_t width,
                         int32_t height, int32_t row0, int32_t rows, uint32_t* vals, uint16_t* masks,
                         uint64_t capacity, uint32_t* ranges, int32_t* overflow, void* ws, size_t ws_bytes,
                         void* stream)
@@ -900,8 +902,8 @@ gs_status gs_tile_lists(const float* rec, const uint16_t* rect, int64_t n, int32
                        n_tiles, capacity, ranges, big);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     if (n == 0) return GS_OK;
-    hipLaunchKernelGGL(k_bin_fill, dim3(bin_blocks), dim3(256), 0, s, rec, rect, G, table, totals, pairs, capacity,
-                       overflow);
+    hipLaunchKernelGGL(k_bin_fill, dim3(bin_blocks), dim3(256), 0, s, rec, rect, depth, G, table, totals, pairs,
+                       capacity, overflow);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     MaskOut mo;
     mo.masks = masks;

@@ -48,6 +48,7 @@ class Buffers:
         V, n, dev = self.V, self.n, device
         self.rec = torch.empty(V * n * L.GS_REC_FLOATS, dtype=torch.float32, device=dev)
         self.rect = torch.empty(V * n * 4, dtype=torch.int16, device=dev)
+        self.depth = torch.empty(V * n, dtype=torch.float32, device=dev)  # compact depths for the list builder
         self.offsets = torch.empty(V * n + 1, dtype=torch.int32, device=dev)
         self.total = torch.zeros(1, dtype=torch.int64, device=dev)
         self.pre_ws = torch.empty(L.preprocess_workspace_bytes(n, V), dtype=torch.uint8, device=dev)
@@ -107,7 +108,7 @@ class Buffers:
     # ---- stages ------------------------------------------------------------
     def preprocess(self, params):
         L.gs_preprocess(params, self.n, self.sh_degree, self.cams, self.rec, self.rect, self.offsets,
-                        self.total, self.pre_ws)
+                        self.total, self.pre_ws, depth=self.depth)
 
     def lists_without_count(self) -> bool:
         """Whether the lists can be built before K is known on the host."""
@@ -133,7 +134,7 @@ class Buffers:
         """The lists and ranges alone (see ``intersections``)."""
         if not read_count and self.lists_without_count():
             L.gs_tile_lists(self.rec, self.rect, self.n, self.V, self.W, self.H, self.vals, self.capacity,
-                            self.ranges, self.overflow, self.tl_ws, masks=self.masks)
+                            self.ranges, self.overflow, self.tl_ws, masks=self.masks, depth=self.depth)
             return
         self.K = int(self.total.item())
         if self.K >= 2 ** 32:
@@ -144,7 +145,7 @@ class Buffers:
         if self.path == "binned":
             self.sorted_in_alt = False
             L.gs_tile_lists(self.rec, self.rect, self.n, self.V, self.W, self.H, self.vals, self.capacity,
-                            self.ranges, self.overflow, self.tl_ws, masks=self.masks)
+                            self.ranges, self.overflow, self.tl_ws, masks=self.masks, depth=self.depth)
             return
         L.gs_emit_intersections(self.rec, self.rect, self.offsets, self.n, self.V, self.W, self.H,
                                 self.keys, self.vals, self.capacity, self.overflow)
@@ -322,7 +323,7 @@ class TrainStep:
             rows = min(self.band_rows, b.TY - row0)
             while True:
                 L.gs_tile_lists(b.rec, b.rect, b.n, b.V, b.W, b.H, b.vals, b.capacity, b.ranges, b.overflow, b.tl_ws,
-                                masks=b.masks, row0=row0, rows=rows)
+                                masks=b.masks, row0=row0, rows=rows, depth=b.depth)
                 if int(b.overflow.item()) == 0:
                     break
                 b.ensure_capacity(2 * b.capacity, slack=1.0)

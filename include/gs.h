@@ -148,6 +148,9 @@ size_t gs_sort_workspace_bytes(uint64_t n_keys);
  *   cams     host array of n_views cameras, all of one image size
  *   rec      out [n_views][n][12] fp32 (see GS_REC_*)
  *   rect     out [n_views][n][4] uint16 x0 y0 x1 y1 (all 0 when culled)
+ *   depth    out [n_views][n] fp32, or NULL: the view-space depth of each
+ *            entry that is not culled (GS_REC_DEPTH of its record; culled
+ *            entries are not written), a compact copy for gs_tile_lists
  *   offsets  out [n_views * n + 1] uint32: offsets[i] = sum of the tile counts
  *            of entries before i (low 32 bits); the count of entry i is the
  *            area of its rectangle
@@ -158,8 +161,9 @@ size_t gs_sort_workspace_bytes(uint64_t n_keys);
  * n_views * tiles_per_view >= 2^31.
  */
 gs_status gs_preprocess(const float* params, int64_t n, int32_t sh_degree, const gs_camera* cams,
-                        int32_t n_views, float* rec, uint16_t* rect, uint32_t* offsets,
-                        uint64_t* total, void* ws, size_t ws_bytes, void* stream);
+                        int32_t n_views, float* rec, uint16_t* rect, float* depth,
+                        uint32_t* offsets, uint64_t* total, void* ws, size_t ws_bytes,
+                        void* stream);
 
 /*
  * gs_emit_intersections -- one key per (view, Gaussian, tile) overlap, the
@@ -210,6 +214,8 @@ size_t gs_tile_lists_workspace_bytes(int64_t n, int32_t n_views, int32_t width, 
  * chunk of Gaussians), scanning the counts into ranges, filling every tile's
  * slots and sorting each tile's slots by (depth, Gaussian index) on its own.
  *   rec, rect, n, n_views, width, height   as for gs_emit_intersections
+ *   depth      the depth output of gs_preprocess, or NULL (then read from
+ *              the records): the same lists either way, with less traffic
  *   row0, rows the window of tile rows [row0, row0 + rows) the lists cover
  *              (0 and gs_tiles_y(height) for the whole image): only
  *              intersections with its tiles are listed, so that an image can
@@ -229,7 +235,7 @@ size_t gs_tile_lists_workspace_bytes(int64_t n, int32_t n_views, int32_t width, 
  * a window outside the tile rows
  * or more than 8192 tile columns.
  */
-gs_status gs_tile_lists(const float* rec, const uint16_t* rect, int64_t n, int32_t n_views,
+gs_status gs_tile_lists(const float* rec, const uint16_t* rect, const float* depth, int64_t n, int32_t n_views,
                         int32_t width, int32_t height, int32_t row0, int32_t rows, uint32_t* vals,
                         uint16_t* masks, uint64_t capacity, uint32_t* ranges, int32_t* overflow,
                         void* ws, size_t ws_bytes, void* stream);

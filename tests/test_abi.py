@@ -62,18 +62,18 @@ def test_invalid_arguments_rejected_on_host(lib):
     fake = ctypes.c_void_p(16)  # never dereferenced: validation fails first
     ws = ctypes.c_size_t(1 << 20)
     # gs_preprocess
-    assert lib.gs_preprocess(fake, -1, 0, cams, 1, fake, fake, fake, fake, fake, ws, None) == INV
-    assert lib.gs_preprocess(fake, 10, 4, cams, 1, fake, fake, fake, fake, fake, ws, None) == INV
-    assert lib.gs_preprocess(fake, 10, 0, cams, 0, fake, fake, fake, fake, fake, ws, None) == INV
-    assert lib.gs_preprocess(fake, 10, 0, cams, 17, fake, fake, fake, fake, fake, ws, None) == INV
-    assert lib.gs_preprocess(fake, 10, 0, cams, 1, fake, fake, None, fake, fake, ws, None) == INV
-    assert lib.gs_preprocess(fake, 10, 0, cams, 1, fake, fake, fake, fake, fake, 0, None) == INV
+    assert lib.gs_preprocess(fake, -1, 0, cams, 1, fake, fake, None, fake, fake, fake, ws, None) == INV
+    assert lib.gs_preprocess(fake, 10, 4, cams, 1, fake, fake, None, fake, fake, fake, ws, None) == INV
+    assert lib.gs_preprocess(fake, 10, 0, cams, 0, fake, fake, None, fake, fake, fake, ws, None) == INV
+    assert lib.gs_preprocess(fake, 10, 0, cams, 17, fake, fake, None, fake, fake, fake, ws, None) == INV
+    assert lib.gs_preprocess(fake, 10, 0, cams, 1, fake, fake, None, None, fake, fake, ws, None) == INV
+    assert lib.gs_preprocess(fake, 10, 0, cams, 1, fake, fake, None, fake, fake, fake, 0, None) == INV
     two = L.cameras([_cam(), _cam(width=128)])
-    assert lib.gs_preprocess(fake, 10, 0, two, 2, fake, fake, fake, fake, fake, ws, None) == INV
+    assert lib.gs_preprocess(fake, 10, 0, two, 2, fake, fake, None, fake, fake, fake, ws, None) == INV
     bad_f = L.cameras([_cam(fx=0.0)])
-    assert lib.gs_preprocess(fake, 10, 0, bad_f, 1, fake, fake, fake, fake, fake, ws, None) == INV
+    assert lib.gs_preprocess(fake, 10, 0, bad_f, 1, fake, fake, None, fake, fake, fake, ws, None) == INV
     huge = L.cameras([_cam(width=16 * 70000)])
-    assert lib.gs_preprocess(fake, 10, 0, huge, 1, fake, fake, fake, fake, fake, ws, None) == INV
+    assert lib.gs_preprocess(fake, 10, 0, huge, 1, fake, fake, None, fake, fake, fake, ws, None) == INV
     # gs_emit_intersections
     assert lib.gs_emit_intersections(fake, fake, fake, -1, 1, 256, 256, fake, fake, 10, fake, None) == INV
     assert lib.gs_emit_intersections(fake, fake, fake, 10, 1, 0, 256, fake, fake, 10, fake, None) == INV
@@ -90,17 +90,17 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert alt.value == 0
     # gs_tile_lists
     big = ctypes.c_size_t(1 << 40)
-    assert lib.gs_tile_lists(fake, fake, -1, 1, 256, 256, 0, 16, fake, None, 10, fake, fake, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, 10, 0, 256, 256, 0, 16, fake, None, 10, fake, fake, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 0, 0, 16, fake, None, 10, fake, fake, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, 0, 16, fake, None, 10, None, fake, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, 0, 16, fake, None, 10, fake, None, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, 0, 16, None, None, 10, fake, fake, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, 0, 16, fake, None, 1 << 32, fake, fake, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, None, -1, 1, 256, 256, 0, 16, fake, None, 10, fake, fake, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, None, 10, 0, 256, 256, 0, 16, fake, None, 10, fake, fake, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, None, 10, 1, 256, 0, 0, 16, fake, None, 10, fake, fake, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, None, 10, 1, 256, 256, 0, 16, fake, None, 10, None, fake, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, None, 10, 1, 256, 256, 0, 16, fake, None, 10, fake, None, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, None, 10, 1, 256, 256, 0, 16, None, None, 10, fake, fake, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, None, 10, 1, 256, 256, 0, 16, fake, None, 1 << 32, fake, fake, fake, big, None) == INV
     need = L.tile_lists_workspace_bytes(10, 1, 256, 256, 10)
     assert need > 0 and L.tile_lists_workspace_bytes(10, 0, 256, 256, 10) == 0
     assert L.tile_lists_workspace_bytes(10, 1, 16 * 8193, 256, 10) == 0
-    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, 0, 16, fake, None, 10, fake, fake, fake, need - 1, None) == INV
+    assert lib.gs_tile_lists(fake, fake, None, 10, 1, 256, 256, 0, 16, fake, None, 10, fake, fake, fake, need - 1, None) == INV
     # gs_tile_ranges
     assert lib.gs_tile_ranges(fake, 10, -1, fake, None) == INV
     assert lib.gs_tile_ranges(None, 10, 4, fake, None) == INV
@@ -119,7 +119,7 @@ def test_invalid_arguments_rejected_on_host(lib):
               None) == INV
     assert lib.gs_rasterize_fwd(fake, 10, fake, fake, fake, cams, 1, 0, 0, bg, fake, fake, fake, None) == INV
     assert lib.gs_rasterize_bwd(fake, 10, fake, fake, fake, cams, 1, -1, 4, bg, fake, fake, fake, fake, 0, None) == INV
-    assert lib.gs_tile_lists(fake, fake, 10, 1, 256, 256, 12, 5, fake, None, 10, fake, fake, fake, big, None) == INV
+    assert lib.gs_tile_lists(fake, fake, None, 10, 1, 256, 256, 12, 5, fake, None, 10, fake, fake, fake, big, None) == INV
     assert f1(fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, fake, 1.0, None, fake, fake, fake, fake, 0, None, qws, None) == INV
     assert f1(fake, 10, fake, fake, None, cams, 1, 0, 16, bg, fake, 1.0, None, fake, fake, fake, fake, 0, fake, qws, None) == INV
     assert lib.gs_rasterize_fwd(fake, 10, fake, fake, fake, cams, 1, 0, 16, None, fake, fake, fake, None) == INV

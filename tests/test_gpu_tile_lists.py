@@ -63,12 +63,17 @@ def test_tile_lists_match_oracle(seed, n, V, big, levels):
     print(f"[tile_lists] seed {seed}: K {K}, longest list {int((ranges[:, 1] - ranges[:, 0]).max())}", flush=True)
     rec_t = torch.from_numpy(rec.reshape(-1)).to(dev)
     rect_t = torch.from_numpy(rect.astype(np.int16).reshape(-1)).to(dev)
-    for cap in (K, K + 1000):
+    # the depths from the records, or from a compact copy (culled pairs hold
+    # garbage there, as preprocess leaves them)
+    depth = rec.reshape(-1, L.GS_REC_FLOATS)[:, L.REC_DEPTH].copy()
+    depth[vis.reshape(-1) == 0] = np.nan
+    depth_t = torch.from_numpy(depth).to(dev)
+    for cap, dep in ((K, None), (K + 1000, None), (K, depth_t)):
         out = torch.full((max(cap, 1),), -1, dtype=torch.int32, device=dev)
         rng_t = torch.full((V * TX * TY * 2,), -1, dtype=torch.int32, device=dev)
         ovf = torch.full((1,), 5, dtype=torch.int32, device=dev)
         ws = torch.empty(L.tile_lists_workspace_bytes(n, V, W, H, cap), dtype=torch.uint8, device=dev)
-        L.gs_tile_lists(rec_t, rect_t, n, V, W, H, out, cap, rng_t, ovf, ws)
+        L.gs_tile_lists(rec_t, rect_t, n, V, W, H, out, cap, rng_t, ovf, ws, depth=dep)
         torch.cuda.synchronize()
         assert int(ovf.item()) == 0
         assert np.array_equal(out.cpu().numpy()[:K].view(np.uint32), vals)
