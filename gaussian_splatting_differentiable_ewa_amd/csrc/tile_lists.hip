@@ -15,9 +15,10 @@
 //   4. k_bin_fill     the workgroups of step 1 again: LDS cursors start at
 //                     tile start + chunk prefix; each (Gaussian, tile) takes
 //                     the next slot (LDS atomic) and writes (depth bits, id);
-//   5. k_tl_sort_small one wave per tile of up to 64 entries: bitonic sort of
-//                     the 64-bit (depth bits, id) across the lanes;
-//      k_tl_sort_wave one wave per tile of up to 512 entries and
+//   5. one wave per tile of up to 64 entries: bitonic sort of the 64-bit
+//                     (depth bits, id) across the lanes; one wave per tile
+//                     of up to 512 entries (the workgroups of k_tl_sort past
+//                     its long tiles take both kinds, four tiles each); and
 //      k_tl_sort      one workgroup per longer tile: stable LSD radix sort by
 //                     the 32 depth bits (8-bit digits; digits equal across the
 //                     tile are skipped), in LDS for up to 4096 entries and
@@ -46,6 +47,7 @@ constexpr int GL_ROUNDS = GL_CHUNK / TL_THREADS;
 constexpr int TL_CLASSES = 4;  // length classes of the tiles k_tl_sort takes, longest first
 constexpr int WV_CAP = 512;  // entries one wave sorts alone
 constexpr int WV_ROUNDS = WV_CAP / 64;
+static_assert(4 * WV_CAP <= TL_CAP, "k_tl_sort's LDS holds four one-wave sorts");
 
 constexpr int BAND_TILES = 8192;  // LDS counters of one band of tile rows
 
@@ -315,21 +317,20 @@ __device__ __forceinline__ void write_ids_masks(const MaskOut& mo, int64_t tile_
     }
 }
 
-// Tiles of up to 64 entries, one wave each: a bitonic sort of the 64-bit
-// values (depth bits << 32 | id) across the lanes (absent lanes hold the
-// largest value and sort last).
-__global__ __launch_bounds__(256) void k_tl_sort_small(const uint32_t* __restrict__ ranges, int64_t n_tiles,
-                                                       const uint64_t* __restrict__ total_dev, uint64_t capacity,
-                                                       const uint2* __restrict__ pairs, uint32_t* __restrict__ vals,
-                                                       const MaskOut mo)
+// A tile of up to 64 entries, one wave: a bitonic sort of the 64-bit values
+// (depth bits << 32 | id) across the lanes (absent lanes hold the largest
+// value and sort last). Run by the workgroups of k_tl_sort past its long
+// tiles, four tiles each.
+__device__ __forceinline__ void tl_sort_small_tile(int64_t tile, uint32_t lane, const uint32_t* __restrict__ ranges,
+                                                   const uint64_t* __restrict__ total_dev, uint64_t capacity,
+                                                   const uint2* __restrict__ pairs, uint32_t* __restrict__ vals,
+                                                   const MaskOut& mo)
 {
-    const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (tile >= n_tiles) return;
     const uint2 rg = *(const uint2*)(ranges + 2 * tile);
     const uint64_t limit = min(capacity, *total_dev);
     const uint32_t start = rg.x, end = (uint32_t)min((uint64_t)rg.y, limit);
     if (end <= start || end - start > 64u) return;  // wave-uniform
-    const uint32_t n = end - start, lane = threadIdx.x & 63u;
+    const uint32_t n = end - start;
     uint64_t key = ~0ull;
     if (lane < n) {
         const uint2 p = pairs[start + lane];
@@ -419,29 +420,22 @@ __device__ __forceinline__ void tl_fix_ties(uint32_t n, KeyAt key_at, ValAt, Les
 }
 
 
-// Tiles of 65..512 entries, one wave each (four per workgroup, no barriers:
-// LDS is in order within a wave): the LSD radix sort of k_tl_sort on one
-// wave's registers and a private slice of LDS.
-__global__ __launch_bounds__(256) void k_tl_sort_wave(const uint32_t* __restrict__ ranges, int64_t n_tiles,
-                                                      const uint64_t* __restrict__ total_dev, uint64_t capacity,
-                                                      const uint2* __restrict__ pairs, uint32_t* __restrict__ vals,
-                                                      const MaskOut mo)
+// A tile of 65..512 entries, one wave alone (no barriers: LDS is in order
+// within a wave): the LSD radix sort of k_tl_sort on the wave's registers and
+// a private slice of LDS (sk, si: WV_CAP entries, cnt: 256 counters). Run by
+// the workgroups of k_tl_sort past its long tiles, four tiles each.
+__device__ __forceinline__ void tl_sort_wave_tile(int64_t tile, uint32_t lane, uint32_t* sk, uint16_t* si,
+                                                  uint32_t* cnt, const uint32_t* __restrict__ ranges,
+                                                  const uint64_t* __restrict__ total_dev, uint64_t capacity,
+                                                  const uint2* __restrict__ pairs, uint32_t* __restrict__ vals,
+                                                  const MaskOut& mo)
 {
-    __shared__ uint32_t s_key[4][WV_CAP];
-    __shared__ uint16_t s_idx[4][WV_CAP];
-    __shared__ uint32_t s_cnt[4][256];
-    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
-    const int64_t tile = (int64_t)blockIdx.x * 4 + wave;
-    if (tile >= n_tiles) return;
     const uint2 rg = *(const uint2*)(ranges + 2 * tile);
     const uint64_t limit = min(capacity, *total_dev);
     const uint32_t start = rg.x, end = (uint32_t)min((uint64_t)rg.y, limit);
     if (end <= start) return;
     const uint32_t n = end - start;
     if (n <= 64u || n > (uint32_t)WV_CAP) return;  // wave-uniform
-    uint32_t* sk = s_key[wave];
-    uint16_t* si = s_idx[wave];
-    uint32_t* cnt = s_cnt[wave];
     const uint32_t R = (n + 63u) / 64u;
     uint32_t key[WV_ROUNDS], idx[WV_ROUNDS], rank[WV_ROUNDS];
     uint32_t kor = 0u, kand = 0xffffffffu;
@@ -544,10 +538,13 @@ __global__ __launch_bounds__(256) void k_tl_sort_wave(const uint32_t* __restrict
     write_ids_masks<64u>(mo, tile, start, n, lane, [&](uint32_t i) { return tp[si[i]].y; }, vals);
 }
 
-// Launched with n_tiles workgroups: workgroup b takes the b-th tile of the
-// length-class lists of k_tl_ranges, longest class first (the workgroups
-// start in about that order, so the long tiles do not finish last); those
-// beyond the listed tiles return.
+// Launched with n_tiles + ceil(n_tiles / 4) workgroups: workgroup b takes
+// the b-th tile of the length-class lists of k_tl_ranges, longest class first
+// (the workgroups start in about that order, so the long tiles do not finish
+// last); the next ceil(n_tiles / 4) take four tiles each, one per wave, and
+// sort those of 65..512 entries (tl_sort_wave_tile), filling the chip while
+// the long tiles finish, and those of up to 64 (tl_sort_small_tile); the
+// rest return.
 __global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restrict__ ranges, int64_t n_tiles,
                                                         const uint64_t* __restrict__ total_dev, uint64_t capacity,
                                                         uint2* __restrict__ pairs, uint2* __restrict__ alt,
@@ -567,7 +564,16 @@ __global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restri
             if (tile < 0 && b < cnt) tile = big[TL_CLASSES + (int64_t)c * n_tiles + b];
             if (tile < 0) b -= cnt;
         }
-        if (tile < 0) return;
+        if (tile < 0) {
+            const uint32_t wave = threadIdx.x >> 6;
+            const int64_t t = (int64_t)b * 4 + wave;
+            if (t < n_tiles) {
+                tl_sort_small_tile(t, threadIdx.x & 63u, ranges, total_dev, capacity, pairs, vals, mo);
+                tl_sort_wave_tile(t, threadIdx.x & 63u, s_key + wave * WV_CAP, s_idx + wave * WV_CAP, wcnt[wave],
+                                  ranges, total_dev, capacity, pairs, vals, mo);
+            }
+            return;
+        }
     }
     const uint2 rg = *(const uint2*)(ranges + 2 * (uint64_t)tile);
     const uint64_t limit = min(capacity, *total_dev);
@@ -575,7 +581,7 @@ __global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restri
     if (end <= start) return;
     const uint32_t n = end - start;
     const uint32_t t = threadIdx.x, lane = t & 63u, wave = t >> 6;
-    if (n <= (uint32_t)WV_CAP) return;  // k_tl_sort_small, k_tl_sort_wave
+    if (n <= (uint32_t)WV_CAP) return;  // tl_sort_small_tile, tl_sort_wave_tile
     if (n <= (uint32_t)TL_CAP) {
         // wave w holds the contiguous run [w L, (w + 1) L), L = 64 R
         const uint32_t R = (n + TL_THREADS - 1) / TL_THREADS;
@@ -914,13 +920,8 @@ gs_status gs_tile_lists(const float* rec, const uint16_t* rect, const float* dep
     mo.TX = G.tiles_x;
     mo.T = (int)G.tiles;
     mo.row0 = row0;
-    hipLaunchKernelGGL(k_tl_sort_small, dim3(grid_for((uint64_t)n_tiles, 4)), dim3(256), 0, s, ranges, n_tiles, total,
-                       capacity, pairs, vals, mo);
-    if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
-    hipLaunchKernelGGL(k_tl_sort_wave, dim3(grid_for((uint64_t)n_tiles, 4)), dim3(256), 0, s, ranges, n_tiles, total,
-                       capacity, pairs, vals, mo);
-    if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
-    hipLaunchKernelGGL(k_tl_sort, dim3((unsigned)n_tiles), dim3(TL_THREADS), 0, s, ranges, n_tiles, total,
+    hipLaunchKernelGGL(k_tl_sort, dim3((unsigned)(n_tiles + grid_for((uint64_t)n_tiles, 4))), dim3(TL_THREADS), 0, s,
+                       ranges, n_tiles, total,
                        capacity, pairs, alt, vals, big, mo);
     return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
 }
