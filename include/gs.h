@@ -379,8 +379,9 @@ gs_status gs_rasterize_bwd(const float* rec, int64_t n, const uint32_t* ranges,
  * Errors: as gs_rasterize_fwd, plus null target / loss / ws / grad2d (n > 0)
  * or a small workspace.
  */
-/* Workspace of gs_rasterize_fwd_bwd_l1 (bytes): one double per 8x8 quarter
- * and one 32-bit tile index per tile of every view; 0 on invalid sizes. */
+/* Workspace of gs_rasterize_fwd_bwd_l1 (bytes): one double per 8x8 quarter,
+ * one 32-bit tile index per tile of every view, and eight 32-bit class counts
+ * per 1024 tiles (the longest-first tile order); 0 on invalid sizes. */
 size_t gs_rasterize_fwd_bwd_l1_workspace_bytes(int32_t n_views, int32_t width, int32_t height);
 
 gs_status gs_rasterize_fwd_bwd_l1(const float* rec, int64_t n, const uint32_t* ranges,
