@@ -154,18 +154,34 @@ __global__ __launch_bounds__(256) void k_bin_colscan(uint32_t* __restrict__ tabl
     const int64_t v = ok ? i / G.tiles : 0, tile = ok ? i - v * G.tiles : 0;
     uint32_t* col = table + v * G.chunks * G.tiles + tile;
     const int32_t q = (G.chunks + 3) / 4, c0 = min((int32_t)w * q, G.chunks), c1 = min(c0 + q, G.chunks);
+    // eight chunks' counts are loaded before any is added or rewritten, so
+    // that eight loads are in flight (a store may alias the next load
+    // otherwise, which serialises them)
+    constexpr int CS_BATCH = 8;
     uint32_t sum = 0u;
     if (ok)
-        for (int32_t c = c0; c < c1; ++c) sum += col[(int64_t)c * G.tiles];
+        for (int32_t c = c0; c < c1; c += CS_BATCH) {
+            uint32_t x[CS_BATCH];
+#pragma unroll
+            for (int k = 0; k < CS_BATCH; ++k) x[k] = c + k < c1 ? col[(int64_t)(c + k) * G.tiles] : 0u;
+#pragma unroll
+            for (int k = 0; k < CS_BATCH; ++k) sum += x[k];
+        }
     part[w][lane] = sum;
     __syncthreads();
     uint32_t run = 0u;
     for (uint32_t k = 0; k < w; ++k) run += part[k][lane];
     if (ok) {
-        for (int32_t c = c0; c < c1; ++c) {
-            const uint32_t x = col[(int64_t)c * G.tiles];
-            col[(int64_t)c * G.tiles] = run;
-            run += x;
+        for (int32_t c = c0; c < c1; c += CS_BATCH) {
+            uint32_t x[CS_BATCH];
+#pragma unroll
+            for (int k = 0; k < CS_BATCH; ++k) x[k] = c + k < c1 ? col[(int64_t)(c + k) * G.tiles] : 0u;
+#pragma unroll
+            for (int k = 0; k < CS_BATCH; ++k)
+                if (c + k < c1) {
+                    col[(int64_t)(c + k) * G.tiles] = run;
+                    run += x[k];
+                }
         }
         if (w == 3) totals[i] = run;
     }
