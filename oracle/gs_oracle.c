@@ -17,6 +17,7 @@
  */
 #define _GNU_SOURCE
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -40,6 +41,85 @@ int or_abi_version(void) { return 1; }
 int or_rec_stride(void) { return OR_REC; }
 int or_int_stride(void) { return OR_INT; }
 int or_camera_bytes(void) { return (int)sizeof(or_camera); }
+int or_max_threads(void) { return omp_get_max_threads(); }
+void or_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+
+/* ---------------------------------------------------------------------------
+ * How far a GPU's exp() may lie from this oracle's, and so which per-pixel
+ * decisions of the compositing rules (alpha >= 1/255, the 0.99 clamp, the
+ * T' < 1e-4 stop) the two sides may take differently.
+ *
+ * A (pixel, entry) pair's power is the same fp32 arithmetic on both sides, so
+ * it is the same number. The GPU's raster passes take G = exp(p) as 2^y with
+ * y = fl(p * L), L = fl32(log2 e), on the hardware exp2, whose result is
+ * within OR_EXP_HW_ULP ulp of 2^y; this oracle takes the C library's expf(p),
+ * within OR_EXP_LIBM_REL (relative) of e^p. With
+ *   dy = |p| (|L - log2 e| + L u)        (the constant's rounding and the
+ *                                         product's, u = 2^-24)
+ *   e_arg = 2^dy - 1                     (2^y against e^p)
+ * the two G differ by at most (relative to the oracle's)
+ *   rG(p) = (1 + e_arg) (1 + 2^-23 OR_EXP_HW_ULP) / (1 - OR_EXP_LIBM_REL) - 1,
+ * and the two products o * G, each rounded once, by
+ *   ra(p) = (1 + rG) (1 + u) / (1 - u) - 1.
+ * One ulp of a normal fp32 result r is at most 2^-23 r. tests/test_oracle_band.py
+ * checks rG against the exact error of the argument for every fp32 power in
+ * [-5.6, 0] and the library's expf against fp64; the GPU test of the exp path
+ * checks the hardware's side.
+ * ------------------------------------------------------------------------ */
+#define OR_U 5.9604644775390625e-08               /* 2^-24, fp32 unit roundoff */
+#define OR_LOG2E 1.44269504088896340736           /* log2 e */
+#define OR_LOG2E_F32 1.44269502162933349609375    /* its nearest fp32 value */
+#define OR_EXP_HW_ULP 1.0
+#define OR_EXP_LIBM_REL (1.01 * OR_U)             /* glibc's expf: < 0.51 ulp */
+
+static double or_band_scale = 1.0; /* test knob: the flags' bands times this (1 = the derived band) */
+static int or_exp_perturb = 0;     /* test knob: 0 off; +1 / -1 every G moved to an edge of its
+                                    * band; 2 the edge chosen per power */
+
+double or_exp_band(float p)
+{
+    const double dy = fabs((double)p) * (fabs(OR_LOG2E_F32 - OR_LOG2E) + OR_LOG2E_F32 * OR_U);
+    const double e_arg = exp2(dy) - 1.0;
+    return (1.0 + e_arg) * (1.0 + OR_EXP_HW_ULP * 2.0 * OR_U) / (1.0 - OR_EXP_LIBM_REL) - 1.0;
+}
+
+double or_alpha_band(float p)
+{
+    return ((1.0 + or_exp_band(p)) * (1.0 + OR_U) / (1.0 - OR_U) - 1.0) * or_band_scale;
+}
+
+double or_exp_libm_rel(void) { return OR_EXP_LIBM_REL; }
+double or_exp_hw_ulp(void) { return OR_EXP_HW_ULP; }
+void or_set_band_scale(double s) { or_band_scale = s; }
+void or_set_exp_perturb(int mode) { or_exp_perturb = mode; }
+
+/* A G the GPU could return where this oracle returns G: G moved towards an
+ * edge of its band (a little inside it, so that the rounding to fp32 stays
+ * within it). */
+static float or_perturbed_exp(float p, float G)
+{
+    double s = (double)or_exp_perturb;
+    if (or_exp_perturb == 2) {
+        uint32_t b;
+        memcpy(&b, &p, 4);
+        b = (b ^ (b >> 13)) * 0x9e3779b1u;
+        s = ((b >> 17) & 1u) ? 1.0 : -1.0;
+    }
+    return (float)((double)G * (1.0 + s * (or_exp_band(p) - 1.01 * OR_U)));
+}
+
+/* expf and the band, element-wise (for the tests of the band). */
+void or_expf_batch(const float* p, float* out, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = expf(p[i]);
+}
+
+void or_exp_band_batch(const float* p, double* out, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = or_exp_band(p[i]);
+}
 
 /* ---- fp32 instantiation --------------------------------------------------- */
 #define REAL float

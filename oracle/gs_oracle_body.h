@@ -304,45 +304,53 @@ static void FN(free_lists)(FN(or_lists) * L)
  *   alpha = min(0.99, o * exp(power));  skip if alpha < 1/255
  *   T' = T * (1 - alpha); stop (entry not blended) if T' < 1e-4
  *   w = alpha * T; C_c = fma(rgb_c, w, C_c); T = T'
- * Returns 0 skip, 1 blended, 2 stop. Near-threshold flags (fp32 only): bit0 an
- * image-changing decision lies within the exp() rounding band, bit1 the 0.99
- * clamp does (changes only gradients).
+ * Returns 0 skip, 1 blended, 2 stop.
+ *
+ * Near-threshold flags (fp32 only), from the band of or_exp_band (the largest
+ * difference between a GPU's exp() and this oracle's): bit0 an image-changing
+ * decision may go the other way on the GPU, bit1 the 0.99 clamp may (changes
+ * only gradients), bit2 the decision was alpha >= 1/255, bit3 it was the stop.
+ *   - alpha: the GPU's o G lies in [oG (1 - ra), oG (1 + ra)], ra = or_alpha_band;
+ *     a threshold inside that interval is flagged.
+ *   - T: *terr bounds |T_gpu / T - 1| for the pixel so far. A blend moves it to
+ *     (1 + terr) (1 + a ra / (1 - a)) q^2 - 1 with q = (1 + u) / (1 - u):
+ *     1 - alpha differs by at most a ra / (1 - a) before rounding, and
+ *     1 - alpha and T (1 - alpha) are each rounded once on each side (2^-24
+ *     relative, u) once their operands may differ. A clamped alpha whose whole
+ *     interval lies above 0.99 is the same constant on both sides (ra = 0).
+ *     The stop T' < 1e-4 is flagged when T' (1 -+ terr') straddles 1e-4.
  * ------------------------------------------------------------------------ */
-#ifndef OR_ALPHA_BAND
-/* A GPU's exp() may differ from this oracle's by a few ulp; these bands are
- * the relative widths inside which such a difference can flip a decision.
- * OR_ALPHA_REL bounds the relative difference of one alpha (several times the
- * error of a hardware exp2 of a rounded argument); T' carries the sum of the
- * alphas' errors, each amplified by alpha / (1 - alpha), plus one rounding per
- * blend, and the band around 1e-4 is twice that running bound. */
-#define OR_ALPHA_BAND 1e-5
-#define OR_ALPHA_REL 4e-6
-#define OR_T_SAFETY 2.0
-#endif
-
 static inline int FN(pair_eval)(const REAL* r, REAL px, REAL py, REAL Tcur, REAL* alpha_out,
-                                REAL* G_out, REAL* Tnext_out, int* amb, double* relerr)
+                                REAL* G_out, REAL* Tnext_out, int* amb, double* terr)
 {
     const REAL dx = r[0] - px, dy = r[1] - py;
     const REAL nA = -0.5f * r[6], nB = -r[7], nC = -0.5f * r[8];
     const REAL power = R_FMA(dx, R_FMA(nA, dx, nB * dy), (nC * dy) * dy);
     if (power > 0) return 0;
-    const REAL G = R_EXP(power);
+    REAL G = R_EXP(power);
+    if (OR_IS_F32 && or_exp_perturb) G = (REAL)or_perturbed_exp((float)power, (float)G);
     const REAL oG = r[9] * G;
     const REAL alpha = R_FMIN((REAL)0.99f, oG);
+    double ra = 0;
     if (OR_IS_F32) {
-        const double d = (double)oG;
-        if (fabs(d - 1.0 / 255.0) <= OR_ALPHA_BAND * (1.0 / 255.0)) *amb |= 1 | 4;
-        if (fabs(d - 0.99) <= OR_ALPHA_BAND * 0.99) *amb |= 2;
+        ra = or_alpha_band((float)power);
+        const double lo = (double)oG * (1.0 - ra), hi = (double)oG * (1.0 + ra);
+        const double amin = (double)(1.0f / 255.0f), amax = (double)0.99f;
+        if (lo < amin && !(hi < amin)) *amb |= 1 | 4;
+        if (!(lo > amax) && hi > amax) *amb |= 2;
+        if (lo > amax) ra = 0; /* clamped on both sides */
     }
     if (alpha < (REAL)(1.0f / 255.0f)) return 0;
     const REAL Tn = Tcur * (1.0f - alpha);
     if (OR_IS_F32) {
-        /* a clamped alpha is the constant 0.99 on both sides: no exp() error */
-        const int clamped_safe = (double)oG > 0.99 * (1.0 + OR_ALPHA_BAND);
-        const double rel = *relerr + (clamped_safe ? 0.0 : (double)alpha / (1.0 - (double)alpha) * OR_ALPHA_REL);
-        if (fabs((double)Tn - 1e-4) <= OR_T_SAFETY * rel * 1e-4) *amb |= 1 | 8;
-        if (!(Tn < (REAL)1e-4f)) *relerr = rel;
+        double e = *terr;
+        if (ra > 0 || e > 0) {
+            const double a = (double)alpha, q = (1.0 + OR_U) / (1.0 - OR_U);
+            e = (1.0 + e) * (1.0 + a * ra / (1.0 - a)) * q * q - 1.0;
+        }
+        const double tmin = (double)1e-4f;
+        if ((double)Tn * (1.0 - e) < tmin && !((double)Tn * (1.0 + e) < tmin)) *amb |= 1 | 8;
+        if (!(Tn < (REAL)1e-4f)) *terr = e;
     }
     *alpha_out = alpha;
     *G_out = G;
@@ -373,12 +381,12 @@ void FN(or_render_fwd)(const REAL* rec, const int32_t* iv, int64_t n, const or_c
                     const REAL px = (REAL)i + 0.5f, py = (REAL)j + 0.5f;
                     REAL T = 1, col[3] = {0, 0, 0};
                     int last = 0, flags = 0;
-                    double relerr = 0;
+                    double terr = 0;
                     uint64_t h = 1469598103934665603ull;
                     for (int64_t e = L.start[tile]; e < L.start[tile + 1]; ++e) {
                         const REAL* r = rv + L.ids[e] * OR_REC;
                         REAL al = 0, G = 0, Tn = 0;
-                        const int res = FN(pair_eval)(r, px, py, T, &al, &G, &Tn, &flags, &relerr);
+                        const int res = FN(pair_eval)(r, px, py, T, &al, &G, &Tn, &flags, &terr);
                         const int clampd = (res != 0) && (r[9] * G > (REAL)0.99f);
                         h = (h ^ (uint64_t)((e - L.start[tile]) * 8 + res * 2 + clampd)) * 1099511628211ull;
                         if (res == 2) break;
@@ -474,11 +482,11 @@ void FN(or_render_bwd)(const REAL* rec, const int32_t* iv, int64_t n, const or_c
                         /* forward decisions in REAL */
                         REAL T = 1;
                         int m = 0, dummy = 0;
-                        double relerr = 0;
+                        double terr = 0;
                         for (int64_t e = L.start[tile]; e < L.start[tile + 1]; ++e) {
                             const REAL* r = rv + L.ids[e] * OR_REC;
                             REAL a = 0, G = 0, Tn = 0;
-                            const int res = FN(pair_eval)(r, px, py, T, &a, &G, &Tn, &dummy, &relerr);
+                            const int res = FN(pair_eval)(r, px, py, T, &a, &G, &Tn, &dummy, &terr);
                             if (res == 2) break;
                             if (res == 1) {
                                 idx[m] = e;

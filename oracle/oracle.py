@@ -65,6 +65,17 @@ def _declare(L):
     L.or_exclusive_scan.argtypes = [P, I64, P]
     L.or_adam.argtypes = [P, P, P, P, I64, ctypes.c_double, ctypes.c_double, ctypes.c_double,
                           ctypes.c_double, I64]
+    L.or_set_threads.argtypes = [I32]
+    L.or_exp_band.argtypes = [ctypes.c_float]
+    L.or_exp_band.restype = ctypes.c_double
+    L.or_alpha_band.argtypes = [ctypes.c_float]
+    L.or_alpha_band.restype = ctypes.c_double
+    L.or_exp_libm_rel.restype = ctypes.c_double
+    L.or_exp_hw_ulp.restype = ctypes.c_double
+    L.or_set_band_scale.argtypes = [ctypes.c_double]
+    L.or_set_exp_perturb.argtypes = [I32]
+    L.or_expf_batch.argtypes = [P, P, I64]
+    L.or_exp_band_batch.argtypes = [P, P, I64]
     assert L.or_camera_bytes() == ctypes.sizeof(OrCamera)
 
 
@@ -216,6 +227,63 @@ def adam(theta, g, m, v, lr, b1, b2, eps, step):
     gg = np.ascontiguousarray(g, dtype=np.float32)
     L.or_adam(_ptr(th), _ptr(gg), _ptr(mm), _ptr(vv), th.size, lr, b1, b2, eps, step)
     return th, mm, vv
+
+
+def max_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().or_max_threads())
+
+
+def set_threads(n: int):
+    lib().or_set_threads(int(n))
+
+
+def expf(p: np.ndarray) -> np.ndarray:
+    """The oracle's fp32 exp (the C library's expf), element-wise."""
+    p = np.ascontiguousarray(p, dtype=np.float32)
+    out = np.empty_like(p)
+    lib().or_expf_batch(_ptr(p), _ptr(out), p.size)
+    return out
+
+
+def exp_band(p: np.ndarray) -> np.ndarray:
+    """rG(p): the largest relative difference between a GPU's exp of the fp32
+    power p and the oracle's (see gs_oracle.c), element-wise, fp64."""
+    p = np.ascontiguousarray(p, dtype=np.float32)
+    out = np.empty(p.shape, dtype=np.float64)
+    lib().or_exp_band_batch(_ptr(p), _ptr(out), p.size)
+    return out
+
+
+class exp_perturbed:
+    """Context: every exp of the fp32 oracle's compositing moved to an edge of
+    its band (mode +1, -1, or 2 = the edge picked per power), as a GPU's exp
+    could be; the flags of the render are then those of the moved values."""
+
+    def __init__(self, mode: int):
+        self.mode = mode
+
+    def __enter__(self):
+        lib().or_set_exp_perturb(self.mode)
+        return self
+
+    def __exit__(self, *a):
+        lib().or_set_exp_perturb(0)
+
+
+class band_scaled:
+    """Context: the flags' bands multiplied by `scale` (a narrowed band is the
+    mistake the band tests must catch)."""
+
+    def __init__(self, scale: float):
+        self.scale = scale
+
+    def __enter__(self):
+        lib().or_set_band_scale(self.scale)
+        return self
+
+    def __exit__(self, *a):
+        lib().or_set_band_scale(1.0)
 
 
 def train_step(params, sh_degree, cams, target, lr, b1, b2, eps, step, m=None, v=None,
