@@ -20,6 +20,8 @@ GS_TILE = 16
 GS_MAX_VIEWS = 16
 GS_REC_FLOATS = 12
 GS_GRAD2D_ROWS = 9
+GS_ACCUMULATE_LOSS, GS_ACCUMULATE_GRAD2D = 1, 2
+ABI_VERSION = 2
 (REC_U, REC_V, REC_A, REC_B, REC_C, REC_OPACITY, REC_R, REC_G, REC_BLUE,
  REC_EXT_X, REC_EXT_Y, REC_DEPTH) = range(12)
 
@@ -32,6 +34,7 @@ EXPORTS = (
     "gs_tile_masks_workspace_bytes",
     "gs_rasterize_fwd", "gs_rasterize_fwd_l1", "gs_loss_l1", "gs_rasterize_bwd", "gs_rasterize_fwd_bwd_l1",
     "gs_preprocess_bwd", "gs_adam_step", "gs_adam_step_unless", "gs_preprocess_bwd_adam",
+    "gs_raster_exp", "gs_stream_copy",
 )
 
 
@@ -74,27 +77,30 @@ def lib():
             "gs_tile_lists_workspace_bytes": ([_I64, _I32, _I32, _I32, _U64], _SZ),
             "gs_rasterize_fwd_l1_workspace_bytes": ([_I32, _I32, _I32], _SZ),
             "gs_rasterize_fwd_bwd_l1_workspace_bytes": ([_I32, _I32, _I32], _SZ),
-            "gs_preprocess": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+            "gs_preprocess": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
             "gs_emit_intersections": ([_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _U64, _P, _P], ctypes.c_int),
             "gs_sort_keys": ([_P, _P, _P, _P, _U64, _I32, _P, _SZ, _P, _P], ctypes.c_int),
             "gs_tile_ranges": ([_P, _U64, _I64, _P, _P], ctypes.c_int),
-            "gs_tile_lists": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P, _U64, _P, _P, _P, _SZ, _P],
-                              ctypes.c_int),
+            "gs_tile_lists": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P, _U64, _P, _P, _P, _P, _SZ,
+                               _P], ctypes.c_int),
             "gs_tile_masks_workspace_bytes": ([_U64], _SZ),
             "gs_tile_masks": ([_P, _I64, _P, _P, _U64, _P, _I32, _P, _P, _SZ, _P], ctypes.c_int),
-            "gs_rasterize_fwd": ([_P, _I64, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P], ctypes.c_int),
-            "gs_rasterize_fwd_l1": ([_P, _I64, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _F32, _P, _P, _P, _P, _P,
-                                     _I32, _P, _SZ, _P], ctypes.c_int),
+            "gs_rasterize_fwd": ([_P, _I64, _P, _P, _P, _U64, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P],
+                                 ctypes.c_int),
+            "gs_rasterize_fwd_l1": ([_P, _I64, _P, _P, _P, _U64, _P, _I32, _I32, _I32, _P, _P, _F32, _P, _P, _P, _P,
+                                     _P, _I32, _P, _SZ, _P], ctypes.c_int),
             "gs_loss_l1": ([_P, _P, _I64, _F32, _P, _P, _I32, _P], ctypes.c_int),
-            "gs_rasterize_fwd_bwd_l1": ([_P, _I64, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _F32, _P, _P, _P, _P,
-                                         _P, _P, _I32, _P, _SZ, _P], ctypes.c_int),
-            "gs_rasterize_bwd": ([_P, _I64, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _I32, _P],
+            "gs_rasterize_fwd_bwd_l1": ([_P, _I64, _P, _P, _P, _U64, _P, _I32, _I32, _I32, _P, _P, _F32, _P, _P,
+                                         _P, _P, _P, _P, _I32, _P, _SZ, _P], ctypes.c_int),
+            "gs_rasterize_bwd": ([_P, _I64, _P, _P, _P, _U64, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _I32, _P],
                                  ctypes.c_int),
             "gs_preprocess_bwd": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P], ctypes.c_int),
             "gs_adam_step": ([_P, _P, _P, _P, _I64, _F64, _F64, _F64, _F64, _I64, _P], ctypes.c_int),
             "gs_adam_step_unless": ([_P, _P, _P, _P, _I64, _F64, _F64, _F64, _F64, _I64, _P, _P], ctypes.c_int),
             "gs_preprocess_bwd_adam": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _F64, _F64, _F64, _F64, _I64, _P,
                                         _P, _P, _P], ctypes.c_int),
+            "gs_raster_exp": ([_P, _P, _I64, _P], ctypes.c_int),
+            "gs_stream_copy": ([_P, _P, _U64, _P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -171,10 +177,12 @@ def tile_lists_workspace_bytes(n: int, n_views: int, width: int, height: int, ca
 
 
 # ---- the step ----------------------------------------------------------------
-def gs_preprocess(params, n, sh_degree, cams, rec, rect, offsets, total, ws, stream=None, depth=None):
+def gs_preprocess(params, n, sh_degree, cams, rec, rect, offsets, total, ws, stream=None, depth=None, grad2d=None):
+    """depth (optional): the compact depth copy; grad2d (optional): 2D-gradient
+    records zeroed for every visible (view, Gaussian)."""
     cc = cameras(cams)
     _check(lib().gs_preprocess(_ptr(params), n, sh_degree, cc, len(cams), _ptr(rec), _ptr(rect), _ptr(depth),
-                               _ptr(offsets), _ptr(total), _ptr(ws), ws.numel() * ws.element_size(),
+                               _ptr(grad2d), _ptr(offsets), _ptr(total), _ptr(ws), ws.numel() * ws.element_size(),
                                _stream(stream)), "gs_preprocess")
 
 
@@ -194,13 +202,14 @@ def _window(height, rows):
 
 
 def gs_tile_lists(rec, rect, n, n_views, width, height, vals, capacity, ranges, overflow, ws, masks=None,
-                  row0=0, rows=None, stream=None, depth=None):
+                  row0=0, rows=None, stream=None, depth=None, sticky=None):
     """masks (optional): the entries' sub-block masks, as gs_tile_masks;
     row0, rows: the window of tile rows (the whole image by default);
-    depth (optional): gs_preprocess's compact depths."""
+    depth (optional): gs_preprocess's compact depths; sticky (optional): a
+    device flag set with the overflow and never cleared."""
     _check(lib().gs_tile_lists(_ptr(rec), _ptr(rect), _ptr(depth), n, n_views, width, height, row0, _window(height, rows),
                                _ptr(vals), _ptr(masks), capacity,
-                               _ptr(ranges), _ptr(overflow), _ptr(ws), ws.numel() * ws.element_size(),
+                               _ptr(ranges), _ptr(overflow), _ptr(sticky), _ptr(ws), ws.numel() * ws.element_size(),
                                _stream(stream)), "gs_tile_lists")
 
 
@@ -228,19 +237,30 @@ def gs_tile_masks(rec, n, ranges, vals, capacity, cams, masks, ws, stream=None):
            "gs_tile_masks")
 
 
-def gs_rasterize_fwd(rec, n, ranges, vals, masks, cams, bg, image, T_final, n_contrib, row0=0, rows=None, stream=None):
+def _capacity(vals, masks, capacity):
+    """List slots the raster calls may read: the given capacity, else the
+    smaller of the two list buffers."""
+    if capacity is not None:
+        return int(capacity)
+    return min(vals.numel(), masks.numel()) if vals is not None and masks is not None else 0
+
+
+def gs_rasterize_fwd(rec, n, ranges, vals, masks, cams, bg, image, T_final, n_contrib, row0=0, rows=None, stream=None,
+                     capacity=None):
     bgv = (ctypes.c_float * 3)(*bg)
-    _check(lib().gs_rasterize_fwd(_ptr(rec), n, _ptr(ranges), _ptr(vals), _ptr(masks), cameras(cams), len(cams), row0,
+    _check(lib().gs_rasterize_fwd(_ptr(rec), n, _ptr(ranges), _ptr(vals), _ptr(masks), _capacity(vals, masks, capacity),
+                                  cameras(cams), len(cams), row0,
                                   _window(cams[0].height, rows), bgv,
                                   _ptr(image), _ptr(T_final), _ptr(n_contrib), _stream(stream)),
            "gs_rasterize_fwd")
 
 
 def gs_rasterize_fwd_l1(rec, n, ranges, vals, masks, cams, bg, target, scale, image, T_final, n_contrib, dL_dimage, loss,
-                        ws, accumulate=False, row0=0, rows=None, stream=None):
+                        ws, accumulate=False, row0=0, rows=None, stream=None, capacity=None):
     """image may be None (not written)."""
     bgv = (ctypes.c_float * 3)(*bg)
-    _check(lib().gs_rasterize_fwd_l1(_ptr(rec), n, _ptr(ranges), _ptr(vals), _ptr(masks), cameras(cams), len(cams),
+    _check(lib().gs_rasterize_fwd_l1(_ptr(rec), n, _ptr(ranges), _ptr(vals), _ptr(masks),
+                                     _capacity(vals, masks, capacity), cameras(cams), len(cams),
                                      row0, _window(cams[0].height, rows), bgv,
                                      _ptr(target), scale, _ptr(image), _ptr(T_final), _ptr(n_contrib),
                                      _ptr(dL_dimage), _ptr(loss), int(bool(accumulate)), _ptr(ws),
@@ -253,9 +273,10 @@ def gs_loss_l1(image, target, count, scale, dL_dimage, loss, accumulate=False, s
 
 
 def gs_rasterize_bwd(rec, n, ranges, vals, masks, cams, bg, T_final, n_contrib, dL_dimage, grad2d,
-                     accumulate=False, row0=0, rows=None, stream=None):
+                     accumulate=False, row0=0, rows=None, stream=None, capacity=None):
     bgv = (ctypes.c_float * 3)(*bg)
-    _check(lib().gs_rasterize_bwd(_ptr(rec), n, _ptr(ranges), _ptr(vals), _ptr(masks), cameras(cams), len(cams), row0,
+    _check(lib().gs_rasterize_bwd(_ptr(rec), n, _ptr(ranges), _ptr(vals), _ptr(masks), _capacity(vals, masks, capacity),
+                                  cameras(cams), len(cams), row0,
                                   _window(cams[0].height, rows), bgv,
                                   _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimage), _ptr(grad2d),
                                   int(bool(accumulate)), _stream(stream)), "gs_rasterize_bwd")
@@ -263,13 +284,19 @@ def gs_rasterize_bwd(rec, n, ranges, vals, masks, cams, bg, T_final, n_contrib, 
 
 def gs_rasterize_fwd_bwd_l1(rec, n, ranges, vals, masks, cams, bg, target, scale, loss, grad2d, ws, image=None,
                             T_final=None, n_contrib=None, dL_dimage=None, accumulate=False, row0=0, rows=None,
-                            stream=None):
-    """image, T_final, n_contrib and dL_dimage are optional outputs."""
+                            stream=None, capacity=None, accumulate_grad2d=None):
+    """image, T_final, n_contrib and dL_dimage are optional outputs.
+    `accumulate` adds to the loss and the 2D gradients; `accumulate_grad2d`,
+    when given, decides for the 2D gradients alone (e.g. records zeroed by
+    gs_preprocess, with the loss overwritten)."""
     bgv = (ctypes.c_float * 3)(*bg)
-    _check(lib().gs_rasterize_fwd_bwd_l1(_ptr(rec), n, _ptr(ranges), _ptr(vals), _ptr(masks), cameras(cams),
+    acc_g = accumulate if accumulate_grad2d is None else accumulate_grad2d
+    flags = (GS_ACCUMULATE_LOSS if accumulate else 0) | (GS_ACCUMULATE_GRAD2D if acc_g else 0)
+    _check(lib().gs_rasterize_fwd_bwd_l1(_ptr(rec), n, _ptr(ranges), _ptr(vals), _ptr(masks),
+                                         _capacity(vals, masks, capacity), cameras(cams),
                                          len(cams), row0, _window(cams[0].height, rows), bgv, _ptr(target), scale,
                                          _ptr(image), _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimage), _ptr(loss),
-                                         _ptr(grad2d), int(bool(accumulate)), _ptr(ws),
+                                         _ptr(grad2d), flags, _ptr(ws),
                                          ws.numel() * ws.element_size(), _stream(stream)), "gs_rasterize_fwd_bwd_l1")
 
 
@@ -295,3 +322,14 @@ def gs_preprocess_bwd_adam(params, n, sh_degree, cams, rect, grad2d, m, v, lr, b
 def gs_adam_step_unless(params, grad, m, v, count, lr, beta1, beta2, eps, step, skip, stream=None):
     _check(lib().gs_adam_step_unless(_ptr(params), _ptr(grad), _ptr(m), _ptr(v), count, lr, beta1, beta2, eps,
                                      step, _ptr(skip), _stream(stream)), "gs_adam_step_unless")
+
+
+def gs_raster_exp(x, y, stream=None):
+    """y = the raster passes' exp of x (device fp32 tensors)."""
+    _check(lib().gs_raster_exp(_ptr(x), _ptr(y), x.numel(), _stream(stream)), "gs_raster_exp")
+
+
+def gs_stream_copy(dst, src, nbytes=None, stream=None):
+    """Plain device copy of nbytes (default: all of src) from src to dst."""
+    nb = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    _check(lib().gs_stream_copy(_ptr(dst), _ptr(src), nb, _stream(stream)), "gs_stream_copy")

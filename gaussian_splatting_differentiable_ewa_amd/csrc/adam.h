@@ -37,6 +37,7 @@ inline bool adam_consts(double lr, double beta1, double beta2, double eps, int64
 
 __device__ __forceinline__ void adam1(float& p, float g, float& m, float& v, const AdamConsts& c)
 {
+#pragma clang fp contract(off)  // the same rounding wherever it is inlined
     m = c.b1 * m + c.omb1 * g;
     v = c.b2 * v + c.omb2 * (g * g);
     p = p - c.step_size * m / (sqrtf(v) * c.inv_sqrt_bc2 + c.eps);

@@ -64,7 +64,8 @@ template <int DEG>
 __global__ __launch_bounds__(PRE_THREADS) void k_preprocess(const float* __restrict__ P, int64_t n,
                                                             const DevCameras cams, const ShConsts K,
                                                             float* __restrict__ rec, uint16_t* __restrict__ rect,
-                                                            float* __restrict__ depth, uint32_t* __restrict__ counts)
+                                                            float* __restrict__ depth, float* __restrict__ g2zero,
+                                                            uint32_t* __restrict__ counts)
 {
     constexpr int NB = (DEG + 1) * (DEG + 1);
     const int64_t g = (int64_t)blockIdx.x * PRE_THREADS + threadIdx.x;
@@ -119,6 +120,11 @@ __global__ __launch_bounds__(PRE_THREADS) void k_preprocess(const float* __restr
         out[1] = make_float4(p.C, L.o, r, gg);
         out[2] = make_float4(b, ex, ey, p.zc);
         if (depth) depth[idx] = p.zc;
+        if (g2zero) {  // the 2D-gradient record the raster passes add to
+            float* gz = g2zero + idx * GS_GRAD2D_ROWS;
+#pragma unroll
+            for (int k = 0; k < GS_GRAD2D_ROWS; ++k) gz[k] = 0.f;
+        }
         *(uint2*)(rect + 4 * idx) = make_uint2((uint32_t)p.x0 | ((uint32_t)p.y0 << 16),
                                                (uint32_t)p.x1 | ((uint32_t)p.y1 << 16));
         counts[idx] = (uint32_t)((p.x1 - p.x0) * (p.y1 - p.y0));
@@ -172,7 +178,7 @@ using namespace gs;
 extern "C" {
 
 gs_status gs_preprocess(const float* params, int64_t n, int32_t sh_degree, const gs_camera* cams,
-                        int32_t n_views, float* rec, uint16_t* rect, float* depth, uint32_t* offsets,
+                        int32_t n_views, float* rec, uint16_t* rect, float* depth, float* grad2d, uint32_t* offsets,
                         uint64_t* total, void* ws, size_t ws_bytes, void* stream)
 {
     if (n < 0 || sh_degree < 0 || sh_degree > 3) return GS_ERR_INVALID_ARGUMENT;
@@ -188,10 +194,10 @@ gs_status gs_preprocess(const float* params, int64_t n, int32_t sh_degree, const
         const dim3 grid(grid_for((uint64_t)n, PRE_THREADS)), block(PRE_THREADS);
         const ShConsts K = sh_constants();
         switch (sh_degree) {
-            case 0: hipLaunchKernelGGL(k_preprocess<0>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, offsets); break;
-            case 1: hipLaunchKernelGGL(k_preprocess<1>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, offsets); break;
-            case 2: hipLaunchKernelGGL(k_preprocess<2>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, offsets); break;
-            default: hipLaunchKernelGGL(k_preprocess<3>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, offsets); break;
+            case 0: hipLaunchKernelGGL(k_preprocess<0>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, grad2d, offsets); break;
+            case 1: hipLaunchKernelGGL(k_preprocess<1>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, grad2d, offsets); break;
+            case 2: hipLaunchKernelGGL(k_preprocess<2>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, grad2d, offsets); break;
+            default: hipLaunchKernelGGL(k_preprocess<3>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, grad2d, offsets); break;
         }
         if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     }

@@ -32,6 +32,10 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(float* __restrict__ P, i
                                                         const AdamConsts ac, const int32_t* __restrict__ skip,
                                                         uint8_t* __restrict__ state)
 {
+    // no contraction: the arithmetic is the written one in both forms of the
+    // kernel, so the gradient the fused update applies is the one
+    // gs_preprocess_bwd writes, bit for bit
+#pragma clang fp contract(off)
     constexpr int NB = (DEG + 1) * (DEG + 1);
     constexpr int ROWS = 11 + 3 * NB;
     const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;

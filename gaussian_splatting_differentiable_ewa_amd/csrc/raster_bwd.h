@@ -68,11 +68,12 @@ __device__ __forceinline__ void raster_bwd_walk(BwdLds& L, const QuarterCtx& t, 
                                                 const float* __restrict__ rec, int64_t n,
                                                 const uint32_t* __restrict__ ranges,
                                                 const uint32_t* __restrict__ vals,
-                                                const uint16_t* __restrict__ masks, float* __restrict__ grad2d)
+                                                const uint16_t* __restrict__ masks, uint32_t cap,
+                                                float* __restrict__ grad2d)
 {
 #pragma clang fp contract(off)
     if (g0 == 0.f && g1 == 0.f && g2 == 0.f) my_last = 0;  // this pixel adds nothing
-    const uint2 rg = *(const uint2*)(ranges + 2 * (uint64_t)t.tile_lin);
+    const uint2 rg = tile_range(ranges, t.tile_lin, cap);
     // never walk past the tile's list, whatever n_contrib holds
     const int32_t row_last = min(row_max16(my_last), (int32_t)(rg.y - rg.x));
     const int32_t rl0 = __builtin_amdgcn_readlane(row_last, 0), rl1 = __builtin_amdgcn_readlane(row_last, 16);
@@ -115,13 +116,13 @@ __device__ __forceinline__ void raster_bwd_walk(BwdLds& L, const QuarterCtx& t, 
     ChunkScan S = scan_start<true>(wave_last - 1, wave_last, rg.x, masks, t, rl);
     Entry cur, nxt, nx2;
     uint32_t n_cur = take_batch<true>(S, cur, wave_last, rg.x, vals, masks, t, rl, L.list);
-    gather_record(cur, rv);
+    gather_record(cur, rv, n);
     uint32_t n_nxt = take_batch<true>(S, nxt, wave_last, rg.x, vals, masks, t, rl, L.list);
     while (n_cur > 0u || n_nxt > 0u || scan_left<true>(S, wave_last)) {
         stage_entry_pair(cur, t.lane, L.rec, L.bp);
 #pragma unroll
         for (int k = 0; k < GS_GRAD2D_ROWS; ++k) L.sum[k][t.lane] = 0.f;
-        gather_record(nxt, rv);
+        gather_record(nxt, rv, n);
         const uint32_t n_nx2 = take_batch<true>(S, nx2, wave_last, rg.x, vals, masks, t, rl, L.list);
         // per row, its staged slots (in descending list order), as record
         // offsets; the rest of the row's list is padding
@@ -266,7 +267,7 @@ __device__ __forceinline__ void raster_bwd_walk(BwdLds& L, const QuarterCtx& t, 
             for (uint32_t c = 0; c < n_cur; c += 7) {
                 const uint32_t ei = c + ke;
                 const uint32_t g = (uint32_t)__shfl((int)cur.gid, (int)min(ei, 63u));
-                if (t.lane < 63 && ei < n_cur) {
+                if (t.lane < 63 && ei < n_cur && (int64_t)g < n) {
                     const float a = L.sum[kk][ei];
                     if (a != 0.f) atomicAdd(g2d + (int64_t)g * GS_GRAD2D_ROWS + kk, a);
                 }

@@ -206,10 +206,12 @@ __device__ __forceinline__ uint32_t take_batch(ChunkScan& S, Entry& E, int32_t l
 }
 
 // An invalid entry gets a zero record (opacity 0): a kernel may evaluate a
-// staged slot that no row holds, and must find finite values there.
-__device__ __forceinline__ void gather_record(Entry& E, const float* __restrict__ rv)
+// staged slot that no row holds, and must find finite values there. So does
+// an id that names no Gaussian (a list buffer the caller never filled): the
+// walks stay inside the records whatever the lists hold.
+__device__ __forceinline__ void gather_record(Entry& E, const float* __restrict__ rv, int64_t n)
 {
-    if (E.valid) {
+    if (E.valid && (int64_t)E.gid < n) {
         const float4* rp = (const float4*)(rv + (int64_t)E.gid * GS_REC_FLOATS);
         E.a = rp[0];
         E.b = rp[1];
@@ -355,23 +357,37 @@ __device__ __forceinline__ int row_max16(int x)
     return x;
 }
 
+// A tile's list [start, end) from the ranges, cut at the list capacity: a
+// stale or foreign ranges buffer cannot send a walk outside vals and masks.
+__device__ __forceinline__ uint2 tile_range(const uint32_t* __restrict__ ranges, uint32_t tile_lin, uint32_t cap)
+{
+    uint2 rg = *(const uint2*)(ranges + 2 * (uint64_t)tile_lin);
+    rg.y = min(rg.y, cap);
+    rg.x = min(rg.x, rg.y);
+    return rg;
+}
+
 struct RasterArgs {
     DevCameras dc;
     int32_t row0, T;  // the window of tile rows: first row, tiles per view
     int64_t n_blocks;
+    uint32_t cap;     // slots of vals and masks
 };
 
 static inline bool raster_args(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
-                               const uint16_t* masks, const gs_camera* cams, int32_t n_views, int32_t row0,
-                               int32_t rows, const float* bg, RasterArgs& a)
+                               const uint16_t* masks, uint64_t capacity, const gs_camera* cams, int32_t n_views,
+                               int32_t row0, int32_t rows, const float* bg, RasterArgs& a)
 {
     if (n < 0 || !ranges || !bg) return false;
-    if (n > 0 && (!rec || !vals || !masks)) return false;
+    if (capacity >= ((uint64_t)1 << 32)) return false;
+    if (capacity > 0 && (!vals || !masks)) return false;
+    if (n > 0 && !rec) return false;
     if (!make_dev_cameras(cams, n_views, a.dc)) return false;
     if (row0 < 0 || rows < 1 || row0 + rows > a.dc.tiles_y) return false;
     a.row0 = row0;
     a.T = a.dc.tiles_x * rows;
     a.n_blocks = (int64_t)n_views * a.T * 4;
+    a.cap = (uint32_t)capacity;
     return a.n_blocks < ((int64_t)1 << 31);
 }
 

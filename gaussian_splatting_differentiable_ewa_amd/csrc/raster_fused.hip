@@ -123,7 +123,8 @@ __global__ __launch_bounds__(ORDER_THREADS) void k_order_place(const uint32_t* _
 // image, T_final, n_contrib and dL may each be null (not written).
 __global__ __launch_bounds__(RW_THREADS) void k_raster_fwd_bwd_l1(
     const float* __restrict__ rec, int64_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ vals,
-    const uint16_t* __restrict__ masks, int W, int H, int TX, int T, int row0, float bg0, float bg1, float bg2,
+    const uint16_t* __restrict__ masks, uint32_t cap, int W, int H, int TX, int T, int row0, float bg0, float bg1,
+    float bg2,
     const float* __restrict__ target, float scale, float* __restrict__ image, float* __restrict__ T_final,
     int32_t* __restrict__ n_contrib, float* __restrict__ dL, double* __restrict__ partial,
     float* __restrict__ grad2d, const uint32_t* __restrict__ order)
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_fwd_bwd_l1(
         tg1 = target[o + HW];
         tg2 = target[o + 2 * HW];
     }
-    const FwdPixel P = raster_fwd_walk(*reinterpret_cast<FwdLds*>(lds), t, rec, n, ranges, vals, masks);
+    const FwdPixel P = raster_fwd_walk(*reinterpret_cast<FwdLds*>(lds), t, rec, n, ranges, vals, masks, cap);
     float g0 = 0.f, g1 = 0.f, g2 = 0.f, ad = 0.f;
     int32_t last = 0;
     if (t.inside) {
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_fwd_bwd_l1(
     loss_partial(ad, t.lane, partial);
     asm volatile("" ::: "memory");  // the forward's LDS reads precede the backward's writes (in order per wave)
     raster_bwd_walk(*reinterpret_cast<BwdLds*>(lds), t, last, P.Tr, g0, g1, g2, bg0, bg1, bg2, rec, n, ranges, vals,
-                    masks, grad2d);
+                    masks, cap, grad2d);
 }
 
 }  // namespace gs
@@ -195,18 +196,20 @@ size_t gs_rasterize_fwd_bwd_l1_workspace_bytes(int32_t n_views, int32_t width, i
 }
 
 gs_status gs_rasterize_fwd_bwd_l1(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
-                                  const uint16_t* masks, const gs_camera* cams, int32_t n_views, int32_t row0,
+                                  const uint16_t* masks, uint64_t capacity, const gs_camera* cams, int32_t n_views, int32_t row0,
                                   int32_t rows, const float* bg, const float* target, float scale, float* image,
                                   float* T_final, int32_t* n_contrib, float* dL_dimage, double* loss, float* grad2d,
                                   int32_t accumulate, void* ws, size_t ws_bytes, void* stream)
 {
     RasterArgs a;
-    if (!raster_args(rec, n, ranges, vals, masks, cams, n_views, row0, rows, bg, a)) return GS_ERR_INVALID_ARGUMENT;
+    if (!raster_args(rec, n, ranges, vals, masks, capacity, cams, n_views, row0, rows, bg, a))
+        return GS_ERR_INVALID_ARGUMENT;
     if (!target || !loss || !ws || (n > 0 && !grad2d)) return GS_ERR_INVALID_ARGUMENT;
     const int64_t n_tiles = a.n_blocks / 4;
     if (ws_bytes < fused_ws_bytes(n_tiles)) return GS_ERR_INVALID_ARGUMENT;
     hipStream_t s = (hipStream_t)stream;
-    if (!accumulate && n > 0) {
+    if (accumulate & ~(GS_ACCUMULATE_LOSS | GS_ACCUMULATE_GRAD2D)) return GS_ERR_INVALID_ARGUMENT;
+    if (!(accumulate & GS_ACCUMULATE_GRAD2D) && n > 0) {
         if (fill_u32((uint32_t*)grad2d, (uint64_t)n_views * GS_GRAD2D_ROWS * (uint64_t)n, 0u, s) != hipSuccess)
             return GS_ERR_HIP;
     }
@@ -218,11 +221,13 @@ gs_status gs_rasterize_fwd_bwd_l1(const float* rec, int64_t n, const uint32_t* r
     hipLaunchKernelGGL(k_order_place, dim3(n_seg), dim3(ORDER_THREADS), 0, s, ranges, n_tiles, table, n_seg, order);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     hipLaunchKernelGGL(k_raster_fwd_bwd_l1, dim3((unsigned)a.n_blocks), dim3(RW_THREADS), 0, s, rec, n, ranges,
-                       vals, masks, a.dc.width, a.dc.height, a.dc.tiles_x, a.T, a.row0, bg[0], bg[1], bg[2], target,
+                       vals, masks, a.cap, a.dc.width, a.dc.height, a.dc.tiles_x, a.T, a.row0, bg[0], bg[1], bg[2], target,
                        scale, image, T_final, n_contrib, dL_dimage, partial, grad2d, order);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
-    return loss_from_partials(partial, a.n_blocks, (double)scale, loss, accumulate != 0, s) == hipSuccess ? GS_OK
-                                                                                                           : GS_ERR_HIP;
+    return loss_from_partials(partial, a.n_blocks, (double)scale, loss, (accumulate & GS_ACCUMULATE_LOSS) != 0, s) ==
+                   hipSuccess
+               ? GS_OK
+               : GS_ERR_HIP;
 }
 
 }  // extern "C"

@@ -59,11 +59,11 @@ struct FwdPixel {
 __device__ __forceinline__ FwdPixel raster_fwd_walk(FwdLds& L, const QuarterCtx& t, const float* __restrict__ rec,
                                                     int64_t n, const uint32_t* __restrict__ ranges,
                                                     const uint32_t* __restrict__ vals,
-                                                    const uint16_t* __restrict__ masks)
+                                                    const uint16_t* __restrict__ masks, uint32_t cap)
 {
 #pragma clang fp contract(off)
     constexpr uint32_t SLOT_BYTES = 48, PAD_OFF = RW_BATCH * SLOT_BYTES;
-    const uint2 rg = *(const uint2*)(ranges + 2 * (uint64_t)t.tile_lin);
+    const uint2 rg = tile_range(ranges, t.tile_lin, cap);
     const float* rv = rec + (int64_t)t.view * n * GS_REC_FLOATS;
     float Tr = 1.f, C0 = 0.f, C1 = 0.f, C2 = 0.f;
     int32_t last = 0;
@@ -80,12 +80,12 @@ __device__ __forceinline__ FwdPixel raster_fwd_walk(FwdLds& L, const QuarterCtx&
     ChunkScan S = scan_start<false>(0, len, rg.x, masks, t, nullptr);
     Entry cur, nxt, nx2;
     uint32_t n_cur = take_batch<false>(S, cur, len, rg.x, vals, masks, t, nullptr, L.list);
-    gather_record(cur, rv);
+    gather_record(cur, rv, n);
     uint32_t n_nxt = take_batch<false>(S, nxt, len, rg.x, vals, masks, t, nullptr, L.list);
     while (n_cur > 0u || n_nxt > 0u || scan_left<false>(S, len)) {
         if (ballot(!done) == 0ull) break;
         stage_entry(cur, t.lane, L.rec);
-        gather_record(nxt, rv);
+        gather_record(nxt, rv, n);
         const uint32_t n_nx2 = take_batch<false>(S, nx2, len, rg.x, vals, masks, t, nullptr, L.list);
         // per row, the staged entries of its sub-block in list order, as
         // record offsets; the rest of the row's list is the padding slot. A

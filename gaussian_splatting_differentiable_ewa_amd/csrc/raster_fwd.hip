@@ -14,8 +14,8 @@ template <bool L1>
 __device__ __forceinline__ void raster_fwd_body(const float* __restrict__ rec, int64_t n,
                                                 const uint32_t* __restrict__ ranges,
                                                 const uint32_t* __restrict__ vals,
-                                                const uint16_t* __restrict__ masks, int W, int H, int TX, int T,
-                                                int row0, float bg0, float bg1, float bg2, float* __restrict__ image,
+                                                const uint16_t* __restrict__ masks, uint32_t cap, int W, int H,
+                                                int TX, int T, int row0, float bg0, float bg1, float bg2, float* __restrict__ image,
                                                 float* __restrict__ T_final, int32_t* __restrict__ n_contrib,
                                                 const float* __restrict__ target, float scale,
                                                 float* __restrict__ dL, double* __restrict__ partial)
@@ -37,7 +37,7 @@ __device__ __forceinline__ void raster_fwd_body(const float* __restrict__ rec, i
         tg1 = target[o + HW];
         tg2 = target[o + 2 * HW];
     }
-    const FwdPixel P = raster_fwd_walk(lds, t, rec, n, ranges, vals, masks);
+    const FwdPixel P = raster_fwd_walk(lds, t, rec, n, ranges, vals, masks, cap);
     float ad = 0.f;  // |I - I*| summed over the channels
     if (t.inside) {
         const float i0 = P.C0 + P.Tr * bg0, i1 = P.C1 + P.Tr * bg1, i2 = P.C2 + P.Tr * bg2;
@@ -62,26 +62,26 @@ __device__ __forceinline__ void raster_fwd_body(const float* __restrict__ rec, i
 __global__ __launch_bounds__(RW_THREADS) void k_raster_fwd(const float* __restrict__ rec, int64_t n,
                                                            const uint32_t* __restrict__ ranges,
                                                            const uint32_t* __restrict__ vals,
-                                                           const uint16_t* __restrict__ masks, int W, int H, int TX,
-                                                           int T, int row0, float bg0, float bg1, float bg2,
-                                                           float* __restrict__ image, float* __restrict__ T_final,
-                                                           int32_t* __restrict__ n_contrib)
+                                                           const uint16_t* __restrict__ masks, uint32_t cap, int W,
+                                                           int H, int TX, int T, int row0, float bg0, float bg1,
+                                                           float bg2, float* __restrict__ image,
+                                                           float* __restrict__ T_final, int32_t* __restrict__ n_contrib)
 {
-    raster_fwd_body<false>(rec, n, ranges, vals, masks, W, H, TX, T, row0, bg0, bg1, bg2, image, T_final, n_contrib, nullptr, 0.f,
+    raster_fwd_body<false>(rec, n, ranges, vals, masks, cap, W, H, TX, T, row0, bg0, bg1, bg2, image, T_final, n_contrib, nullptr, 0.f,
                            nullptr, nullptr);
 }
 
 __global__ __launch_bounds__(RW_THREADS) void k_raster_fwd_l1(const float* __restrict__ rec, int64_t n,
                                                               const uint32_t* __restrict__ ranges,
                                                               const uint32_t* __restrict__ vals,
-                                                              const uint16_t* __restrict__ masks, int W, int H, int TX,
-                                                              int T, int row0, float bg0, float bg1, float bg2,
-                                                              float* __restrict__ image, float* __restrict__ T_final,
-                                                              int32_t* __restrict__ n_contrib,
+                                                              const uint16_t* __restrict__ masks, uint32_t cap, int W,
+                                                              int H, int TX, int T, int row0, float bg0, float bg1,
+                                                              float bg2, float* __restrict__ image,
+                                                              float* __restrict__ T_final, int32_t* __restrict__ n_contrib,
                                                               const float* __restrict__ target, float scale,
                                                               float* __restrict__ dL, double* __restrict__ partial)
 {
-    raster_fwd_body<true>(rec, n, ranges, vals, masks, W, H, TX, T, row0, bg0, bg1, bg2, image, T_final, n_contrib, target, scale,
+    raster_fwd_body<true>(rec, n, ranges, vals, masks, cap, W, H, TX, T, row0, bg0, bg1, bg2, image, T_final, n_contrib, target, scale,
                           dL, partial);
 }
 
@@ -100,6 +100,13 @@ __global__ __launch_bounds__(256) void k_loss_partials(const double* __restrict_
     if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = acc;
     __syncthreads();
     if (threadIdx.x == 0) atomicAdd(loss, (((s_w[0] + s_w[1]) + s_w[2]) + s_w[3]) * scale);
+}
+
+// The raster passes' exponential, element-wise (for checks of its error).
+__global__ __launch_bounds__(256) void k_raster_exp(const float* __restrict__ x, float* __restrict__ y, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) y[i] = exp_fast(x[i]);
 }
 
 hipError_t loss_from_partials(const double* partial, int64_t count, double scale, double* loss, bool accumulate,
@@ -128,19 +135,20 @@ size_t gs_rasterize_fwd_l1_workspace_bytes(int32_t n_views, int32_t width, int32
 }
 
 gs_status gs_rasterize_fwd_l1(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
-                              const uint16_t* masks, const gs_camera* cams, int32_t n_views, int32_t row0,
+                              const uint16_t* masks, uint64_t capacity, const gs_camera* cams, int32_t n_views, int32_t row0,
                               int32_t rows, const float* bg, const float* target,
                               float scale, float* image, float* T_final, int32_t* n_contrib, float* dL_dimage,
                               double* loss, int32_t accumulate, void* ws, size_t ws_bytes, void* stream)
 {
     RasterArgs a;
-    if (!raster_args(rec, n, ranges, vals, masks, cams, n_views, row0, rows, bg, a)) return GS_ERR_INVALID_ARGUMENT;
+    if (!raster_args(rec, n, ranges, vals, masks, capacity, cams, n_views, row0, rows, bg, a))
+        return GS_ERR_INVALID_ARGUMENT;
     if (!T_final || !n_contrib || !target || !dL_dimage || !loss || !ws) return GS_ERR_INVALID_ARGUMENT;
     if (ws_bytes < (size_t)a.n_blocks * sizeof(double)) return GS_ERR_INVALID_ARGUMENT;
     hipStream_t s = (hipStream_t)stream;
     double* partial = (double*)ws;
     hipLaunchKernelGGL(k_raster_fwd_l1, dim3((unsigned)a.n_blocks), dim3(RW_THREADS), 0, s, rec, n, ranges, vals,
-                       masks, a.dc.width, a.dc.height, a.dc.tiles_x, a.T, a.row0, bg[0], bg[1], bg[2], image, T_final,
+                       masks, a.cap, a.dc.width, a.dc.height, a.dc.tiles_x, a.T, a.row0, bg[0], bg[1], bg[2], image, T_final,
                        n_contrib, target, scale, dL_dimage, partial);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     return loss_from_partials(partial, a.n_blocks, (double)scale, loss, accumulate != 0, s) == hipSuccess ? GS_OK
@@ -148,16 +156,25 @@ gs_status gs_rasterize_fwd_l1(const float* rec, int64_t n, const uint32_t* range
 }
 
 gs_status gs_rasterize_fwd(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
-                           const uint16_t* masks, const gs_camera* cams, int32_t n_views, int32_t row0, int32_t rows,
+                           const uint16_t* masks, uint64_t capacity, const gs_camera* cams, int32_t n_views, int32_t row0, int32_t rows,
                            const float* bg, float* image, float* T_final,
                            int32_t* n_contrib, void* stream)
 {
     RasterArgs a;
-    if (!raster_args(rec, n, ranges, vals, masks, cams, n_views, row0, rows, bg, a)) return GS_ERR_INVALID_ARGUMENT;
+    if (!raster_args(rec, n, ranges, vals, masks, capacity, cams, n_views, row0, rows, bg, a))
+        return GS_ERR_INVALID_ARGUMENT;
     if (!image || !T_final || !n_contrib) return GS_ERR_INVALID_ARGUMENT;
     hipLaunchKernelGGL(k_raster_fwd, dim3((unsigned)a.n_blocks), dim3(RW_THREADS), 0, (hipStream_t)stream, rec, n,
-                       ranges, vals, masks, a.dc.width, a.dc.height, a.dc.tiles_x, a.T, a.row0, bg[0], bg[1], bg[2],
+                       ranges, vals, masks, a.cap, a.dc.width, a.dc.height, a.dc.tiles_x, a.T, a.row0, bg[0], bg[1], bg[2],
                        image, T_final, n_contrib);
+    return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
+}
+
+gs_status gs_raster_exp(const float* x, float* y, int64_t n, void* stream)
+{
+    if (n < 0 || (n > 0 && (!x || !y)) || n >= ((int64_t)1 << 40)) return GS_ERR_INVALID_ARGUMENT;
+    if (n == 0) return GS_OK;
+    hipLaunchKernelGGL(k_raster_exp, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, x, y, n);
     return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
 }
 

@@ -240,7 +240,8 @@ __global__ __launch_bounds__(TR_THREADS) void k_tl_ranges(const uint32_t* __rest
 __global__ __launch_bounds__(256) void k_bin_fill(const float* __restrict__ rec, const uint16_t* __restrict__ rect,
                                                   const float* __restrict__ depth, const BinGrid G, const uint32_t* __restrict__ table,
                                                   const uint32_t* __restrict__ starts, uint2* __restrict__ pairs,
-                                                  uint64_t capacity, int32_t* __restrict__ overflow)
+                                                  uint64_t capacity, int32_t* __restrict__ overflow,
+                                                  int32_t* __restrict__ sticky)
 {
     __shared__ uint32_t cur[BAND_TILES];
     const BinBlock B = bin_block(G);
@@ -278,7 +279,10 @@ __global__ __launch_bounds__(256) void k_bin_fill(const float* __restrict__ rec,
                 }
         }
     }
-    if (over) *overflow = 1;
+    if (over) {
+        *overflow = 1;
+        if (sticky) *sticky = 1;
+    }
 }
 
 // Where a kernel writes the id of a tile's entry, its mask too (when wanted).
@@ -298,7 +302,7 @@ __device__ __forceinline__ void write_mask(const MaskOut& mo, int64_t tile_lin, 
     Entry E;
     E.valid = true;
     E.gid = id;
-    gather_record(E, mo.rec + view * mo.n * GS_REC_FLOATS);
+    gather_record(E, mo.rec + view * mo.n * GS_REC_FLOATS, mo.n);
     mo.masks[pos] = (uint16_t)tile_mask16(E, tx * 16, ty * 16, mo.W, mo.H);
 }
 
@@ -326,7 +330,7 @@ __device__ __forceinline__ void write_ids_masks(const MaskOut& mo, int64_t tile_
             if (E[k].valid) vals[start + i0 + (uint32_t)k * STRIDE] = E[k].gid;
         if (!mo.masks) continue;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) gather_record(E[k], rv);
+        for (int k = 0; k < 4; ++k) gather_record(E[k], rv, mo.n);
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             if (E[k].valid) mo.masks[start + i0 + (uint32_t)k * STRIDE] = (uint16_t)tile_mask16(E[k], tx * 16, ty * 16, mo.W, mo.H);
@@ -887,8 +891,8 @@ size_t gs_tile_lists_workspace_bytes(int64_t n, int32_t n_views, int32_t width, 
 
 gs_status gs_tile_lists(const float* rec, const uint16_t* rect, const float* depth, int64_t n, int32_t n_views, int32_t width,
                         int32_t height, int32_t row0, int32_t rows, uint32_t* vals, uint16_t* masks,
-                        uint64_t capacity, uint32_t* ranges, int32_t* overflow, void* ws, size_t ws_bytes,
-                        void* stream)
+                        uint64_t capacity, uint32_t* ranges, int32_t* overflow, int32_t* sticky, void* ws,
+                        size_t ws_bytes, void* stream)
 {
     if (!tl_sizes_ok(n, n_views, width, height)) return GS_ERR_INVALID_ARGUMENT;
     if (row0 < 0 || rows < 1 || row0 + rows > gs_tiles_y(height)) return GS_ERR_INVALID_ARGUMENT;
@@ -925,7 +929,7 @@ gs_status gs_tile_lists(const float* rec, const uint16_t* rect, const float* dep
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     if (n == 0) return GS_OK;
     hipLaunchKernelGGL(k_bin_fill, dim3(bin_blocks), dim3(256), 0, s, rec, rect, depth, G, table, totals, pairs,
-                       capacity, overflow);
+                       capacity, overflow, sticky);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     MaskOut mo;
     mo.masks = masks;

@@ -42,7 +42,7 @@ __global__ __launch_bounds__(TM_THREADS) void k_tile_masks(const float* __restri
     Entry E;
     E.valid = true;
     E.gid = vals[p];
-    gather_record(E, rec + (int64_t)view * n * GS_REC_FLOATS);
+    gather_record(E, rec + (int64_t)view * n * GS_REC_FLOATS, n);
     masks[p] = (uint16_t)tile_mask16(E, tx * 16, ty * 16, W, H);
 }
 

@@ -175,6 +175,15 @@ CONFIGS = {
 }
 
 
+# A parity-test scene beside the five workloads: the object-scale recipe
+# (config 1's distributions) seen by two views of 250x190 pixels, so that
+# neither image side is a multiple of the 16-pixel tile (the last tile column
+# is 10 pixels wide, the last tile row 14 pixels tall).
+RAGGED = SceneConfig("ragged-200k-sh3-2x250x190", 10, 11, 200_000, 3,
+                     (-3.0, -3.0, 3.0), (3.0, 3.0, 12.0), 32, 0.3, -4.0, 0.5,
+                     250, 190, 195.3125, yaws=(0.0, 6.0), orbit_centre=(0.0, 0.0, 7.5))
+
+
 def _normal(rng, shape_or_out, mean, std):
     out = shape_or_out
     rng.standard_normal(dtype=np.float32, out=out)

@@ -107,8 +107,11 @@ class Buffers:
 
     # ---- stages ------------------------------------------------------------
     def preprocess(self, params):
+        """Records, rectangles, scanned counts, the compact depths, and the
+        2D-gradient records of every visible (view, Gaussian) set to zero
+        (the raster passes add to them)."""
         L.gs_preprocess(params, self.n, self.sh_degree, self.cams, self.rec, self.rect, self.offsets,
-                        self.total, self.pre_ws, depth=self.depth)
+                        self.total, self.pre_ws, depth=self.depth, grad2d=self.grad2d)
 
     def lists_without_count(self) -> bool:
         """Whether the lists can be built before K is known on the host."""
@@ -130,11 +133,12 @@ class Buffers:
         L.gs_tile_masks(self.rec, self.n, self.ranges, self.sorted_vals, self.capacity, self.cams, self.masks,
                         self.tm_ws)
 
-    def build_lists(self, read_count: bool = True):
-        """The lists and ranges alone (see ``intersections``)."""
+    def build_lists(self, read_count: bool = True, sticky=None):
+        """The lists and ranges alone (see ``intersections``); `sticky`, a
+        device flag the binned builder sets with its overflow flag."""
         if not read_count and self.lists_without_count():
             L.gs_tile_lists(self.rec, self.rect, self.n, self.V, self.W, self.H, self.vals, self.capacity,
-                            self.ranges, self.overflow, self.tl_ws, masks=self.masks, depth=self.depth)
+                            self.ranges, self.overflow, self.tl_ws, masks=self.masks, depth=self.depth, sticky=sticky)
             return
         self.K = int(self.total.item())
         if self.K >= 2 ** 32:
@@ -171,11 +175,13 @@ class Buffers:
                               self.fwd_l1_ws, accumulate=accumulate, row0=row0, rows=rows)
 
     def rasterize_fwd_bwd_l1(self, target, bg=(0.0, 0.0, 0.0), outputs: bool = False, image: bool = False,
-                             row0: int = 0, rows: Optional[int] = None, accumulate: bool = False):
+                             row0: int = 0, rows: Optional[int] = None, accumulate: bool = False,
+                             accumulate_grad2d: Optional[bool] = None):
         """Forward raster, L1 loss and backward raster in one pass (over a
         window of tile rows when given): the loss and the 2D gradients (both
-        zeroed first unless `accumulate`); T_final, n_contrib and dL/dimage
-        are written only with `outputs`, the image only with `image`."""
+        zeroed first unless `accumulate`; `accumulate_grad2d` decides for the
+        2D gradients alone when given); T_final, n_contrib and dL/dimage are
+        written only with `outputs`, the image only with `image`."""
         scale = 1.0 / (3.0 * self.H * self.W * self.V)
         L.gs_rasterize_fwd_bwd_l1(self.rec, self.n, self.ranges, self.sorted_vals, self.masks, self.cams, bg, target,
                                   scale, self.loss, self.grad2d, self.fwd_l1_ws,
@@ -183,7 +189,7 @@ class Buffers:
                                   T_final=self.T_final if outputs else None,
                                   n_contrib=self.n_contrib if outputs else None,
                                   dL_dimage=self.dL if outputs else None,
-                                  accumulate=accumulate, row0=row0, rows=rows)
+                                  accumulate=accumulate, accumulate_grad2d=accumulate_grad2d, row0=row0, rows=rows)
 
     def backward(self, params, grad, bg=(0.0, 0.0, 0.0)):
         L.gs_rasterize_bwd(self.rec, self.n, self.ranges, self.sorted_vals, self.masks, self.cams, bg, self.T_final,
@@ -298,10 +304,10 @@ class TrainStep:
         """The stages that ``step(marks)`` brackets, in order."""
         tail = ["preprocess_bwd_adam"] if self.fused_adam else ["preprocess_bwd", "adam"]
         if self.band_rows is not None:
-            return ["preprocess", "grad2d_zero", "bands"] + tail
+            return ["preprocess", "bands"] + tail
         if self.fused_raster:
-            return ["preprocess", "intersections", "tile_masks", "grad2d_zero", "raster_fwd_bwd"] + tail
-        return ["preprocess", "intersections", "tile_masks", "raster_fwd_loss", "grad2d_zero", "raster_bwd"] + tail
+            return ["preprocess", "intersections", "tile_masks", "raster_fwd_bwd"] + tail
+        return ["preprocess", "intersections", "tile_masks", "raster_fwd_loss", "raster_bwd"] + tail
 
     def _bands(self, mark):
         """The image in windows of band_rows tile rows: each window's lists
@@ -311,11 +317,8 @@ class TrainStep:
         flag) and doubled, and the window redone, when they did not fit."""
         b = self.buf
         mark(0)
-        b.preprocess(self.params)
+        b.preprocess(self.params)  # also zeroes the visible 2D-gradient records
         mark(1)
-        b.grad2d.zero_()
-        b.loss.zero_()
-        mark(2)
         if b.capacity == 0:
             nb = -(-b.TY // self.band_rows)
             b.ensure_capacity(max(2 * int(b.total.item()) // nb, 1 << 16))
@@ -327,16 +330,17 @@ class TrainStep:
                 if int(b.overflow.item()) == 0:
                     break
                 b.ensure_capacity(2 * b.capacity, slack=1.0)
+            # the loss is overwritten by the first window and added to by the others
             if self.fused_raster:
                 b.rasterize_fwd_bwd_l1(self.target, self.bg, outputs=self.write_image, image=self.write_image,
-                                       row0=row0, rows=rows, accumulate=True)
+                                       row0=row0, rows=rows, accumulate=i > 0, accumulate_grad2d=True)
                 continue
             b.rasterize_loss_l1(self.target, self.bg, image=self.write_image, row0=row0, rows=rows,
-                                accumulate=True)
+                                accumulate=i > 0)
             L.gs_rasterize_bwd(b.rec, b.n, b.ranges, b.sorted_vals, b.masks, b.cams, self.bg, b.T_final, b.n_contrib,
                                b.dL, b.grad2d, accumulate=True, row0=row0, rows=rows)
         b.K = int(b.total.item())
-        mark(3)
+        mark(2)
 
     def step(self, marks=None):
         """One step. `marks`, if given, holds len(stage_names) + 1 events,
@@ -348,38 +352,31 @@ class TrainStep:
         self.t += 1
         if self.band_rows is not None:
             self._bands(mark)
-            m0 = 4
+            m0 = 3
         else:
             mark(0)
-            b.preprocess(self.params)
+            b.preprocess(self.params)  # also zeroes the visible 2D-gradient records
             mark(1)
-            b.build_lists(read_count=not deferred)
-            if deferred:
-                torch.maximum(self.sticky, b.overflow, out=self.sticky)
+            # an overflow of the lists also sets the sticky flag, which voids
+            # this step's update and every later one until it is checked
+            b.build_lists(read_count=not deferred, sticky=self.sticky if deferred else None)
             mark(2)
             b.tile_masks()
             mark(3)
             if self.fused_raster:
-                # 2D gradients and loss cleared by launches of their own, so
-                # that a timing mark brackets the raster pass alone
-                b.grad2d.zero_()
-                b.loss.zero_()
-                mark(4)
+                # the loss is overwritten, the 2D gradients added to the
+                # records the preprocess zeroed
                 b.rasterize_fwd_bwd_l1(self.target, self.bg, outputs=self.write_image, image=self.write_image,
-                                       accumulate=True)
-                mark(5)
-                m0 = 6
+                                       accumulate=False, accumulate_grad2d=True)
+                mark(4)
+                m0 = 5
             else:
                 b.rasterize_loss_l1(self.target, self.bg, image=self.write_image)
                 mark(4)
-                # the 2D-gradient buffer is cleared on its own (a launch of its
-                # own, so that a timing mark can bracket the backward raster)
-                b.grad2d.zero_()
-                mark(5)
                 L.gs_rasterize_bwd(b.rec, b.n, b.ranges, b.sorted_vals, b.masks, b.cams, self.bg, b.T_final,
                                    b.n_contrib, b.dL, b.grad2d, accumulate=True)
-                mark(6)
-                m0 = 7
+                mark(5)
+                m0 = 6
         skip = self.sticky if deferred else None
         if self.fused_adam:
             L.gs_preprocess_bwd_adam(self.params, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, self.m, self.v, self.lr,

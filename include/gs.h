@@ -68,11 +68,15 @@
 extern "C" {
 #endif
 
-#define GS_ABI_VERSION 1
+#define GS_ABI_VERSION 2
 #define GS_TILE 16
 #define GS_MAX_VIEWS 16
 #define GS_REC_FLOATS 12 /* floats per projected record */
 #define GS_GRAD2D_ROWS 9 /* 2D gradient rows per (view, Gaussian) */
+
+/* `accumulate` flags of gs_rasterize_fwd_bwd_l1 */
+#define GS_ACCUMULATE_LOSS 1   /* add to *loss instead of overwriting it */
+#define GS_ACCUMULATE_GRAD2D 2 /* add to grad2d instead of zeroing it first */
 
 typedef enum gs_status {
     GS_OK = 0,
@@ -151,6 +155,11 @@ size_t gs_sort_workspace_bytes(uint64_t n_keys);
  *   depth    out [n_views][n] fp32, or NULL: the view-space depth of each
  *            entry that is not culled (GS_REC_DEPTH of its record; culled
  *            entries are not written), a compact copy for gs_tile_lists
+ *   grad2d   out [n_views][n][9] fp32, or NULL: the 2D-gradient record of
+ *            every entry that is not culled is set to zero (the records the
+ *            raster passes add to and gs_preprocess_bwd reads; the records of
+ *            culled entries are not written), so that the raster passes can
+ *            accumulate without a separate clear
  *   offsets  out [n_views * n + 1] uint32: offsets[i] = sum of the tile counts
  *            of entries before i (low 32 bits); the count of entry i is the
  *            area of its rectangle
@@ -162,8 +171,8 @@ size_t gs_sort_workspace_bytes(uint64_t n_keys);
  */
 gs_status gs_preprocess(const float* params, int64_t n, int32_t sh_degree, const gs_camera* cams,
                         int32_t n_views, float* rec, uint16_t* rect, float* depth,
-                        uint32_t* offsets, uint64_t* total, void* ws, size_t ws_bytes,
-                        void* stream);
+                        float* grad2d, uint32_t* offsets, uint64_t* total, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /*
  * gs_emit_intersections -- one key per (view, Gaussian, tile) overlap, the
@@ -230,6 +239,9 @@ size_t gs_tile_lists_workspace_bytes(int64_t n, int32_t n_views, int32_t width, 
  *   overflow   device int32: cleared, then set to 1 if the intersections
  *              exceed capacity (the lists are then incomplete, and the ranges
  *              are cut at capacity so that their readers stay in bounds)
+ *   sticky     device int32 or NULL: set to 1 together with overflow, and
+ *              never cleared (a flag that outlives the call, e.g. one that
+ *              voids every later update until the caller has checked it)
  *   ws         device workspace of gs_tile_lists_workspace_bytes(...)
  * Errors: as gs_emit_intersections, plus a small workspace, capacity >= 2^32,
  * a window outside the tile rows
@@ -238,7 +250,7 @@ size_t gs_tile_lists_workspace_bytes(int64_t n, int32_t n_views, int32_t width, 
 gs_status gs_tile_lists(const float* rec, const uint16_t* rect, const float* depth, int64_t n, int32_t n_views,
                         int32_t width, int32_t height, int32_t row0, int32_t rows, uint32_t* vals,
                         uint16_t* masks, uint64_t capacity, uint32_t* ranges, int32_t* overflow,
-                        void* ws, size_t ws_bytes, void* stream);
+                        int32_t* sticky, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * gs_tile_ranges -- for every (view, tile) id t = key >> 32, the range
@@ -288,6 +300,9 @@ gs_status gs_tile_masks(const float* rec, int64_t n, const uint32_t* ranges, con
  *   n_contrib out [V][H][W] int32: 1-based list position of the last blended
  *             entry, 0 if none
  *   masks     the lists' sub-block masks of gs_tile_masks
+ *   capacity  slots of vals and masks (< 2^32): every range is cut at it and
+ *             an id >= n reads as an entry of opacity 0, so that no lists
+ *             buffer, however stale, sends a walk outside vals, masks or rec
  *   row0, rows the window of tile rows the lists and ranges cover (as
  *             gs_tile_lists; 0 and gs_tiles_y(height) for the whole image):
  *             only the window's pixels are written
@@ -296,7 +311,8 @@ gs_status gs_tile_masks(const float* rec, int64_t n, const uint32_t* ranges, con
  * outside the tile rows.
  */
 gs_status gs_rasterize_fwd(const float* rec, int64_t n, const uint32_t* ranges,
-                           const uint32_t* vals, const uint16_t* masks, const gs_camera* cams,
+                           const uint32_t* vals, const uint16_t* masks, uint64_t capacity,
+                           const gs_camera* cams,
                            int32_t n_views, int32_t row0, int32_t rows,
                            const float* bg, float* image, float* T_final, int32_t* n_contrib,
                            void* stream);
@@ -325,6 +341,7 @@ size_t gs_rasterize_fwd_l1_workspace_bytes(int32_t n_views, int32_t width, int32
  * sum |I - target| (views averaged as for gs_loss_l1: "On Scaling Up 3D
  * Gaussian Splatting Training", answer on the Independent Gradients
  * Hypothesis). T_final, n_contrib and dL_dimage equal those of the two calls.
+ *   capacity  as gs_rasterize_fwd
  *   target    [V][3][H][W]
  *   image     out [V][3][H][W], or null when not wanted
  *   loss      device double: overwritten, or added to when `accumulate`
@@ -333,7 +350,8 @@ size_t gs_rasterize_fwd_l1_workspace_bytes(int32_t n_views, int32_t width, int32
  * small workspace.
  */
 gs_status gs_rasterize_fwd_l1(const float* rec, int64_t n, const uint32_t* ranges,
-                              const uint32_t* vals, const uint16_t* masks, const gs_camera* cams,
+                              const uint32_t* vals, const uint16_t* masks, uint64_t capacity,
+                              const gs_camera* cams,
                               int32_t n_views, int32_t row0, int32_t rows,
                               const float* bg, const float* target, float scale, float* image,
                               float* T_final, int32_t* n_contrib, float* dL_dimage, double* loss,
@@ -345,12 +363,14 @@ gs_status gs_rasterize_fwd_l1(const float* rec, int64_t n, const uint32_t* range
  * quantities of every (view, Gaussian):
  *   grad2d  [V][n][9] fp32 (rows GS_G2_*): du dv dA dB dC dopacity dr dg db;
  *           zeroed first unless `accumulate` is non-zero
- * Inputs as in gs_rasterize_fwd plus its T_final and n_contrib and dL/dimage.
+ * Inputs as in gs_rasterize_fwd (capacity included) plus its T_final and
+ * n_contrib and dL/dimage.
  * Floating-point atomics make the summation order, and so the last bits, vary
  * between runs. Errors: as gs_rasterize_fwd.
  */
 gs_status gs_rasterize_bwd(const float* rec, int64_t n, const uint32_t* ranges,
-                           const uint32_t* vals, const uint16_t* masks, const gs_camera* cams,
+                           const uint32_t* vals, const uint16_t* masks, uint64_t capacity,
+                           const gs_camera* cams,
                            int32_t n_views, int32_t row0, int32_t rows,
                            const float* bg, const float* T_final, const int32_t* n_contrib,
                            const float* dL_dimage, float* grad2d, int32_t accumulate,
@@ -365,19 +385,21 @@ gs_status gs_rasterize_bwd(const float* rec, int64_t n, const uint32_t* ranges,
  * with T_final, n_contrib and dL/dimage kept on chip. Results equal those of
  * the two calls (image, T_final, n_contrib, dL/dimage and loss bit for bit;
  * grad2d up to the order of its floating-point atomic additions).
+ *   capacity   as gs_rasterize_fwd
  *   target     [V][3][H][W]
  *   image      out [V][3][H][W], or null (not written)
  *   T_final    out [V][H][W], or null
  *   n_contrib  out [V][H][W], or null
  *   dL_dimage  out [V][3][H][W], or null
- *   loss       device double: overwritten, or added to when `accumulate`
+ *   loss       device double: overwritten, or added to when `accumulate` has
+ *              GS_ACCUMULATE_LOSS
  *   grad2d     [V][n][9] fp32 as in gs_rasterize_bwd: zeroed first unless
- *              `accumulate`
+ *              `accumulate` has GS_ACCUMULATE_GRAD2D
  *   ws         device workspace of gs_rasterize_fwd_bwd_l1_workspace_bytes(...):
  *              the per-quarter loss partials and the order in which the pass
  *              takes the tiles (longest lists first)
- * Errors: as gs_rasterize_fwd, plus null target / loss / ws / grad2d (n > 0)
- * or a small workspace.
+ * Errors: as gs_rasterize_fwd, plus null target / loss / ws / grad2d (n > 0),
+ * a small workspace or an `accumulate` with other bits than the two flags.
  */
 /* Workspace of gs_rasterize_fwd_bwd_l1 (bytes): one double per 8x8 quarter,
  * one 32-bit tile index per tile of every view, and eight 32-bit class counts
@@ -385,7 +407,7 @@ gs_status gs_rasterize_bwd(const float* rec, int64_t n, const uint32_t* ranges,
 size_t gs_rasterize_fwd_bwd_l1_workspace_bytes(int32_t n_views, int32_t width, int32_t height);
 
 gs_status gs_rasterize_fwd_bwd_l1(const float* rec, int64_t n, const uint32_t* ranges,
-                                  const uint32_t* vals, const uint16_t* masks,
+                                  const uint32_t* vals, const uint16_t* masks, uint64_t capacity,
                                   const gs_camera* cams, int32_t n_views, int32_t row0,
                                   int32_t rows, const float* bg, const float* target, float scale,
                                   float* image, float* T_final, int32_t* n_contrib,
@@ -456,6 +478,29 @@ gs_status gs_adam_step(float* params, const float* grad, float* m, float* v, int
 gs_status gs_adam_step_unless(float* params, const float* grad, float* m, float* v, int64_t count,
                               double lr, double beta1, double beta2, double eps, int64_t step,
                               const int32_t* skip, void* stream);
+
+/*
+ * gs_raster_exp -- the exponential the raster passes apply to a pair's power,
+ * element-wise: y[i] = 2^fl(x[i] * fl32(log2 e)) on the hardware exp2. The
+ * alpha compositing rules (alpha >= 1/255, the 0.99 clamp, T' < 1e-4) are
+ * decisions on o exp(power), so a reference implementation that uses another
+ * exp must know how far this one may lie from it; this call lets a test
+ * measure that.
+ *   x, y  device fp32 arrays of n elements (y may alias x)
+ * Errors: null pointers (n > 0), n < 0 or n >= 2^40.
+ */
+gs_status gs_raster_exp(const float* x, float* y, int64_t n, void* stream);
+
+/*
+ * gs_stream_copy -- a plain device-to-device copy of `bytes` bytes (16-byte
+ * vectors, a grid that fills the chip): it reads and writes exactly 2 x bytes
+ * of device memory, the reference for the achievable HBM bandwidth and for
+ * scaling the profiler's traffic counters of the other kernels.
+ *   dst, src  device memory, 16-byte aligned, not overlapping
+ *   bytes     a multiple of 16
+ * Errors: null pointers (bytes > 0), misaligned pointers or size.
+ */
+gs_status gs_stream_copy(void* dst, const void* src, uint64_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

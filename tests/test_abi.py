@@ -37,7 +37,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_queries(lib):
-    assert L.abi_version() == 1
+    assert L.abi_version() == L.ABI_VERSION == 2
     assert [L.param_rows(d) for d in range(4)] == [S.param_rows(d) for d in range(4)]
     assert L.param_rows(4) == -1
     assert lib.gs_tiles_x(1920) == 120 and lib.gs_tiles_y(1080) == 68 and lib.gs_tiles_x(1) == 1
@@ -56,24 +56,36 @@ def _cam(**kw):
     return S.Camera(**{**c.__dict__, **kw})
 
 
+def _call(f, names, defaults, **kw):
+    """Call f with its arguments given by name over a set of valid defaults."""
+    unknown = set(kw) - set(names)
+    assert not unknown, unknown
+    return f(*[kw.get(n, defaults[n]) for n in names])
+
+
 def test_invalid_arguments_rejected_on_host(lib):
     INV = L.GS_ERR_INVALID_ARGUMENT
     cams = L.cameras(S.CONFIGS[0].cameras())
     fake = ctypes.c_void_p(16)  # never dereferenced: validation fails first
     ws = ctypes.c_size_t(1 << 20)
     # gs_preprocess
-    assert lib.gs_preprocess(fake, -1, 0, cams, 1, fake, fake, None, fake, fake, fake, ws, None) == INV
-    assert lib.gs_preprocess(fake, 10, 4, cams, 1, fake, fake, None, fake, fake, fake, ws, None) == INV
-    assert lib.gs_preprocess(fake, 10, 0, cams, 0, fake, fake, None, fake, fake, fake, ws, None) == INV
-    assert lib.gs_preprocess(fake, 10, 0, cams, 17, fake, fake, None, fake, fake, fake, ws, None) == INV
-    assert lib.gs_preprocess(fake, 10, 0, cams, 1, fake, fake, None, None, fake, fake, ws, None) == INV
-    assert lib.gs_preprocess(fake, 10, 0, cams, 1, fake, fake, None, fake, fake, fake, 0, None) == INV
-    two = L.cameras([_cam(), _cam(width=128)])
-    assert lib.gs_preprocess(fake, 10, 0, two, 2, fake, fake, None, fake, fake, fake, ws, None) == INV
-    bad_f = L.cameras([_cam(fx=0.0)])
-    assert lib.gs_preprocess(fake, 10, 0, bad_f, 1, fake, fake, None, fake, fake, fake, ws, None) == INV
-    huge = L.cameras([_cam(width=16 * 70000)])
-    assert lib.gs_preprocess(fake, 10, 0, huge, 1, fake, fake, None, fake, fake, fake, ws, None) == INV
+    pre_names = ["params", "n", "sh", "cams", "V", "rec", "rect", "depth", "grad2d", "offsets", "total", "ws",
+                 "ws_bytes", "stream"]
+    pre_ok = dict(params=fake, n=10, sh=0, cams=cams, V=1, rec=fake, rect=fake, depth=None, grad2d=None, offsets=fake,
+                  total=fake, ws=fake, ws_bytes=ws, stream=None)
+
+    def pre(**kw):
+        return _call(lib.gs_preprocess, pre_names, pre_ok, **kw)
+
+    assert pre(n=-1) == INV
+    assert pre(sh=4) == INV
+    assert pre(V=0) == INV
+    assert pre(V=17) == INV
+    assert pre(offsets=None) == INV
+    assert pre(ws_bytes=0) == INV
+    assert pre(cams=L.cameras([_cam(), _cam(width=128)]), V=2) == INV
+    assert pre(cams=L.cameras([_cam(fx=0.0)])) == INV
+    assert pre(cams=L.cameras([_cam(width=16 * 70000)])) == INV
     # gs_emit_intersections
     assert lib.gs_emit_intersections(fake, fake, fake, -1, 1, 256, 256, fake, fake, 10, fake, None) == INV
     assert lib.gs_emit_intersections(fake, fake, fake, 10, 1, 0, 256, fake, fake, 10, fake, None) == INV
@@ -90,65 +102,110 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert alt.value == 0
     # gs_tile_lists
     big = ctypes.c_size_t(1 << 40)
-    assert lib.gs_tile_lists(fake, fake, None, -1, 1, 256, 256, 0, 16, fake, None, 10, fake, fake, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, None, 10, 0, 256, 256, 0, 16, fake, None, 10, fake, fake, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, None, 10, 1, 256, 0, 0, 16, fake, None, 10, fake, fake, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, None, 10, 1, 256, 256, 0, 16, fake, None, 10, None, fake, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, None, 10, 1, 256, 256, 0, 16, fake, None, 10, fake, None, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, None, 10, 1, 256, 256, 0, 16, None, None, 10, fake, fake, fake, big, None) == INV
-    assert lib.gs_tile_lists(fake, fake, None, 10, 1, 256, 256, 0, 16, fake, None, 1 << 32, fake, fake, fake, big, None) == INV
+    tl_names = ["rec", "rect", "depth", "n", "V", "W", "H", "row0", "rows", "vals", "masks", "capacity", "ranges",
+                "overflow", "sticky", "ws", "ws_bytes", "stream"]
+    tl_ok = dict(rec=fake, rect=fake, depth=None, n=10, V=1, W=256, H=256, row0=0, rows=16, vals=fake, masks=None,
+                 capacity=10, ranges=fake, overflow=fake, sticky=None, ws=fake, ws_bytes=big, stream=None)
+
+    def tl(**kw):
+        return _call(lib.gs_tile_lists, tl_names, tl_ok, **kw)
+
+    assert tl(n=-1) == INV
+    assert tl(V=0) == INV
+    assert tl(H=0) == INV
+    assert tl(ranges=None) == INV
+    assert tl(overflow=None) == INV
+    assert tl(vals=None) == INV
+    assert tl(capacity=1 << 32) == INV
+    assert tl(row0=12, rows=5) == INV
     need = L.tile_lists_workspace_bytes(10, 1, 256, 256, 10)
     assert need > 0 and L.tile_lists_workspace_bytes(10, 0, 256, 256, 10) == 0
     assert L.tile_lists_workspace_bytes(10, 1, 16 * 8193, 256, 10) == 0
-    assert lib.gs_tile_lists(fake, fake, None, 10, 1, 256, 256, 0, 16, fake, None, 10, fake, fake, fake, need - 1, None) == INV
+    assert tl(ws_bytes=need - 1) == INV
     # gs_tile_ranges
     assert lib.gs_tile_ranges(fake, 10, -1, fake, None) == INV
     assert lib.gs_tile_ranges(None, 10, 4, fake, None) == INV
-    # raster
+    # raster: every call takes the list capacity, < 2^32, and needs vals and
+    # masks when it is non-zero
     bg = (ctypes.c_float * 3)(0, 0, 0)
     qws = L.rasterize_fwd_l1_workspace_bytes(1, 256, 256)
     assert qws == 16 * 16 * 4 * 8 and L.rasterize_fwd_l1_workspace_bytes(0, 256, 256) == 0
-    f1 = lib.gs_rasterize_fwd_l1
-    assert f1(fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, None, 1.0, None, fake, fake, fake, fake, 0, fake, qws, None) == INV
-    assert f1(fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, fake, 1.0, None, fake, fake, None, fake, 0, fake, qws, None) == INV
-    assert f1(fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, fake, 1.0, None, fake, fake, fake, None, 0, fake, qws, None) == INV
-    assert f1(fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, fake, 1.0, None, fake, fake, fake, fake, 0, fake,
-              qws - 8, None) == INV
-    # windows of tile rows outside the 16 rows of a 256-pixel image
-    assert f1(fake, 10, fake, fake, fake, cams, 1, 8, 9, bg, fake, 1.0, None, fake, fake, fake, fake, 0, fake, qws,
-              None) == INV
-    assert lib.gs_rasterize_fwd(fake, 10, fake, fake, fake, cams, 1, 0, 0, bg, fake, fake, fake, None) == INV
-    assert lib.gs_rasterize_bwd(fake, 10, fake, fake, fake, cams, 1, -1, 4, bg, fake, fake, fake, fake, 0, None) == INV
-    assert lib.gs_tile_lists(fake, fake, None, 10, 1, 256, 256, 12, 5, fake, None, 10, fake, fake, fake, big, None) == INV
-    assert f1(fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, fake, 1.0, None, fake, fake, fake, fake, 0, None, qws, None) == INV
-    assert f1(fake, 10, fake, fake, None, cams, 1, 0, 16, bg, fake, 1.0, None, fake, fake, fake, fake, 0, fake, qws, None) == INV
-    assert lib.gs_rasterize_fwd(fake, 10, fake, fake, fake, cams, 1, 0, 16, None, fake, fake, fake, None) == INV
-    assert lib.gs_rasterize_fwd(fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, None, fake, fake, None) == INV
-    assert lib.gs_rasterize_fwd(fake, -5, fake, fake, fake, cams, 1, 0, 16, bg, fake, fake, fake, None) == INV
-    assert lib.gs_rasterize_fwd(fake, 10, fake, fake, None, cams, 1, 0, 16, bg, fake, fake, fake, None) == INV  # no masks
-    assert lib.gs_rasterize_bwd(fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, fake, fake, None, fake, 0, None) == INV
-    assert lib.gs_rasterize_bwd(fake, 10, fake, fake, fake, cams, 0, 0, 16, bg, fake, fake, fake, fake, 0, None) == INV
-    assert lib.gs_rasterize_bwd(fake, 10, fake, fake, None, cams, 1, 0, 16, bg, fake, fake, fake, fake, 0, None) == INV
-    f2 = lib.gs_rasterize_fwd_bwd_l1
+    head = ["rec", "n", "ranges", "vals", "masks", "capacity", "cams", "V", "row0", "rows", "bg"]
+    head_ok = dict(rec=fake, n=10, ranges=fake, vals=fake, masks=fake, capacity=100, cams=cams, V=1, row0=0, rows=16,
+                   bg=bg)
+
+    def common_cases(f):
+        assert f(n=-5) == INV
+        assert f(masks=None) == INV
+        assert f(vals=None) == INV
+        assert f(capacity=1 << 32) == INV
+        assert f(bg=None) == INV
+        assert f(V=0) == INV
+        assert f(row0=8, rows=9) == INV  # a window outside the 16 tile rows of a 256-pixel image
+        assert f(row0=-1, rows=4) == INV
+        assert f(rows=0) == INV
+
+    fwd_names = head + ["image", "T_final", "n_contrib", "stream"]
+    fwd_ok = dict(head_ok, image=fake, T_final=fake, n_contrib=fake, stream=None)
+
+    def fwd(**kw):
+        return _call(lib.gs_rasterize_fwd, fwd_names, fwd_ok, **kw)
+
+    common_cases(fwd)
+    assert fwd(image=None) == INV
+    assert fwd(n_contrib=None) == INV
+
+    l1_names = head + ["target", "scale", "image", "T_final", "n_contrib", "dL", "loss", "accumulate", "ws",
+                       "ws_bytes", "stream"]
+    l1_ok = dict(head_ok, target=fake, scale=1.0, image=None, T_final=fake, n_contrib=fake, dL=fake, loss=fake,
+                 accumulate=0, ws=fake, ws_bytes=qws, stream=None)
+
+    def l1(**kw):
+        return _call(lib.gs_rasterize_fwd_l1, l1_names, l1_ok, **kw)
+
+    common_cases(l1)
+    assert l1(target=None) == INV
+    assert l1(dL=None) == INV
+    assert l1(loss=None) == INV
+    assert l1(ws=None) == INV
+    assert l1(ws_bytes=qws - 8) == INV
+
+    bwd_names = head + ["T_final", "n_contrib", "dL", "grad2d", "accumulate", "stream"]
+    bwd_ok = dict(head_ok, T_final=fake, n_contrib=fake, dL=fake, grad2d=fake, accumulate=0, stream=None)
+
+    def bwd(**kw):
+        return _call(lib.gs_rasterize_bwd, bwd_names, bwd_ok, **kw)
+
+    common_cases(bwd)
+    assert bwd(dL=None) == INV
+    assert bwd(grad2d=None) == INV
+
     fws = L.rasterize_fwd_bwd_l1_workspace_bytes(1, 256, 256)
     assert fws == 16 * 16 * (4 * 8 + 4) + 8 * 4 and L.rasterize_fwd_bwd_l1_workspace_bytes(1, 0, 256) == 0
-    ok = (fake, 10, fake, fake, fake, cams, 1, 0, 16, bg, fake, 1.0, None, None, None, None, fake, fake, 0, fake, fws,
-          None)
+    fb_names = head + ["target", "scale", "image", "T_final", "n_contrib", "dL", "loss", "grad2d", "accumulate", "ws",
+                       "ws_bytes", "stream"]
+    fb_ok = dict(head_ok, target=fake, scale=1.0, image=None, T_final=None, n_contrib=None, dL=None, loss=fake,
+                 grad2d=fake, accumulate=0, ws=fake, ws_bytes=fws, stream=None)
 
     def fb(**kw):
-        a = list(ok)
-        for i, v in kw.items():
-            a[int(i[1:])] = v
-        return f2(*a)
+        return _call(lib.gs_rasterize_fwd_bwd_l1, fb_names, fb_ok, **kw)
 
-    assert fb(a10=None) == INV  # target
-    assert fb(a16=None) == INV  # loss
-    assert fb(a17=None) == INV  # grad2d
-    assert fb(a19=None) == INV  # workspace
-    assert fb(a20=fws - 4) == INV
-    assert fb(a4=None) == INV  # masks
-    assert fb(a7=8, a8=9) == INV  # window outside the image
-    assert fb(a6=0) == INV  # no views
+    common_cases(fb)
+    assert fb(target=None) == INV
+    assert fb(loss=None) == INV
+    assert fb(grad2d=None) == INV
+    assert fb(ws=None) == INV
+    assert fb(ws_bytes=fws - 4) == INV
+    assert fb(accumulate=4) == INV  # only GS_ACCUMULATE_LOSS | GS_ACCUMULATE_GRAD2D
+    assert fb(accumulate=-1) == INV
+    # the diagnostic exp path and the plain copy
+    assert lib.gs_raster_exp(None, fake, 10, None) == INV
+    assert lib.gs_raster_exp(fake, fake, -1, None) == INV
+    assert lib.gs_raster_exp(None, None, 0, None) == L.GS_OK
+    assert lib.gs_stream_copy(fake, fake, 24, None) == INV  # not a multiple of 16
+    assert lib.gs_stream_copy(ctypes.c_void_p(24), fake, 32, None) == INV  # misaligned
+    assert lib.gs_stream_copy(None, fake, 32, None) == INV
+    assert lib.gs_stream_copy(None, None, 0, None) == L.GS_OK
     # tile masks
     mws = L.tile_masks_workspace_bytes(100)
     assert mws == 400

@@ -70,7 +70,7 @@ def test_forward(run):
     st = PY.check_forward(run["gpu"], run["fwd"])
     _log(st)
     n_px = run["fwd"]["image"][:, 0].size
-    assert st["ambiguous"] <= max(10, n_px // 500)
+    assert st["ambiguous"] <= max(16, n_px // 5000)
 
 
 def _dL(run):

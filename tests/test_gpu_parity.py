@@ -1,6 +1,11 @@
 """GPU parity of every stage of the step against the CPU oracle, through the C
-ABI, on the tiny (10k Gaussians, 256x256, SH 0) and object (200k, 720p, SH 3)
-scenes at full size: each spans many tiles and ends in ragged edge tiles."""
+ABI, at full size on three scenes that span many tiles:
+  * tiny (10k Gaussians, SH 0, 256x256) and object (200k, SH 3, 1280x720),
+    whose sides are multiples of the 16-pixel tile;
+  * ragged (200k, SH 3, two views of 250x190), whose last tile column is 10
+    pixels wide and last tile row 14 pixels tall (partial tiles, sub-blocks
+    cut by the image edge, masks clipped to it), with lists of several
+    thousand entries."""
 
 import numpy as np
 import pytest
@@ -13,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _scene(cfg_id, n=None):
-    cfg = S.CONFIGS[cfg_id]
+    cfg = S.RAGGED if cfg_id == "ragged" else S.CONFIGS[cfg_id]
     params = S.make_params(cfg, n=n)
     cams = cfg.cameras()
     tgt_params = S.make_target_params(cfg, n=n)
@@ -21,7 +26,7 @@ def _scene(cfg_id, n=None):
     return cfg, params, cams, target
 
 
-@pytest.fixture(scope="module", params=[0, 1], ids=["tiny", "object"])
+@pytest.fixture(scope="module", params=[0, 1, "ragged"], ids=["tiny", "object", "ragged"])
 def run(request):
     import torch
     assert torch.cuda.is_available()
@@ -64,9 +69,10 @@ def test_tile_masks(run):
 def test_forward(run):
     st = PY.check_forward(run["gpu"], run["fwd"])
     print(st)
-    # near-threshold pixels are rare: well under 0.2% of the image
+    # near-threshold pixels (the oracle's derived exp band) are rare: at most
+    # 0.02 % of the image (3 of 65536 on tiny, 102 of 921600 on object)
     n_px = run["fwd"]["image"][:, 0].size
-    assert st["ambiguous"] <= max(10, n_px // 500)
+    assert st["ambiguous"] <= max(16, n_px // 5000)
 
 
 def test_loss(run):
@@ -161,10 +167,8 @@ def test_preprocess_bwd_adam_fused(run, step):
     g_sep = PY.gpu_preprocess_bwd(b, params_t, g2)
     m0, v0 = S.adam_state(b.P, b.n, seed=None if step == 1 else 5)
     th, m, v, g = PY.gpu_preprocess_bwd_adam(b, params_t, g2, m0, v0, cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, step)
-    gd = np.abs(g.astype(np.float64) - g_sep)
-    row = np.abs(g_sep).max(axis=1, keepdims=True).astype(np.float64)
-    print(f"fused gradient vs gs_preprocess_bwd: max abs diff {gd.max():.3e}")
-    assert np.all(gd <= 1e-6 * row)
+    # the same arithmetic in both kernels (no contraction): bit for bit
+    assert np.array_equal(g, g_sep)
     ref = O.adam(run["params"], g, m0, v0, cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, step)
     PY.check_adam((th, m, v), ref, run["params"], g, m0, cfg.lr, cfg.beta1)
     # a set flag leaves parameters, moments and the gradient output untouched
@@ -178,7 +182,9 @@ def test_adam_state_skip(run):
     """With the state flags, Gaussians culled in every view and never seen
     are skipped; the result equals the dense update bit for bit over three
     calls whose visibility changes (seen, then culled: the moments keep
-    decaying and theta keeps moving; never seen: untouched)."""
+    decaying and theta keeps moving; never seen: untouched), and each call's
+    parameters and moments equal the oracle's Adam of that call's gradient
+    (gs_preprocess_bwd with the same visibility) from the state before it."""
     import torch
     from gaussian_splatting_differentiable_ewa_amd import _lib as L
     cfg, b = run["cfg"], run["buf"]
@@ -203,8 +209,15 @@ def test_adam_state_skip(run):
         b.grad2d.copy_(g2)
         args = (n, b.sh_degree, b.cams, b.rect, b.grad2d)
         hyper = (cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, step)
+        before = [PY.np_(x).copy() for x in skip]
+        grad = torch.empty_like(p0)
+        L.gs_preprocess_bwd(skip[0], *args, grad)
         L.gs_preprocess_bwd_adam(dense[0], *args, dense[1], dense[2], *hyper)
         L.gs_preprocess_bwd_adam(skip[0], *args, skip[1], skip[2], *hyper, state=state)
+        torch.cuda.synchronize()
+        g = PY.np_(grad)
+        ref = O.adam(before[0], g, before[1], before[2], cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, step)
+        PY.check_adam([PY.np_(x) for x in skip], ref, before[0], g, before[1], cfg.lr, cfg.beta1)
     torch.cuda.synchronize()
     b.rect.copy_(rect0)
     for a, c in zip(dense, skip):
