@@ -54,6 +54,22 @@ __device__ __forceinline__ bool maybe_visible(float x, float y, float z, float s
     return u + rb > 0.f && u - rb < 16.f * (float)TX && v + rb > 0.f && v - rb < 16.f * (float)TY;
 }
 
+// The 2D-gradient records of the wave's 64 Gaussians in view v are one
+// contiguous block of 64 x 9 floats; the wave zeroes the whole block (dword
+// stores, each instruction 256 contiguous bytes) when any of its lanes is
+// visible in the view. Records of culled pairs in such a block are zeroed too
+// (nothing reads them); blocks of waves with no visible lane are left alone.
+__device__ __forceinline__ void zero_grad2d_block(float* __restrict__ g2z, int64_t n, int v, int64_t g0, bool any)
+{
+    if (!g2z || !any) return;  // wave-uniform
+    const int64_t first = ((int64_t)v * n + g0) * GS_GRAD2D_ROWS;
+    const int64_t count = (min(g0 + 64, n) - g0) * GS_GRAD2D_ROWS;
+    const int64_t lane = (int64_t)(threadIdx.x & 63u);
+#pragma unroll
+    for (int k = 0; k < GS_GRAD2D_ROWS; ++k)
+        if (lane + 64 * k < count) g2z[first + lane + 64 * k] = 0.f;
+}
+
 // One thread per Gaussian. The means and log-scales are loaded first; a
 // Gaussian that no view can see (maybe_visible) writes its zero counts and
 // empty rectangles without loading the rest, so that the waves of a scene
@@ -69,66 +85,70 @@ __global__ __launch_bounds__(PRE_THREADS) void k_preprocess(const float* __restr
 {
     constexpr int NB = (DEG + 1) * (DEG + 1);
     const int64_t g = (int64_t)blockIdx.x * PRE_THREADS + threadIdx.x;
-    if (g >= n) return;
+    const int64_t g0 = g & ~(int64_t)63;  // the wave's first Gaussian
+    if (g0 >= n) return;                   // whole waves past the end
+    const bool here = g < n;
     float raw[11];
 #pragma unroll
-    for (int r = 0; r < 6; ++r) raw[r] = P[(int64_t)r * n + g];
-    {
+    for (int r = 0; r < 6; ++r) raw[r] = here ? P[(int64_t)r * n + g] : 0.f;
+    bool maybe = false;
+    if (here) {
         const float smax = __expf(fmaxf(raw[3], fmaxf(raw[4], raw[5]))) * 1.001f;
-        bool maybe = false;
         for (int v = 0; v < cams.n_views; ++v)
             maybe = maybe || maybe_visible(raw[0], raw[1], raw[2], smax, cams.c[v], cams.tiles_x, cams.tiles_y);
-        if (!maybe) {
+    }
+    if (!maybe) {
+        // no view can see it: zero counts, empty rectangles, nothing loaded
+        if (here)
             for (int v = 0; v < cams.n_views; ++v) {
                 const int64_t idx = (int64_t)v * n + g;
                 counts[idx] = 0u;
                 *(uint2*)(rect + 4 * idx) = make_uint2(0u, 0u);
             }
-            return;
+    }
+    uint32_t vis_bits = 0u;  // bit v: visible in view v
+    if (maybe) {
+#pragma unroll
+        for (int r = 6; r < 11; ++r) raw[r] = P[(int64_t)r * n + g];
+        float sh[3 * NB];
+#pragma unroll
+        for (int k = 0; k < 3 * NB; ++k) sh[k] = P[(int64_t)(11 + k) * n + g];
+        const float x = raw[0], y = raw[1], z = raw[2];
+        GaussLocal L;
+        gauss_local(raw[3], raw[4], raw[5], raw[6], raw[7], raw[8], raw[9], raw[10], L);
+        for (int v = 0; v < cams.n_views; ++v) {
+            const DevCamera& cam = cams.c[v];
+            ViewProj p;
+            view_project(x, y, z, L, cam, cams.tiles_x, cams.tiles_y, p);
+            const int64_t idx = (int64_t)v * n + g;
+            if (!p.visible) {
+                counts[idx] = 0u;
+                *(uint2*)(rect + 4 * idx) = make_uint2(0u, 0u);
+                continue;
+            }
+            vis_bits |= 1u << v;
+            float d[3], dist;
+            view_dir(x, y, z, cam, d, dist);
+            float Y[16];
+            sh_eval_basis(K, DEG, d, Y);
+            bool cl;
+            const float r = sh_channel_reg<NB>(sh, 0, Y, cl);
+            const float gg = sh_channel_reg<NB>(sh, 1, Y, cl);
+            const float b = sh_channel_reg<NB>(sh, 2, Y, cl);
+            float ex, ey;
+            alpha_extent(L.o, p.a, p.c, ex, ey);
+            float4* out = (float4*)(rec + idx * GS_REC_FLOATS);
+            out[0] = make_float4(p.u, p.v, p.A, p.B);
+            out[1] = make_float4(p.C, L.o, r, gg);
+            out[2] = make_float4(b, ex, ey, p.zc);
+            if (depth) depth[idx] = p.zc;
+            *(uint2*)(rect + 4 * idx) = make_uint2((uint32_t)p.x0 | ((uint32_t)p.y0 << 16),
+                                                   (uint32_t)p.x1 | ((uint32_t)p.y1 << 16));
+            counts[idx] = (uint32_t)((p.x1 - p.x0) * (p.y1 - p.y0));
         }
     }
-#pragma unroll
-    for (int r = 6; r < 11; ++r) raw[r] = P[(int64_t)r * n + g];
-    float sh[3 * NB];
-#pragma unroll
-    for (int k = 0; k < 3 * NB; ++k) sh[k] = P[(int64_t)(11 + k) * n + g];
-    const float x = raw[0], y = raw[1], z = raw[2];
-    GaussLocal L;
-    gauss_local(raw[3], raw[4], raw[5], raw[6], raw[7], raw[8], raw[9], raw[10], L);
-    for (int v = 0; v < cams.n_views; ++v) {
-        const DevCamera& cam = cams.c[v];
-        ViewProj p;
-        view_project(x, y, z, L, cam, cams.tiles_x, cams.tiles_y, p);
-        const int64_t idx = (int64_t)v * n + g;
-        if (!p.visible) {
-            counts[idx] = 0u;
-            *(uint2*)(rect + 4 * idx) = make_uint2(0u, 0u);
-            continue;
-        }
-        float d[3], dist;
-        view_dir(x, y, z, cam, d, dist);
-        float Y[16];
-        sh_eval_basis(K, DEG, d, Y);
-        bool cl;
-        const float r = sh_channel_reg<NB>(sh, 0, Y, cl);
-        const float gg = sh_channel_reg<NB>(sh, 1, Y, cl);
-        const float b = sh_channel_reg<NB>(sh, 2, Y, cl);
-        float ex, ey;
-        alpha_extent(L.o, p.a, p.c, ex, ey);
-        float4* out = (float4*)(rec + idx * GS_REC_FLOATS);
-        out[0] = make_float4(p.u, p.v, p.A, p.B);
-        out[1] = make_float4(p.C, L.o, r, gg);
-        out[2] = make_float4(b, ex, ey, p.zc);
-        if (depth) depth[idx] = p.zc;
-        if (g2zero) {  // the 2D-gradient record the raster passes add to
-            float* gz = g2zero + idx * GS_GRAD2D_ROWS;
-#pragma unroll
-            for (int k = 0; k < GS_GRAD2D_ROWS; ++k) gz[k] = 0.f;
-        }
-        *(uint2*)(rect + 4 * idx) = make_uint2((uint32_t)p.x0 | ((uint32_t)p.y0 << 16),
-                                               (uint32_t)p.x1 | ((uint32_t)p.y1 << 16));
-        counts[idx] = (uint32_t)((p.x1 - p.x0) * (p.y1 - p.y0));
-    }
+    if (g2zero)
+        for (int v = 0; v < cams.n_views; ++v) zero_grad2d_block(g2zero, n, v, g0, ballot((vis_bits >> v) & 1u) != 0ull);
 }
 
 // One thread per (view, Gaussian): its tiles in row-major order, at its offset.

@@ -423,13 +423,40 @@ __device__ __forceinline__ void tl_or_and(uint32_t v_or, uint32_t v_and, uint32_
     __syncthreads();
 }
 
-// Orders each run of equal keys by Gaussian index (insertion sort by swaps;
-// runs are rare and short). Every run is handled by the thread that owns its
-// first element. less(a, b): item a's index is below item b's.
-template <typename KeyAt, typename ValAt, typename Less, typename Swap>
-__device__ __forceinline__ void tl_fix_ties(uint32_t n, KeyAt key_at, ValAt, Less less, Swap swap)
+// The sorts order a tile by the 64-bit key (depth bits << 32 | Gaussian id):
+// digit positions 0-3 are the id's bytes, 4-7 the depth's, and an LSD pass
+// runs for each position whose digit is not the same across the tile. The
+// id bytes are sorted only when a tile holds a run of more than TIE_RUN equal
+// depths; shorter runs (the only kind that occurs in ordinary scenes) are put
+// in id order by an insertion sort after the depth passes, at most
+// TIE_RUN^2 / 2 steps per run.
+constexpr uint32_t TIE_RUN = 32;
+
+__device__ __forceinline__ uint32_t tl_digit(uint32_t depth, uint32_t id, int p)
 {
-    for (uint32_t i = threadIdx.x; i + 1 < n; i += TL_THREADS) {
+    return p < 4 ? (id >> (8 * p)) & 255u : (depth >> (8 * (p - 4))) & 255u;
+}
+
+// Positions (bits of a mask) whose byte varies, from the OR and AND of the
+// values over the tile: 'base' is 0 for the id, 4 for the depth.
+__device__ __forceinline__ uint32_t tl_varying(uint32_t vor, uint32_t vand, int base)
+{
+    const uint32_t differ = vor ^ vand;
+    uint32_t m = 0u;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        if ((differ >> (8 * b)) & 255u) m |= 1u << (base + b);
+    return m;
+}
+
+// Orders each run of equal keys (of at most TIE_RUN items) by Gaussian index
+// (insertion sort by swaps). Every run is handled by the thread that owns its
+// first element; `first`, `stride`: this thread's items.
+template <typename KeyAt, typename Less, typename Swap>
+__device__ __forceinline__ void tl_fix_short_ties(uint32_t n, uint32_t first, uint32_t stride, KeyAt key_at, Less less,
+                                                  Swap swap)
+{
+    for (uint32_t i = first; i + 1 < n; i += stride) {
         const uint32_t k = key_at(i);
         if ((i > 0 && key_at(i - 1) == k) || key_at(i + 1) != k) continue;
         uint32_t j = i + 1;
@@ -439,47 +466,18 @@ __device__ __forceinline__ void tl_fix_ties(uint32_t n, KeyAt key_at, ValAt, Les
     }
 }
 
-
-// A tile of 65..512 entries, one wave alone (no barriers: LDS is in order
-// within a wave): the LSD radix sort of k_tl_sort on the wave's registers and
-// a private slice of LDS (sk, si: WV_CAP entries, cnt: 256 counters). Run by
-// the workgroups of k_tl_sort past its long tiles, four tiles each.
-__device__ __forceinline__ void tl_sort_wave_tile(int64_t tile, uint32_t lane, uint32_t* sk, uint16_t* si,
-                                                  uint32_t* cnt, const uint32_t* __restrict__ ranges,
-                                                  const uint64_t* __restrict__ total_dev, uint64_t capacity,
-                                                  const uint2* __restrict__ pairs, uint32_t* __restrict__ vals,
-                                                  const MaskOut& mo)
+// LSD passes of one wave over its items key[r] (depth bits) / idx[r]
+// (position of the item in the tile's unsorted pairs), item r * 64 + lane,
+// through a private slice of LDS (sk, si: WV_CAP items; cnt: 256 counters);
+// `positions` the digit positions to sort. The id of an item is read through
+// its position (tp[idx].y) for the id passes.
+__device__ __forceinline__ void tl_wave_passes(uint32_t n, uint32_t R, uint32_t lane, uint32_t positions,
+                                               uint32_t (&key)[WV_ROUNDS], uint32_t (&idx)[WV_ROUNDS], uint32_t* sk,
+                                               uint16_t* si, uint32_t* cnt, const uint2* __restrict__ tp)
 {
-    const uint2 rg = *(const uint2*)(ranges + 2 * tile);
-    const uint64_t limit = min(capacity, *total_dev);
-    const uint32_t start = rg.x, end = (uint32_t)min((uint64_t)rg.y, limit);
-    if (end <= start) return;
-    const uint32_t n = end - start;
-    if (n <= 64u || n > (uint32_t)WV_CAP) return;  // wave-uniform
-    const uint32_t R = (n + 63u) / 64u;
-    uint32_t key[WV_ROUNDS], idx[WV_ROUNDS], rank[WV_ROUNDS];
-    uint32_t kor = 0u, kand = 0xffffffffu;
-#pragma unroll
-    for (int r = 0; r < WV_ROUNDS; ++r) {
-        const uint32_t i = (uint32_t)r * 64u + lane;
-        key[r] = 0u;
-        idx[r] = i;
-        if ((uint32_t)r < R && i < n) {
-            key[r] = pairs[start + i].x;
-            kor |= key[r];
-            kand &= key[r];
-            sk[i] = key[r];
-            si[i] = (uint16_t)i;
-        }
-    }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        kor |= __shfl_xor(kor, off);
-        kand &= __shfl_xor(kand, off);
-    }
-    const uint32_t differ = kor ^ kand;
-    for (int shift = 0; shift < 32; shift += 8) {
-        if (((differ >> shift) & 255u) == 0u) continue;
+    uint32_t rank[WV_ROUNDS], dig[WV_ROUNDS];
+    for (int p = 0; p < 8; ++p) {
+        if (((positions >> p) & 1u) == 0u) continue;
 #pragma unroll
         for (int k = 0; k < 4; ++k) cnt[lane * 4 + k] = 0u;
         asm volatile("" ::: "memory");
@@ -488,13 +486,13 @@ __device__ __forceinline__ void tl_sort_wave_tile(int64_t tile, uint32_t lane, u
             if ((uint32_t)r >= R) break;
             const uint32_t i = (uint32_t)r * 64u + lane;
             const bool valid = i < n;
-            const uint32_t d = (key[r] >> shift) & 255u;
-            const uint64_t peers = tl_peers(d, ballot(valid));
+            dig[r] = valid ? tl_digit(key[r], p < 4 ? tp[idx[r]].y : 0u, p) : 0u;
+            const uint64_t peers = tl_peers(dig[r], ballot(valid));
             const uint32_t below = mask_rank(peers);
-            const uint32_t prior = cnt[d];
+            const uint32_t prior = cnt[dig[r]];
             rank[r] = prior + below;
             asm volatile("" ::: "memory");
-            if (valid && below == 0u) cnt[d] = prior + (uint32_t)__popcll(peers);
+            if (valid && below == 0u) cnt[dig[r]] = prior + (uint32_t)__popcll(peers);
             asm volatile("" ::: "memory");
         }
         // exclusive prefix over the 256 digit counts: four per lane
@@ -523,7 +521,7 @@ __device__ __forceinline__ void tl_sort_wave_tile(int64_t tile, uint32_t lane, u
             if ((uint32_t)r >= R) break;
             const uint32_t i = (uint32_t)r * 64u + lane;
             if (i < n) {
-                const uint32_t pos = cnt[(key[r] >> shift) & 255u] + rank[r];
+                const uint32_t pos = cnt[dig[r]] + rank[r];
                 sk[pos] = key[r];
                 si[pos] = (uint16_t)idx[r];
             }
@@ -540,22 +538,238 @@ __device__ __forceinline__ void tl_sort_wave_tile(int64_t tile, uint32_t lane, u
         }
         asm volatile("" ::: "memory");
     }
-    // equal depths: order the run's items by Gaussian index (one lane per run)
+}
+
+// A tile of 65..512 entries, one wave alone (no barriers: LDS is in order
+// within a wave): LSD passes by depth on the wave's registers and a private
+// slice of LDS (sk, si: WV_CAP entries, cnt: 256 counters), then the ties.
+// Run by the workgroups of k_tl_sort past its long tiles, four tiles each.
+__device__ __forceinline__ void tl_sort_wave_tile(int64_t tile, uint32_t lane, uint32_t* sk, uint16_t* si,
+                                                  uint32_t* cnt, const uint32_t* __restrict__ ranges,
+                                                  const uint64_t* __restrict__ total_dev, uint64_t capacity,
+                                                  const uint2* __restrict__ pairs, uint32_t* __restrict__ vals,
+                                                  const MaskOut& mo)
+{
+    const uint2 rg = *(const uint2*)(ranges + 2 * tile);
+    const uint64_t limit = min(capacity, *total_dev);
+    const uint32_t start = rg.x, end = (uint32_t)min((uint64_t)rg.y, limit);
+    if (end <= start) return;
+    const uint32_t n = end - start;
+    if (n <= 64u || n > (uint32_t)WV_CAP) return;  // wave-uniform
+    const uint32_t R = (n + 63u) / 64u;
     const uint2* tp = pairs + start;
-    for (uint32_t i = lane; i + 1 < n; i += 64) {
-        const uint32_t k = sk[i];
-        if ((i > 0 && sk[i - 1] == k) || sk[i + 1] != k) continue;
-        uint32_t j = i + 1;
-        while (j < n && sk[j] == k) ++j;
-        for (uint32_t a = i + 1; a < j; ++a)
-            for (uint32_t b = a; b > i && tp[si[b]].y < tp[si[b - 1]].y; --b) {
-                const uint16_t tmp = si[b];
-                si[b] = si[b - 1];
-                si[b - 1] = tmp;
-            }
+    uint32_t key[WV_ROUNDS], idx[WV_ROUNDS];
+    uint32_t kor = 0u, kand = 0xffffffffu;
+#pragma unroll
+    for (int r = 0; r < WV_ROUNDS; ++r) {
+        const uint32_t i = (uint32_t)r * 64u + lane;
+        key[r] = 0u;
+        idx[r] = i;
+        if ((uint32_t)r < R && i < n) {
+            key[r] = tp[i].x;
+            kor |= key[r];
+            kand &= key[r];
+            sk[i] = key[r];
+            si[i] = (uint16_t)i;
+        }
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        kor |= __shfl_xor(kor, off);
+        kand &= __shfl_xor(kand, off);
+    }
+    tl_wave_passes(n, R, lane, tl_varying(kor, kand, 4), key, idx, sk, si, cnt, tp);
+    // a run of more than TIE_RUN equal depths: sort again by the whole key
+    bool longrun = false;
+    for (uint32_t i = lane; i + TIE_RUN < n; i += 64) longrun = longrun || sk[i] == sk[i + TIE_RUN];
+    if (ballot(longrun) != 0ull) {
+        uint32_t ior = 0u, iand = 0xffffffffu;
+        for (uint32_t i = lane; i < n; i += 64) {
+            const uint32_t id = tp[i].y;
+            ior |= id;
+            iand &= id;
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            ior |= __shfl_xor(ior, off);
+            iand &= __shfl_xor(iand, off);
+        }
+        tl_wave_passes(n, R, lane, tl_varying(ior, iand, 0) | tl_varying(kor, kand, 4), key, idx, sk, si, cnt, tp);
+    } else {
+        asm volatile("" ::: "memory");
+        tl_fix_short_ties(
+            n, lane, 64u, [&](uint32_t i) { return sk[i]; },
+            [&](uint32_t i, uint32_t a) { return tp[si[i]].y < tp[si[a]].y; },
+            [&](uint32_t i, uint32_t a) { const uint16_t x = si[i]; si[i] = si[a]; si[a] = x; });
     }
     asm volatile("" ::: "memory");
     write_ids_masks<64u>(mo, tile, start, n, lane, [&](uint32_t i) { return tp[si[i]].y; }, vals);
+}
+
+// LSD passes of the workgroup over a tile of up to TL_CAP items in LDS: wave
+// w holds the contiguous run [w L, (w + 1) L), L = 64 R, of items key[r]
+// (depth bits) / idx[r] (position in the unsorted pairs tp).
+__device__ __forceinline__ void tl_wg_passes(uint32_t n, uint32_t R, uint32_t positions, uint32_t (&key)[TL_ROUNDS],
+                                             uint32_t (&idx)[TL_ROUNDS], uint32_t* s_key, uint16_t* s_idx,
+                                             uint32_t (*wcnt)[256], uint32_t* s_misc, const uint2* __restrict__ tp)
+{
+    const uint32_t t = threadIdx.x, lane = t & 63u, wave = t >> 6;
+    const uint32_t wbeg = wave * 64u * R;
+    uint32_t rank[TL_ROUNDS], dig[TL_ROUNDS];
+    for (int p = 0; p < 8; ++p) {
+        if (((positions >> p) & 1u) == 0u) continue;  // uniform digit: order unchanged
+#pragma unroll
+        for (int w = 0; w < 4; ++w) wcnt[w][t] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < TL_ROUNDS; ++r) {
+            if ((uint32_t)r >= R) break;  // uniform across the workgroup
+            const uint32_t i = wbeg + (uint32_t)r * 64u + lane;
+            const bool valid = i < n;
+            dig[r] = valid ? tl_digit(key[r], p < 4 ? tp[idx[r]].y : 0u, p) : 0u;
+            const uint64_t peers = tl_peers(dig[r], ballot(valid));
+            const uint32_t below = mask_rank(peers);
+            const uint32_t prior = wcnt[wave][dig[r]];
+            rank[r] = prior + below;
+            asm volatile("" ::: "memory");  // every lane has read the counter
+            if (valid && below == 0u) wcnt[wave][dig[r]] = prior + (uint32_t)__popcll(peers);
+            asm volatile("" ::: "memory");
+        }
+        __syncthreads();
+        {
+            const uint32_t c0 = wcnt[0][t], c1 = wcnt[1][t], c2 = wcnt[2][t], c3 = wcnt[3][t];
+            const uint32_t lo = tl_exclusive_256(c0 + c1 + c2 + c3, s_misc);
+            wcnt[0][t] = lo;
+            wcnt[1][t] = lo + c0;
+            wcnt[2][t] = lo + c0 + c1;
+            wcnt[3][t] = lo + c0 + c1 + c2;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < TL_ROUNDS; ++r) {
+            if ((uint32_t)r >= R) break;
+            const uint32_t i = wbeg + (uint32_t)r * 64u + lane;
+            if (i < n) {
+                const uint32_t pos = wcnt[wave][dig[r]] + rank[r];
+                s_key[pos] = key[r];
+                s_idx[pos] = (uint16_t)idx[r];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < TL_ROUNDS; ++r) {
+            if ((uint32_t)r >= R) break;
+            const uint32_t i = wbeg + (uint32_t)r * 64u + lane;
+            if (i < n) {
+                key[r] = s_key[i];
+                idx[r] = s_idx[i];
+            }
+        }
+    }
+}
+
+// LSD passes over a tile longer than the LDS holds, in global memory, chunk
+// by chunk (chunks in order keep each pass stable), ping-ponging between src
+// and dst (the tile's slots of the pairs and of a scratch copy). One read of
+// the list forms the histograms of every position in `positions` (a position
+// with one digit across the list is skipped), and each read of a chunk
+// requests all its items before ranking them. Returns the buffer that holds
+// the result. LDS: hist [8][256], cw [4][256], running [256] (3328 words),
+// s_misc.
+__device__ __forceinline__ uint2* tl_global_passes(uint32_t n, uint32_t positions, uint2* src, uint2* dst,
+                                                   uint32_t* lds, uint32_t* s_misc)
+{
+    const uint32_t t = threadIdx.x, lane = t & 63u, wave = t >> 6;
+    uint32_t(*hist)[256] = (uint32_t(*)[256])lds;           // [position][digit] totals of the list
+    uint32_t(*cw)[256] = (uint32_t(*)[256])(lds + 8 * 256);  // [wave][digit] counts of a chunk
+    uint32_t* running = lds + 12 * 256;                      // [256] next free slot of each digit
+#pragma unroll
+    for (int p = 0; p < 8; ++p) hist[p][t] = 0u;
+    if (t == 0) s_misc[4] = 0u;
+    __syncthreads();
+    for (uint32_t base = 0; base < n; base += (uint32_t)GL_CHUNK) {
+        uint2 k[GL_ROUNDS];
+#pragma unroll
+        for (int r = 0; r < GL_ROUNDS; ++r) {
+            const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
+            k[r] = i < n ? src[i] : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int r = 0; r < GL_ROUNDS; ++r) {
+            const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
+            const uint64_t vm = ballot(i < n);
+            if (vm == 0ull) break;  // wave-uniform
+            for (int p = 0; p < 8; ++p) {
+                if (((positions >> p) & 1u) == 0u) continue;
+                const uint32_t d = tl_digit(k[r].x, k[r].y, p);
+                const uint64_t peers = tl_peers(d, vm);
+                if (i < n && mask_rank(peers) == 0u) atomicAdd(&hist[p][d], (uint32_t)__popcll(peers));
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const uint32_t c = hist[p][t];
+        if (((positions >> p) & 1u) && c != 0u && c != n) atomicOr(&s_misc[4], 1u << p);  // two digits or more
+    }
+    __syncthreads();
+    const uint32_t varies = s_misc[4];
+    for (int p = 0; p < 8; ++p) {
+        if (((varies >> p) & 1u) == 0u) continue;
+        running[t] = tl_exclusive_256(hist[p][t], s_misc);
+        __syncthreads();
+        for (uint32_t base = 0; base < n; base += (uint32_t)GL_CHUNK) {
+            // chunk [base, base + 4096): wave w ranks its run of 1024
+            uint2 item[GL_ROUNDS];
+#pragma unroll
+            for (int r = 0; r < GL_ROUNDS; ++r) {
+                const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
+                item[r] = i < n ? src[i] : make_uint2(0u, 0u);
+            }
+#pragma unroll
+            for (int w = 0; w < 4; ++w) cw[w][t] = 0u;
+            __syncthreads();
+            uint32_t rk[GL_ROUNDS];
+#pragma unroll
+            for (int r = 0; r < GL_ROUNDS; ++r) {
+                const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
+                const bool valid = i < n;
+                const uint32_t d = tl_digit(item[r].x, item[r].y, p);
+                const uint64_t peers = tl_peers(d, ballot(valid));
+                const uint32_t below = mask_rank(peers);
+                const uint32_t prior = cw[wave][d];
+                rk[r] = prior + below;
+                asm volatile("" ::: "memory");
+                if (valid && below == 0u) cw[wave][d] = prior + (uint32_t)__popcll(peers);
+                asm volatile("" ::: "memory");
+            }
+            __syncthreads();
+            {
+                const uint32_t c0 = cw[0][t], c1 = cw[1][t], c2 = cw[2][t], c3 = cw[3][t];
+                const uint32_t b0 = running[t];
+                cw[0][t] = b0;
+                cw[1][t] = b0 + c0;
+                cw[2][t] = b0 + c0 + c1;
+                cw[3][t] = b0 + c0 + c1 + c2;
+                running[t] = b0 + c0 + c1 + c2 + c3;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < GL_ROUNDS; ++r) {
+                const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
+                if (i < n) {
+                    const uint32_t pos = cw[wave][tl_digit(item[r].x, item[r].y, p)] + rk[r];
+                    if (pos < n) dst[pos] = item[r];
+                }
+            }
+            __syncthreads();
+        }
+        uint2* tmp = src;
+        src = dst;
+        dst = tmp;
+    }
+    return src;
 }
 
 // Launched with n_tiles + ceil(n_tiles / 4) workgroups: workgroup b takes
@@ -602,17 +816,18 @@ __global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restri
     const uint32_t n = end - start;
     const uint32_t t = threadIdx.x, lane = t & 63u, wave = t >> 6;
     if (n <= (uint32_t)WV_CAP) return;  // tl_sort_small_tile, tl_sort_wave_tile
+    const uint2* tp = pairs + start;
     if (n <= (uint32_t)TL_CAP) {
         // wave w holds the contiguous run [w L, (w + 1) L), L = 64 R
         const uint32_t R = (n + TL_THREADS - 1) / TL_THREADS;
         const uint32_t wbeg = wave * 64u * R;
-        uint32_t key[TL_ROUNDS], idx[TL_ROUNDS], rank[TL_ROUNDS];
+        uint32_t key[TL_ROUNDS], idx[TL_ROUNDS];
         uint32_t kor = 0u, kand = 0xffffffffu;
 #pragma unroll
         for (int r = 0; r < TL_ROUNDS; ++r) {
             const uint32_t i = wbeg + (uint32_t)r * 64u + lane;
             const bool valid = (uint32_t)r < R && i < n;
-            const uint2 p = valid ? pairs[start + i] : make_uint2(0u, 0u);
+            const uint2 p = valid ? tp[i] : make_uint2(0u, 0u);
             key[r] = p.x;
             idx[r] = i;
             if (valid) {
@@ -624,192 +839,68 @@ __global__ __launch_bounds__(TL_THREADS) void k_tl_sort(const uint32_t* __restri
         }
         uint32_t o, a;
         tl_or_and(kor, kand, s_misc, o, a);
-        const uint32_t differ = o ^ a;  // bits that are not equal across the tile
-        for (int shift = 0; shift < 32; shift += 8) {
-            if (((differ >> shift) & 255u) == 0u) continue;  // uniform digit: order unchanged
-#pragma unroll
-            for (int w = 0; w < 4; ++w) wcnt[w][t] = 0u;
-            __syncthreads();
-#pragma unroll
-            for (int r = 0; r < TL_ROUNDS; ++r) {
-                if ((uint32_t)r >= R) break;  // uniform across the workgroup
-                const uint32_t i = wbeg + (uint32_t)r * 64u + lane;
-                const bool valid = i < n;
-                const uint32_t d = (key[r] >> shift) & 255u;
-                const uint64_t peers = tl_peers(d, ballot(valid));
-                const uint32_t below = mask_rank(peers);
-                const uint32_t prior = wcnt[wave][d];
-                rank[r] = prior + below;
-                asm volatile("" ::: "memory");  // every lane has read the counter
-                if (valid && below == 0u) wcnt[wave][d] = prior + (uint32_t)__popcll(peers);
-                asm volatile("" ::: "memory");
-            }
-            __syncthreads();
-            {
-                const uint32_t c0 = wcnt[0][t], c1 = wcnt[1][t], c2 = wcnt[2][t], c3 = wcnt[3][t];
-                const uint32_t lo = tl_exclusive_256(c0 + c1 + c2 + c3, s_misc);
-                wcnt[0][t] = lo;
-                wcnt[1][t] = lo + c0;
-                wcnt[2][t] = lo + c0 + c1;
-                wcnt[3][t] = lo + c0 + c1 + c2;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int r = 0; r < TL_ROUNDS; ++r) {
-                if ((uint32_t)r >= R) break;
-                const uint32_t i = wbeg + (uint32_t)r * 64u + lane;
-                if (i < n) {
-                    const uint32_t pos = wcnt[wave][(key[r] >> shift) & 255u] + rank[r];
-                    s_key[pos] = key[r];
-                    s_idx[pos] = (uint16_t)idx[r];
-                }
-            }
-            __syncthreads();
-#pragma unroll
-            for (int r = 0; r < TL_ROUNDS; ++r) {
-                if ((uint32_t)r >= R) break;
-                const uint32_t i = wbeg + (uint32_t)r * 64u + lane;
-                if (i < n) {
-                    key[r] = s_key[i];
-                    idx[r] = s_idx[i];
-                }
-            }
-        }
+        tl_wg_passes(n, R, tl_varying(o, a, 4), key, idx, s_key, s_idx, wcnt, s_misc, tp);
         __syncthreads();
-        // equal depths: order the run's items by Gaussian index
-        const uint2* tp = pairs + start;
-        tl_fix_ties(
-            n, [&](uint32_t i) { return s_key[i]; }, [&](uint32_t i) { return tp[s_idx[i]].y; },
-            [&](uint32_t i, uint32_t a) { return tp[s_idx[i]].y < tp[s_idx[a]].y; },
-            [&](uint32_t i, uint32_t a) { const uint16_t x = s_idx[i]; s_idx[i] = s_idx[a]; s_idx[a] = x; });
+        // a run of more than TIE_RUN equal depths: sort again by the whole key
+        bool longrun = false;
+        for (uint32_t i = t; i + TIE_RUN < n; i += TL_THREADS) longrun = longrun || s_key[i] == s_key[i + TIE_RUN];
+        if (__syncthreads_or(longrun)) {
+            uint32_t ior = 0u, iand = 0xffffffffu;
+            for (uint32_t i = t; i < n; i += TL_THREADS) {
+                const uint32_t id = tp[i].y;
+                ior |= id;
+                iand &= id;
+            }
+            uint32_t io, ia;
+            tl_or_and(ior, iand, s_misc, io, ia);
+            tl_wg_passes(n, R, tl_varying(io, ia, 0) | tl_varying(o, a, 4), key, idx, s_key, s_idx, wcnt, s_misc,
+                         tp);
+        } else {
+            tl_fix_short_ties(
+                n, t, (uint32_t)TL_THREADS, [&](uint32_t i) { return s_key[i]; },
+                [&](uint32_t i, uint32_t a2) { return tp[s_idx[i]].y < tp[s_idx[a2]].y; },
+                [&](uint32_t i, uint32_t a2) { const uint16_t x = s_idx[i]; s_idx[i] = s_idx[a2]; s_idx[a2] = x; });
+        }
         __syncthreads();
         write_ids_masks<(uint32_t)TL_THREADS>(mo, tile, start, n, t, [&](uint32_t i) { return tp[s_idx[i]].y; },
                                               vals);
         return;
     }
 
-    // a list longer than the LDS holds: the same passes over global memory,
-    // chunk by chunk (chunks in order keep the sort stable), ping-ponging
-    // between the pairs and a scratch copy of the same slots. One read of
-    // the list forms the histograms of all four digits (a digit with one
-    // value across the list is skipped), and each read of a chunk requests
-    // all its items before ranking them.
-    uint2* src = pairs + start;
-    uint2* dst = alt + start;
-    uint32_t(*hist)[256] = wcnt;                   // [digit position][digit] totals of the list
-    uint32_t(*cw)[256] = (uint32_t(*)[256])s_key;  // [wave][digit] counts of a chunk
-    uint32_t* running = s_key + 4 * 256;           // [256] next free slot of each digit
-#pragma unroll
-    for (int w = 0; w < 4; ++w) hist[w][t] = 0u;
-    if (t == 0) s_misc[4] = 0u;
+    // a list longer than the LDS holds: the passes over global memory
+    uint2* src = tl_global_passes(n, 0xf0u, pairs + start, alt + start, s_key, s_misc);
     __syncthreads();
-    for (uint32_t base = 0; base < n; base += (uint32_t)GL_CHUNK) {
-        uint32_t k[GL_ROUNDS];
+    // a run of more than TIE_RUN equal depths: sort again by the whole key;
+    // otherwise order each (short) run's items by Gaussian index, the keys
+    // around eight items per thread requested together
+    bool longrun = false;
+    for (uint32_t i = t; i + TIE_RUN < n; i += TL_THREADS) longrun = longrun || src[i].x == src[i + TIE_RUN].x;
+    if (__syncthreads_or(longrun)) {
+        uint2* other = src == pairs + start ? alt + start : pairs + start;
+        src = tl_global_passes(n, 0xffu, src, other, s_key, s_misc);
+    } else {
+        for (uint32_t base = 0; base < n; base += 8u * TL_THREADS) {
+            uint32_t kp[8], kc[8], kn[8];
 #pragma unroll
-        for (int r = 0; r < GL_ROUNDS; ++r) {
-            const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
-            k[r] = i < n ? src[i].x : 0u;
-        }
-#pragma unroll
-        for (int r = 0; r < GL_ROUNDS; ++r) {
-            const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
-            const uint64_t vm = ballot(i < n);
-            if (vm == 0ull) break;  // wave-uniform
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const uint32_t d = (k[r] >> (8 * p)) & 255u;
-                const uint64_t peers = tl_peers(d, vm);
-                if (i < n && mask_rank(peers) == 0u) atomicAdd(&hist[p][d], (uint32_t)__popcll(peers));
-            }
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint32_t c = hist[p][t];
-        if (c != 0u && c != n) atomicOr(&s_misc[4], 1u << p);  // two digits or more at position p
-    }
-    __syncthreads();
-    const uint32_t varies = s_misc[4];
-    for (int p = 0; p < 4; ++p) {
-        if (((varies >> p) & 1u) == 0u) continue;
-        const int shift = 8 * p;
-        running[t] = tl_exclusive_256(hist[p][t], s_misc);
-        __syncthreads();
-        for (uint32_t base = 0; base < n; base += (uint32_t)GL_CHUNK) {
-            // chunk [base, base + 4096): wave w ranks its run of 1024
-            uint2 item[GL_ROUNDS];
-#pragma unroll
-            for (int r = 0; r < GL_ROUNDS; ++r) {
-                const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
-                item[r] = i < n ? src[i] : make_uint2(0u, 0u);
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t i = base + (uint32_t)u * TL_THREADS + t;
+                kc[u] = i < n ? src[i].x : 0u;
+                kp[u] = i > 0 && i < n ? src[i - 1].x : 0u;
+                kn[u] = i + 1 < n ? src[i + 1].x : 0u;
             }
 #pragma unroll
-            for (int w = 0; w < 4; ++w) cw[w][t] = 0u;
-            __syncthreads();
-            uint32_t rk[GL_ROUNDS];
-#pragma unroll
-            for (int r = 0; r < GL_ROUNDS; ++r) {
-                const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
-                const bool valid = i < n;
-                const uint32_t d = (item[r].x >> shift) & 255u;
-                const uint64_t peers = tl_peers(d, ballot(valid));
-                const uint32_t below = mask_rank(peers);
-                const uint32_t prior = cw[wave][d];
-                rk[r] = prior + below;
-                asm volatile("" ::: "memory");
-                if (valid && below == 0u) cw[wave][d] = prior + (uint32_t)__popcll(peers);
-                asm volatile("" ::: "memory");
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t i = base + (uint32_t)u * TL_THREADS + t;
+                if (i + 1 >= n || kn[u] != kc[u] || (i > 0 && kp[u] == kc[u])) continue;
+                uint32_t j = i + 1;
+                while (j < n && src[j].x == kc[u]) ++j;
+                for (uint32_t x = i + 1; x < j; ++x)
+                    for (uint32_t y = x; y > i && src[y].y < src[y - 1].y; --y) {
+                        const uint32_t g = src[y].y;
+                        src[y].y = src[y - 1].y;
+                        src[y - 1].y = g;
+                    }
             }
-            __syncthreads();
-            {
-                const uint32_t c0 = cw[0][t], c1 = cw[1][t], c2 = cw[2][t], c3 = cw[3][t];
-                const uint32_t b0 = running[t];
-                cw[0][t] = b0;
-                cw[1][t] = b0 + c0;
-                cw[2][t] = b0 + c0 + c1;
-                cw[3][t] = b0 + c0 + c1 + c2;
-                running[t] = b0 + c0 + c1 + c2 + c3;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int r = 0; r < GL_ROUNDS; ++r) {
-                const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
-                if (i < n) {
-                    const uint32_t pos = cw[wave][(item[r].x >> shift) & 255u] + rk[r];
-                    if (pos < n) dst[pos] = item[r];
-                }
-            }
-            __syncthreads();
-        }
-        uint2* tmp = src;
-        src = dst;
-        dst = tmp;
-    }
-    // equal depths: order each run's items by Gaussian index (runs are rare
-    // and short; the thread owning a run's first item sorts it), with the
-    // keys around eight items per thread requested together
-    for (uint32_t base = 0; base < n; base += 8u * TL_THREADS) {
-        uint32_t kp[8], kc[8], kn[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const uint32_t i = base + (uint32_t)u * TL_THREADS + t;
-            kc[u] = i < n ? src[i].x : 0u;
-            kp[u] = i > 0 && i < n ? src[i - 1].x : 0u;
-            kn[u] = i + 1 < n ? src[i + 1].x : 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const uint32_t i = base + (uint32_t)u * TL_THREADS + t;
-            if (i + 1 >= n || kn[u] != kc[u] || (i > 0 && kp[u] == kc[u])) continue;
-            uint32_t j = i + 1;
-            while (j < n && src[j].x == kc[u]) ++j;
-            for (uint32_t x = i + 1; x < j; ++x)
-                for (uint32_t y = x; y > i && src[y].y < src[y - 1].y; --y) {
-                    const uint32_t g = src[y].y;
-                    src[y].y = src[y - 1].y;
-                    src[y - 1].y = g;
-                }
         }
     }
     __syncthreads();

@@ -1,9 +1,10 @@
 """gs_tile_lists through the C ABI against the oracle's emission and library
 sort (ordered by tile, depth bits, Gaussian index) on synthetic rectangles
 and depths built to stress it: many equal depths (the order of equal depths
-is decided by the index), tiles with more entries than one workgroup sorts
-in LDS (4096) and than the long-tile sort holds (8192), empty tiles and
-views, and a capacity with slack."""
+is decided by the index), every depth equal (tiles that are one run of ties,
+of hundreds to thousands of entries), tiles with more entries than one
+workgroup sorts in LDS (4096) and than the long-tile sort holds (8192), empty
+tiles and views, and a capacity with slack."""
 
 import numpy as np
 import pytest
@@ -48,6 +49,13 @@ CASES = [
     (5, 500, 3, (0.0, 1.0, 0.0), 3),     # every Gaussian in every tile of view 1
     (6, 20000, 1, (0.45,), 0),           # every tile > 8192 entries: the global-memory path
     (7, 14000, 2, (0.0, 0.5), 9),        # view 1: 7000-entry tiles in the long-tile LDS sort, ties
+    # every Gaussian at one depth (a wall facing the camera): each tile's list
+    # is one run of equal depths, ordered by index alone -- with one wave
+    # (about 300 entries per tile), one workgroup in LDS (about 2700) and the
+    # global-memory path (about 8100)
+    (8, 1500, 1, (0.2,), 1),
+    (9, 3000, 1, (0.9,), 1),
+    (10, 9000, 1, (0.9,), 1),
 ]
 
 
