@@ -35,6 +35,7 @@ EXPORTS = (
     "gs_rasterize_fwd", "gs_rasterize_fwd_l1", "gs_loss_l1", "gs_rasterize_bwd", "gs_rasterize_fwd_bwd_l1",
     "gs_preprocess_bwd", "gs_adam_step", "gs_adam_step_unless", "gs_preprocess_bwd_adam",
     "gs_raster_exp", "gs_stream_copy",
+    "gs_rasterize_fwd_bwd_l1_noalloc", "gs_rasterize_fwd_bwd_l1_noalloc_max_bytes",
 )
 
 
@@ -99,6 +100,9 @@ def lib():
             "gs_adam_step_unless": ([_P, _P, _P, _P, _I64, _F64, _F64, _F64, _F64, _I64, _P, _P], ctypes.c_int),
             "gs_preprocess_bwd_adam": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _F64, _F64, _F64, _F64, _I64, _P,
                                         _P, _P, _P], ctypes.c_int),
+            "gs_rasterize_fwd_bwd_l1_noalloc": ([_P, _I64, _P, _P, _P, _U64, _P, _I32, _I32, _I32, _P, _P, _F32, _P,
+                                                 _P, _P, _P, _P, _P, _I32, _P], ctypes.c_int),
+            "gs_rasterize_fwd_bwd_l1_noalloc_max_bytes": ([], _SZ),
             "gs_raster_exp": ([_P, _P, _I64, _P], ctypes.c_int),
             "gs_stream_copy": ([_P, _P, _U64, _P], ctypes.c_int),
         }
@@ -298,6 +302,22 @@ def gs_rasterize_fwd_bwd_l1(rec, n, ranges, vals, masks, cams, bg, target, scale
                                          _ptr(image), _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimage), _ptr(loss),
                                          _ptr(grad2d), flags, _ptr(ws),
                                          ws.numel() * ws.element_size(), _stream(stream)), "gs_rasterize_fwd_bwd_l1")
+
+
+def gs_rasterize_fwd_bwd_l1_noalloc(rec, n, ranges, vals, masks, cams, bg, target, scale, loss, grad2d, image=None,
+                                    T_final=None, n_contrib=None, dL_dimage=None, accumulate=False, row0=0, rows=None,
+                                    stream=None, capacity=None, accumulate_grad2d=None):
+    """gs_rasterize_fwd_bwd_l1 with the library's fixed per-device workspace
+    (no workspace argument, nothing allocated)."""
+    bgv = (ctypes.c_float * 3)(*bg)
+    acc_g = accumulate if accumulate_grad2d is None else accumulate_grad2d
+    flags = (GS_ACCUMULATE_LOSS if accumulate else 0) | (GS_ACCUMULATE_GRAD2D if acc_g else 0)
+    _check(lib().gs_rasterize_fwd_bwd_l1_noalloc(_ptr(rec), n, _ptr(ranges), _ptr(vals), _ptr(masks),
+                                                 _capacity(vals, masks, capacity), cameras(cams), len(cams), row0,
+                                                 _window(cams[0].height, rows), bgv, _ptr(target), scale, _ptr(image),
+                                                 _ptr(T_final), _ptr(n_contrib), _ptr(dL_dimage), _ptr(loss),
+                                                 _ptr(grad2d), flags, _stream(stream)),
+           "gs_rasterize_fwd_bwd_l1_noalloc")
 
 
 def gs_preprocess_bwd(params, n, sh_degree, cams, rect, grad2d, grad_params, stream=None):

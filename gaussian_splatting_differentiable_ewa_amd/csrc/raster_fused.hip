@@ -6,6 +6,8 @@
 // through device memory, and the list is walked by the same wave twice
 // without a second launch. The forward walk (raster_fwd.h) and the backward
 // walk (raster_bwd.h) share one LDS allocation, used by one after the other.
+#include <mutex>
+
 #include "raster_bwd.h"
 #include "raster_fwd.h"
 
@@ -195,20 +197,16 @@ size_t gs_rasterize_fwd_bwd_l1_workspace_bytes(int32_t n_views, int32_t width, i
     return fused_ws_bytes((int64_t)n_views * gs_tiles_x(width) * gs_tiles_y(height));
 }
 
-gs_status gs_rasterize_fwd_bwd_l1(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
-                                  const uint16_t* masks, uint64_t capacity, const gs_camera* cams, int32_t n_views, int32_t row0,
-                                  int32_t rows, const float* bg, const float* target, float scale, float* image,
-                                  float* T_final, int32_t* n_contrib, float* dL_dimage, double* loss, float* grad2d,
-                                  int32_t accumulate, void* ws, size_t ws_bytes, void* stream)
+}  // extern "C"
+
+// The launches of the pass with its workspace `ws` (arguments validated).
+static gs_status fused_launch(const RasterArgs& a, const float* rec, int64_t n, const uint32_t* ranges,
+                              const uint32_t* vals, const uint16_t* masks, int32_t n_views, const float* bg,
+                              const float* target, float scale, float* image, float* T_final, int32_t* n_contrib,
+                              float* dL_dimage, double* loss, float* grad2d, int32_t accumulate, void* ws,
+                              hipStream_t s)
 {
-    RasterArgs a;
-    if (!raster_args(rec, n, ranges, vals, masks, capacity, cams, n_views, row0, rows, bg, a))
-        return GS_ERR_INVALID_ARGUMENT;
-    if (!target || !loss || !ws || (n > 0 && !grad2d)) return GS_ERR_INVALID_ARGUMENT;
     const int64_t n_tiles = a.n_blocks / 4;
-    if (ws_bytes < fused_ws_bytes(n_tiles)) return GS_ERR_INVALID_ARGUMENT;
-    hipStream_t s = (hipStream_t)stream;
-    if (accumulate & ~(GS_ACCUMULATE_LOSS | GS_ACCUMULATE_GRAD2D)) return GS_ERR_INVALID_ARGUMENT;
     if (!(accumulate & GS_ACCUMULATE_GRAD2D) && n > 0) {
         if (fill_u32((uint32_t*)grad2d, (uint64_t)n_views * GS_GRAD2D_ROWS * (uint64_t)n, 0u, s) != hipSuccess)
             return GS_ERR_HIP;
@@ -221,13 +219,88 @@ gs_status gs_rasterize_fwd_bwd_l1(const float* rec, int64_t n, const uint32_t* r
     hipLaunchKernelGGL(k_order_place, dim3(n_seg), dim3(ORDER_THREADS), 0, s, ranges, n_tiles, table, n_seg, order);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     hipLaunchKernelGGL(k_raster_fwd_bwd_l1, dim3((unsigned)a.n_blocks), dim3(RW_THREADS), 0, s, rec, n, ranges,
-                       vals, masks, a.cap, a.dc.width, a.dc.height, a.dc.tiles_x, a.T, a.row0, bg[0], bg[1], bg[2], target,
-                       scale, image, T_final, n_contrib, dL_dimage, partial, grad2d, order);
+                       vals, masks, a.cap, a.dc.width, a.dc.height, a.dc.tiles_x, a.T, a.row0, bg[0], bg[1], bg[2],
+                       target, scale, image, T_final, n_contrib, dL_dimage, partial, grad2d, order);
     if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     return loss_from_partials(partial, a.n_blocks, (double)scale, loss, (accumulate & GS_ACCUMULATE_LOSS) != 0, s) ==
                    hipSuccess
                ? GS_OK
                : GS_ERR_HIP;
+}
+
+static gs_status fused_args(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
+                            const uint16_t* masks, uint64_t capacity, const gs_camera* cams, int32_t n_views,
+                            int32_t row0, int32_t rows, const float* bg, const float* target, double* loss,
+                            float* grad2d, int32_t accumulate, RasterArgs& a)
+{
+    if (!raster_args(rec, n, ranges, vals, masks, capacity, cams, n_views, row0, rows, bg, a))
+        return GS_ERR_INVALID_ARGUMENT;
+    if (!target || !loss || (n > 0 && !grad2d)) return GS_ERR_INVALID_ARGUMENT;
+    if (accumulate & ~(GS_ACCUMULATE_LOSS | GS_ACCUMULATE_GRAD2D)) return GS_ERR_INVALID_ARGUMENT;
+    return GS_OK;
+}
+
+// The workspace of gs_rasterize_fwd_bwd_l1_noalloc: one array on each device
+// the library runs on, held until the process ends. Host code never uses the
+// name as an address: the device address comes from hipGetSymbolAddress,
+// looked up once per device on the first call there.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)8 << 20;
+__device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[NOALLOC_MAX_DEVICES];
+
+static gs_status scratch_address(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) return GS_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GS_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GS_OK;
+}
+
+extern "C" {
+
+gs_status gs_rasterize_fwd_bwd_l1(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
+                                  const uint16_t* masks, uint64_t capacity, const gs_camera* cams, int32_t n_views,
+                                  int32_t row0, int32_t rows, const float* bg, const float* target, float scale,
+                                  float* image, float* T_final, int32_t* n_contrib, float* dL_dimage, double* loss,
+                                  float* grad2d, int32_t accumulate, void* ws, size_t ws_bytes, void* stream)
+{
+    RasterArgs a;
+    const gs_status st = fused_args(rec, n, ranges, vals, masks, capacity, cams, n_views, row0, rows, bg, target,
+                                    loss, grad2d, accumulate, a);
+    if (st != GS_OK) return st;
+    if (!ws || ws_bytes < fused_ws_bytes(a.n_blocks / 4)) return GS_ERR_INVALID_ARGUMENT;
+    return fused_launch(a, rec, n, ranges, vals, masks, n_views, bg, target, scale, image, T_final, n_contrib,
+                        dL_dimage, loss, grad2d, accumulate, ws, (hipStream_t)stream);
+}
+
+size_t gs_rasterize_fwd_bwd_l1_noalloc_max_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
+
+gs_status gs_rasterize_fwd_bwd_l1_noalloc(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
+                                          const uint16_t* masks, uint64_t capacity, const gs_camera* cams,
+                                          int32_t n_views, int32_t row0, int32_t rows, const float* bg,
+                                          const float* target, float scale, float* image, float* T_final,
+                                          int32_t* n_contrib, float* dL_dimage, double* loss, float* grad2d,
+                                          int32_t accumulate, void* stream)
+{
+    RasterArgs a;
+    const gs_status st = fused_args(rec, n, ranges, vals, masks, capacity, cams, n_views, row0, rows, bg, target,
+                                    loss, grad2d, accumulate, a);
+    if (st != GS_OK) return st;
+    if (fused_ws_bytes(a.n_blocks / 4) > NOALLOC_SCRATCH_BYTES) return GS_ERR_CAPACITY;
+    void* ws = nullptr;
+    const gs_status sa = scratch_address(&ws);
+    if (sa != GS_OK) return sa;
+    return fused_launch(a, rec, n, ranges, vals, masks, n_views, bg, target, scale, image, T_final, n_contrib,
+                        dL_dimage, loss, grad2d, accumulate, ws, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -415,6 +415,37 @@ gs_status gs_rasterize_fwd_bwd_l1(const float* rec, int64_t n, const uint32_t* r
                                   int32_t accumulate, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * gs_rasterize_fwd_bwd_l1_noalloc -- gs_rasterize_fwd_bwd_l1 without a
+ * workspace argument and without allocating anything, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid allocation, harnesses that prepare every buffer in advance). Same
+ * arguments and results; the workspace is a fixed array of
+ * gs_rasterize_fwd_bwd_l1_noalloc_max_bytes() (8 MiB) on each device, which
+ * the library holds until the process ends and whose address it looks up on
+ * the first call on a device (the device current on the calling thread, which
+ * the stream must belong to).
+ *   Limit: V x tiles_x x rows tiles with a workspace of at most that size
+ *   (36 bytes per tile: about 232,000 tiles, e.g. sixteen 1920x1080 views or
+ *   seven 3840x2160 views); larger windows return GS_ERR_CAPACITY before any
+ *   HIP call.
+ *   Every call on a device uses that device's one array: calls that overlap
+ *   on one device (two streams, two threads) race and must be serialised by
+ *   the caller. Nothing in the array needs clearing between calls.
+ * Errors: as gs_rasterize_fwd_bwd_l1 (without the workspace checks), plus
+ * GS_ERR_CAPACITY, and GS_ERR_HIP when the array's address cannot be found.
+ */
+size_t gs_rasterize_fwd_bwd_l1_noalloc_max_bytes(void);
+
+gs_status gs_rasterize_fwd_bwd_l1_noalloc(const float* rec, int64_t n, const uint32_t* ranges,
+                                          const uint32_t* vals, const uint16_t* masks,
+                                          uint64_t capacity, const gs_camera* cams, int32_t n_views,
+                                          int32_t row0, int32_t rows, const float* bg,
+                                          const float* target, float scale, float* image,
+                                          float* T_final, int32_t* n_contrib, float* dL_dimage,
+                                          double* loss, float* grad2d, int32_t accumulate,
+                                          void* stream);
+
+/*
  * gs_preprocess_bwd -- chain rule from the 2D gradients to all P parameters
  * of every Gaussian, summed over views: conic inverse, EWA covariance
  * (including the depth dependence of the Jacobian), projected mean, 3D

@@ -198,6 +198,20 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert fb(ws_bytes=fws - 4) == INV
     assert fb(accumulate=4) == INV  # only GS_ACCUMULATE_LOSS | GS_ACCUMULATE_GRAD2D
     assert fb(accumulate=-1) == INV
+    # the allocation-free form: the same checks, and windows whose workspace
+    # exceeds the fixed array are refused before any HIP call
+    na_names = [n_ for n_ in fb_names if n_ not in ("ws", "ws_bytes")]
+    na_ok = {k: v for k, v in fb_ok.items() if k not in ("ws", "ws_bytes")}
+
+    def na(**kw):
+        return _call(lib.gs_rasterize_fwd_bwd_l1_noalloc, na_names, na_ok, **kw)
+
+    common_cases(na)
+    assert na(target=None) == INV and na(loss=None) == INV and na(grad2d=None) == INV
+    assert na(accumulate=4) == INV
+    assert lib.gs_rasterize_fwd_bwd_l1_noalloc_max_bytes() == 8 << 20
+    big4k = L.cameras([_cam(width=3840, height=2160)] * 8)  # 8 x 32400 tiles: 9.3 MB of workspace
+    assert na(cams=big4k, V=8, rows=135) == L.GS_ERR_CAPACITY
     # the diagnostic exp path and the plain copy
     assert lib.gs_raster_exp(None, fake, 10, None) == INV
     assert lib.gs_raster_exp(fake, fake, -1, None) == INV
