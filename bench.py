@@ -124,6 +124,9 @@ def parse():
                     help="forward + loss and backward raster as two passes instead of the fused one")
     ap.add_argument("--band-rows", type=int, default=None,
                     help="memory-capped mode: lists and raster one window of this many tile rows at a time")
+    ap.add_argument("--list-budget", type=float, default=None, metavar="MB",
+                    help="memory-capped mode: windows of tile rows planned so that the intersection lists and "
+                         "their workspace stay under this many MB (1e6 bytes)")
     ap.add_argument("--moving-camera", type=float, default=0.0, metavar="DEG",
                     help="turn every camera by this many degrees about its vertical axis after each step, so "
                          "that the visible set changes from step to step (timed steps included)")
@@ -257,7 +260,8 @@ def main():
     target = render(torch.from_numpy(S.make_target_params(cfg)).to(dev), cfg.sh_degree, cams).clone()
     ts = TrainStep(params.clone(), cfg.sh_degree, cams, target, lr=cfg.lr, betas=(cfg.beta1, cfg.beta2),
                    eps=cfg.eps, band_rows=args.band_rows, fused_raster=not args.separate_raster, lists=args.lists,
-                   state_flags=not args.no_state_flags)
+                   state_flags=not args.no_state_flags,
+                   list_budget=int(args.list_budget * 1e6) if args.list_budget else None)
     print(f"[bench] {cfg.name}: inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     b = ts.buf
@@ -311,7 +315,7 @@ def main():
     frac_step = step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9)
     ib = impl_bytes(b.P, b.n, V, K, sum(n_vis), n_any, n_px, n_adam)
     used = ["preprocess"]
-    if args.band_rows or b.path == "binned":
+    if ts.windowed or b.path == "binned":
         used.append("intersections")
     else:
         used += ["emit", "sort", "ranges", "tile_masks"]
@@ -350,10 +354,10 @@ def main():
 
     # intersection statistics; in the memory-capped mode the ranges buffer
     # holds only the last window's tiles
-    n_rng = b.V * b.TX * (b.TY - (b.TY - 1) // args.band_rows * args.band_rows) if args.band_rows else b.V * b.T
+    n_rng = b.V * b.TX * ts.windows[-1][1] if ts.windowed else b.V * b.T
     rng_ = b.ranges.view(-1, 2)[:n_rng].to(torch.int64)
     max_per_tile = int((rng_[:, 1] - rng_[:, 0]).max())
-    peak_list_bytes = b.workspace_bytes()
+    peak_list_bytes = ts.list_bytes()
     copy_gbs = copy_probe(torch, L, dev)
     cpu = cpu1 = None
     if not args.no_cpu_baseline:
@@ -376,7 +380,9 @@ def main():
         "step_hbm_fraction_impl": round(impl_total / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
         "step_impl_bytes": impl_total, "step_impl_bytes_by_stage": impl_terms,
         "intersections": K, "intersections_per_view": K_v, "k_per_gaussian": round(K / b.n, 4),
-        "list_builder": b.path, "band_rows": args.band_rows, "raster": "separate" if args.separate_raster else "fused",
+        "list_builder": b.path, "band_rows": args.band_rows, "list_budget_mb": args.list_budget,
+        "windows": [list(w) for w in ts.windows] if ts.windowed else None,
+        "raster": "separate" if args.separate_raster else "fused",
         "gaussian_order": "generated" if args.generated_order else "morton",
         "adam_state_flags": bool(ts._use_state), "camera_turn_deg_per_step": args.moving_camera,
         "host_count_read": not ts.defer_count or not b.lists_without_count(), "redone_steps": redone,

@@ -36,6 +36,7 @@ EXPORTS = (
     "gs_preprocess_bwd", "gs_adam_step", "gs_adam_step_unless", "gs_preprocess_bwd_adam",
     "gs_raster_exp", "gs_stream_copy",
     "gs_rasterize_fwd_bwd_l1_noalloc", "gs_rasterize_fwd_bwd_l1_noalloc_max_bytes",
+    "gs_window_gaussians", "gs_window_gaussians_workspace_bytes", "gs_adam_step_visible",
 )
 
 
@@ -82,8 +83,10 @@ def lib():
             "gs_emit_intersections": ([_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _U64, _P, _P], ctypes.c_int),
             "gs_sort_keys": ([_P, _P, _P, _P, _U64, _I32, _P, _SZ, _P, _P], ctypes.c_int),
             "gs_tile_ranges": ([_P, _U64, _I64, _P, _P], ctypes.c_int),
-            "gs_tile_lists": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P, _U64, _P, _P, _P, _P, _SZ,
-                               _P], ctypes.c_int),
+            "gs_tile_lists": ([_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P, _U64, _P, _P, _P,
+                               _P, _SZ, _P], ctypes.c_int),
+            "gs_window_gaussians_workspace_bytes": ([_I64, _I32], _SZ),
+            "gs_window_gaussians": ([_P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _SZ, _P], ctypes.c_int),
             "gs_tile_masks_workspace_bytes": ([_U64], _SZ),
             "gs_tile_masks": ([_P, _I64, _P, _P, _U64, _P, _I32, _P, _P, _SZ, _P], ctypes.c_int),
             "gs_rasterize_fwd": ([_P, _I64, _P, _P, _P, _U64, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P],
@@ -95,7 +98,9 @@ def lib():
                                          _P, _P, _P, _P, _I32, _P, _SZ, _P], ctypes.c_int),
             "gs_rasterize_bwd": ([_P, _I64, _P, _P, _P, _U64, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _I32, _P],
                                  ctypes.c_int),
-            "gs_preprocess_bwd": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P], ctypes.c_int),
+            "gs_preprocess_bwd": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _P], ctypes.c_int),
+            "gs_adam_step_visible": ([_P, _P, _P, _P, _I64, _I32, _P, _P, _F64, _F64, _F64, _F64, _I64, _P, _P],
+                                     ctypes.c_int),
             "gs_adam_step": ([_P, _P, _P, _P, _I64, _F64, _F64, _F64, _F64, _I64, _P], ctypes.c_int),
             "gs_adam_step_unless": ([_P, _P, _P, _P, _I64, _F64, _F64, _F64, _F64, _I64, _P, _P], ctypes.c_int),
             "gs_preprocess_bwd_adam": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _F64, _F64, _F64, _F64, _I64, _P,
@@ -206,15 +211,26 @@ def _window(height, rows):
 
 
 def gs_tile_lists(rec, rect, n, n_views, width, height, vals, capacity, ranges, overflow, ws, masks=None,
-                  row0=0, rows=None, stream=None, depth=None, sticky=None):
+                  row0=0, rows=None, stream=None, depth=None, sticky=None, gauss=None, gauss_off=None):
     """masks (optional): the entries' sub-block masks, as gs_tile_masks;
     row0, rows: the window of tile rows (the whole image by default);
     depth (optional): gs_preprocess's compact depths; sticky (optional): a
-    device flag set with the overflow and never cleared."""
-    _check(lib().gs_tile_lists(_ptr(rec), _ptr(rect), _ptr(depth), n, n_views, width, height, row0, _window(height, rows),
+    device flag set with the overflow and never cleared; gauss, gauss_off
+    (optional): gs_window_gaussians' per-view sets to bin."""
+    _check(lib().gs_tile_lists(_ptr(rec), _ptr(rect), _ptr(depth), _ptr(gauss), _ptr(gauss_off), n, n_views, width,
+                               height, row0, _window(height, rows),
                                _ptr(vals), _ptr(masks), capacity,
                                _ptr(ranges), _ptr(overflow), _ptr(sticky), _ptr(ws), ws.numel() * ws.element_size(),
                                _stream(stream)), "gs_tile_lists")
+
+
+def window_gaussians_workspace_bytes(n: int, n_views: int) -> int:
+    return lib().gs_window_gaussians_workspace_bytes(n, n_views)
+
+
+def gs_window_gaussians(rect, n, n_views, height, row0, rows, gauss, gauss_off, ws, stream=None):
+    _check(lib().gs_window_gaussians(_ptr(rect), n, n_views, height, row0, rows, _ptr(gauss), _ptr(gauss_off),
+                                     _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "gs_window_gaussians")
 
 
 def gs_sort_keys(keys, vals, keys_alt, vals_alt, n_keys, end_bit, ws, stream=None) -> bool:
@@ -320,9 +336,19 @@ def gs_rasterize_fwd_bwd_l1_noalloc(rec, n, ranges, vals, masks, cams, bg, targe
            "gs_rasterize_fwd_bwd_l1_noalloc")
 
 
-def gs_preprocess_bwd(params, n, sh_degree, cams, rect, grad2d, grad_params, stream=None):
+def gs_preprocess_bwd(params, n, sh_degree, cams, rect, grad2d, grad_params, stream=None, visible=None):
+    """visible (optional, uint8 [n]): sparse output, rows written only for
+    Gaussians visible in some view (see the header)."""
     _check(lib().gs_preprocess_bwd(_ptr(params), n, sh_degree, cameras(cams), len(cams), _ptr(rect),
-                                   _ptr(grad2d), _ptr(grad_params), _stream(stream)), "gs_preprocess_bwd")
+                                   _ptr(grad2d), _ptr(grad_params), _ptr(visible), _stream(stream)),
+           "gs_preprocess_bwd")
+
+
+def gs_adam_step_visible(params, grad, m, v, n, rows, visible, lr, beta1, beta2, eps, step, state=None, skip=None,
+                         stream=None):
+    _check(lib().gs_adam_step_visible(_ptr(params), _ptr(grad), _ptr(m), _ptr(v), n, rows, _ptr(visible),
+                                      _ptr(state), lr, beta1, beta2, eps, step, _ptr(skip), _stream(stream)),
+           "gs_adam_step_visible")
 
 
 def gs_adam_step(params, grad, m, v, count, lr, beta1, beta2, eps, step, stream=None):

@@ -73,6 +73,56 @@ __global__ __launch_bounds__(EW_THREADS) void k_adam(float* __restrict__ params,
     }
 }
 
+// Adam over a [P][n] block where only the Gaussians with visible[g] set have a
+// gradient (the sparse output of gs_preprocess_bwd): one thread per Gaussian,
+// its P elements one row after the other (consecutive threads, consecutive
+// elements of a row). A Gaussian without a gradient reads no gradient (g = 0:
+// its moments decay and its parameters move by the decayed moments); with
+// state flags, one whose moments are known to be zero is skipped (its update
+// is the identity when eps > 0).
+constexpr int AV_CHUNK = 16;
+
+__global__ __launch_bounds__(EW_THREADS) void k_adam_visible(float* __restrict__ params, const float* __restrict__ grad,
+                                                             float* __restrict__ m, float* __restrict__ v, int64_t n,
+                                                             int32_t P, const uint8_t* __restrict__ visible,
+                                                             uint8_t* __restrict__ state, const AdamConsts c,
+                                                             const int32_t* __restrict__ skip)
+{
+    const int64_t g = (int64_t)blockIdx.x * EW_THREADS + threadIdx.x;
+    if (g >= n) return;
+    if (skip && *skip != 0) return;  // the step's lists overflowed: no update
+    const bool vis = visible[g] != 0;
+    if (state) {
+        if (!vis && state[g] == 0) return;
+        if (vis) state[g] = 1;
+    }
+    for (int r0 = 0; r0 < P; r0 += AV_CHUNK) {
+        float pp[AV_CHUNK], mm[AV_CHUNK], vv[AV_CHUNK], gg[AV_CHUNK];
+#pragma unroll
+        for (int k = 0; k < AV_CHUNK; ++k) {
+            const int r = r0 + k;
+            if (r < P) {
+                const int64_t e = (int64_t)r * n + g;
+                pp[k] = params[e];
+                mm[k] = m[e];
+                vv[k] = v[e];
+                gg[k] = vis ? grad[e] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < AV_CHUNK; ++k) {
+            const int r = r0 + k;
+            if (r < P) {
+                const int64_t e = (int64_t)r * n + g;
+                adam1(pp[k], gg[k], mm[k], vv[k], c);
+                params[e] = pp[k];
+                m[e] = mm[k];
+                v[e] = vv[k];
+            }
+        }
+    }
+}
+
 // Enough blocks to fill the chip several times over; each thread then walks
 // its grid-stride range. The loss uses fewer blocks: each block ends with one
 // fp64 atomic on the same address.
@@ -122,6 +172,22 @@ gs_status gs_adam_step(float* params, const float* grad, float* m, float* v, int
                        double beta2, double eps, int64_t step, void* stream)
 {
     return adam_launch(params, grad, m, v, count, lr, beta1, beta2, eps, step, nullptr, stream);
+}
+
+gs_status gs_adam_step_visible(float* params, const float* grad, float* m, float* v, int64_t n, int32_t rows,
+                               const uint8_t* visible, uint8_t* state, double lr, double beta1, double beta2,
+                               double eps, int64_t step, const int32_t* skip, void* stream)
+{
+    if (n < 0 || rows < 1 || step < 1) return GS_ERR_INVALID_ARGUMENT;
+    if (n > 0 && (!params || !grad || !m || !v || !visible)) return GS_ERR_INVALID_ARGUMENT;
+    if (n > ((int64_t)1 << 31)) return GS_ERR_INVALID_ARGUMENT;
+    AdamConsts c;
+    if (!adam_consts(lr, beta1, beta2, eps, step, c)) return GS_ERR_INVALID_ARGUMENT;
+    if (state && !(eps > 0.0)) return GS_ERR_INVALID_ARGUMENT;  // with eps = 0 the skipped update is 0/0, not the identity
+    if (n == 0) return GS_OK;
+    hipLaunchKernelGGL(k_adam_visible, dim3((unsigned)((n + EW_THREADS - 1) / EW_THREADS)), dim3(EW_THREADS), 0,
+                       (hipStream_t)stream, params, grad, m, v, n, rows, visible, state, c, skip);
+    return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
 }
 
 gs_status gs_adam_step_unless(float* params, const float* grad, float* m, float* v, int64_t count, double lr,

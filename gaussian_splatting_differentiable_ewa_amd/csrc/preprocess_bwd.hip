@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(float* __restrict__ P, i
                                                         const float* __restrict__ grad2d, float* __restrict__ out,
                                                         float* __restrict__ m, float* __restrict__ v,
                                                         const AdamConsts ac, const int32_t* __restrict__ skip,
-                                                        uint8_t* __restrict__ state)
+                                                        uint8_t* __restrict__ state, uint8_t* __restrict__ vis_out)
 {
     // no contraction: the arithmetic is the written one in both forms of the
     // kernel, so the gradient the fused update applies is the one
@@ -55,6 +55,17 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(float* __restrict__ P, i
             return;
         }
         if (seen) state[g] = 1;
+    }
+    if (!ADAM && vis_out) {
+        // sparse output: a Gaussian culled in every view loads nothing and
+        // writes only its flag (its gradient is zero, its rows stay as they are)
+        bool seen = false;
+        for (int v = 0; v < cams.n_views; ++v) {
+            const uint2 rr = *(const uint2*)(rect + 4 * ((int64_t)v * n + g));
+            seen = seen || ((rr.y & 0xffffu) > (rr.x & 0xffffu) && (rr.y >> 16) > (rr.x >> 16));
+        }
+        vis_out[g] = seen ? 1u : 0u;
+        if (!seen) return;
     }
     const float x = P[0 * n + g], y = P[1 * n + g], z = P[2 * n + g];
     GaussLocal L;
@@ -296,15 +307,15 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(float* __restrict__ P, i
 template <bool ADAM>
 static gs_status pbwd_launch(float* params, int64_t n, int32_t sh_degree, const DevCameras& dc,
                              const uint16_t* rect, const float* grad2d, float* out, float* m, float* v,
-                             const AdamConsts& c, const int32_t* skip, uint8_t* state, hipStream_t s)
+                             const AdamConsts& c, const int32_t* skip, uint8_t* state, uint8_t* vis_out, hipStream_t s)
 {
     const dim3 grid(grid_for((uint64_t)n, 256)), block(256);
     const ShConsts K = sh_constants();
     switch (sh_degree) {
-        case 0: hipLaunchKernelGGL((k_preprocess_bwd<0, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip, state); break;
-        case 1: hipLaunchKernelGGL((k_preprocess_bwd<1, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip, state); break;
-        case 2: hipLaunchKernelGGL((k_preprocess_bwd<2, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip, state); break;
-        default: hipLaunchKernelGGL((k_preprocess_bwd<3, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip, state); break;
+        case 0: hipLaunchKernelGGL((k_preprocess_bwd<0, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip, state, vis_out); break;
+        case 1: hipLaunchKernelGGL((k_preprocess_bwd<1, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip, state, vis_out); break;
+        case 2: hipLaunchKernelGGL((k_preprocess_bwd<2, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip, state, vis_out); break;
+        default: hipLaunchKernelGGL((k_preprocess_bwd<3, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip, state, vis_out); break;
     }
     return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
 }
@@ -317,7 +328,7 @@ extern "C" {
 
 gs_status gs_preprocess_bwd(const float* params, int64_t n, int32_t sh_degree, const gs_camera* cams,
                             int32_t n_views, const uint16_t* rect, const float* grad2d, float* grad_params,
-                            void* stream)
+                            uint8_t* visible, void* stream)
 {
     if (n < 0 || sh_degree < 0 || sh_degree > 3) return GS_ERR_INVALID_ARGUMENT;
     if (n > 0 && (!params || !rect || !grad2d || !grad_params)) return GS_ERR_INVALID_ARGUMENT;
@@ -326,7 +337,7 @@ gs_status gs_preprocess_bwd(const float* params, int64_t n, int32_t sh_degree, c
     if (!make_dev_cameras(cams, n_views, dc)) return GS_ERR_INVALID_ARGUMENT;
     if (n == 0) return GS_OK;
     return pbwd_launch<false>((float*)params, n, sh_degree, dc, rect, grad2d, grad_params, nullptr, nullptr,
-                              AdamConsts{}, nullptr, nullptr, (hipStream_t)stream);
+                              AdamConsts{}, nullptr, nullptr, visible, (hipStream_t)stream);
 }
 
 gs_status gs_preprocess_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs_camera* cams,
@@ -342,7 +353,7 @@ gs_status gs_preprocess_bwd_adam(float* params, int64_t n, int32_t sh_degree, co
     AdamConsts c;
     if (!adam_consts(lr, beta1, beta2, eps, step, c)) return GS_ERR_INVALID_ARGUMENT;
     if (n == 0) return GS_OK;
-    return pbwd_launch<true>(params, n, sh_degree, dc, rect, grad2d, grad_params, m, v, c, skip, state,
+    return pbwd_launch<true>(params, n, sh_degree, dc, rect, grad2d, grad_params, m, v, c, skip, state, nullptr,
                              (hipStream_t)stream);
 }
 

@@ -60,6 +60,10 @@ struct BinGrid {
     int64_t chunk;      // Gaussians per chunk
     int32_t band_rows;  // tile rows per band
     int32_t bands;
+    // when given, only the Gaussians list[list_off[v] .. list_off[v + 1]) of
+    // view v are binned (gs_window_gaussians' output); otherwise all n
+    const uint32_t* list;
+    const uint32_t* list_off;
 };
 
 // the workgroup's (view, chunk, band) and its Gaussians and tile rows. The
@@ -72,15 +76,21 @@ struct BinGrid {
 constexpr int64_t BIN_RUN = 16;
 
 struct BinBlock {
-    int64_t v, c, len;  // len: local indices of the chunk (some past n in its last run)
+    int64_t v, c, len;  // len: local indices of the chunk (some past m in its last run)
+    int64_t m;          // Gaussians of the view's set (n, or its list's length)
+    const uint32_t* lv; // the view's list, or null
     uint32_t ty0, ty1;
 };
 
-// The Gaussian at local index l of chunk c (may be >= n in the last run).
-__device__ __forceinline__ int64_t bin_gauss(const BinGrid& G, const BinBlock& B, int64_t l)
+// The position in the view's set of local index l of chunk c (may be >= m in
+// the last run).
+__device__ __forceinline__ int64_t bin_pos(const BinGrid& G, const BinBlock& B, int64_t l)
 {
     return ((l / BIN_RUN) * G.chunks + B.c) * BIN_RUN + (l % BIN_RUN);
 }
+
+// The Gaussian at position p < m of the view's set.
+__device__ __forceinline__ int64_t bin_id(const BinBlock& B, int64_t p) { return B.lv ? (int64_t)B.lv[p] : p; }
 
 __device__ __forceinline__ BinBlock bin_block(const BinGrid& G)
 {
@@ -90,7 +100,15 @@ __device__ __forceinline__ BinBlock bin_block(const BinGrid& G)
     const int64_t rem = blockIdx.x - B.v * per_view;
     B.c = rem / G.bands;
     const int64_t band = rem - B.c * G.bands;
-    const int64_t runs = (G.n + BIN_RUN - 1) / BIN_RUN;
+    if (G.list) {
+        const uint32_t o0 = G.list_off[B.v], o1 = G.list_off[B.v + 1];
+        B.lv = G.list + o0;
+        B.m = o1 > o0 ? (int64_t)(o1 - o0) : 0;
+    } else {
+        B.lv = nullptr;
+        B.m = G.n;
+    }
+    const int64_t runs = (B.m + BIN_RUN - 1) / BIN_RUN;
     B.len = B.c < runs ? (runs - B.c + G.chunks - 1) / G.chunks * BIN_RUN : 0;
     B.ty0 = (uint32_t)(band * G.band_rows);
     B.ty1 = min((uint32_t)G.tiles_y, B.ty0 + (uint32_t)G.band_rows);
@@ -125,8 +143,9 @@ __global__ __launch_bounds__(256) void k_bin_count(const uint16_t* __restrict__ 
         uint2 rr[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int64_t l = l4 + 256 * k, g = bin_gauss(G, B, l);
-            rr[k] = l < B.len && g < G.n ? *(const uint2*)(rect + 4 * (B.v * G.n + g)) : make_uint2(0u, 0u);
+            const int64_t l = l4 + 256 * k, p = bin_pos(G, B, l);
+            const bool in = l < B.len && p < B.m;
+            rr[k] = in ? *(const uint2*)(rect + 4 * (B.v * G.n + bin_id(B, p))) : make_uint2(0u, 0u);
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -254,11 +273,13 @@ __global__ __launch_bounds__(256) void k_bin_fill(const float* __restrict__ rec,
     bool over = false;
     for (int64_t l4 = threadIdx.x; l4 < B.len; l4 += 4 * 256) {
         uint2 rr[4];
-        uint32_t zb[4];
+        uint32_t zb[4], gid[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int64_t l = l4 + 256 * k, g = bin_gauss(G, B, l), idx = B.v * G.n + g;
-            const bool in = l < B.len && g < G.n;
+            const int64_t l = l4 + 256 * k, p = bin_pos(G, B, l);
+            const bool in = l < B.len && p < B.m;
+            const int64_t g = in ? bin_id(B, p) : 0, idx = B.v * G.n + g;
+            gid[k] = (uint32_t)g;
             rr[k] = in ? *(const uint2*)(rect + 4 * idx) : make_uint2(0u, 0u);
             // the compact depths when given: one float of each 48-byte
             // record would touch every cache line of the records
@@ -268,12 +289,11 @@ __global__ __launch_bounds__(256) void k_bin_fill(const float* __restrict__ rec,
         for (int k = 0; k < 4; ++k) {
             uint32_t x0, y0, x1, y1;
             if (!band_rect(rr[k], G, B.ty0, B.ty1, x0, y0, x1, y1)) continue;
-            const uint32_t gid = (uint32_t)bin_gauss(G, B, l4 + 256 * k);
             for (uint32_t ty = y0; ty < y1; ++ty)
                 for (uint32_t tx = x0; tx < x1; ++tx) {
                     const uint32_t pos = atomicAdd(&cur[(ty - B.ty0) * G.tiles_x + tx], 1u);
                     if (pos < capacity)
-                        pairs[pos] = make_uint2(zb[k], gid);
+                        pairs[pos] = make_uint2(zb[k], gid[k]);
                     else
                         over = true;
                 }
@@ -940,6 +960,8 @@ static BinGrid bin_grid(int64_t n, int32_t n_views, int32_t width, int32_t heigh
     G.chunk = std::max<int64_t>(1, (n + G.chunks - 1) / G.chunks);
     G.band_rows = std::max<int32_t>(1, std::min<int32_t>(G.tiles_y, BAND_TILES / G.tiles_x));
     G.bands = (G.tiles_y + G.band_rows - 1) / G.band_rows;
+    G.list = nullptr;
+    G.list_off = nullptr;
     return G;
 }
 
@@ -980,7 +1002,8 @@ size_t gs_tile_lists_workspace_bytes(int64_t n, int32_t n_views, int32_t width, 
     return tl_layout(bin_grid(n, n_views, width, height), n_views, capacity).bytes;
 }
 
-gs_status gs_tile_lists(const float* rec, const uint16_t* rect, const float* depth, int64_t n, int32_t n_views, int32_t width,
+gs_status gs_tile_lists(const float* rec, const uint16_t* rect, const float* depth, const uint32_t* gauss,
+                        const uint32_t* gauss_off, int64_t n, int32_t n_views, int32_t width,
                         int32_t height, int32_t row0, int32_t rows, uint32_t* vals, uint16_t* masks,
                         uint64_t capacity, uint32_t* ranges, int32_t* overflow, int32_t* sticky, void* ws,
                         size_t ws_bytes, void* stream)
@@ -991,7 +1014,10 @@ gs_status gs_tile_lists(const float* rec, const uint16_t* rect, const float* dep
     if (n > 0 && (!rec || !rect)) return GS_ERR_INVALID_ARGUMENT;
     if (capacity > 0 && !vals) return GS_ERR_INVALID_ARGUMENT;
     if (capacity >= ((uint64_t)1 << 32)) return GS_ERR_INVALID_ARGUMENT;
-    const BinGrid G = bin_grid(n, n_views, width, height, row0, rows);
+    if (gauss && !gauss_off) return GS_ERR_INVALID_ARGUMENT;
+    BinGrid G = bin_grid(n, n_views, width, height, row0, rows);
+    G.list = gauss;
+    G.list_off = gauss ? gauss_off : nullptr;
     const TlLayout L = tl_layout(G, n_views, capacity);
     if (ws_bytes < L.bytes) return GS_ERR_INVALID_ARGUMENT;
     const int64_t n_tiles = G.tiles * n_views;

@@ -253,15 +253,28 @@ class TrainStep:
     ``state_flags`` (the default; it takes effect when eps > 0) Adam keeps a
     byte per Gaussian that says whether its moments may be non-zero, and skips
     a Gaussian whose moments are zero and that no view sees, without reading
-    it: its update would leave parameters and moments unchanged."""
+    it: its update would leave parameters and moments unchanged.
+
+    The memory-capped mode (``band_rows`` tile rows per window, or
+    ``list_budget`` bytes for the intersection lists and their workspace)
+    builds and rasterizes the image one window of tile rows at a time, so that
+    the list buffers hold one window: each window bins only the Gaussians
+    whose rectangles meet it (``gs_window_gaussians``), and the loss and 2D
+    gradients are summed over the windows. The windows are planned from the
+    per-tile-row intersection counts, read on the host at the first step and
+    after an overflow only; in between no window reads anything back (an
+    overflow sets the sticky flag, which voids the step's update, and the step
+    is redone with a new plan)."""
 
     RING = 4  # steps whose count and flag may be in flight
+    LIST_SLOT_BYTES = 22  # per list slot: id 4, mask 2, and the builder's two 8-byte (depth, id) copies
 
     def __init__(self, params: torch.Tensor, sh_degree: int, cams: Sequence, target: torch.Tensor,
                  lr=1e-3, betas=(0.9, 0.999), eps=1e-15, bg=(0.0, 0.0, 0.0),
                  m: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None, defer_count: bool = True,
                  fused_adam: bool = True, write_image: bool = False, band_rows: Optional[int] = None,
-                 fused_raster: bool = True, lists: str = "auto", state_flags: bool = True):
+                 fused_raster: bool = True, lists: str = "auto", state_flags: bool = True,
+                 list_budget: Optional[int] = None, sparse_grad: bool = True):
         assert params.is_cuda and params.dtype == torch.float32 and params.is_contiguous()
         self.params = params
         self.sh_degree = sh_degree
@@ -280,16 +293,29 @@ class TrainStep:
         # in a spatial storage order whole waves of such Gaussians skip
         self._use_state = state_flags and eps > 0
         self.grad = None if fused_adam else torch.empty_like(params)
+        # the separate backward and Adam: gradients written and read only for
+        # Gaussians visible in some view (a flag per Gaussian), or dense
+        self.sparse_grad = sparse_grad and not fused_adam
+        self.visible = (torch.zeros(params.shape[1], dtype=torch.uint8, device=params.device)
+                        if self.sparse_grad else None)
         self.lr, self.betas, self.eps, self.bg = lr, betas, eps, bg
         self.t = 0
         self.defer_count = defer_count
         self.fused_adam = fused_adam
         self.fused_raster = fused_raster
         self.band_rows = band_rows
-        if band_rows is not None:
-            if band_rows < 1:
-                raise ValueError("band_rows must be positive")
-            self.buf.lists, self.buf.path = "binned", "binned"
+        self.list_budget = list_budget
+        self.windowed = band_rows is not None or list_budget is not None
+        self.windows = None  # the plan: [(row0, rows)], made at the first step and after an overflow
+        if band_rows is not None and band_rows < 1:
+            raise ValueError("band_rows must be positive")
+        if self.windowed:
+            b = self.buf
+            b.lists, b.path = "binned", "binned"
+            dev = params.device
+            self.win_gauss = torch.empty(max(1, b.V * b.n), dtype=torch.int32, device=dev)
+            self.win_off = torch.empty(b.V + 1, dtype=torch.int32, device=dev)
+            self.win_ws = torch.empty(L.window_gaussians_workspace_bytes(b.n, b.V), dtype=torch.uint8, device=dev)
         self.write_image = write_image
         dev = params.device
         self.sticky = torch.zeros(1, dtype=torch.int32, device=dev)  # an unverified step overflowed
@@ -303,33 +329,99 @@ class TrainStep:
     def stage_names(self):
         """The stages that ``step(marks)`` brackets, in order."""
         tail = ["preprocess_bwd_adam"] if self.fused_adam else ["preprocess_bwd", "adam"]
-        if self.band_rows is not None:
-            return ["preprocess", "bands"] + tail
+        if self.windowed:
+            return ["preprocess", "windows"] + tail
         if self.fused_raster:
             return ["preprocess", "intersections", "tile_masks", "raster_fwd_bwd"] + tail
         return ["preprocess", "intersections", "tile_masks", "raster_fwd_loss", "raster_bwd"] + tail
 
-    def _bands(self, mark):
-        """The image in windows of band_rows tile rows: each window's lists
-        (list buffers sized for the largest window), forward + loss and
-        backward raster, 2D gradients and loss summed over the windows. The
-        capacity is checked after each window's lists (a read of the overflow
-        flag) and doubled, and the window redone, when they did not fit."""
+    def _plan_windows(self):
+        """Windows of tile rows from the per-row intersection counts of the
+        step's rectangles (a host read of the rectangles): rows of band_rows,
+        or the longest runs of rows whose lists, with slack, fit the budget.
+        Sizes the list buffers for the largest window."""
+        import numpy as np
+
+        b = self.buf
+        r = b.rect.view(b.V, b.n, 4).cpu().numpy().view(np.uint16).astype(np.int64)
+        vis = (r[..., 2] > r[..., 0]) & (r[..., 3] > r[..., 1])
+        w, y0, y1 = (r[..., 2] - r[..., 0])[vis], r[..., 1][vis], r[..., 3][vis]
+        diff = np.zeros(b.TY + 1, np.int64)
+        np.add.at(diff, y0, w)
+        np.add.at(diff, y1, -w)
+        per_row = np.cumsum(diff)[:b.TY]  # intersections in each tile row (all views)
+        slack = 1.25
+
+        def slots(k):
+            return int(k * slack) + 4096
+
+        # the window's Gaussian set and its workspace
+        set_bytes = (self.win_gauss.numel() + self.win_off.numel()) * 4 + self.win_ws.numel()
+
+        def fixed(rows):  # the builder's workspace apart from its slots, and the set
+            return L.tile_lists_workspace_bytes(b.n, b.V, b.W, 16 * rows, 0) + set_bytes
+
+        def plan(budget):
+            if self.band_rows is not None:
+                return [(r0, min(self.band_rows, b.TY - r0)) for r0 in range(0, b.TY, self.band_rows)]
+            out, row0 = [], 0
+            while row0 < b.TY:
+                rows, k = 1, int(per_row[row0])
+                while row0 + rows < b.TY:
+                    k2 = k + int(per_row[row0 + rows])
+                    if fixed(rows + 1) + self.LIST_SLOT_BYTES * slots(k2) > budget:
+                        break
+                    rows, k = rows + 1, k2
+                if fixed(rows) + self.LIST_SLOT_BYTES * slots(k) > budget:
+                    raise L.GsError(f"tile row {row0} alone needs more than the list budget of "
+                                    f"{self.list_budget} bytes")
+                out.append((row0, rows))
+                row0 += rows
+            return out
+
+        def peak(ws_):  # the buffers are sized for the most rows and the most intersections
+            k_m = max(int(per_row[a:a + n].sum()) for a, n in ws_)
+            return fixed(max(n for _, n in ws_)) + self.LIST_SLOT_BYTES * slots(k_m)
+
+        windows = plan(self.list_budget)
+        if self.band_rows is None:
+            budget = self.list_budget
+            for _ in range(16):  # shrink the planning budget until the sizing fits too
+                over = peak(windows) - self.list_budget
+                if over <= 0:
+                    break
+                budget -= over + 4096 * self.LIST_SLOT_BYTES
+                windows = plan(budget)
+        k_max = max(int(per_row[a:a + n].sum()) for a, n in windows)
+        rows_max = max(n for _, n in windows)
+        b.K = int(per_row.sum())
+        cap = slots(k_max)
+        if cap != b.capacity or b.allocated_for != b.path:  # sized for this plan, never more
+            b.vals = b.masks = None
+            b.vals = torch.empty(cap, dtype=torch.int32, device=b.device)
+            b.masks = torch.empty(cap, dtype=torch.int16, device=b.device)
+            b.capacity, b.allocated_for = cap, b.path
+        ws = L.tile_lists_workspace_bytes(b.n, b.V, b.W, 16 * rows_max, b.capacity)
+        if getattr(b, "tl_ws", None) is None or b.tl_ws.numel() != ws:
+            b.tl_ws = None
+            b.tl_ws = torch.empty(ws, dtype=torch.uint8, device=b.device)
+        self.windows = windows
+
+    def _windows(self, mark):
+        """The image window by window (see the class note): each window's
+        Gaussian set, lists (the overflow sets the sticky flag), forward + L1
+        + backward raster; no host reads unless a new plan is needed."""
         b = self.buf
         mark(0)
         b.preprocess(self.params)  # also zeroes the visible 2D-gradient records
         mark(1)
-        if b.capacity == 0:
-            nb = -(-b.TY // self.band_rows)
-            b.ensure_capacity(max(2 * int(b.total.item()) // nb, 1 << 16))
-        for i, row0 in enumerate(range(0, b.TY, self.band_rows)):
-            rows = min(self.band_rows, b.TY - row0)
-            while True:
-                L.gs_tile_lists(b.rec, b.rect, b.n, b.V, b.W, b.H, b.vals, b.capacity, b.ranges, b.overflow, b.tl_ws,
-                                masks=b.masks, row0=row0, rows=rows, depth=b.depth)
-                if int(b.overflow.item()) == 0:
-                    break
-                b.ensure_capacity(2 * b.capacity, slack=1.0)
+        if self.windows is None:
+            self._plan_windows()
+        for i, (row0, rows) in enumerate(self.windows):
+            L.gs_window_gaussians(b.rect, b.n, b.V, b.H, row0, rows, self.win_gauss, self.win_off, self.win_ws)
+            L.gs_tile_lists(b.rec, b.rect, b.n, b.V, b.W, b.H, b.vals, b.capacity, b.ranges, b.overflow, b.tl_ws,
+                            masks=b.masks, row0=row0, rows=rows, depth=b.depth, sticky=self.sticky,
+                            gauss=self.win_gauss, gauss_off=self.win_off)
             # the loss is overwritten by the first window and added to by the others
             if self.fused_raster:
                 b.rasterize_fwd_bwd_l1(self.target, self.bg, outputs=self.write_image, image=self.write_image,
@@ -339,8 +431,16 @@ class TrainStep:
                                 accumulate=i > 0)
             L.gs_rasterize_bwd(b.rec, b.n, b.ranges, b.sorted_vals, b.masks, b.cams, self.bg, b.T_final, b.n_contrib,
                                b.dL, b.grad2d, accumulate=True, row0=row0, rows=rows)
-        b.K = int(b.total.item())
         mark(2)
+
+    def list_bytes(self) -> int:
+        """Bytes of the intersection lists and their workspaces (in the
+        memory-capped mode also the window's Gaussian set)."""
+        b = self.buf
+        extra = 0
+        if self.windowed:
+            extra = (self.win_gauss.numel() + self.win_off.numel()) * 4 + self.win_ws.numel()
+        return b.workspace_bytes() + extra
 
     def step(self, marks=None):
         """One step. `marks`, if given, holds len(stage_names) + 1 events,
@@ -348,10 +448,10 @@ class TrainStep:
         b = self.buf
         self._settle(block=len(self._pending) >= self.RING - 1)
         mark = (lambda i: marks[i].record()) if marks is not None else (lambda i: None)
-        deferred = self.defer_count and b.lists_without_count() and self.band_rows is None
+        deferred = self.defer_count and (self.windowed or b.lists_without_count())
         self.t += 1
-        if self.band_rows is not None:
-            self._bands(mark)
+        if self.windowed:
+            self._windows(mark)
             m0 = 3
         else:
             mark(0)
@@ -383,14 +483,20 @@ class TrainStep:
                                      self.betas[0], self.betas[1], self.eps, self.t, skip=skip,
                                      state=self.adam_state if self._use_state else None)
         else:
-            L.gs_preprocess_bwd(self.params, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, self.grad)
+            L.gs_preprocess_bwd(self.params, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, self.grad,
+                                visible=self.visible)
             mark(m0)
-            args = (self.params, self.grad, self.m, self.v, self.params.numel(), self.lr, self.betas[0],
-                    self.betas[1], self.eps, self.t)
-            if deferred:
-                L.gs_adam_step_unless(*args, skip)
+            if self.sparse_grad:
+                L.gs_adam_step_visible(self.params, self.grad, self.m, self.v, b.n, b.P, self.visible, self.lr,
+                                       self.betas[0], self.betas[1], self.eps, self.t,
+                                       state=self.adam_state if self._use_state else None, skip=skip)
             else:
-                L.gs_adam_step(*args)
+                args = (self.params, self.grad, self.m, self.v, self.params.numel(), self.lr, self.betas[0],
+                        self.betas[1], self.eps, self.t)
+                if deferred:
+                    L.gs_adam_step_unless(*args, skip)
+                else:
+                    L.gs_adam_step(*args)
         if deferred:
             hk, hf = self._host[self._slot]
             self._slot = (self._slot + 1) % self.RING
@@ -440,6 +546,9 @@ class TrainStep:
                 self.redone += self.t - (t - 1)
                 self._pending.clear()
                 self.sticky.zero_()
-                b.ensure_capacity(b.K, slack=1.5)
+                if self.windowed:
+                    self.windows = None  # a new plan (and list buffers) at the next step
+                else:
+                    b.ensure_capacity(b.K, slack=1.5)
                 self.t = t - 1
                 return

@@ -225,6 +225,11 @@ size_t gs_tile_lists_workspace_bytes(int64_t n, int32_t n_views, int32_t width, 
  *   rec, rect, n, n_views, width, height   as for gs_emit_intersections
  *   depth      the depth output of gs_preprocess, or NULL (then read from
  *              the records): the same lists either way, with less traffic
+ *   gauss, gauss_off  device, or NULL: bin only the Gaussians
+ *              gauss[gauss_off[v] .. gauss_off[v + 1]) of view v (the output
+ *              of gs_window_gaussians for the same window), so that a window
+ *              reads only the Gaussians that meet it; the lists are the same
+ *              whenever the set holds every Gaussian that meets the window
  *   row0, rows the window of tile rows [row0, row0 + rows) the lists cover
  *              (0 and gs_tiles_y(height) for the whole image): only
  *              intersections with its tiles are listed, so that an image can
@@ -244,13 +249,39 @@ size_t gs_tile_lists_workspace_bytes(int64_t n, int32_t n_views, int32_t width, 
  *              voids every later update until the caller has checked it)
  *   ws         device workspace of gs_tile_lists_workspace_bytes(...)
  * Errors: as gs_emit_intersections, plus a small workspace, capacity >= 2^32,
- * a window outside the tile rows
- * or more than 8192 tile columns.
+ * a window outside the tile rows, gauss without gauss_off, or more than 8192
+ * tile columns.
  */
-gs_status gs_tile_lists(const float* rec, const uint16_t* rect, const float* depth, int64_t n, int32_t n_views,
+gs_status gs_tile_lists(const float* rec, const uint16_t* rect, const float* depth, const uint32_t* gauss,
+                        const uint32_t* gauss_off, int64_t n, int32_t n_views,
                         int32_t width, int32_t height, int32_t row0, int32_t rows, uint32_t* vals,
                         uint16_t* masks, uint64_t capacity, uint32_t* ranges, int32_t* overflow,
                         int32_t* sticky, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace of gs_window_gaussians (bytes); 0 on invalid sizes. */
+size_t gs_window_gaussians_workspace_bytes(int64_t n, int32_t n_views);
+
+/*
+ * gs_window_gaussians -- per view, the Gaussians whose tile rectangle (from
+ * gs_preprocess) meets the window of tile rows [row0, row0 + rows), in index
+ * order: the set gs_tile_lists needs to bin for that window, so that an image
+ * processed window by window (list buffers sized for one window: the
+ * per-tile intersection lists are what runs out of memory first at 4K, "AMD
+ * ROCm team open-sources distributed 3D Gaussian Splatting training",
+ * section "Distributed training architecture and memory scaling") reads
+ * only those Gaussians in each window's binning.
+ *   rect      [n_views][n][4] uint16 from gs_preprocess
+ *   gauss     device out, room for n_views * n ids: view v's members at
+ *             gauss[gauss_off[v] ..], ascending
+ *   gauss_off device out [n_views + 1]: segment starts, gauss_off[n_views] =
+ *             the total
+ *   ws        device workspace of gs_window_gaussians_workspace_bytes(n, V)
+ * Errors: null pointers, n < 0 or n > 2^31, bad view count, a window outside
+ * the tile rows of `height`, a small workspace.
+ */
+gs_status gs_window_gaussians(const uint16_t* rect, int64_t n, int32_t n_views, int32_t height, int32_t row0,
+                              int32_t rows, uint32_t* gauss, uint32_t* gauss_off, void* ws, size_t ws_bytes,
+                              void* stream);
 
 /*
  * gs_tile_ranges -- for every (view, tile) id t = key >> 32, the range
@@ -452,12 +483,22 @@ gs_status gs_rasterize_fwd_bwd_l1_noalloc(const float* rec, int64_t n, const uin
  * covariance from scale and rotation, quaternion normalisation, sigmoid,
  * SH colour (coefficients and view direction). Zero where a Gaussian is culled
  * in every view.
- *   grad_params  out [P][n] fp32, overwritten
+ *   grad_params  out [P][n] fp32, overwritten (see `visible`)
+ *   visible      device out uint8 [n], or NULL. When given, the output is
+ *                sparse: a Gaussian culled in every view reads nothing but
+ *                its rectangles, gets visible[g] = 0 and its rows of
+ *                grad_params are not written (its gradient is zero); the
+ *                others get visible[g] = 1 and their rows. The single-GPU
+ *                half of sending only non-zero gradients (the ByteSplat
+ *                abstract): gs_adam_step_visible then reads gradients only
+ *                where visible[g] is set. NULL: every row written (zeros for
+ *                culled Gaussians).
  * Errors: as gs_preprocess.
  */
 gs_status gs_preprocess_bwd(const float* params, int64_t n, int32_t sh_degree,
                             const gs_camera* cams, int32_t n_views, const uint16_t* rect,
-                            const float* grad2d, float* grad_params, void* stream);
+                            const float* grad2d, float* grad_params, uint8_t* visible,
+                            void* stream);
 
 /*
  * gs_preprocess_bwd_adam -- gs_preprocess_bwd followed by gs_adam_step over
@@ -498,6 +539,24 @@ gs_status gs_preprocess_bwd_adam(float* params, int64_t n, int32_t sh_degree, co
  */
 gs_status gs_adam_step(float* params, const float* grad, float* m, float* v, int64_t count,
                        double lr, double beta1, double beta2, double eps, int64_t step, void* stream);
+
+/*
+ * gs_adam_step_visible -- gs_adam_step over a [rows][n] block whose gradient
+ * exists only for the Gaussians with visible[g] set (the sparse output of
+ * gs_preprocess_bwd), with the same update arithmetic: the gradient of a
+ * Gaussian without the flag is not read (g = 0: its moments still decay and
+ * its parameters still move by them, as in the dense update). With `state`
+ * (uint8 [n], as in gs_preprocess_bwd_adam: 0 asserts that the Gaussian's
+ * moments are zero), a Gaussian without the flag and with state 0 is skipped
+ * without reading anything (its update is the identity when eps > 0), and a
+ * Gaussian with the flag gets state 1. `skip` (device int32 or NULL): no
+ * update at all while it is non-zero (as gs_adam_step_unless).
+ * Errors: null pointers, n < 0 or n > 2^31, rows < 1, step < 1, beta outside
+ * [0, 1), eps < 0, state with eps = 0.
+ */
+gs_status gs_adam_step_visible(float* params, const float* grad, float* m, float* v, int64_t n, int32_t rows,
+                               const uint8_t* visible, uint8_t* state, double lr, double beta1, double beta2,
+                               double eps, int64_t step, const int32_t* skip, void* stream);
 
 /*
  * gs_adam_step_unless -- gs_adam_step, skipped on the device when *skip is

@@ -102,10 +102,11 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert alt.value == 0
     # gs_tile_lists
     big = ctypes.c_size_t(1 << 40)
-    tl_names = ["rec", "rect", "depth", "n", "V", "W", "H", "row0", "rows", "vals", "masks", "capacity", "ranges",
-                "overflow", "sticky", "ws", "ws_bytes", "stream"]
-    tl_ok = dict(rec=fake, rect=fake, depth=None, n=10, V=1, W=256, H=256, row0=0, rows=16, vals=fake, masks=None,
-                 capacity=10, ranges=fake, overflow=fake, sticky=None, ws=fake, ws_bytes=big, stream=None)
+    tl_names = ["rec", "rect", "depth", "gauss", "gauss_off", "n", "V", "W", "H", "row0", "rows", "vals", "masks",
+                "capacity", "ranges", "overflow", "sticky", "ws", "ws_bytes", "stream"]
+    tl_ok = dict(rec=fake, rect=fake, depth=None, gauss=None, gauss_off=None, n=10, V=1, W=256, H=256, row0=0,
+                 rows=16, vals=fake, masks=None, capacity=10, ranges=fake, overflow=fake, sticky=None, ws=fake,
+                 ws_bytes=big, stream=None)
 
     def tl(**kw):
         return _call(lib.gs_tile_lists, tl_names, tl_ok, **kw)
@@ -122,6 +123,16 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert need > 0 and L.tile_lists_workspace_bytes(10, 0, 256, 256, 10) == 0
     assert L.tile_lists_workspace_bytes(10, 1, 16 * 8193, 256, 10) == 0
     assert tl(ws_bytes=need - 1) == INV
+    assert tl(gauss=fake) == INV  # a set without its offsets
+    # gs_window_gaussians
+    wws = L.window_gaussians_workspace_bytes(1000, 2)
+    assert wws > 0 and L.window_gaussians_workspace_bytes(-1, 2) == 0
+    wg = lib.gs_window_gaussians
+    assert wg(fake, 1000, 2, 256, 12, 5, fake, fake, fake, wws, None) == INV  # window past the 16 tile rows
+    assert wg(fake, 1000, 2, 256, 0, 16, fake, None, fake, wws, None) == INV
+    assert wg(fake, 1000, 2, 256, 0, 16, fake, fake, fake, wws - 4, None) == INV
+    assert wg(fake, -1, 2, 256, 0, 16, fake, fake, fake, wws, None) == INV
+    assert wg(fake, 1000, 0, 256, 0, 16, fake, fake, fake, wws, None) == INV
     # gs_tile_ranges
     assert lib.gs_tile_ranges(fake, 10, -1, fake, None) == INV
     assert lib.gs_tile_ranges(None, 10, 4, fake, None) == INV
@@ -233,8 +244,15 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert lib.gs_loss_l1(fake, fake, -1, 1.0, fake, fake, 0, None) == INV
     assert lib.gs_loss_l1(fake, fake, 10, 1.0, fake, None, 0, None) == INV
     assert lib.gs_loss_l1(ctypes.c_void_p(20), fake, 10, 1.0, fake, fake, 0, None) == INV  # misaligned
-    assert lib.gs_preprocess_bwd(fake, 10, 5, cams, 1, fake, fake, fake, None) == INV
-    assert lib.gs_preprocess_bwd(fake, 10, 3, cams, 1, None, fake, fake, None) == INV
+    assert lib.gs_preprocess_bwd(fake, 10, 5, cams, 1, fake, fake, fake, None, None) == INV
+    assert lib.gs_preprocess_bwd(fake, 10, 3, cams, 1, None, fake, fake, None, None) == INV
+    av = lib.gs_adam_step_visible
+    assert av(fake, fake, fake, fake, 10, 59, None, None, 1e-3, 0.9, 0.999, 1e-15, 1, None, None) == INV  # flags
+    assert av(fake, fake, fake, fake, 10, 0, fake, None, 1e-3, 0.9, 0.999, 1e-15, 1, None, None) == INV
+    assert av(fake, fake, fake, fake, -1, 59, fake, None, 1e-3, 0.9, 0.999, 1e-15, 1, None, None) == INV
+    assert av(fake, fake, fake, fake, 10, 59, fake, None, 1e-3, 0.9, 0.999, 1e-15, 0, None, None) == INV
+    assert av(fake, fake, fake, fake, 10, 59, fake, fake, 1e-3, 0.9, 0.999, 0.0, 1, None, None) == INV  # state, eps 0
+    assert av(fake, None, fake, fake, 10, 59, fake, None, 1e-3, 0.9, 0.999, 1e-15, 1, None, None) == INV
     assert lib.gs_adam_step(fake, fake, fake, fake, 10, 1e-3, 0.9, 0.999, 1e-15, 0, None) == INV
     assert lib.gs_adam_step(fake, fake, fake, fake, 10, 1e-3, 1.0, 0.999, 1e-15, 1, None) == INV
     assert lib.gs_adam_step(fake, fake, fake, fake, -1, 1e-3, 0.9, 0.999, 1e-15, 1, None) == INV

@@ -184,7 +184,10 @@ def test_adam_state_skip(run):
     calls whose visibility changes (seen, then culled: the moments keep
     decaying and theta keeps moving; never seen: untouched), and each call's
     parameters and moments equal the oracle's Adam of that call's gradient
-    (gs_preprocess_bwd with the same visibility) from the state before it."""
+    (gs_preprocess_bwd with the same visibility) from the state before it.
+    The separate path with a sparse gradient (gs_preprocess_bwd writing rows
+    only for Gaussians seen in the call, gs_adam_step_visible reading only
+    those) gives the same bits, and leaves the other rows unwritten."""
     import torch
     from gaussian_splatting_differentiable_ewa_amd import _lib as L
     cfg, b = run["cfg"], run["buf"]
@@ -201,7 +204,10 @@ def test_adam_state_skip(run):
     keep[2][: n // 8] = False
     dense = [p0.clone(), torch.zeros_like(p0), torch.zeros_like(p0)]
     skip = [p0.clone(), torch.zeros_like(p0), torch.zeros_like(p0)]
+    sparse = [p0.clone(), torch.zeros_like(p0), torch.zeros_like(p0)]
     state = torch.zeros(n, dtype=torch.uint8, device=dev)
+    state_sp = torch.zeros(n, dtype=torch.uint8, device=dev)
+    visible = torch.zeros(n, dtype=torch.uint8, device=dev)
     for step, kp in enumerate(keep, start=1):
         r = rect0.view(b.V, n, 4).clone()
         r[:, torch.from_numpy(~kp).to(dev)] = 0
@@ -214,7 +220,17 @@ def test_adam_state_skip(run):
         L.gs_preprocess_bwd(skip[0], *args, grad)
         L.gs_preprocess_bwd_adam(dense[0], *args, dense[1], dense[2], *hyper)
         L.gs_preprocess_bwd_adam(skip[0], *args, skip[1], skip[2], *hyper, state=state)
+        g_sp = torch.full_like(p0, float("nan"))
+        L.gs_preprocess_bwd(sparse[0], *args, g_sp, visible=visible)
+        L.gs_adam_step_visible(sparse[0], g_sp, sparse[1], sparse[2], n, b.P, visible, *hyper, state=state_sp)
         torch.cuda.synchronize()
+        seen_now = (r.cpu().numpy().view(np.uint16).astype(np.int32)[..., 2]
+                    > r.cpu().numpy().view(np.uint16).astype(np.int32)[..., 0]).any(axis=0)
+        assert np.array_equal(visible.cpu().numpy() != 0, seen_now)
+        gs_np = PY.np_(g_sp)
+        assert np.isnan(gs_np[:, ~seen_now]).all() and not np.isnan(gs_np[:, seen_now]).any()
+        for a, c in zip(dense, sparse):
+            assert torch.equal(a, c)
         g = PY.np_(grad)
         ref = O.adam(before[0], g, before[1], before[2], cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, step)
         PY.check_adam([PY.np_(x) for x in skip], ref, before[0], g, before[1], cfg.lr, cfg.beta1)

@@ -86,3 +86,63 @@ def test_tile_lists_match_oracle(seed, n, V, big, levels):
         assert int(ovf.item()) == 0
         assert np.array_equal(out.cpu().numpy()[:K].view(np.uint32), vals)
         assert np.array_equal(rng_t.cpu().numpy().view(np.uint32).reshape(-1, 2), ranges)
+
+
+WINDOW_CASES = [
+    # seed, n, views, big share, depth levels, windows of tile rows
+    (11, 3000, 2, (0.1, 0.0), 0, [(0, 5), (5, 5), (10, 2)]),
+    (12, 9000, 1, (0.3,), 5, [(0, 1), (1, 7), (8, 4)]),
+    (13, 2000, 3, (0.0, 0.5, 0.0), 0, [(3, 4), (11, 1)]),
+]
+
+
+@pytest.mark.parametrize("seed,n,V,big,levels,windows", WINDOW_CASES)
+def test_window_sets_and_lists(seed, n, V, big, levels, windows):
+    """gs_window_gaussians lists, per view and in index order, exactly the
+    Gaussians whose rectangle meets the window's tile rows; gs_tile_lists fed
+    that set gives, bit for bit, the oracle's lists of the window's tiles
+    (the whole-image key list restricted to those rows), and the same lists
+    as without the set."""
+    import torch
+    dev = torch.device("cuda:0")
+    rect, vis, z, rec, TX, TY = _scene(seed, n, V, big, levels)
+    rect[vis == 0] = 0
+    keys, vals = O.emit_sorted(rect, vis, z, TX, TY)
+    tile = (keys >> np.uint64(32)).astype(np.int64)
+    view, t = tile // (TX * TY), tile % (TX * TY)
+    ty, tx = t // TX, t % TX
+    rec_t = torch.from_numpy(rec.reshape(-1)).to(dev)
+    rect_t = torch.from_numpy(rect.astype(np.int16).reshape(-1)).to(dev)
+    gauss = torch.full((V * n,), -1, dtype=torch.int32, device=dev)
+    off = torch.full((V + 1,), -1, dtype=torch.int32, device=dev)
+    wws = torch.empty(L.window_gaussians_workspace_bytes(n, V), dtype=torch.uint8, device=dev)
+    for row0, rows in windows:
+        # the window's Gaussian sets against a host compaction
+        L.gs_window_gaussians(rect_t, n, V, H, row0, rows, gauss, off, wws)
+        torch.cuda.synchronize()
+        o = off.cpu().numpy().astype(np.int64)
+        g = gauss.cpu().numpy()
+        meets = (vis == 1) & (rect[..., 1] < row0 + rows) & (rect[..., 3] > row0)
+        assert o[0] == 0 and o[V] == int(meets.sum())
+        for v in range(V):
+            assert np.array_equal(g[o[v]:o[v + 1]], np.nonzero(meets[v])[0])
+        # the oracle's lists of the window's tiles, in window-local tile order
+        sel = (ty >= row0) & (ty < row0 + rows)
+        wtile = view[sel] * (TX * rows) + (ty[sel] - row0) * TX + tx[sel]
+        wkeys = (wtile.astype(np.uint64) << np.uint64(32)) | (keys[sel] & np.uint64(0xffffffff))
+        wvals = vals[sel]
+        wranges = O.tile_ranges(wkeys, V * TX * rows)
+        K = wvals.size
+        for with_set in (True, False):
+            cap = K + 64
+            out = torch.full((cap,), -1, dtype=torch.int32, device=dev)
+            rng_t = torch.full((V * TX * rows * 2,), -1, dtype=torch.int32, device=dev)
+            ovf = torch.full((1,), 5, dtype=torch.int32, device=dev)
+            ws = torch.empty(L.tile_lists_workspace_bytes(n, V, W, 16 * rows, cap), dtype=torch.uint8, device=dev)
+            L.gs_tile_lists(rec_t, rect_t, n, V, W, H, out, cap, rng_t, ovf, ws, row0=row0, rows=rows,
+                            gauss=gauss if with_set else None, gauss_off=off if with_set else None)
+            torch.cuda.synchronize()
+            assert int(ovf.item()) == 0
+            assert np.array_equal(out.cpu().numpy()[:K].view(np.uint32), wvals), (row0, rows, with_set)
+            assert np.array_equal(rng_t.cpu().numpy().view(np.uint32).reshape(-1, 2), wranges), (row0, rows, with_set)
+        print(f"[tile_lists] seed {seed} window {row0}+{rows}: {K} entries, set {o[V]} of {V * n}", flush=True)

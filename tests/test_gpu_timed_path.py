@@ -1,7 +1,9 @@
 """The step exactly as the benchmark times it, against the oracle, element by
 element, through the C ABI:
 
-  * TrainStep's defaults: binned per-tile lists built with the capacity the
+  * TrainStep's defaults (and, on the odd-size scene, the separate raster
+    passes with the separate backward writing a sparse gradient and Adam
+    reading it only for visible Gaussians): binned per-tile lists built with the capacity the
     step has (no host read of the intersection count) under the sticky
     overflow flag; the fused forward + L1 + backward raster pass, tiles taken
     longest list first; 2D-gradient records cleared by the preprocess; Adam
@@ -11,7 +13,8 @@ element, through the C ABI:
     bottom tile row 8 pixels tall, lists of more than 4096 entries) and on an
     odd-size scene (two 250x190 views: a last tile column 10 pixels wide and a
     last tile row 14 pixels tall), the latter also in the memory-capped mode
-    (windows of 5 tile rows, the last one ragged).
+    (windows of 5 tile rows, the last one ragged; and windows planned for a
+    list budget of 26 MB).
 
 Two steps run: the first reads the intersection count on the host, the second
 (the form the benchmark times) does not. The second is compared with the
@@ -46,7 +49,7 @@ def _log(msg):
     print(f"[timed] {msg}", flush=True)
 
 
-def _run_timed(cfg, band_rows=None):
+def _run_timed(cfg, band_rows=None, list_budget=None, separate=False):
     import torch
 
     from gaussian_splatting_differentiable_ewa_amd.step import TrainStep, render, spatial_order
@@ -58,7 +61,8 @@ def _run_timed(cfg, band_rows=None):
     p_np = np.ascontiguousarray(p_np[:, spatial_order(p_np[:3])])
     target0 = S.random_image(cfg.target_seed, len(cams), cams[0].height, cams[0].width)
     ts = TrainStep(torch.from_numpy(p_np).to(dev), cfg.sh_degree, cams, torch.from_numpy(target0).to(dev),
-                   lr=cfg.lr, betas=(cfg.beta1, cfg.beta2), eps=cfg.eps, write_image=True, band_rows=band_rows)
+                   lr=cfg.lr, betas=(cfg.beta1, cfg.beta2), eps=cfg.eps, write_image=True, band_rows=band_rows,
+                   list_budget=list_budget, fused_raster=not separate, fused_adam=not separate)
     ts.step()
     ts.flush()
     assert ts.t == 1
@@ -75,7 +79,12 @@ def _run_timed(cfg, band_rows=None):
     torch.cuda.synchronize()
     b = ts.buf
     assert ts.t == 2 and ts.redone == 0
-    if band_rows is None:
+    if ts.windowed:
+        _log(f"windows {ts.windows}, list bytes {ts.list_bytes()}")
+        assert len(ts.windows) >= 2 and (list_budget is None or ts.list_bytes() <= list_budget)
+    elif separate:
+        assert not ts.fused_raster and not ts.fused_adam and ts.sparse_grad and ts._use_state
+    else:
         assert b.lists_without_count() and b.path == "binned" and ts.fused_raster and ts._use_state
     out = {"image": PY.np_(b.image), "T_final": PY.np_(b.T_final), "n_contrib": PY.np_(b.n_contrib),
            "dL": PY.np_(b.dL), "loss": float(b.loss.item()),
@@ -93,12 +102,20 @@ def _run_timed(cfg, band_rows=None):
             "target": target, "gpu": out, "K": b.K}
 
 
-@pytest.fixture(scope="module", params=["ragged", "ragged-bands", "headline"])
+@pytest.fixture(scope="module", params=["ragged", "ragged-bands", "ragged-budget", "ragged-separate", "headline"])
 def timed(request):
     import torch
     assert torch.cuda.is_available()
     if request.param == "headline":
         r = _run_timed(S.CONFIGS[2])
+    elif request.param == "ragged-separate":
+        # the separate forward + L1 and backward passes, and the separate
+        # backward (sparse gradient) and Adam (visible set, state flags)
+        r = _run_timed(S.RAGGED, separate=True)
+    elif request.param == "ragged-budget":
+        # the lists and their workspace under 26 MB (38.7 MB for the whole
+        # image): windows planned from the per-row counts
+        r = _run_timed(S.RAGGED, list_budget=26_000_000)
     else:
         r = _run_timed(S.RAGGED, band_rows=5 if request.param == "ragged-bands" else None)
     yield r
