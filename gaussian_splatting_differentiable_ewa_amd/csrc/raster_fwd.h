@@ -107,13 +107,13 @@ __device__ __forceinline__ FwdPixel raster_fwd_walk(FwdLds& L, const QuarterCtx&
         }
         const uint32_t iters = max(max(cnt[0], cnt[1]), max(cnt[2], cnt[3]));
         const uint16_t* my_list = L.list + t.row * RW_BATCH;
-        // groups of 8 entries: their record offsets in one 16-byte read
+        // groups of 8 entries: their record offsets in one 16-byte read; a
+        // full group runs as one straight block (no test between entries),
+        // so the scheduler may overlap one entry's LDS reads with the last
         for (uint32_t sb = 0; sb < iters; sb += 8) {
             const uint4 ids = *(const uint4*)(my_list + sb);
             const uint32_t idw[4] = {ids.x, ids.y, ids.z, ids.w};
-#pragma unroll
-            for (uint32_t i = 0; i < 8u; ++i) {
-                if (sb + i >= iters) break;  // wave-uniform
+            auto f1 = [&](uint32_t i) {
                 const uint32_t off = (idw[i >> 1] >> (16 * (i & 1))) & 0xffffu;
                 const float4 q0 = *(const float4*)(recb + off);
                 const float4 q1 = *(const float4*)(recb + off + 16);
@@ -134,6 +134,16 @@ __device__ __forceinline__ FwdPixel raster_fwd_walk(FwdLds& L, const QuarterCtx&
                 Tr = blend ? Tn : Tr;
                 last = blend ? __float_as_int(q2.y) : last;
                 done = done || stop;
+            };
+            if (sb + 8u <= iters) {
+#pragma unroll
+                for (uint32_t i = 0; i < 8u; ++i) f1(i);
+            } else {
+#pragma unroll
+                for (uint32_t i = 0; i < 8u; ++i) {
+                    if (sb + i >= iters) break;  // wave-uniform
+                    f1(i);
+                }
             }
             if (ballot(!done) == 0ull) break;
         }
