@@ -138,6 +138,10 @@ def parse():
     ap.add_argument("--counters-summary", nargs="+", metavar="DIR",
                     help="no benchmark: turn rocprofv3 --pmc runs (SQ counters, csv output) into "
                          "profiles/counters_<workload>.md")
+    ap.add_argument("--runs-summary", nargs="+", metavar="JSON",
+                    help="no benchmark: turn output lines of this script (one file each) into "
+                         "profiles/bench_runs.md; the command of a line is its own 'argv' field, else the "
+                         "--command given for that file, in order")
     ap.add_argument("--command", action="append", default=[],
                     help="for the summaries: a command that produced the profiler output (repeatable; "
                          "quoted in the summary)")
@@ -225,6 +229,8 @@ def impl_bytes(P, n, V, K, Nv, n_any, n_px, n_adam=None):
 # ---- the benchmark ---------------------------------------------------------------
 def main():
     args = parse()
+    if args.runs_summary:
+        return runs_summary(args.runs_summary, args.command, args.note)
     if args.stats_summary:
         return stats_summary(args.stats_summary[0], args.stats_summary[1], args.command, args.note)
     if args.traffic_summary:
@@ -369,6 +375,7 @@ def main():
             cpu1 = cpu_baseline(cfg, params_np, bcams, tgt, threads=1)
 
     out = {
+        "argv": "python bench.py " + " ".join(sys.argv[1:]),
         "metric": METRIC, "value": round(it_s, 3), "unit": "iter/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
@@ -461,32 +468,37 @@ def cpu_baseline(cfg, params_np, cams, target, threads=None):
         st = {}
         clock = time.perf_counter
         t_all = clock()
+
+        def done(stage, t_stage):
+            st[stage] = clock() - t_stage
+            print(f"[bench] oracle {stage}: {st[stage]:.2f} s ({used} threads)", file=sys.stderr, flush=True)
+
         t = clock()
         proj = O.preprocess(params_np, cfg.sh_degree, cams)
-        st["preprocess"] = clock() - t
+        done("preprocess", t)
         rect, vis, z = O.rects(proj)
         t = clock()
         keys, _ = O.emit_sorted(rect, vis, z, cams[0].tiles_x, cams[0].tiles_y)
-        st["emit_sort"] = clock() - t
+        done("emit_sort", t)
         t = clock()
         O.tile_ranges(keys, len(cams) * cams[0].n_tiles)
-        st["ranges"] = clock() - t
+        done("ranges", t)
         t = clock()
         fwd = O.render_fwd(proj, cams)
-        st["raster_fwd"] = clock() - t
+        done("raster_fwd", t)
         t = clock()
         _, dL = O.loss_l1(fwd["image"], target)
-        st["loss"] = clock() - t
+        done("loss", t)
         t = clock()
         g2 = O.render_bwd(proj, cams, dL)
-        st["raster_bwd"] = clock() - t
+        done("raster_bwd", t)
         t = clock()
         grad = O.preprocess_bwd(params_np, cfg.sh_degree, cams, g2)
-        st["preprocess_bwd"] = clock() - t
+        done("preprocess_bwd", t)
         z0 = np.zeros_like(params_np)
         t = clock()
         O.adam(params_np, grad.astype(np.float32), z0, z0, cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, 1)
-        st["adam"] = clock() - t
+        done("adam", t)
         total = clock() - t_all
     finally:
         if threads is not None:
@@ -514,6 +526,57 @@ def _header(title, commands, note):
     if note:
         text += [note, ""]
     return text
+
+
+def runs_summary(files, commands, note):
+    """One row per benchmark line (the last line of each file): workload and
+    options, it/s, ms, Mpix/s, the step's HBM fractions, the stages, the
+    dominant kernel's roofline fraction, and the CPU oracle's whole step."""
+    rows, cmds = [], []
+    for i, path in enumerate(files):
+        with open(path) as fh:
+            d = json.loads(fh.read().strip().splitlines()[-1])
+        cmd = d.get("argv") or (commands[i] if i < len(commands) else "?")
+        cmds.append(cmd)
+        opts = []
+        if d.get("list_budget_mb"):
+            opts.append(f"budget {d['list_budget_mb']:g} MB, {len(d['windows'])} windows")
+        if d.get("band_rows"):
+            opts.append(f"windows of {d['band_rows']} rows")
+        if d.get("raster") == "separate":
+            opts.append("separate raster")
+        if d.get("gaussian_order") == "generated":
+            opts.append("generated order")
+        if not d.get("adam_state_flags"):
+            opts.append("dense Adam")
+        if d.get("camera_turn_deg_per_step"):
+            opts.append(f"camera {d['camera_turn_deg_per_step']:g} deg/step")
+        opts.append(d.get("list_builder", ""))
+        rf = d["roofline"]
+        cpu = d.get("cpu_baseline") or {}
+        cpu1 = d.get("cpu_baseline_1thread") or {}
+        cpu_s = f"{1.0 / cpu['value']:.2f} s ({cpu['cores']} thr)" if cpu else "-"
+        if cpu1:
+            cpu_s += f"; {1.0 / cpu1['value']:.2f} s (1 thr)"
+        stages = ", ".join(f"{k} {v:.3f}" for k, v in d["stages_ms"].items())
+        rows.append(f"| {i + 1} | {d['config']['workload']} | {'; '.join(o for o in opts if o)} | {d['value']:.1f} | "
+                    f"{d['ms_per_step']:.3f} | {d['mpix_per_s']:.0f} | {d['step_hbm_fraction']:.3f} | "
+                    f"{d['step_hbm_fraction_impl']:.3f} | {d['k_per_gaussian']:.2f} | "
+                    f"{d['peak_intersection_bytes'] / 1e6:.1f} | {d.get('redone_steps', 0)} | {stages} | "
+                    f"{rf['kernel']} {rf['frac']:.3f} of {rf['peak']} {rf['unit']} | {cpu_s} |")
+    text = _header("Benchmark lines (bench.py, one MI355X)", [f"({i + 1}) {c}" for i, c in enumerate(cmds)], note)
+    text += ["Columns: it/s and ms per step over the timed steps; Mpix/s = views x W x H x it/s / 1e6; the step's "
+             "HBM fraction with the method's per-stage bytes and with this implementation's; intersections per "
+             "Gaussian; peak list bytes (MB); steps redone after a list overflow; event-timed stages (ms); the "
+             "dominant kernel's roofline fraction; the CPU oracle's whole step (seconds, threads).", "",
+             "| # | workload | options | it/s | ms | Mpix/s | HBM frac (method) | HBM frac (impl) | K/N | list MB | "
+             "redone | stages ms | dominant kernel | CPU oracle step |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"] + rows
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, "bench_runs.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(text) + "\n")
+    print(path)
 
 
 def stats_summary(stats_csv, name, commands, note):

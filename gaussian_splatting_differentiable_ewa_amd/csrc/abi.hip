@@ -218,14 +218,19 @@ __global__ __launch_bounds__(COPY_THREADS) void k_stream_copy(float4* __restrict
 {
     const uint64_t stride = (uint64_t)gridDim.x * COPY_THREADS;
     uint64_t i = (uint64_t)blockIdx.x * COPY_THREADS + threadIdx.x;
+    // streaming (nontemporal) loads and stores: each byte is touched once
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    const v4f* s4 = (const v4f*)src;
+    v4f* d4 = (v4f*)dst;
     for (; i + 3 * stride < n4; i += 4 * stride) {
-        const float4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-        dst[i] = a;
-        dst[i + stride] = b;
-        dst[i + 2 * stride] = c;
-        dst[i + 3 * stride] = d;
+        const v4f a = __builtin_nontemporal_load(s4 + i), b = __builtin_nontemporal_load(s4 + i + stride),
+                  c = __builtin_nontemporal_load(s4 + i + 2 * stride), d = __builtin_nontemporal_load(s4 + i + 3 * stride);
+        __builtin_nontemporal_store(a, d4 + i);
+        __builtin_nontemporal_store(b, d4 + i + stride);
+        __builtin_nontemporal_store(c, d4 + i + 2 * stride);
+        __builtin_nontemporal_store(d, d4 + i + 3 * stride);
     }
-    for (; i < n4; i += stride) dst[i] = src[i];
+    for (; i < n4; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(s4 + i), d4 + i);
 }
 
 }  // namespace gs

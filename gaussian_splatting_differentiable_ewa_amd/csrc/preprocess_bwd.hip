@@ -274,7 +274,10 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(float* __restrict__ P, i
     if (ADAM) {
         // the parameters still in registers (position, SH) are not read
         // again; the moments of CH rows are requested before any is used, so
-        // that each wave keeps many loads in flight
+        // that each wave keeps many loads in flight. Moments and parameters
+        // stream through with nontemporal loads and stores: kept in the
+        // caches as dirty lines, the 708 bytes per Gaussian were written back
+        // while the next step's preprocess ran, and slowed it
         constexpr int CH = 20;
 #pragma unroll
         for (int r0 = 0; r0 < ROWS; r0 += CH) {
@@ -284,8 +287,8 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(float* __restrict__ P, i
                 const int r = r0 + c;
                 if (r < ROWS) {
                     const int64_t e = (int64_t)r * n + g;
-                    mm[c] = m[e];
-                    vv[c] = v[e];
+                    mm[c] = __builtin_nontemporal_load(m + e);
+                    vv[c] = __builtin_nontemporal_load(v + e);
                     pp[c] = r == 0 ? x : r == 1 ? y : r == 2 ? z : r >= 11 ? sh[r - 11] : P[e];
                 }
             }
@@ -295,9 +298,9 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(float* __restrict__ P, i
                 if (r < ROWS) {
                     const int64_t e = (int64_t)r * n + g;
                     adam1(pp[c], G[r], mm[c], vv[c], ac);
-                    P[e] = pp[c];
-                    m[e] = mm[c];
-                    v[e] = vv[c];
+                    __builtin_nontemporal_store(pp[c], P + e);
+                    __builtin_nontemporal_store(mm[c], m + e);
+                    __builtin_nontemporal_store(vv[c], v + e);
                 }
             }
         }
