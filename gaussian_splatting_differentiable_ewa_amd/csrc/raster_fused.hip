@@ -142,10 +142,10 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_fwd_bwd_l1(
     const int64_t pix = (int64_t)t.j * W + t.i;
     const int64_t o = (int64_t)t.view * 3 * HW + pix;
     float tg0 = 0.f, tg1 = 0.f, tg2 = 0.f;
-    if (t.inside) {
-        tg0 = target[o];
-        tg1 = target[o + HW];
-        tg2 = target[o + 2 * HW];
+    if (t.inside) {  // read once per step: streamed past the caches
+        tg0 = __builtin_nontemporal_load(target + o);
+        tg1 = __builtin_nontemporal_load(target + o + HW);
+        tg2 = __builtin_nontemporal_load(target + o + 2 * HW);
     }
     const FwdPixel P = raster_fwd_walk(*reinterpret_cast<FwdLds*>(lds), t, rec, n, ranges, vals, masks, cap);
     float g0 = 0.f, g1 = 0.f, g2 = 0.f, ad = 0.f;
