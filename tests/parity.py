@@ -303,7 +303,7 @@ def check_param_grads(g_gpu, g_ref):
     bad = ~(err <= lim)
     assert not bad.any(), f"{bad.sum()} parameter gradients out of tolerance, rows {np.unique(np.nonzero(bad)[0])}"
     nz = np.abs(ref) > 0
-    return {"pgrad_within_1e-3_rel": float(np.mean(err[nz] <= PGRAD_RTOL * np.abs(ref[nz])))}
+    return {"pgrad_within_1e-3_rel": float(np.mean(err[nz] <= PGRAD_RTOL * np.abs(ref[nz]))) if nz.any() else 1.0}
 
 
 def param_grads_e2e(g_gpu, g_ref):

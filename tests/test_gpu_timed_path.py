@@ -14,7 +14,9 @@ element, through the C ABI:
     odd-size scene (two 250x190 views: a last tile column 10 pixels wide and a
     last tile row 14 pixels tall), the latter also in the memory-capped mode
     (windows of 5 tile rows, the last one ragged; and windows planned for a
-    list budget of 26 MB).
+    list budget of 26 MB);
+  * on degenerate scenes (DEGENERATE below): no Gaussian in front of the
+    camera, sixteen views (SH 1), a 17x3 image (SH 2), a single Gaussian.
 
 Two steps run: the first reads the intersection count on the host, the second
 (the form the benchmark times) does not. The second is compared with the
@@ -49,7 +51,7 @@ def _log(msg):
     print(f"[timed] {msg}", flush=True)
 
 
-def _run_timed(cfg, band_rows=None, list_budget=None, separate=False):
+def _run_timed(cfg, band_rows=None, list_budget=None, separate=False, lists="auto"):
     import torch
 
     from gaussian_splatting_differentiable_ewa_amd.step import TrainStep, render, spatial_order
@@ -62,7 +64,7 @@ def _run_timed(cfg, band_rows=None, list_budget=None, separate=False):
     target0 = S.random_image(cfg.target_seed, len(cams), cams[0].height, cams[0].width)
     ts = TrainStep(torch.from_numpy(p_np).to(dev), cfg.sh_degree, cams, torch.from_numpy(target0).to(dev),
                    lr=cfg.lr, betas=(cfg.beta1, cfg.beta2), eps=cfg.eps, write_image=True, band_rows=band_rows,
-                   list_budget=list_budget, fused_raster=not separate, fused_adam=not separate)
+                   list_budget=list_budget, fused_raster=not separate, fused_adam=not separate, lists=lists)
     ts.step()
     ts.flush()
     assert ts.t == 1
@@ -102,11 +104,36 @@ def _run_timed(cfg, band_rows=None, list_budget=None, separate=False):
             "target": target, "gpu": out, "K": b.K}
 
 
-@pytest.fixture(scope="module", params=["ragged", "ragged-bands", "ragged-budget", "ragged-separate", "headline"])
+# Degenerate scenes for the same path: every Gaussian behind the camera (no
+# intersection: the background everywhere, nothing seen, Adam skips them all);
+# sixteen views, the most one call takes; a 17x3 image (one tile row 3 pixels
+# tall, a last tile column 1 pixel wide, three of a tile's four quarters
+# empty); a single Gaussian.
+DEGENERATE = {
+    "culled": S.SceneConfig("culled-5k-sh3-64x48", 20, 21, 5000, 3, (-2.0, -2.0, -6.0), (2.0, 2.0, -2.0), 0, 0.0,
+                            -3.0, 0.3, 64, 48, 64.0),
+    "sixteen-views": S.SceneConfig("sixteen-3k-sh1-16x64x48", 22, 23, 3000, 1, (-1.0, -1.0, 3.0), (1.0, 1.0, 6.0),
+                                   4, 0.3, -3.5, 0.4, 64, 48, 64.0, yaws=tuple(2.0 * i for i in range(16)),
+                                   orbit_centre=(0.0, 0.0, 4.5)),
+    "sliver": S.SceneConfig("sliver-2k-sh2-17x3", 24, 25, 2000, 2, (-0.5, -0.2, 2.0), (0.5, 0.2, 4.0), 0, 0.0,
+                            -3.5, 0.4, 17, 3, 20.0),
+    "single": S.SceneConfig("single-1-sh3-32x32", 26, 27, 1, 3, (-0.1, -0.1, 2.0), (0.1, 0.1, 2.5), 0, 0.0,
+                            -1.5, 0.1, 32, 32, 32.0),
+}
+
+
+@pytest.fixture(scope="module", params=["ragged", "ragged-bands", "ragged-budget", "ragged-separate", "headline"]
+                + list(DEGENERATE))
 def timed(request):
     import torch
     assert torch.cuda.is_available()
-    if request.param == "headline":
+    if request.param in DEGENERATE:
+        # the binned lists as on the timed path, whatever the intersection count
+        r = _run_timed(DEGENERATE[request.param], lists="binned")
+        if request.param == "culled":
+            assert r["K"] == 0
+            assert not r["gpu"]["state"].any()
+    elif request.param == "headline":
         r = _run_timed(S.CONFIGS[2])
     elif request.param == "ragged-separate":
         # the separate forward + L1 and backward passes, and the separate
