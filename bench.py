@@ -114,8 +114,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="scene id (2 = the headline workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--lists", choices=["auto", "binned", "radix"], default="auto",
-                    help="list builder: binning per tile, the global key sort, or chosen per scene")
+    ap.add_argument("--lists", choices=["auto", "binned", "radix", "compact"], default="auto",
+                    help="list builder: binning per tile, the global key sort, binning of the Gaussians each view "
+                         "sees, or chosen per scene")
     ap.add_argument("--no-state-flags", action="store_true",
                     help="dense Adam: read every Gaussian's moments, also those known to be zero and unseen")
     ap.add_argument("--generated-order", action="store_true",
@@ -204,6 +205,9 @@ def impl_bytes(P, n, V, K, Nv, n_any, n_px, n_adam=None):
         # intersection, each sorted through LDS (read + write of depth and
         # id), ranges; the masks' record gathers are cache traffic
         "intersections": 2 * 12 * Nv + (8 + 8) * K + (4 + 2) * K + 8 * V * n_px // 256,
+        # the "compact" builder's sets: every pair's rectangle read twice
+        # (count, write), each seen Gaussian's index written
+        "visible_sets": 2 * 8 * V * n + 4 * Nv,
         # the three global-sort stages and the mask pass
         "emit": 16 * V * n + 12 * K,
         "sort": 24 * K,
@@ -321,8 +325,10 @@ def main():
     frac_step = step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9)
     ib = impl_bytes(b.P, b.n, V, K, sum(n_vis), n_any, n_px, n_adam)
     used = ["preprocess"]
-    if ts.windowed or b.path == "binned":
+    if ts.windowed or b.binned:
         used.append("intersections")
+        if b.path == "compact" and not ts.windowed:
+            used.append("visible_sets")
     else:
         used += ["emit", "sort", "ranges", "tile_masks"]
     used += ["raster_fwd_bwd"] if ts.fused_raster else ["raster_fwd_loss", "raster_bwd"]

@@ -83,7 +83,7 @@ def lib():
             "gs_emit_intersections": ([_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _U64, _P, _P], ctypes.c_int),
             "gs_sort_keys": ([_P, _P, _P, _P, _U64, _I32, _P, _SZ, _P, _P], ctypes.c_int),
             "gs_tile_ranges": ([_P, _U64, _I64, _P, _P], ctypes.c_int),
-            "gs_tile_lists": ([_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P, _U64, _P, _P, _P,
+            "gs_tile_lists": ([_P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P, _U64, _P, _P, _P,
                                _P, _SZ, _P], ctypes.c_int),
             "gs_window_gaussians_workspace_bytes": ([_I64, _I32], _SZ),
             "gs_window_gaussians": ([_P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _SZ, _P], ctypes.c_int),
@@ -211,13 +211,15 @@ def _window(height, rows):
 
 
 def gs_tile_lists(rec, rect, n, n_views, width, height, vals, capacity, ranges, overflow, ws, masks=None,
-                  row0=0, rows=None, stream=None, depth=None, sticky=None, gauss=None, gauss_off=None):
+                  row0=0, rows=None, stream=None, depth=None, sticky=None, gauss=None, gauss_off=None, set_max=0):
     """masks (optional): the entries' sub-block masks, as gs_tile_masks;
     row0, rows: the window of tile rows (the whole image by default);
     depth (optional): gs_preprocess's compact depths; sticky (optional): a
     device flag set with the overflow and never cleared; gauss, gauss_off
-    (optional): gs_window_gaussians' per-view sets to bin."""
-    _check(lib().gs_tile_lists(_ptr(rec), _ptr(rect), _ptr(depth), _ptr(gauss), _ptr(gauss_off), n, n_views, width,
+    (optional): gs_window_gaussians' per-view sets to bin; set_max: the
+    largest set expected (sizes the binning grid; 0 for all n)."""
+    _check(lib().gs_tile_lists(_ptr(rec), _ptr(rect), _ptr(depth), _ptr(gauss), _ptr(gauss_off), set_max, n,
+                               n_views, width,
                                height, row0, _window(height, rows),
                                _ptr(vals), _ptr(masks), capacity,
                                _ptr(ranges), _ptr(overflow), _ptr(sticky), _ptr(ws), ws.numel() * ws.element_size(),

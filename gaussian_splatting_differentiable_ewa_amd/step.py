@@ -13,10 +13,13 @@ skipped, so the state is exactly that of the step before).
 
 The per-tile lists come from ``gs_tile_lists`` (binning, then a sort of each
 tile on its own) or from the global 64-bit key path (``gs_emit_intersections``,
-``gs_sort_keys``, ``gs_tile_ranges``); both give the same ids and ranges.
-``lists="auto"`` picks binning unless the (view, Gaussian) pairs outnumber the
-intersections (a large scene mostly outside the views, where binning's two
-passes over every pair cost more than the sort).
+``gs_sort_keys``, ``gs_tile_ranges``); all give the same ids and ranges.
+``lists="compact"`` bins only the Gaussians each view sees: ``gs_window_gaussians``
+over the whole image lists them, and ``gs_tile_lists`` bins that set with its
+grid sized for it (planned from the set sizes read when K is read).
+``lists="auto"`` picks binning of every pair unless the (view, Gaussian) pairs
+outnumber the intersections (a large scene mostly outside the views), and the
+compacted set then.
 """
 
 from __future__ import annotations
@@ -32,7 +35,7 @@ class Buffers:
     """Device buffers of one step for N Gaussians and a set of same-size views."""
 
     def __init__(self, n: int, sh_degree: int, cams: Sequence, device="cuda", lists: str = "auto"):
-        if lists not in ("auto", "binned", "radix"):
+        if lists not in ("auto", "binned", "radix", "compact"):
             raise ValueError(f"unknown list builder {lists!r}")
         self.lists = lists
         self.path = "binned" if lists == "auto" else lists
@@ -69,6 +72,8 @@ class Buffers:
         self.K = 0
         self.sorted_in_alt = False
         self.device = dev
+        self.set_gauss = None  # the "compact" builder's visible sets (gs_window_gaussians)
+        self.set_max = 0
 
     def ensure_capacity(self, K: int, slack: float = 1.25):
         if K <= self.capacity and self.capacity > 0 and self.allocated_for == self.path:
@@ -95,7 +100,16 @@ class Buffers:
             return 0
         if self.path == "radix":
             return 2 * 12 * self.capacity + 6 * self.capacity + self.sort_ws.numel()
-        return 6 * self.capacity + self.tl_ws.numel()
+        extra = 0
+        if self.path == "compact" and self.set_gauss is not None:
+            extra = (self.set_gauss.numel() + self.set_off.numel()) * 4 + self.set_ws.numel()
+        return 6 * self.capacity + self.tl_ws.numel() + extra
+
+    @property
+    def binned(self) -> bool:
+        """Whether the lists come from gs_tile_lists (with or without the
+        compacted sets)."""
+        return self.path in ("binned", "compact")
 
     @property
     def sorted_keys(self):
@@ -115,7 +129,7 @@ class Buffers:
 
     def lists_without_count(self) -> bool:
         """Whether the lists can be built before K is known on the host."""
-        return self.path == "binned" and self.capacity > 0 and self.lists != "radix"
+        return self.binned and self.capacity > 0 and self.lists != "radix"
 
     def intersections(self, read_count: bool = True):
         """Build the per-tile lists, their ranges and sub-block masks: read K
@@ -128,7 +142,7 @@ class Buffers:
     def tile_masks(self):
         """The lists' sub-block masks: written by the binned builder with the
         lists; computed from the finished lists on the global-sort path."""
-        if self.path == "binned":
+        if self.binned:
             return
         L.gs_tile_masks(self.rec, self.n, self.ranges, self.sorted_vals, self.capacity, self.cams, self.masks,
                         self.tm_ws)
@@ -137,25 +151,46 @@ class Buffers:
         """The lists and ranges alone (see ``intersections``); `sticky`, a
         device flag the binned builder sets with its overflow flag."""
         if not read_count and self.lists_without_count():
-            L.gs_tile_lists(self.rec, self.rect, self.n, self.V, self.W, self.H, self.vals, self.capacity,
-                            self.ranges, self.overflow, self.tl_ws, masks=self.masks, depth=self.depth, sticky=sticky)
+            self._bin(sticky)
             return
         self.K = int(self.total.item())
         if self.K >= 2 ** 32:
             raise L.GsError(f"{self.K} intersections exceed the 32-bit key index")
         if self.lists == "auto":
-            self.path = "binned" if self.V * self.n <= self.K else "radix"
+            self.path = "binned" if self.V * self.n <= self.K else "compact"
         self.ensure_capacity(self.K)
-        if self.path == "binned":
+        if self.binned:
             self.sorted_in_alt = False
-            L.gs_tile_lists(self.rec, self.rect, self.n, self.V, self.W, self.H, self.vals, self.capacity,
-                            self.ranges, self.overflow, self.tl_ws, masks=self.masks, depth=self.depth)
+            self._bin(None, plan=True)
             return
         L.gs_emit_intersections(self.rec, self.rect, self.offsets, self.n, self.V, self.W, self.H,
                                 self.keys, self.vals, self.capacity, self.overflow)
         self.sorted_in_alt = L.gs_sort_keys(self.keys, self.vals, self.keys_alt, self.vals_alt, self.K,
                                             self.end_bit, self.sort_ws)
         L.gs_tile_ranges(self.sorted_keys, self.K, self.V * self.T, self.ranges)
+
+    def _bin(self, sticky, plan: bool = False):
+        """gs_tile_lists over every (view, Gaussian) pair, or ("compact")
+        over the sets of Gaussians each view sees; `plan` (a point where K is
+        read on the host anyway): read the set sizes and size the binning
+        grid for them, with slack (a larger set later is still binned whole)."""
+        gauss = off = None
+        if self.path == "compact":
+            if self.set_gauss is None:
+                dev = self.device
+                self.set_gauss = torch.empty(max(1, self.V * self.n), dtype=torch.int32, device=dev)
+                self.set_off = torch.empty(self.V + 1, dtype=torch.int32, device=dev)
+                self.set_ws = torch.empty(L.window_gaussians_workspace_bytes(self.n, self.V), dtype=torch.uint8,
+                                          device=dev)
+            L.gs_window_gaussians(self.rect, self.n, self.V, self.H, 0, self.TY, self.set_gauss, self.set_off,
+                                  self.set_ws)
+            if plan or self.set_max == 0:
+                o = self.set_off.cpu().numpy().astype("int64")
+                self.set_max = min(self.n, int(1.25 * int((o[1:] - o[:-1]).max(initial=0))) + 4096)
+            gauss, off = self.set_gauss, self.set_off
+        L.gs_tile_lists(self.rec, self.rect, self.n, self.V, self.W, self.H, self.vals, self.capacity, self.ranges,
+                        self.overflow, self.tl_ws, masks=self.masks, depth=self.depth, sticky=sticky, gauss=gauss,
+                        gauss_off=off, set_max=self.set_max if gauss is not None else 0)
 
     def rasterize(self, bg=(0.0, 0.0, 0.0)):
         L.gs_rasterize_fwd(self.rec, self.n, self.ranges, self.sorted_vals, self.masks, self.cams, bg, self.image,
@@ -307,6 +342,7 @@ class TrainStep:
         self.list_budget = list_budget
         self.windowed = band_rows is not None or list_budget is not None
         self.windows = None  # the plan: [(row0, rows)], made at the first step and after an overflow
+        self.set_max = 0  # the largest window set of the plan (with slack)
         if band_rows is not None and band_rows < 1:
             raise ValueError("band_rows must be positive")
         if self.windowed:
@@ -345,6 +381,7 @@ class TrainStep:
         b = self.buf
         r = b.rect.view(b.V, b.n, 4).cpu().numpy().view(np.uint16).astype(np.int64)
         vis = (r[..., 2] > r[..., 0]) & (r[..., 3] > r[..., 1])
+        y0_all, y1_all = r[..., 1], r[..., 3]
         w, y0, y1 = (r[..., 2] - r[..., 0])[vis], r[..., 1][vis], r[..., 3][vis]
         diff = np.zeros(b.TY + 1, np.int64)
         np.add.at(diff, y0, w)
@@ -394,6 +431,13 @@ class TrainStep:
                 windows = plan(budget)
         k_max = max(int(per_row[a:a + n].sum()) for a, n in windows)
         rows_max = max(n for _, n in windows)
+        # the most Gaussians a view's window set holds (with slack): sizes the
+        # binning grid for the sets (a larger set later is still binned whole)
+        set_max = 0
+        for a, n_rows in windows:
+            meets = vis & (y0_all < a + n_rows) & (y1_all > a)
+            set_max = max(set_max, int(meets.sum(axis=1).max(initial=0)))
+        self.set_max = min(b.n, int(1.25 * set_max) + 4096)
         b.K = int(per_row.sum())
         cap = slots(k_max)
         if cap != b.capacity or b.allocated_for != b.path:  # sized for this plan, never more
@@ -421,7 +465,7 @@ class TrainStep:
             L.gs_window_gaussians(b.rect, b.n, b.V, b.H, row0, rows, self.win_gauss, self.win_off, self.win_ws)
             L.gs_tile_lists(b.rec, b.rect, b.n, b.V, b.W, b.H, b.vals, b.capacity, b.ranges, b.overflow, b.tl_ws,
                             masks=b.masks, row0=row0, rows=rows, depth=b.depth, sticky=self.sticky,
-                            gauss=self.win_gauss, gauss_off=self.win_off)
+                            gauss=self.win_gauss, gauss_off=self.win_off, set_max=self.set_max)
             # the loss is overwritten by the first window and added to by the others
             if self.fused_raster:
                 b.rasterize_fwd_bwd_l1(self.target, self.bg, outputs=self.write_image, image=self.write_image,

@@ -230,6 +230,11 @@ size_t gs_tile_lists_workspace_bytes(int64_t n, int32_t n_views, int32_t width, 
  *              of gs_window_gaussians for the same window), so that a window
  *              reads only the Gaussians that meet it; the lists are the same
  *              whenever the set holds every Gaussian that meets the window
+ *   set_max    with gauss: the most Gaussians a view's set is expected to
+ *              hold (0: n), to size the binning grid for the set rather than
+ *              for all n Gaussians (a far smaller count table when few are
+ *              visible); a larger set is still binned whole, only more
+ *              slowly. Must be 0 without gauss.
  *   row0, rows the window of tile rows [row0, row0 + rows) the lists cover
  *              (0 and gs_tiles_y(height) for the whole image): only
  *              intersections with its tiles are listed, so that an image can
@@ -249,11 +254,11 @@ size_t gs_tile_lists_workspace_bytes(int64_t n, int32_t n_views, int32_t width, 
  *              voids every later update until the caller has checked it)
  *   ws         device workspace of gs_tile_lists_workspace_bytes(...)
  * Errors: as gs_emit_intersections, plus a small workspace, capacity >= 2^32,
- * a window outside the tile rows, gauss without gauss_off, or more than 8192
- * tile columns.
+ * a window outside the tile rows, gauss without gauss_off, set_max < 0 or
+ * set_max > 0 without gauss, or more than 8192 tile columns.
  */
 gs_status gs_tile_lists(const float* rec, const uint16_t* rect, const float* depth, const uint32_t* gauss,
-                        const uint32_t* gauss_off, int64_t n, int32_t n_views,
+                        const uint32_t* gauss_off, int64_t set_max, int64_t n, int32_t n_views,
                         int32_t width, int32_t height, int32_t row0, int32_t rows, uint32_t* vals,
                         uint16_t* masks, uint64_t capacity, uint32_t* ranges, int32_t* overflow,
                         int32_t* sticky, void* ws, size_t ws_bytes, void* stream);

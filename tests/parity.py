@@ -63,6 +63,16 @@ def gpu_forward(params_np: np.ndarray, sh: int, cams, bg=(0.0, 0.0, 0.0)):
     out["overflow"] = int(np_(br.overflow)[0])
     out["radix_masks"] = np_(br.masks[:K]).view(np.uint16)  # gs_tile_masks on the sorted keys' lists
     del br
+    # the binned builder on the sets of Gaussians each view sees
+    bc = Buffers(p.shape[1], sh, cams, device=dev, lists="compact")
+    bc.rec, bc.rect, bc.offsets, bc.total, bc.depth = b.rec, b.rect, b.offsets, b.total, b.depth
+    bc.intersections()
+    torch.cuda.synchronize()
+    out["compact_vals"] = np_(bc.sorted_vals[:K]).view(np.uint32)
+    out["compact_ranges"] = np_(bc.ranges).view(np.uint32).reshape(-1, 2)
+    out["compact_masks"] = np_(bc.masks[:K]).view(np.uint16)
+    out["compact_set_max"] = bc.set_max
+    del bc
     b.intersections()
     b.rasterize(bg)
     torch.cuda.synchronize()

@@ -102,9 +102,10 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert alt.value == 0
     # gs_tile_lists
     big = ctypes.c_size_t(1 << 40)
-    tl_names = ["rec", "rect", "depth", "gauss", "gauss_off", "n", "V", "W", "H", "row0", "rows", "vals", "masks",
+    tl_names = ["rec", "rect", "depth", "gauss", "gauss_off", "set_max", "n", "V", "W", "H", "row0", "rows", "vals",
+                "masks",
                 "capacity", "ranges", "overflow", "sticky", "ws", "ws_bytes", "stream"]
-    tl_ok = dict(rec=fake, rect=fake, depth=None, gauss=None, gauss_off=None, n=10, V=1, W=256, H=256, row0=0,
+    tl_ok = dict(rec=fake, rect=fake, depth=None, gauss=None, gauss_off=None, set_max=0, n=10, V=1, W=256, H=256, row0=0,
                  rows=16, vals=fake, masks=None, capacity=10, ranges=fake, overflow=fake, sticky=None, ws=fake,
                  ws_bytes=big, stream=None)
 
@@ -124,6 +125,8 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert L.tile_lists_workspace_bytes(10, 1, 16 * 8193, 256, 10) == 0
     assert tl(ws_bytes=need - 1) == INV
     assert tl(gauss=fake) == INV  # a set without its offsets
+    assert tl(set_max=5) == INV  # a set size without a set
+    assert tl(gauss=fake, gauss_off=fake, set_max=-1) == INV
     # gs_window_gaussians
     wws = L.window_gaussians_workspace_bytes(1000, 2)
     assert wws > 0 and L.window_gaussians_workspace_bytes(-1, 2) == 0

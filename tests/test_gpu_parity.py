@@ -61,6 +61,11 @@ def test_tile_masks(run):
     # are the same lists): identical bits
     assert np.array_equal(gpu["vals"], gpu["binned_vals"])
     assert np.array_equal(gpu["masks"], gpu["radix_masks"])
+    # binning only the Gaussians each view sees (gs_window_gaussians over the
+    # whole image, the grid sized for those sets): the same lists and masks
+    assert np.array_equal(gpu["compact_vals"], gpu["binned_vals"])
+    assert np.array_equal(gpu["compact_ranges"], gpu["binned_ranges"])
+    assert np.array_equal(gpu["compact_masks"], gpu["masks"])
     st = PY.check_masks(gpu["masks"], gpu["binned_vals"], gpu["binned_ranges"], run["orc"], run["cams"],
                         sample=200000)
     print(st)

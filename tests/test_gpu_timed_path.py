@@ -15,6 +15,9 @@ element, through the C ABI:
     last tile row 14 pixels tall), the latter also in the memory-capped mode
     (windows of 5 tile rows, the last one ragged; and windows planned for a
     list budget of 26 MB);
+  * the odd-size scene also with the lists binned from the sets of
+    Gaussians each view sees (gs_window_gaussians, the binning grid sized for
+    them);
   * on degenerate scenes (DEGENERATE below): no Gaussian in front of the
     camera, sixteen views (SH 1), a 17x3 image (SH 2), a single Gaussian.
 
@@ -87,7 +90,8 @@ def _run_timed(cfg, band_rows=None, list_budget=None, separate=False, lists="aut
     elif separate:
         assert not ts.fused_raster and not ts.fused_adam and ts.sparse_grad and ts._use_state
     else:
-        assert b.lists_without_count() and b.path == "binned" and ts.fused_raster and ts._use_state
+        assert b.lists_without_count() and b.path == (lists if lists != "auto" else "binned")
+        assert ts.fused_raster and ts._use_state
     out = {"image": PY.np_(b.image), "T_final": PY.np_(b.T_final), "n_contrib": PY.np_(b.n_contrib),
            "dL": PY.np_(b.dL), "loss": float(b.loss.item()),
            "grad2d": PY.np_(b.grad2d).reshape(b.V, b.n, 9).copy(),
@@ -122,8 +126,8 @@ DEGENERATE = {
 }
 
 
-@pytest.fixture(scope="module", params=["ragged", "ragged-bands", "ragged-budget", "ragged-separate", "headline"]
-                + list(DEGENERATE))
+@pytest.fixture(scope="module", params=["ragged", "ragged-bands", "ragged-budget", "ragged-separate", "ragged-compact",
+                                        "headline"] + list(DEGENERATE))
 def timed(request):
     import torch
     assert torch.cuda.is_available()
@@ -139,6 +143,10 @@ def timed(request):
         # the separate forward + L1 and backward passes, and the separate
         # backward (sparse gradient) and Adam (visible set, state flags)
         r = _run_timed(S.RAGGED, separate=True)
+    elif request.param == "ragged-compact":
+        # binning only the Gaussians each view sees, the grid sized for them
+        # (the builder the step picks when most (view, Gaussian) pairs are culled)
+        r = _run_timed(S.RAGGED, lists="compact")
     elif request.param == "ragged-budget":
         # the lists and their workspace under 26 MB (38.7 MB for the whole
         # image): windows planned from the per-row counts
