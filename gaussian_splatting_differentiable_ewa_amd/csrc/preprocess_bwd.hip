@@ -40,14 +40,19 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(float* __restrict__ P, i
     constexpr int ROWS = 11 + 3 * NB;
     const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (g >= n) return;
-    if (ADAM && skip && *skip != 0) return;  // the step's lists overflowed: no update
     if (ADAM && state) {
+        // the skip flag, the rectangles and the state flag are requested
+        // together: most waves of a large scene mostly outside the views end
+        // here, after one round trip instead of three
+        const int32_t sk = skip ? *skip : 0;
+        const uint32_t st = state[g];
         bool seen = false;  // visible in some view
         for (int v = 0; v < cams.n_views; ++v) {
             const uint2 rr = *(const uint2*)(rect + 4 * ((int64_t)v * n + g));
             seen = seen || ((rr.y & 0xffffu) > (rr.x & 0xffffu) && (rr.y >> 16) > (rr.x >> 16));
         }
-        if (!seen && state[g] == 0) {
+        if (sk != 0) return;  // the step's lists overflowed: no update
+        if (!seen && st == 0) {
             if (out) {
 #pragma unroll
                 for (int r = 0; r < ROWS; ++r) out[(int64_t)r * n + g] = 0.f;
@@ -55,6 +60,8 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(float* __restrict__ P, i
             return;
         }
         if (seen) state[g] = 1;
+    } else if (ADAM && skip && *skip != 0) {
+        return;  // the step's lists overflowed: no update
     }
     if (!ADAM && vis_out) {
         // sparse output: a Gaussian culled in every view loads nothing and
