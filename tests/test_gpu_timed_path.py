@@ -19,7 +19,9 @@ element, through the C ABI:
     Gaussians each view sees (gs_window_gaussians, the binning grid sized for
     them);
   * on degenerate scenes (DEGENERATE below): no Gaussian in front of the
-    camera, sixteen views (SH 1), a 17x3 image (SH 2), a single Gaussian.
+    camera (also with the lists from the seen sets), sixteen views (SH 1), a
+    17x3 image (SH 2), a single Gaussian, and two views of which one sees
+    nothing (lists from the seen sets: one set empty).
 
 Two steps run: the first reads the intersection count on the host, the second
 (the form the benchmark times) does not. The second is compared with the
@@ -123,18 +125,26 @@ DEGENERATE = {
                             -3.5, 0.4, 17, 3, 20.0),
     "single": S.SceneConfig("single-1-sh3-32x32", 26, 27, 1, 3, (-0.1, -0.1, 2.0), (0.1, 0.1, 2.5), 0, 0.0,
                             -1.5, 0.1, 32, 32, 32.0),
+    # two views from the origin, the second turned away from every Gaussian:
+    # its set of seen Gaussians is empty (lists from the seen sets)
+    "one-view-empty": S.SceneConfig("oneempty-4k-sh3-2x64x48", 28, 29, 4000, 3, (-1.0, -1.0, 3.0), (1.0, 1.0, 6.0),
+                                    4, 0.3, -3.5, 0.4, 64, 48, 64.0, yaws=(0.0, 180.0)),
 }
+# the list builder per degenerate scene (the binned lists of the timed path,
+# or those from the sets each view sees)
+DEGENERATE_LISTS = {"one-view-empty": "compact", "culled-compact": "compact"}
 
 
 @pytest.fixture(scope="module", params=["ragged", "ragged-bands", "ragged-budget", "ragged-separate", "ragged-compact",
-                                        "headline"] + list(DEGENERATE))
+                                        "headline", "culled-compact"] + list(DEGENERATE))
 def timed(request):
     import torch
     assert torch.cuda.is_available()
-    if request.param in DEGENERATE:
+    if request.param in DEGENERATE or request.param == "culled-compact":
         # the binned lists as on the timed path, whatever the intersection count
-        r = _run_timed(DEGENERATE[request.param], lists="binned")
-        if request.param == "culled":
+        cfg = DEGENERATE[request.param.replace("-compact", "")]
+        r = _run_timed(cfg, lists=DEGENERATE_LISTS.get(request.param, "binned"))
+        if request.param.startswith("culled"):
             assert r["K"] == 0
             assert not r["gpu"]["state"].any()
     elif request.param == "headline":
