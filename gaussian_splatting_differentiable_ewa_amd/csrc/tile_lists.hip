@@ -24,10 +24,17 @@
 //                     tile are skipped), in LDS for up to 4096 entries and
 //                     through a global scratch copy beyond; k_tl_ranges lists
 //                     its tiles by length class and it takes the longest
-//                     first; then runs of equal depth put in id order.
+//                     first; then runs of equal depth put in id order
+//                     (runs longer than TIE_RUN: the whole 64-bit key sorted).
 // (depth, id) is a total order, so the arbitrary slot order of step 4 never
 // shows: the lists equal those of the global key sort. The positive fp32
 // depths order like their bit patterns.
+//
+// Steps 1 and 4 may take, per view, a set of Gaussians instead of all n (the
+// output of gs_window_gaussians: those meeting a window of tile rows, or
+// every Gaussian the view sees). With the set's expected size, the grid of
+// chunks is sized for the set and its tile rows split into more bands (see
+// bin_grid).
 //
 // With a mask output, each sort kernel also writes every entry's 16-bit
 // sub-block mask (gs_tile_masks' test, tile_mask16 in raster_common.h) as it
