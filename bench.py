@@ -123,6 +123,10 @@ def parse():
                     help="keep the Gaussians in the generated (random) order instead of the Morton order of their means")
     ap.add_argument("--separate-raster", action="store_true",
                     help="forward + loss and backward raster as two passes instead of the fused one")
+    ap.add_argument("--separate-backward", choices=["visible", "compact", "dense"], default=None,
+                    help="the preprocess backward and Adam as two calls instead of the fused pass: the gradient "
+                         "written for the Gaussians seen in the step only (a [P][n] buffer with visibility flags, "
+                         "or their columns stored consecutively), or for every Gaussian")
     ap.add_argument("--band-rows", type=int, default=None,
                     help="memory-capped mode: lists and raster one window of this many tile rows at a time")
     ap.add_argument("--list-budget", type=float, default=None, metavar="MB",
@@ -222,6 +226,15 @@ def impl_bytes(P, n, V, K, Nv, n_any, n_px, n_adam=None):
         "raster_fwd_bwd": 6 * K + 36 * Nv + 12 * V * n_px + 36 * Nv,
         "preprocess_bwd": Bp * n_any + 44 * Nv + Bp * n,
         "adam": 7 * Bp * n,
+        # the separate pair with the gradient of the seen Gaussians only: their
+        # parameters read and gradient columns written (and a visibility byte
+        # per Gaussian); Adam reads those columns and the visibility (the
+        # flags, or every rectangle) and updates the n_adam Gaussians; the
+        # compact form's list of seen Gaussians (rectangles read twice)
+        "preprocess_bwd_visible": Bp * n_any + 44 * Nv + Bp * n_any + n,
+        "adam_visible": n + Bp * n_any + 6 * Bp * n_adam,
+        "preprocess_bwd_compact": 2 * 8 * V * n + 4 * n_any + Bp * n_any + 44 * Nv + Bp * n_any,
+        "adam_compact": 8 * V * n + 4 * n_any + Bp * n_any + 6 * Bp * n_adam,
         # the two above in one pass: every (view, Gaussian) rectangle and each
         # visible pair's 2D gradient read, the gradient never stored; for each
         # Gaussian updated, parameters and moments read once, parameters and
@@ -271,7 +284,10 @@ def main():
     ts = TrainStep(params.clone(), cfg.sh_degree, cams, target, lr=cfg.lr, betas=(cfg.beta1, cfg.beta2),
                    eps=cfg.eps, band_rows=args.band_rows, fused_raster=not args.separate_raster, lists=args.lists,
                    state_flags=not args.no_state_flags,
-                   list_budget=int(args.list_budget * 1e6) if args.list_budget else None)
+                   list_budget=int(args.list_budget * 1e6) if args.list_budget else None,
+                   fused_adam=args.separate_backward is None,
+                   sparse_grad={"visible": True, "compact": "compact", "dense": False}.get(args.separate_backward,
+                                                                                         False))
     print(f"[bench] {cfg.name}: inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     b = ts.buf
@@ -319,7 +335,7 @@ def main():
     K = sum(K_v)
     # with the state flags on, the fused backward + Adam touches only the
     # Gaussians whose moments are not known to be zero (those seen so far)
-    n_adam = int((ts.adam_state != 0).sum()) if ts.fused_adam and ts._use_state else b.n
+    n_adam = int((ts.adam_state != 0).sum()) if (ts.fused_adam or ts.sparse_grad) and ts._use_state else b.n
     mb = method_bytes(b.P, b.n, K_v, n_vis, n_any, n_px)
     step_bytes = sum(mb.values())
     frac_step = step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9)
@@ -332,8 +348,13 @@ def main():
     else:
         used += ["emit", "sort", "ranges", "tile_masks"]
     used += ["raster_fwd_bwd"] if ts.fused_raster else ["raster_fwd_loss", "raster_bwd"]
+    sep = {None: "", "visible": "_visible", "compact": "_compact", "dense": ""}[args.separate_backward]
+    # a stage's impl term under the stage's own name (the separate backward's
+    # sparse forms have their own byte counts)
+    stage_term = {"preprocess_bwd": "preprocess_bwd" + sep, "adam": "adam" + sep}
     used += ["preprocess_bwd_adam"] if ts.fused_adam else ["preprocess_bwd", "adam"]
-    impl_terms = {k: int(ib[k]) for k in used}
+    impl_terms = {k: int(ib[stage_term.get(k, k)]) for k in used}
+    ib = {k: ib[stage_term.get(k, k)] for k in ib}
     impl_total = sum(impl_terms.values())
 
     # dominant kernel: the single-kernel stage with the largest time
@@ -341,6 +362,10 @@ def main():
     single = {"raster_fwd_loss": "k_raster_fwd_l1", "raster_bwd": "k_raster_bwd", "adam": "k_adam",
               "preprocess_bwd": "k_preprocess_bwd", "preprocess_bwd_adam": "k_preprocess_bwd",
               "raster_fwd_bwd": "k_raster_fwd_bwd_l1"}
+    if args.separate_backward == "visible":
+        single["adam"] = "k_adam_visible"
+    elif args.separate_backward == "compact":
+        del single["adam"], single["preprocess_bwd"]  # two kernels each (the seen list; listed and unlisted)
     single = {k: v for k, v in single.items() if k in stage_ms}
     dom = max(single, key=lambda k: stage_ms[k])
     kern = single[dom]
@@ -396,6 +421,8 @@ def main():
         "list_builder": b.path, "band_rows": args.band_rows, "list_budget_mb": args.list_budget,
         "windows": [list(w) for w in ts.windows] if ts.windowed else None,
         "raster": "separate" if args.separate_raster else "fused",
+        "backward": args.separate_backward or "fused",
+        "grad_buffer_bytes": int(ts.grad.numel() * 4) if ts.grad is not None else 0,
         "gaussian_order": "generated" if args.generated_order else "morton",
         "adam_state_flags": bool(ts._use_state), "camera_turn_deg_per_step": args.moving_camera,
         "host_count_read": not ts.defer_count or not b.lists_without_count(), "redone_steps": redone,

@@ -37,6 +37,7 @@ EXPORTS = (
     "gs_raster_exp", "gs_stream_copy",
     "gs_rasterize_fwd_bwd_l1_noalloc", "gs_rasterize_fwd_bwd_l1_noalloc_max_bytes",
     "gs_window_gaussians", "gs_window_gaussians_workspace_bytes", "gs_adam_step_visible",
+    "gs_seen_gaussians", "gs_seen_gaussians_workspace_bytes", "gs_preprocess_bwd_compact", "gs_adam_step_compact",
 )
 
 
@@ -101,6 +102,11 @@ def lib():
             "gs_preprocess_bwd": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _P], ctypes.c_int),
             "gs_adam_step_visible": ([_P, _P, _P, _P, _I64, _I32, _P, _P, _F64, _F64, _F64, _F64, _I64, _P, _P],
                                      ctypes.c_int),
+            "gs_seen_gaussians_workspace_bytes": ([_I64], _SZ),
+            "gs_seen_gaussians": ([_P, _I64, _I32, _P, _P, _P, _SZ, _P], ctypes.c_int),
+            "gs_preprocess_bwd_compact": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _I64, _P, _P, _P], ctypes.c_int),
+            "gs_adam_step_compact": ([_P, _P, _I64, _P, _P, _P, _P, _I64, _I32, _P, _I32, _P, _F64, _F64, _F64, _F64,
+                                      _I64, _P, _P], ctypes.c_int),
             "gs_adam_step": ([_P, _P, _P, _P, _I64, _F64, _F64, _F64, _F64, _I64, _P], ctypes.c_int),
             "gs_adam_step_unless": ([_P, _P, _P, _P, _I64, _F64, _F64, _F64, _F64, _I64, _P, _P], ctypes.c_int),
             "gs_preprocess_bwd_adam": ([_P, _I64, _I32, _P, _I32, _P, _P, _P, _P, _F64, _F64, _F64, _F64, _I64, _P,
@@ -351,6 +357,29 @@ def gs_adam_step_visible(params, grad, m, v, n, rows, visible, lr, beta1, beta2,
     _check(lib().gs_adam_step_visible(_ptr(params), _ptr(grad), _ptr(m), _ptr(v), n, rows, _ptr(visible),
                                       _ptr(state), lr, beta1, beta2, eps, step, _ptr(skip), _stream(stream)),
            "gs_adam_step_visible")
+
+
+def seen_gaussians_workspace_bytes(n: int) -> int:
+    return lib().gs_seen_gaussians_workspace_bytes(n)
+
+
+def gs_seen_gaussians(rect, n, n_views, gauss, count, ws, stream=None):
+    _check(lib().gs_seen_gaussians(_ptr(rect), n, n_views, _ptr(gauss), _ptr(count), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)), "gs_seen_gaussians")
+
+
+def gs_preprocess_bwd_compact(params, n, sh_degree, cams, rect, grad2d, gauss, count, stride, grad_compact, overflow,
+                              stream=None):
+    _check(lib().gs_preprocess_bwd_compact(_ptr(params), n, sh_degree, cameras(cams), len(cams), _ptr(rect),
+                                           _ptr(grad2d), _ptr(gauss), _ptr(count), stride, _ptr(grad_compact),
+                                           _ptr(overflow), _stream(stream)), "gs_preprocess_bwd_compact")
+
+
+def gs_adam_step_compact(params, grad_compact, stride, gauss, count, m, v, n, rows, rect, n_views, lr, beta1, beta2,
+                         eps, step, state=None, skip=None, stream=None):
+    _check(lib().gs_adam_step_compact(_ptr(params), _ptr(grad_compact), stride, _ptr(gauss), _ptr(count), _ptr(m),
+                                      _ptr(v), n, rows, _ptr(rect), n_views, _ptr(state), lr, beta1, beta2, eps, step,
+                                      _ptr(skip), _stream(stream)), "gs_adam_step_compact")
 
 
 def gs_adam_step(params, grad, m, v, count, lr, beta1, beta2, eps, step, stream=None):

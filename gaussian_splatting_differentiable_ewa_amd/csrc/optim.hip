@@ -9,6 +9,8 @@
 // training architecture and memory scaling").
 #include <math.h>
 
+#include <algorithm>
+
 #include "adam.h"
 #include "internal.h"
 
@@ -123,6 +125,83 @@ __global__ __launch_bounds__(EW_THREADS) void k_adam_visible(float* __restrict__
     }
 }
 
+// Adam from a compact gradient: k_adam_listed updates the Gaussians of the
+// list (list[j] with its gradient in column j of grad, rows `stride` apart;
+// j < min(*count, stride)), AL_ROWS rows of one Gaussian per thread, the grid's
+// y dimension over the row groups (more independent loads in flight than one
+// thread walking all rows: city block 1.14 -> 1.09 ms); k_adam_unlisted applies
+// the update of a zero gradient to every other Gaussian (one that no view
+// sees: the list holds exactly those some view sees), or, with state flags,
+// only to those whose moments may be non-zero. Same arithmetic as k_adam, so
+// the same bits as the dense update of the dense gradient.
+constexpr int AL_ROWS = 4;
+constexpr int AL_MAX_ROWS = 65535 * AL_ROWS;  // the grid's y dimension
+
+__global__ __launch_bounds__(EW_THREADS) void k_adam_listed(float* __restrict__ params, const float* __restrict__ grad,
+                                                            int64_t stride, const uint32_t* __restrict__ list,
+                                                            const uint32_t* __restrict__ count,
+                                                            float* __restrict__ m, float* __restrict__ v, int64_t n,
+                                                            int32_t P, uint8_t* __restrict__ state,
+                                                            const AdamConsts c, const int32_t* __restrict__ skip)
+{
+    const int64_t j = (int64_t)blockIdx.x * EW_THREADS + threadIdx.x;
+    if (j >= stride || j >= (int64_t)*count) return;
+    if (skip && *skip != 0) return;  // the step's lists overflowed: no update
+    const int64_t g = (int64_t)list[j];
+    if (g >= n) return;
+    const int r0 = (int)blockIdx.y * AL_ROWS;
+    if (state && r0 == 0) state[g] = 1;
+    float pp[AL_ROWS], mm[AL_ROWS], vv[AL_ROWS], gg[AL_ROWS];
+#pragma unroll
+    for (int k = 0; k < AL_ROWS; ++k) {
+        const int r = r0 + k;
+        if (r < P) {
+            const int64_t e = (int64_t)r * n + g;
+            pp[k] = params[e];
+            mm[k] = m[e];
+            vv[k] = v[e];
+            gg[k] = grad[(int64_t)r * stride + j];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < AL_ROWS; ++k) {
+        const int r = r0 + k;
+        if (r < P) {
+            const int64_t e = (int64_t)r * n + g;
+            adam1(pp[k], gg[k], mm[k], vv[k], c);
+            params[e] = pp[k];
+            m[e] = mm[k];
+            v[e] = vv[k];
+        }
+    }
+}
+
+__global__ __launch_bounds__(EW_THREADS) void k_adam_unlisted(float* __restrict__ params, float* __restrict__ m,
+                                                              float* __restrict__ v, int64_t n, int32_t P,
+                                                              const uint16_t* __restrict__ rect, int32_t n_views,
+                                                              const uint8_t* __restrict__ state, const AdamConsts c,
+                                                              const int32_t* __restrict__ skip)
+{
+    const int64_t g = (int64_t)blockIdx.x * EW_THREADS + threadIdx.x;
+    if (g >= n) return;
+    const int32_t sk = skip ? *skip : 0;
+    const uint32_t st = state ? state[g] : 1u;
+    bool seen = false;
+    for (int vw = 0; vw < n_views; ++vw) {
+        const uint2 rr = *(const uint2*)(rect + 4 * ((int64_t)vw * n + g));
+        seen = seen || ((rr.y & 0xffffu) > (rr.x & 0xffffu) && (rr.y >> 16) > (rr.x >> 16));
+    }
+    if (sk != 0 || seen || st == 0u) return;  // no update, a listed Gaussian, or moments known zero
+    for (int r = 0; r < P; ++r) {
+        const int64_t e = (int64_t)r * n + g;
+        float pp = params[e], mm = m[e], vv = v[e];
+        adam1(pp, 0.f, mm, vv, c);
+        params[e] = pp;
+        m[e] = mm;
+        v[e] = vv;
+    }
+}
+
 // Enough blocks to fill the chip several times over; each thread then walks
 // its grid-stride range. The loss uses fewer blocks: each block ends with one
 // fp64 atomic on the same address.
@@ -187,6 +266,32 @@ gs_status gs_adam_step_visible(float* params, const float* grad, float* m, float
     if (n == 0) return GS_OK;
     hipLaunchKernelGGL(k_adam_visible, dim3((unsigned)((n + EW_THREADS - 1) / EW_THREADS)), dim3(EW_THREADS), 0,
                        (hipStream_t)stream, params, grad, m, v, n, rows, visible, state, c, skip);
+    return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
+}
+
+gs_status gs_adam_step_compact(float* params, const float* grad_compact, int64_t stride, const uint32_t* list,
+                               const uint32_t* count, float* m, float* v, int64_t n, int32_t rows,
+                               const uint16_t* rect, int32_t n_views, uint8_t* state, double lr, double beta1,
+                               double beta2, double eps, int64_t step, const int32_t* skip, void* stream)
+{
+    if (n < 0 || rows < 1 || rows > AL_MAX_ROWS || step < 1 || stride < 1 || n_views < 1 || n_views > GS_MAX_VIEWS)
+        return GS_ERR_INVALID_ARGUMENT;
+    if (!list || !count || !grad_compact) return GS_ERR_INVALID_ARGUMENT;
+    if (n > 0 && (!params || !m || !v || !rect)) return GS_ERR_INVALID_ARGUMENT;
+    if (n > ((int64_t)1 << 31) || stride > ((int64_t)1 << 31)) return GS_ERR_INVALID_ARGUMENT;
+    AdamConsts c;
+    if (!adam_consts(lr, beta1, beta2, eps, step, c)) return GS_ERR_INVALID_ARGUMENT;
+    if (state && !(eps > 0.0)) return GS_ERR_INVALID_ARGUMENT;  // with eps = 0 the skipped update is 0/0, not the identity
+    if (n == 0) return GS_OK;
+    hipStream_t s = (hipStream_t)stream;
+    // the unlisted first: it reads the state flags before the listed pass sets them
+    hipLaunchKernelGGL(k_adam_unlisted, dim3((unsigned)((n + EW_THREADS - 1) / EW_THREADS)), dim3(EW_THREADS), 0, s,
+                       params, m, v, n, rows, rect, n_views, state, c, skip);
+    if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
+    const int64_t lj = std::min<int64_t>(n, stride);
+    const dim3 lgrid((unsigned)((lj + EW_THREADS - 1) / EW_THREADS), (unsigned)((rows + AL_ROWS - 1) / AL_ROWS));
+    hipLaunchKernelGGL(k_adam_listed, lgrid, dim3(EW_THREADS), 0, s,
+                       params, grad_compact, stride, list, count, m, v, n, rows, state, c, skip);
     return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
 }
 

@@ -17,20 +17,29 @@
 // with g = m = v = 0 Adam leaves theta, m and v as they are (eps > 0), so
 // only Gaussians seen at least once cost moment traffic.
 #include "adam.h"
+#include <algorithm>
+
 #include "internal.h"
 #include "project.h"
 
 namespace gs {
 
 // P is written only with ADAM (each thread its own Gaussian's elements,
-// after reading them); out may then be null.
+// after reading them); out may then be null. With a list (compact output,
+// not with ADAM): thread j takes Gaussian list[j] for j < *count and writes
+// its gradient to column j of out, rows ostride apart (j < ostride; a list
+// longer than ostride sets *overflow, never clears it, and writes nothing
+// past it).
 template <int DEG, bool ADAM>
 __global__ __launch_bounds__(256) void k_preprocess_bwd(float* __restrict__ P, int64_t n, const DevCameras cams,
                                                         const ShConsts K, const uint16_t* __restrict__ rect,
                                                         const float* __restrict__ grad2d, float* __restrict__ out,
                                                         float* __restrict__ m, float* __restrict__ v,
                                                         const AdamConsts ac, const int32_t* __restrict__ skip,
-                                                        uint8_t* __restrict__ state, uint8_t* __restrict__ vis_out)
+                                                        uint8_t* __restrict__ state, uint8_t* __restrict__ vis_out,
+                                                        const uint32_t* __restrict__ list,
+                                                        const uint32_t* __restrict__ count, int64_t ostride,
+                                                        int32_t* __restrict__ overflow)
 {
     // no contraction: the arithmetic is the written one in both forms of the
     // kernel, so the gradient the fused update applies is the one
@@ -38,7 +47,16 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(float* __restrict__ P, i
 #pragma clang fp contract(off)
     constexpr int NB = (DEG + 1) * (DEG + 1);
     constexpr int ROWS = 11 + 3 * NB;
-    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    int64_t g = tid, col = tid, cstride = n;  // the Gaussian, and where its gradient goes
+    if (!ADAM && list) {
+        const int64_t cnt = (int64_t)*count;
+        if (tid == 0 && cnt > ostride) *overflow = 1;
+        if (tid >= cnt || tid >= ostride) return;
+        g = (int64_t)list[tid];
+        if (g >= n) return;  // not a Gaussian (a list the caller never filled)
+        cstride = ostride;
+    }
     if (g >= n) return;
     if (ADAM && state) {
         // the skip flag, the rectangles and the state flag are requested
@@ -276,7 +294,7 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(float* __restrict__ P, i
     }
     if (!ADAM || out) {
 #pragma unroll
-        for (int r = 0; r < ROWS; ++r) out[(int64_t)r * n + g] = G[r];
+        for (int r = 0; r < ROWS; ++r) out[(int64_t)r * cstride + col] = G[r];
     }
     if (ADAM) {
         // the parameters still in registers (position, SH) are not read
@@ -317,15 +335,19 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(float* __restrict__ P, i
 template <bool ADAM>
 static gs_status pbwd_launch(float* params, int64_t n, int32_t sh_degree, const DevCameras& dc,
                              const uint16_t* rect, const float* grad2d, float* out, float* m, float* v,
-                             const AdamConsts& c, const int32_t* skip, uint8_t* state, uint8_t* vis_out, hipStream_t s)
+                             const AdamConsts& c, const int32_t* skip, uint8_t* state, uint8_t* vis_out, hipStream_t s,
+                             const uint32_t* list = nullptr, const uint32_t* count = nullptr, int64_t ostride = 0,
+                             int32_t* overflow = nullptr)
 {
-    const dim3 grid(grid_for((uint64_t)n, 256)), block(256);
+    // with a list, one thread per possible list entry: at most min(n, ostride)
+    const int64_t threads = list ? std::min<int64_t>(n, ostride) : n;
+    const dim3 grid(grid_for((uint64_t)std::max<int64_t>(threads, 1), 256)), block(256);
     const ShConsts K = sh_constants();
     switch (sh_degree) {
-        case 0: hipLaunchKernelGGL((k_preprocess_bwd<0, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip, state, vis_out); break;
-        case 1: hipLaunchKernelGGL((k_preprocess_bwd<1, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip, state, vis_out); break;
-        case 2: hipLaunchKernelGGL((k_preprocess_bwd<2, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip, state, vis_out); break;
-        default: hipLaunchKernelGGL((k_preprocess_bwd<3, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip, state, vis_out); break;
+        case 0: hipLaunchKernelGGL((k_preprocess_bwd<0, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip, state, vis_out, list, count, ostride, overflow); break;
+        case 1: hipLaunchKernelGGL((k_preprocess_bwd<1, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip, state, vis_out, list, count, ostride, overflow); break;
+        case 2: hipLaunchKernelGGL((k_preprocess_bwd<2, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip, state, vis_out, list, count, ostride, overflow); break;
+        default: hipLaunchKernelGGL((k_preprocess_bwd<3, ADAM>), grid, block, 0, s, params, n, dc, K, rect, grad2d, out, m, v, c, skip, state, vis_out, list, count, ostride, overflow); break;
     }
     return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
 }
@@ -348,6 +370,23 @@ gs_status gs_preprocess_bwd(const float* params, int64_t n, int32_t sh_degree, c
     if (n == 0) return GS_OK;
     return pbwd_launch<false>((float*)params, n, sh_degree, dc, rect, grad2d, grad_params, nullptr, nullptr,
                               AdamConsts{}, nullptr, nullptr, visible, (hipStream_t)stream);
+}
+
+gs_status gs_preprocess_bwd_compact(const float* params, int64_t n, int32_t sh_degree, const gs_camera* cams,
+                                    int32_t n_views, const uint16_t* rect, const float* grad2d,
+                                    const uint32_t* list, const uint32_t* count, int64_t stride,
+                                    float* grad_compact, int32_t* overflow, void* stream)
+{
+    if (n < 0 || sh_degree < 0 || sh_degree > 3 || stride < 1) return GS_ERR_INVALID_ARGUMENT;
+    if (!list || !count || !grad_compact || !overflow) return GS_ERR_INVALID_ARGUMENT;
+    if (n > 0 && (!params || !rect || !grad2d)) return GS_ERR_INVALID_ARGUMENT;
+    if (n > ((int64_t)1 << 31) || stride > ((int64_t)1 << 31)) return GS_ERR_INVALID_ARGUMENT;
+    DevCameras dc;
+    if (!make_dev_cameras(cams, n_views, dc)) return GS_ERR_INVALID_ARGUMENT;
+    if (n == 0) return GS_OK;
+    return pbwd_launch<false>((float*)params, n, sh_degree, dc, rect, grad2d, grad_compact, nullptr, nullptr,
+                              AdamConsts{}, nullptr, nullptr, nullptr, (hipStream_t)stream, list, count, stride,
+                              overflow);
 }
 
 gs_status gs_preprocess_bwd_adam(float* params, int64_t n, int32_t sh_degree, const gs_camera* cams,

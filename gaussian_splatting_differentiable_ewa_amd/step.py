@@ -309,7 +309,7 @@ class TrainStep:
                  m: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None, defer_count: bool = True,
                  fused_adam: bool = True, write_image: bool = False, band_rows: Optional[int] = None,
                  fused_raster: bool = True, lists: str = "auto", state_flags: bool = True,
-                 list_budget: Optional[int] = None, sparse_grad: bool = True):
+                 list_budget: Optional[int] = None, sparse_grad=True):
         assert params.is_cuda and params.dtype == torch.float32 and params.is_contiguous()
         self.params = params
         self.sh_degree = sh_degree
@@ -327,12 +327,28 @@ class TrainStep:
         # sees (its update is the identity when eps > 0) without reading it;
         # in a spatial storage order whole waves of such Gaussians skip
         self._use_state = state_flags and eps > 0
-        self.grad = None if fused_adam else torch.empty_like(params)
         # the separate backward and Adam: gradients written and read only for
-        # Gaussians visible in some view (a flag per Gaussian), or dense
-        self.sparse_grad = sparse_grad and not fused_adam
+        # Gaussians visible in some view (a flag per Gaussian, the gradient
+        # buffer [P][n]), or "compact": only their columns, stored
+        # consecutively in a buffer sized for the Gaussians seen (planned from
+        # a host read of their number at the first step, and again after a
+        # step whose gradients did not fit: that step sets the sticky flag and
+        # is redone), or dense
+        if sparse_grad not in (True, False, "compact"):
+            raise ValueError("sparse_grad must be True, False or 'compact'")
+        self.sparse_grad = sparse_grad if not fused_adam else False
+        self.compact_grad = self.sparse_grad == "compact"
+        self.grad = None if fused_adam or self.compact_grad else torch.empty_like(params)
         self.visible = (torch.zeros(params.shape[1], dtype=torch.uint8, device=params.device)
-                        if self.sparse_grad else None)
+                        if self.sparse_grad is True else None)
+        if self.compact_grad:
+            n_g = params.shape[1]
+            self.seen_list = torch.empty(max(1, n_g), dtype=torch.int32, device=params.device)
+            self.seen_count = torch.zeros(1, dtype=torch.int32, device=params.device)
+            self.seen_ws = torch.empty(max(1, L.seen_gaussians_workspace_bytes(n_g)), dtype=torch.uint8,
+                                       device=params.device)
+            self.grad_ovf = torch.zeros(1, dtype=torch.int32, device=params.device)
+        self.grad_stride = 0  # columns of the compact gradient (0: plan at the next step)
         self.lr, self.betas, self.eps, self.bg = lr, betas, eps, bg
         self.t = 0
         self.defer_count = defer_count
@@ -477,6 +493,29 @@ class TrainStep:
                                b.dL, b.grad2d, accumulate=True, row0=row0, rows=rows)
         mark(2)
 
+    def _compact_backward(self, skip, deferred, mark, m0):
+        """The separate backward into the compact gradient, then Adam from it.
+        A deferred step does not read the number of Gaussians seen (except to
+        plan): a list longer than the buffer sets the sticky flag, and the
+        step is redone. Otherwise the number is read and the buffer grown."""
+        b = self.buf
+        L.gs_seen_gaussians(b.rect, b.n, b.V, self.seen_list, self.seen_count, self.seen_ws)
+        plan = self.grad_stride == 0
+        if plan or not deferred:
+            seen = int(self.seen_count.item())
+            if plan or seen > self.grad_stride:
+                # room for the Gaussians seen and some more (a moving view)
+                self.grad_stride = max(1, min(b.n, int(1.25 * seen) + 4096))
+                self.grad = None
+                self.grad = torch.empty((b.P, self.grad_stride), dtype=torch.float32, device=b.device)
+        L.gs_preprocess_bwd_compact(self.params, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, self.seen_list,
+                                    self.seen_count, self.grad_stride, self.grad,
+                                    self.sticky if deferred else self.grad_ovf)
+        mark(m0)
+        L.gs_adam_step_compact(self.params, self.grad, self.grad_stride, self.seen_list, self.seen_count, self.m,
+                               self.v, b.n, b.P, b.rect, b.V, self.lr, self.betas[0], self.betas[1], self.eps, self.t,
+                               state=self.adam_state if self._use_state else None, skip=skip)
+
     def list_bytes(self) -> int:
         """Bytes of the intersection lists and their workspaces (in the
         memory-capped mode also the window's Gaussian set)."""
@@ -526,6 +565,8 @@ class TrainStep:
             L.gs_preprocess_bwd_adam(self.params, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, self.m, self.v, self.lr,
                                      self.betas[0], self.betas[1], self.eps, self.t, skip=skip,
                                      state=self.adam_state if self._use_state else None)
+        elif self.compact_grad:
+            self._compact_backward(skip, deferred, mark, m0)
         else:
             L.gs_preprocess_bwd(self.params, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, self.grad,
                                 visible=self.visible)
@@ -594,5 +635,6 @@ class TrainStep:
                     self.windows = None  # a new plan (and list buffers) at the next step
                 else:
                     b.ensure_capacity(b.K, slack=1.5)
+                self.grad_stride = 0  # the compact gradient too
                 self.t = t - 1
                 return

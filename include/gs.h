@@ -288,6 +288,25 @@ gs_status gs_window_gaussians(const uint16_t* rect, int64_t n, int32_t n_views, 
                               int32_t rows, uint32_t* gauss, uint32_t* gauss_off, void* ws, size_t ws_bytes,
                               void* stream);
 
+/* Workspace of gs_seen_gaussians (bytes); 0 on n < 0. */
+size_t gs_seen_gaussians_workspace_bytes(int64_t n);
+
+/*
+ * gs_seen_gaussians -- the Gaussians that some view sees (a non-empty
+ * rectangle in some view of gs_preprocess's rect), in index order: the set
+ * whose gradients gs_preprocess_bwd_compact writes and gs_adam_step_compact
+ * reads (the gradients of the visible Gaussians compacted, the single-GPU half
+ * of sending only non-zero gradients: ByteSplat abstract).
+ *   rect, n, n_views  as for gs_preprocess_bwd
+ *   list   device out [n] uint32: the Gaussians, list[0 .. *count)
+ *   count  device out uint32: their number
+ *   ws     device workspace of gs_seen_gaussians_workspace_bytes(n)
+ * Errors: null pointers, n < 0 or n > 2^31, n_views outside [1, 16], a small
+ * workspace.
+ */
+gs_status gs_seen_gaussians(const uint16_t* rect, int64_t n, int32_t n_views, uint32_t* list, uint32_t* count,
+                            void* ws, size_t ws_bytes, void* stream);
+
 /*
  * gs_tile_ranges -- for every (view, tile) id t = key >> 32, the range
  * [start, end) of its keys in the sorted list; (0, 0) when it has none.
@@ -562,6 +581,49 @@ gs_status gs_adam_step(float* params, const float* grad, float* m, float* v, int
 gs_status gs_adam_step_visible(float* params, const float* grad, float* m, float* v, int64_t n, int32_t rows,
                                const uint8_t* visible, uint8_t* state, double lr, double beta1, double beta2,
                                double eps, int64_t step, const int32_t* skip, void* stream);
+
+/*
+ * gs_preprocess_bwd_compact -- gs_preprocess_bwd for the Gaussians of a list
+ * (gs_seen_gaussians' output) only, their gradients compacted: Gaussian
+ * list[j] (j < *count) gets exactly the gradient gs_preprocess_bwd computes
+ * for it, in column j of grad_compact ([rows][stride], rows of
+ * gs_param_rows(sh_degree)). The parameter-gradient step of "A Scalable
+ * PyTorch Abstraction for Multi-GPU Gaussian Splatting" (reference [10]) as
+ * for gs_preprocess_bwd; the compaction is the ByteSplat abstract's (only the
+ * non-zero gradients of a step are kept).
+ *   list, count  device: the Gaussians and their number
+ *   stride       columns of grad_compact (> 0): entries j >= stride are not
+ *                written, and *overflow is set when *count > stride
+ *   overflow     device int32: set to 1 as above, otherwise left as it is (a
+ *                sticky flag: the caller clears it; the skip flag of
+ *                gs_adam_step_compact, e.g. gs_tile_lists' sticky flag, so
+ *                that a step whose gradients did not fit changes nothing)
+ * Errors: as gs_preprocess_bwd, plus stride < 1, null list, count or
+ * overflow.
+ */
+gs_status gs_preprocess_bwd_compact(const float* params, int64_t n, int32_t sh_degree, const gs_camera* cams,
+                                    int32_t n_views, const uint16_t* rect, const float* grad2d,
+                                    const uint32_t* list, const uint32_t* count, int64_t stride,
+                                    float* grad_compact, int32_t* overflow, void* stream);
+
+/*
+ * gs_adam_step_compact -- gs_adam_step over a [rows][n] block from the
+ * compact gradient of gs_preprocess_bwd_compact (same update arithmetic, so
+ * the same bits as gs_adam_step on the dense gradient): Gaussian list[j]
+ * (j < min(*count, stride)) is updated with column j of grad_compact; every
+ * Gaussian that no view sees (rect, n_views: the Gaussians not in the list
+ * when it is gs_seen_gaussians' output for this rect) with g = 0, its moments
+ * decaying as in the dense update. With `state` (as in gs_adam_step_visible)
+ * an unseen Gaussian with state 0 is skipped without reading anything, and a
+ * listed one gets state 1. `skip`: no update at all while non-zero.
+ * Errors: null pointers, n < 0 or n > 2^31, rows outside [1, 262140], stride
+ * < 1, n_views outside [1, 16], step < 1, beta outside [0, 1), eps < 0, state
+ * with eps = 0.
+ */
+gs_status gs_adam_step_compact(float* params, const float* grad_compact, int64_t stride, const uint32_t* list,
+                               const uint32_t* count, float* m, float* v, int64_t n, int32_t rows,
+                               const uint16_t* rect, int32_t n_views, uint8_t* state, double lr, double beta1,
+                               double beta2, double eps, int64_t step, const int32_t* skip, void* stream);
 
 /*
  * gs_adam_step_unless -- gs_adam_step, skipped on the device when *skip is

@@ -136,6 +136,16 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert wg(fake, 1000, 2, 256, 0, 16, fake, fake, fake, wws - 4, None) == INV
     assert wg(fake, -1, 2, 256, 0, 16, fake, fake, fake, wws, None) == INV
     assert wg(fake, 1000, 0, 256, 0, 16, fake, fake, fake, wws, None) == INV
+    # gs_seen_gaussians
+    sws = L.seen_gaussians_workspace_bytes(1000)
+    assert sws > 0 and L.seen_gaussians_workspace_bytes(-1) == 0
+    sg = lib.gs_seen_gaussians
+    assert sg(fake, 1000, 2, fake, fake, fake, sws - 4, None) == INV
+    assert sg(fake, 1000, 2, fake, None, fake, sws, None) == INV
+    assert sg(fake, 1000, 2, None, fake, fake, sws, None) == INV
+    assert sg(fake, -1, 2, fake, fake, fake, sws, None) == INV
+    assert sg(fake, 1000, 17, fake, fake, fake, sws, None) == INV
+    assert sg(fake, (1 << 31) + 1, 1, fake, fake, fake, 1 << 40, None) == INV
     # gs_tile_ranges
     assert lib.gs_tile_ranges(fake, 10, -1, fake, None) == INV
     assert lib.gs_tile_ranges(None, 10, 4, fake, None) == INV
@@ -249,6 +259,41 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert lib.gs_loss_l1(ctypes.c_void_p(20), fake, 10, 1.0, fake, fake, 0, None) == INV  # misaligned
     assert lib.gs_preprocess_bwd(fake, 10, 5, cams, 1, fake, fake, fake, None, None) == INV
     assert lib.gs_preprocess_bwd(fake, 10, 3, cams, 1, None, fake, fake, None, None) == INV
+    # the compact backward: a list, its count, a stride >= 1 and the overflow flag
+    pc = lib.gs_preprocess_bwd_compact
+    assert pc(fake, 10, 3, cams, 1, fake, fake, fake, fake, 0, fake, fake, None) == INV
+    assert pc(fake, 10, 3, cams, 1, fake, fake, None, fake, 4, fake, fake, None) == INV
+    assert pc(fake, 10, 3, cams, 1, fake, fake, fake, None, 4, fake, fake, None) == INV
+    assert pc(fake, 10, 3, cams, 1, fake, fake, fake, fake, 4, None, fake, None) == INV
+    assert pc(fake, 10, 3, cams, 1, fake, fake, fake, fake, 4, fake, None, None) == INV
+    assert pc(fake, 10, 4, cams, 1, fake, fake, fake, fake, 4, fake, fake, None) == INV
+    assert pc(fake, 10, 3, cams, 0, fake, fake, fake, fake, 4, fake, fake, None) == INV
+    assert pc(fake, 10, 3, cams, 1, None, fake, fake, fake, 4, fake, fake, None) == INV
+    assert pc(fake, -1, 3, cams, 1, fake, fake, fake, fake, 4, fake, fake, None) == INV
+    ac = lib.gs_adam_step_compact
+    ac_names = ["params", "grad", "stride", "list", "count", "m", "v", "n", "rows", "rect", "V", "state", "lr", "b1",
+                "b2", "eps", "step", "skip", "stream"]
+    ac_ok = dict(params=fake, grad=fake, stride=4, list=fake, count=fake, m=fake, v=fake, n=10, rows=59, rect=fake,
+                 V=1, state=None, lr=1e-3, b1=0.9, b2=0.999, eps=1e-15, step=1, skip=None, stream=None)
+
+    def acc(**kw):
+        return _call(ac, ac_names, ac_ok, **kw)
+
+    assert acc(stride=0) == INV
+    assert acc(list=None) == INV
+    assert acc(count=None) == INV
+    assert acc(grad=None) == INV
+    assert acc(rect=None) == INV
+    assert acc(m=None) == INV
+    assert acc(rows=0) == INV
+    assert acc(rows=262141) == INV
+    assert acc(n=-1) == INV
+    assert acc(V=17) == INV
+    assert acc(step=0) == INV
+    assert acc(b2=1.0) == INV
+    assert acc(eps=-1.0) == INV
+    assert acc(state=fake, eps=0.0) == INV
+    assert acc(n=(1 << 31) + 1) == INV
     av = lib.gs_adam_step_visible
     assert av(fake, fake, fake, fake, 10, 59, None, None, 1e-3, 0.9, 0.999, 1e-15, 1, None, None) == INV  # flags
     assert av(fake, fake, fake, fake, 10, 0, fake, None, 1e-3, 0.9, 0.999, 1e-15, 1, None, None) == INV

@@ -192,7 +192,13 @@ def test_adam_state_skip(run):
     (gs_preprocess_bwd with the same visibility) from the state before it.
     The separate path with a sparse gradient (gs_preprocess_bwd writing rows
     only for Gaussians seen in the call, gs_adam_step_visible reading only
-    those) gives the same bits, and leaves the other rows unwritten."""
+    those) gives the same bits, and leaves the other rows unwritten. So does
+    the compact path: gs_seen_gaussians lists exactly the Gaussians seen in
+    the call, gs_preprocess_bwd_compact writes their gradients (the dense
+    gradient's columns, bit for bit) to consecutive columns, and
+    gs_adam_step_compact applies them. A compact buffer narrower than the list
+    sets the overflow flag (which no call clears), still writes the columns
+    that fit, and with that flag as `skip` the update changes nothing."""
     import torch
     from gaussian_splatting_differentiable_ewa_amd import _lib as L
     cfg, b = run["cfg"], run["buf"]
@@ -213,6 +219,13 @@ def test_adam_state_skip(run):
     state = torch.zeros(n, dtype=torch.uint8, device=dev)
     state_sp = torch.zeros(n, dtype=torch.uint8, device=dev)
     visible = torch.zeros(n, dtype=torch.uint8, device=dev)
+    compact = [p0.clone(), torch.zeros_like(p0), torch.zeros_like(p0)]
+    state_c = torch.zeros(n, dtype=torch.uint8, device=dev)
+    glist = torch.full((n,), -1, dtype=torch.int32, device=dev)
+    gcount = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    sws = torch.empty(L.seen_gaussians_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    ovf = torch.zeros(1, dtype=torch.int32, device=dev)
+    stride = n - n // 16  # wider than any call's list (an eighth is never seen), not n
     for step, kp in enumerate(keep, start=1):
         r = rect0.view(b.V, n, 4).clone()
         r[:, torch.from_numpy(~kp).to(dev)] = 0
@@ -228,6 +241,11 @@ def test_adam_state_skip(run):
         g_sp = torch.full_like(p0, float("nan"))
         L.gs_preprocess_bwd(sparse[0], *args, g_sp, visible=visible)
         L.gs_adam_step_visible(sparse[0], g_sp, sparse[1], sparse[2], n, b.P, visible, *hyper, state=state_sp)
+        L.gs_seen_gaussians(b.rect, n, b.V, glist, gcount, sws)
+        g_c = torch.full((b.P, stride), float("nan"), device=dev)
+        L.gs_preprocess_bwd_compact(compact[0], *args, glist, gcount, stride, g_c, ovf)
+        L.gs_adam_step_compact(compact[0], g_c, stride, glist, gcount, compact[1], compact[2], n, b.P, b.rect, b.V,
+                               *hyper, state=state_c)
         torch.cuda.synchronize()
         seen_now = (r.cpu().numpy().view(np.uint16).astype(np.int32)[..., 2]
                     > r.cpu().numpy().view(np.uint16).astype(np.int32)[..., 0]).any(axis=0)
@@ -236,6 +254,14 @@ def test_adam_state_skip(run):
         assert np.isnan(gs_np[:, ~seen_now]).all() and not np.isnan(gs_np[:, seen_now]).any()
         for a, c in zip(dense, sparse):
             assert torch.equal(a, c)
+        for a, c in zip(dense, compact):
+            assert torch.equal(a, c)
+        cnt = int(gcount.item())
+        assert int(ovf.item()) == 0
+        assert np.array_equal(glist[:cnt].cpu().numpy(), np.flatnonzero(seen_now))
+        gc_np = PY.np_(g_c)
+        assert np.array_equal(gc_np[:, :cnt].view(np.uint32), PY.np_(grad)[:, seen_now].view(np.uint32))
+        assert np.isnan(gc_np[:, cnt:]).all()
         g = PY.np_(grad)
         ref = O.adam(before[0], g, before[1], before[2], cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, step)
         PY.check_adam([PY.np_(x) for x in skip], ref, before[0], g, before[1], cfg.lr, cfg.beta1)
@@ -248,6 +274,30 @@ def test_adam_state_skip(run):
     vis0 = ((r0[..., 2] > r0[..., 0]) & (r0[..., 3] > r0[..., 1])).any(axis=0)  # visible in the scene itself
     ever = (keep[0] | keep[1] | keep[2]) & vis0
     assert np.array_equal(st != 0, ever)
+    assert torch.equal(state, state_c)
     # never seen: untouched
     assert torch.equal(skip[0][:, : n // 8], p0[:, : n // 8])
+    # a compact buffer too narrow: the flag, the columns that fit, no update
+    L.gs_seen_gaussians(b.rect, n, b.V, glist, gcount, sws)
+    torch.cuda.synchronize()
+    cnt = int(gcount.item())
+    narrow = max(1, cnt // 3)
+    assert cnt > narrow
+    g_full = torch.empty_like(p0)
+    L.gs_preprocess_bwd(compact[0], n, b.sh_degree, b.cams, b.rect, b.grad2d, g_full)
+    g_n = torch.full((b.P, narrow), float("nan"), device=dev)
+    L.gs_preprocess_bwd_compact(compact[0], n, b.sh_degree, b.cams, b.rect, b.grad2d, glist, gcount, narrow, g_n,
+                                ovf)
+    held = [x.clone() for x in compact]
+    L.gs_adam_step_compact(compact[0], g_n, narrow, glist, gcount, compact[1], compact[2], n, b.P, b.rect, b.V,
+                           cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, 4, state=state_c, skip=ovf)
+    torch.cuda.synchronize()
+    assert int(ovf.item()) == 1
+    L.gs_preprocess_bwd_compact(compact[0], n, b.sh_degree, b.cams, b.rect, b.grad2d, glist, gcount, stride, g_c, ovf)
+    torch.cuda.synchronize()
+    assert int(ovf.item()) == 1  # sticky: a call that fits leaves it set
+    cols = glist[:narrow].long()
+    assert np.array_equal(PY.np_(g_n).view(np.uint32), PY.np_(g_full[:, cols]).view(np.uint32))
+    for a, c in zip(held, compact):
+        assert torch.equal(a, c)
     print({"never_seen": int((~ever).sum()), "seen": int(ever.sum())})

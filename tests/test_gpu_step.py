@@ -86,6 +86,57 @@ def test_deferred_count_redoes_overflowing_steps():
     assert ts.redone > r0 and int(ts.sticky.item()) == 0 and b.capacity >= b.K > 16
 
 
+def test_compact_gradient_redoes_a_step_that_does_not_fit():
+    """The separate backward into the compact gradient: each step's update is
+    the dense Adam of the dense gradient of that step's own 2D gradients, bit
+    for bit; a step whose seen Gaussians do not fit the buffer sets the sticky
+    flag, changes nothing, and is redone with a buffer planned for them."""
+    import torch
+    dev = torch.device("cuda:0")
+    cfg = S.CONFIGS[0]
+    cams = cfg.cameras()
+    p = torch.from_numpy(S.make_params(cfg)).to(dev)
+    target = render(torch.from_numpy(S.make_target_params(cfg)).to(dev), cfg.sh_degree, cams).clone()
+    ts = TrainStep(p.clone(), cfg.sh_degree, cams, target, lr=cfg.lr, betas=(cfg.beta1, cfg.beta2), eps=cfg.eps,
+                   fused_adam=False, fused_raster=False, sparse_grad="compact")
+    b = ts.buf
+
+    def check_dense(before):
+        """ts's state against the dense update from `before` with the step's
+        2D gradients (still in the buffers)"""
+        th, m, v = (x.clone() for x in before)
+        g = torch.empty_like(th)
+        L.gs_preprocess_bwd(th, b.n, b.sh_degree, b.cams, b.rect, b.grad2d, g)
+        L.gs_adam_step(th, g, m, v, th.numel(), cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, ts.t)
+        torch.cuda.synchronize()
+        for a, c in ((th, ts.params), (m, ts.m), (v, ts.v)):
+            assert torch.equal(a, c)
+
+    start = [x.clone() for x in (ts.params, ts.m, ts.v)]
+    ts.step()
+    ts.flush()
+    assert ts.compact_grad and ts.grad.shape[1] == ts.grad_stride > 16 and b.lists_without_count()
+    check_dense(start)
+    after1 = [x.clone() for x in (ts.params, ts.m, ts.v)]
+    # a buffer of 16 columns: the step is voided on the device, then redone
+    ts.grad_stride = 16
+    ts.grad = torch.empty((b.P, 16), dtype=torch.float32, device=dev)
+    ts.step()
+    torch.cuda.synchronize()
+    assert int(ts.sticky.item()) == 1
+    for a, c in zip(after1, (ts.params, ts.m, ts.v)):
+        assert torch.equal(a, c)
+    ts.flush()
+    assert ts.t == 1 and ts.redone == 1 and int(ts.sticky.item()) == 0 and ts.grad_stride == 0
+    ts.step()
+    ts.flush()
+    before3 = [x.clone() for x in (ts.params, ts.m, ts.v)]
+    ts.step()
+    ts.flush()
+    assert ts.t == 3 and ts.redone == 1 and ts.grad_stride >= int(ts.seen_count.item())
+    check_dense(before3)
+
+
 @pytest.mark.parametrize("fused_raster", [True, False], ids=["fused", "separate"])
 @pytest.mark.parametrize("band_rows", [8, 13])
 def test_bands_equal_whole_image(band_rows, fused_raster):

@@ -3,7 +3,8 @@ element, through the C ABI:
 
   * TrainStep's defaults (and, on the odd-size scene, the separate raster
     passes with the separate backward writing a sparse gradient and Adam
-    reading it only for visible Gaussians): binned per-tile lists built with the capacity the
+    reading it only for visible Gaussians, or writing only the seen
+    Gaussians' columns, consecutively: also on the culled scene): binned per-tile lists built with the capacity the
     step has (no host read of the intersection count) under the sticky
     overflow flag; the fused forward + L1 + backward raster pass, tiles taken
     longest list first; 2D-gradient records cleared by the preprocess; Adam
@@ -56,7 +57,7 @@ def _log(msg):
     print(f"[timed] {msg}", flush=True)
 
 
-def _run_timed(cfg, band_rows=None, list_budget=None, separate=False, lists="auto"):
+def _run_timed(cfg, band_rows=None, list_budget=None, separate=False, lists="auto", sparse_grad=True):
     import torch
 
     from gaussian_splatting_differentiable_ewa_amd.step import TrainStep, render, spatial_order
@@ -69,7 +70,8 @@ def _run_timed(cfg, band_rows=None, list_budget=None, separate=False, lists="aut
     target0 = S.random_image(cfg.target_seed, len(cams), cams[0].height, cams[0].width)
     ts = TrainStep(torch.from_numpy(p_np).to(dev), cfg.sh_degree, cams, torch.from_numpy(target0).to(dev),
                    lr=cfg.lr, betas=(cfg.beta1, cfg.beta2), eps=cfg.eps, write_image=True, band_rows=band_rows,
-                   list_budget=list_budget, fused_raster=not separate, fused_adam=not separate, lists=lists)
+                   list_budget=list_budget, fused_raster=not separate, fused_adam=not separate, lists=lists,
+                   sparse_grad=sparse_grad)
     ts.step()
     ts.flush()
     assert ts.t == 1
@@ -90,7 +92,8 @@ def _run_timed(cfg, band_rows=None, list_budget=None, separate=False, lists="aut
         _log(f"windows {ts.windows}, list bytes {ts.list_bytes()}")
         assert len(ts.windows) >= 2 and (list_budget is None or ts.list_bytes() <= list_budget)
     elif separate:
-        assert not ts.fused_raster and not ts.fused_adam and ts.sparse_grad and ts._use_state
+        assert not ts.fused_raster and not ts.fused_adam and ts.sparse_grad == sparse_grad and ts._use_state
+        assert ts.compact_grad == (sparse_grad == "compact")
     else:
         assert b.lists_without_count() and b.path == (lists if lists != "auto" else "binned")
         assert ts.fused_raster and ts._use_state
@@ -136,11 +139,16 @@ DEGENERATE_LISTS = {"one-view-empty": "compact", "culled-compact": "compact"}
 
 
 @pytest.fixture(scope="module", params=["ragged", "ragged-bands", "ragged-budget", "ragged-separate", "ragged-compact",
-                                        "headline", "culled-compact"] + list(DEGENERATE))
+                                        "ragged-compact-grad", "headline", "culled-compact", "culled-compact-grad"]
+                + list(DEGENERATE))
 def timed(request):
     import torch
     assert torch.cuda.is_available()
-    if request.param in DEGENERATE or request.param == "culled-compact":
+    if request.param == "culled-compact-grad":
+        # nothing seen: an empty compact gradient, Adam touching nothing
+        r = _run_timed(DEGENERATE["culled"], lists="binned", separate=True, sparse_grad="compact")
+        assert r["K"] == 0 and not r["gpu"]["state"].any()
+    elif request.param in DEGENERATE or request.param == "culled-compact":
         # the binned lists as on the timed path, whatever the intersection count
         cfg = DEGENERATE[request.param.replace("-compact", "")]
         r = _run_timed(cfg, lists=DEGENERATE_LISTS.get(request.param, "binned"))
@@ -153,6 +161,10 @@ def timed(request):
         # the separate forward + L1 and backward passes, and the separate
         # backward (sparse gradient) and Adam (visible set, state flags)
         r = _run_timed(S.RAGGED, separate=True)
+    elif request.param == "ragged-compact-grad":
+        # the separate passes with the backward writing only the columns of
+        # the Gaussians seen, consecutively, and Adam reading them
+        r = _run_timed(S.RAGGED, separate=True, sparse_grad="compact")
     elif request.param == "ragged-compact":
         # binning only the Gaussians each view sees, the grid sized for them
         # (the builder the step picks when most (view, Gaussian) pairs are culled)
