@@ -2,6 +2,8 @@
 // and the prefix-sum / fill kernels used by several stages.
 #include <math.h>
 
+#include <algorithm>
+
 #include "internal.h"
 
 namespace gs {
@@ -271,7 +273,8 @@ int32_t gs_sort_end_bit(int32_t n_views, int64_t tiles_per_view)
 size_t gs_preprocess_workspace_bytes(int64_t n, int32_t n_views)
 {
     if (n < 0 || n_views < 1) return 0;
-    return gs::scan_workspace_bytes((uint64_t)n * (uint64_t)n_views);
+    // the scan of the counts, or (without offsets) the wave sums
+    return std::max<size_t>(gs::scan_workspace_bytes((uint64_t)n * (uint64_t)n_views), (size_t)((n + 63) / 64) * 4);
 }
 
 gs_status gs_stream_copy(void* dst, const void* src, uint64_t bytes, void* stream)

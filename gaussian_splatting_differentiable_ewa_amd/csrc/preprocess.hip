@@ -75,13 +75,16 @@ __device__ __forceinline__ void zero_grad2d_block(float* __restrict__ g2z, int64
 // empty rectangles without loading the rest, so that the waves of a scene
 // stored in a spatial order that lie outside every view read 24 of 236 bytes.
 // The others load their remaining rows together, then every view is pure
-// arithmetic plus the record stores.
+// arithmetic plus the record stores. The per-(view, Gaussian) tile counts go
+// to `counts` when it is given; with `wave_sums`, each wave's sum of them goes
+// to wave_sums[g / 64] (for the total alone, without the offsets).
 template <int DEG>
 __global__ __launch_bounds__(PRE_THREADS) void k_preprocess(const float* __restrict__ P, int64_t n,
                                                             const DevCameras cams, const ShConsts K,
                                                             float* __restrict__ rec, uint16_t* __restrict__ rect,
                                                             float* __restrict__ depth, float* __restrict__ g2zero,
-                                                            uint32_t* __restrict__ counts)
+                                                            uint32_t* __restrict__ counts,
+                                                            uint32_t* __restrict__ wave_sums)
 {
     constexpr int NB = (DEG + 1) * (DEG + 1);
     const int64_t g = (int64_t)blockIdx.x * PRE_THREADS + threadIdx.x;
@@ -102,11 +105,12 @@ __global__ __launch_bounds__(PRE_THREADS) void k_preprocess(const float* __restr
         if (here)
             for (int v = 0; v < cams.n_views; ++v) {
                 const int64_t idx = (int64_t)v * n + g;
-                counts[idx] = 0u;
+                if (counts) counts[idx] = 0u;
                 *(uint2*)(rect + 4 * idx) = make_uint2(0u, 0u);
             }
     }
     uint32_t vis_bits = 0u;  // bit v: visible in view v
+    uint32_t my_count = 0u;  // tile count summed over the views
     if (maybe) {
 #pragma unroll
         for (int r = 6; r < 11; ++r) raw[r] = P[(int64_t)r * n + g];
@@ -122,7 +126,7 @@ __global__ __launch_bounds__(PRE_THREADS) void k_preprocess(const float* __restr
             view_project(x, y, z, L, cam, cams.tiles_x, cams.tiles_y, p);
             const int64_t idx = (int64_t)v * n + g;
             if (!p.visible) {
-                counts[idx] = 0u;
+                if (counts) counts[idx] = 0u;
                 *(uint2*)(rect + 4 * idx) = make_uint2(0u, 0u);
                 continue;
             }
@@ -144,11 +148,36 @@ __global__ __launch_bounds__(PRE_THREADS) void k_preprocess(const float* __restr
             if (depth) depth[idx] = p.zc;
             *(uint2*)(rect + 4 * idx) = make_uint2((uint32_t)p.x0 | ((uint32_t)p.y0 << 16),
                                                    (uint32_t)p.x1 | ((uint32_t)p.y1 << 16));
-            counts[idx] = (uint32_t)((p.x1 - p.x0) * (p.y1 - p.y0));
+            const uint32_t cnt = (uint32_t)((p.x1 - p.x0) * (p.y1 - p.y0));
+            if (counts) counts[idx] = cnt;
+            my_count += cnt;
         }
+    }
+    if (wave_sums) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) my_count += __shfl_xor(my_count, off);
+        if ((threadIdx.x & 63u) == 0u) wave_sums[g0 >> 6] = my_count;
     }
     if (g2zero)
         for (int v = 0; v < cams.n_views; ++v) zero_grad2d_block(g2zero, n, v, g0, ballot((vis_bits >> v) & 1u) != 0ull);
+}
+
+// *total = the sum of `count` wave sums (one workgroup; 64-bit).
+__global__ __launch_bounds__(1024) void k_sum_counts(const uint32_t* __restrict__ s, int64_t count,
+                                                     uint64_t* __restrict__ total)
+{
+    __shared__ uint64_t w[16];
+    uint64_t acc = 0;
+    for (int64_t i = threadIdx.x; i < count; i += 1024) acc += s[i];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if ((threadIdx.x & 63u) == 0u) w[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t t = 0;
+        for (int k = 0; k < 16; ++k) t += w[k];
+        *total = t;
+    }
 }
 
 // One thread per (view, Gaussian): its tiles in row-major order, at its offset.
@@ -202,28 +231,35 @@ gs_status gs_preprocess(const float* params, int64_t n, int32_t sh_degree, const
                         uint64_t* total, void* ws, size_t ws_bytes, void* stream)
 {
     if (n < 0 || sh_degree < 0 || sh_degree > 3) return GS_ERR_INVALID_ARGUMENT;
-    if (!offsets || !total || !ws) return GS_ERR_INVALID_ARGUMENT;
+    if (!total || !ws) return GS_ERR_INVALID_ARGUMENT;
     if (n > 0 && (!params || !rec || !rect)) return GS_ERR_INVALID_ARGUMENT;
     if (n > ((int64_t)1 << 31)) return GS_ERR_INVALID_ARGUMENT;
     DevCameras dc;
     if (!make_dev_cameras(cams, n_views, dc)) return GS_ERR_INVALID_ARGUMENT;
     const uint64_t entries = (uint64_t)n * (uint64_t)n_views;
-    if (ws_bytes < scan_workspace_bytes(entries)) return GS_ERR_INVALID_ARGUMENT;
+    const int64_t waves = (n + 63) / 64;
+    if (ws_bytes < (offsets ? scan_workspace_bytes(entries) : (size_t)waves * 4)) return GS_ERR_INVALID_ARGUMENT;
     hipStream_t s = (hipStream_t)stream;
+    uint32_t* wave_sums = offsets ? nullptr : (uint32_t*)ws;
     if (n > 0) {
         const dim3 grid(grid_for((uint64_t)n, PRE_THREADS)), block(PRE_THREADS);
         const ShConsts K = sh_constants();
         switch (sh_degree) {
-            case 0: hipLaunchKernelGGL(k_preprocess<0>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, grad2d, offsets); break;
-            case 1: hipLaunchKernelGGL(k_preprocess<1>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, grad2d, offsets); break;
-            case 2: hipLaunchKernelGGL(k_preprocess<2>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, grad2d, offsets); break;
-            default: hipLaunchKernelGGL(k_preprocess<3>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, grad2d, offsets); break;
+            case 0: hipLaunchKernelGGL(k_preprocess<0>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, grad2d, offsets, wave_sums); break;
+            case 1: hipLaunchKernelGGL(k_preprocess<1>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, grad2d, offsets, wave_sums); break;
+            case 2: hipLaunchKernelGGL(k_preprocess<2>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, grad2d, offsets, wave_sums); break;
+            default: hipLaunchKernelGGL(k_preprocess<3>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, grad2d, offsets, wave_sums); break;
         }
         if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     }
-    // counts were written into `offsets`; scan them in place
-    if (scan_u32(offsets, offsets, entries, total, ws, s) != hipSuccess) return GS_ERR_HIP;
-    return GS_OK;
+    if (offsets) {
+        // counts were written into `offsets`; scan them in place
+        if (scan_u32(offsets, offsets, entries, total, ws, s) != hipSuccess) return GS_ERR_HIP;
+        return GS_OK;
+    }
+    if (n == 0) return fill_u32((uint32_t*)total, 2, 0u, s) == hipSuccess ? GS_OK : GS_ERR_HIP;
+    hipLaunchKernelGGL(k_sum_counts, dim3(1), dim3(1024), 0, s, wave_sums, waves, total);
+    return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
 }
 
 gs_status gs_emit_intersections(const float* rec, const uint16_t* rect, const uint32_t* offsets, int64_t n,

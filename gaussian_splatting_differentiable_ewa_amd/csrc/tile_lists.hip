@@ -138,10 +138,13 @@ __device__ __forceinline__ bool band_rect(uint2 rr, const BinGrid& G, uint32_t t
     return x1 > x0 && ly1 > ly0;
 }
 
+// Also clears the overflow flag (which k_bin_fill may set), so that no launch
+// of its own is needed.
 __global__ __launch_bounds__(256) void k_bin_count(const uint16_t* __restrict__ rect, const BinGrid G,
-                                                   uint32_t* __restrict__ table)
+                                                   uint32_t* __restrict__ table, int32_t* __restrict__ overflow)
 {
     __shared__ uint32_t cnt[BAND_TILES];
+    if (blockIdx.x == 0 && threadIdx.x == 0) *overflow = 0;
     const BinBlock B = bin_block(G);
     const uint32_t nt = (B.ty1 - B.ty0) * (uint32_t)G.tiles_x;
     for (uint32_t i = threadIdx.x; i < nt; i += 256) cnt[i] = 0u;
@@ -1055,12 +1058,12 @@ gs_status gs_tile_lists(const float* rec, const uint16_t* rect, const float* dep
     uint2* alt = (uint2*)(w + L.alt);
     uint32_t* big = (uint32_t*)(w + L.big);
     hipStream_t s = (hipStream_t)stream;
-    if (fill_u32((uint32_t*)overflow, 1, 0u, s) != hipSuccess) return GS_ERR_HIP;
     const unsigned bin_blocks = (unsigned)((int64_t)n_views * G.chunks * G.bands);
     if (n > 0) {
-        hipLaunchKernelGGL(k_bin_count, dim3(bin_blocks), dim3(256), 0, s, rect, G, table);
+        hipLaunchKernelGGL(k_bin_count, dim3(bin_blocks), dim3(256), 0, s, rect, G, table, overflow);
         if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
-    } else if (fill_u32(table, (uint64_t)n_tiles * G.chunks, 0u, s) != hipSuccess) {
+    } else if (fill_u32((uint32_t*)overflow, 1, 0u, s) != hipSuccess ||
+               fill_u32(table, (uint64_t)n_tiles * G.chunks, 0u, s) != hipSuccess) {
         return GS_ERR_HIP;
     }
     hipLaunchKernelGGL(k_bin_colscan, dim3(grid_for((uint64_t)n_tiles, 64)), dim3(256), 0, s, table, G, n_views,

@@ -34,10 +34,15 @@ from . import _lib as L
 class Buffers:
     """Device buffers of one step for N Gaussians and a set of same-size views."""
 
-    def __init__(self, n: int, sh_degree: int, cams: Sequence, device="cuda", lists: str = "auto"):
+    def __init__(self, n: int, sh_degree: int, cams: Sequence, device="cuda", lists: str = "auto",
+                 offsets: Optional[bool] = None):
         if lists not in ("auto", "binned", "radix", "compact"):
             raise ValueError(f"unknown list builder {lists!r}")
         self.lists = lists
+        # the per-entry offsets of the tile counts: only the global key sort
+        # needs them (the preprocess then scans the counts; otherwise it forms
+        # the total alone)
+        self.with_offsets = lists == "radix" if offsets is None else bool(offsets)
         self.path = "binned" if lists == "auto" else lists
         self.n = int(n)
         self.sh_degree = int(sh_degree)
@@ -52,7 +57,7 @@ class Buffers:
         self.rec = torch.empty(V * n * L.GS_REC_FLOATS, dtype=torch.float32, device=dev)
         self.rect = torch.empty(V * n * 4, dtype=torch.int16, device=dev)
         self.depth = torch.empty(V * n, dtype=torch.float32, device=dev)  # compact depths for the list builder
-        self.offsets = torch.empty(V * n + 1, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(V * n + 1, dtype=torch.int32, device=dev) if self.with_offsets else None
         self.total = torch.zeros(1, dtype=torch.int64, device=dev)
         self.pre_ws = torch.empty(L.preprocess_workspace_bytes(n, V), dtype=torch.uint8, device=dev)
         self.ranges = torch.empty(V * self.T * 2, dtype=torch.int32, device=dev)
@@ -124,8 +129,9 @@ class Buffers:
         """Records, rectangles, scanned counts, the compact depths, and the
         2D-gradient records of every visible (view, Gaussian) set to zero
         (the raster passes add to them)."""
-        L.gs_preprocess(params, self.n, self.sh_degree, self.cams, self.rec, self.rect, self.offsets,
-                        self.total, self.pre_ws, depth=self.depth, grad2d=self.grad2d)
+        L.gs_preprocess(params, self.n, self.sh_degree, self.cams, self.rec, self.rect,
+                        self.offsets if self.with_offsets else None, self.total, self.pre_ws, depth=self.depth,
+                        grad2d=self.grad2d)
 
     def lists_without_count(self) -> bool:
         """Whether the lists can be built before K is known on the host."""

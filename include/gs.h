@@ -162,12 +162,16 @@ size_t gs_sort_workspace_bytes(uint64_t n_keys);
  *            accumulate without a separate clear
  *   offsets  out [n_views * n + 1] uint32: offsets[i] = sum of the tile counts
  *            of entries before i (low 32 bits); the count of entry i is the
- *            area of its rectangle
+ *            area of its rectangle. Or NULL: no counts or offsets are
+ *            written and only the total is formed (per-wave sums of the
+ *            counts, then their sum), which is all gs_tile_lists needs;
+ *            gs_emit_intersections needs the offsets
  *   total    out device uint64: total intersection count K
  *   ws       device workspace of gs_preprocess_workspace_bytes(n, n_views)
+ *            (with NULL offsets, 4 ceil(n / 64) bytes suffice)
  * n may be 0. Errors: n < 0, sh_degree outside 0..3, n_views outside
- * 1..GS_MAX_VIEWS, views of different sizes, null pointers, small workspace,
- * n_views * tiles_per_view >= 2^31.
+ * 1..GS_MAX_VIEWS, views of different sizes, null pointers (other than the
+ * optional ones), small workspace, n_views * tiles_per_view >= 2^31.
  */
 gs_status gs_preprocess(const float* params, int64_t n, int32_t sh_degree, const gs_camera* cams,
                         int32_t n_views, float* rec, uint16_t* rect, float* depth,

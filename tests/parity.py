@@ -42,7 +42,7 @@ def gpu_forward(params_np: np.ndarray, sh: int, cams, bg=(0.0, 0.0, 0.0)):
     the Buffers object (device state kept for the backward) and host copies."""
     dev = torch.device("cuda:0")
     p = torch.from_numpy(np.ascontiguousarray(params_np)).to(dev)
-    b = Buffers(p.shape[1], sh, cams, device=dev, lists="binned")
+    b = Buffers(p.shape[1], sh, cams, device=dev, lists="binned", offsets=True)
     b.preprocess(p)
     torch.cuda.synchronize()
     out = {"params_t": p,

@@ -81,7 +81,9 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert pre(sh=4) == INV
     assert pre(V=0) == INV
     assert pre(V=17) == INV
-    assert pre(offsets=None) == INV
+    assert pre(total=None) == INV
+    assert pre(offsets=None, total=None) == INV
+    assert pre(offsets=None, ws_bytes=ctypes.c_size_t(3)) == INV  # the wave sums of 10 Gaussians: 4 bytes
     assert pre(ws_bytes=0) == INV
     assert pre(cams=L.cameras([_cam(), _cam(width=128)]), V=2) == INV
     assert pre(cams=L.cameras([_cam(fx=0.0)])) == INV

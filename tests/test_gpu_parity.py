@@ -45,6 +45,28 @@ def test_preprocess(run):
     assert st["K"] > 0
 
 
+def test_preprocess_without_offsets(run):
+    """gs_preprocess without offsets (the binned path's form: no per-entry
+    counts written or scanned): the same records, rectangles and depths bit
+    for bit, and the same total K."""
+    import torch
+    from gaussian_splatting_differentiable_ewa_amd import _lib as L
+    from gaussian_splatting_differentiable_ewa_amd.step import Buffers
+    b0, gpu = run["buf"], run["gpu"]
+    b = Buffers(b0.n, b0.sh_degree, b0.cams, device=b0.device, lists="binned")
+    assert not b.with_offsets and b.offsets is None
+    b.total.fill_(12345)
+    b.preprocess(gpu["params_t"])
+    torch.cuda.synchronize()
+    assert int(b.total.item()) == gpu["total"]
+    assert torch.equal(b.rect, b0.rect)
+    r = b.rect.view(b.V, b.n, 4).to(torch.int32) & 0xffff
+    vis = (r[..., 2] > r[..., 0]) & (r[..., 3] > r[..., 1])  # records of culled pairs are not written
+    assert torch.equal(b.rec.view(b.V, b.n, L.GS_REC_FLOATS)[vis], b0.rec.view(b.V, b.n, L.GS_REC_FLOATS)[vis])
+    assert torch.equal(b.depth.view(b.V, b.n)[vis], b0.depth.view(b.V, b.n)[vis])
+    print({"K": gpu["total"]})
+
+
 def test_keys_sort_ranges(run):
     K = PY.check_keys(run["gpu"], run["cams"])
     # end to end: the oracle's own projection gives the same keys
