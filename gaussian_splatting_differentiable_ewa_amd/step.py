@@ -376,10 +376,14 @@ class TrainStep:
             self.win_ws = torch.empty(L.window_gaussians_workspace_bytes(b.n, b.V), dtype=torch.uint8, device=dev)
         self.write_image = write_image
         dev = params.device
-        self.sticky = torch.zeros(1, dtype=torch.int32, device=dev)  # an unverified step overflowed
-        self._host = [(torch.zeros(1, dtype=torch.int64, pin_memory=True),
-                       torch.zeros(1, dtype=torch.int32, pin_memory=True)) for _ in range(self.RING)]
-        self._pending = []  # (t, event, host K, host flag), oldest first
+        # the intersection count K and the sticky flag (an unverified step
+        # overflowed) side by side, so that one asynchronous copy takes both
+        # to the host after a step
+        self._dev_state = torch.zeros(2, dtype=torch.int64, device=dev)
+        self.buf.total = self._dev_state[0:1]
+        self.sticky = self._dev_state[1:2].view(torch.int32)[0:1]
+        self._host = [torch.zeros(2, dtype=torch.int64, pin_memory=True) for _ in range(self.RING)]
+        self._pending = []  # (t, event, host copy of K and the flag), oldest first
         self._slot = 0
         self.redone = 0  # steps redone after an overflow
 
@@ -589,13 +593,12 @@ class TrainStep:
                 else:
                     L.gs_adam_step(*args)
         if deferred:
-            hk, hf = self._host[self._slot]
+            h = self._host[self._slot]
             self._slot = (self._slot + 1) % self.RING
-            hk.copy_(b.total, non_blocking=True)
-            hf.copy_(self.sticky, non_blocking=True)
+            h.copy_(self._dev_state, non_blocking=True)
             ev = torch.cuda.Event()
             ev.record()
-            self._pending.append((self.t, ev, hk, hf))
+            self._pending.append((self.t, ev, h))
         mark(len(self.stage_names))
 
     def evaluated_pairs(self) -> int:
@@ -622,15 +625,15 @@ class TrainStep:
         """Check the oldest launched steps' copied K and flag, in order."""
         b = self.buf
         while self._pending:
-            t, ev, hk, hf = self._pending[0]
+            t, ev, h = self._pending[0]
             if not ev.query():
                 if not block:
                     return
                 ev.synchronize()
                 block = False  # one wait frees a slot
             self._pending.pop(0)
-            b.K = int(hk.item())
-            if int(hf.item()) != 0:
+            b.K = int(h[0])
+            if int(h[1]) != 0:  # the flag (the upper half of the word is never written)
                 # step t is the first whose lists overflowed: every update from
                 # it on was skipped, so redo from step t with room for K
                 torch.cuda.synchronize()
