@@ -24,7 +24,10 @@ hipError_t scan_u32(const uint32_t* in, uint32_t* out, uint64_t count, uint64_t*
 hipError_t fill_u32(uint32_t* dst, uint64_t count, uint32_t value, hipStream_t stream);
 
 // *loss (+)= scale * sum of `count` per-quarter partial sums of |I - I*|
-// (the L1 loss of the raster kernels); zeroed first unless `accumulate`.
+// (the L1 loss of the raster kernels): overwritten unless `accumulate`; the
+// same bits on every run. The workspace holds, after the partials, the
+// reduction's tail (LOSS_TAIL_BYTES, raster_fwd.h), whose counter the raster
+// kernel that wrote the partials has reset.
 hipError_t loss_from_partials(const double* partial, int64_t count, double scale, double* loss, bool accumulate,
                               hipStream_t stream);
 

@@ -133,6 +133,7 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_fwd_bwd_l1(
 {
 #pragma clang fp contract(off)
     __shared__ __align__(16) unsigned char lds[FUSED_LDS_BYTES];
+    if (blockIdx.x == 0 && threadIdx.x == 0) *loss_counter(partial, gridDim.x) = 0u;
     const QuarterCtx t = quarter_ctx(W, H, TX, T, row0, order);
     if (t.empty) {
         if (t.lane == 0) partial[blockIdx.x] = 0.0;
@@ -183,12 +184,14 @@ using namespace gs;
 
 extern "C" {
 
-// per quarter a loss partial; per tile its slot in the order; per segment of
-// ORDER_SEG tiles its class counts
+// per quarter a loss partial, then the loss reduction's sums and counter;
+// per tile its slot in the order; per segment of ORDER_SEG tiles its class
+// counts
 static size_t fused_ws_bytes(int64_t tiles)
 {
     const int64_t segs = (tiles + ORDER_SEG - 1) / ORDER_SEG;
-    return (size_t)(tiles * 4 * sizeof(double) + tiles * sizeof(uint32_t) + segs * ORDER_CLASSES * sizeof(uint32_t));
+    return (size_t)(tiles * 4 * sizeof(double) + LOSS_TAIL_BYTES + tiles * sizeof(uint32_t) +
+                    segs * ORDER_CLASSES * sizeof(uint32_t));
 }
 
 size_t gs_rasterize_fwd_bwd_l1_workspace_bytes(int32_t n_views, int32_t width, int32_t height)
@@ -212,7 +215,7 @@ static gs_status fused_launch(const RasterArgs& a, const float* rec, int64_t n, 
             return GS_ERR_HIP;
     }
     double* partial = (double*)ws;
-    uint32_t* order = (uint32_t*)(partial + a.n_blocks);
+    uint32_t* order = (uint32_t*)((char*)(partial + a.n_blocks) + LOSS_TAIL_BYTES);
     uint32_t* table = order + n_tiles;
     const uint32_t n_seg = (uint32_t)((n_tiles + ORDER_SEG - 1) / ORDER_SEG);
     hipLaunchKernelGGL(k_order_count, dim3(n_seg), dim3(ORDER_THREADS), 0, s, ranges, n_tiles, table);

@@ -168,6 +168,17 @@ __device__ __forceinline__ FwdPixel raster_fwd_walk(FwdLds& L, const QuarterCtx&
 // dL/dI of one channel for L1: scale * sign(I - I*), sign(0) = 0.
 __device__ __forceinline__ float l1_grad(float d, float scale) { return d > 0.f ? scale : (d < 0.f ? -scale : 0.f); }
 
+// After the per-quarter partial sums in a raster pass's workspace: the loss
+// reduction's per-workgroup sums and its arrival counter. The pass's first
+// workgroup resets the counter (so a fresh workspace needs no clearing) and
+// the reduction's last workgroup resets it again.
+constexpr int LOSS_BLOCKS = 256;
+constexpr size_t LOSS_TAIL_BYTES = (LOSS_BLOCKS + 2) * sizeof(double);
+__host__ __device__ inline uint32_t* loss_counter(double* partial, int64_t n_partials)
+{
+    return (uint32_t*)(partial + n_partials + LOSS_BLOCKS);
+}
+
 // The wave's sum of `ad` (fp64) written to partial[blockIdx.x] by lane 0.
 __device__ __forceinline__ void loss_partial(float ad, int lane, double* __restrict__ partial)
 {

@@ -22,6 +22,7 @@ __device__ __forceinline__ void raster_fwd_body(const float* __restrict__ rec, i
 {
 #pragma clang fp contract(off)
     __shared__ FwdLds lds;
+    if (L1 && blockIdx.x == 0 && threadIdx.x == 0) *loss_counter(partial, gridDim.x) = 0u;
     const QuarterCtx t = quarter_ctx(W, H, TX, T, row0);
     if (t.empty) {
         if (L1 && t.lane == 0) partial[blockIdx.x] = 0.0;
@@ -85,21 +86,48 @@ __global__ __launch_bounds__(RW_THREADS) void k_raster_fwd_l1(const float* __res
                           dL, partial);
 }
 
-// loss += scale * sum of the per-quarter partial sums: each workgroup sums a
-// contiguous slice, then one fp64 atomic per workgroup
-__global__ __launch_bounds__(256) void k_loss_partials(const double* __restrict__ partial, int64_t count,
-                                                       double scale, double* __restrict__ loss)
+// The sum of 256 values, one per thread, in a fixed order (every thread
+// returns it).
+__device__ __forceinline__ double block_sum_256(double v, double* s_w)
 {
-    __shared__ double s_w[4];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return ((s_w[0] + s_w[1]) + s_w[2]) + s_w[3];
+}
+
+// loss (+)= scale * sum of the per-quarter partial sums, the same bits on
+// every run: each workgroup sums a contiguous slice in a fixed order and
+// stores it; the workgroup that arrives last (the arrival counter after the
+// sums) adds the workgroups' sums in index order and writes the loss.
+__global__ __launch_bounds__(256) void k_loss_partials(const double* __restrict__ partial, int64_t count,
+                                                       double scale, double* __restrict__ loss, int accumulate)
+{
+    __shared__ double s_w[4], s_w2[4];
+    __shared__ int s_last;
+    double* bsum = const_cast<double*>(partial) + count;
+    uint32_t* counter = loss_counter(const_cast<double*>(partial), count);
     const int64_t per = (count + gridDim.x - 1) / gridDim.x;
     const int64_t b0 = (int64_t)blockIdx.x * per, b1 = min(count, b0 + per);
     double acc = 0.0;
     for (int64_t i = b0 + threadIdx.x; i < b1; i += 256) acc += partial[i];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = acc;
+    const double mine = block_sum_256(acc, s_w);
+    if (threadIdx.x == 0) {
+        __hip_atomic_store(bsum + blockIdx.x, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t before = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = before == gridDim.x - 1u;
+    }
     __syncthreads();
-    if (threadIdx.x == 0) atomicAdd(loss, (((s_w[0] + s_w[1]) + s_w[2]) + s_w[3]) * scale);
+    if (!s_last) return;
+    const double v = threadIdx.x < gridDim.x
+                         ? __hip_atomic_load(bsum + threadIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : 0.0;
+    const double total = block_sum_256(v, s_w2);
+    if (threadIdx.x == 0) {
+        *loss = accumulate ? *loss + total * scale : total * scale;
+        __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // The raster passes' exponential, element-wise (for checks of its error).
@@ -112,12 +140,9 @@ __global__ __launch_bounds__(256) void k_raster_exp(const float* __restrict__ x,
 hipError_t loss_from_partials(const double* partial, int64_t count, double scale, double* loss, bool accumulate,
                               hipStream_t stream)
 {
-    if (!accumulate) {
-        const hipError_t e = fill_u32((uint32_t*)loss, 2, 0u, stream);
-        if (e != hipSuccess) return e;
-    }
-    const unsigned red_blocks = (unsigned)(count < 256 * 64 ? (count + 63) / 64 : 256);
-    hipLaunchKernelGGL(k_loss_partials, dim3(red_blocks), dim3(256), 0, stream, partial, count, scale, loss);
+    const unsigned red_blocks = (unsigned)(count < LOSS_BLOCKS * 64 ? (count + 63) / 64 : LOSS_BLOCKS);
+    hipLaunchKernelGGL(k_loss_partials, dim3(red_blocks), dim3(256), 0, stream, partial, count, scale, loss,
+                       accumulate ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -131,7 +156,7 @@ size_t gs_rasterize_fwd_l1_workspace_bytes(int32_t n_views, int32_t width, int32
 {
     if (n_views < 1 || n_views > GS_MAX_VIEWS || width <= 0 || height <= 0) return 0;
     const int64_t quarters = (int64_t)n_views * gs_tiles_x(width) * gs_tiles_y(height) * 4;
-    return (size_t)quarters * sizeof(double);
+    return (size_t)quarters * sizeof(double) + LOSS_TAIL_BYTES;
 }
 
 gs_status gs_rasterize_fwd_l1(const float* rec, int64_t n, const uint32_t* ranges, const uint32_t* vals,
@@ -144,7 +169,7 @@ gs_status gs_rasterize_fwd_l1(const float* rec, int64_t n, const uint32_t* range
     if (!raster_args(rec, n, ranges, vals, masks, capacity, cams, n_views, row0, rows, bg, a))
         return GS_ERR_INVALID_ARGUMENT;
     if (!T_final || !n_contrib || !target || !dL_dimage || !loss || !ws) return GS_ERR_INVALID_ARGUMENT;
-    if (ws_bytes < (size_t)a.n_blocks * sizeof(double)) return GS_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < (size_t)a.n_blocks * sizeof(double) + LOSS_TAIL_BYTES) return GS_ERR_INVALID_ARGUMENT;
     hipStream_t s = (hipStream_t)stream;
     double* partial = (double*)ws;
     hipLaunchKernelGGL(k_raster_fwd_l1, dim3((unsigned)a.n_blocks), dim3(RW_THREADS), 0, s, rec, n, ranges, vals,

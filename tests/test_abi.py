@@ -155,7 +155,7 @@ def test_invalid_arguments_rejected_on_host(lib):
     # masks when it is non-zero
     bg = (ctypes.c_float * 3)(0, 0, 0)
     qws = L.rasterize_fwd_l1_workspace_bytes(1, 256, 256)
-    assert qws == 16 * 16 * 4 * 8 and L.rasterize_fwd_l1_workspace_bytes(0, 256, 256) == 0
+    assert qws == 16 * 16 * 4 * 8 + 258 * 8 and L.rasterize_fwd_l1_workspace_bytes(0, 256, 256) == 0
     head = ["rec", "n", "ranges", "vals", "masks", "capacity", "cams", "V", "row0", "rows", "bg"]
     head_ok = dict(rec=fake, n=10, ranges=fake, vals=fake, masks=fake, capacity=100, cams=cams, V=1, row0=0, rows=16,
                    bg=bg)
@@ -207,7 +207,7 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert bwd(grad2d=None) == INV
 
     fws = L.rasterize_fwd_bwd_l1_workspace_bytes(1, 256, 256)
-    assert fws == 16 * 16 * (4 * 8 + 4) + 8 * 4 and L.rasterize_fwd_bwd_l1_workspace_bytes(1, 0, 256) == 0
+    assert fws == 16 * 16 * (4 * 8 + 4) + 258 * 8 + 8 * 4 and L.rasterize_fwd_bwd_l1_workspace_bytes(1, 0, 256) == 0
     fb_names = head + ["target", "scale", "image", "T_final", "n_contrib", "dL", "loss", "grad2d", "accumulate", "ws",
                        "ws_bytes", "stream"]
     fb_ok = dict(head_ok, target=fake, scale=1.0, image=None, T_final=None, n_contrib=None, dL=None, loss=fake,

@@ -121,6 +121,30 @@ def test_forward_l1_fused(run):
     assert fused["loss"] == pytest.approx(loss_o, rel=1e-6)
 
 
+def test_loss_deterministic(run):
+    """The raster passes' loss is the same fp64 value on every call, also
+    from a workspace whose bytes are garbage (the reduction's counter lives
+    there), and an accumulating call adds exactly that value."""
+    import torch
+    b = run["buf"]
+    tgt = torch.from_numpy(np.ascontiguousarray(run["target"])).to(b.device)
+    vals = []
+    for fill in (0xFF, 0x00, 0x5A):
+        b.fwd_l1_ws.fill_(fill)
+        b.rasterize_loss_l1(tgt)
+        torch.cuda.synchronize()
+        vals.append(float(b.loss.item()))
+        b.rasterize_fwd_bwd_l1(tgt, accumulate=False)
+        torch.cuda.synchronize()
+        vals.append(float(b.loss.item()))
+    assert len(set(vals)) == 1, vals
+    b.rasterize_fwd_bwd_l1(tgt, accumulate=True)  # loss += the same value
+    torch.cuda.synchronize()
+    assert float(b.loss.item()) == vals[0] + vals[0]
+    loss_o, _ = O.loss_l1(run["gpu"]["image"], run["target"])
+    assert vals[0] == pytest.approx(loss_o, rel=1e-6)
+
+
 def test_backward(run):
     fwd = run["fwd"]
     _, dL = O.loss_l1(fwd["image"], run["target"])
