@@ -137,6 +137,49 @@ def test_compact_gradient_redoes_a_step_that_does_not_fit():
     check_dense(before3)
 
 
+ZERO_MODES = {
+    "default": dict(),
+    "separate": dict(fused_raster=False, fused_adam=False),
+    "compact-grad": dict(fused_raster=False, fused_adam=False, sparse_grad="compact"),
+    "compact-lists": dict(lists="compact"),
+    "bands": dict(band_rows=3),
+    "budget": dict(list_budget=20_000_000),
+}
+
+
+@pytest.mark.parametrize("mode", list(ZERO_MODES))
+def test_zero_gaussians(mode):
+    """A scene with no Gaussians (every call takes n = 0) on the odd-size
+    views: each pixel is the background, T_final is 1 and n_contrib 0, the
+    loss is the oracle's L1 of that image against the target, and the steps
+    run and count as applied."""
+    import torch
+
+    from oracle import oracle as O
+    dev = torch.device("cuda:0")
+    cfg = S.RAGGED
+    cams = cfg.cameras()
+    p = torch.zeros((L.param_rows(cfg.sh_degree), 0), dtype=torch.float32, device=dev)
+    rng = np.random.default_rng(5)
+    target = rng.random((len(cams), 3, cams[0].height, cams[0].width)).astype(np.float32)
+    bg = (0.25, 0.5, 0.75)
+    ts = TrainStep(p, cfg.sh_degree, cams, torch.from_numpy(target).to(dev), bg=bg, write_image=True,
+                   **ZERO_MODES[mode])
+    for _ in range(2):
+        ts.step()
+    ts.flush()
+    torch.cuda.synchronize()
+    b = ts.buf
+    assert ts.t == 2 and ts.redone == 0 and b.K == 0
+    img = b.image.cpu().numpy()
+    expect = np.broadcast_to(np.asarray(bg, np.float32)[None, :, None, None], img.shape)
+    assert np.array_equal(img, expect)
+    if not ts.windowed:  # the windowed step writes these per window, not kept
+        assert (b.T_final.cpu().numpy() == 1.0).all() and (b.n_contrib.cpu().numpy() == 0).all()
+    loss_o, _ = O.loss_l1(np.ascontiguousarray(expect), target)
+    assert float(b.loss.item()) == pytest.approx(loss_o, rel=1e-6)
+
+
 @pytest.mark.parametrize("fused_raster", [True, False], ids=["fused", "separate"])
 @pytest.mark.parametrize("band_rows", [8, 13])
 def test_bands_equal_whole_image(band_rows, fused_raster):
