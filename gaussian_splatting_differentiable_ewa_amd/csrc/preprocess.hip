@@ -6,6 +6,8 @@
 // 48-byte record per view as three 16-byte stores.
 #include <math.h>
 
+#include <algorithm>
+
 #include "internal.h"
 #include "project.h"
 
@@ -77,15 +79,18 @@ __device__ __forceinline__ void zero_grad2d_block(float* __restrict__ g2z, int64
 // The others load their remaining rows together, then every view is pure
 // arithmetic plus the record stores. The per-(view, Gaussian) tile counts go
 // to `counts` when it is given; with `wave_sums`, each wave's sum of them goes
-// to wave_sums[g / 64] (for the total alone, without the offsets).
+// to wave_sums[g / 64] (for the total alone, without the offsets), and the
+// first thread zeroes *total, which k_sum_counts then adds to.
 template <int DEG>
 __global__ __launch_bounds__(PRE_THREADS) void k_preprocess(const float* __restrict__ P, int64_t n,
                                                             const DevCameras cams, const ShConsts K,
                                                             float* __restrict__ rec, uint16_t* __restrict__ rect,
                                                             float* __restrict__ depth, float* __restrict__ g2zero,
                                                             uint32_t* __restrict__ counts,
-                                                            uint32_t* __restrict__ wave_sums)
+                                                            uint32_t* __restrict__ wave_sums,
+                                                            uint64_t* __restrict__ total)
 {
+    if (wave_sums && blockIdx.x == 0 && threadIdx.x == 0) *total = 0;
     constexpr int NB = (DEG + 1) * (DEG + 1);
     const int64_t g = (int64_t)blockIdx.x * PRE_THREADS + threadIdx.x;
     const int64_t g0 = g & ~(int64_t)63;  // the wave's first Gaussian
@@ -162,21 +167,25 @@ __global__ __launch_bounds__(PRE_THREADS) void k_preprocess(const float* __restr
         for (int v = 0; v < cams.n_views; ++v) zero_grad2d_block(g2zero, n, v, g0, ballot((vis_bits >> v) & 1u) != 0ull);
 }
 
-// *total = the sum of `count` wave sums (one workgroup; 64-bit).
-__global__ __launch_bounds__(1024) void k_sum_counts(const uint32_t* __restrict__ s, int64_t count,
-                                                     uint64_t* __restrict__ total)
+// *total (zeroed by k_preprocess) += the sum of `count` wave sums: each
+// workgroup sums a contiguous slice and adds it with one 64-bit integer
+// atomic (exact in any order).
+constexpr int SUM_THREADS = 256;
+__global__ __launch_bounds__(SUM_THREADS) void k_sum_counts(const uint32_t* __restrict__ s, int64_t count,
+                                                            uint64_t* __restrict__ total)
 {
-    __shared__ uint64_t w[16];
+    __shared__ uint64_t w[SUM_THREADS / 64];
+    const int64_t per = (count + gridDim.x - 1) / gridDim.x;
+    const int64_t b0 = (int64_t)blockIdx.x * per, b1 = min(count, b0 + per);
     uint64_t acc = 0;
-    for (int64_t i = threadIdx.x; i < count; i += 1024) acc += s[i];
+    for (int64_t i = b0 + threadIdx.x; i < b1; i += SUM_THREADS) acc += s[i];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
     if ((threadIdx.x & 63u) == 0u) w[threadIdx.x >> 6] = acc;
     __syncthreads();
     if (threadIdx.x == 0) {
-        uint64_t t = 0;
-        for (int k = 0; k < 16; ++k) t += w[k];
-        *total = t;
+        const uint64_t t = (w[0] + w[1]) + (w[2] + w[3]);
+        if (t) atomicAdd((unsigned long long*)total, (unsigned long long)t);
     }
 }
 
@@ -245,10 +254,10 @@ gs_status gs_preprocess(const float* params, int64_t n, int32_t sh_degree, const
         const dim3 grid(grid_for((uint64_t)n, PRE_THREADS)), block(PRE_THREADS);
         const ShConsts K = sh_constants();
         switch (sh_degree) {
-            case 0: hipLaunchKernelGGL(k_preprocess<0>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, grad2d, offsets, wave_sums); break;
-            case 1: hipLaunchKernelGGL(k_preprocess<1>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, grad2d, offsets, wave_sums); break;
-            case 2: hipLaunchKernelGGL(k_preprocess<2>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, grad2d, offsets, wave_sums); break;
-            default: hipLaunchKernelGGL(k_preprocess<3>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, grad2d, offsets, wave_sums); break;
+            case 0: hipLaunchKernelGGL(k_preprocess<0>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, grad2d, offsets, wave_sums, total); break;
+            case 1: hipLaunchKernelGGL(k_preprocess<1>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, grad2d, offsets, wave_sums, total); break;
+            case 2: hipLaunchKernelGGL(k_preprocess<2>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, grad2d, offsets, wave_sums, total); break;
+            default: hipLaunchKernelGGL(k_preprocess<3>, grid, block, 0, s, params, n, dc, K, rec, rect, depth, grad2d, offsets, wave_sums, total); break;
         }
         if (hipGetLastError() != hipSuccess) return GS_ERR_HIP;
     }
@@ -258,7 +267,9 @@ gs_status gs_preprocess(const float* params, int64_t n, int32_t sh_degree, const
         return GS_OK;
     }
     if (n == 0) return fill_u32((uint32_t*)total, 2, 0u, s) == hipSuccess ? GS_OK : GS_ERR_HIP;
-    hipLaunchKernelGGL(k_sum_counts, dim3(1), dim3(1024), 0, s, wave_sums, waves, total);
+    // a workgroup per 2048 wave sums, at most 1024 workgroups
+    const unsigned sum_blocks = (unsigned)std::min<int64_t>(1024, (waves + 2047) / 2048);
+    hipLaunchKernelGGL(k_sum_counts, dim3(sum_blocks), dim3(SUM_THREADS), 0, s, wave_sums, waves, total);
     return hipGetLastError() == hipSuccess ? GS_OK : GS_ERR_HIP;
 }
 
