@@ -202,7 +202,11 @@ def impl_bytes(P, n, V, K, Nv, n_any, n_px, n_adam=None):
         # means for culling, the rest for Gaussians visible anywhere; per
         # visible pair a 48-byte record, an 8-byte rectangle, a 4-byte depth
         # copy and its 36-byte 2D-gradient record zeroed; a count per pair
+        # (the global key sort's path, which then scans them: "scan"), or
+        # per wave of 64 Gaussians a 4-byte sum of its counts (the binned
+        # path: only the total is formed)
         "preprocess": 12 * n + (Bp - 12) * n_any + (48 + 8 + 4 + 36) * Nv + 4 * V * n,
+        "preprocess_total": 12 * n + (Bp - 12) * n_any + (48 + 8 + 4 + 36) * Nv + 4 * ((n + 63) // 64),
         "scan": 8 * V * n,
         # the binned lists: rectangles and depths of visible pairs read twice
         # (count, fill), an id and a 16-bit sub-block mask written per
@@ -340,7 +344,7 @@ def main():
     step_bytes = sum(mb.values())
     frac_step = step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9)
     ib = impl_bytes(b.P, b.n, V, K, sum(n_vis), n_any, n_px, n_adam)
-    used = ["preprocess"]
+    used = ["preprocess"] + (["scan"] if b.with_offsets else [])
     if ts.windowed or b.binned:
         used.append("intersections")
         if b.path == "compact" and not ts.windowed:
@@ -351,7 +355,8 @@ def main():
     sep = {None: "", "visible": "_visible", "compact": "_compact", "dense": ""}[args.separate_backward]
     # a stage's impl term under the stage's own name (the separate backward's
     # sparse forms have their own byte counts)
-    stage_term = {"preprocess_bwd": "preprocess_bwd" + sep, "adam": "adam" + sep}
+    stage_term = {"preprocess_bwd": "preprocess_bwd" + sep, "adam": "adam" + sep,
+                  "preprocess": "preprocess" if b.with_offsets else "preprocess_total"}
     used += ["preprocess_bwd_adam"] if ts.fused_adam else ["preprocess_bwd", "adam"]
     impl_terms = {k: int(ib[stage_term.get(k, k)]) for k in used}
     ib = {k: ib[stage_term.get(k, k)] for k in ib}
@@ -584,6 +589,8 @@ def runs_summary(files, commands, note):
             opts.append("dense Adam")
         if d.get("camera_turn_deg_per_step"):
             opts.append(f"camera {d['camera_turn_deg_per_step']:g} deg/step")
+        if d.get("backward", "fused") != "fused":
+            opts.append(f"separate backward ({d['backward']} gradient, {d['grad_buffer_bytes'] / 1e6:.0f} MB)")
         opts.append(d.get("list_builder", ""))
         rf = d["roofline"]
         cpu = d.get("cpu_baseline") or {}
