@@ -49,8 +49,9 @@ namespace gs {
 constexpr int TL_THREADS = 256;
 constexpr int TL_CAP = 4096;                    // entries a tile sorts in LDS
 constexpr int TL_ROUNDS = TL_CAP / TL_THREADS;  // rounds of 64 keys per wave, at most
-constexpr int GL_CHUNK = 4096;                  // entries per chunk of the global-memory path
+constexpr int GL_CHUNK = 2048;                  // entries per chunk of the global-memory path
 constexpr int GL_ROUNDS = GL_CHUNK / TL_THREADS;
+constexpr uint32_t GL_RUN = GL_ROUNDS * 64;  // a chunk's items ranked by one wave (a contiguous run)
 constexpr int TL_CLASSES = 4;  // length classes of the tiles k_tl_sort takes, longest first
 constexpr int WV_CAP = 512;  // entries one wave sorts alone
 constexpr int WV_ROUNDS = WV_CAP / 64;
@@ -339,8 +340,9 @@ __device__ __forceinline__ void write_mask(const MaskOut& mo, int64_t tile_lin, 
 }
 
 // The ids of a sorted tile and, when wanted, their masks: positions first,
-// first + stride, ... of the tile, four at a time so that the id reads and
-// then the record gathers of four entries are in flight together.
+// first + stride, ... of the tile, MASK_BATCH at a time so that the id reads
+// and then the record gathers of that many entries are in flight together.
+constexpr int MASK_BATCH = 4;
 template <uint32_t STRIDE, typename IdAt>
 __device__ __forceinline__ void write_ids_masks(const MaskOut& mo, int64_t tile_lin, uint32_t start, uint32_t n,
                                                 uint32_t first, IdAt id_at, uint32_t* __restrict__ vals)
@@ -349,22 +351,22 @@ __device__ __forceinline__ void write_ids_masks(const MaskOut& mo, int64_t tile_
     const int tile = (int)(tile_lin - view * mo.T);
     const int wy = tile / mo.TX, tx = tile - wy * mo.TX, ty = wy + mo.row0;
     const float* rv = mo.rec + view * mo.n * GS_REC_FLOATS;
-    for (uint32_t i0 = first; i0 < n; i0 += 4 * STRIDE) {
-        Entry E[4];
+    for (uint32_t i0 = first; i0 < n; i0 += MASK_BATCH * STRIDE) {
+        Entry E[MASK_BATCH];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < MASK_BATCH; ++k) {
             const uint32_t i = i0 + (uint32_t)k * STRIDE;
             E[k].valid = i < n;
             E[k].gid = E[k].valid ? id_at(i) : 0u;
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int k = 0; k < MASK_BATCH; ++k)
             if (E[k].valid) vals[start + i0 + (uint32_t)k * STRIDE] = E[k].gid;
         if (!mo.masks) continue;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) gather_record(E[k], rv, mo.n);
+        for (int k = 0; k < MASK_BATCH; ++k) gather_record(E[k], rv, mo.n);
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int k = 0; k < MASK_BATCH; ++k)
             if (E[k].valid) mo.masks[start + i0 + (uint32_t)k * STRIDE] = (uint16_t)tile_mask16(E[k], tx * 16, ty * 16, mo.W, mo.H);
     }
 }
@@ -647,7 +649,11 @@ __device__ __forceinline__ void tl_wg_passes(uint32_t n, uint32_t R, uint32_t po
 {
     const uint32_t t = threadIdx.x, lane = t & 63u, wave = t >> 6;
     const uint32_t wbeg = wave * 64u * R;
-    uint32_t rank[TL_ROUNDS], dig[TL_ROUNDS];
+    // idx[r] holds the item's position (bits 0-11, < TL_CAP); during a pass
+    // its rank among the wave's items of its digit (bits 12-22, < 64 R <=
+    // 1024) and the digit (bits 23-30) ride in the same register, which keeps
+    // the kernel's registers low enough for more waves per SIMD
+    static_assert(TL_CAP <= 4096 && TL_ROUNDS * 64 <= 2048, "position and rank fields");
     for (int p = 0; p < 8; ++p) {
         if (((positions >> p) & 1u) == 0u) continue;  // uniform digit: order unchanged
 #pragma unroll
@@ -658,13 +664,14 @@ __device__ __forceinline__ void tl_wg_passes(uint32_t n, uint32_t R, uint32_t po
             if ((uint32_t)r >= R) break;  // uniform across the workgroup
             const uint32_t i = wbeg + (uint32_t)r * 64u + lane;
             const bool valid = i < n;
-            dig[r] = valid ? tl_digit(key[r], p < 4 ? tp[idx[r]].y : 0u, p) : 0u;
-            const uint64_t peers = tl_peers(dig[r], ballot(valid));
+            const uint32_t pos12 = idx[r] & 0xfffu;
+            const uint32_t d = valid ? tl_digit(key[r], p < 4 ? tp[pos12].y : 0u, p) : 0u;
+            const uint64_t peers = tl_peers(d, ballot(valid));
             const uint32_t below = mask_rank(peers);
-            const uint32_t prior = wcnt[wave][dig[r]];
-            rank[r] = prior + below;
+            const uint32_t prior = wcnt[wave][d];
+            idx[r] = pos12 | ((prior + below) << 12) | (d << 23);
             asm volatile("" ::: "memory");  // every lane has read the counter
-            if (valid && below == 0u) wcnt[wave][dig[r]] = prior + (uint32_t)__popcll(peers);
+            if (valid && below == 0u) wcnt[wave][d] = prior + (uint32_t)__popcll(peers);
             asm volatile("" ::: "memory");
         }
         __syncthreads();
@@ -682,9 +689,9 @@ __device__ __forceinline__ void tl_wg_passes(uint32_t n, uint32_t R, uint32_t po
             if ((uint32_t)r >= R) break;
             const uint32_t i = wbeg + (uint32_t)r * 64u + lane;
             if (i < n) {
-                const uint32_t pos = wcnt[wave][dig[r]] + rank[r];
+                const uint32_t pos = wcnt[wave][idx[r] >> 23] + ((idx[r] >> 12) & 0x7ffu);
                 s_key[pos] = key[r];
-                s_idx[pos] = (uint16_t)idx[r];
+                s_idx[pos] = (uint16_t)(idx[r] & 0xfffu);
             }
         }
         __syncthreads();
@@ -723,12 +730,12 @@ __device__ __forceinline__ uint2* tl_global_passes(uint32_t n, uint32_t position
         uint2 k[GL_ROUNDS];
 #pragma unroll
         for (int r = 0; r < GL_ROUNDS; ++r) {
-            const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
+            const uint32_t i = base + wave * GL_RUN + (uint32_t)r * 64u + lane;
             k[r] = i < n ? src[i] : make_uint2(0u, 0u);
         }
 #pragma unroll
         for (int r = 0; r < GL_ROUNDS; ++r) {
-            const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
+            const uint32_t i = base + wave * GL_RUN + (uint32_t)r * 64u + lane;
             const uint64_t vm = ballot(i < n);
             if (vm == 0ull) break;  // wave-uniform
             for (int p = 0; p < 8; ++p) {
@@ -752,11 +759,11 @@ __device__ __forceinline__ uint2* tl_global_passes(uint32_t n, uint32_t position
         running[t] = tl_exclusive_256(hist[p][t], s_misc);
         __syncthreads();
         for (uint32_t base = 0; base < n; base += (uint32_t)GL_CHUNK) {
-            // chunk [base, base + 4096): wave w ranks its run of 1024
+            // chunk [base, base + GL_CHUNK): wave w ranks its run of GL_RUN
             uint2 item[GL_ROUNDS];
 #pragma unroll
             for (int r = 0; r < GL_ROUNDS; ++r) {
-                const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
+                const uint32_t i = base + wave * GL_RUN + (uint32_t)r * 64u + lane;
                 item[r] = i < n ? src[i] : make_uint2(0u, 0u);
             }
 #pragma unroll
@@ -765,7 +772,7 @@ __device__ __forceinline__ uint2* tl_global_passes(uint32_t n, uint32_t position
             uint32_t rk[GL_ROUNDS];
 #pragma unroll
             for (int r = 0; r < GL_ROUNDS; ++r) {
-                const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
+                const uint32_t i = base + wave * GL_RUN + (uint32_t)r * 64u + lane;
                 const bool valid = i < n;
                 const uint32_t d = tl_digit(item[r].x, item[r].y, p);
                 const uint64_t peers = tl_peers(d, ballot(valid));
@@ -789,7 +796,7 @@ __device__ __forceinline__ uint2* tl_global_passes(uint32_t n, uint32_t position
             __syncthreads();
 #pragma unroll
             for (int r = 0; r < GL_ROUNDS; ++r) {
-                const uint32_t i = base + wave * 1024u + (uint32_t)r * 64u + lane;
+                const uint32_t i = base + wave * GL_RUN + (uint32_t)r * 64u + lane;
                 if (i < n) {
                     const uint32_t pos = cw[wave][tl_digit(item[r].x, item[r].y, p)] + rk[r];
                     if (pos < n) dst[pos] = item[r];
