@@ -3,8 +3,8 @@ sort (ordered by tile, depth bits, Gaussian index) on synthetic rectangles
 and depths built to stress it: many equal depths (the order of equal depths
 is decided by the index), every depth equal (tiles that are one run of ties,
 of hundreds to thousands of entries), tiles with more entries than one
-workgroup sorts in LDS (4096) and than the long-tile sort holds (8192), empty
-tiles and views, and a capacity with slack."""
+workgroup sorts in LDS (4096: their passes run over global memory in chunks,
+several chunks per tile), empty tiles and views, and a capacity with slack."""
 
 import numpy as np
 import pytest
@@ -47,8 +47,8 @@ CASES = [
     (3, 9000, 2, (0.6, 0.0), 0),         # view 0: every tile > 4096 entries
     (4, 9000, 2, (0.55, 0.02), 7),       # long lists with heavy ties
     (5, 500, 3, (0.0, 1.0, 0.0), 3),     # every Gaussian in every tile of view 1
-    (6, 20000, 1, (0.45,), 0),           # every tile > 8192 entries: the global-memory path
-    (7, 14000, 2, (0.0, 0.5), 9),        # view 1: 7000-entry tiles in the long-tile LDS sort, ties
+    (6, 20000, 1, (0.45,), 0),           # every tile > 8192 entries: the global-memory path, 5 chunks
+    (7, 14000, 2, (0.0, 0.5), 9),        # view 1: 7000-entry tiles over global memory, with ties
     # every Gaussian at one depth (a wall facing the camera): each tile's list
     # is one run of equal depths, ordered by index alone -- with one wave
     # (about 300 entries per tile), one workgroup in LDS (about 2700) and the
