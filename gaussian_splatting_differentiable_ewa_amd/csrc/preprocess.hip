@@ -1,5 +1,5 @@
-// gs_preprocess (Gaussian-wise projection + prefix sum of tile counts),
-// gs_emit_intersections and gs_tile_ranges.
+// gs_preprocess (Gaussian-wise projection + prefix sum of tile counts, or
+// their total alone), gs_emit_intersections and gs_tile_ranges.
 //
 // Layout: parameters are [P][n] SoA, so a wave's 64 lanes read 64 consecutive
 // floats of each row (one 256-byte line per row). Each lane writes its

@@ -147,7 +147,8 @@ size_t gs_sort_workspace_bytes(uint64_t n_keys);
  * rectangle), EWA 2D covariance and its conic, radius ceil(3 sqrt(lambda_max)),
  * tile rectangle [x0, x1) x [y0, y1), SH colour; then an exclusive prefix sum
  * of the per-(v, g) tile counts (the scan is decoupled look-back in
- * reference [21] of the fVDB page; here a reduce-then-scan).
+ * reference [21] of the fVDB page; here a reduce-then-scan), or only their
+ * total.
  *   params   [P][n] fp32 (P from sh_degree), read only
  *   cams     host array of n_views cameras, all of one image size
  *   rec      out [n_views][n][12] fp32 (see GS_REC_*)
