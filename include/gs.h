@@ -391,7 +391,8 @@ gs_status gs_loss_l1(const float* image, const float* target, int64_t count, flo
                      float* dL_dimage, double* loss, int32_t accumulate, void* stream);
 
 /* Workspace of gs_rasterize_fwd_l1 (bytes): one double per 8x8 quarter of
- * every tile; 0 on invalid sizes. */
+ * every tile, then the loss reduction's 256 workgroup sums and its arrival
+ * counter (2064 bytes; no clearing needed); 0 on invalid sizes. */
 size_t gs_rasterize_fwd_l1_workspace_bytes(int32_t n_views, int32_t width, int32_t height);
 
 /*
@@ -404,7 +405,9 @@ size_t gs_rasterize_fwd_l1_workspace_bytes(int32_t n_views, int32_t width, int32
  *   capacity  as gs_rasterize_fwd
  *   target    [V][3][H][W]
  *   image     out [V][3][H][W], or null when not wanted
- *   loss      device double: overwritten, or added to when `accumulate`
+ *   loss      device double: overwritten, or added to when `accumulate`; the
+ *             same bits on every call (the partial sums are added in a fixed
+ *             order)
  *   ws        device workspace of gs_rasterize_fwd_l1_workspace_bytes(...)
  * Errors: as gs_rasterize_fwd, plus null target / dL_dimage / loss / ws or a
  * small workspace.
@@ -452,18 +455,20 @@ gs_status gs_rasterize_bwd(const float* rec, int64_t n, const uint32_t* ranges,
  *   n_contrib  out [V][H][W], or null
  *   dL_dimage  out [V][3][H][W], or null
  *   loss       device double: overwritten, or added to when `accumulate` has
- *              GS_ACCUMULATE_LOSS
+ *              GS_ACCUMULATE_LOSS; the same bits on every call
  *   grad2d     [V][n][9] fp32 as in gs_rasterize_bwd: zeroed first unless
  *              `accumulate` has GS_ACCUMULATE_GRAD2D
  *   ws         device workspace of gs_rasterize_fwd_bwd_l1_workspace_bytes(...):
- *              the per-quarter loss partials and the order in which the pass
- *              takes the tiles (longest lists first)
+ *              the per-quarter loss partials and their reduction's sums and
+ *              counter, and the order in which the pass takes the tiles
+ *              (longest lists first)
  * Errors: as gs_rasterize_fwd, plus null target / loss / ws / grad2d (n > 0),
  * a small workspace or an `accumulate` with other bits than the two flags.
  */
 /* Workspace of gs_rasterize_fwd_bwd_l1 (bytes): one double per 8x8 quarter,
- * one 32-bit tile index per tile of every view, and eight 32-bit class counts
- * per 1024 tiles (the longest-first tile order); 0 on invalid sizes. */
+ * the loss reduction's 2064 bytes, one 32-bit tile index per tile of every
+ * view, and eight 32-bit class counts per 1024 tiles (the longest-first tile
+ * order); 0 on invalid sizes. */
 size_t gs_rasterize_fwd_bwd_l1_workspace_bytes(int32_t n_views, int32_t width, int32_t height);
 
 gs_status gs_rasterize_fwd_bwd_l1(const float* rec, int64_t n, const uint32_t* ranges,
